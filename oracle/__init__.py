@@ -1,0 +1,155 @@
+"""CPU oracle (float64) for the gated delta rule recurrence with state fake-quantization.
+
+TEST INFRASTRUCTURE ONLY: this package may be imported by the tests, by
+``__graft_entry__.smoke()`` and by the bench's CPU-baseline leg, never by the
+library.  It wraps ``oracle.c`` (plain C, built with gcc) through ctypes and
+shares no code with the GPU path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "oracle.c")
+_LIB = os.path.join(_DIR, "liboracle.so")
+
+GATE_SCALAR, GATE_KEY = 0, 1
+QDQ_NONE, QDQ_INT8, QDQ_E4M3 = 0, 1, 2
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_DIR, "oracle.h"))
+    ):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True, cwd=_DIR)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("B", "T", "H", "dk", "dv", "gate", "qdq", "group", "hadamard", "qdq_interval",
+                 "ckpt_interval")]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = build()
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        lib.oracle_e4m3_code.restype = ctypes.c_int
+        lib.oracle_e4m3_code.argtypes = [ctypes.c_double]
+        lib.oracle_hadamard.restype = None
+        lib.oracle_hadamard.argtypes = [ctypes.c_int, ctypes.c_int, dp, dp]
+        lib.oracle_qdq.restype = ctypes.c_int
+        lib.oracle_qdq.argtypes = [ctypes.c_int] * 5 + [dp, dp, ctypes.c_void_p, ctypes.c_void_p,
+                                                       ctypes.c_void_p]
+        lib.oracle_fwd.restype = ctypes.c_int
+        lib.oracle_fwd.argtypes = [ctypes.POINTER(_Cfg)] + [ctypes.c_void_p] * 9
+        lib.oracle_bwd.restype = ctypes.c_int
+        lib.oracle_bwd.argtypes = [ctypes.POINTER(_Cfg)] + [ctypes.c_void_p] * 15
+        _lib = lib
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _d(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def e4m3_value(code: int) -> float:
+    return _load().oracle_e4m3_value(int(code))
+
+
+def e4m3_code(y: float) -> int:
+    return _load().oracle_e4m3_code(float(y))
+
+
+def hadamard(X: np.ndarray) -> np.ndarray:
+    """Hn X along the first (key) axis of a d_k x d_v matrix."""
+    X = _d(X)
+    Y = np.empty_like(X)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _load().oracle_hadamard(X.shape[0], X.shape[1], X.ctypes.data_as(dp), Y.ctypes.data_as(dp))
+    return Y
+
+
+def qdq(X: np.ndarray, mode: int, group: int, hadamard: bool = False):
+    """Fake-quantize one d_k x d_v state; returns (Xhat, codes, scales, ypre)."""
+    X = _d(X)
+    dk, dv = X.shape
+    Xh = np.empty_like(X)
+    codes = np.zeros((dk, dv), dtype=np.int32)
+    nsc = (dk * (dv // group)) if mode == QDQ_INT8 else (dv // group)
+    scales = np.zeros(nsc, dtype=np.float32)
+    ypre = np.zeros((dk, dv), dtype=np.float32)
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = _load().oracle_qdq(mode, group, int(hadamard), dk, dv, X.ctypes.data_as(dp),
+                            Xh.ctypes.data_as(dp), _p(codes), _p(scales), _p(ypre))
+    if rc:
+        raise ValueError("oracle_qdq rejected its arguments")
+    return Xh, codes, scales, ypre
+
+
+def _cfg(B, T, H, dk, dv, gate, qdq_mode, group, hadamard, qdq_interval, ckpt_interval):
+    return _Cfg(B, T, H, dk, dv, gate, qdq_mode, group, int(hadamard), qdq_interval, ckpt_interval)
+
+
+def fwd(q, k, v, g, beta, S0=None, *, gate=GATE_SCALAR, qdq_mode=QDQ_NONE, group=32,
+        hadamard=False, qdq_interval=1, ckpt_interval=0):
+    """Forward recurrence.  Returns (o, S_T, ckpts or None), all float64."""
+    q, k, v, g, beta = map(_d, (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S0 = None if S0 is None else _d(S0)
+    o = np.zeros((B, T, H, dv))
+    ST = np.zeros((B, H, dk, dv))
+    ck = None
+    if ckpt_interval > 0:
+        ck = np.zeros((B, H, (T + ckpt_interval - 1) // ckpt_interval, dk, dv))
+    c = _cfg(B, T, H, dk, dv, gate, qdq_mode, group, hadamard, qdq_interval, ckpt_interval)
+    rc = _load().oracle_fwd(ctypes.byref(c), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(o),
+                            _p(ST), _p(ck))
+    if rc:
+        raise ValueError("oracle_fwd rejected its configuration")
+    return o, ST, ck
+
+
+def bwd(q, k, v, g, beta, S0, dout, dST=None, states=None, *, gate=GATE_SCALAR,
+        qdq_mode=QDQ_NONE, group=32, hadamard=False, qdq_interval=1):
+    """Straight-through backward.  Returns dict of dq, dk, dv, dg, dbeta, dS0 (float64)."""
+    q, k, v, g, beta, dout = map(_d, (q, k, v, g, beta, dout))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S0 = None if S0 is None else _d(S0)
+    dST = None if dST is None else _d(dST)
+    states = None if states is None else _d(states)
+    out = {
+        "dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+        "dg": np.zeros_like(g), "dbeta": np.zeros_like(beta), "dS0": np.zeros((B, H, dk, dv)),
+    }
+    c = _cfg(B, T, H, dk, dv, gate, qdq_mode, group, hadamard, qdq_interval, 0)
+    rc = _load().oracle_bwd(ctypes.byref(c), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
+                            _p(states), _p(dout), _p(dST), _p(out["dq"]), _p(out["dk"]),
+                            _p(out["dv"]), _p(out["dg"]), _p(out["dbeta"]), _p(out["dS0"]))
+    if rc:
+        raise ValueError("oracle_bwd rejected its configuration")
+    return out
