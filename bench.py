@@ -1,0 +1,225 @@
+"""Benchmark: token-head state updates per second of the batched decode step.
+
+Workload (one step): GDN single-token decode over B=256 sequences x H=16 heads, d_k = d_v =
+128, bf16 q/k/v/g/beta, FP32 state (268 MB) read, updated, INT8 group-32 fake-quantized and
+written back in place.  Inputs are resident in HBM before the timed region; three state
+buffers (805 MB, above the 256 MB Infinity Cache) are rotated so each step streams its state
+from HBM.  Prints one JSON line with the throughput, the decode kernel's roofline figures
+(HBM-bound; algorithmic bytes per launch / mean launch time) and the CPU oracle's rate on the
+host cores for the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X vector FP32 (packed)
+METRIC = "token·head state updates/s + % of HBM/VALU roofline, GDN/KDA d=128 QDQ"
+
+
+def decode_algorithmic_bytes(B, H, dk, dv, in_bytes=2, out_bytes=4):
+    """State read + write, q/k/v, g/beta, o: what one decode launch must move."""
+    state = 2 * 4 * B * H * dk * dv
+    qkv = B * H * (2 * dk + dv) * in_bytes
+    gb = 2 * B * H * in_bytes
+    o = B * H * dv * out_bytes
+    return state + qkv + gb + o
+
+
+def kernel_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "quantized_state_qat_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(summary_name, khash):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was taken on the
+    current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", summary_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_hash") != khash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def bench_decode(steps, warmup):
+    import numpy as np
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    w = synth.WORKLOADS[1]
+    d = synth.generate(w)
+    dev = {k: torch.from_numpy(d[k].bits.astype(np.int16)).view(torch.bfloat16).cuda()
+           for k in ("q", "k", "v", "g", "beta")}
+    S0 = torch.from_numpy(d["S0"].f32).cuda()
+    states = [S0.clone() for _ in range(3)]
+    o = torch.empty((w.B, 1, w.H, w.d_v), device="cuda")
+    c = la.Config(B=w.B, T=1, H=w.H, d_k=w.d_k, d_v=w.d_v, qdq=la.LA_QDQ_INT8_GROUP, group=32)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        la.la_decode_step(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], states[i % 3], o,
+                          stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    total = ev[0][0].elapsed_time(ev[-1][1]) * 1e-3
+    mean_launch = sum(per) / len(per)
+    nbytes = decode_algorithmic_bytes(w.B, w.H, w.d_k, w.d_v)
+    return {
+        "w": w, "d": d, "total_s": total, "wall_s": wall, "mean_launch_s": mean_launch,
+        "updates": w.B * w.H * steps, "bytes_per_launch": nbytes,
+    }
+
+
+def bench_long_e4m3(steps=3, warmup=1):
+    """GDN B=8 H=16 T=4096 d=128, E4M3 tile QDQ every 64 tokens (FP32 VALU-bound)."""
+    import numpy as np
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    w = synth.WORKLOADS[2]
+    d = synth.generate(w)
+    dev = {}
+    for k in ("q", "k", "v"):
+        dev[k] = torch.from_numpy(d[k].bits.astype(np.int16)).view(torch.bfloat16).cuda()
+    for k in ("g", "beta"):
+        dev[k] = torch.from_numpy(d[k].f32).cuda()
+    del d
+    o = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
+    ST = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    c = la.Config(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v, qdq=la.LA_QDQ_E4M3_TILE, group=64,
+                  qdq_interval=64, gate_dtype=la.LA_F32)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o, ST, stream=stream)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o, ST, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    t = sum(times) / len(times)
+    flops = 7.0 * w.d_k * w.d_v * w.B * w.H * w.T
+    return {
+        "workload": "gdn_long_e4m3_64 B=8 H=16 T=4096 d_k=d_v=128 bf16 q/k/v, fp32 g/beta/state, E4M3 tile QDQ every 64 tokens",
+        "ms_per_call": t * 1e3, "updates_per_s": w.B * w.H * w.T / t,
+        "roofline": {"bound": "valu_fp32", "achieved": flops / t / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / t / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                     "flops_per_call": flops},
+    }
+
+
+def cpu_baseline(d, w, budget_s=12.0):
+    """The float64 oracle's decode step on the host cores (same generated inputs), repeated on
+    the full batch until about budget_s seconds of CPU time."""
+    import oracle
+    oracle.build()
+    args = [d[k].f64 for k in ("q", "k", "v", "g", "beta")]
+    S0 = d["S0"].f64
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.fwd(*args, S0, qdq_mode=oracle.QDQ_INT8, group=32, qdq_interval=1)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    rate = reps * w.B * w.H / el
+    return {"value": rate, "unit": "token·head updates/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} full decode steps of the B={w.B} H={w.H} d={w.d_k} batch in {el:.1f} s "
+                      "(float64 oracle, OpenMP over (sequence, head) units)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-sequence E4M3 measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over (sequence, head) with no collective; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    import quantized_state_qat_amd as la
+    la.load_library()
+
+    r = bench_decode(args.steps, args.warmup)
+    w = r["w"]
+    value = r["updates"] / r["total_s"]
+    achieved = r["bytes_per_launch"] / r["mean_launch_s"] / 1e9
+    khash = kernel_hash(["decode.hip", "la_device.hpp"])
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "token·head updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["total_s"] / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "gdn_decode_int8g32: single-token GDN decode, B=256 H=16 d_k=d_v=128, bf16 q/k/v/g/beta, "
+                        "fp32 state updated in place with INT8 group-32 QDQ (3 rotating state buffers)",
+            "B": w.B, "H": w.H, "d_k": w.d_k, "d_v": w.d_v, "qdq": "int8_group32_every_token",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": pmc_traffic("decode_int8g32_b256h16_pmc.json", khash),
+            "bytes_per_launch": r["bytes_per_launch"], "mean_launch_us": r["mean_launch_s"] * 1e6,
+            "kernel_source_hash": khash,
+        },
+    }
+    if not args.no_extra:
+        line["extra"] = {"long_sequence": bench_long_e4m3()}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(r["d"], w)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -50,6 +50,8 @@ def _load():
         path = build()
         lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
         lib.oracle_e4m3_code.restype = ctypes.c_int
@@ -73,6 +75,11 @@ def _p(a: Optional[np.ndarray]):
 
 def _d(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops over (sequence, head) units use."""
+    return int(_load().oracle_num_threads())
 
 
 def e4m3_value(code: int) -> float:

@@ -46,6 +46,19 @@
 
 #include "oracle.h"
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the parallel loops over units use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* FP8 E4M3FN value table                                                                */
 /* ------------------------------------------------------------------------------------ */

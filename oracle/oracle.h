@@ -23,6 +23,7 @@ typedef struct {
     int ckpt_interval; /* 0: no checkpoints */
 } oracle_cfg;
 
+int oracle_num_threads(void);
 double oracle_e4m3_value(int code);
 int oracle_e4m3_code(double y);
 void oracle_hadamard(int dk, int dv, const double* X, double* Y);

@@ -1,0 +1,269 @@
+// Single-token batched decode: the FP32 state is streamed HBM -> VGPR -> HBM in place.
+//
+// One workgroup per (sequence, head, 64-column value tile), 256 threads laid out as
+// 16 column quads x 16 row groups: thread (rg, cq) holds rows [rg*R, rg*R + R) of the
+// four columns 4cq..4cq+3 (R = d_k / 16), loaded as float4 so that every wave reads
+// 256-byte contiguous row segments.  Key-axis reductions are in-thread over R rows, then
+// across the 4 row groups of a wave (lane xor 16, 32), then across the 4 waves in LDS in a
+// fixed order.  INT8 groups are 4..16 consecutive quads of one row (lane xor 1..8).
+#include "la_device.hpp"
+#include "la_internal.hpp"
+
+namespace la {
+
+struct DecParams {
+    int H, dv;
+    int qkv_dt, gate_dt, out_dt;
+};
+
+template <int DK>
+struct DecSmem {
+    float k[DK], q[DK], a[DK], ak[DK];
+    float beta;
+    float4 red_u[4][16];
+    float4 red_o[4][16];
+    float amax[4];
+};
+
+__device__ __forceinline__ float4 f4_add(float4 x, float4 y) {
+    return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+}
+__device__ __forceinline__ float4 f4_shfl_xor(float4 x, int m) {
+    return make_float4(xor_shfl(x.x, m), xor_shfl(x.y, m), xor_shfl(x.z, m), xor_shfl(x.w, m));
+}
+
+// 4 consecutive elements starting at element idx (idx % 4 == 0), float32 or bfloat16.
+__device__ __forceinline__ float4 load4(const void* p, size_t idx, int dtype) {
+    if (dtype == 0) return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
+    uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + idx);
+    return make_float4(bf16_bits_to_f32(u.x & 0xFFFFu), bf16_bits_to_f32(u.x >> 16),
+                       bf16_bits_to_f32(u.y & 0xFFFFu), bf16_bits_to_f32(u.y >> 16));
+}
+
+__device__ __forceinline__ void store4(void* p, size_t idx, int dtype, float4 x) {
+    if (dtype == 0) {
+        *reinterpret_cast<float4*>(static_cast<float*>(p) + idx) = x;
+    } else {
+        uint2 u;
+        u.x = static_cast<uint32_t>(f32_to_bf16_bits(x.x)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.y)) << 16);
+        u.y = static_cast<uint32_t>(f32_to_bf16_bits(x.z)) | (static_cast<uint32_t>(f32_to_bf16_bits(x.w)) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + idx) = u;
+    }
+}
+
+__device__ __forceinline__ float& f4_at(float4& x, int i) {
+    return i == 0 ? x.x : (i == 1 ? x.y : (i == 2 ? x.z : x.w));
+}
+
+// Column sums over all rows of the workgroup (fixed order), result in every thread.
+template <int DK>
+__device__ __forceinline__ float4 colsum(float4 part, float4 (&red)[4][16], int lane, int w, int cq) {
+    part = f4_add(part, f4_shfl_xor(part, 16));
+    part = f4_add(part, f4_shfl_xor(part, 32));
+    if (lane < 16) red[w][cq] = part;
+    __syncthreads();
+    return f4_add(f4_add(f4_add(red[0][cq], red[1][cq]), red[2][cq]), red[3][cq]);
+}
+
+template <int DK, int QMODE, int G, bool HAD, bool KDA>
+__global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) {
+    constexpr int R = DK / 16;
+    __shared__ DecSmem<DK> sm;
+    __shared__ float tile[HAD ? DK * 64 : 1];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int cq = tid & 15, rg = tid >> 4;
+    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int H = p.H, DV = p.dv;
+    const size_t tok = static_cast<size_t>(b) * H + h;  // T == 1
+    const int col0 = blk * 64 + cq * 4;
+    float* Sbase = a.S + tok * DK * DV;
+
+    float4 s[R];
+#pragma unroll
+    for (int m = 0; m < R; m++)
+        s[m] = *reinterpret_cast<const float4*>(Sbase + static_cast<size_t>(rg * R + m) * DV + col0);
+
+    if (tid < DK) {
+        float kk = load_elem(a.k, tok * DK + tid, p.qkv_dt);
+        float qv = load_elem(a.q, tok * DK + tid, p.qkv_dt);
+        float gv = KDA ? load_elem(a.g, tok * DK + tid, p.gate_dt) : load_elem(a.g, tok, p.gate_dt);
+        float ai = expf(gv);
+        sm.k[tid] = kk;
+        sm.q[tid] = qv;
+        sm.a[tid] = ai;
+        sm.ak[tid] = ai * kk;
+    }
+    if (tid == 0) sm.beta = load_elem(a.beta, tok, p.gate_dt);
+    float4 vv = load4(a.v, tok * DV + col0, p.qkv_dt);
+    __syncthreads();
+
+    // u = S~^T k = sum_i a_i S_ij k_i
+    float4 pu = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int m = 0; m < R; m++) {
+        float wk = sm.ak[rg * R + m];
+        pu.x = __builtin_fmaf(s[m].x, wk, pu.x);
+        pu.y = __builtin_fmaf(s[m].y, wk, pu.y);
+        pu.z = __builtin_fmaf(s[m].z, wk, pu.z);
+        pu.w = __builtin_fmaf(s[m].w, wk, pu.w);
+    }
+    float4 u = colsum<DK>(pu, sm.red_u, lane, w, cq);
+    const float beta = sm.beta;
+    float4 dl = make_float4(beta * (vv.x - u.x), beta * (vv.y - u.y), beta * (vv.z - u.z), beta * (vv.w - u.w));
+
+    // S' = diag(a) S + k delta^T ; o = S'^T q
+    float4 po = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int m = 0; m < R; m++) {
+        const int row = rg * R + m;
+        float ar = sm.a[row], kr = sm.k[row], qr = sm.q[row];
+        s[m].x = __builtin_fmaf(kr, dl.x, ar * s[m].x);
+        s[m].y = __builtin_fmaf(kr, dl.y, ar * s[m].y);
+        s[m].z = __builtin_fmaf(kr, dl.z, ar * s[m].z);
+        s[m].w = __builtin_fmaf(kr, dl.w, ar * s[m].w);
+        po.x = __builtin_fmaf(s[m].x, qr, po.x);
+        po.y = __builtin_fmaf(s[m].y, qr, po.y);
+        po.z = __builtin_fmaf(s[m].z, qr, po.z);
+        po.w = __builtin_fmaf(s[m].w, qr, po.w);
+    }
+    float4 o = colsum<DK>(po, sm.red_o, lane, w, cq);
+    if (rg == 0) store4(a.o, tok * DV + col0, p.out_dt, o);
+
+    if (HAD) {
+        // S' -> Hu S' through LDS (key axis), quantize there, then back: S = Hu Yhat / d_k
+#pragma unroll
+        for (int m = 0; m < R; m++)
+            *reinterpret_cast<float4*>(&tile[(rg * R + m) * 64 + cq * 4]) = s[m];
+#pragma unroll 1
+        for (int hs = 1; hs < DK; hs <<= 1) {
+            __syncthreads();
+            for (int idx = tid; idx < DK * 32; idx += 256) {
+                int c = idx & 63, pp = idx >> 6;
+                int i = (pp / hs) * 2 * hs + (pp % hs);
+                float x0 = tile[i * 64 + c], x1 = tile[(i + hs) * 64 + c];
+                tile[i * 64 + c] = x0 + x1;
+                tile[(i + hs) * 64 + c] = x0 - x1;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < R; m++) s[m] = *reinterpret_cast<const float4*>(&tile[(rg * R + m) * 64 + cq * 4]);
+    }
+
+    if (QMODE == LA_QDQ_INT8_GROUP) {
+        constexpr int QPG = G / 4;  // quads per group
+#pragma unroll
+        for (int m = 0; m < R; m++) {
+            const int row = rg * R + m;
+            float mx = fmaxf(fmaxf(fabsf(s[m].x), fabsf(s[m].y)), fmaxf(fabsf(s[m].z), fabsf(s[m].w)));
+            mx = group_max<QPG>(mx);
+            float sc = int8_scale(mx);
+            float4 c = make_float4(int8_code(s[m].x, sc), int8_code(s[m].y, sc), int8_code(s[m].z, sc),
+                                   int8_code(s[m].w, sc));
+            s[m] = make_float4(c.x * sc, c.y * sc, c.z * sc, c.w * sc);
+            if (a.codes) {
+                char4 cc = make_char4(static_cast<signed char>(c.x), static_cast<signed char>(c.y),
+                                      static_cast<signed char>(c.z), static_cast<signed char>(c.w));
+                *reinterpret_cast<char4*>(static_cast<int8_t*>(a.codes) + (tok * DK + row) * DV + col0) = cc;
+            }
+            if (a.scales && (cq % QPG) == 0) a.scales[(tok * DK + row) * (DV / G) + col0 / G] = sc;
+        }
+    } else if (QMODE == LA_QDQ_E4M3_TILE) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int m = 0; m < R; m++)
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(s[m].x), fabsf(s[m].y)), fmaxf(fabsf(s[m].z), fabsf(s[m].w))));
+        mx = group_max<64>(mx);
+        if (lane == 0) sm.amax[w] = mx;
+        __syncthreads();
+        float amax = fmaxf(fmaxf(sm.amax[0], sm.amax[1]), fmaxf(sm.amax[2], sm.amax[3]));
+        float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+        for (int m = 0; m < R; m++) {
+            const int row = rg * R + m;
+            float4 y = make_float4(e4m3_round(s[m].x / sc), e4m3_round(s[m].y / sc), e4m3_round(s[m].z / sc),
+                                   e4m3_round(s[m].w / sc));
+            s[m] = make_float4(y.x * sc, y.y * sc, y.z * sc, y.w * sc);
+            if (a.codes) {
+                uchar4 cc = make_uchar4(e4m3_bits(y.x), e4m3_bits(y.y), e4m3_bits(y.z), e4m3_bits(y.w));
+                *reinterpret_cast<uchar4*>(static_cast<uint8_t*>(a.codes) + (tok * DK + row) * DV + col0) = cc;
+            }
+        }
+        if (a.scales && tid == 0) a.scales[tok * (DV / 64) + blk] = sc;
+    }
+
+    if (HAD) {
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < R; m++)
+            *reinterpret_cast<float4*>(&tile[(rg * R + m) * 64 + cq * 4]) = s[m];
+#pragma unroll 1
+        for (int hs = 1; hs < DK; hs <<= 1) {
+            __syncthreads();
+            for (int idx = tid; idx < DK * 32; idx += 256) {
+                int c = idx & 63, pp = idx >> 6;
+                int i = (pp / hs) * 2 * hs + (pp % hs);
+                float x0 = tile[i * 64 + c], x1 = tile[(i + hs) * 64 + c];
+                tile[i * 64 + c] = x0 + x1;
+                tile[(i + hs) * 64 + c] = x0 - x1;
+            }
+        }
+        __syncthreads();
+        constexpr float inv = 1.0f / DK;
+#pragma unroll
+        for (int m = 0; m < R; m++) {
+            float4 y = *reinterpret_cast<const float4*>(&tile[(rg * R + m) * 64 + cq * 4]);
+            s[m] = make_float4(y.x * inv, y.y * inv, y.z * inv, y.w * inv);
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < R; m++)
+        *reinterpret_cast<float4*>(Sbase + static_cast<size_t>(rg * R + m) * DV + col0) = s[m];
+}
+
+template <int DK, int QMODE, int G, bool HAD, bool KDA>
+static hipError_t launch_dec_t(const la_config& c, const DecodeArgs& a, hipStream_t s) {
+    DecParams p;
+    p.H = c.H; p.dv = c.d_v; p.qkv_dt = c.qkv_dtype; p.gate_dt = c.gate_dtype; p.out_dt = c.out_dtype;
+    dim3 grid(c.d_v / 64, c.H, c.B);
+    hipLaunchKernelGGL((decode_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(256), 0, s, p, a);
+    return hipGetLastError();
+}
+
+template <int DK>
+static hipError_t launch_dec_dk(const la_config& c, const DecodeArgs& a, hipStream_t s) {
+    const bool kda = c.gate == LA_GATE_KEY;
+    if (c.qdq == LA_QDQ_NONE)
+        return kda ? launch_dec_t<DK, LA_QDQ_NONE, 4, false, true>(c, a, s)
+                   : launch_dec_t<DK, LA_QDQ_NONE, 4, false, false>(c, a, s);
+    if (c.qdq == LA_QDQ_E4M3_TILE)
+        return kda ? launch_dec_t<DK, LA_QDQ_E4M3_TILE, 64, false, true>(c, a, s)
+                   : launch_dec_t<DK, LA_QDQ_E4M3_TILE, 64, false, false>(c, a, s);
+    if (c.hadamard) {
+        switch (c.group) {
+            case 16: return launch_dec_t<DK, LA_QDQ_INT8_GROUP, 16, true, false>(c, a, s);
+            case 32: return launch_dec_t<DK, LA_QDQ_INT8_GROUP, 32, true, false>(c, a, s);
+            default: return launch_dec_t<DK, LA_QDQ_INT8_GROUP, 64, true, false>(c, a, s);
+        }
+    }
+    switch (c.group) {
+        case 16: return kda ? launch_dec_t<DK, LA_QDQ_INT8_GROUP, 16, false, true>(c, a, s)
+                            : launch_dec_t<DK, LA_QDQ_INT8_GROUP, 16, false, false>(c, a, s);
+        case 32: return kda ? launch_dec_t<DK, LA_QDQ_INT8_GROUP, 32, false, true>(c, a, s)
+                            : launch_dec_t<DK, LA_QDQ_INT8_GROUP, 32, false, false>(c, a, s);
+        default: return kda ? launch_dec_t<DK, LA_QDQ_INT8_GROUP, 64, false, true>(c, a, s)
+                            : launch_dec_t<DK, LA_QDQ_INT8_GROUP, 64, false, false>(c, a, s);
+    }
+}
+
+hipError_t launch_decode(const la_config& c, const DecodeArgs& a, hipStream_t s) {
+    switch (c.d_k) {
+        case 16: return launch_dec_dk<16>(c, a, s);
+        case 32: return launch_dec_dk<32>(c, a, s);
+        case 64: return launch_dec_dk<64>(c, a, s);
+        default: return launch_dec_dk<128>(c, a, s);
+    }
+}
+
+}  // namespace la

@@ -1,0 +1,68 @@
+// Internal launch interface between the C ABI (la_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/la.h"
+
+namespace la {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* S0;
+    void* o;        // may be null (backward recompute)
+    float* ST;      // may be null
+    float* ckpts;   // may be null
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    float* S;
+    void* o;
+    void* codes;    // may be null
+    float* scales;  // may be null
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* ckpts;  // checkpoints every cfg.ckpt_interval tokens
+    const float* dout;
+    const float* dST;    // may be null
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dg;
+    float* dbeta;
+    float* dS0;
+    float* ws_states;    // per workgroup: chunk x d_k x 64 carried states
+    float* ws_vecs;      // per workgroup: chunk x 2 x 64 (u, delta)
+    float* ws_part;      // per value block partial row sums
+};
+
+// Host-side layout helpers (shared by the ABI and the launchers).
+inline int n_value_blocks(const la_config& c) { return c.d_v / 64; }
+inline int n_ckpts(const la_config& c) {
+    return c.ckpt_interval > 0 ? (c.T + c.ckpt_interval - 1) / c.ckpt_interval : 0;
+}
+inline int part_width(const la_config& c) { return 2 * c.d_k + (c.gate == LA_GATE_KEY ? c.d_k : 1) + 1; }
+
+hipError_t launch_decode(const la_config& c, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_fwd(const la_config& c, const FwdArgs& a, hipStream_t s);
+hipError_t launch_copy_state(const la_config& c, const float* src, float* dst, hipStream_t s);
+hipError_t launch_bwd(const la_config& c, const BwdArgs& a, hipStream_t s);
+
+}  // namespace la

@@ -12,9 +12,10 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
-def pytest_collection_modifyitems(config, items):
-    # GPU tests announce themselves before running so that a fault names its case.
-    pass
+def pytest_runtest_setup(item):
+    # name the case before any GPU work starts, so that a fault can be attributed
+    if item.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu case] {item.nodeid}", flush=True)
 
 
 @pytest.fixture(scope="session")

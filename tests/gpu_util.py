@@ -1,0 +1,154 @@
+"""Helpers for the GPU parity tests: device transfer of generated inputs, calls through the
+C ABI, the error metric and the quantization-code comparison protocol.
+
+Error metric: e(x, ref) = max|x - ref| / max|ref| over a whole tensor.
+Code protocol (teacher forced): at a quantization point the GPU's carried state and the
+oracle's must agree code for code; the only allowed differences are +-1 at near-ties
+(where the oracle's pre-rounding value lies within TIE_WINDOW of a rounding boundary),
+on at most 1e-4 of the codes.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+import quantized_state_qat_amd as la
+import synth
+
+TIE_WINDOW = 2e-3          # distance of x/s to a rounding boundary, in code units
+CODE_MISMATCH_MAX = 1e-4   # fraction of codes allowed to differ (by one, at near-ties)
+TOL_BF16 = 2e-3            # output/state error bound with bf16 inputs
+TOL_F32 = 1e-5             # output/state error bound with fp32 inputs
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev(t: synth.Tensor):
+    """Device tensor with the storage dtype of a generated tensor."""
+    torch = torch_mod()
+    if t.dtype == "bf16":
+        return torch.from_numpy(t.bits.astype(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t.f32)).cuda()
+
+
+def dtype_code(t: synth.Tensor) -> int:
+    return la.LA_BF16 if t.dtype == "bf16" else la.LA_F32
+
+
+def err(x, ref) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.abs(ref).max()
+    if den == 0:
+        return float(np.abs(x).max())
+    return float(np.abs(x - ref).max() / den)
+
+
+def cfg_for(w: synth.Workload, d, **kw) -> la.Config:
+    c = la.Config(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v,
+                  gate=la.LA_GATE_KEY if w.gate == "key" else la.LA_GATE_SCALAR,
+                  qkv_dtype=dtype_code(d["q"]), gate_dtype=dtype_code(d["g"]))
+    for k_, v_ in kw.items():
+        setattr(c, k_, v_)
+    return c
+
+
+def nan_like(torch, shape, dtype=None):
+    return torch.full(shape, float("nan"), dtype=dtype or torch.float32, device="cuda")
+
+
+def run_fwd(c: la.Config, d, S0=None, ckpt_interval=0, dev_inputs=None):
+    """GPU forward; returns numpy (o, S_T, ckpts or None)."""
+    torch = torch_mod()
+    c.ckpt_interval = ckpt_interval
+    di = dev_inputs or {k: dev(d[k]) for k in ("q", "k", "v", "g", "beta")}
+    S0d = None
+    if S0 is not None:
+        S0d = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).cuda()
+    o = nan_like(torch, (c.B, c.T, c.H, c.d_v), torch.float32 if c.out_dtype == la.LA_F32 else torch.bfloat16)
+    ST = nan_like(torch, (c.B, c.H, c.d_k, c.d_v))
+    ck = None
+    if ckpt_interval > 0:
+        nck = (c.T + ckpt_interval - 1) // ckpt_interval
+        ck = nan_like(torch, (c.B, c.H, nck, c.d_k, c.d_v))
+    la.la_recurrent_fwd(c, di["q"], di["k"], di["v"], di["g"], di["beta"], S0d, o, ST, ck)
+    torch.cuda.synchronize()
+    return (o.float().cpu().numpy(), ST.cpu().numpy(), None if ck is None else ck.cpu().numpy())
+
+
+def run_bwd(c: la.Config, d, dout, S0=None, dST=None, ckpts=None, dev_inputs=None):
+    torch = torch_mod()
+    di = dev_inputs or {k: dev(d[k]) for k in ("q", "k", "v", "g", "beta")}
+    f = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    gshape = (c.B, c.T, c.H, c.d_k) if c.gate == la.LA_GATE_KEY else (c.B, c.T, c.H)
+    out = {
+        "dq": nan_like(torch, (c.B, c.T, c.H, c.d_k)), "dk": nan_like(torch, (c.B, c.T, c.H, c.d_k)),
+        "dv": nan_like(torch, (c.B, c.T, c.H, c.d_v)), "dg": nan_like(torch, gshape),
+        "dbeta": nan_like(torch, (c.B, c.T, c.H)), "dS0": nan_like(torch, (c.B, c.H, c.d_k, c.d_v)),
+    }
+    nbytes = la.la_bwd_workspace_bytes(c)
+    ws = torch.full((nbytes // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    la.la_recurrent_bwd_ste(c, di["q"], di["k"], di["v"], di["g"], di["beta"], f(S0), f(ckpts), f(dout),
+                            f(dST), out["dq"], out["dk"], out["dv"], out["dg"], out["dbeta"], out["dS0"],
+                            ws, nbytes)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def int8_codes_from_state(X: np.ndarray, group: int):
+    """Recover (codes, scales) from a dequantized INT8-group state [.., d_k, d_v]: the
+    largest magnitude in a group is 127 * s (to one fp32 rounding)."""
+    X = np.asarray(X, dtype=np.float64)
+    G = X.reshape(*X.shape[:-1], X.shape[-1] // group, group)
+    amax = np.abs(G).max(axis=-1, keepdims=True)
+    s = np.where(amax > 0, amax / 127.0, 1.0)
+    c = np.rint(G / s)
+    return c.reshape(X.shape).astype(np.int32), s[..., 0]
+
+
+def e4m3_codes_from_state(X: np.ndarray, tile: int = 64):
+    """Recover E4M3 grid values (codes as values y) from a dequantized tile state [d_k, d_v]."""
+    X = np.asarray(X, dtype=np.float64)
+    dk, dv = X.shape[-2:]
+    out = np.zeros_like(X)
+    for t in range(dv // tile):
+        sl = X[..., t * tile:(t + 1) * tile]
+        amax = np.abs(sl).max()
+        s = amax / 448.0 if amax > 0 else 1.0
+        y = sl / s
+        out[..., t * tile:(t + 1) * tile] = np.vectorize(lambda z: oracle.e4m3_value(oracle.e4m3_code(z)))(y)
+    return out
+
+
+def hadamard_n(n: int) -> np.ndarray:
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H / math.sqrt(n)
+
+
+def compare_int8_codes(gpu_state, ora_codes, ora_ypre, group, hadamard=False):
+    """Teacher-forced code comparison for one INT8 quantization point.
+    gpu_state [.., d_k, d_v] is the GPU's dequantized carried state; returns the mismatch
+    fraction after asserting that every mismatch is +-1 at a near-tie."""
+    X = np.asarray(gpu_state, dtype=np.float64)
+    if hadamard:
+        Hn = hadamard_n(X.shape[-2])
+        X = np.einsum("ij,...jk->...ik", Hn, X)
+    codes, _ = int8_codes_from_state(X, group)
+    diff = codes != ora_codes
+    nmis = int(diff.sum())
+    if nmis:
+        d = np.abs(codes[diff] - ora_codes[diff])
+        assert d.max() == 1, f"code mismatch larger than one: {d.max()}"
+        y = np.asarray(ora_ypre, dtype=np.float64)[diff]
+        dist = np.abs(np.abs(y - np.floor(y)) - 0.5)
+        assert dist.max() <= TIE_WINDOW, f"mismatch away from a tie (distance {dist.max()})"
+    frac = nmis / codes.size
+    assert frac <= CODE_MISMATCH_MAX, f"code mismatch fraction {frac}"
+    return frac

@@ -1,0 +1,122 @@
+"""The C ABI library on the host (no GPU needed): it loads, exports every entry point that
+include/la.h declares, and rejects invalid calls on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_state_qat_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced: every call below is
+                # rejected (or has no work) before the library touches device memory
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "la.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:la_status|size_t|const char\*)\s+(la_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = la.load_library()
+    names = header_functions()
+    assert set(names) == {"la_recurrent_fwd", "la_decode_step", "la_recurrent_bwd_ste",
+                          "la_bwd_workspace_bytes", "la_status_string", "la_last_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert la.la_status_string(la.LA_OK) == "ok"
+    assert la.la_status_string(la.LA_ERR_UNSUPPORTED) == "unsupported configuration"
+    assert la.la_status_string(99) == "unknown status"
+
+
+def cfg(**kw):
+    base = dict(B=2, T=8, H=2, d_k=128, d_v=128, qdq=la.LA_QDQ_INT8_GROUP, group=32, ckpt_interval=4)
+    base.update(kw)
+    return la.Config(**base)
+
+
+def fwd(c, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, o=FAKE, S_T=None, ckpts=None)
+    p.update(ptrs)
+    return la.la_recurrent_fwd(c, p["q"], p["k"], p["v"], p["g"], p["beta"], p["S0"], p["o"],
+                               p["S_T"], p["ckpts"], stream=0)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d_k=96), la.LA_ERR_UNSUPPORTED, "d_k"),
+    (dict(d_k=256), la.LA_ERR_UNSUPPORTED, "d_k"),
+    (dict(d_v=96), la.LA_ERR_UNSUPPORTED, "d_v"),
+    (dict(group=8), la.LA_ERR_UNSUPPORTED, "group"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=32), la.LA_ERR_UNSUPPORTED, "E4M3"),
+    (dict(hadamard=1, gate=la.LA_GATE_KEY), la.LA_ERR_UNSUPPORTED, "Hadamard"),
+    (dict(hadamard=1, qdq=la.LA_QDQ_NONE), la.LA_ERR_INVALID_ARG, "hadamard"),
+    (dict(qdq_interval=0), la.LA_ERR_INVALID_ARG, "qdq_interval"),
+    (dict(qdq=7), la.LA_ERR_INVALID_ARG, "qdq"),
+    (dict(gate=3), la.LA_ERR_INVALID_ARG, "gate"),
+    (dict(qkv_dtype=5), la.LA_ERR_INVALID_ARG, "dtype"),
+    (dict(T=-1), la.LA_ERR_INVALID_ARG, "size"),
+    (dict(B=70000), la.LA_ERR_UNSUPPORTED, "65535"),
+])
+def test_fwd_rejects_invalid_config(kw, status, msg):
+    with pytest.raises(la.LaError) as e:
+        fwd(cfg(**kw))
+    assert e.value.status == status
+    assert msg in str(e.value)
+
+
+def test_fwd_rejects_null_and_misaligned_pointers():
+    with pytest.raises(la.LaError) as e:
+        fwd(cfg(), q=None)
+    assert e.value.status == la.LA_ERR_INVALID_ARG and "q is NULL" in str(e.value)
+    with pytest.raises(la.LaError) as e:
+        fwd(cfg(), v=FAKE + 4)
+    assert e.value.status == la.LA_ERR_ALIGNMENT and "v" in str(e.value)
+    with pytest.raises(la.LaError) as e:
+        fwd(cfg(ckpt_interval=0), ckpts=FAKE)
+    assert e.value.status == la.LA_ERR_INVALID_ARG
+
+
+def test_null_cfg():
+    lib = la.load_library()
+    assert lib.la_recurrent_fwd(None, *([None] * 10)) == la.LA_ERR_INVALID_ARG
+    assert b"cfg is NULL" in lib.la_last_error()
+    assert lib.la_bwd_workspace_bytes(None) == 0
+
+
+def test_empty_batch_is_a_no_op():
+    fwd(cfg(B=0), q=None, k=None, v=None, g=None, beta=None, o=None)
+    la.la_decode_step(cfg(T=1, H=0), None, None, None, None, None, None, None, stream=0)
+    assert la.la_last_error() == ""
+
+
+def test_decode_checks():
+    with pytest.raises(la.LaError) as e:
+        la.la_decode_step(cfg(T=2), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert "T == 1" in str(e.value)
+    with pytest.raises(la.LaError) as e:
+        la.la_decode_step(cfg(T=1, qdq=la.LA_QDQ_NONE), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          codes=FAKE, stream=0)
+    assert e.value.status == la.LA_ERR_INVALID_ARG
+
+
+def test_bwd_workspace_and_checks():
+    c = cfg(T=256, ckpt_interval=64)
+    n = la.la_bwd_workspace_bytes(c)
+    nwg = 2 * 2 * 2
+    states = nwg * 64 * 128 * 64 * 4
+    vecs = nwg * 64 * 4 * 2 * 64 * 4
+    part = 2 * 2 * 256 * 2 * (2 * 128 + 1 + 1) * 4
+    ck = 2 * 2 * 4 * 128 * 128 * 4
+    assert n >= states + vecs + part + ck and n < states + vecs + part + ck + 4 * 256
+    assert la.la_bwd_workspace_bytes(cfg(ckpt_interval=0)) == 0
+    args = [FAKE] * 5 + [None, None, FAKE, None] + [FAKE] * 6
+    with pytest.raises(la.LaError) as e:
+        la.la_recurrent_bwd_ste(c, *args, FAKE, n - 1, stream=0)
+    assert e.value.status == la.LA_ERR_WORKSPACE
+    with pytest.raises(la.LaError) as e:
+        la.la_recurrent_bwd_ste(cfg(ckpt_interval=0), *args, FAKE, n, stream=0)
+    assert "ckpt_interval" in str(e.value)

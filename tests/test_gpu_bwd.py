@@ -1,0 +1,99 @@
+"""GPU parity of la_recurrent_bwd_ste against the CPU oracle.
+
+The backward uses identity straight-through gradients through the state quantizer with
+checkpointed recompute ("GDN state/W QAT foundation" and "Fused Triton GDN/KDA decode QAT",
+both under "What does this PR do?").  With the quantizer off the gradient map is a smooth
+function of the GPU's FP32 trajectory; with it on, the gradient is the unquantized
+adjoint evaluated on the quantized trajectory.  The oracle is therefore fed the GPU's own
+carried state entering every token (forward with per-token checkpoints): teacher forcing
+of the trajectory; everything after that is float64.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_state_qat_amd as la
+import synth
+from tests import gpu_util as gu
+from tests.test_gpu_fwd import sl
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ["dq", "dk", "dv", "dg", "dbeta", "dS0"]
+
+
+def _check_against_oracle(c, d, S0, do, dST, g_gpu, tol):
+    _, ST, states = gu.run_fwd(c, d, S0=S0, ckpt_interval=1)
+    ref = oracle.bwd(d["q"].f64, d["k"].f64, d["v"].f64, d["g"].f64, d["beta"].f64,
+                     None if S0 is None else S0.astype(np.float64), do.astype(np.float64),
+                     None if dST is None else dST.astype(np.float64), states=states.astype(np.float64),
+                     gate=c.gate, qdq_mode=c.qdq, group=c.group, hadamard=bool(c.hadamard),
+                     qdq_interval=c.qdq_interval)
+    errs = {}
+    for name in GRADS:
+        assert np.all(np.isfinite(g_gpu[name])), name
+        errs[name] = gu.err(g_gpu[name], ref[name])
+    assert max(errs.values()) <= tol, errs
+    return errs
+
+
+CASES = [
+    # id, workload, qdq, group, hadamard, qdq_interval, ckpt, with dS_T
+    ("gdn_wht_int8g32_tok", synth.Workload("w", B=2, T=130, H=2, d_k=128, d_v=128, config_id=31),
+     la.LA_QDQ_INT8_GROUP, 32, 1, 1, 64, True),
+    ("kda_int8g64_tok", synth.Workload("k", B=2, T=100, H=2, d_k=128, d_v=128, gate="key", config_id=32),
+     la.LA_QDQ_INT8_GROUP, 64, 0, 1, 64, False),
+    ("gdn_e4m3_64", synth.Workload("e", B=2, T=150, H=2, d_k=128, d_v=128, gate_dtype="f32", config_id=33),
+     la.LA_QDQ_E4M3_TILE, 64, 0, 64, 64, True),
+    ("gdn_fp32_noqdq_dk64", synth.Workload("n", B=1, T=50, H=3, d_k=64, d_v=64, qkv_dtype="f32",
+                                           gate_dtype="f32", s0_sigma=0.3, config_id=34),
+     la.LA_QDQ_NONE, 32, 0, 1, 16, True),
+    ("kda_int8g16_dv192_ckpt16", synth.Workload("r", B=1, T=45, H=2, d_k=32, d_v=192, gate="key",
+                                                s0_sigma=0.1, config_id=35),
+     la.LA_QDQ_INT8_GROUP, 16, 0, 1, 16, True),
+]
+
+
+@pytest.mark.parametrize("name,w,mode,group,had,interval,ckpt,with_dst", CASES, ids=[x[0] for x in CASES])
+def test_bwd_matches_oracle(name, w, mode, group, had, interval, ckpt, with_dst):
+    d = synth.generate(w, with_do=True, with_dST=with_dst)
+    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=had, qdq_interval=interval)
+    S0 = d["S0"].f32 if w.s0_sigma > 0 else None
+    dST = d["dST"].f32 if with_dst else None
+    c.ckpt_interval = ckpt
+    g1 = gu.run_bwd(c, d, d["do"].f32, S0=S0, dST=dST)            # recomputes checkpoints
+    _, _, ck = gu.run_fwd(c, d, S0=S0, ckpt_interval=ckpt)
+    c.ckpt_interval = ckpt
+    g2 = gu.run_bwd(c, d, d["do"].f32, S0=S0, dST=dST, ckpts=ck)  # uses the forward's
+    for name_ in GRADS:
+        np.testing.assert_array_equal(g1[name_], g2[name_])
+    g3 = gu.run_bwd(c, d, d["do"].f32, S0=S0, dST=dST, ckpts=ck)
+    for name_ in GRADS:
+        np.testing.assert_array_equal(g3[name_], g2[name_])   # deterministic
+    tol = gu.TOL_F32 if w.qkv_dtype == "f32" else gu.TOL_BF16
+    errs = _check_against_oracle(c, d, S0, d["do"].f32, dST, g1, tol)
+    print(name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+def test_bwd_full_size_sampled_units():
+    """GDN + Hadamard + INT8 g32 per token, B=4 H=16 T=2048 d=128, checkpoints every 64:
+    full-size backward, then two units re-run alone (bit-identical by batch independence)
+    and compared with the oracle over all 2048 tokens on the GPU's trajectory."""
+    w = synth.WORKLOADS[4]
+    d = synth.generate(w, with_do=True)
+    c = gu.cfg_for(w, d, qdq=la.LA_QDQ_INT8_GROUP, group=32, hadamard=1, qdq_interval=1)
+    c.ckpt_interval = 64
+    g = gu.run_bwd(c, d, d["do"].f32)
+    for name in GRADS:
+        assert np.all(np.isfinite(g[name])), name
+    for (b, h) in [(0, 0), (3, 15)]:
+        dd = sl(d, b, b + 1, 0, w.T, h, h + 1)
+        dd["do"] = synth.Tensor(f32=np.ascontiguousarray(d["do"].f32[b:b + 1, :, h:h + 1]), dtype="f32")
+        cu = gu.cfg_for(w, dd, qdq=la.LA_QDQ_INT8_GROUP, group=32, hadamard=1, qdq_interval=1)
+        cu.B, cu.H, cu.ckpt_interval = 1, 1, 64
+        gu1 = gu.run_bwd(cu, dd, dd["do"].f32)
+        for name in ["dq", "dk", "dv", "dbeta", "dg"]:
+            np.testing.assert_array_equal(gu1[name][0, :, 0], g[name][b, :, h])
+        np.testing.assert_array_equal(gu1["dS0"][0, 0], g["dS0"][b, h])
+        errs = _check_against_oracle(cu, dd, None, dd["do"].f32, None, gu1, gu.TOL_BF16)
+        print(f"unit ({b},{h})", {k: f"{v:.2e}" for k, v in errs.items()})

@@ -1,0 +1,236 @@
+"""GPU parity of la_recurrent_fwd against the CPU oracle.
+
+Per-token quantization (INT8 groups, optionally around a Hadamard rotation; "Torch GDN/KDA
+decode QAT + INT8", "What does this PR do?") is checked teacher forced token by token: the
+GPU returns its carried state entering every token (checkpoint interval 1), the oracle
+advances each of those states by one token in float64 and rounds it with the FP32 codec,
+and codes, outputs and states are compared.  Interval-64 quantization (E4M3 tiles, "GDN
+state/W QAT foundation", "What does this PR do?") is teacher forced per 64-token segment
+from the GPU's checkpoints.  Full-size workloads are checked on sampled units and windows,
+and through properties that hold exactly at any size (determinism, checkpoint
+independence, batch independence, split/resume, power-of-two equivariance).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_state_qat_amd as la
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def sl(d, b0, b1, t0, t1, h0, h1):
+    """Slice generated inputs along (B, T, H)."""
+    out = {}
+    for key in ("q", "k", "v", "g", "beta"):
+        x = d[key]
+        idx = (slice(b0, b1), slice(t0, t1), slice(h0, h1))
+        out[key] = synth.Tensor(f32=np.ascontiguousarray(x.f32[idx]), dtype=x.dtype,
+                                bits=None if x.bits is None else np.ascontiguousarray(x.bits[idx]))
+    return out
+
+
+def _oracle_kw(c):
+    return dict(gate=c.gate, group=c.group, hadamard=bool(c.hadamard))
+
+
+def per_token_teacher_forced(c, d, ck, ST, o_gpu, tol):
+    """Compare every token: GPU state entering token t -> oracle one step -> GPU state after
+    token t (codes) and o_t.  Returns (max output error, max code-mismatch fraction)."""
+    T = c.T
+    worst_o, worst_code = 0.0, 0.0
+    for t in range(T):
+        S_in = ck[:, :, t].astype(np.float64)
+        S_out = ck[:, :, t + 1] if t + 1 < T else ST
+        o_t, Sp, _ = oracle.fwd(d["q"].f64[:, t:t + 1], d["k"].f64[:, t:t + 1], d["v"].f64[:, t:t + 1],
+                                d["g"].f64[:, t:t + 1], d["beta"].f64[:, t:t + 1], S_in, gate=c.gate)
+        worst_o = max(worst_o, gu.err(o_gpu[:, t], o_t[:, 0]))
+        qpoint = c.qdq != la.LA_QDQ_NONE and ((t + 1) % c.qdq_interval == 0 or t == T - 1)
+        if not qpoint:
+            assert gu.err(S_out, Sp) <= 1e-5
+            continue
+        for b in range(c.B):
+            for h in range(c.H):
+                Xh, codes, _, ypre = oracle.qdq(Sp[b, h], c.qdq, c.group, bool(c.hadamard))
+                if c.qdq == la.LA_QDQ_INT8_GROUP:
+                    frac = gu.compare_int8_codes(S_out[b, h], codes, ypre, c.group, bool(c.hadamard))
+                else:
+                    yg = gu.e4m3_codes_from_state(S_out[b, h])
+                    yo = gu.e4m3_codes_from_state(Xh)
+                    frac = float(np.mean(yg != yo))
+                    assert frac <= gu.CODE_MISMATCH_MAX
+                worst_code = max(worst_code, frac)
+    assert worst_o <= tol, worst_o
+    return worst_o, worst_code
+
+
+PER_TOKEN = [
+    # id, workload, qdq, group, hadamard
+    ("cfg0_gdn_fp32_int8g32", synth.WORKLOADS[0], la.LA_QDQ_INT8_GROUP, 32, 0),
+    ("kda_int8g64_ragged", synth.Workload("kda", B=2, T=70, H=2, d_k=128, d_v=128, gate="key", config_id=21),
+     la.LA_QDQ_INT8_GROUP, 64, 0),
+    ("gdn_wht_int8g32_ragged", synth.Workload("wht", B=2, T=70, H=2, d_k=128, d_v=128, config_id=22),
+     la.LA_QDQ_INT8_GROUP, 32, 1),
+    ("gdn_int8g16_dk32_dv128", synth.Workload("g16", B=1, T=33, H=3, d_k=32, d_v=128, config_id=23),
+     la.LA_QDQ_INT8_GROUP, 16, 0),
+    ("kda_e4m3_tok_dk64", synth.Workload("e4t", B=1, T=20, H=2, d_k=64, d_v=64, gate="key", config_id=24),
+     la.LA_QDQ_E4M3_TILE, 64, 0),
+    ("gdn_noqdq_dk16_dv192", synth.Workload("nq", B=2, T=25, H=1, d_k=16, d_v=192, config_id=25),
+     la.LA_QDQ_NONE, 32, 0),
+]
+
+
+@pytest.mark.parametrize("name,w,mode,group,had", PER_TOKEN, ids=[p[0] for p in PER_TOKEN])
+def test_per_token_teacher_forced(name, w, mode, group, had):
+    d = synth.generate(w)
+    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=had, qdq_interval=1)
+    S0 = d["S0"].f32
+    o, ST, ck = gu.run_fwd(c, d, S0=S0, ckpt_interval=1)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ST))
+    tol = gu.TOL_F32 if w.qkv_dtype == "f32" else gu.TOL_BF16
+    worst_o, worst_code = per_token_teacher_forced(c, d, ck, ST, o, tol)
+    if w.qkv_dtype == "f32":
+        assert worst_o <= 1e-5
+    print(f"{name}: max output error {worst_o:.3e}, max code mismatch {worst_code:.2e}")
+
+
+def segment_teacher_forced(c, d, ck, ST, o_gpu, units, segments, seg=64):
+    """Interval-64 quantization: from the GPU checkpoint entering each sampled segment the
+    oracle runs the segment in float64 and rounds at its end."""
+    T = c.T
+    worst_o = 0.0
+    for (b, h) in units:
+        for s_idx in segments:
+            t0, t1 = s_idx * seg, min(T, s_idx * seg + seg)
+            dd = sl(d, b, b + 1, t0, t1, h, h + 1)
+            S_in = ck[b:b + 1, h:h + 1, s_idx].astype(np.float64)
+            o_r, Sp, _ = oracle.fwd(dd["q"].f64, dd["k"].f64, dd["v"].f64, dd["g"].f64, dd["beta"].f64,
+                                    S_in, gate=c.gate)
+            worst_o = max(worst_o, gu.err(o_gpu[b, t0:t1, h], o_r[0, :, 0]))
+            S_out = ck[b, h, s_idx + 1] if t1 < T else ST[b, h]
+            Xh, codes, _, ypre = oracle.qdq(Sp[0, 0], c.qdq, c.group, False)
+            yg = gu.e4m3_codes_from_state(S_out)
+            yo = gu.e4m3_codes_from_state(Xh)
+            assert np.mean(yg != yo) <= gu.CODE_MISMATCH_MAX
+    assert worst_o <= gu.TOL_BF16, worst_o
+    return worst_o
+
+
+def test_e4m3_interval64_small_ragged():
+    w = synth.Workload("e4m3", B=2, T=200, H=3, d_k=128, d_v=128, gate_dtype="f32", config_id=26)
+    d = synth.generate(w)
+    c = gu.cfg_for(w, d, qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64)
+    o, ST, ck = gu.run_fwd(c, d, ckpt_interval=64)
+    units = [(b, h) for b in range(2) for h in range(3)]
+    worst = segment_teacher_forced(c, d, ck, ST, o, units, range(4))
+    print(f"e4m3 small: max output error {worst:.3e}")
+
+
+def test_e4m3_interval64_full_size():
+    """B=8, H=16, T=4096, d=128, bf16 q/k/v, fp32 g/beta and state, E4M3 every 64 tokens."""
+    w = synth.WORKLOADS[2]
+    d = synth.generate(w)
+    c = gu.cfg_for(w, d, qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64)
+    torch = gu.torch_mod()
+    di = {k: gu.dev(d[k]) for k in ("q", "k", "v", "g", "beta")}
+    o, ST, ck = gu.run_fwd(c, d, ckpt_interval=64, dev_inputs=di)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ST))
+    # checkpointing does not change the arithmetic; a second run is bit-identical
+    o2, ST2, _ = gu.run_fwd(c, d, ckpt_interval=0, dev_inputs=di)
+    np.testing.assert_array_equal(o2, o)
+    np.testing.assert_array_equal(ST2, ST)
+    del di
+    torch.cuda.empty_cache()
+    units = [(0, 0), (3, 7), (7, 15)]
+    worst = segment_teacher_forced(c, d, ck, ST, o, units, [0, 1, 31, 32, 63])
+    print(f"e4m3 full size: max output error {worst:.3e}")
+
+
+@pytest.mark.parametrize("cid,mode,group,had", [(3, la.LA_QDQ_INT8_GROUP, 64, 0), (4, la.LA_QDQ_INT8_GROUP, 32, 1)],
+                         ids=["kda_int8g64_full", "gdn_wht_int8g32_full"])
+def test_per_token_full_size_windows(cid, mode, group, had):
+    """Full-size per-token workloads (KDA B=4 H=32 T=2048; GDN+Hadamard B=4 H=16 T=2048):
+    one run at full size with 64-token checkpoints; then, for sampled units, the first and
+    last 64-token windows are re-run alone from the checkpoint with per-token checkpoints
+    (bit-identical to the full run by batch independence and exact resume) and teacher
+    forced token by token against the oracle."""
+    w = synth.WORKLOADS[cid]
+    d = synth.generate(w)
+    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=had, qdq_interval=1)
+    o, ST, ck = gu.run_fwd(c, d, ckpt_interval=64)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ST))
+    worst = 0.0
+    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
+        for s_idx in (0, w.T // 64 - 1):
+            t0, t1 = 64 * s_idx, 64 * s_idx + 64
+            dd = sl(d, b, b + 1, t0, t1, h, h + 1)
+            cw = gu.cfg_for(w, dd, qdq=mode, group=group, hadamard=had, qdq_interval=1)
+            cw.B, cw.T, cw.H = 1, 64, 1
+            ow, STw, ckw = gu.run_fwd(cw, dd, S0=ck[b:b + 1, h:h + 1, s_idx], ckpt_interval=1)
+            np.testing.assert_array_equal(ow[0, :, 0], o[b, t0:t1, h])
+            ref_end = ck[b, h, s_idx + 1] if t1 < w.T else ST[b, h]
+            np.testing.assert_array_equal(STw[0, 0], ref_end)
+            wo, _ = per_token_teacher_forced(cw, dd, ckw, STw, ow, gu.TOL_BF16)
+            worst = max(worst, wo)
+    print(f"config {cid}: max windowed output error {worst:.3e}")
+
+
+@pytest.mark.parametrize("mode,group,had,gate,interval", [
+    (la.LA_QDQ_INT8_GROUP, 32, 0, "scalar", 1), (la.LA_QDQ_INT8_GROUP, 64, 0, "key", 1),
+    (la.LA_QDQ_INT8_GROUP, 32, 1, "scalar", 1), (la.LA_QDQ_E4M3_TILE, 64, 0, "scalar", 64),
+    (la.LA_QDQ_INT8_GROUP, 16, 0, "scalar", 16)])
+def test_exact_properties(mode, group, had, gate, interval):
+    """Exact at any size: power-of-two scaling and negation of (v, S_0) scale o and S_T
+    exactly; units are independent; a call split at a quantization point resumes exactly;
+    repeated runs are bit-identical; T = 0 copies S_0."""
+    w = synth.Workload("prop", B=3, T=128, H=2, d_k=128, d_v=128, gate=gate, s0_sigma=0.2, config_id=27)
+    d = synth.generate(w)
+    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=had, qdq_interval=interval)
+    S0 = d["S0"].f32
+    o, ST, _ = gu.run_fwd(c, d, S0=S0)
+    o_b, ST_b, _ = gu.run_fwd(c, d, S0=S0)
+    np.testing.assert_array_equal(o, o_b)
+    np.testing.assert_array_equal(ST, ST_b)
+    d2 = dict(d)
+    d2["v"] = synth.cast(d["v"].f64 * 2.0 ** 4, "bf16")
+    o2, ST2, _ = gu.run_fwd(c, d2, S0=S0 * np.float32(2.0 ** 4))
+    np.testing.assert_array_equal(o2, o * 2.0 ** 4)
+    np.testing.assert_array_equal(ST2, ST * 2.0 ** 4)
+    d3 = dict(d)
+    d3["v"] = synth.cast(-d["v"].f64, "bf16")
+    o3, ST3, _ = gu.run_fwd(c, d3, S0=-S0)
+    np.testing.assert_array_equal(o3, -o)
+    np.testing.assert_array_equal(ST3, -ST)
+    # unit (2, 1) alone
+    d1 = sl(d, 2, 3, 0, 128, 1, 2)
+    c1 = gu.cfg_for(w, d1, qdq=mode, group=group, hadamard=had, qdq_interval=interval)
+    c1.B, c1.H = 1, 1
+    o1, ST1, _ = gu.run_fwd(c1, d1, S0=S0[2:3, 1:2])
+    np.testing.assert_array_equal(o1[0, :, 0], o[2, :, 1])
+    np.testing.assert_array_equal(ST1[0, 0], ST[2, 1])
+    # split at token 64
+    da, db = sl(d, 0, 3, 0, 64, 0, 2), sl(d, 0, 3, 64, 128, 0, 2)
+    ca = gu.cfg_for(w, da, qdq=mode, group=group, hadamard=had, qdq_interval=interval)
+    ca.T = 64
+    oa, Sa, _ = gu.run_fwd(ca, da, S0=S0)
+    ob, Sb, _ = gu.run_fwd(ca, db, S0=Sa)
+    np.testing.assert_array_equal(np.concatenate([oa, ob], axis=1), o)
+    np.testing.assert_array_equal(Sb, ST)
+    # T = 0: S_T = S_0
+    c0 = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=had, qdq_interval=interval)
+    c0.T = 0
+    _, ST0, _ = gu.run_fwd(c0, sl(d, 0, 3, 0, 0, 0, 2), S0=S0)
+    np.testing.assert_array_equal(ST0, S0)
+
+
+def test_bf16_output_is_rounded_fp32_output():
+    w = synth.Workload("bf16o", B=2, T=40, H=2, d_k=64, d_v=128, config_id=28)
+    d = synth.generate(w)
+    c = gu.cfg_for(w, d, qdq=la.LA_QDQ_INT8_GROUP, group=32)
+    o32, ST32, _ = gu.run_fwd(c, d)
+    c.out_dtype = la.LA_BF16
+    o16, ST16, _ = gu.run_fwd(c, d)
+    np.testing.assert_array_equal(ST16, ST32)
+    np.testing.assert_array_equal(o16, synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(o32.astype(np.float32))).reshape(o32.shape))
