@@ -37,7 +37,9 @@
  *   o          [B][T][H][d_v]          dtype out_dtype
  *   S0, S_T, S [B][H][d_k][d_v]        float32
  *   ckpts      [B][H][ceil(T/ckpt_interval)][d_k][d_v] float32: the carried state entering
- *              tokens 0, n, 2n, ... (n = ckpt_interval)
+ *              tokens 0, n, 2n, ... (n = ckpt_interval).  In Hadamard mode the carried state
+ *              is kept, and checkpointed, in its rotated form Y = Hu S (Hu the unnormalized
+ *              Sylvester matrix, Hu Hu = d_k I), on which the INT8 codes act; S = Hu Y / d_k.
  *   dout       [B][T][H][d_v]          float32
  *   dq, dk     [B][T][H][d_k], dv [B][T][H][d_v], dg like g, dbeta [B][T][H],
  *   dS_T, dS0  [B][H][d_k][d_v]        all float32
@@ -87,6 +89,11 @@ typedef struct la_config {
     int32_t qkv_dtype;     /* la_dtype of q, k, v */
     int32_t gate_dtype;    /* la_dtype of g, beta */
     int32_t out_dtype;     /* la_dtype of o */
+    int32_t state_rotated; /* Hadamard mode only.  0: S0, S_T, S (decode), dS_T and dS0 hold the
+                              state S.  1: they hold the rotated state Y = Hu S (and the
+                              gradients dL/dY), the representation the codes act on; chained
+                              calls then resume bit for bit and a decode step rotates only the
+                              key and query vectors, never the state. */
 } la_config;
 
 /*

@@ -31,7 +31,7 @@ class LaError(RuntimeError):
 class la_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "H", "d_k", "d_v", "gate", "qdq", "group", "hadamard", "qdq_interval",
-                 "ckpt_interval", "qkv_dtype", "gate_dtype", "out_dtype")]
+                 "ckpt_interval", "qkv_dtype", "gate_dtype", "out_dtype", "state_rotated")]
 
 
 @dataclasses.dataclass
@@ -50,6 +50,7 @@ class Config:
     qkv_dtype: int = LA_BF16
     gate_dtype: int = LA_BF16
     out_dtype: int = LA_F32
+    state_rotated: int = 0
 
     def c(self) -> la_config:
         return la_config(*[int(getattr(self, f.name)) for f in dataclasses.fields(self)])

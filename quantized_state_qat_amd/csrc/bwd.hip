@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(Params p, BwdArgs a) {
 #pragma unroll
     for (int m = 0; m < R; m++)
         lam[m] = a.dST ? a.dST[state_off + static_cast<size_t>(w * R + m) * DV + col] : 0.0f;
-    if (HAD) rotate_state<DK>(sm, lam, 1.0f / DK);
+    if (HAD && !p.rot) rotate_state<DK>(sm, lam, 1.0f / DK);  // dL/dY = Hu dL/dS / d_k
 
 #pragma unroll 1
     for (int c = p.nck - 1; c >= 0; c--) {
@@ -90,7 +90,6 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(Params p, BwdArgs a) {
         const float* ck = a.ckpts + (bh * p.nck + c) * DK * DV;
 #pragma unroll
         for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(w * R + m) * DV + col];
-        if (HAD) rotate_state<DK>(sm, s, 1.0f);
 #pragma unroll 1
         for (int t = t0; t < t1; t++) {
             float* dst = wsS + static_cast<size_t>(t - t0) * DK * kTileCols;
@@ -180,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(Params p, BwdArgs a) {
             for (int m = 0; m < R; m++) lam[m] = sm.a[w * R + m] * lam[m];
         }
     }
-    if (HAD) rotate_state<DK>(sm, lam, 1.0f);
+    if (HAD && !p.rot) rotate_state<DK>(sm, lam, 1.0f);  // dL/dS = Hu dL/dY
 #pragma unroll
     for (int m = 0; m < R; m++) a.dS0[state_off + static_cast<size_t>(w * R + m) * DV + col] = lam[m];
 }

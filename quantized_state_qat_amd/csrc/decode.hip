@@ -14,6 +14,7 @@ namespace la {
 struct DecParams {
     int H, dv;
     int qkv_dt, gate_dt, out_dt;
+    int rot;  // Hadamard mode with the state held rotated (Y = Hu S)
 };
 
 template <int DK>
@@ -96,6 +97,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
     if (tid == 0) sm.beta = load_elem(a.beta, tok, p.gate_dt);
     float4 vv = load4(a.v, tok * DV + col0, p.qkv_dt);
     __syncthreads();
+    if (HAD && p.rot) {
+        // state held as Y = Hu S: rotate the key and query instead of the state.
+        // u = S~^T k = Y~^T (Hu k) / d_k, Y' = Y~ + (Hu k) delta^T, o = Y'^T (Hu q) / d_k.
+#pragma unroll 1
+        for (int hs = 1; hs < DK; hs <<= 1) {
+            if (tid < DK) {
+                float* vec = (tid < DK / 2) ? sm.k : sm.q;
+                int pp = tid & (DK / 2 - 1);
+                int i = (pp / hs) * 2 * hs + (pp % hs);
+                float x0 = vec[i], x1 = vec[i + hs];
+                vec[i] = x0 + x1;
+                vec[i + hs] = x0 - x1;
+            }
+            __syncthreads();
+        }
+        if (tid < DK) {
+            constexpr float inv = 1.0f / DK;
+            sm.ak[tid] = sm.a[tid] * (sm.k[tid] * inv);
+            sm.q[tid] = sm.q[tid] * inv;
+        }
+        __syncthreads();
+    }
 
     // u = S~^T k = sum_i a_i S_ij k_i
     float4 pu = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -129,7 +152,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
     float4 o = colsum<DK>(po, sm.red_o, lane, w, cq);
     if (rg == 0) store4(a.o, tok * DV + col0, p.out_dt, o);
 
-    if (HAD) {
+    if (HAD && !p.rot) {
         // S' -> Hu S' through LDS (key axis), quantize there, then back: S = Hu Yhat / d_k
 #pragma unroll
         for (int m = 0; m < R; m++)
@@ -192,7 +215,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
         if (a.scales && tid == 0) a.scales[tok * (DV / 64) + blk] = sc;
     }
 
-    if (HAD) {
+    if (HAD && !p.rot) {
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < R; m++)
@@ -226,6 +249,7 @@ template <int DK, int QMODE, int G, bool HAD, bool KDA>
 static hipError_t launch_dec_t(const la_config& c, const DecodeArgs& a, hipStream_t s) {
     DecParams p;
     p.H = c.H; p.dv = c.d_v; p.qkv_dt = c.qkv_dtype; p.gate_dt = c.gate_dtype; p.out_dt = c.out_dtype;
+    p.rot = c.hadamard && c.state_rotated;
     dim3 grid(c.d_v / 64, c.H, c.B);
     hipLaunchKernelGGL((decode_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(256), 0, s, p, a);
     return hipGetLastError();

@@ -19,23 +19,16 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(Params p, FwdArgs a) {
 #pragma unroll
     for (int m = 0; m < R; m++)
         s[m] = a.S0 ? a.S0[state_off + static_cast<size_t>(w * R + m) * DV + col] : 0.0f;
-    if (HAD) rotate_state<DK>(sm, s, 1.0f);
+    if (HAD && !p.rot) rotate_state<DK>(sm, s, 1.0f);
 
 #pragma unroll 1
     for (int t = 0; t < T; t++) {
         if (a.ckpts && (t % p.ckpt_interval) == 0) {
+            // Hadamard mode stores the carried state in its rotated form Hu S (exactly what
+            // the token loop carries), so a recompute resumes bit for bit.
             float* dst = a.ckpts + (bh * p.nck + t / p.ckpt_interval) * DK * DV;
-            if (HAD) {
-                float tmp[R];
 #pragma unroll
-                for (int m = 0; m < R; m++) tmp[m] = s[m];
-                rotate_state<DK>(sm, tmp, 1.0f / DK);
-#pragma unroll
-                for (int m = 0; m < R; m++) dst[static_cast<size_t>(w * R + m) * DV + col] = tmp[m];
-            } else {
-#pragma unroll
-                for (int m = 0; m < R; m++) dst[static_cast<size_t>(w * R + m) * DV + col] = s[m];
-            }
+            for (int m = 0; m < R; m++) dst[static_cast<size_t>(w * R + m) * DV + col] = s[m];
         }
         const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
         float vj = load_elem(a.v, tok * DV + col, p.qkv_dt);
@@ -46,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(Params p, FwdArgs a) {
         if (a.o && w == 0) store_elem(a.o, tok * DV + col, p.out_dt, o);
     }
     if (a.ST) {
-        if (HAD) rotate_state<DK>(sm, s, 1.0f / DK);
+        if (HAD && !p.rot) rotate_state<DK>(sm, s, 1.0f / DK);
 #pragma unroll
         for (int m = 0; m < R; m++) a.ST[state_off + static_cast<size_t>(w * R + m) * DV + col] = s[m];
     }
@@ -64,6 +57,7 @@ Params make_params(const la_config& c) {
     p.qdq_interval = c.qdq == LA_QDQ_NONE ? 1 : c.qdq_interval;
     p.ckpt_interval = c.ckpt_interval > 0 ? c.ckpt_interval : 1;
     p.nck = n_ckpts(c);
+    p.rot = c.hadamard && c.state_rotated;
     return p;
 }
 

@@ -45,6 +45,10 @@ la_status check_config(const la_config* c, bool decode) {
         if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_INVALID_ARG, "unknown dtype %d", dt);
     if (c->ckpt_interval < 0) return fail(LA_ERR_INVALID_ARG, "ckpt_interval < 0");
     if (c->hadamard != 0 && c->hadamard != 1) return fail(LA_ERR_INVALID_ARG, "hadamard must be 0 or 1");
+    if (c->state_rotated != 0 && c->state_rotated != 1)
+        return fail(LA_ERR_INVALID_ARG, "state_rotated must be 0 or 1");
+    if (c->state_rotated && !c->hadamard)
+        return fail(LA_ERR_INVALID_ARG, "state_rotated needs the Hadamard rotation");
     switch (c->qdq) {
         case LA_QDQ_NONE:
             if (c->hadamard) return fail(LA_ERR_INVALID_ARG, "hadamard needs the INT8 quantizer");

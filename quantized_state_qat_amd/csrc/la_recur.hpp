@@ -31,6 +31,7 @@ struct Params {
     int B, T, H, dk, dv;
     int qkv_dt, gate_dt, out_dt;
     int qdq_interval, ckpt_interval, nck;
+    int rot;  // state tensors hold the rotated state (Hadamard mode)
 };
 
 template <int DK>

@@ -60,6 +60,8 @@ def fwd(c, **ptrs):
     (dict(qkv_dtype=5), la.LA_ERR_INVALID_ARG, "dtype"),
     (dict(T=-1), la.LA_ERR_INVALID_ARG, "size"),
     (dict(B=70000), la.LA_ERR_UNSUPPORTED, "65535"),
+    (dict(state_rotated=1), la.LA_ERR_INVALID_ARG, "state_rotated"),
+    (dict(state_rotated=2, hadamard=1), la.LA_ERR_INVALID_ARG, "state_rotated"),
 ])
 def test_fwd_rejects_invalid_config(kw, status, msg):
     with pytest.raises(la.LaError) as e:

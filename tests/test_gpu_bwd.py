@@ -23,16 +23,27 @@ GRADS = ["dq", "dk", "dv", "dg", "dbeta", "dS0"]
 
 
 def _check_against_oracle(c, d, S0, do, dST, g_gpu, tol):
+    """S0 and dST are given in the representation the call used (rotated when
+    c.state_rotated); the oracle works on the unrotated state."""
+    had, rot = bool(c.hadamard), bool(c.state_rotated)
     _, ST, states = gu.run_fwd(c, d, S0=S0, ckpt_interval=1)
+    states = gu.rotated_to_state(states) if had else states.astype(np.float64)
+    S0_phys = None if S0 is None else (gu.rotated_to_state(S0) if rot else S0.astype(np.float64))
+    dST_phys = None
+    if dST is not None:
+        # dL/dS = Hu dL/dY for a state held rotated
+        dST_phys = gu.rotated_to_state(dST) * c.d_k if rot else dST.astype(np.float64)
     ref = oracle.bwd(d["q"].f64, d["k"].f64, d["v"].f64, d["g"].f64, d["beta"].f64,
-                     None if S0 is None else S0.astype(np.float64), do.astype(np.float64),
-                     None if dST is None else dST.astype(np.float64), states=states.astype(np.float64),
-                     gate=c.gate, qdq_mode=c.qdq, group=c.group, hadamard=bool(c.hadamard),
+                     S0_phys, do.astype(np.float64), dST_phys, states=states,
+                     gate=c.gate, qdq_mode=c.qdq, group=c.group, hadamard=had,
                      qdq_interval=c.qdq_interval)
+    g_cmp = dict(g_gpu)
+    if rot:
+        g_cmp["dS0"] = gu.rotated_to_state(g_gpu["dS0"]) * c.d_k
     errs = {}
     for name in GRADS:
         assert np.all(np.isfinite(g_gpu[name])), name
-        errs[name] = gu.err(g_gpu[name], ref[name])
+        errs[name] = gu.err(g_cmp[name], ref[name])
     assert max(errs.values()) <= tol, errs
     return errs
 
@@ -41,6 +52,9 @@ CASES = [
     # id, workload, qdq, group, hadamard, qdq_interval, ckpt, with dS_T
     ("gdn_wht_int8g32_tok", synth.Workload("w", B=2, T=130, H=2, d_k=128, d_v=128, config_id=31),
      la.LA_QDQ_INT8_GROUP, 32, 1, 1, 64, True),
+    ("gdn_wht_int8g32_rotated_state", synth.Workload("wr", B=1, T=70, H=2, d_k=64, d_v=128, s0_sigma=0.2,
+                                                     config_id=36),
+     la.LA_QDQ_INT8_GROUP, 32, 2, 1, 32, True),
     ("kda_int8g64_tok", synth.Workload("k", B=2, T=100, H=2, d_k=128, d_v=128, gate="key", config_id=32),
      la.LA_QDQ_INT8_GROUP, 64, 0, 1, 64, False),
     ("gdn_e4m3_64", synth.Workload("e", B=2, T=150, H=2, d_k=128, d_v=128, gate_dtype="f32", config_id=33),
@@ -57,7 +71,9 @@ CASES = [
 @pytest.mark.parametrize("name,w,mode,group,had,interval,ckpt,with_dst", CASES, ids=[x[0] for x in CASES])
 def test_bwd_matches_oracle(name, w, mode, group, had, interval, ckpt, with_dst):
     d = synth.generate(w, with_do=True, with_dST=with_dst)
-    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=had, qdq_interval=interval)
+    # had == 2: Hadamard with the state tensors held rotated
+    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=int(had > 0), qdq_interval=interval,
+                   state_rotated=int(had == 2))
     S0 = d["S0"].f32 if w.s0_sigma > 0 else None
     dST = d["dST"].f32 if with_dst else None
     c.ckpt_interval = ckpt

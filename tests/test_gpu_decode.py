@@ -34,10 +34,12 @@ def _run_decode(c, d, S_init, want_codes=True):
             None if codes is None else codes.cpu().numpy(), None if scales is None else scales.cpu().numpy())
 
 
-def _oracle_step(d, S_init, gate, mode, group, had):
-    """o and S' (float64) of one token, then the codec per unit."""
+def _oracle_step(d, S_init, gate, mode, group, had, rot=False):
+    """o and S' (float64) of one token, then the codec per unit.  rot: S_init holds the
+    rotated state Hu S."""
+    S_phys = gu.rotated_to_state(S_init) if rot else S_init.astype(np.float64)
     o, Sp, _ = oracle.fwd(d["q"].f64, d["k"].f64, d["v"].f64, d["g"].f64, d["beta"].f64,
-                          S_init.astype(np.float64), gate=gate)
+                          S_phys, gate=gate)
     B, H = Sp.shape[:2]
     Xh = np.zeros_like(Sp)
     codes = np.zeros(Sp.shape, dtype=np.int32)
@@ -60,6 +62,7 @@ CASES = [
     ("int8g64_kda", 2, 2, 128, 128, "key", la.LA_QDQ_INT8_GROUP, 64, 0),
     ("e4m3", 2, 3, 128, 128, "scalar", la.LA_QDQ_E4M3_TILE, 64, 0),
     ("wht_int8g32", 2, 2, 128, 128, "scalar", la.LA_QDQ_INT8_GROUP, 32, 1),
+    ("wht_int8g16_rotated_state", 2, 3, 128, 128, "scalar", la.LA_QDQ_INT8_GROUP, 16, 2),
     ("none_dk32", 2, 2, 32, 64, "scalar", la.LA_QDQ_NONE, 32, 0),
     ("int8g32_dk16", 1, 3, 16, 64, "scalar", la.LA_QDQ_INT8_GROUP, 32, 0),
 ]
@@ -69,20 +72,23 @@ CASES = [
 def test_decode_matches_oracle(name, B, H, dk, dv, gate, mode, group, had):
     w = synth.Workload(name, B=B, T=1, H=H, d_k=dk, d_v=dv, gate=gate, s0_sigma=0.05, config_id=11)
     d = synth.generate(w)
-    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=had)
+    rot = had == 2  # Hadamard with the state held rotated (Y = Hu S in and out)
+    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=int(had > 0), state_rotated=int(rot))
     S_init = d["S0"].f32
     S, o, codes, scales = _run_decode(c, d, S_init)
-    o_r, Sp, Xh, codes_r, ypre, scales_r = _oracle_step(d, S_init, c.gate, mode, group, bool(had))
+    o_r, Sp, Xh, codes_r, ypre, scales_r = _oracle_step(d, S_init, c.gate, mode, group, had > 0, rot)
+    if rot:
+        S = gu.rotated_to_state(S)  # compare states unrotated
     assert gu.err(o, o_r) <= gu.TOL_BF16
     assert gu.err(o, o_r) <= 1e-5  # same inputs, one token: fp32 rounding only
     if mode == la.LA_QDQ_NONE:
         assert gu.err(S, Sp) <= 1e-6
         return
     if mode == la.LA_QDQ_INT8_GROUP:
-        frac = gu.compare_int8_codes(S, codes_r, ypre, group, hadamard=bool(had))
+        frac = gu.compare_int8_codes(S, codes_r, ypre, group, hadamard=had > 0)
         mism = codes.astype(np.int32) != codes_r
         assert mism.mean() <= gu.CODE_MISMATCH_MAX and mism.mean() == pytest.approx(frac, abs=1e-12)
-        if not had:
+        if had == 0:
             # where every code of a group agrees, the scale and the dequantized state agree to an ulp
             sc = scales.reshape(-1)
             np.testing.assert_allclose(sc, scales_r.reshape(-1), rtol=2 ** -22)
