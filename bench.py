@@ -162,6 +162,18 @@ def cpu_baseline(d, w, budget_s=12.0):
                       "(float64 oracle, OpenMP over (sequence, head) units)"}
 
 
+def profile_mode(steps):
+    import torch
+    r = bench_decode(steps, 1)
+    src = torch.empty(268435456 // 4, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"profile mode: {steps} decode launches (mean {r['mean_launch_s'] * 1e6:.1f} us), "
+          f"2 copies of {src.numel() * 4} bytes", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +181,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the long-sequence E4M3 measurement")
+    ap.add_argument("--profile", action="store_true",
+                    help="counter-collection mode: a few decode launches and one plain copy of a "
+                         "256 MiB state buffer (the calibration kernel for HBM byte counters); no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -180,6 +195,10 @@ def main():
     torch.cuda.set_device(0)
     import quantized_state_qat_amd as la
     la.load_library()
+
+    if args.profile:
+        profile_mode(min(args.steps, 5))
+        return
 
     r = bench_decode(args.steps, args.warmup)
     w = r["w"]

@@ -1,11 +1,14 @@
 // Single-token batched decode: the FP32 state is streamed HBM -> VGPR -> HBM in place.
 //
 // One workgroup per (sequence, head, 64-column value tile), 256 threads laid out as
-// 16 column quads x 16 row groups: thread (rg, cq) holds rows [rg*R, rg*R + R) of the
-// four columns 4cq..4cq+3 (R = d_k / 16), loaded as float4 so that every wave reads
-// 256-byte contiguous row segments.  Key-axis reductions are in-thread over R rows, then
-// across the 4 row groups of a wave (lane xor 16, 32), then across the 4 waves in LDS in a
-// fixed order.  INT8 groups are 4..16 consecutive quads of one row (lane xor 1..8).
+// 16 column quads x 16 row groups: thread (rg, cq) holds rows [rg*R, rg*R + R) of the four
+// columns 4cq..4cq+3 (R = d_k / 16), loaded as float4 so that every wave reads 256-byte
+// contiguous row segments.  One pass over the state produces both key-axis reductions the
+// token needs, u = S~^T k and r = S~^T q, because the output read before rounding is
+//     o = S'^T q = S~^T q + delta (k . q),
+// so a single reduction round (in-thread over R rows, across the 4 row groups of a wave
+// with permlane swaps, across the 4 waves through LDS in a fixed order) precedes the update.
+// INT8 groups are 4..16 consecutive quads of one row (DPP within a row of 16 lanes).
 #include "la_device.hpp"
 #include "la_internal.hpp"
 
@@ -19,19 +22,12 @@ struct DecParams {
 
 template <int DK>
 struct DecSmem {
-    float k[DK], q[DK], a[DK], ak[DK];
-    float beta;
-    float4 red_u[4][16];
-    float4 red_o[4][16];
+    float k[DK], a[DK], ak[DK], aq[DK];
+    float q[DK];
+    float beta, kqp[2];
+    float4 red[4][16][2];
     float amax[4];
 };
-
-__device__ __forceinline__ float4 f4_add(float4 x, float4 y) {
-    return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
-}
-__device__ __forceinline__ float4 f4_shfl_xor(float4 x, int m) {
-    return make_float4(xor_shfl(x.x, m), xor_shfl(x.y, m), xor_shfl(x.z, m), xor_shfl(x.w, m));
-}
 
 // 4 consecutive elements starting at element idx (idx % 4 == 0), float32 or bfloat16.
 __device__ __forceinline__ float4 load4(const void* p, size_t idx, int dtype) {
@@ -52,21 +48,35 @@ __device__ __forceinline__ void store4(void* p, size_t idx, int dtype, float4 x)
     }
 }
 
-__device__ __forceinline__ float& f4_at(float4& x, int i) {
-    return i == 0 ? x.x : (i == 1 ? x.y : (i == 2 ? x.z : x.w));
+__device__ __forceinline__ float4 rows_sum4(float4 x) {
+    return make_float4(rows_sum(x.x), rows_sum(x.y), rows_sum(x.z), rows_sum(x.w));
+}
+__device__ __forceinline__ float4 add4(float4 x, float4 y) {
+    return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+}
+__device__ __forceinline__ float max4abs(float4 x) {
+    return fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
 }
 
-// Column sums over all rows of the workgroup (fixed order), result in every thread.
+// In-LDS unnormalized Walsh-Hadamard transform over the key axis of a DK x 64 tile
+// (all threads call).
 template <int DK>
-__device__ __forceinline__ float4 colsum(float4 part, float4 (&red)[4][16], int lane, int w, int cq) {
-    part = f4_add(part, f4_shfl_xor(part, 16));
-    part = f4_add(part, f4_shfl_xor(part, 32));
-    if (lane < 16) red[w][cq] = part;
+__device__ __forceinline__ void dec_tile_wht(float* tile) {
+#pragma unroll 1
+    for (int hs = 1; hs < DK; hs <<= 1) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < DK * 32; idx += 256) {
+            int c = idx & 63, pp = idx >> 6;
+            int i = (pp / hs) * 2 * hs + (pp % hs);
+            float x0 = tile[i * 64 + c], x1 = tile[(i + hs) * 64 + c];
+            tile[i * 64 + c] = x0 + x1;
+            tile[(i + hs) * 64 + c] = x0 - x1;
+        }
+    }
     __syncthreads();
-    return f4_add(f4_add(f4_add(red[0][cq], red[1][cq]), red[2][cq]), red[3][cq]);
 }
 
-template <int DK, int QMODE, int G, bool HAD, bool KDA>
+template <int DK, int QMODE, int G, bool HAD, bool KDA, bool CODES>
 __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) {
     constexpr int R = DK / 16;
     __shared__ DecSmem<DK> sm;
@@ -77,31 +87,37 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
     const int H = p.H, DV = p.dv;
     const size_t tok = static_cast<size_t>(b) * H + h;  // T == 1
     const int col0 = blk * 64 + cq * 4;
-    float* Sbase = a.S + tok * DK * DV;
+    float* Srow = a.S + (tok * DK + static_cast<size_t>(rg) * R) * DV + col0;
 
+    // token vectors first, so that waiting for them does not wait for the state
+    float kk = 0.f, qv = 0.f, ai = 0.f;
+    if (tid < DK) {
+        kk = load_elem(a.k, tok * DK + tid, p.qkv_dt);
+        qv = load_elem(a.q, tok * DK + tid, p.qkv_dt);
+        float gv = KDA ? load_elem(a.g, tok * DK + tid, p.gate_dt) : load_elem(a.g, tok, p.gate_dt);
+        ai = expf(gv);
+    }
+    const float beta = load_elem(a.beta, tok, p.gate_dt);
+    const float4 vv = load4(a.v, tok * DV + col0, p.qkv_dt);
     float4 s[R];
 #pragma unroll
-    for (int m = 0; m < R; m++)
-        s[m] = *reinterpret_cast<const float4*>(Sbase + static_cast<size_t>(rg * R + m) * DV + col0);
+    for (int m = 0; m < R; m++) s[m] = *reinterpret_cast<const float4*>(Srow + static_cast<size_t>(m) * DV);
 
     if (tid < DK) {
-        float kk = load_elem(a.k, tok * DK + tid, p.qkv_dt);
-        float qv = load_elem(a.q, tok * DK + tid, p.qkv_dt);
-        float gv = KDA ? load_elem(a.g, tok * DK + tid, p.gate_dt) : load_elem(a.g, tok, p.gate_dt);
-        float ai = expf(gv);
         sm.k[tid] = kk;
         sm.q[tid] = qv;
         sm.a[tid] = ai;
-        sm.ak[tid] = ai * kk;
     }
-    if (tid == 0) sm.beta = load_elem(a.beta, tok, p.gate_dt);
-    float4 vv = load4(a.v, tok * DV + col0, p.qkv_dt);
-    __syncthreads();
+    if (w < 2) {  // k . q: one partial per 64 keys, fixed butterfly order
+        float kqp = wave_sum(tid < DK ? kk * qv : 0.0f);
+        if (lane == 0) sm.kqp[w] = kqp;
+    }
     if (HAD && p.rot) {
         // state held as Y = Hu S: rotate the key and query instead of the state.
-        // u = S~^T k = Y~^T (Hu k) / d_k, Y' = Y~ + (Hu k) delta^T, o = Y'^T (Hu q) / d_k.
+        // u = Y~^T (Hu k) / d_k, Y' = Y~ + (Hu k) delta^T, o = Y~^T (Hu q) / d_k + delta (k . q).
 #pragma unroll 1
         for (int hs = 1; hs < DK; hs <<= 1) {
+            __syncthreads();
             if (tid < DK) {
                 float* vec = (tid < DK / 2) ? sm.k : sm.q;
                 int pp = tid & (DK / 2 - 1);
@@ -110,65 +126,66 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
                 vec[i] = x0 + x1;
                 vec[i + hs] = x0 - x1;
             }
-            __syncthreads();
         }
+        __syncthreads();
         if (tid < DK) {
             constexpr float inv = 1.0f / DK;
             sm.ak[tid] = sm.a[tid] * (sm.k[tid] * inv);
-            sm.q[tid] = sm.q[tid] * inv;
+            sm.aq[tid] = sm.a[tid] * (sm.q[tid] * inv);
         }
-        __syncthreads();
+    } else if (tid < DK) {
+        sm.ak[tid] = ai * kk;
+        sm.aq[tid] = ai * qv;
     }
+    __syncthreads();
 
-    // u = S~^T k = sum_i a_i S_ij k_i
-    float4 pu = make_float4(0.f, 0.f, 0.f, 0.f);
+    // one pass: u = S~^T k and r = S~^T q (partial over this thread's rows)
+    float4 pu = make_float4(0.f, 0.f, 0.f, 0.f), pr = pu;
 #pragma unroll
     for (int m = 0; m < R; m++) {
-        float wk = sm.ak[rg * R + m];
+        const float wk = sm.ak[rg * R + m], wq = sm.aq[rg * R + m];
         pu.x = __builtin_fmaf(s[m].x, wk, pu.x);
         pu.y = __builtin_fmaf(s[m].y, wk, pu.y);
         pu.z = __builtin_fmaf(s[m].z, wk, pu.z);
         pu.w = __builtin_fmaf(s[m].w, wk, pu.w);
+        pr.x = __builtin_fmaf(s[m].x, wq, pr.x);
+        pr.y = __builtin_fmaf(s[m].y, wq, pr.y);
+        pr.z = __builtin_fmaf(s[m].z, wq, pr.z);
+        pr.w = __builtin_fmaf(s[m].w, wq, pr.w);
     }
-    float4 u = colsum<DK>(pu, sm.red_u, lane, w, cq);
-    const float beta = sm.beta;
-    float4 dl = make_float4(beta * (vv.x - u.x), beta * (vv.y - u.y), beta * (vv.z - u.z), beta * (vv.w - u.w));
+    pu = rows_sum4(pu);
+    pr = rows_sum4(pr);
+    if (lane < 16) {
+        sm.red[w][cq][0] = pu;
+        sm.red[w][cq][1] = pr;
+    }
+    __syncthreads();
+    const float4 u = add4(add4(add4(sm.red[0][cq][0], sm.red[1][cq][0]), sm.red[2][cq][0]), sm.red[3][cq][0]);
+    const float4 r = add4(add4(add4(sm.red[0][cq][1], sm.red[1][cq][1]), sm.red[2][cq][1]), sm.red[3][cq][1]);
+    const float kq = sm.kqp[0] + sm.kqp[1];
+    const float4 dl = make_float4(beta * (vv.x - u.x), beta * (vv.y - u.y), beta * (vv.z - u.z), beta * (vv.w - u.w));
+    if (rg == 0) {
+        const float4 o = make_float4(__builtin_fmaf(dl.x, kq, r.x), __builtin_fmaf(dl.y, kq, r.y),
+                                     __builtin_fmaf(dl.z, kq, r.z), __builtin_fmaf(dl.w, kq, r.w));
+        store4(a.o, tok * DV + col0, p.out_dt, o);
+    }
 
-    // S' = diag(a) S + k delta^T ; o = S'^T q
-    float4 po = make_float4(0.f, 0.f, 0.f, 0.f);
+    // S' = diag(a) S + k delta^T
 #pragma unroll
     for (int m = 0; m < R; m++) {
         const int row = rg * R + m;
-        float ar = sm.a[row], kr = sm.k[row], qr = sm.q[row];
+        const float ar = sm.a[row], kr = sm.k[row];
         s[m].x = __builtin_fmaf(kr, dl.x, ar * s[m].x);
         s[m].y = __builtin_fmaf(kr, dl.y, ar * s[m].y);
         s[m].z = __builtin_fmaf(kr, dl.z, ar * s[m].z);
         s[m].w = __builtin_fmaf(kr, dl.w, ar * s[m].w);
-        po.x = __builtin_fmaf(s[m].x, qr, po.x);
-        po.y = __builtin_fmaf(s[m].y, qr, po.y);
-        po.z = __builtin_fmaf(s[m].z, qr, po.z);
-        po.w = __builtin_fmaf(s[m].w, qr, po.w);
     }
-    float4 o = colsum<DK>(po, sm.red_o, lane, w, cq);
-    if (rg == 0) store4(a.o, tok * DV + col0, p.out_dt, o);
 
     if (HAD && !p.rot) {
-        // S' -> Hu S' through LDS (key axis), quantize there, then back: S = Hu Yhat / d_k
+        // S' -> Hu S' through LDS (key axis); quantize there; S = Hu Yhat / d_k afterwards
 #pragma unroll
-        for (int m = 0; m < R; m++)
-            *reinterpret_cast<float4*>(&tile[(rg * R + m) * 64 + cq * 4]) = s[m];
-#pragma unroll 1
-        for (int hs = 1; hs < DK; hs <<= 1) {
-            __syncthreads();
-            for (int idx = tid; idx < DK * 32; idx += 256) {
-                int c = idx & 63, pp = idx >> 6;
-                int i = (pp / hs) * 2 * hs + (pp % hs);
-                float x0 = tile[i * 64 + c], x1 = tile[(i + hs) * 64 + c];
-                tile[i * 64 + c] = x0 + x1;
-                tile[(i + hs) * 64 + c] = x0 - x1;
-            }
-        }
-        __syncthreads();
+        for (int m = 0; m < R; m++) *reinterpret_cast<float4*>(&tile[(rg * R + m) * 64 + cq * 4]) = s[m];
+        dec_tile_wht<DK>(tile);
 #pragma unroll
         for (int m = 0; m < R; m++) s[m] = *reinterpret_cast<const float4*>(&tile[(rg * R + m) * 64 + cq * 4]);
     }
@@ -177,61 +194,64 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
         constexpr int QPG = G / 4;  // quads per group
 #pragma unroll
         for (int m = 0; m < R; m++) {
-            const int row = rg * R + m;
-            float mx = fmaxf(fmaxf(fabsf(s[m].x), fabsf(s[m].y)), fmaxf(fabsf(s[m].z), fabsf(s[m].w)));
-            mx = group_max<QPG>(mx);
-            float sc = int8_scale(mx);
-            float4 c = make_float4(int8_code(s[m].x, sc), int8_code(s[m].y, sc), int8_code(s[m].z, sc),
-                                   int8_code(s[m].w, sc));
-            s[m] = make_float4(c.x * sc, c.y * sc, c.z * sc, c.w * sc);
-            if (a.codes) {
-                char4 cc = make_char4(static_cast<signed char>(c.x), static_cast<signed char>(c.y),
-                                      static_cast<signed char>(c.z), static_cast<signed char>(c.w));
-                *reinterpret_cast<char4*>(static_cast<int8_t*>(a.codes) + (tok * DK + row) * DV + col0) = cc;
+            const float mx = group_max<QPG>(max4abs(s[m]));
+            const float sc = int8_scale(mx);
+            float4 c;
+            if (sc >= kFastQuotMinScale) {
+                const float y = 1.0f / sc;
+                c = make_float4(int8_code_y(s[m].x, sc, y), int8_code_y(s[m].y, sc, y),
+                                int8_code_y(s[m].z, sc, y), int8_code_y(s[m].w, sc, y));
+            } else {
+                c = make_float4(int8_code(s[m].x, sc), int8_code(s[m].y, sc), int8_code(s[m].z, sc),
+                                int8_code(s[m].w, sc));
             }
-            if (a.scales && (cq % QPG) == 0) a.scales[(tok * DK + row) * (DV / G) + col0 / G] = sc;
+            s[m] = make_float4(c.x * sc, c.y * sc, c.z * sc, c.w * sc);
+            if (CODES) {
+                const int row = rg * R + m;
+                if (a.codes) {
+                    char4 cc = make_char4(static_cast<signed char>(c.x), static_cast<signed char>(c.y),
+                                          static_cast<signed char>(c.z), static_cast<signed char>(c.w));
+                    *reinterpret_cast<char4*>(static_cast<int8_t*>(a.codes) + (tok * DK + row) * DV + col0) = cc;
+                }
+                if (a.scales && (cq % QPG) == 0) a.scales[(tok * DK + row) * (DV / G) + col0 / G] = sc;
+            }
         }
     } else if (QMODE == LA_QDQ_E4M3_TILE) {
         float mx = 0.0f;
 #pragma unroll
-        for (int m = 0; m < R; m++)
-            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(s[m].x), fabsf(s[m].y)), fmaxf(fabsf(s[m].z), fabsf(s[m].w))));
+        for (int m = 0; m < R; m++) mx = fmaxf(mx, max4abs(s[m]));
         mx = group_max<64>(mx);
         if (lane == 0) sm.amax[w] = mx;
         __syncthreads();
-        float amax = fmaxf(fmaxf(sm.amax[0], sm.amax[1]), fmaxf(sm.amax[2], sm.amax[3]));
-        float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        const float amax = fmaxf(fmaxf(sm.amax[0], sm.amax[1]), fmaxf(sm.amax[2], sm.amax[3]));
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        const bool fast = sc >= kFastQuotMinScaleE4M3;
+        const float y = 1.0f / sc;
 #pragma unroll
         for (int m = 0; m < R; m++) {
-            const int row = rg * R + m;
-            float4 y = make_float4(e4m3_round(s[m].x / sc), e4m3_round(s[m].y / sc), e4m3_round(s[m].z / sc),
-                                   e4m3_round(s[m].w / sc));
-            s[m] = make_float4(y.x * sc, y.y * sc, y.z * sc, y.w * sc);
-            if (a.codes) {
-                uchar4 cc = make_uchar4(e4m3_bits(y.x), e4m3_bits(y.y), e4m3_bits(y.z), e4m3_bits(y.w));
+            float4 e;
+            if (fast) {
+                e = make_float4(e4m3_round(quot_rn(s[m].x, sc, y)), e4m3_round(quot_rn(s[m].y, sc, y)),
+                                e4m3_round(quot_rn(s[m].z, sc, y)), e4m3_round(quot_rn(s[m].w, sc, y)));
+            } else {
+                e = make_float4(e4m3_round(s[m].x / sc), e4m3_round(s[m].y / sc), e4m3_round(s[m].z / sc),
+                                e4m3_round(s[m].w / sc));
+            }
+            s[m] = make_float4(e.x * sc, e.y * sc, e.z * sc, e.w * sc);
+            if (CODES && a.codes) {
+                const int row = rg * R + m;
+                uchar4 cc = make_uchar4(e4m3_bits(e.x), e4m3_bits(e.y), e4m3_bits(e.z), e4m3_bits(e.w));
                 *reinterpret_cast<uchar4*>(static_cast<uint8_t*>(a.codes) + (tok * DK + row) * DV + col0) = cc;
             }
         }
-        if (a.scales && tid == 0) a.scales[tok * (DV / 64) + blk] = sc;
+        if (CODES && a.scales && tid == 0) a.scales[tok * (DV / 64) + blk] = sc;
     }
 
     if (HAD && !p.rot) {
         __syncthreads();
 #pragma unroll
-        for (int m = 0; m < R; m++)
-            *reinterpret_cast<float4*>(&tile[(rg * R + m) * 64 + cq * 4]) = s[m];
-#pragma unroll 1
-        for (int hs = 1; hs < DK; hs <<= 1) {
-            __syncthreads();
-            for (int idx = tid; idx < DK * 32; idx += 256) {
-                int c = idx & 63, pp = idx >> 6;
-                int i = (pp / hs) * 2 * hs + (pp % hs);
-                float x0 = tile[i * 64 + c], x1 = tile[(i + hs) * 64 + c];
-                tile[i * 64 + c] = x0 + x1;
-                tile[(i + hs) * 64 + c] = x0 - x1;
-            }
-        }
-        __syncthreads();
+        for (int m = 0; m < R; m++) *reinterpret_cast<float4*>(&tile[(rg * R + m) * 64 + cq * 4]) = s[m];
+        dec_tile_wht<DK>(tile);
         constexpr float inv = 1.0f / DK;
 #pragma unroll
         for (int m = 0; m < R; m++) {
@@ -241,8 +261,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
     }
 
 #pragma unroll
-    for (int m = 0; m < R; m++)
-        *reinterpret_cast<float4*>(Sbase + static_cast<size_t>(rg * R + m) * DV + col0) = s[m];
+    for (int m = 0; m < R; m++) *reinterpret_cast<float4*>(Srow + static_cast<size_t>(m) * DV) = s[m];
 }
 
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
@@ -251,7 +270,10 @@ static hipError_t launch_dec_t(const la_config& c, const DecodeArgs& a, hipStrea
     p.H = c.H; p.dv = c.d_v; p.qkv_dt = c.qkv_dtype; p.gate_dt = c.gate_dtype; p.out_dt = c.out_dtype;
     p.rot = c.hadamard && c.state_rotated;
     dim3 grid(c.d_v / 64, c.H, c.B);
-    hipLaunchKernelGGL((decode_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(256), 0, s, p, a);
+    if (a.codes || a.scales)
+        hipLaunchKernelGGL((decode_kernel<DK, QMODE, G, HAD, KDA, true>), grid, dim3(256), 0, s, p, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<DK, QMODE, G, HAD, KDA, false>), grid, dim3(256), 0, s, p, a);
     return hipGetLastError();
 }
 

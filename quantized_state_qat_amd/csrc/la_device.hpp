@@ -31,21 +31,85 @@ __device__ __forceinline__ void store_elem(void* p, size_t idx, int dtype, float
 }
 
 // ------------------------------------------------------------------ cross-lane
-__device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, kWave); }
+// Lane exchanges use DPP (within rows of 16 lanes) and the gfx950 permlane swaps (across
+// rows), never the LDS crossbar.  Every reduction step combines a lane with one partner
+// in the complementary half of its group, and IEEE add/max are commutative, so all lanes of
+// a group end with bit-identical results.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
 
-// Max over aligned groups of `n` lanes (n a power of two <= 64); result in every lane.
+struct Pair {
+    float a, b;
+};
+// (x of this lane, x of lane ^ 16)
+__device__ __forceinline__ Pair swap16(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// (x of this lane, x of lane ^ 32)
+__device__ __forceinline__ Pair swap32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Max over aligned groups of N lanes (N a power of two <= 64); result in every lane.
 template <int N>
 __device__ __forceinline__ float group_max(float x) {
-#pragma unroll
-    for (int m = 1; m < N; m <<= 1) x = fmaxf(x, xor_shfl(x, m));
+    if (N >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
+    if (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
+    if (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+    if (N >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
+    if (N >= 32) { Pair p = swap16(x); x = fmaxf(p.a, p.b); }
+    if (N >= 64) { Pair p = swap32(x); x = fmaxf(p.a, p.b); }
     return x;
 }
 
-// Sum over the whole wave with a fixed butterfly order; result in every lane.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) x += xor_shfl(x, m);
+// Sum over aligned groups of N lanes; result in every lane.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    if (N >= 2) x = x + dpp<kDppXor1>(x);
+    if (N >= 4) x = x + dpp<kDppXor2>(x);
+    if (N >= 8) x = x + dpp<kDppHalfMirror>(x);
+    if (N >= 16) x = x + dpp<kDppMirror>(x);
+    if (N >= 32) { Pair p = swap16(x); x = p.a + p.b; }
+    if (N >= 64) { Pair p = swap32(x); x = p.a + p.b; }
     return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<kWave>(x); }
+
+// Sum over the four lanes {i, i^16, i^32, i^48}: the same position in each row of 16.
+__device__ __forceinline__ float rows_sum(float x) {
+    Pair p = swap16(x);
+    x = p.a + p.b;
+    p = swap32(x);
+    return p.a + p.b;
+}
+
+// General lane exchange (LDS crossbar), for patterns the above do not cover.
+__device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, kWave); }
+
+// ------------------------------------------------------------------ correctly rounded quotient
+// x / s rounded to nearest even, given y = RN(1/s) (Markstein, "Computation of elementary
+// functions on the IBM RISC System/6000 processor", IBM J. Res. Dev. 34(1), 1990): with y
+// within half an ulp of 1/s, one residual correction brings q = RN(x y) within one ulp of
+// x/s, and a second residual correction r = x - s q (exact by FMA) gives q + r y = RN(x/s).
+// Valid when no intermediate underflows or overflows: callers use it for |x/s| <= 2^8 and
+// s >= 2^-100 and fall back to the division otherwise.  The sign of a zero quotient is
+// restored from x.
+__device__ __forceinline__ float quot_rn(float x, float s, float y) {
+    float q = x * y;
+    float r = __builtin_fmaf(-s, q, x);
+    q = __builtin_fmaf(r, y, q);
+    r = __builtin_fmaf(-s, q, x);
+    q = __builtin_fmaf(r, y, q);
+    return copysignf(q, x);
 }
 
 // ------------------------------------------------------------------ INT8 group codec
@@ -57,6 +121,15 @@ __device__ __forceinline__ float int8_code(float x, float s) {
     float r = rintf(x / s);
     return fminf(fmaxf(r, -127.0f), 127.0f);
 }
+
+// Same code from a precomputed y = RN(1/s) (see quot_rn; requires s >= 2^-100).
+__device__ __forceinline__ float int8_code_y(float x, float s, float y) {
+    float r = rintf(quot_rn(x, s, y));
+    return fminf(fmaxf(r, -127.0f), 127.0f);
+}
+
+constexpr float kFastQuotMinScale = 0x1p-100f;      // INT8: decisions need |x/s| >= 1/2
+constexpr float kFastQuotMinScaleE4M3 = 0x1p-80f;   // E4M3: decisions down to |x/s| ~ 2^-10
 
 // ------------------------------------------------------------------ E4M3FN codec
 // Nearest OCP E4M3FN value to y (ties to even, saturating at +-448).  For |y| in the binade
