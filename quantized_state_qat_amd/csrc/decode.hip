@@ -1,9 +1,9 @@
 // Single-token batched decode: the FP32 state is streamed HBM -> VGPR -> HBM in place.
 //
-// One workgroup per (sequence, head, 64-column value tile), 256 threads laid out as
-// 16 column quads x 16 row groups: thread (rg, cq) holds rows [rg*R, rg*R + R) of the four
-// columns 4cq..4cq+3 (R = d_k / 16), loaded as float4 so that every wave reads 256-byte
-// contiguous row segments.  One pass over the state produces both key-axis reductions the
+// One workgroup per (sequence, head, 64-column value tile), laid out as 16 column quads x
+// (d_k / R) row groups: thread (rg, cq) holds rows [rg*R, rg*R + R) of the four columns
+// 4cq..4cq+3, loaded as float4 so that every wave reads 256-byte contiguous row segments.
+// The state is streamed with non-temporal loads and stores (it is touched once per step).  One pass over the state produces both key-axis reductions the
 // token needs, u = S~^T k and r = S~^T q, because the output read before rounding is
 //     o = S'^T q = S~^T q + delta (k . q),
 // so a single reduction round (in-thread over R rows, across the 4 row groups of a wave
@@ -20,14 +20,24 @@ struct DecParams {
     int rot;  // Hadamard mode with the state held rotated (Y = Hu S)
 };
 
-template <int DK>
+template <int DK, int NW>
 struct DecSmem {
     float k[DK], a[DK], ak[DK], aq[DK];
     float q[DK];
     float beta, kqp[2];
-    float4 red[4][16][2];
-    float amax[4];
+    float4 red[NW][16][2];
+    float amax[NW];
 };
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_nt(const float* p) {
+    v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_nt(float* p, float4 x) {
+    v4f v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
+}
 
 // 4 consecutive elements starting at element idx (idx % 4 == 0), float32 or bfloat16.
 __device__ __forceinline__ float4 load4(const void* p, size_t idx, int dtype) {
@@ -59,13 +69,13 @@ __device__ __forceinline__ float max4abs(float4 x) {
 }
 
 // In-LDS unnormalized Walsh-Hadamard transform over the key axis of a DK x 64 tile
-// (all threads call).
-template <int DK>
+// (all NT threads call).
+template <int DK, int NT>
 __device__ __forceinline__ void dec_tile_wht(float* tile) {
 #pragma unroll 1
     for (int hs = 1; hs < DK; hs <<= 1) {
         __syncthreads();
-        for (int idx = threadIdx.x; idx < DK * 32; idx += 256) {
+        for (int idx = threadIdx.x; idx < DK * 32; idx += NT) {
             int c = idx & 63, pp = idx >> 6;
             int i = (pp / hs) * 2 * hs + (pp % hs);
             float x0 = tile[i * 64 + c], x1 = tile[(i + hs) * 64 + c];
@@ -76,10 +86,11 @@ __device__ __forceinline__ void dec_tile_wht(float* tile) {
     __syncthreads();
 }
 
-template <int DK, int QMODE, int G, bool HAD, bool KDA, bool CODES>
-__global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) {
-    constexpr int R = DK / 16;
-    __shared__ DecSmem<DK> sm;
+template <int DK, int R, int QMODE, int G, bool HAD, bool KDA, bool CODES>
+__global__ __launch_bounds__(16 * (DK / R)) void decode_kernel(DecParams p, DecodeArgs a) {
+    constexpr int NT = 16 * (DK / R);  // threads
+    constexpr int NW = NT / 64;        // waves
+    __shared__ DecSmem<DK, NW> sm;
     __shared__ float tile[HAD ? DK * 64 : 1];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int cq = tid & 15, rg = tid >> 4;
@@ -101,7 +112,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
     const float4 vv = load4(a.v, tok * DV + col0, p.qkv_dt);
     float4 s[R];
 #pragma unroll
-    for (int m = 0; m < R; m++) s[m] = *reinterpret_cast<const float4*>(Srow + static_cast<size_t>(m) * DV);
+    for (int m = 0; m < R; m++) s[m] = load_nt(Srow + static_cast<size_t>(m) * DV);
 
     if (tid < DK) {
         sm.k[tid] = kk;
@@ -160,8 +171,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
         sm.red[w][cq][1] = pr;
     }
     __syncthreads();
-    const float4 u = add4(add4(add4(sm.red[0][cq][0], sm.red[1][cq][0]), sm.red[2][cq][0]), sm.red[3][cq][0]);
-    const float4 r = add4(add4(add4(sm.red[0][cq][1], sm.red[1][cq][1]), sm.red[2][cq][1]), sm.red[3][cq][1]);
+    float4 u = sm.red[0][cq][0], r = sm.red[0][cq][1];
+#pragma unroll
+    for (int ww = 1; ww < NW; ww++) {
+        u = add4(u, sm.red[ww][cq][0]);
+        r = add4(r, sm.red[ww][cq][1]);
+    }
     const float kq = sm.kqp[0] + sm.kqp[1];
     const float4 dl = make_float4(beta * (vv.x - u.x), beta * (vv.y - u.y), beta * (vv.z - u.z), beta * (vv.w - u.w));
     if (rg == 0) {
@@ -185,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
         // S' -> Hu S' through LDS (key axis); quantize there; S = Hu Yhat / d_k afterwards
 #pragma unroll
         for (int m = 0; m < R; m++) *reinterpret_cast<float4*>(&tile[(rg * R + m) * 64 + cq * 4]) = s[m];
-        dec_tile_wht<DK>(tile);
+        dec_tile_wht<DK, NT>(tile);
 #pragma unroll
         for (int m = 0; m < R; m++) s[m] = *reinterpret_cast<const float4*>(&tile[(rg * R + m) * 64 + cq * 4]);
     }
@@ -223,7 +238,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
         mx = group_max<64>(mx);
         if (lane == 0) sm.amax[w] = mx;
         __syncthreads();
-        const float amax = fmaxf(fmaxf(sm.amax[0], sm.amax[1]), fmaxf(sm.amax[2], sm.amax[3]));
+        float amax = sm.amax[0];
+#pragma unroll
+        for (int ww = 1; ww < NW; ww++) amax = fmaxf(amax, sm.amax[ww]);
         const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
         const bool fast = sc >= kFastQuotMinScaleE4M3;
         const float y = 1.0f / sc;
@@ -251,7 +268,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < R; m++) *reinterpret_cast<float4*>(&tile[(rg * R + m) * 64 + cq * 4]) = s[m];
-        dec_tile_wht<DK>(tile);
+        dec_tile_wht<DK, NT>(tile);
         constexpr float inv = 1.0f / DK;
 #pragma unroll
         for (int m = 0; m < R; m++) {
@@ -261,19 +278,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p, DecodeArgs a) 
     }
 
 #pragma unroll
-    for (int m = 0; m < R; m++) *reinterpret_cast<float4*>(Srow + static_cast<size_t>(m) * DV) = s[m];
+    for (int m = 0; m < R; m++) store_nt(Srow + static_cast<size_t>(m) * DV, s[m]);
 }
+
+// Rows per thread: 8 at d_k = 128 (256 threads; measured faster than 4 or 2 rows per thread
+// for the in-place stream), one row group per 16 rows otherwise.
+#ifndef LA_DECODE_R128
+#define LA_DECODE_R128 8
+#endif
+template <int DK>
+constexpr int dec_rows() { return DK == 128 ? LA_DECODE_R128 : DK / 16; }
 
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
 static hipError_t launch_dec_t(const la_config& c, const DecodeArgs& a, hipStream_t s) {
     DecParams p;
     p.H = c.H; p.dv = c.d_v; p.qkv_dt = c.qkv_dtype; p.gate_dt = c.gate_dtype; p.out_dt = c.out_dtype;
     p.rot = c.hadamard && c.state_rotated;
+    constexpr int R = dec_rows<DK>();
+    constexpr int NT = 16 * (DK / R);
     dim3 grid(c.d_v / 64, c.H, c.B);
     if (a.codes || a.scales)
-        hipLaunchKernelGGL((decode_kernel<DK, QMODE, G, HAD, KDA, true>), grid, dim3(256), 0, s, p, a);
+        hipLaunchKernelGGL((decode_kernel<DK, R, QMODE, G, HAD, KDA, true>), grid, dim3(NT), 0, s, p, a);
     else
-        hipLaunchKernelGGL((decode_kernel<DK, QMODE, G, HAD, KDA, false>), grid, dim3(256), 0, s, p, a);
+        hipLaunchKernelGGL((decode_kernel<DK, R, QMODE, G, HAD, KDA, false>), grid, dim3(NT), 0, s, p, a);
     return hipGetLastError();
 }
 
