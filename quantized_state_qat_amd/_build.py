@@ -10,11 +10,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblaqat.so")
-SOURCES = ["la_api.cpp", "fwd.hip", "fwd_fast.hip", "decode.hip", "bwd.hip"]
+SOURCES = ["la_api.cpp", "fwd.hip", "fwd_fast.hip", "fwd_wave.hip", "decode.hip", "bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "-std=c++17", "-O3", "-fPIC", "--offload-arch=gfx950",
+    "-std=c++20", "-O3", "-fPIC", "--offload-arch=gfx950",
     # contraction only where the source writes fmaf: the forward and the backward's recompute
     # must round identically
     "-ffp-contract=off",
