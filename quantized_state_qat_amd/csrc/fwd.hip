@@ -96,6 +96,7 @@ static hipError_t launch_fwd_dk(const la_config& c, const FwdArgs& a, hipStream_
 }
 
 hipError_t launch_fwd(const la_config& c, const FwdArgs& a, hipStream_t s) {
+    if (fwd_mfma_eligible(c)) return launch_fwd_mfma(c, a, s);
     if (fwd_wave_eligible(c)) return launch_fwd_wave(c, a, s);
     if (fwd_fast_eligible(c)) return launch_fwd_fast(c, a, s);
     switch (c.d_k) {

@@ -1,0 +1,388 @@
+// Long-sequence forward on the matrix cores: scalar gate, d_k = 128, bf16 keys, queries and
+// values, state rounded at most once per block of 16 tokens (no quantizer, or INT8/E4M3 at an
+// interval that is a multiple of 16).
+//
+// The recurrence is advanced a block of 16 tokens at a time.  With S_0 the (true) state
+// entering the block, Gamma_j the product of the block's gates up to token j and
+// dd_j = delta_j / Gamma_j, the state inside the block is
+//     S_j = Gamma_j (S_0 + sum_{i<=j} k_i dd_i^T),
+// so every token's key and query projections follow from one projection of S_0:
+//     u_j = Gamma_j (P'_j + sum_{i<j} (k_i . k_j) dd_i),      P' = S_0^T K
+//     o_j = Gamma_j (Q'_j + sum_{i<=j} (k_i . q_j) dd_i),     Q' = S_0^T Q
+//     dd_j = beta_j (v_j / Gamma_j - P'_j - sum_{i<j} (k_i . k_j) dd_i)
+// and the block ends with S_16 = Gamma_15 (S_0 + K^T DD).  This is the gated delta rule
+// itself, regrouped; every product is formed in fp32.  Per wave (128 key rows x 16 value
+// columns, lane 16 g + c holding column c and rows 32 g + m in s[m]):
+//  * P', Q' (16 tokens x 16 columns each): 2 x 32 fp32 MFMAs (16x16x4), the state register
+//    s[sigma] serving directly as the B operand of slice sigma; the key rows are assigned so
+//    that each lane's share of a token's keys comes from one coalesced 64-byte line per load:
+//    s[m] of lane group g is key row 32 (m / 8) + 8 g + m % 8;
+//  * the Gram matrices K K^T and K Q^T: bf16 MFMAs on the raw keys and queries (exact
+//    products, fp32 sums);
+//  * the triangular recurrence for dd in four stages: lane group g solves tokens 4 g .. 4 g + 3
+//    of its column from its own coefficients, and after each stage one fp32 MFMA adds the
+//    stage's dd to the projections of all later tokens;
+//  * o = Gamma (Q' + tril(K Q^T)^T DD): 4 fp32 MFMAs on the Gram output registers;
+//  * S_0 + K^T DD: 32 fp32 MFMAs with s[4 tau .. 4 tau + 3] as the accumulator tile tau and
+//    the keys read transposed from LDS; then the fold by Gamma_15.
+// A block whose gate products leave [2^-60, 2^60] is run token by token with the gates
+// applied to the state (the DPP passes of the wave layout).  Tokens past the end read zero
+// inputs and beta = 0 and leave the state unchanged; their outputs are dropped.
+#include "la_device.hpp"
+#include "la_internal.hpp"
+#include "la_recur.hpp"
+#include "la_wave.hpp"
+
+namespace la {
+
+Params make_params(const la_config& c);
+
+namespace {
+
+constexpr int kBlk = 16;                       // tokens per block
+constexpr int kMThreads = kWaveTileWaves * 64;  // 4 waves = 64 value columns
+constexpr float kGammaLo = 0x1p-60f, kGammaHi = 0x1p60f;
+constexpr int kDppRowShr = 0x110;              // row_shr:n = kDppRowShr + n
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+// Per-wave LDS of one block.
+struct BlockShared {
+    float Gk[kBlk][kBlk];    // [j][i] = k_i . k_j
+    float dd[4][kBlk][4];    // [lane group][column][r]: dd of tokens 4 g + r, for the stage MFMAs
+    float gam[kBlk], rgam[kBlk], beta[kBlk];
+};
+
+// Key row held in s[m] by lane group g.
+__device__ __forceinline__ int state_row(int m, int g) { return 32 * (m >> 3) + 8 * g + (m & 7); }
+
+// Product with identity-filled lanes: x[lane - n] of the same row of 16, 1.0 below the row.
+template <int N>
+__device__ __forceinline__ float row_shr_or_one(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), kDppRowShr + N, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+}  // namespace
+
+template <int QMODE, int G, bool GF32, bool OBF16>
+__global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a) {
+    constexpr int DK = 128, R = 32;
+    constexpr int GB = GF32 ? 4 : 2, OB = OBF16 ? 2 : 4;
+
+    __shared__ WaveQdqShared<DK, QMODE, G> qsh;
+    __shared__ uint16_t kT[2][DK][kBlk];  // the block's keys, [row][token], by block parity
+    __shared__ BlockShared bsh[kWaveTileWaves];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int col = blockIdx.x * kTileCols + w * kWaveCols + c;
+    const int T = p.T, H = p.H, DV = p.dv;
+    const size_t bh = static_cast<size_t>(b) * H + h;
+    const size_t state_off = bh * DK * DV;
+    const size_t seq0 = static_cast<size_t>(b) * T * H;
+    const size_t seq_tok = static_cast<size_t>(T) * H;
+    BlockShared& sh = bsh[w];
+
+    // Buffer resources over exactly this sequence's tokens (offsets < 2^31, checked on the
+    // host): reads past its last token return zero, stores there are dropped.
+    const auto rk = make_rsrc(static_cast<const char*>(a.k) + seq0 * DK * 2, seq_tok * DK * 2);
+    const auto rq = make_rsrc(static_cast<const char*>(a.q) + seq0 * DK * 2, seq_tok * DK * 2);
+    const auto rv = make_rsrc(static_cast<const char*>(a.v) + seq0 * DV * 2, seq_tok * DV * 2);
+    const auto rgt = make_rsrc(static_cast<const char*>(a.g) + seq0 * GB, seq_tok * GB);
+    const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
+    const bool has_o = a.o != nullptr;
+    const auto ro = make_rsrc(has_o ? static_cast<const char*>(a.o) + seq0 * DV * OB : nullptr,
+                              has_o ? seq_tok * DV * OB : 0);
+
+    // ---------------------------------------------------------------- state
+    float s[R];
+#pragma unroll
+    for (int m = 0; m < R; m++)
+        s[m] = a.S0 ? a.S0[state_off + static_cast<size_t>(state_row(m, g)) * DV + col] : 0.0f;
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---------------------------------------------------------------- block inputs
+    // Lane (g, c): the keys and queries of token t0 + c at rows state_row(0..31, g) (load i
+    // brings rows 32 i + 8 g .. + 7, the four lane groups together one 64-byte line); the
+    // values of tokens t0 + 4 g .. 4 g + 3 at its column; gate and beta of token t0 + c.
+    struct BlockIn {
+        u4 k[4], q[4];
+        uint32_t v[4];
+        uint32_t g, b;
+    };
+    const int voff_kq = (c * H * DK + 8 * g) * 2;
+    const int voff_v = (4 * g * H * DV + col) * 2;
+    const int voff_gate = c * H * GB;
+    auto fetch = [&](BlockIn& in, int t0) {
+        const int so = (t0 * H + h) * DK * 2;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            in.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so, 0);
+            in.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            in.v[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff_v, ((t0 + r) * H + h) * DV * 2, 0);
+        const int sg = (t0 * H + h) * GB;
+        if (GF32) {
+            in.g = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gate, sg, 0);
+            in.b = __builtin_amdgcn_raw_buffer_load_b32(rbt, voff_gate, sg, 0);
+        } else {
+            in.g = __builtin_amdgcn_raw_buffer_load_b16(rgt, voff_gate, sg, 0);
+            in.b = __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, sg, 0);
+        }
+    };
+    auto kword = [](const u4 (&x)[4], int i) { return x[i >> 2][i & 3]; };  // dword i of 16
+
+    // ---------------------------------------------------------------- outputs
+    const int voff_o = (4 * g * H * DV + col) * OB;  // register r: token t0 + 4 g + r
+    auto store_o = [&](int t0, int r, float ov) {
+        const int so = ((t0 + r) * H + h) * DV * OB;
+        if (OBF16) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(ov), ro, voff_o, so, 0);
+        else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), ro, voff_o, so, 0);
+    };
+
+    // ---------------------------------------------------------------- block loop
+    int qpar = 0;
+    const int qi = p.qdq_interval;
+    int q_next = QMODE != LA_QDQ_NONE ? min(qi, T) - 1 : T;
+    int ck_next = a.ckpts ? 0 : T;
+
+    BlockIn cur, nxt;
+    fetch(cur, 0);
+    int par = 0;
+#pragma unroll 1
+    for (int t0 = 0; t0 < T; t0 += kBlk, par ^= 1) {
+        fetch(nxt, t0 + kBlk);
+        if (t0 == ck_next) {
+            float* dst = a.ckpts + (bh * p.nck + t0 / p.ckpt_interval) * DK * DV;
+#pragma unroll
+            for (int m = 0; m < R; m++) dst[static_cast<size_t>(state_row(m, g)) * DV + col] = s[m];
+            ck_next += p.ckpt_interval;
+        }
+
+        // gates of the block: lane (g, c) holds token t0 + c; every row of 16 computes the
+        // same inclusive product
+        const bool valid = t0 + c < T;
+        const float gv = GF32 ? __uint_as_float(cur.g) : bf_lo(cur.g);
+        const float bv = GF32 ? __uint_as_float(cur.b) : bf_lo(cur.b);
+        const float eg = valid ? expf(gv) : 1.0f;
+        float gam = eg;
+        gam *= row_shr_or_one<1>(gam);
+        gam *= row_shr_or_one<2>(gam);
+        gam *= row_shr_or_one<4>(gam);
+        gam *= row_shr_or_one<8>(gam);
+        const bool in_range = __all(gam >= kGammaLo && gam <= kGammaHi);
+        if (g == 0) {
+            sh.gam[c] = gam;
+            sh.rgam[c] = 1.0f / gam;
+            sh.beta[c] = valid ? bv : 0.0f;
+        }
+
+        // the block's keys, transposed into LDS for the update (wave w writes dwords
+        // 4 w .. 4 w + 3 of each lane: rows 32 w + 8 g .. + 7; the four waves hold the same keys)
+        auto write_kT = [&](auto wc) {  // static register indices for wave wc
+            constexpr int W = decltype(wc)::value;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t wd = kword(cur.k, 4 * W + i);
+                kT[par][32 * W + 8 * g + 2 * i][c] = static_cast<uint16_t>(wd & 0xFFFFu);
+                kT[par][32 * W + 8 * g + 2 * i + 1][c] = static_cast<uint16_t>(wd >> 16);
+            }
+        };
+        switch (w) {
+            case 0: write_kT(std::integral_constant<int, 0>{}); break;
+            case 1: write_kT(std::integral_constant<int, 1>{}); break;
+            case 2: write_kT(std::integral_constant<int, 2>{}); break;
+            default: write_kT(std::integral_constant<int, 3>{}); break;
+        }
+
+        if (in_range) {
+            // Gram matrices: gk (lane (g, n), register r) = k_{4g+r} . k_n, gq = k_{4g+r} . q_n
+            f4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint32_t ka[2] = {kword(cur.k, 2 * i), kword(cur.k, 2 * i + 1)};
+                const uint32_t qa[2] = {kword(cur.q, 2 * i), kword(cur.q, 2 * i + 1)};
+                s4 ak, bq;
+                __builtin_memcpy(&ak, ka, 8);
+                __builtin_memcpy(&bq, qa, 8);
+                gk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, ak, gk, 0, 0, 0);
+                gq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, bq, gq, 0, 0, 0);
+            }
+            *reinterpret_cast<f4*>(&sh.Gk[c][4 * g]) = gk;  // symmetric: [c][i] = k_i . k_c
+
+            // projections of S_0: dk (lane (g, c), register r) = P'_{4g+r}[c], dq = Q'
+            f4 dk = {0.0f, 0.0f, 0.0f, 0.0f}, dq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const uint32_t kw = kword(cur.k, i), qw = kword(cur.q, i);
+                dk = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_lo(kw), s[2 * i], dk, 0, 0, 0);
+                dq = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_lo(qw), s[2 * i], dq, 0, 0, 0);
+                dk = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_hi(kw), s[2 * i + 1], dk, 0, 0, 0);
+                dq = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_hi(qw), s[2 * i + 1], dq, 0, 0, 0);
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+            // per-lane constants of the recurrence: this lane group's tokens 4 g + r ...
+            const f4 gam4 = *reinterpret_cast<const f4*>(&sh.gam[4 * g]);
+            const f4 rgam4 = *reinterpret_cast<const f4*>(&sh.rgam[4 * g]);
+            const f4 beta4 = *reinterpret_cast<const f4*>(&sh.beta[4 * g]);
+            // ... k_{4g+i} . k_{4g+j} within the group (i < j) ...
+            const float c01 = sh.Gk[4 * g + 1][4 * g], c02 = sh.Gk[4 * g + 2][4 * g];
+            const float c12 = sh.Gk[4 * g + 2][4 * g + 1], c03 = sh.Gk[4 * g + 3][4 * g];
+            const float c13 = sh.Gk[4 * g + 3][4 * g + 1], c23 = sh.Gk[4 * g + 3][4 * g + 2];
+            // ... and the stage MFMAs' A operands: lane (kk, j) = k_{4s+kk} . k_j for tokens j
+            // of later groups (j >= 4 s + 4), else 0
+            float ast[3];
+#pragma unroll
+            for (int st = 0; st < 3; st++) ast[st] = c >= 4 * st + 4 ? sh.Gk[c][4 * st + g] : 0.0f;
+
+            // dd in four stages; after stage st, lane group st's values are final and the
+            // MFMA adds their contribution to the later tokens' projections
+            float sel[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; st++) {
+                const float x0 = beta4[0] * __builtin_fmaf(bf_lo(cur.v[0]), rgam4[0], -dk[0]);
+                const float x1 = beta4[1] * __builtin_fmaf(bf_lo(cur.v[1]), rgam4[1], -__builtin_fmaf(c01, x0, dk[1]));
+                const float x2 = beta4[2] * __builtin_fmaf(bf_lo(cur.v[2]), rgam4[2],
+                                                           -__builtin_fmaf(c12, x1, __builtin_fmaf(c02, x0, dk[2])));
+                const float x3 = beta4[3] * __builtin_fmaf(bf_lo(cur.v[3]), rgam4[3],
+                                                           -__builtin_fmaf(c23, x2, __builtin_fmaf(c13, x1, __builtin_fmaf(c03, x0, dk[3]))));
+                if (g == st) {
+                    sel[0] = x0; sel[1] = x1; sel[2] = x2; sel[3] = x3;
+                }
+                if (st < 3) {
+                    const f4 xv = {x0, x1, x2, x3};
+                    *reinterpret_cast<f4*>(&sh.dd[g][c][0]) = xv;
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    const float bst = sh.dd[st][c][g];  // B: lane (kk, n) = dd_{4 st + kk}[n]
+                    dk = __builtin_amdgcn_mfma_f32_16x16x4f32(ast[st], bst, dk, 0, 0, 0);
+                }
+            }
+
+            // o_i = Gamma_i (Q'_i + sum_{j <= i} (k_j . q_i) dd_j)
+            f4 ov = dq;
+#pragma unroll
+            for (int kp = 0; kp < 4; kp++) {
+                const float am = 4 * g + kp <= c ? gq[kp] : 0.0f;
+                ov = __builtin_amdgcn_mfma_f32_16x16x4f32(am, sel[kp], ov, 0, 0, 0);
+            }
+            if (has_o) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) store_o(t0, r, gam4[r] * ov[r]);
+            }
+
+            // S_0 + K^T DD, tile tau = s[4 tau .. 4 tau + 3]: accumulator row i = 4 g' + r is
+            // key row state_row(4 tau + r, g'); A (row i = c, token slot g) = k_{4g+kappa} there
+            __syncthreads();
+#pragma unroll
+            for (int tau = 0; tau < 8; tau++) {
+                const int row = state_row(4 * tau + (c & 3), c >> 2);
+                const uint2 kr = *reinterpret_cast<const uint2*>(&kT[par][row][4 * g]);
+                f4 st = {s[4 * tau], s[4 * tau + 1], s[4 * tau + 2], s[4 * tau + 3]};
+                st = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_lo(kr.x), sel[0], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_hi(kr.x), sel[1], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_lo(kr.y), sel[2], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_hi(kr.y), sel[3], st, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; r++) s[4 * tau + r] = st[r];
+            }
+            const float gend = lane_of(gam, kBlk - 1);
+#pragma unroll
+            for (int m = 0; m < R; m++) s[m] *= gend;
+        } else {
+            // steep gates: token by token, each gate applied to the state
+            __syncthreads();  // keeps the barrier count of the block
+#pragma unroll 1
+            for (int j = 0; j < kBlk && t0 + j < T; j++) {
+                const float aj = lane_of(eg, j);
+                const float bj = sh.beta[j];
+#pragma unroll
+                for (int m = 0; m < R; m++) s[m] *= aj;
+                // keys and queries of token t0 + j in the DPP layout: lane L of row group g holds
+                // rows 2 L, 2 L + 1 of the group's list, state_row(2 L, g) and the next
+                const int so = ((t0 + j) * H + h) * DK * 2;
+                const int eoff = state_row(2 * c, g) * 2;
+                const uint32_t kwd = __builtin_amdgcn_raw_buffer_load_b32(rk, eoff, so, 0);
+                const uint32_t qwd = __builtin_amdgcn_raw_buffer_load_b32(rq, eoff, so, 0);
+                float k0, k1, q0, q1;
+                widen_pairs(kwd, qwd, k0, k1, q0, q1);
+                const float kq = wave_sum(__builtin_fmaf(k1, q1, k0 * q0));
+                float pk, pq, P, Q;
+                dot_pass<R>(s, k0, k1, q0, q1, pk, pq);
+                rows_sum2(pk, pq, P, Q);
+                const uint32_t vwd = __builtin_amdgcn_raw_buffer_load_b16(rv, col * 2, ((t0 + j) * H + h) * DV * 2, 0);
+                const float delta = bj * (bf_lo(vwd) - P);
+                const float o = __builtin_fmaf(delta, kq, Q);
+                update_pass<R>(s, k0, k1, delta);
+                if (has_o && g == 0) {
+                    const int so_o = ((t0 + j) * H + h) * DV * OB;
+                    if (OBF16) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(o), ro, col * OB, so_o, 0);
+                    else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ro, col * OB, so_o, 0);
+                }
+            }
+        }
+
+        if (min(t0 + kBlk, T) - 1 == q_next) {
+            wave_quantize<R, QMODE, G>(s, qsh, lane, w, qpar);
+            q_next = q_next + qi <= T - 1 ? q_next + qi : (q_next < T - 1 ? T - 1 : T);
+        }
+        cur = nxt;
+    }
+    if (a.ST) {
+#pragma unroll
+        for (int m = 0; m < R; m++) a.ST[state_off + static_cast<size_t>(state_row(m, g)) * DV + col] = s[m];
+    }
+}
+
+namespace {
+
+template <int QMODE, int G, bool GF32>
+hipError_t launch_mfma_o(const la_config& c, const FwdArgs& a, hipStream_t s) {
+    dim3 grid(c.d_v / kTileCols, c.H, c.B);
+    if (c.out_dtype == LA_BF16)
+        hipLaunchKernelGGL((fwd_mfma_kernel<QMODE, G, GF32, true>), grid, dim3(kMThreads), 0, s, make_params(c), a);
+    else
+        hipLaunchKernelGGL((fwd_mfma_kernel<QMODE, G, GF32, false>), grid, dim3(kMThreads), 0, s, make_params(c), a);
+    return hipGetLastError();
+}
+
+template <int QMODE, int G>
+hipError_t launch_mfma_t(const la_config& c, const FwdArgs& a, hipStream_t s) {
+    if (c.gate_dtype == LA_F32) return launch_mfma_o<QMODE, G, true>(c, a, s);
+    return launch_mfma_o<QMODE, G, false>(c, a, s);
+}
+
+}  // namespace
+
+bool fwd_mfma_eligible(const la_config& c) {
+    if (!fwd_fast_eligible(c)) return false;
+    if (c.d_k != 128 || c.qkv_dtype != LA_BF16) return false;
+    if (c.qdq != LA_QDQ_NONE && c.qdq_interval % kBlk != 0) return false;
+    if (c.ckpt_interval > 0 && c.ckpt_interval % kBlk != 0) return false;
+    // 32-bit buffer offsets within one sequence, the prefetched block included
+    const size_t span = static_cast<size_t>(c.T + 2 * kBlk) * c.H * (c.d_k > c.d_v ? c.d_k : c.d_v) * 4;
+    return span < (static_cast<size_t>(1) << 31);
+}
+
+hipError_t launch_fwd_mfma(const la_config& c, const FwdArgs& a, hipStream_t s) {
+    if (c.qdq == LA_QDQ_NONE) return launch_mfma_t<LA_QDQ_NONE, 1>(c, a, s);
+    if (c.qdq == LA_QDQ_E4M3_TILE) return launch_mfma_t<LA_QDQ_E4M3_TILE, 64>(c, a, s);
+    switch (c.group) {
+        case 16: return launch_mfma_t<LA_QDQ_INT8_GROUP, 16>(c, a, s);
+        case 32: return launch_mfma_t<LA_QDQ_INT8_GROUP, 32>(c, a, s);
+        default: return launch_mfma_t<LA_QDQ_INT8_GROUP, 64>(c, a, s);
+    }
+}
+
+}  // namespace la

@@ -64,6 +64,8 @@ hipError_t launch_decode(const la_config& c, const DecodeArgs& a, hipStream_t s)
 hipError_t launch_fwd(const la_config& c, const FwdArgs& a, hipStream_t s);
 bool fwd_fast_eligible(const la_config& c);
 hipError_t launch_fwd_fast(const la_config& c, const FwdArgs& a, hipStream_t s);
+bool fwd_mfma_eligible(const la_config& c);
+hipError_t launch_fwd_mfma(const la_config& c, const FwdArgs& a, hipStream_t s);
 bool fwd_wave_eligible(const la_config& c);
 hipError_t launch_fwd_wave(const la_config& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_copy_state(const la_config& c, const float* src, float* dst, hipStream_t s);
