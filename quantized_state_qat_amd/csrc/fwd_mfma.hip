@@ -13,18 +13,20 @@
 // and the block ends with S_16 = Gamma_15 (S_0 + K^T DD).  This is the gated delta rule
 // itself, regrouped; every product is formed in fp32.  Per wave (128 key rows x 16 value
 // columns, lane 16 g + c holding column c and rows 32 g + m in s[m]):
-//  * P', Q' (16 tokens x 16 columns each): 2 x 32 fp32 MFMAs (16x16x4), the state register
-//    s[sigma] serving directly as the B operand of slice sigma; the key rows are assigned so
-//    that each lane's share of a token's keys comes from one coalesced 64-byte line per load:
-//    s[m] of lane group g is key row 32 (m / 8) + 8 g + m % 8;
+//  * P', Q' (16 tokens x 16 columns each): bf16 MFMAs (16x16x32) of the raw keys and queries
+//    (exact in bf16) with the state split exactly into three bf16 parts, 3 x 4 K-slices each;
+//    slice i uses s[8 i .. 8 i + 7], and the key rows are assigned so that the same slice of
+//    a token's keys is the lane's 16-byte load i (the four lane groups together reading one
+//    coalesced 64-byte line): s[m] of lane group g is key row 32 (m / 8) + 8 g + m % 8;
 //  * the Gram matrices K K^T and K Q^T: bf16 MFMAs on the raw keys and queries (exact
 //    products, fp32 sums);
 //  * the triangular recurrence for dd in four stages: lane group g solves tokens 4 g .. 4 g + 3
 //    of its column from its own coefficients, and after each stage one fp32 MFMA adds the
 //    stage's dd to the projections of all later tokens;
 //  * o = Gamma (Q' + tril(K Q^T)^T DD): 4 fp32 MFMAs on the Gram output registers;
-//  * S_0 + K^T DD: 32 fp32 MFMAs with s[4 tau .. 4 tau + 3] as the accumulator tile tau and
-//    the keys read transposed from LDS; then the fold by Gamma_15.
+//  * S_0 + K^T DD: bf16 MFMAs (16x16x16) with s[4 tau .. 4 tau + 3] as the accumulator tile
+//    tau, the keys read transposed from LDS and DD split exactly into three bf16 parts; then
+//    the fold by Gamma_15.
 // A block whose gate products leave [2^-60, 2^60] is run token by token with the gates
 // applied to the state (the DPP passes of the wave layout).  Tokens past the end read zero
 // inputs and beta = 0 and leave the state unchanged; their outputs are dropped.
@@ -45,8 +47,24 @@ constexpr float kGammaLo = 0x1p-60f, kGammaHi = 0x1p60f;
 constexpr int kDppRowShr = 0x110;              // row_shr:n = kDppRowShr + n
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+// x = hi + lo + lo2 exactly, each part a bf16 (nearest at each step): the residual of rounding
+// an fp32 value to bf16 is exact in fp32 and has at most 16 significant bits, the residual of
+// that at most 8, which bf16 holds exactly.  Products of exact bf16 inputs with the parts are
+// exact in fp32, so an MFMA over the three parts forms fp32 products (summed in fp32).
+template <typename FV, typename BV>
+__device__ __forceinline__ void split3(const FV& x, BV& hi, BV& lo, BV& lo2) {
+    hi = __builtin_convertvector(x, BV);
+    const FV r1 = x - __builtin_convertvector(hi, FV);
+    lo = __builtin_convertvector(r1, BV);
+    const FV r2 = r1 - __builtin_convertvector(lo, FV);
+    lo2 = __builtin_convertvector(r2, BV);
+}
 
 // Per-wave LDS of one block.
 struct BlockShared {
@@ -65,7 +83,6 @@ __device__ __forceinline__ float row_shr_or_one(float x) {
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 }  // namespace
 
@@ -120,7 +137,7 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
     const int voff_kq = (c * H * DK + 8 * g) * 2;
     const int voff_v = (4 * g * H * DV + col) * 2;
     const int voff_gate = c * H * GB;
-    auto fetch = [&](BlockIn& in, int t0) {
+    auto fetch = [&](BlockIn& in, int t0) __attribute__((always_inline)) {
         const int so = (t0 * H + h) * DK * 2;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -139,17 +156,20 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             in.b = __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, sg, 0);
         }
     };
-    auto kword = [](const u4 (&x)[4], int i) { return x[i >> 2][i & 3]; };  // dword i of 16
+    auto kword = [](const u4 (&x)[4], int i) __attribute__((always_inline)) { return x[i >> 2][i & 3]; };  // dword i of 16
 
     // ---------------------------------------------------------------- outputs
     const int voff_o = (4 * g * H * DV + col) * OB;  // register r: token t0 + 4 g + r
-    auto store_o = [&](int t0, int r, float ov) {
+    auto store_o = [&](int t0, int r, float ov) __attribute__((always_inline)) {
         const int so = ((t0 + r) * H + h) * DV * OB;
         if (OBF16) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(ov), ro, voff_o, so, 0);
         else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), ro, voff_o, so, 0);
     };
 
     // ---------------------------------------------------------------- block loop
+    // Order of issue within a block: the Gram and projection MFMAs first; while they run, the gates, the
+    // transposed keys and the next block's loads; then the staged recurrence (on P') while
+    // the Q' MFMAs finish; then the output and update MFMAs and the fold.
     int qpar = 0;
     const int qi = p.qdq_interval;
     int q_next = QMODE != LA_QDQ_NONE ? min(qi, T) - 1 : T;
@@ -160,13 +180,38 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
     int par = 0;
 #pragma unroll 1
     for (int t0 = 0; t0 < T; t0 += kBlk, par ^= 1) {
-        fetch(nxt, t0 + kBlk);
         if (t0 == ck_next) {
             float* dst = a.ckpts + (bh * p.nck + t0 / p.ckpt_interval) * DK * DV;
 #pragma unroll
             for (int m = 0; m < R; m++) dst[static_cast<size_t>(state_row(m, g)) * DV + col] = s[m];
             ck_next += p.ckpt_interval;
         }
+
+        // Gram matrices: gk (lane (g, n), register r) = k_{4g+r} . k_n, gq = k_{4g+r} . q_n
+        f4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const bf8 ak = __builtin_bit_cast(bf8, cur.k[i]), aq = __builtin_bit_cast(bf8, cur.q[i]);
+            gk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, ak, gk, 0, 0, 0);
+            gq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, aq, gq, 0, 0, 0);
+        }
+        // projections of S_0: dk (lane (g, c), register r) = P'_{4g+r}[c], dq = Q'
+        f4 dk = {0.0f, 0.0f, 0.0f, 0.0f}, dq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const f8 xs = {s[8 * i], s[8 * i + 1], s[8 * i + 2], s[8 * i + 3],
+                           s[8 * i + 4], s[8 * i + 5], s[8 * i + 6], s[8 * i + 7]};
+            bf8 h, l, l2;
+            split3(xs, h, l, l2);
+            const bf8 ak = __builtin_bit_cast(bf8, cur.k[i]), aq = __builtin_bit_cast(bf8, cur.q[i]);
+            dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l2, dk, 0, 0, 0);
+            dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, l2, dq, 0, 0, 0);
+            dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l, dk, 0, 0, 0);
+            dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, l, dq, 0, 0, 0);
+            dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, h, dk, 0, 0, 0);
+            dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, h, dq, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 
         // gates of the block: lane (g, c) holds token t0 + c; every row of 16 computes the
         // same inclusive product
@@ -185,10 +230,9 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             sh.rgam[c] = 1.0f / gam;
             sh.beta[c] = valid ? bv : 0.0f;
         }
-
         // the block's keys, transposed into LDS for the update (wave w writes dwords
         // 4 w .. 4 w + 3 of each lane: rows 32 w + 8 g .. + 7; the four waves hold the same keys)
-        auto write_kT = [&](auto wc) {  // static register indices for wave wc
+        auto write_kT = [&](auto wc) __attribute__((always_inline)) {  // static register indices for wave wc
             constexpr int W = decltype(wc)::value;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
@@ -203,35 +247,13 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             case 2: write_kT(std::integral_constant<int, 2>{}); break;
             default: write_kT(std::integral_constant<int, 3>{}); break;
         }
+        fetch(nxt, t0 + kBlk);
+        *reinterpret_cast<f4*>(&sh.Gk[c][4 * g]) = gk;  // symmetric: [c][i] = k_i . k_c
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_sched_barrier(0);
 
         if (in_range) {
-            // Gram matrices: gk (lane (g, n), register r) = k_{4g+r} . k_n, gq = k_{4g+r} . q_n
-            f4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gq = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const uint32_t ka[2] = {kword(cur.k, 2 * i), kword(cur.k, 2 * i + 1)};
-                const uint32_t qa[2] = {kword(cur.q, 2 * i), kword(cur.q, 2 * i + 1)};
-                s4 ak, bq;
-                __builtin_memcpy(&ak, ka, 8);
-                __builtin_memcpy(&bq, qa, 8);
-                gk = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, ak, gk, 0, 0, 0);
-                gq = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ak, bq, gq, 0, 0, 0);
-            }
-            *reinterpret_cast<f4*>(&sh.Gk[c][4 * g]) = gk;  // symmetric: [c][i] = k_i . k_c
-
-            // projections of S_0: dk (lane (g, c), register r) = P'_{4g+r}[c], dq = Q'
-            f4 dk = {0.0f, 0.0f, 0.0f, 0.0f}, dq = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const uint32_t kw = kword(cur.k, i), qw = kword(cur.q, i);
-                dk = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_lo(kw), s[2 * i], dk, 0, 0, 0);
-                dq = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_lo(qw), s[2 * i], dq, 0, 0, 0);
-                dk = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_hi(kw), s[2 * i + 1], dk, 0, 0, 0);
-                dq = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_hi(qw), s[2 * i + 1], dq, 0, 0, 0);
-            }
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-
             // per-lane constants of the recurrence: this lane group's tokens 4 g + r ...
             const f4 gam4 = *reinterpret_cast<const f4*>(&sh.gam[4 * g]);
             const f4 rgam4 = *reinterpret_cast<const f4*>(&sh.rgam[4 * g]);
@@ -277,25 +299,28 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
                 const float am = 4 * g + kp <= c ? gq[kp] : 0.0f;
                 ov = __builtin_amdgcn_mfma_f32_16x16x4f32(am, sel[kp], ov, 0, 0, 0);
             }
-            if (has_o) {
-#pragma unroll
-                for (int r = 0; r < 4; r++) store_o(t0, r, gam4[r] * ov[r]);
-            }
 
             // S_0 + K^T DD, tile tau = s[4 tau .. 4 tau + 3]: accumulator row i = 4 g' + r is
-            // key row state_row(4 tau + r, g'); A (row i = c, token slot g) = k_{4g+kappa} there
+            // key row state_row(4 tau + r, g'); A (row i = c, tokens 4 g .. 4 g + 3) = the keys
+            // of those tokens there; B (tokens 4 g + j, column c) = dd, in three bf16 parts
+            const f4 ddv = {sel[0], sel[1], sel[2], sel[3]};
+            bf4 dh, dl, dl2;
+            split3(ddv, dh, dl, dl2);
             __syncthreads();
 #pragma unroll
             for (int tau = 0; tau < 8; tau++) {
                 const int row = state_row(4 * tau + (c & 3), c >> 2);
-                const uint2 kr = *reinterpret_cast<const uint2*>(&kT[par][row][4 * g]);
+                const bf4 kr = *reinterpret_cast<const bf4*>(&kT[par][row][4 * g]);
                 f4 st = {s[4 * tau], s[4 * tau + 1], s[4 * tau + 2], s[4 * tau + 3]};
-                st = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_lo(kr.x), sel[0], st, 0, 0, 0);
-                st = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_hi(kr.x), sel[1], st, 0, 0, 0);
-                st = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_lo(kr.y), sel[2], st, 0, 0, 0);
-                st = __builtin_amdgcn_mfma_f32_16x16x4f32(bf_hi(kr.y), sel[3], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, kr), __builtin_bit_cast(s4, dl2), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, kr), __builtin_bit_cast(s4, dl), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, kr), __builtin_bit_cast(s4, dh), st, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; r++) s[4 * tau + r] = st[r];
+            }
+            if (has_o) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) store_o(t0, r, gam4[r] * ov[r]);
             }
             const float gend = lane_of(gam, kBlk - 1);
 #pragma unroll

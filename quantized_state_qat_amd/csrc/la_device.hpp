@@ -146,6 +146,17 @@ __device__ __forceinline__ float e4m3_round(float y) {
     return fminf(fmaxf(r, -448.0f), 448.0f);
 }
 
+// e4m3_round of two values with the gfx950 conversion instructions (OCP E4M3FN, round to
+// nearest even).  Inputs are clamped to +-448 first, where the conversion saturates the same
+// way e4m3_round does; for every |y| <= 448 the two agree bit for bit.
+__device__ __forceinline__ void e4m3_round2(float& a, float& b) {
+    const float ya = fminf(fmaxf(a, -448.0f), 448.0f);
+    const float yb = fminf(fmaxf(b, -448.0f), 448.0f);
+    const int p = __builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, 0, false);
+    a = __builtin_amdgcn_cvt_f32_fp8(p, 0);
+    b = __builtin_amdgcn_cvt_f32_fp8(p, 1);
+}
+
 // Bit pattern of an E4M3FN grid value v (|v| <= 448, v on the grid).
 __device__ __forceinline__ uint8_t e4m3_bits(float v) {
     uint32_t u = __float_as_uint(v);

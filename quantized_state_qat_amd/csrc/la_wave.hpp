@@ -185,13 +185,20 @@ __device__ __forceinline__ void wave_quantize(float* s, WaveQdqShared<DK, QMODE,
 #pragma unroll
         for (int ww = 1; ww < kWaveTileWaves; ww++) amax = fmaxf(amax, sh.amax[qpar][ww]);
         const float sce = amax > 0.0f ? amax / 448.0f : 1.0f;
+        float yv[R];
         if (sce >= kFastQuotMinScaleE4M3) {
             const float y = 1.0f / sce;
 #pragma unroll
-            for (int m = 0; m < R; m++) s[m] = e4m3_round(quot_rn(s[m], sce, y)) * sce;
+            for (int m = 0; m < R; m++) yv[m] = quot_rn(s[m], sce, y);
         } else {
 #pragma unroll
-            for (int m = 0; m < R; m++) s[m] = e4m3_round(s[m] / sce) * sce;
+            for (int m = 0; m < R; m++) yv[m] = s[m] / sce;
+        }
+#pragma unroll
+        for (int m = 0; m < R; m += 2) {
+            e4m3_round2(yv[m], yv[m + 1]);
+            s[m] = yv[m] * sce;
+            s[m + 1] = yv[m + 1] * sce;
         }
     } else if (QMODE == LA_QDQ_INT8_GROUP) {
         float gm[R];
