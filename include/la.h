@@ -136,6 +136,20 @@ la_status la_recurrent_bwd_ste(const la_config* cfg, const void* q, const void* 
  * includes room for recomputed checkpoints, so it does not depend on whether ckpts is NULL). */
 size_t la_bwd_workspace_bytes(const la_config* cfg);
 
+/*
+ * Which forward kernel la_recurrent_fwd runs for cfg (diagnostic; no GPU work, no state):
+ *   "block"  GDN, d_k = 128, bf16 q/k/v, rounding at most every 16 tokens (interval and
+ *            checkpoint spacing multiples of 16): 16-token blocks on the matrix cores;
+ *   "wave"   GDN, no Hadamard, interval and checkpoint spacing multiples of 8: one wave per
+ *            16 value columns, no barrier per token;
+ *   "fast"   GDN, no Hadamard, rounding at most every 2 tokens, no rounding point strictly
+ *            inside a checkpoint chunk: eight waves per 64 columns, rescaled state;
+ *   "token"  every other valid configuration (KDA, Hadamard, rounding every token).
+ * Returns "" (and sets la_last_error) for an invalid cfg.  The kernels differ only in the
+ * order of floating-point operations; every one computes the same recurrence.
+ */
+const char* la_fwd_kernel_name(const la_config* cfg);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 

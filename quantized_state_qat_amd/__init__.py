@@ -66,6 +66,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
                                "(hipcc, gfx950); there is no fallback path")
+        # torch carries its own HIP runtime, whose soname matches the one the library needs.
+        # Loaded first, it is the runtime the library binds to; loaded after the library,
+        # torch would bring a second runtime into the process, and the two cannot share
+        # devices, pointers or streams.
+        import torch  # noqa: F401
         lib = ctypes.CDLL(path)
         vp, cp = ctypes.c_void_p, ctypes.POINTER(la_config)
         lib.la_recurrent_fwd.restype = ctypes.c_int
@@ -80,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_status_string.argtypes = [ctypes.c_int]
         lib.la_last_error.restype = ctypes.c_char_p
         lib.la_last_error.argtypes = []
+        lib.la_fwd_kernel_name.restype = ctypes.c_char_p
+        lib.la_fwd_kernel_name.argtypes = [cp]
         _lib = lib
     return _lib
 
@@ -135,6 +142,12 @@ def la_recurrent_bwd_ste(cfg: Config, q, k, v, g, beta, S0, ckpts, dout, dS_T, d
                                     _ptr(S0), _ptr(ckpts), _ptr(dout), _ptr(dS_T), _ptr(dq), _ptr(dk),
                                     _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dS0), _ptr(workspace),
                                     int(ws_bytes), _stream(stream)))
+
+
+def la_fwd_kernel_name(cfg: Config) -> str:
+    """Which forward kernel serves cfg: "block", "wave", "fast" or "token" ("" if invalid)."""
+    c = cfg.c()
+    return load_library().la_fwd_kernel_name(ctypes.byref(c)).decode()
 
 
 def la_status_string(status: int) -> str:

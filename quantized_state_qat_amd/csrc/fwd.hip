@@ -95,6 +95,13 @@ static hipError_t launch_fwd_dk(const la_config& c, const FwdArgs& a, hipStream_
     }
 }
 
+const char* fwd_kernel_name(const la_config& c) {
+    if (fwd_mfma_eligible(c)) return "block";
+    if (fwd_wave_eligible(c)) return "wave";
+    if (fwd_fast_eligible(c)) return "fast";
+    return "token";
+}
+
 hipError_t launch_fwd(const la_config& c, const FwdArgs& a, hipStream_t s) {
     if (fwd_mfma_eligible(c)) return launch_fwd_mfma(c, a, s);
     if (fwd_wave_eligible(c)) return launch_fwd_wave(c, a, s);

@@ -126,6 +126,11 @@ const char* la_status_string(la_status s) {
 
 const char* la_last_error(void) { return g_err; }
 
+const char* la_fwd_kernel_name(const la_config* cfg) {
+    if (check_config(cfg, false) != LA_OK) return "";
+    return la::fwd_kernel_name(*cfg);
+}
+
 la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, const void* v,
                            const void* g, const void* beta, const float* S0, void* o,
                            float* S_T, float* ckpts, void* stream) {

@@ -62,6 +62,7 @@ inline int part_width(const la_config& c) { return 2 * c.d_k + (c.gate == LA_GAT
 
 hipError_t launch_decode(const la_config& c, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fwd(const la_config& c, const FwdArgs& a, hipStream_t s);
+const char* fwd_kernel_name(const la_config& c);
 bool fwd_fast_eligible(const la_config& c);
 hipError_t launch_fwd_fast(const la_config& c, const FwdArgs& a, hipStream_t s);
 bool fwd_mfma_eligible(const la_config& c);

@@ -22,7 +22,8 @@ def test_library_exports_every_declared_function():
     lib = la.load_library()
     names = header_functions()
     assert set(names) == {"la_recurrent_fwd", "la_decode_step", "la_recurrent_bwd_ste",
-                          "la_bwd_workspace_bytes", "la_status_string", "la_last_error"}
+                          "la_bwd_workspace_bytes", "la_fwd_kernel_name", "la_status_string",
+                          "la_last_error"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -122,3 +123,44 @@ def test_bwd_workspace_and_checks():
     with pytest.raises(la.LaError) as e:
         la.la_recurrent_bwd_ste(cfg(ckpt_interval=0), *args, FAKE, n, stream=0)
     assert "ckpt_interval" in str(e.value)
+
+
+@pytest.mark.parametrize("kw,name", [
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64), "block"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=16, qdq_interval=16, ckpt_interval=16), "block"),
+    (dict(qdq=la.LA_QDQ_NONE, ckpt_interval=0), "block"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=8), "wave"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, d_k=64), "wave"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=64, qdq_interval=8, ckpt_interval=8), "wave"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=64, qkv_dtype=la.LA_F32), "wave"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=16, qdq_interval=3, ckpt_interval=3), "fast"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=12, ckpt_interval=0), "fast"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=1, ckpt_interval=0), "token"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=64, hadamard=1), "token"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, gate=la.LA_GATE_KEY), "token"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=16), "block"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=4), "fast"),
+])
+def test_fwd_kernel_selection(kw, name):
+    """Which forward kernel serves a configuration (host-side selection, documented in la.h)."""
+    base = dict(B=2, T=100, H=2, d_k=128, d_v=128)
+    base.update(kw)
+    assert la.la_fwd_kernel_name(la.Config(**base)) == name
+
+
+def test_fwd_kernel_name_invalid():
+    assert la.la_fwd_kernel_name(la.Config(B=1, T=4, H=1, d_k=100, d_v=128)) == ""
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the library before anything imports torch must still leave one HIP runtime
+    in the process (two runtimes cannot share devices, pointers or streams)."""
+    import subprocess
+    import sys
+    prog = ("import quantized_state_qat_amd as la; la.load_library(); import torch; "
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}; "
+            "print(len(paths), sorted(paths))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", prog], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split()[0] == "1", out.stdout

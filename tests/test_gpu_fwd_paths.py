@@ -1,0 +1,79 @@
+"""Every forward kernel against the float64 oracle, teacher forced per rounding interval.
+
+la_recurrent_fwd selects one of four kernels from the configuration (la_fwd_kernel_name):
+the block kernel (16-token blocks on the matrix cores), the single-wave kernel, the
+eight-wave kernel and the per-token kernel.  Each case below is chosen to land on one of them
+(asserted), runs with checkpoints at the rounding interval, and then, for every unit and every
+interval, the oracle advances the GPU's checkpoint over that interval in float64 and rounds it
+with the FP32 codec ("GDN state/W QAT foundation", "Torch GDN/KDA decode QAT + INT8": What
+does this PR do?).  Both sides read the same input values (bf16 inputs widen exactly), so the
+only difference is fp32 against float64 arithmetic over one interval: outputs and unrounded
+carried states agree to 1e-5 of their largest magnitude, quantization codes exactly except
++-1 at near-ties (aggregate budget).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_state_qat_amd as la
+import synth
+from tests import gpu_util as gu
+from tests.test_gpu_fwd import sl
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+INT8, E4M3, NONE = la.LA_QDQ_INT8_GROUP, la.LA_QDQ_E4M3_TILE, la.LA_QDQ_NONE
+
+CASES = [
+    # id, workload, quantizer, group, interval (= checkpoint spacing), kernel
+    ("block_int8g32_i16", W("bi8", B=2, T=90, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=40), INT8, 32, 16, "block"),
+    ("block_e4m3_i32_dv192", W("be4", B=1, T=77, H=2, d_k=128, d_v=192, s0_sigma=0.2, config_id=41), E4M3, 64, 32, "block"),
+    ("block_noqdq_i16", W("bnq", B=2, T=50, H=1, d_k=128, d_v=64, s0_sigma=0.2, config_id=42), NONE, 32, 16, "block"),
+    ("wave_e4m3_dk64_i64", W("we4", B=2, T=150, H=2, d_k=64, d_v=128, s0_sigma=0.2, config_id=43), E4M3, 64, 64, "wave"),
+    ("wave_fp32_int8g64_i8", W("wi8", B=1, T=45, H=3, d_k=128, d_v=128, qkv_dtype="f32", gate_dtype="f32",
+                                s0_sigma=0.2, config_id=44), INT8, 64, 8, "wave"),
+    ("wave_int8g16_dk32_i24", W("wdk32", B=2, T=60, H=1, d_k=32, d_v=64, s0_sigma=0.2, config_id=45), INT8, 16, 24, "wave"),
+    ("fast_int8g16_i3", W("fi8", B=1, T=40, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=46), INT8, 16, 3, "fast"),
+    ("fast_e4m3_dk16_i5", W("fe4", B=2, T=33, H=2, d_k=16, d_v=64, s0_sigma=0.2, config_id=47), E4M3, 64, 5, "fast"),
+    ("token_kda_e4m3_i16", W("tk", B=1, T=40, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=48), E4M3, 64, 16, "token"),
+]
+
+
+@pytest.mark.parametrize("name,w,mode,group,interval,kernel", CASES, ids=[c[0] for c in CASES])
+def test_intervals_against_oracle(name, w, mode, group, interval, kernel):
+    d = synth.generate(w)
+    c = gu.cfg_for(w, d, qdq=mode, group=group, qdq_interval=interval if mode != NONE else 1)
+    c.ckpt_interval = interval
+    assert la.la_fwd_kernel_name(c) == kernel
+    S0 = d["S0"].f32
+    o, ST, ck = gu.run_fwd(c, d, S0=S0, ckpt_interval=interval)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ST)) and np.all(np.isfinite(ck))
+    tally = gu.CodeTally()
+    worst_o, worst_s = 0.0, 0.0
+    nseg = (w.T + interval - 1) // interval
+    for b in range(w.B):
+        for h in range(w.H):
+            for s in range(nseg):
+                t0, t1 = s * interval, min(w.T, (s + 1) * interval)
+                dd = sl(d, b, b + 1, t0, t1, h, h + 1)
+                S_in = ck[b:b + 1, h:h + 1, s].astype(np.float64)
+                o_r, Sp, _ = oracle.fwd(dd["q"].f64, dd["k"].f64, dd["v"].f64, dd["g"].f64, dd["beta"].f64,
+                                        S_in, gate=c.gate)
+                worst_o = max(worst_o, gu.err(o[b, t0:t1, h], o_r[0, :, 0]))
+                S_out = ck[b, h, s + 1] if t1 < w.T else ST[b, h]
+                if mode == NONE:
+                    worst_s = max(worst_s, gu.err(S_out, Sp[0, 0]))
+                    continue
+                Xh, codes, _, ypre = oracle.qdq(Sp[0, 0], mode, group, False)
+                if mode == INT8:
+                    gu.compare_int8_codes(S_out, codes, ypre, group, tally=tally)
+                else:
+                    yg = gu.e4m3_codes_from_state(S_out)
+                    yo = gu.e4m3_codes_from_state(Xh)
+                    tally.add(int(np.sum(yg != yo)), yg.size)
+    assert worst_o <= gu.TOL_F32, worst_o
+    assert worst_s <= gu.TOL_F32, worst_s
+    frac = tally.check()
+    print(f"{name} [{kernel}]: max output error {worst_o:.3e}, state error {worst_s:.2e}, "
+          f"code mismatches {tally.mismatches}/{tally.total} ({frac:.2e})")
