@@ -99,7 +99,7 @@ def bench_decode(steps, warmup):
 
 
 def bench_long_e4m3(steps=3, warmup=1):
-    """GDN B=8 H=16 T=4096 d=128, E4M3 tile QDQ every 64 tokens (FP32 VALU-bound)."""
+    """GDN B=8 H=16 T=4096 d=128, E4M3 tile QDQ every 64 tokens."""
     import numpy as np
     import torch
 
@@ -119,28 +119,121 @@ def bench_long_e4m3(steps=3, warmup=1):
     c = la.Config(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v, qdq=la.LA_QDQ_E4M3_TILE, group=64,
                   qdq_interval=64, gate_dtype=la.LA_F32)
     stream = torch.cuda.current_stream()
+    t = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
+                                                ST, stream=stream), steps, warmup, stream)
+    flops = 7.0 * w.d_k * w.d_v * w.B * w.H * w.T
+    return {
+        "workload": "gdn_long_e4m3_64 B=8 H=16 T=4096 d_k=d_v=128 bf16 q/k/v, fp32 g/beta/state, E4M3 tile QDQ every 64 tokens",
+        "kernel": la.la_fwd_kernel_name(c), "ms_per_call": t * 1e3, "updates_per_s": w.B * w.H * w.T / t,
+        "roofline": _fp32_roofline(flops, t, "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head) "
+                                             "against the FP32 peak; the block kernel forms it on the matrix cores "
+                                             "from exact bf16 products with fp32 sums"),
+    }
+
+
+def _dev(t):
+    """Device copy of a generated tensor in its storage dtype."""
+    import numpy as np
+    import torch
+    if t.dtype == "bf16":
+        return torch.from_numpy(t.bits.astype(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t.f32)).cuda()
+
+
+def _fp32_roofline(flops, t, what):
+    return {"bound": "fp32", "achieved": flops / t / 1e12, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": flops / t / 1e12 / FP32_VALU_PEAK_TFLOPS, "flops_per_call": flops, "note": what}
+
+
+def _time_calls(fn, steps, warmup, stream):
+    import torch
     for _ in range(warmup):
-        la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o, ST, stream=stream)
+        fn()
     torch.cuda.synchronize()
     times = []
     for _ in range(steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o, ST, stream=stream)
+        fn()
         b.record(stream)
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b) * 1e-3)
-    t = sum(times) / len(times)
+    return sum(times) / len(times)
+
+
+def bench_kda_tok(steps=3, warmup=1):
+    """KDA B=4 H=32 T=2048 d=128, bf16 inputs, INT8 group-64 QDQ after every token."""
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    w = synth.WORKLOADS[3]
+    d = synth.generate(w)
+    dev = {k: _dev(d[k]) for k in ("q", "k", "v", "g", "beta")}
+    del d
+    o = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
+    ST = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    c = la.Config(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v, gate=la.LA_GATE_KEY, qdq=la.LA_QDQ_INT8_GROUP,
+                  group=64, qdq_interval=1)
+    stream = torch.cuda.current_stream()
+    t = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
+                                                ST, stream=stream), steps, warmup, stream)
     flops = 7.0 * w.d_k * w.d_v * w.B * w.H * w.T
     return {
-        "workload": "gdn_long_e4m3_64 B=8 H=16 T=4096 d_k=d_v=128 bf16 q/k/v, fp32 g/beta/state, E4M3 tile QDQ every 64 tokens",
-        "ms_per_call": t * 1e3, "updates_per_s": w.B * w.H * w.T / t,
-        "roofline": {"bound": "fp32", "achieved": flops / t / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": flops / t / 1e12 / FP32_VALU_PEAK_TFLOPS,
-                     "flops_per_call": flops,
-                     "note": "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head) against the "
-                             "FP32 peak; the block kernel forms it on the matrix cores from exact bf16 products "
-                             "with fp32 sums"},
+        "workload": "kda_int8g64_tok B=4 H=32 T=2048 d_k=d_v=128 bf16 inputs, KDA gate, INT8 group-64 QDQ every token",
+        "kernel": la.la_fwd_kernel_name(c), "ms_per_call": t * 1e3, "updates_per_s": w.B * w.H * w.T / t,
+        "roofline": _fp32_roofline(flops, t, "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head); "
+                                             "the INT8 codec is not counted"),
+    }
+
+
+def bench_wht_fwdbwd(steps=2, warmup=1):
+    """GDN B=4 H=16 T=2048 d=128, bf16 inputs, Hadamard + INT8 group-32 every token: forward with
+    64-token checkpoints, then the straight-through backward from them."""
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    w = synth.WORKLOADS[4]
+    d = synth.generate(w, with_do=True)
+    dev = {k: _dev(d[k]) for k in ("q", "k", "v", "g", "beta")}
+    dout = _dev(d["do"])
+    del d
+    c = la.Config(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v, qdq=la.LA_QDQ_INT8_GROUP, group=32, hadamard=1,
+                  qdq_interval=1, ckpt_interval=64)
+    o = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
+    ST = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    ck = torch.empty((w.B, w.H, (w.T + 63) // 64, w.d_k, w.d_v), device="cuda")
+    grads = [torch.empty((w.B, w.T, w.H, n), device="cuda") for n in (w.d_k, w.d_k, w.d_v)]
+    dg = torch.empty((w.B, w.T, w.H), device="cuda")
+    dbeta = torch.empty((w.B, w.T, w.H), device="cuda")
+    dS0 = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    nbytes = la.la_bwd_workspace_bytes(c)
+    ws = torch.empty((nbytes + 255) // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o, ST, ck, stream=stream)
+
+    def bwd():
+        la.la_recurrent_bwd_ste(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, ck, dout, None,
+                                grads[0], grads[1], grads[2], dg, dbeta, dS0, ws, nbytes, stream=stream)
+
+    t_f = _time_calls(fwd, steps, warmup, stream)
+    t_b = _time_calls(bwd, steps, warmup, stream)
+    unit = w.d_k * w.d_v * w.B * w.H * w.T
+    return {
+        "workload": "gdn_fwdbwd_wht_int8g32 B=4 H=16 T=2048 d_k=d_v=128 bf16 inputs, Hadamard + INT8 group-32 every "
+                    "token, forward with 64-token checkpoints + STE backward",
+        "kernel": la.la_fwd_kernel_name(c), "ms_fwd": t_f * 1e3, "ms_bwd": t_b * 1e3,
+        "updates_per_s": w.B * w.H * w.T / (t_f + t_b),
+        "roofline": _fp32_roofline(29.0 * unit, t_f + t_b,
+                                   "forward 7 + recompute 7 + adjoint 15 d_k d_v flops per token-head; the "
+                                   "rotations and the codec are not counted"),
+        "roofline_fwd": _fp32_roofline(7.0 * unit, t_f, "forward only"),
+        "roofline_bwd": _fp32_roofline(22.0 * unit, t_b, "backward only (recompute + adjoint)"),
     }
 
 
@@ -156,7 +249,7 @@ def cpu_baseline(d, w, budget_s=12.0):
         oracle.fwd(*args, S0, qdq_mode=oracle.QDQ_INT8, group=32, qdq_interval=1)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
+        if el >= budget_s or reps >= 5000:
             break
     rate = reps * w.B * w.H / el
     return {"value": rate, "unit": "token·head updates/s", "cores": oracle.num_threads(), "kind": "oracle",
@@ -182,7 +275,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="skip the long-sequence E4M3 measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the long-sequence, KDA and Hadamard forward/backward measurements")
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection mode: a few decode launches and one plain copy of a "
                          "256 MiB state buffer (the calibration kernel for HBM byte counters); no JSON")
@@ -234,7 +328,8 @@ def main():
         },
     }
     if not args.no_extra:
-        line["extra"] = {"long_sequence": bench_long_e4m3()}
+        line["extra"] = {"long_sequence": bench_long_e4m3(), "kda_int8g64_tok": bench_kda_tok(),
+                         "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd()}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["d"], w)
     else:

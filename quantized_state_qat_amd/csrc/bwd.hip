@@ -1,194 +1,255 @@
 // Straight-through backward of the recurrence.
 //
-// One workgroup per (sequence, head, 64-column value tile), the same lane/row layout as
-// the forward.  Chunks of C = ckpt_interval tokens are processed last to first:
-//   phase A  recompute the chunk from its checkpoint with the forward's own device code
-//            (la_recur.hpp), spilling the state entering each token and (u, delta) of each
-//            token to a per-workgroup workspace;
-//   phase B  walk the chunk backwards with the adjoint lambda = dL/dS in VGPRs.
-// Per token (general form of la_recur.hpp: S~ = diag(a) S, u = S~^T kp, S' = S~ + ku delta^T,
-// o = S'^T qq, identity straight-through gradient through the quantizer):
+// One workgroup per (sequence, head, 64-column value tile) in the token layout of
+// la_tok.hpp (eight waves, lane j = column j, wave w = key rows [w R, (w+1) R)).  Chunks of
+// C = ckpt_interval tokens are processed last to first, each in blocks of eight tokens:
+//   phase A  recompute the chunk from its checkpoint with the forward's own token step,
+//            storing the state entering every fourth token in the workspace;
+//   phase B  for each group of four tokens, last to first: recompute it from the stored
+//            state, keeping the state entering every token in registers, then walk it
+//            backwards with the adjoint lambda = dL/dS in registers.
+// A block's token records (la_tok.hpp) are published once per pass by its eight waves (wave w:
+// token w of the block), and the next block's inputs are fetched while a block is processed.
+// Per token (S~ = diag(a) S, u = S~^T k, S' = S~ + ku delta^T, o = S'^T qq; the quantizer
+// passes the gradient through unchanged):
 //   dS'    = lambda + qq do^T
-//   dqq    = S' do                        (row sums over value columns)
+//   dqq    = S' do                        (row sums over the value columns)
 //   ddelta = dS'^T ku,  dv = beta ddelta, du = -beta ddelta, dbeta = ddelta . (v - u)
 //   dku    = dS' delta,  dkp = S~ du      (row sums)
 //   dS~    = dS' + kp du^T
 //   da_i   = sum_j S_ij dS~_ij,  dg = a da (KDA per row; GDN summed over the state)
 //   lambda = diag(a) dS~
-// Row sums are partial over the tile's 64 columns; they are written per value tile and
-// summed in a fixed order by bwd_reduce_kernel, which also maps the rotated-domain key and
-// query gradients back (dk = Hu (dku + dkp / d_k), dq = Hu dqq / d_k) in Hadamard mode.
-#include "la_recur.hpp"
+// In Hadamard mode the state is carried rotated, Y = Hu S: ku = Hu k, kp = Hu k / d_k,
+// qq = Hu q / d_k, and lambda is dL/dY.  Row sums are partial over the
+// tile's 64 columns; they are written per value tile and summed in a fixed order by
+// bwd_reduce_kernel, which also maps the rotated-domain key and query gradients back
+// (dk = Hu (dku + dkp / d_k), dq = Hu dqq / d_k).
+#include "la_tok.hpp"
 
 namespace la {
 
-Params make_params(const la_config& c);
+TokParams make_tok_params(const la_config& c);
 
-// Sum over the 64 lanes of x[i] for every i < R, delivered transposed: afterwards lane L
-// holds the total of row rowsum_row<R>(L).  A reduce-scatter butterfly: at each step a lane
-// keeps one half of its vector and adds the partner's copy of that half.
-template <int R>
-__device__ __forceinline__ float rowsum(float (&x)[R], int lane) {
+constexpr int kBlkTok = kTokWaves;  // tokens per block (one record per wave)
+constexpr int kSubTok = 4;          // tokens per stored state: phase B keeps kSubTok states live
+
+// Partial-sum record of one token and value tile: dqq rows, dku + c1 dkp rows, the gate term
+// (KDA: a_i da_i per row; GDN: a times one partial sum per wave) and dbeta.
+template <int DK, bool KDA>
+struct PartLayout {
+    static constexpr int GW = KDA ? DK : kTokWaves;
+    static constexpr int PW = 2 * DK + GW + 1;
+};
+
+// One token of the adjoint.  st: the state entering the token; u, dl: its u and delta;
+// lam: dL/dS_t on entry, dL/dS_{t-1} on return.
+template <int DK, bool KDA, bool HAD>
+__device__ __forceinline__ void tok_adjoint(const float (&st)[DK / kTokWaves], float u, float dl,
+                                            const TokOps<DK, KDA>& op, const float* ga_row, float (&lam)[DK / kTokWaves],
+                                            float2 (*red)[kTokCols], int w, int lane, float* part, float* dv_out,
+                                            bool writer) {
+    constexpr int R = DK / kTokWaves;
+    constexpr float c1 = HAD ? 1.0f / DK : 1.0f;
+    constexpr int GW = PartLayout<DK, KDA>::GW;
+    const int row = w * R + reduce_scatter_row<R, 64>(lane);
+    float sa[R], x[R];
+    float pd = 0.0f;
 #pragma unroll
-    for (int st = 0; (R >> st) > 1; st++) {
-        const int len = R >> st, half = len / 2, mask = 32 >> st;
-        const bool up = (lane & mask) != 0;
-#pragma unroll
-        for (int i = 0; i < half; i++) {
-            float send = up ? x[i] : x[i + half];
-            float keep = up ? x[i + half] : x[i];
-            x[i] = keep + xor_shfl(send, mask);
-        }
+    for (int m = 0; m < R; m++) {
+        sa[m] = (KDA ? op.ar[m] : op.a) * st[m];                     // S~
+        const float spm = __builtin_fmaf(op.kr[m], dl, sa[m]);       // S' (before rounding)
+        lam[m] = __builtin_fmaf(op.qr[m] * c1, op.dj, lam[m]);       // dS' = lambda + qq do^T
+        x[m] = spm * op.dj;
+        pd = __builtin_fmaf(lam[m], op.kr[m], pd);
     }
-    float y = x[0];
+    red[w][lane] = make_float2(pd, 0.0f);
+    __syncthreads();
+    float r[kTokWaves];
 #pragma unroll
-    for (int m = (64 / R) / 2; m >= 1; m >>= 1) y += xor_shfl(y, m);
-    return y;
-}
-
-template <int R>
-__device__ __forceinline__ int rowsum_row(int lane) {
-    int row = 0;
+    for (int i = 0; i < kTokWaves; i++) r[i] = red[i][lane].x;
+    float ddel = r[0];
 #pragma unroll
-    for (int st = 0; (R >> st) > 1; st++) row += ((lane >> (5 - st)) & 1) * (R >> (st + 1));
-    return row;
+    for (int i = 1; i < kTokWaves; i++) ddel += r[i];
+    const float x1 = reduce_scatter<OpAdd, R, 64>(x, lane);
+    const float du = -op.beta * ddel;
+#pragma unroll
+    for (int m = 0; m < R; m++) {
+        x[m] = __builtin_fmaf(lam[m], dl, c1 * (sa[m] * du));       // dku + c1 dkp
+        lam[m] = __builtin_fmaf(op.kr[m] * c1, du, lam[m]);          // dS~ = dS' + kp du^T
+    }
+    const float x2 = reduce_scatter<OpAdd, R, 64>(x, lane);
+    part[row] = x1;
+    part[DK + row] = x2;
+    if (KDA) {
+#pragma unroll
+        for (int m = 0; m < R; m++) x[m] = st[m] * lam[m];
+        const float x3 = reduce_scatter<OpAdd, R, 64>(x, lane);
+        part[2 * DK + row] = ga_row[row] * x3;
+    } else {
+        float gp = 0.0f;
+#pragma unroll
+        for (int m = 0; m < R; m++) gp = __builtin_fmaf(st[m], lam[m], gp);
+        gp = wave_sum(gp);
+        if (lane == 0) part[2 * DK + w] = op.a * gp;
+    }
+#pragma unroll
+    for (int m = 0; m < R; m++) lam[m] = (KDA ? op.ar[m] : op.a) * lam[m];
+    if (writer) {
+        *dv_out = op.beta * ddel;
+        const float db = wave_sum(ddel * (op.vj - u));
+        if (lane == 0) part[2 * DK + GW] = db;
+    }
 }
 
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
-__global__ __launch_bounds__(kThreads) void bwd_kernel(Params p, BwdArgs a) {
-    constexpr int R = DK / 4;
-    constexpr int GW = KDA ? DK : 1;
-    constexpr int PW = 2 * DK + GW + 1;
-    constexpr float c1 = HAD ? 1.0f / DK : 1.0f;
-    __shared__ Smem<DK> sm;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdArgs a) {
+    constexpr int R = DK / kTokWaves;
+    constexpr int PW = PartLayout<DK, KDA>::PW;
+    __shared__ TokRing<DK, KDA, true> ring;
+    __shared__ float2 red[2][kTokWaves][kTokCols];
+    __shared__ TokQdqShared<DK, QMODE, G> qsh;
+    __shared__ float tile[HAD ? DK * kTokCols : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int T = p.T, H = p.H, DV = p.dv, C = p.ckpt_interval;
-    const int NB = DV / kTileCols;
-    const int col = blk * kTileCols + lane;
+    const int NB = DV / kTokCols;
+    const int col = blk * kTokCols + lane;
     const size_t bh = static_cast<size_t>(b) * H + h;
     const size_t state_off = bh * DK * DV;
     const size_t wg = bh * NB + blk;
     const size_t ntok = static_cast<size_t>(p.B) * T * H;
-    float* wsS = a.ws_states + wg * static_cast<size_t>(C) * DK * kTileCols;
-    float* wsV = a.ws_vecs + wg * static_cast<size_t>(C) * 4 * 2 * kTileCols;
-    const int my_row = w * R + rowsum_row<R>(lane);
-    const bool row_writer = (lane & (64 / R - 1)) == 0;
+    const size_t tok0 = static_cast<size_t>(b) * T * H + h;
+    const int nsub = (C + kSubTok - 1) / kSubTok;
+    float* wsS = a.ws_states + wg * static_cast<size_t>(nsub) * DK * kTokCols;
+    const TokInputs in{a.q, a.k, a.v, a.g, a.beta, a.dout};
 
     float lam[R];
 #pragma unroll
     for (int m = 0; m < R; m++)
         lam[m] = a.dST ? a.dST[state_off + static_cast<size_t>(w * R + m) * DV + col] : 0.0f;
-    if (HAD && !p.rot) rotate_state<DK>(sm, lam, 1.0f / DK);  // dL/dY = Hu dL/dS / d_k
+    if (HAD && !p.rot) tok_rotate<DK>(lam, tile, w, lane, 1.0f / DK);  // dL/dY = Hu dL/dS / d_k
 
+    // Blocks in processing order: chunk c from last to first; in each, phase A over blocks
+    // j = 0 .. nb-1, then phase B over j = nb-1 .. 0.  The inputs of the next block in this
+    // order are fetched while a block is processed.
+    auto nblocks = [&](int c) { return (min(T, (c + 1) * C) - c * C + kBlkTok - 1) / kBlkTok; };
+    TokFetch<DK, KDA, true> f;
+    auto fetch = [&](int c, int j) __attribute__((always_inline)) {
+        if (c < 0) return;
+        const int t = c * C + kBlkTok * j + w;
+        if (t < min(T, (c + 1) * C)) f.fetch(in, p, tok0 + static_cast<size_t>(t) * H, col, lane);
+    };
+    // publish block (c, j) from the fetched words, fetch (nc, nj), make the records visible
+    auto publish = [&](int nt, int nc, int nj) __attribute__((always_inline)) {
+        __syncthreads();  // the previous block's records are no longer read
+        if (w < nt) f.template publish<HAD>(ring, w, p, lane);
+        fetch(nc, nj);
+        __syncthreads();
+    };
+
+    fetch(p.nck - 1, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    int rp = 0;
 #pragma unroll 1
     for (int c = p.nck - 1; c >= 0; c--) {
-        const int t0 = c * C;
-        const int t1 = min(T, t0 + C);
-        // ---------------- phase A: recompute the chunk's carried states
-        float s[R];
-        const float* ck = a.ckpts + (bh * p.nck + c) * DK * DV;
+        const int t0 = c * C, t1 = min(T, t0 + C);
+        const int nb = nblocks(c);
+        // ---------------- phase A: advance through the chunk, storing the state entering
+        // every fourth token (the chunk's first state is its checkpoint)
+        {
+            float s[R];
+            const float* ck = a.ckpts + (bh * p.nck + c) * DK * DV;
 #pragma unroll
-        for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(w * R + m) * DV + col];
+            for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(w * R + m) * DV + col];
 #pragma unroll 1
-        for (int t = t0; t < t1; t++) {
-            float* dst = wsS + static_cast<size_t>(t - t0) * DK * kTileCols;
-#pragma unroll
-            for (int m = 0; m < R; m++) dst[(w * R + m) * kTileCols + lane] = s[m];
-            const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
-            float vj = load_elem(a.v, tok * DV + col, p.qkv_dt);
-            stage_token<DK, HAD, KDA>(sm, a.q, a.k, a.g, a.beta, tok, p.qkv_dt, p.gate_dt);
-            float u, d, o;
-            bool qnow = (QMODE != LA_QDQ_NONE) && is_qdq_point(t, T, p.qdq_interval);
-            token_step<DK, QMODE, G>(sm, s, vj, qnow, u, d, o);
-            float* vec = wsV + (static_cast<size_t>(t - t0) * 4 + w) * 2 * kTileCols;
-            vec[lane] = u;
-            vec[kTileCols + lane] = d;
-        }
-        // ---------------- phase B: reverse adjoint over the chunk
+            for (int j = 0; j < nb; j++) {
+                const int tb = t0 + kBlkTok * j;
+                const int nt = min(kBlkTok, t1 - tb);
+                if (j + 1 < nb) publish(nt, c, j + 1);
+                else publish(nt, c, j);  // phase B starts with the same block
 #pragma unroll 1
-        for (int t = t1 - 1; t >= t0; t--) {
-            const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
-            stage_token<DK, HAD, KDA>(sm, a.q, a.k, a.g, a.beta, tok, p.qkv_dt, p.gate_dt);
-            const float* src = wsS + static_cast<size_t>(t - t0) * DK * kTileCols;
-            float sp[R];
+                for (int i = 0; i < nt; i++) {
+                    if ((i % kSubTok) == 0 && (j > 0 || i > 0)) {
+                        float* dst = wsS + static_cast<size_t>(kBlkTok / kSubTok * j + i / kSubTok) * DK * kTokCols;
 #pragma unroll
-            for (int m = 0; m < R; m++) sp[m] = src[(w * R + m) * kTileCols + lane];
-            const float* vec = wsV + (static_cast<size_t>(t - t0) * 4 + w) * 2 * kTileCols;
-            const float u = vec[lane], d = vec[kTileCols + lane];
-            const float vj = load_elem(a.v, tok * DV + col, p.qkv_dt);
-            const float doj = a.dout[tok * DV + col];
-            const float beta = sm.beta;
-            float x[R];
-            // dS' = lambda + qq do^T ;  dqq = S' do  (S' recomputed exactly as the forward does)
-#pragma unroll
-            for (int m = 0; m < R; m++) {
-                const int row = w * R + m;
-                lam[m] = __builtin_fmaf(sm.qraw[row], doj, lam[m]);
-                float spr = __builtin_fmaf(sm.ku[row], d, sm.a[row] * sp[m]);
-                x[m] = spr * doj;
-            }
-            float X1 = rowsum<R>(x, lane);
-            // ddelta = dS'^T ku (column sums over the key axis)
-            float pd = 0.0f;
-#pragma unroll
-            for (int m = 0; m < R; m++) pd = __builtin_fmaf(lam[m], sm.ku[w * R + m], pd);
-            sm.red[w][lane] = make_float2(pd, 0.0f);
-            __syncthreads();
-            const float ddel = ((sm.red[0][lane].x + sm.red[1][lane].x) + sm.red[2][lane].x) + sm.red[3][lane].x;
-            const float du = -beta * ddel;
-            // dku + c1 dkp = dS' delta + c1 S~ du
-#pragma unroll
-            for (int m = 0; m < R; m++) {
-                const int row = w * R + m;
-                x[m] = __builtin_fmaf(lam[m], d, c1 * ((sm.a[row] * sp[m]) * du));
-            }
-            float X2 = rowsum<R>(x, lane);
-            // dS~ = dS' + kp du^T
-#pragma unroll
-            for (int m = 0; m < R; m++) lam[m] = __builtin_fmaf(sm.kraw[w * R + m], du, lam[m]);
-            float X3 = 0.0f;
-            if (KDA) {
-#pragma unroll
-                for (int m = 0; m < R; m++) x[m] = sp[m] * lam[m];
-                X3 = rowsum<R>(x, lane);
-            } else {
-                float gp = 0.0f;
-#pragma unroll
-                for (int m = 0; m < R; m++) gp = __builtin_fmaf(sp[m], lam[m], gp);
-                gp = wave_sum(gp);
-                if (lane == 0) sm.scal[w] = gp;
-                __syncthreads();
-            }
-            float* part = a.ws_part + (static_cast<size_t>(blk) * ntok + tok) * PW;
-            if (row_writer) {
-                part[my_row] = X1;
-                part[DK + my_row] = X2;
-                if (KDA) part[2 * DK + my_row] = sm.a[my_row] * X3;
-            }
-            if (w == 0) {
-                a.dv[tok * DV + col] = beta * ddel;
-                float db = wave_sum(ddel * (vj - u));
-                if (lane == 0) {
-                    part[2 * DK + GW] = db;
-                    if (!KDA) part[2 * DK] = sm.a[0] * (((sm.scal[0] + sm.scal[1]) + sm.scal[2]) + sm.scal[3]);
+                        for (int m = 0; m < R; m++) dst[(w * R + m) * kTokCols + lane] = s[m];
+                    }
+                    TokOps<DK, KDA> op;
+                    tok_read<DK, KDA, true>(op, ring, i, w, lane);
+                    float u, dl, o;
+                    tok_step<DK, KDA, HAD>(s, op, red[rp], w, lane, u, dl, o);
+                    rp ^= 1;
+                    const int t = tb + i;
+                    if (QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1))
+                        tok_qdq<DK, QMODE, G>(s, qsh, w, lane);
                 }
             }
-            // lambda = diag(a) dS~  (= dL/dS_{t-1})
+        }
+        // ---------------- phase B: per group of four tokens, last first: recompute it keeping
+        // every entering state, then the adjoint
+#pragma unroll 1
+        for (int j = nb - 1; j >= 0; j--) {
+            const int tb = t0 + kBlkTok * j;
+            const int nt = min(kBlkTok, t1 - tb);
+            if (j > 0) publish(nt, c, j - 1);
+            else publish(nt, c - 1, 0);
+#pragma unroll 1
+            for (int hh = (nt - 1) / kSubTok; hh >= 0; hh--) {
+                const int i0 = kSubTok * hh, n = min(kSubTok, nt - i0);
+                float s[R];
+                if (j == 0 && hh == 0) {
+                    const float* ck = a.ckpts + (bh * p.nck + c) * DK * DV;
 #pragma unroll
-            for (int m = 0; m < R; m++) lam[m] = sm.a[w * R + m] * lam[m];
+                    for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(w * R + m) * DV + col];
+                } else {
+                    const float* src = wsS + static_cast<size_t>(kBlkTok / kSubTok * j + hh) * DK * kTokCols;
+#pragma unroll
+                    for (int m = 0; m < R; m++) s[m] = src[(w * R + m) * kTokCols + lane];
+                }
+                float st[kSubTok][R];
+                float uu[kSubTok], dd[kSubTok];
+#pragma unroll
+                for (int i = 0; i < kSubTok; i++) {
+                    if (i < n) {
+#pragma unroll
+                        for (int m = 0; m < R; m++) st[i][m] = s[m];
+                        TokOps<DK, KDA> op;
+                        tok_read<DK, KDA, true>(op, ring, i0 + i, w, lane);
+                        float o;
+                        tok_step<DK, KDA, HAD>(s, op, red[rp], w, lane, uu[i], dd[i], o);
+                        rp ^= 1;
+                        const int t = tb + i0 + i;
+                        if (QMODE != LA_QDQ_NONE && i + 1 < n && (((t + 1) % p.qdq_interval) == 0 || t == T - 1))
+                            tok_qdq<DK, QMODE, G>(s, qsh, w, lane);
+                    }
+                }
+#pragma unroll
+                for (int i = kSubTok - 1; i >= 0; i--) {
+                    if (i < n) {
+                        TokOps<DK, KDA> op;
+                        tok_read<DK, KDA, true>(op, ring, i0 + i, w, lane);
+                        const size_t tok = tok0 + static_cast<size_t>(tb + i0 + i) * H;
+                        float* part = a.ws_part + (static_cast<size_t>(blk) * ntok + tok) * PW;
+                        tok_adjoint<DK, KDA, HAD>(st[i], uu[i], dd[i], op, ring.ga[i0 + i], lam, red[rp], w, lane,
+                                                  part, a.dv + tok * DV + col, w == i0 + i);
+                        rp ^= 1;
+                    }
+                }
+            }
         }
     }
-    if (HAD && !p.rot) rotate_state<DK>(sm, lam, 1.0f);  // dL/dS = Hu dL/dY
+    if (HAD && !p.rot) tok_rotate<DK>(lam, tile, w, lane, 1.0f);  // dL/dS = Hu dL/dY
 #pragma unroll
     for (int m = 0; m < R; m++) a.dS0[state_off + static_cast<size_t>(w * R + m) * DV + col] = lam[m];
 }
 
 // Sum the per-tile partials in tile order and write dq, dk, dg, dbeta.  One wave per token.
 template <int DK, bool HAD, bool KDA>
-__global__ __launch_bounds__(64) void bwd_reduce_kernel(Params p, BwdArgs a, int NB) {
-    constexpr int GW = KDA ? DK : 1;
-    constexpr int PW = 2 * DK + GW + 1;
+__global__ __launch_bounds__(64) void bwd_reduce_kernel(TokParams p, BwdArgs a, int NB) {
+    constexpr int GW = PartLayout<DK, KDA>::GW;
+    constexpr int PW = PartLayout<DK, KDA>::PW;
     constexpr int NV = (DK + 63) / 64;
     const int lane = threadIdx.x;
     const size_t tok = blockIdx.x;
@@ -246,7 +307,8 @@ __global__ __launch_bounds__(64) void bwd_reduce_kernel(Params p, BwdArgs a, int
         }
     } else if (lane == 0) {
         float acc = 0.0f;
-        for (int nb = 0; nb < NB; nb++) acc += a.ws_part[(static_cast<size_t>(nb) * ntok + tok) * PW + 2 * DK];
+        for (int nb = 0; nb < NB; nb++)
+            for (int i = 0; i < GW; i++) acc += a.ws_part[(static_cast<size_t>(nb) * ntok + tok) * PW + 2 * DK + i];
         a.dg[tok] = acc;
     }
     if (lane == 0) {
@@ -256,45 +318,43 @@ __global__ __launch_bounds__(64) void bwd_reduce_kernel(Params p, BwdArgs a, int
     }
 }
 
+namespace {
+
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
-static hipError_t launch_bwd_t(const la_config& c, const BwdArgs& a, hipStream_t s) {
-    Params p = make_params(c);
-    dim3 grid(c.d_v / kTileCols, c.H, c.B);
-    hipLaunchKernelGGL((bwd_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(kThreads), 0, s, p, a);
+hipError_t launch_bwd_t(const la_config& c, const BwdArgs& a, hipStream_t s) {
+    const TokParams p = make_tok_params(c);
+    dim3 grid(c.d_v / kTokCols, c.H, c.B);
+    hipLaunchKernelGGL((bwd_tok_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(kTokThreads), 0, s, p, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    size_t ntok = static_cast<size_t>(c.B) * c.T * c.H;
+    const size_t ntok = static_cast<size_t>(c.B) * c.T * c.H;
     if (ntok == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_reduce_kernel<DK, HAD, KDA>), dim3(static_cast<unsigned>(ntok)), dim3(64), 0, s, p,
-                       a, c.d_v / kTileCols);
+    hipLaunchKernelGGL((bwd_reduce_kernel<DK, HAD, KDA>), dim3(static_cast<unsigned>(ntok)), dim3(64), 0, s, p, a,
+                       c.d_v / kTokCols);
     return hipGetLastError();
 }
 
-template <int DK>
-static hipError_t launch_bwd_dk(const la_config& c, const BwdArgs& a, hipStream_t s) {
-    const bool kda = c.gate == LA_GATE_KEY;
-    if (c.qdq == LA_QDQ_NONE)
-        return kda ? launch_bwd_t<DK, LA_QDQ_NONE, 1, false, true>(c, a, s)
-                   : launch_bwd_t<DK, LA_QDQ_NONE, 1, false, false>(c, a, s);
-    if (c.qdq == LA_QDQ_E4M3_TILE)
-        return kda ? launch_bwd_t<DK, LA_QDQ_E4M3_TILE, 64, false, true>(c, a, s)
-                   : launch_bwd_t<DK, LA_QDQ_E4M3_TILE, 64, false, false>(c, a, s);
-    if (c.hadamard) {
-        switch (c.group) {
-            case 16: return launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 16, true, false>(c, a, s);
-            case 32: return launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 32, true, false>(c, a, s);
-            default: return launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 64, true, false>(c, a, s);
-        }
+template <int DK, bool HAD, bool KDA>
+hipError_t launch_bwd_q(const la_config& c, const BwdArgs& a, hipStream_t s) {
+    if (!HAD) {
+        if (c.qdq == LA_QDQ_NONE) return launch_bwd_t<DK, LA_QDQ_NONE, 16, HAD, KDA>(c, a, s);
+        if (c.qdq == LA_QDQ_E4M3_TILE) return launch_bwd_t<DK, LA_QDQ_E4M3_TILE, 64, HAD, KDA>(c, a, s);
     }
     switch (c.group) {
-        case 16: return kda ? launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 16, false, true>(c, a, s)
-                            : launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 16, false, false>(c, a, s);
-        case 32: return kda ? launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 32, false, true>(c, a, s)
-                            : launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 32, false, false>(c, a, s);
-        default: return kda ? launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 64, false, true>(c, a, s)
-                            : launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 64, false, false>(c, a, s);
+        case 16: return launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 16, HAD, KDA>(c, a, s);
+        case 32: return launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 32, HAD, KDA>(c, a, s);
+        default: return launch_bwd_t<DK, LA_QDQ_INT8_GROUP, 64, HAD, KDA>(c, a, s);
     }
 }
+
+template <int DK>
+hipError_t launch_bwd_dk(const la_config& c, const BwdArgs& a, hipStream_t s) {
+    if (c.hadamard) return launch_bwd_q<DK, true, false>(c, a, s);
+    if (c.gate == LA_GATE_KEY) return launch_bwd_q<DK, false, true>(c, a, s);
+    return launch_bwd_q<DK, false, false>(c, a, s);
+}
+
+}  // namespace
 
 hipError_t launch_bwd(const la_config& c, const BwdArgs& a, hipStream_t s) {
     switch (c.d_k) {

@@ -1,0 +1,142 @@
+// Token forward: every configuration the regrouped kernels do not take (per-key gates,
+// the Hadamard rotation, a rounding point after every token or at intervals that do not
+// fall on their block ends).  The layout and the per-token step are those of la_tok.hpp.
+//
+// Token inputs arrive in blocks of eight: wave w fetches token 8 J + w of block J two blocks
+// ahead (raw words in registers), publishes it into the LDS ring one block ahead, and every
+// wave reads its rows of a token's record at the end of the previous token.  The only
+// barrier per token is the one inside tok_step (plus one more for an E4M3 rounding point).
+#include "la_tok.hpp"
+
+namespace la {
+
+TokParams make_tok_params(const la_config& c) {
+    TokParams p;
+    p.B = c.B; p.T = c.T; p.H = c.H; p.dk = c.d_k; p.dv = c.d_v;
+    p.qkv_dt = c.qkv_dtype; p.gate_dt = c.gate_dtype; p.out_dt = c.out_dtype;
+    p.qdq_interval = c.qdq == LA_QDQ_NONE ? 1 : c.qdq_interval;
+    p.ckpt_interval = c.ckpt_interval > 0 ? c.ckpt_interval : 1;
+    p.nck = n_ckpts(c);
+    p.rot = c.hadamard && c.state_rotated;
+    return p;
+}
+
+template <int DK, int QMODE, int G, bool HAD, bool KDA>
+__global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdArgs a) {
+    constexpr int R = DK / kTokWaves;
+    __shared__ TokRing<DK, KDA, false> ring;
+    __shared__ float2 red[2][kTokWaves][kTokCols];
+    __shared__ TokQdqShared<DK, QMODE, G> qsh;
+    __shared__ float tile[HAD ? DK * kTokCols : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int T = p.T, H = p.H, DV = p.dv;
+    const int col = blk * kTokCols + lane;
+    const size_t bh = static_cast<size_t>(b) * H + h;
+    const size_t state_off = bh * DK * DV;
+    const size_t tok0 = static_cast<size_t>(b) * T * H + h;  // token 0 of this (b, h)
+    const TokInputs in{a.q, a.k, a.v, a.g, a.beta, nullptr};
+
+    TokFetch<DK, KDA, false> f;
+    auto fetch = [&](int u) __attribute__((always_inline)) {
+        if (u < T) f.fetch(in, p, tok0 + static_cast<size_t>(u) * H, col, lane);
+    };
+    auto publish = [&](int u) __attribute__((always_inline)) {
+        if (u < T) f.template publish<HAD>(ring, u % kTokRing, p, lane);
+    };
+
+    float s[R];
+#pragma unroll
+    for (int m = 0; m < R; m++)
+        s[m] = a.S0 ? a.S0[state_off + static_cast<size_t>(w * R + m) * DV + col] : 0.0f;
+    if (HAD && !p.rot) tok_rotate<DK>(s, tile, w, lane, 1.0f);
+
+    fetch(w);
+    publish(w);
+    // Settle every load issued so far before the first prefetch: otherwise the compiler's
+    // wait analysis keeps them pending around the token loop and waits for all memory
+    // traffic, prefetches included, at every token.
+    __builtin_amdgcn_s_waitcnt(0);
+    fetch(kTokWaves + w);
+    __syncthreads();
+
+    TokOps<DK, KDA> op;
+    if (T > 0) tok_read<DK, KDA, false>(op, ring, 0, w, lane);
+    int ck_next = a.ckpts ? 0 : T;                                        // next checkpoint token
+    int q_next = QMODE != LA_QDQ_NONE ? min(p.qdq_interval, T) - 1 : T;  // next rounding token
+    size_t tok = tok0;
+
+#pragma unroll 1
+    for (int t = 0; t < T; t++, tok += H) {
+        if ((t & (kTokWaves - 1)) == kTokWaves - 2) {  // publish the next block, fetch the one after
+            const int u = t + 2 + w;
+            publish(u);
+            fetch(u + kTokWaves);
+        }
+        if (t == ck_next) {
+            // checkpoints hold the carried state as the loop carries it (rotated in Hadamard mode)
+            float* dst = a.ckpts + (bh * p.nck + t / p.ckpt_interval) * DK * DV;
+#pragma unroll
+            for (int m = 0; m < R; m++) dst[static_cast<size_t>(w * R + m) * DV + col] = s[m];
+            ck_next += p.ckpt_interval;
+        }
+        float u, delta, o;
+        tok_step<DK, KDA, HAD>(s, op, red[t & 1], w, lane, u, delta, o);
+        if (a.o && w == (t & (kTokWaves - 1))) store_elem(a.o, tok * DV + col, p.out_dt, o);
+        if (t + 1 < T) tok_read<DK, KDA, false>(op, ring, (t + 1) % kTokRing, w, lane);
+        if (t == q_next) {
+            q_next = min(q_next + p.qdq_interval, T - 1);
+            if (q_next == t) q_next = T;
+            tok_qdq<DK, QMODE, G>(s, qsh, w, lane);
+        }
+    }
+    if (a.ST) {
+        if (HAD && !p.rot) tok_rotate<DK>(s, tile, w, lane, 1.0f / DK);
+#pragma unroll
+        for (int m = 0; m < R; m++) a.ST[state_off + static_cast<size_t>(w * R + m) * DV + col] = s[m];
+    }
+}
+
+namespace {
+
+template <int DK, int QMODE, int G, bool HAD, bool KDA>
+hipError_t launch_tok_t(const la_config& c, const FwdArgs& a, hipStream_t s) {
+    dim3 grid(c.d_v / kTokCols, c.H, c.B);
+    hipLaunchKernelGGL((fwd_tok_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(kTokThreads), 0, s, make_tok_params(c), a);
+    return hipGetLastError();
+}
+
+template <int DK, bool HAD, bool KDA>
+hipError_t launch_tok_q(const la_config& c, const FwdArgs& a, hipStream_t s) {
+    if (!HAD) {
+        if (c.qdq == LA_QDQ_NONE) return launch_tok_t<DK, LA_QDQ_NONE, 16, HAD, KDA>(c, a, s);
+        if (c.qdq == LA_QDQ_E4M3_TILE) return launch_tok_t<DK, LA_QDQ_E4M3_TILE, 64, HAD, KDA>(c, a, s);
+    }
+    switch (c.group) {
+        case 16: return launch_tok_t<DK, LA_QDQ_INT8_GROUP, 16, HAD, KDA>(c, a, s);
+        case 32: return launch_tok_t<DK, LA_QDQ_INT8_GROUP, 32, HAD, KDA>(c, a, s);
+        default: return launch_tok_t<DK, LA_QDQ_INT8_GROUP, 64, HAD, KDA>(c, a, s);
+    }
+}
+
+template <int DK>
+hipError_t launch_tok_dk(const la_config& c, const FwdArgs& a, hipStream_t s) {
+    if (c.hadamard) return launch_tok_q<DK, true, false>(c, a, s);
+    if (c.gate == LA_GATE_KEY) return launch_tok_q<DK, false, true>(c, a, s);
+    return launch_tok_q<DK, false, false>(c, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_tok(const la_config& c, const FwdArgs& a, hipStream_t s) {
+    switch (c.d_k) {
+        case 16: return launch_tok_dk<16>(c, a, s);
+        case 32: return launch_tok_dk<32>(c, a, s);
+        case 64: return launch_tok_dk<64>(c, a, s);
+        default: return launch_tok_dk<128>(c, a, s);
+    }
+}
+
+}  // namespace la

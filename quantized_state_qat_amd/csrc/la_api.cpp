@@ -92,16 +92,14 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-    size_t states, vecs, part, ckpts, total;
+    size_t states, part, ckpts, total;
 };
 
 WsLayout ws_layout(const la_config& c) {
     WsLayout L;
     const size_t nwg = static_cast<size_t>(c.B) * c.H * la::n_value_blocks(c);
-    const size_t C = static_cast<size_t>(c.ckpt_interval);
     L.states = 0;
-    L.vecs = round_up(nwg * C * c.d_k * 64 * sizeof(float));
-    L.part = L.vecs + round_up(nwg * C * 4 * 2 * 64 * sizeof(float));
+    L.part = round_up(nwg * static_cast<size_t>(la::n_sub_states(c)) * c.d_k * 64 * sizeof(float));
     L.ckpts = L.part + round_up(static_cast<size_t>(la::n_value_blocks(c)) * c.B * c.T * c.H *
                                 la::part_width(c) * sizeof(float));
     L.total = L.ckpts + round_up(static_cast<size_t>(c.B) * c.H * la::n_ckpts(c) * c.d_k * c.d_v * sizeof(float));
@@ -227,8 +225,7 @@ la_status la_recurrent_bwd_ste(const la_config* cfg, const void* q, const void* 
         ck = ckw;
     }
     la::BwdArgs a{q, k, v, g, beta, ck, dout, dS_T, dq, dk, dv, dg, dbeta, dS0,
-                  reinterpret_cast<float*>(ws + L.states), reinterpret_cast<float*>(ws + L.vecs),
-                  reinterpret_cast<float*>(ws + L.part)};
+                  reinterpret_cast<float*>(ws + L.states), reinterpret_cast<float*>(ws + L.part)};
     return hip_status(la::launch_bwd(c, a, s), "la_recurrent_bwd_ste launch");
 }
 

@@ -48,9 +48,8 @@ struct BwdArgs {
     float* dg;
     float* dbeta;
     float* dS0;
-    float* ws_states;    // per workgroup: chunk x d_k x 64 carried states
-    float* ws_vecs;      // per workgroup: chunk x 2 x 64 (u, delta)
-    float* ws_part;      // per value block partial row sums
+    float* ws_states;    // per workgroup: the state entering every 4th token of a chunk (d_k x 64 each)
+    float* ws_part;      // per value tile and token: partial row sums
 };
 
 // Host-side layout helpers (shared by the ABI and the launchers).
@@ -58,7 +57,11 @@ inline int n_value_blocks(const la_config& c) { return c.d_v / 64; }
 inline int n_ckpts(const la_config& c) {
     return c.ckpt_interval > 0 ? (c.T + c.ckpt_interval - 1) / c.ckpt_interval : 0;
 }
-inline int part_width(const la_config& c) { return 2 * c.d_k + (c.gate == LA_GATE_KEY ? c.d_k : 1) + 1; }
+// Backward partial sums per (value tile, token): two d_k rows, the gate term (KDA: one per
+// key row; GDN: one per wave of the eight-wave token layout) and beta.
+inline int part_width(const la_config& c) { return 2 * c.d_k + (c.gate == LA_GATE_KEY ? c.d_k : 8) + 1; }
+// Backward states per workgroup: the state entering every fourth token of a chunk.
+inline int n_sub_states(const la_config& c) { return (c.ckpt_interval + 3) / 4; }
 
 hipError_t launch_decode(const la_config& c, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fwd(const la_config& c, const FwdArgs& a, hipStream_t s);
@@ -69,6 +72,7 @@ bool fwd_mfma_eligible(const la_config& c);
 hipError_t launch_fwd_mfma(const la_config& c, const FwdArgs& a, hipStream_t s);
 bool fwd_wave_eligible(const la_config& c);
 hipError_t launch_fwd_wave(const la_config& c, const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_tok(const la_config& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_copy_state(const la_config& c, const float* src, float* dst, hipStream_t s);
 hipError_t launch_bwd(const la_config& c, const BwdArgs& a, hipStream_t s);
 

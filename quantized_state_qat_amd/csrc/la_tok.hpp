@@ -1,0 +1,432 @@
+// Per-token layout shared by the token forward kernel (fwd_tok.hip) and the backward's
+// recompute (bwd.hip): the two run exactly these functions, so a recompute meets the
+// forward's carried states and rounding decisions bit for bit.
+//
+// One workgroup per (sequence, head, 64-column value tile), eight waves: lane j holds value
+// column j of the tile, wave w holds key rows [w R, (w+1) R), R = d_k / 8, in registers.
+// Per token:
+//  * one wave has published the token's operands in an LDS ring (keys and queries, rotated
+//    by the Walsh-Hadamard transform in Hadamard mode; the gate, exp(g), per key row or
+//    scalar; beta; k . q; the tile's values), a block of eight tokens ahead of use;
+//  * the decayed state's projections onto the key and the query are in-lane chains over the
+//    wave's rows, and the eight waves' partial sums meet in LDS behind one barrier, summed in
+//    a fixed order;
+//  * the update is one FMA per element;
+//  * at a rounding point the INT8 group maxima are taken by a reduce-scatter across the
+//    lanes (each lane ends with the maximum of one (row, group)), the lane computes that
+//    group's scale and reciprocal once, and the wave reads all of them back through LDS.
+// In Hadamard mode the state is carried rotated, Y = Hu S (Hu the unnormalized Sylvester
+// matrix): the update is the same map with Hu k in place of k, projections scaled by 1/d_k
+// (an exact power of two), and the INT8 codec acts on Y directly.
+#pragma once
+
+#include "la_device.hpp"
+#include "la_internal.hpp"
+
+namespace la {
+
+constexpr int kTokWaves = 8;                  // waves per workgroup = tokens per block
+constexpr int kTokThreads = kTokWaves * 64;
+constexpr int kTokRing = 2 * kTokWaves;       // token records in the LDS ring
+constexpr int kTokCols = 64;                  // value columns per workgroup
+
+struct TokParams {
+    int B, T, H, dk, dv;
+    int qkv_dt, gate_dt, out_dt;
+    int qdq_interval, ckpt_interval, nck;
+    int rot;  // state tensors hold the rotated state (Hadamard mode)
+};
+
+// ------------------------------------------------------------------ lane reduce-scatter
+// Reduce N values per lane (x[0..N-1], value i belonging to row i) over aligned groups of
+// G lanes so that each lane ends with the reduction of one row over its group.  Each level
+// halves the values a lane carries: the lane keeps one half and combines it with its
+// partner's copy of that half.  Levels, in order: lanes 32 apart (permlane32 swap, G = 64),
+// 16 apart (permlane16 swap, G >= 32), then within each row of 16 lanes the DPP mirror
+// (lane i <-> 15 - i), half mirror (i <-> 7 - i within 8), and the quad exchanges i ^ 2 and
+// i ^ 1.  Once a lane carries a single value the remaining levels reduce it in place.
+// The row a lane ends with is reduce_scatter_row<N, G>(lane).
+struct OpMax {
+    static __device__ __forceinline__ float f(float a, float b) { return fmaxf(a, b); }
+};
+struct OpAdd {
+    static __device__ __forceinline__ float f(float a, float b) { return a + b; }
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// One swap level over lanes 32 (SW = 32) or 16 (SW = 16) apart.  After a permlane swap of
+// (A, B), A's register holds in the lower half of each lane pair the lane's own A and in the
+// upper half the partner's B, and B's register the partner's A and the lane's own B.
+template <class Op, int SW, int N>
+__device__ __forceinline__ void rs_swap_level(float* x) {
+    if constexpr (N == 1) {
+        const auto r = SW == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[0]), false, false)
+                                : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[0]), __float_as_uint(x[0]), false, false);
+        x[0] = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    } else {
+#pragma unroll
+        for (int i = 0; i < N / 2; i++) {
+            const auto r = SW == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + N / 2]), false, false)
+                                    : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i + N / 2]), false, false);
+            x[i] = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
+    }
+}
+
+// One DPP level: the partner differs from the lane in bit BIT of the lane index (and the
+// pattern keeps every bit above BIT within the row of 16).
+template <class Op, int CTRL, int BIT, int N>
+__device__ __forceinline__ void rs_dpp_level(float* x, int lane) {
+    if constexpr (N == 1) {
+        x[0] = Op::f(x[0], dpp_mov<CTRL>(x[0]));
+    } else {
+        const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+        for (int i = 0; i < N / 2; i++) {
+            const float send = hi ? x[i] : x[i + N / 2];
+            const float keep = hi ? x[i + N / 2] : x[i];
+            x[i] = Op::f(keep, dpp_mov<CTRL>(send));
+        }
+    }
+}
+
+constexpr int kCtrlMirror = 0x140, kCtrlHalfMirror = 0x141, kCtrlXor2 = 0x4E, kCtrlXor1 = 0xB1;
+
+template <class Op, int N, int G>
+__device__ __forceinline__ float reduce_scatter(float* x, int lane) {
+    static_assert(G == 16 || G == 32 || G == 64, "groups of 16, 32 or 64 lanes");
+    constexpr int N1 = G == 64 ? (N > 1 ? N / 2 : 1) : N;
+    constexpr int N2 = G >= 32 ? (N1 > 1 ? N1 / 2 : 1) : N1;
+    constexpr int N3 = N2 > 1 ? N2 / 2 : 1;
+    constexpr int N4 = N3 > 1 ? N3 / 2 : 1;
+    constexpr int N5 = N4 > 1 ? N4 / 2 : 1;
+    if constexpr (G == 64) rs_swap_level<Op, 32, N>(x);
+    if constexpr (G >= 32) rs_swap_level<Op, 16, N1>(x);
+    rs_dpp_level<Op, kCtrlMirror, 3, N2>(x, lane);
+    rs_dpp_level<Op, kCtrlHalfMirror, 2, N3>(x, lane);
+    rs_dpp_level<Op, kCtrlXor2, 1, N4>(x, lane);
+    rs_dpp_level<Op, kCtrlXor1, 0, N5>(x, lane);
+    return x[0];
+}
+
+// Row whose reduction lane `lane` holds after reduce_scatter<Op, N, G>: every level that
+// splits n > 1 values sends the lane to the upper half (offset n/2) when its bit is set.
+template <int N, int G>
+__device__ __forceinline__ int reduce_scatter_row(int lane) {
+    int row = 0, n = N;
+    if (G == 64) {
+        if (n > 1) { row += ((lane >> 5) & 1) * (n / 2); n /= 2; }
+    }
+    if (G >= 32) {
+        if (n > 1) { row += ((lane >> 4) & 1) * (n / 2); n /= 2; }
+    }
+    if (n > 1) { row += ((lane >> 3) & 1) * (n / 2); n /= 2; }
+    if (n > 1) { row += ((lane >> 2) & 1) * (n / 2); n /= 2; }
+    if (n > 1) { row += ((lane >> 1) & 1) * (n / 2); n /= 2; }
+    if (n > 1) { row += (lane & 1) * (n / 2); n /= 2; }
+    return row;
+}
+
+// ------------------------------------------------------------------ token records
+// One token's operands in the LDS ring, written by one wave and read by all eight.
+template <int DK, bool KDA, bool BWD>
+struct TokRing {
+    float ku[kTokRing][DK];                 // k, or Hu k
+    float qu[kTokRing][DK];                 // q, or Hu q
+    float ga[kTokRing][KDA ? DK : 1];       // exp(g) per key row (KDA)
+    float v[kTokRing][kTokCols];            // the tile's values
+    float dout[kTokRing][BWD ? kTokCols : 1];
+    float4 sc[kTokRing];                    // (exp(g) (scalar gate; 1 for KDA), beta, k . q, 0)
+};
+
+struct TokInputs {
+    const void *q, *k, *v, *g, *beta;
+    const float* dout;
+};
+
+// Element layout of a length-DK vector over the lanes of one wave: bf16 rows arrive as one
+// word (two elements) per lane, element 2 lane + e; fp32 rows as element lane + 64 e.
+__device__ __forceinline__ int tok_elem(bool bf16, int lane, int e) { return bf16 ? 2 * lane + e : lane + 64 * e; }
+
+// Unnormalized Sylvester Walsh-Hadamard transform of a length-DK vector held in that layout:
+// the in-lane element bit is one butterfly stage, every lane bit one more (lane ^ mask).
+template <int DK>
+__device__ __forceinline__ void lane_wht(float& x0, float& x1, int lane, bool bf16) {
+    auto stage = [&](int m) __attribute__((always_inline)) {
+        const bool hi = (lane & m) != 0;
+        const float p0 = xor_shfl(x0, m), p1 = xor_shfl(x1, m);
+        x0 = hi ? p0 - x0 : x0 + p0;
+        x1 = hi ? p1 - x1 : x1 + p1;
+    };
+    if (bf16) {
+        const float a = x0 + x1, b = x0 - x1;
+        x0 = a;
+        x1 = b;
+#pragma unroll
+        for (int m = 1; 2 * m < DK; m <<= 1) stage(m);
+    } else {
+#pragma unroll
+        for (int m = 1; m < DK && m < 64; m <<= 1) stage(m);
+        if (DK > 64) {
+            const float a = x0 + x1, b = x0 - x1;
+            x0 = a;
+            x1 = b;
+        }
+    }
+}
+
+// Raw words of one token for the wave that publishes it (widened only when published, so
+// that the loads are not waited on early).
+template <int DK, bool KDA, bool BWD>
+struct TokFetch {
+    uint32_t k0 = 0, k1 = 0, q0 = 0, q1 = 0, g0 = 0, g1 = 0, b = 0, v = 0;
+    float d = 0.0f;
+
+    __device__ __forceinline__ void fetch(const TokInputs& in, const TokParams& p, size_t tok, int col, int lane) {
+        const bool bf = p.qkv_dt == LA_BF16, gf = p.gate_dt == LA_F32;
+        if (bf) {
+            if (lane < DK / 2) {
+                k0 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(in.k) + tok * DK)[lane];
+                q0 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(in.q) + tok * DK)[lane];
+            }
+            v = static_cast<const uint16_t*>(in.v)[tok * p.dv + col];
+        } else {
+            const uint32_t* kp = static_cast<const uint32_t*>(in.k) + tok * DK;
+            const uint32_t* qp = static_cast<const uint32_t*>(in.q) + tok * DK;
+            if (lane < DK) { k0 = kp[lane]; q0 = qp[lane]; }
+            if (lane + 64 < DK) { k1 = kp[lane + 64]; q1 = qp[lane + 64]; }
+            v = static_cast<const uint32_t*>(in.v)[tok * p.dv + col];
+        }
+        if (KDA) {
+            if (!gf) {
+                if (lane < DK / 2) g0 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(in.g) + tok * DK)[lane];
+            } else {
+                const uint32_t* gp = static_cast<const uint32_t*>(in.g) + tok * DK;
+                if (lane < DK) g0 = gp[lane];
+                if (lane + 64 < DK) g1 = gp[lane + 64];
+            }
+        } else {
+            g0 = gf ? static_cast<const uint32_t*>(in.g)[tok] : static_cast<const uint16_t*>(in.g)[tok];
+        }
+        b = gf ? static_cast<const uint32_t*>(in.beta)[tok] : static_cast<const uint16_t*>(in.beta)[tok];
+        if (BWD) d = in.dout[tok * p.dv + col];
+    }
+
+    template <bool HAD>
+    __device__ __forceinline__ void publish(TokRing<DK, KDA, BWD>& ring, int slot, const TokParams& p, int lane) const {
+        const bool bf = p.qkv_dt == LA_BF16, gf = p.gate_dt == LA_F32;
+        auto wid = [](uint32_t x, bool b16) { return b16 ? __uint_as_float(x << 16) : __uint_as_float(x); };
+        float kx0, kx1, qx0, qx1;
+        if (bf) {
+            kx0 = __uint_as_float(k0 << 16);
+            kx1 = __uint_as_float(k0 & 0xFFFF0000u);
+            qx0 = __uint_as_float(q0 << 16);
+            qx1 = __uint_as_float(q0 & 0xFFFF0000u);
+        } else {
+            kx0 = __uint_as_float(k0);
+            kx1 = __uint_as_float(k1);
+            qx0 = __uint_as_float(q0);
+            qx1 = __uint_as_float(q1);
+        }
+        const float kq = wave_sum(__builtin_fmaf(kx1, qx1, kx0 * qx0));
+        if (HAD) {
+            lane_wht<DK>(kx0, kx1, lane, bf);
+            lane_wht<DK>(qx0, qx1, lane, bf);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+            const int i = tok_elem(bf, lane, e);
+            if (i < DK && (bf || lane < 64)) {
+                ring.ku[slot][i] = e ? kx1 : kx0;
+                ring.qu[slot][i] = e ? qx1 : qx0;
+            }
+        }
+        float a = 1.0f;
+        if (KDA) {
+            float gx0, gx1;
+            if (!gf) {
+                gx0 = __uint_as_float(g0 << 16);
+                gx1 = __uint_as_float(g0 & 0xFFFF0000u);
+            } else {
+                gx0 = __uint_as_float(g0);
+                gx1 = __uint_as_float(g1);
+            }
+#pragma unroll
+            for (int e = 0; e < 2; e++) {
+                const int i = tok_elem(!gf, lane, e);
+                if (i < DK) ring.ga[slot][i] = expf(e ? gx1 : gx0);
+            }
+        } else {
+            a = expf(wid(g0, !gf));
+        }
+        ring.v[slot][lane] = wid(v, bf);
+        if (BWD) ring.dout[slot][lane] = d;
+        if (lane == 0) ring.sc[slot] = make_float4(a, wid(b, !gf), kq, 0.0f);
+    }
+};
+
+// A wave's view of one token: its rows of the key, query (and KDA gate) vectors, the scalars
+// and its column's value (and upstream output gradient).
+template <int DK, bool KDA>
+struct TokOps {
+    static constexpr int R = DK / kTokWaves;
+    float kr[R], qr[R], ar[KDA ? R : 1];
+    float a, beta, kq, vj, dj;
+};
+
+template <int DK, bool KDA, bool BWD>
+__device__ __forceinline__ void tok_read(TokOps<DK, KDA>& op, const TokRing<DK, KDA, BWD>& ring, int slot, int w, int lane) {
+    constexpr int R = DK / kTokWaves;
+#pragma unroll
+    for (int m = 0; m < R; m++) {
+        op.kr[m] = ring.ku[slot][w * R + m];
+        op.qr[m] = ring.qu[slot][w * R + m];
+        if (KDA) op.ar[m] = ring.ga[slot][w * R + m];
+    }
+    const float4 sc = ring.sc[slot];
+    op.a = sc.x;
+    op.beta = sc.y;
+    op.kq = sc.z;
+    op.vj = ring.v[slot][lane];
+    op.dj = BWD ? ring.dout[slot][lane] : 0.0f;
+}
+
+// ------------------------------------------------------------------ one token
+// s: the state entering the token (rows w R .. w R + R - 1 of this lane's column), advanced
+// in place to S' = a S + ku delta^T (before rounding).  red: this token's reduction buffer
+// (kTokWaves x 64 float2).  Returns u = S~^T k, delta and o = S'^T q for the column.
+template <int DK, bool KDA, bool HAD>
+__device__ __forceinline__ void tok_step(float (&s)[DK / kTokWaves], const TokOps<DK, KDA>& op, float2 (*red)[kTokCols],
+                                         int w, int lane, float& u, float& delta, float& o) {
+    constexpr int R = DK / kTokWaves;
+    float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+    for (int m = 0; m < R; m++) {
+        s[m] = (KDA ? op.ar[m] : op.a) * s[m];
+        pk = __builtin_fmaf(s[m], op.kr[m], pk);
+        pq = __builtin_fmaf(s[m], op.qr[m], pq);
+    }
+    red[w][lane] = make_float2(pk, pq);
+    __syncthreads();
+    float2 x[kTokWaves];
+#pragma unroll
+    for (int i = 0; i < kTokWaves; i++) x[i] = red[i][lane];
+    float P = x[0].x, Q = x[0].y;
+#pragma unroll
+    for (int i = 1; i < kTokWaves; i++) {
+        P += x[i].x;
+        Q += x[i].y;
+    }
+    if (HAD) {
+        P *= 1.0f / DK;
+        Q *= 1.0f / DK;
+    }
+    delta = op.beta * (op.vj - P);
+    o = __builtin_fmaf(delta, op.kq, Q);
+    u = P;
+#pragma unroll
+    for (int m = 0; m < R; m++) s[m] = __builtin_fmaf(op.kr[m], delta, s[m]);
+}
+
+// ------------------------------------------------------------------ codecs
+// INT8 groups of G columns: each lane takes the maximum of one (row, group) by a
+// reduce-scatter, computes s = amax / 127 (1 when amax = 0) and y = RN(1 / s) once, and the
+// wave reads every (s, y) of its groups back from LDS (scr: 64 / G x R float2 per wave).
+template <int R, int G>
+__device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
+    float x[R];
+#pragma unroll
+    for (int m = 0; m < R; m++) x[m] = fabsf(s[m]);
+    const float mx = reduce_scatter<OpMax, R, G>(x, lane);
+    const int row = reduce_scatter_row<R, G>(lane), grp = lane / G;
+    const float sc = int8_scale(mx);
+    scr[grp * R + row] = make_float2(sc, 1.0f / sc);
+    const bool tiny = __any(sc < kFastQuotMinScale);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    float2 sy[R];
+#pragma unroll
+    for (int m = 0; m < R; m++) sy[m] = scr[grp * R + m];
+    if (!tiny) {
+#pragma unroll
+        for (int m = 0; m < R; m++) s[m] = int8_code_y(s[m], sy[m].x, sy[m].y) * sy[m].x;
+    } else {
+#pragma unroll
+        for (int m = 0; m < R; m++) s[m] = int8_code(s[m], sy[m].x) * sy[m].x;
+    }
+    __builtin_amdgcn_wave_barrier();  // scr is rewritten only after every lane has read it
+}
+
+// E4M3 with one scale per 64-column tile (all key rows: the eight waves meet through LDS).
+template <int R>
+__device__ __forceinline__ void tok_e4m3(float (&s)[R], float* amax_sh, int w, int lane) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int m = 0; m < R; m++) mx = fmaxf(mx, fabsf(s[m]));
+    mx = group_max<64>(mx);
+    if (lane == 0) amax_sh[w] = mx;
+    __syncthreads();
+    float amax = amax_sh[0];
+#pragma unroll
+    for (int i = 1; i < kTokWaves; i++) amax = fmaxf(amax, amax_sh[i]);
+    const float sce = amax > 0.0f ? amax / 448.0f : 1.0f;
+    float yv[R];
+    if (sce >= kFastQuotMinScaleE4M3) {
+        const float y = 1.0f / sce;
+#pragma unroll
+        for (int m = 0; m < R; m++) yv[m] = quot_rn(s[m], sce, y);
+    } else {
+#pragma unroll
+        for (int m = 0; m < R; m++) yv[m] = s[m] / sce;
+    }
+#pragma unroll
+    for (int m = 0; m < R; m += 2) {
+        e4m3_round2(yv[m], yv[m + 1]);
+        s[m] = yv[m] * sce;
+        s[m + 1] = yv[m + 1] * sce;
+    }
+}
+
+template <int DK, int QMODE, int G>
+struct TokQdqShared {
+    float2 scr[QMODE == LA_QDQ_INT8_GROUP ? kTokWaves : 1][QMODE == LA_QDQ_INT8_GROUP ? (kTokCols / G) * (DK / kTokWaves) : 1];
+    float amax[kTokWaves];
+};
+
+template <int DK, int QMODE, int G>
+__device__ __forceinline__ void tok_qdq(float (&s)[DK / kTokWaves], TokQdqShared<DK, QMODE, G>& sh, int w, int lane) {
+    if (QMODE == LA_QDQ_INT8_GROUP) tok_int8<DK / kTokWaves, G>(s, sh.scr[w], lane);
+    else if (QMODE == LA_QDQ_E4M3_TILE) tok_e4m3<DK / kTokWaves>(s, sh.amax, w, lane);
+}
+
+// ------------------------------------------------------------------ state rotation
+// s <- (Hu s) * scale along the key axis, through an LDS tile of DK x 64 floats.  Every
+// thread of the workgroup calls it.
+template <int DK>
+__device__ __forceinline__ void tok_rotate(float (&s)[DK / kTokWaves], float* tile, int w, int lane, float scale) {
+    constexpr int R = DK / kTokWaves;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < R; m++) tile[(w * R + m) * kTokCols + lane] = s[m];
+#pragma unroll 1
+    for (int h = 1; h < DK; h <<= 1) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < (DK / 2) * kTokCols; idx += kTokThreads) {
+            const int c = idx & (kTokCols - 1), pr = idx / kTokCols;
+            const int i = (pr / h) * 2 * h + (pr % h);
+            const float x = tile[i * kTokCols + c], y = tile[(i + h) * kTokCols + c];
+            tile[i * kTokCols + c] = x + y;
+            tile[(i + h) * kTokCols + c] = x - y;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < R; m++) s[m] = tile[(w * R + m) * kTokCols + lane] * scale;
+    __syncthreads();
+}
+
+}  // namespace la
