@@ -65,6 +65,15 @@ CASES = [
     ("kda_int8g16_dv192_ckpt16", synth.Workload("r", B=1, T=45, H=2, d_k=32, d_v=192, gate="key",
                                                 s0_sigma=0.1, config_id=35),
      la.LA_QDQ_INT8_GROUP, 16, 0, 1, 16, True),
+    # recompute chunks that are not whole blocks of eight or groups of four tokens
+    ("gdn_int8g32_ckpt5", synth.Workload("c5", B=1, T=23, H=2, d_k=128, d_v=64, s0_sigma=0.2, config_id=37),
+     la.LA_QDQ_INT8_GROUP, 32, 0, 1, 5, True),
+    ("kda_e4m3_i3_ckpt12_dk16", synth.Workload("c12", B=2, T=37, H=1, d_k=16, d_v=64, gate="key", s0_sigma=0.2,
+                                               config_id=38),
+     la.LA_QDQ_E4M3_TILE, 64, 0, 3, 12, True),
+    ("gdn_wht_int8g16_fp32_ckpt7_dk32", synth.Workload("c7", B=1, T=30, H=2, d_k=32, d_v=64, qkv_dtype="f32",
+                                                       gate_dtype="f32", s0_sigma=0.2, config_id=39),
+     la.LA_QDQ_INT8_GROUP, 16, 1, 1, 7, False),
 ]
 
 
