@@ -1,7 +1,7 @@
 // Straight-through backward of the recurrence.
 //
-// One workgroup per (sequence, head, 64-column value tile) in the token layout of
-// la_tok.hpp (eight waves, lane j = column j, wave w = key rows [w R, (w+1) R)).  Chunks of
+// One workgroup per (sequence, head, value tile) in the token layout of la_tok.hpp (eight
+// waves; each lane one value column of the tile and R key rows of it).  Chunks of
 // C = ckpt_interval tokens are processed last to first, each in blocks of eight tokens:
 //   phase A  recompute the chunk from its checkpoint with the forward's own token step,
 //            storing the state entering every fourth token in the workspace;
@@ -20,8 +20,7 @@
 //   da_i   = sum_j S_ij dS~_ij,  dg = a da (KDA per row; GDN summed over the state)
 //   lambda = diag(a) dS~
 // In Hadamard mode the state is carried rotated, Y = Hu S: ku = Hu k, kp = Hu k / d_k,
-// qq = Hu q / d_k, and lambda is dL/dY.  Row sums are partial over the
-// tile's 64 columns; they are written per value tile and summed in a fixed order by
+// qq = Hu q / d_k, and lambda is dL/dY.  Row sums are partial over the tile's columns; they are written per value tile and summed in a fixed order by
 // bwd_reduce_kernel, which also maps the rotated-domain key and query gradients back
 // (dk = Hu (dku + dkp / d_k), dq = Hu dqq / d_k).
 #include "la_tok.hpp"
@@ -42,16 +41,15 @@ struct PartLayout {
 };
 
 // One token of the adjoint.  st: the state entering the token; u, dl: its u and delta;
-// lam: dL/dS_t on entry, dL/dS_{t-1} on return.
-template <int DK, bool KDA, bool HAD>
-__device__ __forceinline__ void tok_adjoint(const float (&st)[DK / kTokWaves], float u, float dl,
-                                            const TokOps<DK, KDA>& op, const float* ga_row, float (&lam)[DK / kTokWaves],
-                                            float2 (*red)[kTokCols], int w, int lane, float* part, float* dv_out,
-                                            bool writer) {
-    constexpr int R = DK / kTokWaves;
+// lam: dL/dS_t on entry, dL/dS_{t-1} on return.  Row sums run over the tile's TC columns.
+template <class S, bool KDA, bool HAD>
+__device__ __forceinline__ void tok_adjoint(const float (&st)[S::R], float u, float dl, const TokOps<S, KDA>& op,
+                                            const float* ga_row, float (&lam)[S::R], float2 (*red)[S::TC], int w,
+                                            int lane, float* part, float* dv_out, bool writer) {
+    constexpr int R = S::R, TC = S::TC, DK = S::DK;
     constexpr float c1 = HAD ? 1.0f / DK : 1.0f;
     constexpr int GW = PartLayout<DK, KDA>::GW;
-    const int row = w * R + reduce_scatter_row<R, 64>(lane);
+    const int row = tok_row0<S>(w, lane) + reduce_scatter_row<R, TC>(lane);
     float sa[R], x[R];
     float pd = 0.0f;
 #pragma unroll
@@ -62,28 +60,30 @@ __device__ __forceinline__ void tok_adjoint(const float (&st)[DK / kTokWaves], f
         x[m] = spm * op.dj;
         pd = __builtin_fmaf(lam[m], op.kr[m], pd);
     }
-    red[w][lane] = make_float2(pd, 0.0f);
+    pd = tok_rows_combine<S>(pd);
+    if (lane < TC) red[w][lane] = make_float2(pd, 0.0f);
     __syncthreads();
+    const int c = lane % TC;
     float r[kTokWaves];
 #pragma unroll
-    for (int i = 0; i < kTokWaves; i++) r[i] = red[i][lane].x;
+    for (int i = 0; i < kTokWaves; i++) r[i] = red[i][c].x;
     float ddel = r[0];
 #pragma unroll
     for (int i = 1; i < kTokWaves; i++) ddel += r[i];
-    const float x1 = reduce_scatter<OpAdd, R, 64>(x, lane);
+    const float x1 = reduce_scatter<OpAdd, R, TC>(x, lane);
     const float du = -op.beta * ddel;
 #pragma unroll
     for (int m = 0; m < R; m++) {
         x[m] = __builtin_fmaf(lam[m], dl, c1 * (sa[m] * du));       // dku + c1 dkp
         lam[m] = __builtin_fmaf(op.kr[m] * c1, du, lam[m]);          // dS~ = dS' + kp du^T
     }
-    const float x2 = reduce_scatter<OpAdd, R, 64>(x, lane);
+    const float x2 = reduce_scatter<OpAdd, R, TC>(x, lane);
     part[row] = x1;
     part[DK + row] = x2;
     if (KDA) {
 #pragma unroll
         for (int m = 0; m < R; m++) x[m] = st[m] * lam[m];
-        const float x3 = reduce_scatter<OpAdd, R, 64>(x, lane);
+        const float x3 = reduce_scatter<OpAdd, R, TC>(x, lane);
         part[2 * DK + row] = ga_row[row] * x3;
     } else {
         float gp = 0.0f;
@@ -95,47 +95,49 @@ __device__ __forceinline__ void tok_adjoint(const float (&st)[DK / kTokWaves], f
 #pragma unroll
     for (int m = 0; m < R; m++) lam[m] = (KDA ? op.ar[m] : op.a) * lam[m];
     if (writer) {
-        *dv_out = op.beta * ddel;
-        const float db = wave_sum(ddel * (op.vj - u));
+        if (lane < TC) *dv_out = op.beta * ddel;
+        const float db = group_sum<TC>(ddel * (op.vj - u));
         if (lane == 0) part[2 * DK + GW] = db;
     }
 }
 
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
 __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdArgs a) {
-    constexpr int R = DK / kTokWaves;
+    using S = TokShape<DK, QMODE, G>;
+    constexpr int R = S::R, TC = S::TC;
     constexpr int PW = PartLayout<DK, KDA>::PW;
-    __shared__ TokRing<DK, KDA, true> ring;
-    __shared__ float2 red[2][kTokWaves][kTokCols];
-    __shared__ TokQdqShared<DK, QMODE, G> qsh;
-    __shared__ float tile[HAD ? DK * kTokCols : 1];
+    __shared__ TokRing<S, KDA, true> ring;
+    __shared__ float2 red[2][kTokWaves][TC];
+    __shared__ TokQdqShared<S> qsh;
+    __shared__ float tile[HAD ? DK * TC : 1];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int T = p.T, H = p.H, DV = p.dv, C = p.ckpt_interval;
-    const int NB = DV / kTokCols;
-    const int col = blk * kTokCols + lane;
+    const int NB = DV / TC;
+    const int col = blk * TC + lane % TC;
+    const int r0 = tok_row0<S>(w, lane);
     const size_t bh = static_cast<size_t>(b) * H + h;
     const size_t state_off = bh * DK * DV;
     const size_t wg = bh * NB + blk;
     const size_t ntok = static_cast<size_t>(p.B) * T * H;
     const size_t tok0 = static_cast<size_t>(b) * T * H + h;
     const int nsub = (C + kSubTok - 1) / kSubTok;
-    float* wsS = a.ws_states + wg * static_cast<size_t>(nsub) * DK * kTokCols;
+    float* wsS = a.ws_states + wg * static_cast<size_t>(nsub) * DK * TC;
     const TokInputs in{a.q, a.k, a.v, a.g, a.beta, a.dout};
 
     float lam[R];
 #pragma unroll
     for (int m = 0; m < R; m++)
-        lam[m] = a.dST ? a.dST[state_off + static_cast<size_t>(w * R + m) * DV + col] : 0.0f;
-    if (HAD && !p.rot) tok_rotate<DK>(lam, tile, w, lane, 1.0f / DK);  // dL/dY = Hu dL/dS / d_k
+        lam[m] = a.dST ? a.dST[state_off + static_cast<size_t>(r0 + m) * DV + col] : 0.0f;
+    if (HAD && !p.rot) tok_rotate<S>(lam, tile, w, lane, 1.0f / DK);  // dL/dY = Hu dL/dS / d_k
 
     // Blocks in processing order: chunk c from last to first; in each, phase A over blocks
     // j = 0 .. nb-1, then phase B over j = nb-1 .. 0.  The inputs of the next block in this
     // order are fetched while a block is processed.
     auto nblocks = [&](int c) { return (min(T, (c + 1) * C) - c * C + kBlkTok - 1) / kBlkTok; };
-    TokFetch<DK, KDA, true> f;
+    TokFetch<S, KDA, true> f;
     auto fetch = [&](int c, int j) __attribute__((always_inline)) {
         if (c < 0) return;
         const int t = c * C + kBlkTok * j + w;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
             float s[R];
             const float* ck = a.ckpts + (bh * p.nck + c) * DK * DV;
 #pragma unroll
-            for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(w * R + m) * DV + col];
+            for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
 #pragma unroll 1
             for (int j = 0; j < nb; j++) {
                 const int tb = t0 + kBlkTok * j;
@@ -172,18 +174,18 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
 #pragma unroll 1
                 for (int i = 0; i < nt; i++) {
                     if ((i % kSubTok) == 0 && (j > 0 || i > 0)) {
-                        float* dst = wsS + static_cast<size_t>(kBlkTok / kSubTok * j + i / kSubTok) * DK * kTokCols;
+                        float* dst = wsS + static_cast<size_t>(kBlkTok / kSubTok * j + i / kSubTok) * DK * TC;
 #pragma unroll
-                        for (int m = 0; m < R; m++) dst[(w * R + m) * kTokCols + lane] = s[m];
+                        for (int m = 0; m < R; m++) dst[(r0 + m) * TC + lane % TC] = s[m];
                     }
-                    TokOps<DK, KDA> op;
-                    tok_read<DK, KDA, true>(op, ring, i, w, lane);
+                    TokOps<S, KDA> op;
+                    tok_read<S, KDA, true>(op, ring, i, w, lane);
                     float u, dl, o;
-                    tok_step<DK, KDA, HAD>(s, op, red[rp], w, lane, u, dl, o);
+                    tok_step<S, KDA, HAD>(s, op, red[rp], w, lane, u, dl, o);
                     rp ^= 1;
                     const int t = tb + i;
                     if (QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1))
-                        tok_qdq<DK, QMODE, G>(s, qsh, w, lane);
+                        tok_qdq<S>(s, qsh, w, lane);
                 }
             }
         }
@@ -202,11 +204,11 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                 if (j == 0 && hh == 0) {
                     const float* ck = a.ckpts + (bh * p.nck + c) * DK * DV;
 #pragma unroll
-                    for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(w * R + m) * DV + col];
+                    for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
                 } else {
-                    const float* src = wsS + static_cast<size_t>(kBlkTok / kSubTok * j + hh) * DK * kTokCols;
+                    const float* src = wsS + static_cast<size_t>(kBlkTok / kSubTok * j + hh) * DK * TC;
 #pragma unroll
-                    for (int m = 0; m < R; m++) s[m] = src[(w * R + m) * kTokCols + lane];
+                    for (int m = 0; m < R; m++) s[m] = src[(r0 + m) * TC + lane % TC];
                 }
                 float st[kSubTok][R];
                 float uu[kSubTok], dd[kSubTok];
@@ -215,24 +217,24 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                     if (i < n) {
 #pragma unroll
                         for (int m = 0; m < R; m++) st[i][m] = s[m];
-                        TokOps<DK, KDA> op;
-                        tok_read<DK, KDA, true>(op, ring, i0 + i, w, lane);
+                        TokOps<S, KDA> op;
+                        tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
                         float o;
-                        tok_step<DK, KDA, HAD>(s, op, red[rp], w, lane, uu[i], dd[i], o);
+                        tok_step<S, KDA, HAD>(s, op, red[rp], w, lane, uu[i], dd[i], o);
                         rp ^= 1;
                         const int t = tb + i0 + i;
                         if (QMODE != LA_QDQ_NONE && i + 1 < n && (((t + 1) % p.qdq_interval) == 0 || t == T - 1))
-                            tok_qdq<DK, QMODE, G>(s, qsh, w, lane);
+                            tok_qdq<S>(s, qsh, w, lane);
                     }
                 }
 #pragma unroll
                 for (int i = kSubTok - 1; i >= 0; i--) {
                     if (i < n) {
-                        TokOps<DK, KDA> op;
-                        tok_read<DK, KDA, true>(op, ring, i0 + i, w, lane);
+                        TokOps<S, KDA> op;
+                        tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
                         const size_t tok = tok0 + static_cast<size_t>(tb + i0 + i) * H;
                         float* part = a.ws_part + (static_cast<size_t>(blk) * ntok + tok) * PW;
-                        tok_adjoint<DK, KDA, HAD>(st[i], uu[i], dd[i], op, ring.ga[i0 + i], lam, red[rp], w, lane,
+                        tok_adjoint<S, KDA, HAD>(st[i], uu[i], dd[i], op, ring.ga[i0 + i], lam, red[rp], w, lane,
                                                   part, a.dv + tok * DV + col, w == i0 + i);
                         rp ^= 1;
                     }
@@ -240,9 +242,9 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
             }
         }
     }
-    if (HAD && !p.rot) tok_rotate<DK>(lam, tile, w, lane, 1.0f);  // dL/dS = Hu dL/dY
+    if (HAD && !p.rot) tok_rotate<S>(lam, tile, w, lane, 1.0f);  // dL/dS = Hu dL/dY
 #pragma unroll
-    for (int m = 0; m < R; m++) a.dS0[state_off + static_cast<size_t>(w * R + m) * DV + col] = lam[m];
+    for (int m = 0; m < R; m++) a.dS0[state_off + static_cast<size_t>(r0 + m) * DV + col] = lam[m];
 }
 
 // Sum the per-tile partials in tile order and write dq, dk, dg, dbeta.  One wave per token.
@@ -323,14 +325,15 @@ namespace {
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
 hipError_t launch_bwd_t(const la_config& c, const BwdArgs& a, hipStream_t s) {
     const TokParams p = make_tok_params(c);
-    dim3 grid(c.d_v / kTokCols, c.H, c.B);
+    constexpr int TC = tok_tile_cols(DK, QMODE, G);
+    dim3 grid(c.d_v / TC, c.H, c.B);
     hipLaunchKernelGGL((bwd_tok_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(kTokThreads), 0, s, p, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t ntok = static_cast<size_t>(c.B) * c.T * c.H;
     if (ntok == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_reduce_kernel<DK, HAD, KDA>), dim3(static_cast<unsigned>(ntok)), dim3(64), 0, s, p, a,
-                       c.d_v / kTokCols);
+                       c.d_v / TC);
     return hipGetLastError();
 }
 

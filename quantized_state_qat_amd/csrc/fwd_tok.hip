@@ -2,8 +2,9 @@
 // the Hadamard rotation, a rounding point after every token or at intervals that do not
 // fall on their block ends).  The layout and the per-token step are those of la_tok.hpp.
 //
-// Token inputs arrive in blocks of eight: wave w fetches token 8 J + w of block J two blocks
-// ahead (raw words in registers), publishes it into the LDS ring one block ahead, and every
+// The tile is 64 or 32 value columns wide (TokShape).  Token inputs arrive in blocks of eight:
+// wave w fetches token 8 J + w of block J two blocks ahead (raw words in registers),
+// publishes it into the LDS ring one block ahead, and every
 // wave reads its rows of a token's record at the end of the previous token.  The only
 // barrier per token is the one inside tok_step (plus one more for an E4M3 rounding point).
 #include "la_tok.hpp"
@@ -23,23 +24,25 @@ TokParams make_tok_params(const la_config& c) {
 
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
 __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdArgs a) {
-    constexpr int R = DK / kTokWaves;
-    __shared__ TokRing<DK, KDA, false> ring;
-    __shared__ float2 red[2][kTokWaves][kTokCols];
-    __shared__ TokQdqShared<DK, QMODE, G> qsh;
-    __shared__ float tile[HAD ? DK * kTokCols : 1];
+    using S = TokShape<DK, QMODE, G>;
+    constexpr int R = S::R, TC = S::TC;
+    __shared__ TokRing<S, KDA, false> ring;
+    __shared__ float2 red[2][kTokWaves][TC];
+    __shared__ TokQdqShared<S> qsh;
+    __shared__ float tile[HAD ? DK * TC : 1];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int T = p.T, H = p.H, DV = p.dv;
-    const int col = blk * kTokCols + lane;
+    const int col = blk * TC + lane % TC;
+    const int r0 = tok_row0<S>(w, lane);
     const size_t bh = static_cast<size_t>(b) * H + h;
     const size_t state_off = bh * DK * DV;
     const size_t tok0 = static_cast<size_t>(b) * T * H + h;  // token 0 of this (b, h)
     const TokInputs in{a.q, a.k, a.v, a.g, a.beta, nullptr};
 
-    TokFetch<DK, KDA, false> f;
+    TokFetch<S, KDA, false> f;
     auto fetch = [&](int u) __attribute__((always_inline)) {
         if (u < T) f.fetch(in, p, tok0 + static_cast<size_t>(u) * H, col, lane);
     };
@@ -50,8 +53,8 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
     float s[R];
 #pragma unroll
     for (int m = 0; m < R; m++)
-        s[m] = a.S0 ? a.S0[state_off + static_cast<size_t>(w * R + m) * DV + col] : 0.0f;
-    if (HAD && !p.rot) tok_rotate<DK>(s, tile, w, lane, 1.0f);
+        s[m] = a.S0 ? a.S0[state_off + static_cast<size_t>(r0 + m) * DV + col] : 0.0f;
+    if (HAD && !p.rot) tok_rotate<S>(s, tile, w, lane, 1.0f);
 
     fetch(w);
     publish(w);
@@ -62,8 +65,8 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
     fetch(kTokWaves + w);
     __syncthreads();
 
-    TokOps<DK, KDA> op;
-    if (T > 0) tok_read<DK, KDA, false>(op, ring, 0, w, lane);
+    TokOps<S, KDA> op;
+    if (T > 0) tok_read<S, KDA, false>(op, ring, 0, w, lane);
     int ck_next = a.ckpts ? 0 : T;                                        // next checkpoint token
     int q_next = QMODE != LA_QDQ_NONE ? min(p.qdq_interval, T) - 1 : T;  // next rounding token
     size_t tok = tok0;
@@ -79,23 +82,23 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
             // checkpoints hold the carried state as the loop carries it (rotated in Hadamard mode)
             float* dst = a.ckpts + (bh * p.nck + t / p.ckpt_interval) * DK * DV;
 #pragma unroll
-            for (int m = 0; m < R; m++) dst[static_cast<size_t>(w * R + m) * DV + col] = s[m];
+            for (int m = 0; m < R; m++) dst[static_cast<size_t>(r0 + m) * DV + col] = s[m];
             ck_next += p.ckpt_interval;
         }
         float u, delta, o;
-        tok_step<DK, KDA, HAD>(s, op, red[t & 1], w, lane, u, delta, o);
-        if (a.o && w == (t & (kTokWaves - 1))) store_elem(a.o, tok * DV + col, p.out_dt, o);
-        if (t + 1 < T) tok_read<DK, KDA, false>(op, ring, (t + 1) % kTokRing, w, lane);
+        tok_step<S, KDA, HAD>(s, op, red[t & 1], w, lane, u, delta, o);
+        if (a.o && w == (t & (kTokWaves - 1)) && lane < TC) store_elem(a.o, tok * DV + col, p.out_dt, o);
+        if (t + 1 < T) tok_read<S, KDA, false>(op, ring, (t + 1) % kTokRing, w, lane);
         if (t == q_next) {
             q_next = min(q_next + p.qdq_interval, T - 1);
             if (q_next == t) q_next = T;
-            tok_qdq<DK, QMODE, G>(s, qsh, w, lane);
+            tok_qdq<S>(s, qsh, w, lane);
         }
     }
     if (a.ST) {
-        if (HAD && !p.rot) tok_rotate<DK>(s, tile, w, lane, 1.0f / DK);
+        if (HAD && !p.rot) tok_rotate<S>(s, tile, w, lane, 1.0f / DK);
 #pragma unroll
-        for (int m = 0; m < R; m++) a.ST[state_off + static_cast<size_t>(w * R + m) * DV + col] = s[m];
+        for (int m = 0; m < R; m++) a.ST[state_off + static_cast<size_t>(r0 + m) * DV + col] = s[m];
     }
 }
 
@@ -103,7 +106,7 @@ namespace {
 
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
 hipError_t launch_tok_t(const la_config& c, const FwdArgs& a, hipStream_t s) {
-    dim3 grid(c.d_v / kTokCols, c.H, c.B);
+    dim3 grid(c.d_v / tok_tile_cols(DK, QMODE, G), c.H, c.B);
     hipLaunchKernelGGL((fwd_tok_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(kTokThreads), 0, s, make_tok_params(c), a);
     return hipGetLastError();
 }

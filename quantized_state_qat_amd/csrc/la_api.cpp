@@ -97,11 +97,13 @@ struct WsLayout {
 
 WsLayout ws_layout(const la_config& c) {
     WsLayout L;
-    const size_t nwg = static_cast<size_t>(c.B) * c.H * la::n_value_blocks(c);
+    // the backward runs in the token layout: tiles of tok_tile_cols value columns
+    const size_t tc = static_cast<size_t>(la::tok_tile_cols(c.d_k, c.qdq, c.group));
+    const size_t tiles = static_cast<size_t>(la::tok_tiles(c));
+    const size_t nwg = static_cast<size_t>(c.B) * c.H * tiles;
     L.states = 0;
-    L.part = round_up(nwg * static_cast<size_t>(la::n_sub_states(c)) * c.d_k * 64 * sizeof(float));
-    L.ckpts = L.part + round_up(static_cast<size_t>(la::n_value_blocks(c)) * c.B * c.T * c.H *
-                                la::part_width(c) * sizeof(float));
+    L.part = round_up(nwg * static_cast<size_t>(la::n_sub_states(c)) * c.d_k * tc * sizeof(float));
+    L.ckpts = L.part + round_up(tiles * c.B * c.T * c.H * la::part_width(c) * sizeof(float));
     L.total = L.ckpts + round_up(static_cast<size_t>(c.B) * c.H * la::n_ckpts(c) * c.d_k * c.d_v * sizeof(float));
     return L;
 }

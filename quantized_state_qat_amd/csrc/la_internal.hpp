@@ -48,12 +48,18 @@ struct BwdArgs {
     float* dg;
     float* dbeta;
     float* dS0;
-    float* ws_states;    // per workgroup: the state entering every 4th token of a chunk (d_k x 64 each)
+    float* ws_states;    // per workgroup: the state entering every 4th token of a chunk (d_k x tile columns)
     float* ws_part;      // per value tile and token: partial row sums
 };
 
 // Host-side layout helpers (shared by the ABI and the launchers).
 inline int n_value_blocks(const la_config& c) { return c.d_v / 64; }
+// Value columns per workgroup of the token forward and the backward: 32 when every rounding
+// group fits in 32 columns (no quantizer, or INT8 groups of 16 or 32) and d_k >= 32, else 64.
+constexpr int tok_tile_cols(int dk, int qdq, int group) {
+    return (dk >= 32 && (qdq == LA_QDQ_NONE || (qdq == LA_QDQ_INT8_GROUP && group <= 32))) ? 32 : 64;
+}
+inline int tok_tiles(const la_config& c) { return c.d_v / tok_tile_cols(c.d_k, c.qdq, c.group); }
 inline int n_ckpts(const la_config& c) {
     return c.ckpt_interval > 0 ? (c.T + c.ckpt_interval - 1) / c.ckpt_interval : 0;
 }

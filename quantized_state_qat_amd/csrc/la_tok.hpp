@@ -2,8 +2,8 @@
 // recompute (bwd.hip): the two run exactly these functions, so a recompute meets the
 // forward's carried states and rounding decisions bit for bit.
 //
-// One workgroup per (sequence, head, 64-column value tile), eight waves: lane j holds value
-// column j of the tile, wave w holds key rows [w R, (w+1) R), R = d_k / 8, in registers.
+// One workgroup per (sequence, head, tile of 64 or 32 value columns), eight waves: each lane
+// holds one value column of the tile and R key rows of it in registers (TokShape).
 // Per token:
 //  * one wave has published the token's operands in an LDS ring (keys and queries, rotated
 //    by the Walsh-Hadamard transform in Hadamard mode; the gate, exp(g), per key row or
@@ -28,7 +28,6 @@ namespace la {
 constexpr int kTokWaves = 8;                  // waves per workgroup = tokens per block
 constexpr int kTokThreads = kTokWaves * 64;
 constexpr int kTokRing = 2 * kTokWaves;       // token records in the LDS ring
-constexpr int kTokCols = 64;                  // value columns per workgroup
 
 struct TokParams {
     int B, T, H, dk, dv;
@@ -131,16 +130,32 @@ __device__ __forceinline__ int reduce_scatter_row(int lane) {
     return row;
 }
 
+// ------------------------------------------------------------------ tile shape
+// A workgroup covers TC value columns of one (sequence, head): 64, or 32 when every rounding
+// group fits in 32 columns (tok_tile_cols), which doubles the workgroups of a small batch.  The
+// 64 lanes of a wave are TC columns x RH = 64 / TC row groups; wave w holds key rows
+// [w RW, (w+1) RW), RW = d_k / 8, and lane (rh, c) rows w RW + rh R .. + R - 1 of column c.
+template <int DK_, int QMODE_, int G_>
+struct TokShape {
+    static constexpr int DK = DK_, QMODE = QMODE_, G = G_;
+    static constexpr int TC = tok_tile_cols(DK, QMODE, G);
+    static constexpr int RH = 64 / TC;
+    static constexpr int RW = DK / kTokWaves;
+    static constexpr int R = RW / RH;
+    static_assert(R >= 1 && (QMODE != LA_QDQ_E4M3_TILE || (TC == 64 && R % 2 == 0)), "token tile shape");
+    static_assert(QMODE != LA_QDQ_INT8_GROUP || G <= TC, "INT8 groups within a tile");
+};
+
 // ------------------------------------------------------------------ token records
 // One token's operands in the LDS ring, written by one wave and read by all eight.
-template <int DK, bool KDA, bool BWD>
+template <class S, bool KDA, bool BWD>
 struct TokRing {
-    float ku[kTokRing][DK];                 // k, or Hu k
-    float qu[kTokRing][DK];                 // q, or Hu q
-    float ga[kTokRing][KDA ? DK : 1];       // exp(g) per key row (KDA)
-    float v[kTokRing][kTokCols];            // the tile's values
-    float dout[kTokRing][BWD ? kTokCols : 1];
-    float4 sc[kTokRing];                    // (exp(g) (scalar gate; 1 for KDA), beta, k . q, 0)
+    float ku[kTokRing][S::DK];                 // k, or Hu k
+    float qu[kTokRing][S::DK];                 // q, or Hu q
+    float ga[kTokRing][KDA ? S::DK : 1];       // exp(g) per key row (KDA)
+    float v[kTokRing][S::TC];                  // the tile's values
+    float dout[kTokRing][BWD ? S::TC : 1];
+    float4 sc[kTokRing];                       // (exp(g) (scalar gate; 1 for KDA), beta, k . q, 0)
 };
 
 struct TokInputs {
@@ -180,9 +195,10 @@ __device__ __forceinline__ void lane_wht(float& x0, float& x1, int lane, bool bf
 }
 
 // Raw words of one token for the wave that publishes it (widened only when published, so
-// that the loads are not waited on early).
-template <int DK, bool KDA, bool BWD>
+// that the loads are not waited on early).  col: this lane's value column (lanes < TC).
+template <class S, bool KDA, bool BWD>
 struct TokFetch {
+    static constexpr int DK = S::DK;
     uint32_t k0 = 0, k1 = 0, q0 = 0, q1 = 0, g0 = 0, g1 = 0, b = 0, v = 0;
     float d = 0.0f;
 
@@ -193,13 +209,13 @@ struct TokFetch {
                 k0 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(in.k) + tok * DK)[lane];
                 q0 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(in.q) + tok * DK)[lane];
             }
-            v = static_cast<const uint16_t*>(in.v)[tok * p.dv + col];
+            if (lane < S::TC) v = static_cast<const uint16_t*>(in.v)[tok * p.dv + col];
         } else {
             const uint32_t* kp = static_cast<const uint32_t*>(in.k) + tok * DK;
             const uint32_t* qp = static_cast<const uint32_t*>(in.q) + tok * DK;
             if (lane < DK) { k0 = kp[lane]; q0 = qp[lane]; }
             if (lane + 64 < DK) { k1 = kp[lane + 64]; q1 = qp[lane + 64]; }
-            v = static_cast<const uint32_t*>(in.v)[tok * p.dv + col];
+            if (lane < S::TC) v = static_cast<const uint32_t*>(in.v)[tok * p.dv + col];
         }
         if (KDA) {
             if (!gf) {
@@ -213,11 +229,11 @@ struct TokFetch {
             g0 = gf ? static_cast<const uint32_t*>(in.g)[tok] : static_cast<const uint16_t*>(in.g)[tok];
         }
         b = gf ? static_cast<const uint32_t*>(in.beta)[tok] : static_cast<const uint16_t*>(in.beta)[tok];
-        if (BWD) d = in.dout[tok * p.dv + col];
+        if (BWD && lane < S::TC) d = in.dout[tok * p.dv + col];
     }
 
     template <bool HAD>
-    __device__ __forceinline__ void publish(TokRing<DK, KDA, BWD>& ring, int slot, const TokParams& p, int lane) const {
+    __device__ __forceinline__ void publish(TokRing<S, KDA, BWD>& ring, int slot, const TokParams& p, int lane) const {
         const bool bf = p.qkv_dt == LA_BF16, gf = p.gate_dt == LA_F32;
         auto wid = [](uint32_t x, bool b16) { return b16 ? __uint_as_float(x << 16) : __uint_as_float(x); };
         float kx0, kx1, qx0, qx1;
@@ -263,58 +279,78 @@ struct TokFetch {
         } else {
             a = expf(wid(g0, !gf));
         }
-        ring.v[slot][lane] = wid(v, bf);
-        if (BWD) ring.dout[slot][lane] = d;
+        if (lane < S::TC) {
+            ring.v[slot][lane] = wid(v, bf);
+            if (BWD) ring.dout[slot][lane] = d;
+        }
         if (lane == 0) ring.sc[slot] = make_float4(a, wid(b, !gf), kq, 0.0f);
     }
 };
 
 // A wave's view of one token: its rows of the key, query (and KDA gate) vectors, the scalars
 // and its column's value (and upstream output gradient).
-template <int DK, bool KDA>
+template <class S, bool KDA>
 struct TokOps {
-    static constexpr int R = DK / kTokWaves;
-    float kr[R], qr[R], ar[KDA ? R : 1];
+    float kr[S::R], qr[S::R], ar[KDA ? S::R : 1];
     float a, beta, kq, vj, dj;
 };
 
-template <int DK, bool KDA, bool BWD>
-__device__ __forceinline__ void tok_read(TokOps<DK, KDA>& op, const TokRing<DK, KDA, BWD>& ring, int slot, int w, int lane) {
-    constexpr int R = DK / kTokWaves;
+// First key row of this lane (rows row0 .. row0 + R - 1).
+template <class S>
+__device__ __forceinline__ int tok_row0(int w, int lane) { return w * S::RW + (lane / S::TC) * S::R; }
+
+template <class S, bool KDA, bool BWD>
+__device__ __forceinline__ void tok_read(TokOps<S, KDA>& op, const TokRing<S, KDA, BWD>& ring, int slot, int w, int lane) {
+    const int r0 = tok_row0<S>(w, lane);
 #pragma unroll
-    for (int m = 0; m < R; m++) {
-        op.kr[m] = ring.ku[slot][w * R + m];
-        op.qr[m] = ring.qu[slot][w * R + m];
-        if (KDA) op.ar[m] = ring.ga[slot][w * R + m];
+    for (int m = 0; m < S::R; m++) {
+        op.kr[m] = ring.ku[slot][r0 + m];
+        op.qr[m] = ring.qu[slot][r0 + m];
+        if (KDA) op.ar[m] = ring.ga[slot][r0 + m];
     }
     const float4 sc = ring.sc[slot];
     op.a = sc.x;
     op.beta = sc.y;
     op.kq = sc.z;
-    op.vj = ring.v[slot][lane];
-    op.dj = BWD ? ring.dout[slot][lane] : 0.0f;
+    const int c = lane % S::TC;
+    op.vj = ring.v[slot][c];
+    op.dj = BWD ? ring.dout[slot][c] : 0.0f;
+}
+
+// Sum of a value over the RH row groups of a wave (lanes 32 apart hold the same column when
+// RH = 2); every lane of the column ends with the same bits.
+template <class S>
+__device__ __forceinline__ float tok_rows_combine(float x) {
+    if constexpr (S::RH == 2) {
+        const Pair p = swap32(x);
+        return p.a + p.b;
+    } else {
+        return x;
+    }
 }
 
 // ------------------------------------------------------------------ one token
-// s: the state entering the token (rows w R .. w R + R - 1 of this lane's column), advanced
-// in place to S' = a S + ku delta^T (before rounding).  red: this token's reduction buffer
-// (kTokWaves x 64 float2).  Returns u = S~^T k, delta and o = S'^T q for the column.
-template <int DK, bool KDA, bool HAD>
-__device__ __forceinline__ void tok_step(float (&s)[DK / kTokWaves], const TokOps<DK, KDA>& op, float2 (*red)[kTokCols],
+// s: the state entering the token (this lane's rows of its column), advanced in place to
+// S' = a S + ku delta^T (before rounding).  red: this token's reduction buffer (kTokWaves x TC
+// float2).  Returns u = S~^T k, delta and o = S'^T q for the column.
+template <class S, bool KDA, bool HAD>
+__device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>& op, float2 (*red)[S::TC],
                                          int w, int lane, float& u, float& delta, float& o) {
-    constexpr int R = DK / kTokWaves;
     float pk = 0.0f, pq = 0.0f;
 #pragma unroll
-    for (int m = 0; m < R; m++) {
+    for (int m = 0; m < S::R; m++) {
         s[m] = (KDA ? op.ar[m] : op.a) * s[m];
         pk = __builtin_fmaf(s[m], op.kr[m], pk);
         pq = __builtin_fmaf(s[m], op.qr[m], pq);
     }
-    red[w][lane] = make_float2(pk, pq);
+    pk = tok_rows_combine<S>(pk);
+    pq = tok_rows_combine<S>(pq);
+    if (lane < S::TC) red[w][lane] = make_float2(pk, pq);
     __syncthreads();
+    const int c = lane % S::TC;
     float2 x[kTokWaves];
 #pragma unroll
-    for (int i = 0; i < kTokWaves; i++) x[i] = red[i][lane];
+    for (int i = 0; i < kTokWaves; i++) x[i] = red[i][c];
     float P = x[0].x, Q = x[0].y;
 #pragma unroll
     for (int i = 1; i < kTokWaves; i++) {
@@ -322,20 +358,32 @@ __device__ __forceinline__ void tok_step(float (&s)[DK / kTokWaves], const TokOp
         Q += x[i].y;
     }
     if (HAD) {
-        P *= 1.0f / DK;
-        Q *= 1.0f / DK;
+        P *= 1.0f / S::DK;
+        Q *= 1.0f / S::DK;
     }
     delta = op.beta * (op.vj - P);
     o = __builtin_fmaf(delta, op.kq, Q);
     u = P;
 #pragma unroll
-    for (int m = 0; m < R; m++) s[m] = __builtin_fmaf(op.kr[m], delta, s[m]);
+    for (int m = 0; m < S::R; m++) s[m] = __builtin_fmaf(op.kr[m], delta, s[m]);
 }
 
 // ------------------------------------------------------------------ codecs
 // INT8 groups of G columns: each lane takes the maximum of one (row, group) by a
 // reduce-scatter, computes s = amax / 127 (1 when amax = 0) and y = RN(1 / s) once, and the
 // wave reads every (s, y) of its groups back from LDS (scr: 64 / G x R float2 per wave).
+//  * s: RN(amax * c) with c = RN(1/127), then one residual correction r = amax - 127 q (exact
+//    by FMA), s = RN(q + r c).  This equals the IEEE quotient amax / 127 for every amax whose
+//    quotient is at least 2^-100 (checked exhaustively over all significands in ten binades
+//    from 2^-95 to 2^100; the map commutes with scaling by powers of two in that range).
+//  * y: the hardware reciprocal refined by one Newton step, fma(fma(-s, r, 1), r, r); equal to
+//    the IEEE quotient 1 / s for every significand (checked exhaustively on gfx950 in twelve
+//    binades from 2^-100 to 2^99).
+//  * per element: x / s correctly rounded from y (quot_rn without the sign restore, which only
+//    affects the sign of an exactly zero quotient), then rint.  No clamp is needed: with
+//    |x| <= amax, |x / s| <= 127 (1 + 2^-24), which rounds to at most 127.
+// A group whose scale is below 2^-100 takes the IEEE division and the clamp instead (the
+// whole wave, when any lane has one).
 template <int R, int G>
 __device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
     float x[R];
@@ -343,9 +391,16 @@ __device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
     for (int m = 0; m < R; m++) x[m] = fabsf(s[m]);
     const float mx = reduce_scatter<OpMax, R, G>(x, lane);
     const int row = reduce_scatter_row<R, G>(lane), grp = lane / G;
-    const float sc = int8_scale(mx);
-    scr[grp * R + row] = make_float2(sc, 1.0f / sc);
-    const bool tiny = __any(sc < kFastQuotMinScale);
+    constexpr float c127 = 1.0f / 127.0f;
+    const float q0 = mx * c127;
+    float sc = __builtin_fmaf(__builtin_fmaf(-127.0f, q0, mx), c127, q0);
+    sc = mx > 0.0f ? sc : 1.0f;
+    const bool tiny_l = sc < kFastQuotMinScale;
+    if (tiny_l) sc = int8_scale(mx);
+    const float r = __builtin_amdgcn_rcpf(sc);
+    const float y = __builtin_fmaf(__builtin_fmaf(-sc, r, 1.0f), r, r);
+    scr[grp * R + row] = make_float2(sc, y);
+    const bool tiny = __any(tiny_l);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     float2 sy[R];
@@ -353,7 +408,13 @@ __device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
     for (int m = 0; m < R; m++) sy[m] = scr[grp * R + m];
     if (!tiny) {
 #pragma unroll
-        for (int m = 0; m < R; m++) s[m] = int8_code_y(s[m], sy[m].x, sy[m].y) * sy[m].x;
+        for (int m = 0; m < R; m++) {
+            const float xs = s[m], sm = sy[m].x, ym = sy[m].y;
+            float q = xs * ym;
+            q = __builtin_fmaf(__builtin_fmaf(-sm, q, xs), ym, q);
+            q = __builtin_fmaf(__builtin_fmaf(-sm, q, xs), ym, q);
+            s[m] = rintf(q) * sm;
+        }
     } else {
 #pragma unroll
         for (int m = 0; m < R; m++) s[m] = int8_code(s[m], sy[m].x) * sy[m].x;
@@ -391,41 +452,43 @@ __device__ __forceinline__ void tok_e4m3(float (&s)[R], float* amax_sh, int w, i
     }
 }
 
-template <int DK, int QMODE, int G>
+template <class S>
 struct TokQdqShared {
-    float2 scr[QMODE == LA_QDQ_INT8_GROUP ? kTokWaves : 1][QMODE == LA_QDQ_INT8_GROUP ? (kTokCols / G) * (DK / kTokWaves) : 1];
+    static constexpr bool I8 = S::QMODE == LA_QDQ_INT8_GROUP;
+    float2 scr[I8 ? kTokWaves : 1][I8 ? (64 / S::G) * S::R : 1];
     float amax[kTokWaves];
 };
 
-template <int DK, int QMODE, int G>
-__device__ __forceinline__ void tok_qdq(float (&s)[DK / kTokWaves], TokQdqShared<DK, QMODE, G>& sh, int w, int lane) {
-    if (QMODE == LA_QDQ_INT8_GROUP) tok_int8<DK / kTokWaves, G>(s, sh.scr[w], lane);
-    else if (QMODE == LA_QDQ_E4M3_TILE) tok_e4m3<DK / kTokWaves>(s, sh.amax, w, lane);
+template <class S>
+__device__ __forceinline__ void tok_qdq(float (&s)[S::R], TokQdqShared<S>& sh, int w, int lane) {
+    if constexpr (S::QMODE == LA_QDQ_INT8_GROUP) tok_int8<S::R, S::G>(s, sh.scr[w], lane);
+    else if constexpr (S::QMODE == LA_QDQ_E4M3_TILE) tok_e4m3<S::R>(s, sh.amax, w, lane);
 }
 
 // ------------------------------------------------------------------ state rotation
-// s <- (Hu s) * scale along the key axis, through an LDS tile of DK x 64 floats.  Every
+// s <- (Hu s) * scale along the key axis, through an LDS tile of DK x TC floats.  Every
 // thread of the workgroup calls it.
-template <int DK>
-__device__ __forceinline__ void tok_rotate(float (&s)[DK / kTokWaves], float* tile, int w, int lane, float scale) {
-    constexpr int R = DK / kTokWaves;
+template <class S>
+__device__ __forceinline__ void tok_rotate(float (&s)[S::R], float* tile, int w, int lane, float scale) {
+    constexpr int DK = S::DK, TC = S::TC;
+    const int r0 = tok_row0<S>(w, lane), c = lane % TC;
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < R; m++) tile[(w * R + m) * kTokCols + lane] = s[m];
+    for (int m = 0; m < S::R; m++) tile[(r0 + m) * TC + c] = s[m];
 #pragma unroll 1
     for (int h = 1; h < DK; h <<= 1) {
         __syncthreads();
-        for (int idx = threadIdx.x; idx < (DK / 2) * kTokCols; idx += kTokThreads) {
-            const int c = idx & (kTokCols - 1), pr = idx / kTokCols;
+        for (int idx = threadIdx.x; idx < (DK / 2) * TC; idx += kTokThreads) {
+            const int cc = idx % TC, pr = idx / TC;
             const int i = (pr / h) * 2 * h + (pr % h);
-            const float x = tile[i * kTokCols + c], y = tile[(i + h) * kTokCols + c];
-            tile[i * kTokCols + c] = x + y;
-            tile[(i + h) * kTokCols + c] = x - y;
+            const float x = tile[i * TC + cc], y = tile[(i + h) * TC + cc];
+            tile[i * TC + cc] = x + y;
+            tile[(i + h) * TC + cc] = x - y;
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < R; m++) s[m] = tile[(w * R + m) * kTokCols + lane] * scale;
+    for (int m = 0; m < S::R; m++) s[m] = tile[(r0 + m) * TC + c] * scale;
     __syncthreads();
 }
 

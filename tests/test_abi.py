@@ -109,14 +109,20 @@ def test_decode_checks():
 def test_bwd_workspace_and_checks():
     c = cfg(T=256, ckpt_interval=64)
     n = la.la_bwd_workspace_bytes(c)
-    # per workgroup (B x H x value tiles) the state entering every fourth token of a chunk;
-    # per value tile and token the partial sums (two d_k rows, eight GDN gate terms, beta);
-    # room for recomputed checkpoints
-    nwg = 2 * 2 * 2
-    states = nwg * (64 // 4) * 128 * 64 * 4
-    part = 2 * 2 * 256 * 2 * (2 * 128 + 8 + 1) * 4
+    # INT8 groups of 32: the backward's tiles are 32 value columns wide (4 per head).  Per
+    # workgroup (B x H x tiles) the state entering every fourth token of a chunk; per tile and
+    # token the partial sums (two d_k rows, eight GDN gate terms, beta); room for recomputed
+    # checkpoints
+    nwg = 2 * 2 * 4
+    states = nwg * (64 // 4) * 128 * 32 * 4
+    part = 4 * 2 * 256 * 2 * (2 * 128 + 8 + 1) * 4
     ck = 2 * 2 * 4 * 128 * 128 * 4
     assert n >= states + part + ck and n < states + part + ck + 3 * 256
+    c64 = cfg(T=256, ckpt_interval=64, group=64)   # groups of 64: tiles of 64 columns
+    n64 = la.la_bwd_workspace_bytes(c64)
+    states64 = 2 * 2 * 2 * (64 // 4) * 128 * 64 * 4
+    part64 = 2 * 2 * 256 * 2 * (2 * 128 + 8 + 1) * 4
+    assert n64 >= states64 + part64 + ck and n64 < states64 + part64 + ck + 3 * 256
     assert la.la_bwd_workspace_bytes(cfg(ckpt_interval=0)) == 0
     args = [FAKE] * 5 + [None, None, FAKE, None] + [FAKE] * 6
     with pytest.raises(la.LaError) as e:
