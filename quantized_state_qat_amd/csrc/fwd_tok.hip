@@ -65,14 +65,14 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
     fetch(kTokWaves + w);
     __syncthreads();
 
-    TokOps<S, KDA> op;
-    if (T > 0) tok_read<S, KDA, false>(op, ring, 0, w, lane);
+    // operands of token t are read at the end of token t - 1, into the other of two buffers
+    TokOps<S, KDA> opA, opB;
+    if (T > 0) tok_read<S, KDA, false>(opA, ring, 0, w, lane);
     int ck_next = a.ckpts ? 0 : T;                                        // next checkpoint token
     int q_next = QMODE != LA_QDQ_NONE ? min(p.qdq_interval, T) - 1 : T;  // next rounding token
-    size_t tok = tok0;
 
-#pragma unroll 1
-    for (int t = 0; t < T; t++, tok += H) {
+    auto token = [&](int t, const TokOps<S, KDA>& op, TokOps<S, KDA>& op_next) __attribute__((always_inline)) {
+        const size_t tok = tok0 + static_cast<size_t>(t) * H;
         if ((t & (kTokWaves - 1)) == kTokWaves - 2) {  // publish the next block, fetch the one after
             const int u = t + 2 + w;
             publish(u);
@@ -88,12 +88,17 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
         float u, delta, o;
         tok_step<S, KDA, HAD>(s, op, red[t & 1], w, lane, u, delta, o);
         if (a.o && w == (t & (kTokWaves - 1)) && lane < TC) store_elem(a.o, tok * DV + col, p.out_dt, o);
-        if (t + 1 < T) tok_read<S, KDA, false>(op, ring, (t + 1) % kTokRing, w, lane);
+        if (t + 1 < T) tok_read<S, KDA, false>(op_next, ring, (t + 1) % kTokRing, w, lane);
         if (t == q_next) {
             q_next = min(q_next + p.qdq_interval, T - 1);
             if (q_next == t) q_next = T;
             tok_qdq<S>(s, qsh, w, lane);
         }
+    };
+#pragma unroll 1
+    for (int t = 0; t < T; t += 2) {
+        token(t, opA, opB);
+        if (t + 1 < T) token(t + 1, opB, opA);
     }
     if (a.ST) {
         if (HAD && !p.rot) tok_rotate<S>(s, tile, w, lane, 1.0f / DK);

@@ -45,33 +45,49 @@ struct TokParams {
 // (lane i <-> 15 - i), half mirror (i <-> 7 - i within 8), and the quad exchanges i ^ 2 and
 // i ^ 1.  Once a lane carries a single value the remaining levels reduce it in place.
 // The row a lane ends with is reduce_scatter_row<N, G>(lane).
-struct OpMax {
-    static __device__ __forceinline__ float f(float a, float b) { return fmaxf(a, b); }
+// Op::T is the value type moved between lanes.  OpMaxAbs reduces absolute values as their
+// bit patterns (sign cleared): for non-negative floats the unsigned integer order is the float
+// order, and the integer max needs none of the canonicalizing moves a float max takes after a
+// cross-lane move.
+struct OpMaxAbs {
+    using T = uint32_t;
+    static __device__ __forceinline__ T f(T a, T b) { return a > b ? a : b; }
 };
 struct OpAdd {
-    static __device__ __forceinline__ float f(float a, float b) { return a + b; }
+    using T = float;
+    static __device__ __forceinline__ T f(T a, T b) { return a + b; }
 };
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+template <class T>
+__device__ __forceinline__ uint32_t as_u32(T x) { return __builtin_bit_cast(uint32_t, x); }
+template <class T>
+__device__ __forceinline__ T from_u32(uint32_t x) { return __builtin_bit_cast(T, x); }
+
+// DPP move with every lane in range (bound_ctrl set, all rows and banks): the move folds into
+// the instruction that consumes it.
+template <int CTRL, class T>
+__device__ __forceinline__ T dpp_mov(T x) {
+    return from_u32<T>(static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(as_u32(x)), CTRL, 0xF, 0xF, true)));
 }
 
 // One swap level over lanes 32 (SW = 32) or 16 (SW = 16) apart.  After a permlane swap of
 // (A, B), A's register holds in the lower half of each lane pair the lane's own A and in the
 // upper half the partner's B, and B's register the partner's A and the lane's own B.
 template <class Op, int SW, int N>
-__device__ __forceinline__ void rs_swap_level(float* x) {
+__device__ __forceinline__ void rs_swap_level(typename Op::T* x) {
+    using T = typename Op::T;
+    auto swap = [](T a, T b) __attribute__((always_inline)) {
+        return SW == 32 ? __builtin_amdgcn_permlane32_swap(as_u32(a), as_u32(b), false, false)
+                        : __builtin_amdgcn_permlane16_swap(as_u32(a), as_u32(b), false, false);
+    };
     if constexpr (N == 1) {
-        const auto r = SW == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[0]), false, false)
-                                : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[0]), __float_as_uint(x[0]), false, false);
-        x[0] = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        const auto r = swap(x[0], x[0]);
+        x[0] = Op::f(from_u32<T>(r[0]), from_u32<T>(r[1]));
     } else {
 #pragma unroll
         for (int i = 0; i < N / 2; i++) {
-            const auto r = SW == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + N / 2]), false, false)
-                                    : __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(x[i + N / 2]), false, false);
-            x[i] = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+            const auto r = swap(x[i], x[i + N / 2]);
+            x[i] = Op::f(from_u32<T>(r[0]), from_u32<T>(r[1]));
         }
     }
 }
@@ -79,15 +95,16 @@ __device__ __forceinline__ void rs_swap_level(float* x) {
 // One DPP level: the partner differs from the lane in bit BIT of the lane index (and the
 // pattern keeps every bit above BIT within the row of 16).
 template <class Op, int CTRL, int BIT, int N>
-__device__ __forceinline__ void rs_dpp_level(float* x, int lane) {
+__device__ __forceinline__ void rs_dpp_level(typename Op::T* x, int lane) {
+    using T = typename Op::T;
     if constexpr (N == 1) {
         x[0] = Op::f(x[0], dpp_mov<CTRL>(x[0]));
     } else {
         const bool hi = (lane >> BIT) & 1;
 #pragma unroll
         for (int i = 0; i < N / 2; i++) {
-            const float send = hi ? x[i] : x[i + N / 2];
-            const float keep = hi ? x[i + N / 2] : x[i];
+            const T send = hi ? x[i] : x[i + N / 2];
+            const T keep = hi ? x[i + N / 2] : x[i];
             x[i] = Op::f(keep, dpp_mov<CTRL>(send));
         }
     }
@@ -96,7 +113,7 @@ __device__ __forceinline__ void rs_dpp_level(float* x, int lane) {
 constexpr int kCtrlMirror = 0x140, kCtrlHalfMirror = 0x141, kCtrlXor2 = 0x4E, kCtrlXor1 = 0xB1;
 
 template <class Op, int N, int G>
-__device__ __forceinline__ float reduce_scatter(float* x, int lane) {
+__device__ __forceinline__ typename Op::T reduce_scatter(typename Op::T* x, int lane) {
     static_assert(G == 16 || G == 32 || G == 64, "groups of 16, 32 or 64 lanes");
     constexpr int N1 = G == 64 ? (N > 1 ? N / 2 : 1) : N;
     constexpr int N2 = G >= 32 ? (N1 > 1 ? N1 / 2 : 1) : N1;
@@ -386,10 +403,10 @@ __device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>&
 // whole wave, when any lane has one).
 template <int R, int G>
 __device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
-    float x[R];
+    uint32_t x[R];
 #pragma unroll
-    for (int m = 0; m < R; m++) x[m] = fabsf(s[m]);
-    const float mx = reduce_scatter<OpMax, R, G>(x, lane);
+    for (int m = 0; m < R; m++) x[m] = __float_as_uint(s[m]) & 0x7FFFFFFFu;
+    const float mx = __uint_as_float(reduce_scatter<OpMaxAbs, R, G>(x, lane));
     const int row = reduce_scatter_row<R, G>(lane), grp = lane / G;
     constexpr float c127 = 1.0f / 127.0f;
     const float q0 = mx * c127;
