@@ -50,13 +50,15 @@ __device__ __forceinline__ void tok_adjoint(const float (&st)[S::R], float u, fl
     constexpr float c1 = HAD ? 1.0f / DK : 1.0f;
     constexpr int GW = PartLayout<DK, KDA>::GW;
     const int row = tok_row0<S>(w, lane) + reduce_scatter_row<R, TC>(lane);
+    // c1 is a power of two: (q c1) do and q (c1 do) round to the same value
+    const float c1do = c1 * op.dj;
     float sa[R], x[R];
     float pd = 0.0f;
 #pragma unroll
     for (int m = 0; m < R; m++) {
         sa[m] = (KDA ? op.ar[m] : op.a) * st[m];                     // S~
         const float spm = __builtin_fmaf(op.kr[m], dl, sa[m]);       // S' (before rounding)
-        lam[m] = __builtin_fmaf(op.qr[m] * c1, op.dj, lam[m]);       // dS' = lambda + qq do^T
+        lam[m] = __builtin_fmaf(op.qr[m], c1do, lam[m]);             // dS' = lambda + qq do^T
         x[m] = spm * op.dj;
         pd = __builtin_fmaf(lam[m], op.kr[m], pd);
     }
@@ -72,10 +74,11 @@ __device__ __forceinline__ void tok_adjoint(const float (&st)[S::R], float u, fl
     for (int i = 1; i < kTokWaves; i++) ddel += r[i];
     const float x1 = reduce_scatter<OpAdd, R, TC>(x, lane);
     const float du = -op.beta * ddel;
+    const float c1du = c1 * du;
 #pragma unroll
     for (int m = 0; m < R; m++) {
-        x[m] = __builtin_fmaf(lam[m], dl, c1 * (sa[m] * du));       // dku + c1 dkp
-        lam[m] = __builtin_fmaf(op.kr[m] * c1, du, lam[m]);          // dS~ = dS' + kp du^T
+        x[m] = __builtin_fmaf(lam[m], dl, sa[m] * c1du);            // dku + c1 dkp
+        lam[m] = __builtin_fmaf(op.kr[m], c1du, lam[m]);             // dS~ = dS' + kp du^T
     }
     const float x2 = reduce_scatter<OpAdd, R, TC>(x, lane);
     part[row] = x1;
@@ -158,6 +161,8 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     for (int c = p.nck - 1; c >= 0; c--) {
         const int t0 = c * C, t1 = min(T, t0 + C);
         const int nb = nblocks(c);
+        const int last_sub = ((t1 - t0 - 1) / kSubTok) * kSubTok;  // chunk offset of the last stored state
+
         // ---------------- phase A: advance through the chunk, storing the state entering
         // every fourth token (the chunk's first state is its checkpoint)
         {
@@ -173,11 +178,14 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                 else publish(nt, c, j);  // phase B starts with the same block
 #pragma unroll 1
                 for (int i = 0; i < nt; i++) {
-                    if ((i % kSubTok) == 0 && (j > 0 || i > 0)) {
-                        float* dst = wsS + static_cast<size_t>(kBlkTok / kSubTok * j + i / kSubTok) * DK * TC;
+                    const int off = kBlkTok * j + i;  // token offset in the chunk
+                    if ((off % kSubTok) == 0 && off > 0) {
+                        float* dst = wsS + static_cast<size_t>(off / kSubTok) * DK * TC;
 #pragma unroll
                         for (int m = 0; m < R; m++) dst[(r0 + m) * TC + lane % TC] = s[m];
                     }
+                    // the last group of the chunk is recomputed in phase B from its stored state
+                    if (off >= last_sub) break;
                     TokOps<S, KDA> op;
                     tok_read<S, KDA, true>(op, ring, i, w, lane);
                     float u, dl, o;

@@ -23,6 +23,8 @@
 #include "la_device.hpp"
 #include "la_internal.hpp"
 
+#include <type_traits>
+
 namespace la {
 
 constexpr int kTokWaves = 8;                  // waves per workgroup = tokens per block
@@ -184,25 +186,51 @@ struct TokInputs {
 // word (two elements) per lane, element 2 lane + e; fp32 rows as element lane + 64 e.
 __device__ __forceinline__ int tok_elem(bool bf16, int lane, int e) { return bf16 ? 2 * lane + e : lane + 64 * e; }
 
+// Value of lane ^ M (M a power of two below 64), by DPP within rows of 16 lanes and the
+// permlane swaps across rows.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+    if constexpr (M == 1) return dpp_mov<kCtrlXor1>(x);
+    else if constexpr (M == 2) return dpp_mov<kCtrlXor2>(x);
+    else if constexpr (M == 4) {
+        const float up = dpp_mov<0x104>(x), dn = dpp_mov<0x114>(x);  // row_shl:4, row_shr:4
+        return (lane & 4) ? dn : up;
+    } else if constexpr (M == 8) return dpp_mov<0x128>(x);       // row_ror:8
+    else {
+        const Pair p = M == 16 ? swap16(x) : swap32(x);
+        return (lane & M) ? p.a : p.b;
+    }
+}
+
 // Unnormalized Sylvester Walsh-Hadamard transform of a length-DK vector held in that layout:
-// the in-lane element bit is one butterfly stage, every lane bit one more (lane ^ mask).
+// the in-lane element bit is one butterfly stage, every lane bit one more (partner lane ^ m,
+// new value partner + x or partner - x by the lane's side).
 template <int DK>
 __device__ __forceinline__ void lane_wht(float& x0, float& x1, int lane, bool bf16) {
-    auto stage = [&](int m) __attribute__((always_inline)) {
-        const bool hi = (lane & m) != 0;
-        const float p0 = xor_shfl(x0, m), p1 = xor_shfl(x1, m);
-        x0 = hi ? p0 - x0 : x0 + p0;
-        x1 = hi ? p1 - x1 : x1 + p1;
+    auto stage = [&](auto mc) __attribute__((always_inline)) {
+        constexpr int M = decltype(mc)::value;
+        const float sg = (lane & M) ? -1.0f : 1.0f;
+        const float p0 = lane_xor<M>(x0, lane), p1 = lane_xor<M>(x1, lane);
+        x0 = __builtin_fmaf(sg, x0, p0);
+        x1 = __builtin_fmaf(sg, x1, p1);
     };
+    auto lane_stages = [&](auto first) __attribute__((always_inline)) {  // lane bits m = 1 .. < bound
+        constexpr int B = decltype(first)::value;                        // number of lane bits
+        if constexpr (B > 0) stage(std::integral_constant<int, 1>{});
+        if constexpr (B > 1) stage(std::integral_constant<int, 2>{});
+        if constexpr (B > 2) stage(std::integral_constant<int, 4>{});
+        if constexpr (B > 3) stage(std::integral_constant<int, 8>{});
+        if constexpr (B > 4) stage(std::integral_constant<int, 16>{});
+        if constexpr (B > 5) stage(std::integral_constant<int, 32>{});
+    };
+    constexpr int LOG = DK == 128 ? 7 : DK == 64 ? 6 : DK == 32 ? 5 : 4;
     if (bf16) {
         const float a = x0 + x1, b = x0 - x1;
         x0 = a;
         x1 = b;
-#pragma unroll
-        for (int m = 1; 2 * m < DK; m <<= 1) stage(m);
+        lane_stages(std::integral_constant<int, LOG - 1>{});
     } else {
-#pragma unroll
-        for (int m = 1; m < DK && m < 64; m <<= 1) stage(m);
+        lane_stages(std::integral_constant<int, (LOG < 6 ? LOG : 6)>{});
         if (DK > 64) {
             const float a = x0 + x1, b = x0 - x1;
             x0 = a;
