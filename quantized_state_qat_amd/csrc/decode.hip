@@ -209,13 +209,12 @@ __global__ __launch_bounds__(16 * (DK / R)) void decode_kernel(DecParams p, Deco
         constexpr int QPG = G / 4;  // quads per group
 #pragma unroll
         for (int m = 0; m < R; m++) {
-            const float mx = group_max<QPG>(max4abs(s[m]));
-            const float sc = int8_scale(mx);
+            const float mx = group_max_abs<QPG>(max4abs(s[m]));
+            float sc, y;
             float4 c;
-            if (sc >= kFastQuotMinScale) {
-                const float y = 1.0f / sc;
-                c = make_float4(int8_code_y(s[m].x, sc, y), int8_code_y(s[m].y, sc, y),
-                                int8_code_y(s[m].z, sc, y), int8_code_y(s[m].w, sc, y));
+            if (int8_scale_recip(mx, sc, y)) {
+                c = make_float4(int8_code_fast(s[m].x, sc, y), int8_code_fast(s[m].y, sc, y),
+                                int8_code_fast(s[m].z, sc, y), int8_code_fast(s[m].w, sc, y));
             } else {
                 c = make_float4(int8_code(s[m].x, sc), int8_code(s[m].y, sc), int8_code(s[m].z, sc),
                                 int8_code(s[m].w, sc));

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace la {
 
 constexpr int kWave = 64;
@@ -70,6 +72,24 @@ __device__ __forceinline__ float group_max(float x) {
     return x;
 }
 
+// Max of |x| over aligned groups of N lanes (N <= 16), as the unsigned max of the sign-cleared
+// bit patterns: for non-negative floats the integer order is the float order, and the integer
+// max needs no canonicalizing moves after the DPP exchange.  Result (>= 0) in every lane.
+template <int N>
+__device__ __forceinline__ float group_max_abs(float x) {
+    static_assert(N <= 16, "within a row of 16 lanes");
+    uint32_t u = __float_as_uint(x) & 0x7FFFFFFFu;
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    auto dp = [](uint32_t v, auto ctrl) {
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    if (N >= 2) u = mx(u, dp(u, std::integral_constant<int, kDppXor1>{}));
+    if (N >= 4) u = mx(u, dp(u, std::integral_constant<int, kDppXor2>{}));
+    if (N >= 8) u = mx(u, dp(u, std::integral_constant<int, kDppHalfMirror>{}));
+    if (N >= 16) u = mx(u, dp(u, std::integral_constant<int, kDppMirror>{}));
+    return __uint_as_float(u);
+}
+
 // Sum over aligned groups of N lanes; result in every lane.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
@@ -129,6 +149,37 @@ __device__ __forceinline__ float int8_code_y(float x, float s, float y) {
 }
 
 constexpr float kFastQuotMinScale = 0x1p-100f;      // INT8: decisions need |x/s| >= 1/2
+
+// s = amax/127 (1 when amax == 0) and y = RN(1/s) without a division, both equal to the IEEE
+// quotients for s >= 2^-100:
+//  * s: RN(amax * c), c = RN(1/127), then one residual correction r = amax - 127 q (exact by
+//    FMA), s = RN(q + r c) -- checked exhaustively against amax / 127 over all significands
+//    in ten binades from 2^-95 to 2^100 (the map commutes with scaling by powers of two there);
+//  * y: the hardware reciprocal refined by one Newton step, fma(fma(-s, r, 1), r, r) --
+//    checked exhaustively against 1 / s on gfx950 in twelve binades from 2^-100 to 2^99.
+// Returns false (and the IEEE s) when s < 2^-100; callers then use the division per element.
+__device__ __forceinline__ bool int8_scale_recip(float amax, float& s, float& y) {
+    constexpr float c127 = 1.0f / 127.0f;
+    const float q0 = amax * c127;
+    s = __builtin_fmaf(__builtin_fmaf(-127.0f, q0, amax), c127, q0);
+    s = amax > 0.0f ? s : 1.0f;
+    const bool fast = s >= kFastQuotMinScale;
+    if (!fast) s = int8_scale(amax);
+    const float r = __builtin_amdgcn_rcpf(s);
+    y = __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r);
+    return fast;
+}
+
+// INT8 code of x for a scale s >= 2^-100 with y = RN(1/s): rint of the correctly rounded
+// quotient x / s (quot_rn without the sign restore, which only decides the sign of an exactly
+// zero quotient).  No clamp: with |x| <= amax and s = RN(amax/127), |x/s| <= 127 (1 + 2^-24),
+// which rounds to at most 127.
+__device__ __forceinline__ float int8_code_fast(float x, float s, float y) {
+    float q = x * y;
+    q = __builtin_fmaf(__builtin_fmaf(-s, q, x), y, q);
+    q = __builtin_fmaf(__builtin_fmaf(-s, q, x), y, q);
+    return rintf(q);
+}
 constexpr float kFastQuotMinScaleE4M3 = 0x1p-80f;   // E4M3: decisions down to |x/s| ~ 2^-10
 
 // ------------------------------------------------------------------ E4M3FN codec

@@ -415,20 +415,11 @@ __device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>&
 
 // ------------------------------------------------------------------ codecs
 // INT8 groups of G columns: each lane takes the maximum of one (row, group) by a
-// reduce-scatter, computes s = amax / 127 (1 when amax = 0) and y = RN(1 / s) once, and the
-// wave reads every (s, y) of its groups back from LDS (scr: 64 / G x R float2 per wave).
-//  * s: RN(amax * c) with c = RN(1/127), then one residual correction r = amax - 127 q (exact
-//    by FMA), s = RN(q + r c).  This equals the IEEE quotient amax / 127 for every amax whose
-//    quotient is at least 2^-100 (checked exhaustively over all significands in ten binades
-//    from 2^-95 to 2^100; the map commutes with scaling by powers of two in that range).
-//  * y: the hardware reciprocal refined by one Newton step, fma(fma(-s, r, 1), r, r); equal to
-//    the IEEE quotient 1 / s for every significand (checked exhaustively on gfx950 in twelve
-//    binades from 2^-100 to 2^99).
-//  * per element: x / s correctly rounded from y (quot_rn without the sign restore, which only
-//    affects the sign of an exactly zero quotient), then rint.  No clamp is needed: with
-//    |x| <= amax, |x / s| <= 127 (1 + 2^-24), which rounds to at most 127.
-// A group whose scale is below 2^-100 takes the IEEE division and the clamp instead (the
-// whole wave, when any lane has one).
+// reduce-scatter, computes s = amax / 127 (1 when amax = 0) and y = RN(1 / s) once
+// (int8_scale_recip), and the wave reads every (s, y) of its groups back from LDS (scr: 64 / G
+// x R float2 per wave); each element is then coded by int8_code_fast.  A group whose scale is
+// below 2^-100 takes the IEEE division and the clamp instead (the whole wave, when any lane
+// has one).
 template <int R, int G>
 __device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
     uint32_t x[R];
@@ -436,14 +427,8 @@ __device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
     for (int m = 0; m < R; m++) x[m] = __float_as_uint(s[m]) & 0x7FFFFFFFu;
     const float mx = __uint_as_float(reduce_scatter<OpMaxAbs, R, G>(x, lane));
     const int row = reduce_scatter_row<R, G>(lane), grp = lane / G;
-    constexpr float c127 = 1.0f / 127.0f;
-    const float q0 = mx * c127;
-    float sc = __builtin_fmaf(__builtin_fmaf(-127.0f, q0, mx), c127, q0);
-    sc = mx > 0.0f ? sc : 1.0f;
-    const bool tiny_l = sc < kFastQuotMinScale;
-    if (tiny_l) sc = int8_scale(mx);
-    const float r = __builtin_amdgcn_rcpf(sc);
-    const float y = __builtin_fmaf(__builtin_fmaf(-sc, r, 1.0f), r, r);
+    float sc, y;
+    const bool tiny_l = !int8_scale_recip(mx, sc, y);
     scr[grp * R + row] = make_float2(sc, y);
     const bool tiny = __any(tiny_l);
     __builtin_amdgcn_wave_barrier();
@@ -453,13 +438,7 @@ __device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
     for (int m = 0; m < R; m++) sy[m] = scr[grp * R + m];
     if (!tiny) {
 #pragma unroll
-        for (int m = 0; m < R; m++) {
-            const float xs = s[m], sm = sy[m].x, ym = sy[m].y;
-            float q = xs * ym;
-            q = __builtin_fmaf(__builtin_fmaf(-sm, q, xs), ym, q);
-            q = __builtin_fmaf(__builtin_fmaf(-sm, q, xs), ym, q);
-            s[m] = rintf(q) * sm;
-        }
+        for (int m = 0; m < R; m++) s[m] = int8_code_fast(s[m], sy[m].x, sy[m].y) * sy[m].x;
     } else {
 #pragma unroll
         for (int m = 0; m < R; m++) s[m] = int8_code(s[m], sy[m].x) * sy[m].x;
