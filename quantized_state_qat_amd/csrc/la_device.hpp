@@ -32,6 +32,13 @@ __device__ __forceinline__ void store_elem(void* p, size_t idx, int dtype, float
     else static_cast<uint16_t*>(p)[idx] = f32_to_bf16_bits(x);
 }
 
+// Buffer resource over `bytes` bytes at base: loads past the end return zero and stores there
+// are dropped (raw buffer addressing, 32-bit offsets).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+    const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n), 0x00020000);
+}
+
 // ------------------------------------------------------------------ cross-lane
 // Lane exchanges use DPP (within rows of 16 lanes) and the gfx950 permlane swaps (across
 // rows), never the LDS crossbar.  Every reduction step combines a lane with one partner

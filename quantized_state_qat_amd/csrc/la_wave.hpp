@@ -153,10 +153,6 @@ __device__ __forceinline__ float lane_of(float x, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
-    const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n), 0x00020000);
-}
 
 // ------------------------------------------------------------------ rounding the state
 // LDS for the cross-wave maxima of one workgroup (four waves, 64 columns).  Each rounding
