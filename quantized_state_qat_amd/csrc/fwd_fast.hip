@@ -226,25 +226,25 @@ __global__ __launch_bounds__(kFastThreads) void fwd_fast_kernel(Params p, FwdArg
             if (QMODE == LA_QDQ_INT8_GROUP) {
 #pragma unroll
                 for (int m = 0; m < R; m++) {
-                    const float sc8 = int8_scale(group_max<G>(fabsf(s[m])));
-                    const float c = sc8 >= kFastQuotMinScale ? int8_code_y(s[m], sc8, 1.0f / sc8) : int8_code(s[m], sc8);
+                    float sc8, y;
+                    const float c = int8_scale_recip(group_max_abs<G>(s[m]), sc8, y) ? int8_code_fast(s[m], sc8, y)
+                                                                                     : int8_code(s[m], sc8);
                     s[m] = c * sc8;
                 }
             } else if (QMODE == LA_QDQ_E4M3_TILE) {
                 float mx = 0.0f;
 #pragma unroll
                 for (int m = 0; m < R; m++) mx = fmaxf(mx, fabsf(s[m]));
-                mx = group_max<64>(mx);
+                mx = wave_max_abs(mx);
                 if (lane == 0) amax_s[w] = mx;
                 __syncthreads();
                 float amax = amax_s[0];
 #pragma unroll
                 for (int ww = 1; ww < NW; ww++) amax = fmaxf(amax, amax_s[ww]);
-                const float sce = amax > 0.0f ? amax / 448.0f : 1.0f;
-                if (sce >= kFastQuotMinScaleE4M3) {
-                    const float y = 1.0f / sce;
+                float sce, y;
+                if (e4m3_scale_recip(amax, sce, y)) {
 #pragma unroll
-                    for (int m = 0; m < R; m++) s[m] = e4m3_round(quot_rn(s[m], sce, y)) * sce;
+                    for (int m = 0; m < R; m++) s[m] = e4m3_round(quot_rn_fast(s[m], sce, y)) * sce;
                 } else {
 #pragma unroll
                     for (int m = 0; m < R; m++) s[m] = e4m3_round(s[m] / sce) * sce;

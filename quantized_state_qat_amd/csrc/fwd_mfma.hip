@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
     constexpr int GB = GF32 ? 4 : 2, OB = OBF16 ? 2 : 4;
 
     __shared__ WaveQdqShared<DK, QMODE, G> qsh;
-    __shared__ uint16_t kT[2][DK][kBlk];  // the block's keys, [row][token], by block parity
+    __shared__ uint16_t kT[kWaveTileWaves][2][DK][kBlk];  // per wave: the block's keys, [row][token], by block parity
     __shared__ BlockShared bsh[kWaveTileWaves];
 
     const int lane = threadIdx.x & 63;
@@ -230,22 +230,15 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             sh.rgam[c] = 1.0f / gam;
             sh.beta[c] = valid ? bv : 0.0f;
         }
-        // the block's keys, transposed into LDS for the update (wave w writes dwords
-        // 4 w .. 4 w + 3 of each lane: rows 32 w + 8 g .. + 7; the four waves hold the same keys)
-        auto write_kT = [&](auto wc) __attribute__((always_inline)) {  // static register indices for wave wc
-            constexpr int W = decltype(wc)::value;
+        // the block's keys, transposed into this wave's LDS copy for the update (dword j of
+        // a lane holds rows 32 (j / 4) + 8 g + 2 (j % 4) and the next), so that the update
+        // waits for no other wave
+        uint16_t (*kTw)[kBlk] = kT[w][par];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const uint32_t wd = kword(cur.k, 4 * W + i);
-                kT[par][32 * W + 8 * g + 2 * i][c] = static_cast<uint16_t>(wd & 0xFFFFu);
-                kT[par][32 * W + 8 * g + 2 * i + 1][c] = static_cast<uint16_t>(wd >> 16);
-            }
-        };
-        switch (w) {
-            case 0: write_kT(std::integral_constant<int, 0>{}); break;
-            case 1: write_kT(std::integral_constant<int, 1>{}); break;
-            case 2: write_kT(std::integral_constant<int, 2>{}); break;
-            default: write_kT(std::integral_constant<int, 3>{}); break;
+        for (int j = 0; j < 16; j++) {
+            const uint32_t wd = kword(cur.k, j);
+            kTw[32 * (j / 4) + 8 * g + 2 * (j % 4)][c] = static_cast<uint16_t>(wd & 0xFFFFu);
+            kTw[32 * (j / 4) + 8 * g + 2 * (j % 4) + 1][c] = static_cast<uint16_t>(wd >> 16);
         }
         fetch(nxt, t0 + kBlk);
         *reinterpret_cast<f4*>(&sh.Gk[c][4 * g]) = gk;  // symmetric: [c][i] = k_i . k_c
@@ -306,11 +299,12 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             const f4 ddv = {sel[0], sel[1], sel[2], sel[3]};
             bf4 dh, dl, dl2;
             split3(ddv, dh, dl, dl2);
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
             for (int tau = 0; tau < 8; tau++) {
                 const int row = state_row(4 * tau + (c & 3), c >> 2);
-                const bf4 kr = *reinterpret_cast<const bf4*>(&kT[par][row][4 * g]);
+                const bf4 kr = *reinterpret_cast<const bf4*>(&kTw[row][4 * g]);
                 f4 st = {s[4 * tau], s[4 * tau + 1], s[4 * tau + 2], s[4 * tau + 3]};
                 st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, kr), __builtin_bit_cast(s4, dl2), st, 0, 0, 0);
                 st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, kr), __builtin_bit_cast(s4, dl), st, 0, 0, 0);
@@ -327,7 +321,6 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             for (int m = 0; m < R; m++) s[m] *= gend;
         } else {
             // steep gates: token by token, each gate applied to the state
-            __syncthreads();  // keeps the barrier count of the block
 #pragma unroll 1
             for (int j = 0; j < kBlk && t0 + j < T; j++) {
                 const float aj = lane_of(eg, j);

@@ -79,12 +79,12 @@ __device__ __forceinline__ float group_max(float x) {
     return x;
 }
 
-// Max of |x| over aligned groups of N lanes (N <= 16), as the unsigned max of the sign-cleared
-// bit patterns: for non-negative floats the integer order is the float order, and the integer
-// max needs no canonicalizing moves after the DPP exchange.  Result (>= 0) in every lane.
+// Max of |x| over aligned groups of N lanes (N a power of two <= 64), as the unsigned max of
+// the sign-cleared bit patterns: for non-negative floats the integer order is the float order,
+// and the integer max needs no canonicalizing moves after a cross-lane exchange.  DPP within
+// rows of 16 lanes, then the permlane swaps.  Result (>= 0) in every lane of the group.
 template <int N>
 __device__ __forceinline__ float group_max_abs(float x) {
-    static_assert(N <= 16, "within a row of 16 lanes");
     uint32_t u = __float_as_uint(x) & 0x7FFFFFFFu;
     auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
     auto dp = [](uint32_t v, auto ctrl) {
@@ -94,6 +94,14 @@ __device__ __forceinline__ float group_max_abs(float x) {
     if (N >= 4) u = mx(u, dp(u, std::integral_constant<int, kDppXor2>{}));
     if (N >= 8) u = mx(u, dp(u, std::integral_constant<int, kDppHalfMirror>{}));
     if (N >= 16) u = mx(u, dp(u, std::integral_constant<int, kDppMirror>{}));
+    if (N >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        u = mx(r[0], r[1]);
+    }
+    if (N >= 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        u = mx(r[0], r[1]);
+    }
     return __uint_as_float(u);
 }
 
@@ -187,6 +195,7 @@ __device__ __forceinline__ float int8_code_fast(float x, float s, float y) {
     q = __builtin_fmaf(__builtin_fmaf(-s, q, x), y, q);
     return rintf(q);
 }
+
 constexpr float kFastQuotMinScaleE4M3 = 0x1p-80f;   // E4M3: decisions down to |x/s| ~ 2^-10
 
 // ------------------------------------------------------------------ E4M3FN codec
@@ -214,6 +223,34 @@ __device__ __forceinline__ void e4m3_round2(float& a, float& b) {
     a = __builtin_amdgcn_cvt_f32_fp8(p, 0);
     b = __builtin_amdgcn_cvt_f32_fp8(p, 1);
 }
+
+// E4M3 tile scale s = amax/448 (1 when amax == 0) and y = RN(1/s) without a division, both
+// equal to the IEEE quotients for s >= 2^-80 (the fast-quotient domain of E4M3 decisions):
+// s from RN(amax * c), c = RN(1/448), and one residual correction -- checked exhaustively
+// against amax / 448 over all significands in ten binades from 2^-95 to 2^100; y as in
+// int8_scale_recip.  Returns false (and the IEEE s) when s < 2^-80.
+__device__ __forceinline__ bool e4m3_scale_recip(float amax, float& s, float& y) {
+    constexpr float c448 = 1.0f / 448.0f;
+    const float q0 = amax * c448;
+    s = __builtin_fmaf(__builtin_fmaf(-448.0f, q0, amax), c448, q0);
+    s = amax > 0.0f ? s : 1.0f;
+    const bool fast = s >= kFastQuotMinScaleE4M3;
+    if (!fast) s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const float r = __builtin_amdgcn_rcpf(s);
+    y = __builtin_fmaf(__builtin_fmaf(-s, r, 1.0f), r, r);
+    return fast;
+}
+
+// x / s correctly rounded from y = RN(1/s) (quot_rn without the sign restore, which only
+// decides the sign of an exactly zero quotient; valid for s >= 2^-100).
+__device__ __forceinline__ float quot_rn_fast(float x, float s, float y) {
+    float q = x * y;
+    q = __builtin_fmaf(__builtin_fmaf(-s, q, x), y, q);
+    return __builtin_fmaf(__builtin_fmaf(-s, q, x), y, q);
+}
+
+// Max of |x| over the 64 lanes of the wave; result (>= 0) in every lane.
+__device__ __forceinline__ float wave_max_abs(float x) { return group_max_abs<64>(x); }
 
 // Bit pattern of an E4M3FN grid value v (|v| <= 448, v on the grid).
 __device__ __forceinline__ uint8_t e4m3_bits(float v) {

@@ -452,18 +452,17 @@ __device__ __forceinline__ void tok_e4m3(float (&s)[R], float* amax_sh, int w, i
     float mx = 0.0f;
 #pragma unroll
     for (int m = 0; m < R; m++) mx = fmaxf(mx, fabsf(s[m]));
-    mx = group_max<64>(mx);
+    mx = wave_max_abs(mx);
     if (lane == 0) amax_sh[w] = mx;
     __syncthreads();
     float amax = amax_sh[0];
 #pragma unroll
     for (int i = 1; i < kTokWaves; i++) amax = fmaxf(amax, amax_sh[i]);
-    const float sce = amax > 0.0f ? amax / 448.0f : 1.0f;
+    float sce, y;
     float yv[R];
-    if (sce >= kFastQuotMinScaleE4M3) {
-        const float y = 1.0f / sce;
+    if (e4m3_scale_recip(amax, sce, y)) {
 #pragma unroll
-        for (int m = 0; m < R; m++) yv[m] = quot_rn(s[m], sce, y);
+        for (int m = 0; m < R; m++) yv[m] = quot_rn_fast(s[m], sce, y);
     } else {
 #pragma unroll
         for (int m = 0; m < R; m++) yv[m] = s[m] / sce;

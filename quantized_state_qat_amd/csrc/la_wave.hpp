@@ -174,18 +174,17 @@ __device__ __forceinline__ void wave_quantize(float* s, WaveQdqShared<DK, QMODE,
         float mx = 0.0f;
 #pragma unroll
         for (int m = 0; m < R; m++) mx = fmaxf(mx, fabsf(s[m]));
-        mx = group_max<64>(mx);
+        mx = wave_max_abs(mx);
         if (lane == 0) sh.amax[qpar][w] = mx;
         __syncthreads();
         float amax = sh.amax[qpar][0];
 #pragma unroll
         for (int ww = 1; ww < kWaveTileWaves; ww++) amax = fmaxf(amax, sh.amax[qpar][ww]);
-        const float sce = amax > 0.0f ? amax / 448.0f : 1.0f;
+        float sce, y;
         float yv[R];
-        if (sce >= kFastQuotMinScaleE4M3) {
-            const float y = 1.0f / sce;
+        if (e4m3_scale_recip(amax, sce, y)) {
 #pragma unroll
-            for (int m = 0; m < R; m++) yv[m] = quot_rn(s[m], sce, y);
+            for (int m = 0; m < R; m++) yv[m] = quot_rn_fast(s[m], sce, y);
         } else {
 #pragma unroll
             for (int m = 0; m < R; m++) yv[m] = s[m] / sce;
@@ -199,7 +198,7 @@ __device__ __forceinline__ void wave_quantize(float* s, WaveQdqShared<DK, QMODE,
     } else if (QMODE == LA_QDQ_INT8_GROUP) {
         float gm[R];
 #pragma unroll
-        for (int m = 0; m < R; m++) gm[m] = group_max<(G < kWaveCols ? G : kWaveCols)>(fabsf(s[m]));
+        for (int m = 0; m < R; m++) gm[m] = group_max_abs<(G < kWaveCols ? G : kWaveCols)>(s[m]);
         if constexpr (G > kWaveCols) {
             constexpr int NG = G / kWaveCols;
             if (c == 0) {
@@ -218,8 +217,8 @@ __device__ __forceinline__ void wave_quantize(float* s, WaveQdqShared<DK, QMODE,
         }
 #pragma unroll
         for (int m = 0; m < R; m++) {
-            const float sc8 = int8_scale(gm[m]);
-            const float cde = sc8 >= kFastQuotMinScale ? int8_code_y(s[m], sc8, 1.0f / sc8) : int8_code(s[m], sc8);
+            float sc8, y;
+            const float cde = int8_scale_recip(gm[m], sc8, y) ? int8_code_fast(s[m], sc8, y) : int8_code(s[m], sc8);
             s[m] = cde * sc8;
         }
     }
