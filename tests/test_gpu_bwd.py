@@ -122,3 +122,26 @@ def test_bwd_full_size_sampled_units():
         np.testing.assert_array_equal(gu1["dS0"][0, 0], g["dS0"][b, h])
         errs = _check_against_oracle(cu, dd, None, dd["do"].f32, None, gu1, gu.TOL_BF16)
         print(f"unit ({b},{h})", {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+STEEP_CASES = [
+    ("gdn_wht_int8g32_i1", synth.Workload("sb1", B=1, T=90, H=2, d_k=64, d_v=128, s0_sigma=0.2, config_id=56),
+     la.LA_QDQ_INT8_GROUP, 32, 1, 1, 16),
+    ("kda_e4m3_i16", synth.Workload("sb2", B=1, T=85, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=57),
+     la.LA_QDQ_E4M3_TILE, 64, 0, 16, 32),
+]
+
+
+@pytest.mark.parametrize("name,w,mode,group,had,interval,ckpt", STEEP_CASES, ids=[x[0] for x in STEEP_CASES])
+def test_bwd_steep_gates(name, w, mode, group, had, interval, ckpt):
+    """Gates whose products leave every rescaling range, one of them underflowing to zero in
+    FP32 (the forward path tests' pattern): the backward applies gates token by token, so
+    these check that decays of 2^-7 per token and a zero gate keep the adjoint finite and
+    on the oracle's."""
+    from tests.test_gpu_fwd_paths import steep_gates
+    d = steep_gates(synth.generate(w, with_do=True, with_dST=True), w)
+    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=had, qdq_interval=interval)
+    c.ckpt_interval = ckpt
+    g = gu.run_bwd(c, d, d["do"].f32, S0=d["S0"].f32, dST=d["dST"].f32)
+    errs = _check_against_oracle(c, d, d["S0"].f32, d["do"].f32, d["dST"].f32, g, gu.TOL_BF16)
+    print(name, {k: f"{v:.2e}" for k, v in errs.items()})

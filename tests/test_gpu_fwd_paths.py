@@ -40,9 +40,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,w,mode,group,interval,kernel", CASES, ids=[c[0] for c in CASES])
-def test_intervals_against_oracle(name, w, mode, group, interval, kernel):
-    d = synth.generate(w)
+def _check_intervals(name, w, d, mode, group, interval, kernel):
     c = gu.cfg_for(w, d, qdq=mode, group=group, qdq_interval=interval if mode != NONE else 1)
     c.ckpt_interval = interval
     assert la.la_fwd_kernel_name(c) == kernel
@@ -77,3 +75,48 @@ def test_intervals_against_oracle(name, w, mode, group, interval, kernel):
     frac = tally.check()
     print(f"{name} [{kernel}]: max output error {worst_o:.3e}, state error {worst_s:.2e}, "
           f"code mismatches {tally.mismatches}/{tally.total} ({frac:.2e})")
+
+
+@pytest.mark.parametrize("name,w,mode,group,interval,kernel", CASES, ids=[c[0] for c in CASES])
+def test_intervals_against_oracle(name, w, mode, group, interval, kernel):
+    _check_intervals(name, w, synth.generate(w), mode, group, interval, kernel)
+
+
+def steep_gates(d, w):
+    """Log gates with stretches that leave the kernels' rescaling ranges: tokens 16..39 at
+    g = -5 (eight tokens decay by about 2^-58, sixteen by 2^-115: the block kernel's
+    token-by-token path and the wave kernel's per-token fold), tokens 40..69 at g = -1.5
+    (a few tokens' product leaves [2^-30, 2^30]: the wave and eight-wave kernels fold the
+    scale back into the state), token 75 at g = -200 (the gate underflows to zero in FP32 and
+    erases the state; in float64 it is 1.4e-87), the rest as drawn.  Per-key gates get the
+    same pattern on even keys only."""
+    g = d["g"].f64.copy()
+    t = np.arange(w.T)
+    for lo, hi, val in ((16, 40, -5.0), (40, 70, -1.5), (75, 76, -200.0)):
+        idx = (slice(None), (t >= lo) & (t < hi))
+        if w.gate == "key":
+            g[idx[0], idx[1], :, 0::2] = val
+        else:
+            g[idx] = val
+    out = dict(d)
+    out["g"] = synth.cast(g, w.gate_dtype)
+    return out
+
+
+STEEP = [
+    ("block_int8g32_i16", W("sbi8", B=1, T=96, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=50), INT8, 32, 16, "block"),
+    ("block_noqdq_i16_f32gate", W("sbnq", B=1, T=90, H=1, d_k=128, d_v=64, gate_dtype="f32",
+                                s0_sigma=0.2, config_id=51), NONE, 32, 16, "block"),
+    ("wave_e4m3_dk64_i64", W("swe4", B=1, T=150, H=2, d_k=64, d_v=128, s0_sigma=0.2, config_id=52), E4M3, 64, 64, "wave"),
+    ("wave_int8g64_i8", W("swi8", B=1, T=85, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=53), INT8, 64, 8, "wave"),
+    ("fast_int8g16_i3", W("sfi8", B=1, T=80, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=54), INT8, 16, 3, "fast"),
+    ("token_kda_int8g32_i16", W("stk", B=1, T=80, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=55),
+     INT8, 32, 16, "token"),
+]
+
+
+@pytest.mark.parametrize("name,w,mode,group,interval,kernel", STEEP, ids=[c[0] for c in STEEP])
+def test_steep_gates_against_oracle(name, w, mode, group, interval, kernel):
+    d = steep_gates(synth.generate(w), w)
+    assert np.min(d["g"].f32) == -200.0
+    _check_intervals("steep " + name, w, d, mode, group, interval, kernel)
