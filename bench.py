@@ -8,6 +8,10 @@ from HBM.  Prints one JSON line with the throughput, the decode kernel's rooflin
 (HBM-bound; algorithmic bytes per launch / mean launch time) and the CPU oracle's rate on the
 host cores for the same step.
 
+The default warm-up is long on purpose: back-to-back decode steps on a fresh process run about
+5% slower for the first hundred or so launches (measured in kernel traces: about 95 us per
+step, settling at 91 us after 100-150 launches), so the timed steps follow 150 untimed ones.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
 """
 from __future__ import annotations
@@ -272,8 +276,8 @@ def profile_mode(steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the long-sequence, KDA and Hadamard forward/backward measurements")
