@@ -20,6 +20,8 @@ FLAGS = [
     "-ffp-contract=off",
     # no packed FP32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs (gfx950 allows it): no accumulator-register copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -53,23 +53,44 @@ typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
 // x = hi + lo + lo2 exactly, each part a bf16 (nearest at each step): the residual of rounding
 // an fp32 value to bf16 is exact in fp32 and has at most 16 significant bits, the residual of
 // that at most 8, which bf16 holds exactly.  Products of exact bf16 inputs with the parts are
 // exact in fp32, so an MFMA over the three parts forms fp32 products (summed in fp32).
-template <typename FV, typename BV>
+// Two values at a time: one packed conversion per part, whose halves widen back by a shift
+// and a mask (11 operations per pair).
+__device__ __forceinline__ void split3_pair(float x0, float x1, uint32_t& hi, uint32_t& lo, uint32_t& lo2) {
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0, x1}, bf2));
+    const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf2));
+    const float q0 = r0 - __uint_as_float(lo << 16), q1 = r1 - __uint_as_float(lo & 0xFFFF0000u);
+    lo2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{q0, q1}, bf2));
+}
+template <int N, typename FV, typename BV>
 __device__ __forceinline__ void split3(const FV& x, BV& hi, BV& lo, BV& lo2) {
-    hi = __builtin_convertvector(x, BV);
-    const FV r1 = x - __builtin_convertvector(hi, FV);
-    lo = __builtin_convertvector(r1, BV);
-    const FV r2 = r1 - __builtin_convertvector(lo, FV);
-    lo2 = __builtin_convertvector(r2, BV);
+    typedef uint32_t uv __attribute__((ext_vector_type(N / 2)));
+    uv h, l, l2;
+#pragma unroll
+    for (int i = 0; i < N / 2; i++) {
+        uint32_t a, b, c;
+        split3_pair(x[2 * i], x[2 * i + 1], a, b, c);
+        h[i] = a;
+        l[i] = b;
+        l2[i] = c;
+    }
+    hi = __builtin_bit_cast(BV, h);
+    lo = __builtin_bit_cast(BV, l);
+    lo2 = __builtin_bit_cast(BV, l2);
 }
 
 // Per-wave LDS of one block.
 struct BlockShared {
     float Gk[kBlk][kBlk];    // [j][i] = k_i . k_j
-    float dd[4][kBlk][4];    // [lane group][column][r]: dd of tokens 4 g + r, for the stage MFMAs
+    float dd[4][kBlk][4];    // [lane group][column][r]: stage values of tokens 4 g + r, for the stage MFMAs
+    float Ms[kBlk][20];      // [c][j] = M[j][c] (rows padded to 20 floats: no bank conflicts)
     float gam[kBlk], rgam[kBlk], beta[kBlk];
 };
 
@@ -114,6 +135,10 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
     const auto rv = make_rsrc(static_cast<const char*>(a.v) + seq0 * DV * 2, seq_tok * DV * 2);
     const auto rgt = make_rsrc(static_cast<const char*>(a.g) + seq0 * GB, seq_tok * GB);
     const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
+    // this unit's checkpoints (the eligibility check keeps their offsets below 2^31)
+    const size_t ck_unit = static_cast<size_t>(p.nck) * DK * DV;
+    const auto rck = make_rsrc(a.ckpts ? a.ckpts + bh * ck_unit : nullptr, a.ckpts ? ck_unit * 4 : 0);
+    const int voff_ck = (state_row(0, g) * DV + col) * 4;
     const bool has_o = a.o != nullptr;
     const auto ro = make_rsrc(has_o ? static_cast<const char*>(a.o) + seq0 * DV * OB : nullptr,
                               has_o ? seq_tok * DV * OB : 0);
@@ -137,12 +162,21 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
     const int voff_kq = (c * H * DK + 8 * g) * 2;
     const int voff_v = (4 * g * H * DV + col) * 2;
     const int voff_gate = c * H * GB;
-    auto fetch = [&](BlockIn& in, int t0) __attribute__((always_inline)) {
+    // The loads of a block in three parts (keys; queries; values, gates and beta).  The four
+    // waves of a workgroup load the same keys and queries, so a burst of all of them fills the
+    // CU's address queue and stalls the issuing wave for about a thousand cycles; the block
+    // loop spreads the parts of the next block's loads over its first steps instead.
+    auto fetch_part = [&](BlockIn& in, int t0, int part) __attribute__((always_inline)) {
         const int so = (t0 * H + h) * DK * 2;
+        if (part == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            in.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so, 0);
-            in.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so, 0);
+            for (int i = 0; i < 4; i++) in.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so, 0);
+            return;
+        }
+        if (part == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) in.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so, 0);
+            return;
         }
 #pragma unroll
         for (int r = 0; r < 4; r++)
@@ -156,6 +190,11 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             in.b = __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, sg, 0);
         }
     };
+    auto fetch = [&](BlockIn& in, int t0) __attribute__((always_inline)) {
+        fetch_part(in, t0, 0);
+        fetch_part(in, t0, 1);
+        fetch_part(in, t0, 2);
+    };
     auto kword = [](const u4 (&x)[4], int i) __attribute__((always_inline)) { return x[i >> 2][i & 3]; };  // dword i of 16
 
     // ---------------------------------------------------------------- outputs
@@ -167,9 +206,9 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
     };
 
     // ---------------------------------------------------------------- block loop
-    // Order of issue within a block: the Gram and projection MFMAs first; while they run, the gates, the
-    // transposed keys and the next block's loads; then the staged recurrence (on P') while
-    // the Q' MFMAs finish; then the output and update MFMAs and the fold.
+    // Order of issue within a block: the Gram MFMAs, with the next block's loads spread over the
+    // gates and the transposed keys; the solve for M interleaved with the projection MFMAs;
+    // dd = M R; the output and update MFMAs; the fold.
     int qpar = 0;
     const int qi = p.qdq_interval;
     int q_next = QMODE != LA_QDQ_NONE ? min(qi, T) - 1 : T;
@@ -181,9 +220,12 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
 #pragma unroll 1
     for (int t0 = 0; t0 < T; t0 += kBlk, par ^= 1) {
         if (t0 == ck_next) {
-            float* dst = a.ckpts + (bh * p.nck + t0 / p.ckpt_interval) * DK * DV;
+            // rows state_row(m, g) = state_row(0, g) + 32 (m / 8) + m % 8: the row step is uniform
+            const int so = t0 / p.ckpt_interval * DK * DV * 4;
 #pragma unroll
-            for (int m = 0; m < R; m++) dst[static_cast<size_t>(state_row(m, g)) * DV + col] = s[m];
+            for (int m = 0; m < R; m++)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s[m]), rck, voff_ck,
+                                                      so + (32 * (m >> 3) + (m & 7)) * DV * 4, 0);
             ck_next += p.ckpt_interval;
         }
 
@@ -195,23 +237,7 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             gk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, ak, gk, 0, 0, 0);
             gq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, aq, gq, 0, 0, 0);
         }
-        // projections of S_0: dk (lane (g, c), register r) = P'_{4g+r}[c], dq = Q'
-        f4 dk = {0.0f, 0.0f, 0.0f, 0.0f}, dq = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const f8 xs = {s[8 * i], s[8 * i + 1], s[8 * i + 2], s[8 * i + 3],
-                           s[8 * i + 4], s[8 * i + 5], s[8 * i + 6], s[8 * i + 7]};
-            bf8 h, l, l2;
-            split3(xs, h, l, l2);
-            const bf8 ak = __builtin_bit_cast(bf8, cur.k[i]), aq = __builtin_bit_cast(bf8, cur.q[i]);
-            dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l2, dk, 0, 0, 0);
-            dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, l2, dq, 0, 0, 0);
-            dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l, dk, 0, 0, 0);
-            dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, l, dq, 0, 0, 0);
-            dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, h, dk, 0, 0, 0);
-            dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, h, dq, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        fetch_part(nxt, t0 + kBlk, 0);  // the next block's keys
 
         // gates of the block: lane (g, c) holds token t0 + c; every row of 16 computes the
         // same inclusive product
@@ -230,6 +256,7 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             sh.rgam[c] = 1.0f / gam;
             sh.beta[c] = valid ? bv : 0.0f;
         }
+        fetch_part(nxt, t0 + kBlk, 1);  // ... its queries
         // the block's keys, transposed into this wave's LDS copy for the update (dword j of
         // a lane holds rows 32 (j / 4) + 8 g + 2 (j % 4) and the next), so that the update
         // waits for no other wave
@@ -240,13 +267,16 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             kTw[32 * (j / 4) + 8 * g + 2 * (j % 4)][c] = static_cast<uint16_t>(wd & 0xFFFFu);
             kTw[32 * (j / 4) + 8 * g + 2 * (j % 4) + 1][c] = static_cast<uint16_t>(wd >> 16);
         }
-        fetch(nxt, t0 + kBlk);
+        fetch_part(nxt, t0 + kBlk, 2);  // ... its values, gates and beta
         *reinterpret_cast<f4*>(&sh.Gk[c][4 * g]) = gk;  // symmetric: [c][i] = k_i . k_c
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_sched_barrier(0);
 
-        if (in_range) {
+        // Gamma_15, applied to the state after either path (1 after the token-by-token one): the
+        // loop-carried state leaves both paths through the same multiply, so no register copies
+        float fold = 1.0f;
+        if (__builtin_expect(in_range, 1)) {
             // per-lane constants of the recurrence: this lane group's tokens 4 g + r ...
             const f4 gam4 = *reinterpret_cast<const f4*>(&sh.gam[4 * g]);
             const f4 rgam4 = *reinterpret_cast<const f4*>(&sh.rgam[4 * g]);
@@ -261,29 +291,60 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
 #pragma unroll
             for (int st = 0; st < 3; st++) ast[st] = c >= 4 * st + 4 ? sh.Gk[c][4 * st + g] : 0.0f;
 
-            // dd in four stages; after stage st, lane group st's values are final and the
-            // MFMA adds their contribution to the later tokens' projections
-            float sel[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            // M = (I + diag(beta) L)^{-1} diag(beta), L the strictly lower part of K K^T, so that
+            // dd = M (V / Gamma - P'): the four-stage solve on the identity (lane (g, c) solves
+            // column c for tokens 4 g .. 4 g + 3; after stage st, lane group st's values are final
+            // and the stage MFMA adds their contribution to the later tokens).  It needs only the
+            // keys and beta, so its stages are interleaved with the slices of the projections of
+            // the entering state, whose MFMAs run while a stage waits on its own results.
+            // Projections: dk (lane (g, c), register r) = P'_{4g+r}[c], dq = Q'.
+            f4 dk = {0.0f, 0.0f, 0.0f, 0.0f}, dq = {0.0f, 0.0f, 0.0f, 0.0f}, dm = {0.0f, 0.0f, 0.0f, 0.0f};
+            f4 selm = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int st = 0; st < 4; st++) {
-                const float x0 = beta4[0] * __builtin_fmaf(bf_lo(cur.v[0]), rgam4[0], -dk[0]);
-                const float x1 = beta4[1] * __builtin_fmaf(bf_lo(cur.v[1]), rgam4[1], -__builtin_fmaf(c01, x0, dk[1]));
-                const float x2 = beta4[2] * __builtin_fmaf(bf_lo(cur.v[2]), rgam4[2],
-                                                           -__builtin_fmaf(c12, x1, __builtin_fmaf(c02, x0, dk[2])));
-                const float x3 = beta4[3] * __builtin_fmaf(bf_lo(cur.v[3]), rgam4[3],
-                                                           -__builtin_fmaf(c23, x2, __builtin_fmaf(c13, x1, __builtin_fmaf(c03, x0, dk[3]))));
-                if (g == st) {
-                    sel[0] = x0; sel[1] = x1; sel[2] = x2; sel[3] = x3;
-                }
+                const float e0 = 4 * g == c ? 1.0f : 0.0f, e1 = 4 * g + 1 == c ? 1.0f : 0.0f;
+                const float e2 = 4 * g + 2 == c ? 1.0f : 0.0f, e3 = 4 * g + 3 == c ? 1.0f : 0.0f;
+                const float x0 = beta4[0] * (e0 - dm[0]);
+                const float x1 = beta4[1] * (e1 - __builtin_fmaf(c01, x0, dm[1]));
+                const float x2 = beta4[2] * (e2 - __builtin_fmaf(c12, x1, __builtin_fmaf(c02, x0, dm[2])));
+                const float x3 = beta4[3] * (e3 - __builtin_fmaf(c23, x2, __builtin_fmaf(c13, x1, __builtin_fmaf(c03, x0, dm[3]))));
+                if (g == st) selm = f4{x0, x1, x2, x3};
                 if (st < 3) {
                     const f4 xv = {x0, x1, x2, x3};
                     *reinterpret_cast<f4*>(&sh.dd[g][c][0]) = xv;
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                    const float bst = sh.dd[st][c][g];  // B: lane (kk, n) = dd_{4 st + kk}[n]
-                    dk = __builtin_amdgcn_mfma_f32_16x16x4f32(ast[st], bst, dk, 0, 0, 0);
+                    const float bst = sh.dd[st][c][g];  // B: lane (kk, n) = M[4 st + kk][n]
+                    dm = __builtin_amdgcn_mfma_f32_16x16x4f32(ast[st], bst, dm, 0, 0, 0);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                // slice st of the projections (state rows 32 st .. 32 st + 31 of this lane's list)
+                const f8 xs = {s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3],
+                               s[8 * st + 4], s[8 * st + 5], s[8 * st + 6], s[8 * st + 7]};
+                bf8 h, l, l2;
+                split3<8>(xs, h, l, l2);
+                const bf8 ak = __builtin_bit_cast(bf8, cur.k[st]), aq = __builtin_bit_cast(bf8, cur.q[st]);
+                dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l2, dk, 0, 0, 0);
+                dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, l2, dq, 0, 0, 0);
+                dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l, dk, 0, 0, 0);
+                dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, l, dq, 0, 0, 0);
+                dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, h, dk, 0, 0, 0);
+                dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, h, dq, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            // M transposed through LDS: lane (g, c) needs M[c][4 g + s], the A operand of slice s
+            *reinterpret_cast<f4*>(&sh.Ms[c][4 * g]) = selm;
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            // dd = M R with R = V / Gamma - P': slice s pairs input token 4 g + s (lane group g)
+            // with A = M[c][4 g + s] and B = R[4 g + s][c], this lane's register s of R
+            f4 ddm = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int sl = 0; sl < 4; sl++) {
+                const float rr = __builtin_fmaf(bf_lo(cur.v[sl]), rgam4[sl], -dk[sl]);
+                ddm = __builtin_amdgcn_mfma_f32_16x16x4f32(sh.Ms[4 * g + sl][c], rr, ddm, 0, 0, 0);
+            }
+            const float sel[4] = {ddm[0], ddm[1], ddm[2], ddm[3]};
 
             // o_i = Gamma_i (Q'_i + sum_{j <= i} (k_j . q_i) dd_j)
             f4 ov = dq;
@@ -298,7 +359,7 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             // of those tokens there; B (tokens 4 g + j, column c) = dd, in three bf16 parts
             const f4 ddv = {sel[0], sel[1], sel[2], sel[3]};
             bf4 dh, dl, dl2;
-            split3(ddv, dh, dl, dl2);
+            split3<4>(ddv, dh, dl, dl2);
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
@@ -316,9 +377,7 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
 #pragma unroll
                 for (int r = 0; r < 4; r++) store_o(t0, r, gam4[r] * ov[r]);
             }
-            const float gend = lane_of(gam, kBlk - 1);
-#pragma unroll
-            for (int m = 0; m < R; m++) s[m] *= gend;
+            fold = lane_of(gam, kBlk - 1);
         } else {
             // steep gates: token by token, each gate applied to the state
 #pragma unroll 1
@@ -350,6 +409,9 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
                 }
             }
         }
+
+#pragma unroll
+        for (int m = 0; m < R; m++) s[m] *= fold;
 
         if (min(t0 + kBlk, T) - 1 == q_next) {
             wave_quantize<R, QMODE, G>(s, qsh, lane, w, qpar);
@@ -390,7 +452,9 @@ bool fwd_mfma_eligible(const la_config& c) {
     if (c.ckpt_interval > 0 && c.ckpt_interval % kBlk != 0) return false;
     // 32-bit buffer offsets within one sequence, the prefetched block included
     const size_t span = static_cast<size_t>(c.T + 2 * kBlk) * c.H * (c.d_k > c.d_v ? c.d_k : c.d_v) * 4;
-    return span < (static_cast<size_t>(1) << 31);
+    // and within one unit's checkpoints
+    const size_t ck_span = static_cast<size_t>(n_ckpts(c)) * c.d_k * c.d_v * 4;
+    return span < (static_cast<size_t>(1) << 31) && ck_span < (static_cast<size_t>(1) << 31);
 }
 
 hipError_t launch_fwd_mfma(const la_config& c, const FwdArgs& a, hipStream_t s) {
