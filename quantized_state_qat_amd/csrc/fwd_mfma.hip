@@ -45,6 +45,9 @@ constexpr int kBlk = 16;                       // tokens per block
 constexpr int kMThreads = kWaveTileWaves * 64;  // 4 waves = 64 value columns
 constexpr float kGammaLo = 0x1p-60f, kGammaHi = 0x1p60f;
 constexpr int kDppRowShr = 0x110;              // row_shr:n = kDppRowShr + n
+// LDS row of one token's 128 keys, in bf16 elements: 320 bytes, so that the transposed reads of
+// the update (four tokens 320 bytes apart, four 16-byte row offsets) hit distinct banks
+constexpr int kKeyRow = 160;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f8 __attribute__((ext_vector_type(8)));
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
     constexpr int GB = GF32 ? 4 : 2, OB = OBF16 ? 2 : 4;
 
     __shared__ WaveQdqShared<DK, QMODE, G> qsh;
-    __shared__ uint16_t kT[kWaveTileWaves][2][DK][kBlk];  // per wave: the block's keys, [row][token], by block parity
+    __shared__ uint16_t kN[kWaveTileWaves][kBlk][kKeyRow];  // per wave: the block's keys, [token][row]
     __shared__ BlockShared bsh[kWaveTileWaves];
 
     const int lane = threadIdx.x & 63;
@@ -195,7 +198,6 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
         fetch_part(in, t0, 1);
         fetch_part(in, t0, 2);
     };
-    auto kword = [](const u4 (&x)[4], int i) __attribute__((always_inline)) { return x[i >> 2][i & 3]; };  // dword i of 16
 
     // ---------------------------------------------------------------- outputs
     const int voff_o = (4 * g * H * DV + col) * OB;  // register r: token t0 + 4 g + r
@@ -216,9 +218,8 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
 
     BlockIn cur, nxt;
     fetch(cur, 0);
-    int par = 0;
 #pragma unroll 1
-    for (int t0 = 0; t0 < T; t0 += kBlk, par ^= 1) {
+    for (int t0 = 0; t0 < T; t0 += kBlk) {
         if (t0 == ck_next) {
             // rows state_row(m, g) = state_row(0, g) + 32 (m / 8) + m % 8: the row step is uniform
             const int so = t0 / p.ckpt_interval * DK * DV * 4;
@@ -257,16 +258,11 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             sh.beta[c] = valid ? bv : 0.0f;
         }
         fetch_part(nxt, t0 + kBlk, 1);  // ... its queries
-        // the block's keys, transposed into this wave's LDS copy for the update (dword j of
-        // a lane holds rows 32 (j / 4) + 8 g + 2 (j % 4) and the next), so that the update
-        // waits for no other wave
-        uint16_t (*kTw)[kBlk] = kT[w][par];
+        // the block's keys into this wave's own LDS copy for the update, as loaded (token c,
+        // rows 32 i + 8 g .. + 7 from load i), so that the update waits for no other wave
+        uint16_t (*kNw)[kKeyRow] = kN[w];
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-            const uint32_t wd = kword(cur.k, j);
-            kTw[32 * (j / 4) + 8 * g + 2 * (j % 4)][c] = static_cast<uint16_t>(wd & 0xFFFFu);
-            kTw[32 * (j / 4) + 8 * g + 2 * (j % 4) + 1][c] = static_cast<uint16_t>(wd >> 16);
-        }
+        for (int i = 0; i < 4; i++) *reinterpret_cast<u4*>(&kNw[c][32 * i + 8 * g]) = cur.k[i];
         fetch_part(nxt, t0 + kBlk, 2);  // ... its values, gates and beta
         *reinterpret_cast<f4*>(&sh.Gk[c][4 * g]) = gk;  // symmetric: [c][i] = k_i . k_c
         __builtin_amdgcn_wave_barrier();
@@ -356,7 +352,12 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
 
             // S_0 + K^T DD, tile tau = s[4 tau .. 4 tau + 3]: accumulator row i = 4 g' + r is
             // key row state_row(4 tau + r, g'); A (row i = c, tokens 4 g .. 4 g + 3) = the keys
-            // of those tokens there; B (tokens 4 g + j, column c) = dd, in three bf16 parts
+            // of those tokens there; B (tokens 4 g + j, column c) = dd, in three bf16 parts.
+            // A comes from the gfx950 transposed LDS read: within each group of 16 lanes, slot j
+            // of lane i is element i % 4 of the 8 bytes addressed by lane 4 j + i / 4.  The rows
+            // lanes 4 a .. 4 a + 3 need are consecutive (32 (tau / 2) + 8 a + 4 (tau % 2) + b), so
+            // lane s of group g addresses token 4 g + s / 4 at the first of lane group
+            // s % 4's rows, and slot j of lane c receives token 4 g + j at row(c).
             const f4 ddv = {sel[0], sel[1], sel[2], sel[3]};
             bf4 dh, dl, dl2;
             split3<4>(ddv, dh, dl, dl2);
@@ -364,12 +365,13 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
             for (int tau = 0; tau < 8; tau++) {
-                const int row = state_row(4 * tau + (c & 3), c >> 2);
-                const bf4 kr = *reinterpret_cast<const bf4*>(&kTw[row][4 * g]);
+                const int off = (4 * g + (c >> 2)) * kKeyRow + 32 * (tau >> 1) + 8 * (c & 3) + 4 * (tau & 1);
+                typedef __attribute__((address_space(3))) s4 lds_s4;
+                const s4 kr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(&kN[w][0][0] + off));
                 f4 st = {s[4 * tau], s[4 * tau + 1], s[4 * tau + 2], s[4 * tau + 3]};
-                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, kr), __builtin_bit_cast(s4, dl2), st, 0, 0, 0);
-                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, kr), __builtin_bit_cast(s4, dl), st, 0, 0, 0);
-                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, kr), __builtin_bit_cast(s4, dh), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr, __builtin_bit_cast(s4, dl2), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr, __builtin_bit_cast(s4, dl), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr, __builtin_bit_cast(s4, dh), st, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; r++) s[4 * tau + r] = st[r];
             }
