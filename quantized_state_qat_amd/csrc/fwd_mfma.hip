@@ -296,8 +296,23 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             // Projections: dk (lane (g, c), register r) = P'_{4g+r}[c], dq = Q'.
             f4 dk = {0.0f, 0.0f, 0.0f, 0.0f}, dq = {0.0f, 0.0f, 0.0f, 0.0f}, dm = {0.0f, 0.0f, 0.0f, 0.0f};
             f4 selm = {0.0f, 0.0f, 0.0f, 0.0f};
+            // The exact bf16 parts of the state slices (slice st: s[8 st .. 8 st + 7], key rows
+            // 32 st .. 32 st + 31 of this lane's list), one slice ahead: slice st + 1 is split while
+            // slice st's MFMAs run, one MFMA between every seven vector instructions.
+            uint32_t ph[2][4], pl[2][4], pl2[2][4];
+            auto split_pairs = [&](int st, int b, int i0) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = i0; i < i0 + 2; i++)
+                    split3_pair(s[8 * st + 2 * i], s[8 * st + 2 * i + 1], ph[b][i], pl[b][i], pl2[b][i]);
+            };
+            auto bf8_of = [](const uint32_t (&x)[4]) __attribute__((always_inline)) {
+                return __builtin_bit_cast(bf8, u4{x[0], x[1], x[2], x[3]});
+            };
+            split_pairs(0, 0, 0);
+            split_pairs(0, 0, 2);
 #pragma unroll
             for (int st = 0; st < 4; st++) {
+                const int b = st & 1;
                 const float e0 = 4 * g == c ? 1.0f : 0.0f, e1 = 4 * g + 1 == c ? 1.0f : 0.0f;
                 const float e2 = 4 * g + 2 == c ? 1.0f : 0.0f, e3 = 4 * g + 3 == c ? 1.0f : 0.0f;
                 const float x0 = beta4[0] * (e0 - dm[0]);
@@ -308,24 +323,36 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
                 if (st < 3) {
                     const f4 xv = {x0, x1, x2, x3};
                     *reinterpret_cast<f4*>(&sh.dd[g][c][0]) = xv;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const bf8 ak = __builtin_bit_cast(bf8, cur.k[st]), aq = __builtin_bit_cast(bf8, cur.q[st]);
+                const bf8 h = bf8_of(ph[b]), l = bf8_of(pl[b]), l2 = bf8_of(pl2[b]);
+                dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l2, dk, 0, 0, 0);
+                dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, l2, dq, 0, 0, 0);
+                dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l, dk, 0, 0, 0);
+                if (st < 3) split_pairs(st + 1, b ^ 1, 0);
+#pragma unroll
+                for (int r = 0; r < 3; r++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (st < 3) {
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
                     const float bst = sh.dd[st][c][g];  // B: lane (kk, n) = M[4 st + kk][n]
                     dm = __builtin_amdgcn_mfma_f32_16x16x4f32(ast[st], bst, dm, 0, 0, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // slice st of the projections (state rows 32 st .. 32 st + 31 of this lane's list)
-                const f8 xs = {s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3],
-                               s[8 * st + 4], s[8 * st + 5], s[8 * st + 6], s[8 * st + 7]};
-                bf8 h, l, l2;
-                split3<8>(xs, h, l, l2);
-                const bf8 ak = __builtin_bit_cast(bf8, cur.k[st]), aq = __builtin_bit_cast(bf8, cur.q[st]);
-                dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l2, dk, 0, 0, 0);
-                dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, l2, dq, 0, 0, 0);
-                dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, l, dk, 0, 0, 0);
                 dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, l, dq, 0, 0, 0);
                 dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, h, dk, 0, 0, 0);
                 dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, h, dq, 0, 0, 0);
+                if (st < 3) split_pairs(st + 1, b ^ 1, 2);
+#pragma unroll
+                for (int r = 0; r < 3; r++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             // M transposed through LDS: lane (g, c) needs M[c][4 g + s], the A operand of slice s
