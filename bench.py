@@ -192,6 +192,54 @@ def bench_kda_tok(steps=3, warmup=1):
     }
 
 
+def bench_decode_slots(steps=100, warmup=150):
+    """Serving decode over a slot pool: the decode workload's B=256 x H=16 states in a pool of
+    3 B + 1 slots (slot 0 reserved), each step naming a shuffled set of B slots, the three
+    sets in rotation so that every step streams its states from HBM."""
+    import numpy as np
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    w = synth.WORKLOADS[1]
+    d = synth.generate(w)
+    dev = {k: torch.from_numpy(d[k].bits.astype(np.int16)).view(torch.bfloat16).cuda()
+           for k in ("q", "k", "v", "g", "beta")}
+    n_slots = 3 * w.B + 1
+    pool = torch.from_numpy(d["S0"].f32).cuda().repeat(3, 1, 1, 1)
+    pool = torch.cat([torch.zeros_like(pool[:1]), pool])
+    rng = np.random.default_rng(5)
+    sets = [torch.from_numpy((1 + i * w.B + rng.permutation(w.B)).astype(np.int32)).cuda() for i in range(3)]
+    o = torch.empty((w.B, 1, w.H, w.d_v), device="cuda")
+    c = la.Config(B=w.B, T=1, H=w.H, d_k=w.d_k, d_v=w.d_v, qdq=la.LA_QDQ_INT8_GROUP, group=32)
+    stream = torch.cuda.current_stream()
+    i = [0]
+
+    def step():
+        la.la_decode_step_slots(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], pool, sets[i[0] % 3],
+                                n_slots, o, stream=stream)
+        i[0] += 1
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    nbytes = decode_algorithmic_bytes(w.B, w.H, w.d_k, w.d_v) + 4 * w.B
+    return {
+        "workload": "gdn_decode_int8g32 over a slot pool: B=256 entries x H=16, d=128, pool of 769 slots, "
+                    "INT8 group-32, three shuffled slot sets in rotation",
+        "kernel": "decode (slot pool)", "us_per_step": t * 1e6, "updates_per_s": w.B * w.H / t,
+        "roofline": {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / t / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": nbytes},
+    }
+
+
 def bench_wht_fwdbwd(steps=2, warmup=1):
     """GDN B=4 H=16 T=2048 d=128, bf16 inputs, Hadamard + INT8 group-32 every token: forward with
     64-token checkpoints, then the straight-through backward from them."""
@@ -333,7 +381,7 @@ def main():
     }
     if not args.no_extra:
         line["extra"] = {"long_sequence": bench_long_e4m3(), "kda_int8g64_tok": bench_kda_tok(),
-                         "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd()}
+                         "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "decode_slots": bench_decode_slots()}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["d"], w)
     else:

@@ -119,6 +119,23 @@ la_status la_decode_step(const la_config* cfg, const void* q, const void* k, con
                          float* scales, void* stream);
 
 /*
+ * One decode token for a serving batch whose states live in a pool of slots (the decode-side
+ * neighbour of la_decode_step; linear-attention state-QAT pages, "Torch/Triton GDN/KDA decode
+ * QAT", the serving adapter's reserved paged-cache index zero).  Batch entry b advances the
+ * state S_pool[slots[b]] in place exactly as la_decode_step advances S[b]; q, k, v, g, beta,
+ * o, codes and scales are indexed by batch entry as there.
+ *   S_pool  float [n_slots][H][d_k][d_v], device memory owned by the caller.
+ *   slots   int32 [B], device memory.  Slot 0 is reserved: an entry with slots[b] == 0 (the
+ *           padding of a packed batch) leaves the pool untouched, writes zeros to o[b] and
+ *           writes no codes or scales; so does an index outside [0, n_slots).  Two entries of
+ *           one call must not name the same slot other than 0 (their updates would race).
+ * cfg->T must be 1; n_slots >= 1.
+ */
+la_status la_decode_step_slots(const la_config* cfg, const void* q, const void* k, const void* v,
+                               const void* g, const void* beta, float* S_pool, const int32_t* slots,
+                               int32_t n_slots, void* o, void* codes, float* scales, void* stream);
+
+/*
  * Straight-through backward of la_recurrent_fwd for the upstream gradients dout (o) and
  * dS_T (S_T; NULL = zero).  Recomputation runs in chunks of cfg->ckpt_interval (>= 1)
  * tokens from ckpts (the forward's checkpoints with the same interval); ckpts == NULL

@@ -140,6 +140,31 @@ def fwd(q, k, v, g, beta, S0=None, *, gate=GATE_SCALAR, qdq_mode=QDQ_NONE, group
     return o, ST, ck
 
 
+def decode_slots(q, k, v, g, beta, S_pool, slots, *, gate=GATE_SCALAR, qdq_mode=QDQ_NONE, group=32,
+                 hadamard=False):
+    """One decode token over a pool of state slots (the serving adapter's paged cache with index
+    zero reserved; linear-attention state-QAT pages, "Torch/Triton GDN/KDA decode QAT").  Entry
+    b of the batch (q, k, v, g, beta of shape [B, 1, H, ...]) advances pool slot slots[b] by the
+    forward step above with a rounding point at its token; slot 0 and indices outside the pool
+    are padding: o[b] = 0 and the pool is left as it was.  Returns (o [B, 1, H, d_v], new pool),
+    float64.  Entries are taken one at a time, in order."""
+    q, k, v, g, beta = map(_d, (q, k, v, g, beta))
+    pool = _d(S_pool).copy()
+    B, T, H, dk = q.shape
+    assert T == 1
+    dv = v.shape[-1]
+    o = np.zeros((B, 1, H, dv))
+    for b in range(B):
+        sl = int(slots[b])
+        if sl <= 0 or sl >= pool.shape[0]:
+            continue
+        ob, Sb, _ = fwd(q[b:b + 1], k[b:b + 1], v[b:b + 1], g[b:b + 1], beta[b:b + 1], pool[sl:sl + 1],
+                        gate=gate, qdq_mode=qdq_mode, group=group, hadamard=hadamard, qdq_interval=1)
+        o[b] = ob[0]
+        pool[sl] = Sb[0]
+    return o, pool
+
+
 def bwd(q, k, v, g, beta, S0, dout, dST=None, states=None, *, gate=GATE_SCALAR,
         qdq_mode=QDQ_NONE, group=32, hadamard=False, qdq_interval=1):
     """Straight-through backward.  Returns dict of dq, dk, dv, dg, dbeta, dS0 (float64)."""

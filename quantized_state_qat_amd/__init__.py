@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_decode_step.argtypes = [cp] + [vp] * 10
         lib.la_recurrent_bwd_ste.restype = ctypes.c_int
         lib.la_recurrent_bwd_ste.argtypes = [cp] + [vp] * 16 + [ctypes.c_size_t, vp]
+        lib.la_decode_step_slots.restype = ctypes.c_int
+        lib.la_decode_step_slots.argtypes = [cp] + [vp] * 7 + [ctypes.c_int32] + [vp] * 4
         lib.la_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.la_bwd_workspace_bytes.argtypes = [cp]
         lib.la_status_string.restype = ctypes.c_char_p
@@ -127,6 +129,15 @@ def la_decode_step(cfg: Config, q, k, v, g, beta, S, o, codes=None, scales=None,
     c = cfg.c()
     _check(lib.la_decode_step(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                               _ptr(S), _ptr(o), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def la_decode_step_slots(cfg: Config, q, k, v, g, beta, S_pool, slots, n_slots: int, o, codes=None,
+                         scales=None, stream=None) -> None:
+    lib = load_library()
+    c = cfg.c()
+    _check(lib.la_decode_step_slots(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(S_pool), _ptr(slots), int(n_slots), _ptr(o), _ptr(codes),
+                                    _ptr(scales), _stream(stream)))
 
 
 def la_bwd_workspace_bytes(cfg: Config) -> int:

@@ -98,7 +98,18 @@ __global__ __launch_bounds__(16 * (DK / R)) void decode_kernel(DecParams p, Deco
     const int H = p.H, DV = p.dv;
     const size_t tok = static_cast<size_t>(b) * H + h;  // T == 1
     const int col0 = blk * 64 + cq * 4;
-    float* Srow = a.S + (tok * DK + static_cast<size_t>(rg) * R) * DV + col0;
+    // the state this entry advances: S[b], or pool slot slots[b] (slot 0 and indices outside
+    // the pool are padding: zero output, nothing else written; uniform over the workgroup)
+    size_t stok = tok;
+    if (a.slots) {
+        const int sl = a.slots[b];
+        if (sl <= 0 || sl >= a.n_slots) {
+            if (rg == 0) store4(a.o, tok * DV + col0, p.out_dt, make_float4(0.f, 0.f, 0.f, 0.f));
+            return;
+        }
+        stok = static_cast<size_t>(sl) * H + h;
+    }
+    float* Srow = a.S + (stok * DK + static_cast<size_t>(rg) * R) * DV + col0;
 
     // token vectors first, so that waiting for them does not wait for the state
     float kk = 0.f, qv = 0.f, ai = 0.f;

@@ -179,6 +179,32 @@ la_status la_decode_step(const la_config* cfg, const void* q, const void* k, con
     return hip_status(la::launch_decode(c, a, static_cast<hipStream_t>(stream)), "la_decode_step launch");
 }
 
+la_status la_decode_step_slots(const la_config* cfg, const void* q, const void* k, const void* v,
+                               const void* g, const void* beta, float* S_pool, const int32_t* slots,
+                               int32_t n_slots, void* o, void* codes, float* scales, void* stream) {
+    CHECK(check_config(cfg, true));
+    const la_config& c = *cfg;
+    const bool work = c.B > 0 && c.H > 0;
+    CHECK(check_ptr(q, "q", work));
+    CHECK(check_ptr(k, "k", work));
+    CHECK(check_ptr(v, "v", work));
+    CHECK(check_ptr(g, "g", work));
+    CHECK(check_ptr(beta, "beta", work));
+    CHECK(check_ptr(S_pool, "S_pool", work));
+    CHECK(check_ptr(slots, "slots", work));
+    CHECK(check_ptr(o, "o", work));
+    CHECK(check_ptr(codes, "codes", false));
+    CHECK(check_ptr(scales, "scales", false));
+    if (n_slots < 1) return fail(LA_ERR_INVALID_ARG, "n_slots must be >= 1 (slot 0 is reserved), got %d", n_slots);
+    if ((codes || scales) && c.qdq == LA_QDQ_NONE)
+        return fail(LA_ERR_INVALID_ARG, "codes/scales requested without a quantizer");
+    if (!work) return ok();
+    la::DecodeArgs a{q, k, v, g, beta, S_pool, o, codes, scales};
+    a.slots = slots;
+    a.n_slots = n_slots;
+    return hip_status(la::launch_decode(c, a, static_cast<hipStream_t>(stream)), "la_decode_step_slots launch");
+}
+
 size_t la_bwd_workspace_bytes(const la_config* cfg) {
     if (check_config(cfg, false) != LA_OK || cfg->ckpt_interval < 1) return 0;
     return ws_layout(*cfg).total;

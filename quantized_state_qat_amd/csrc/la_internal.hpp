@@ -31,6 +31,8 @@ struct DecodeArgs {
     void* o;
     void* codes;    // may be null
     float* scales;  // may be null
+    const int32_t* slots = nullptr;  // null: entry b is state b; else the state slot of entry b
+    int n_slots = 0;                 // slots outside [1, n_slots) are padding
 };
 
 struct BwdArgs {

@@ -21,9 +21,9 @@ def header_functions():
 def test_library_exports_every_declared_function():
     lib = la.load_library()
     names = header_functions()
-    assert set(names) == {"la_recurrent_fwd", "la_decode_step", "la_recurrent_bwd_ste",
-                          "la_bwd_workspace_bytes", "la_fwd_kernel_name", "la_status_string",
-                          "la_last_error"}
+    assert set(names) == {"la_recurrent_fwd", "la_decode_step", "la_decode_step_slots",
+                          "la_recurrent_bwd_ste", "la_bwd_workspace_bytes", "la_fwd_kernel_name",
+                          "la_status_string", "la_last_error"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -104,6 +104,21 @@ def test_decode_checks():
         la.la_decode_step(cfg(T=1, qdq=la.LA_QDQ_NONE), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                           codes=FAKE, stream=0)
     assert e.value.status == la.LA_ERR_INVALID_ARG
+
+
+def test_decode_slots_checks():
+    c = cfg(T=1)
+    with pytest.raises(la.LaError) as e:
+        la.la_decode_step_slots(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, stream=0)
+    assert "n_slots" in str(e.value)
+    with pytest.raises(la.LaError) as e:
+        la.la_decode_step_slots(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, stream=0)
+    assert "slots" in str(e.value)
+    with pytest.raises(la.LaError) as e:
+        la.la_decode_step_slots(cfg(T=2), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, stream=0)
+    assert "T == 1" in str(e.value)
+    la.la_decode_step_slots(cfg(T=1, B=0), None, None, None, None, None, None, None, 1, None, stream=0)
+    assert la.la_last_error() == ""
 
 
 def test_bwd_workspace_and_checks():

@@ -167,3 +167,68 @@ def test_decode_deterministic_and_overwrites():
     for x, y in zip(r1, r2):
         np.testing.assert_array_equal(x, y)
     assert all(np.all(np.isfinite(x)) for x in r1[:2])
+
+
+SLOT_CASES = [
+    # name, B, H, d_k, d_v, gate, qdq, group, had
+    ("int8g32", 6, 2, 128, 128, "scalar", la.LA_QDQ_INT8_GROUP, 32, 0),
+    ("e4m3_kda_dk64", 5, 3, 64, 128, "key", la.LA_QDQ_E4M3_TILE, 64, 0),
+    ("wht_int8g16_rotated_state", 4, 2, 128, 64, "scalar", la.LA_QDQ_INT8_GROUP, 16, 2),
+]
+
+
+@pytest.mark.parametrize("name,B,H,dk,dv,gate,mode,group,had", SLOT_CASES, ids=[c[0] for c in SLOT_CASES])
+def test_decode_slots(name, B, H, dk, dv, gate, mode, group, had):
+    """Slot-pool decode: live entries advance the slot they name exactly as la_decode_step
+    advances the gathered states (bit for bit, same kernel), and match the oracle's slot decode;
+    padding entries (slot 0, indices outside the pool) write zeros to o and nothing else; slots
+    no entry names keep their bits."""
+    torch = gu.torch_mod()
+    w = synth.Workload(name, B=B, T=1, H=H, d_k=dk, d_v=dv, gate=gate, s0_sigma=0.05, config_id=13)
+    d = synth.generate(w)
+    rot = had == 2
+    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=int(had > 0), state_rotated=int(rot))
+    n_slots = B + 3
+    rng = np.random.default_rng(7)
+    pool = (rng.standard_normal((n_slots, H, dk, dv)) * 0.05).astype(np.float32)
+    live = rng.permutation(np.arange(1, n_slots))[:B].astype(np.int32)
+    slots = live.copy()
+    slots[1] = 0            # padding
+    slots[-1] = n_slots + 4  # outside the pool: padding too
+    di = {k_: gu.dev(d[k_]) for k_ in ("q", "k", "v", "g", "beta")}
+    P = torch.from_numpy(pool.copy()).cuda()
+    sl = torch.from_numpy(slots).cuda()
+    o = gu.nan_like(torch, (B, 1, H, dv))
+    cdt = torch.int8 if mode == la.LA_QDQ_INT8_GROUP else torch.uint8
+    codes = torch.full((B, H, dk, dv), 99, dtype=cdt, device="cuda")
+    nsc = (B, H, dk, dv // group) if mode == la.LA_QDQ_INT8_GROUP else (B, H, dv // 64)
+    scales = gu.nan_like(torch, nsc)
+    la.la_decode_step_slots(c, di["q"], di["k"], di["v"], di["g"], di["beta"], P, sl, n_slots, o, codes, scales)
+    torch.cuda.synchronize()
+    P, o, codes, scales = P.cpu().numpy(), o.cpu().numpy(), codes.cpu().numpy(), scales.cpu().numpy()
+    is_live = (slots >= 1) & (slots < n_slots)
+    # padding entries
+    assert np.all(o[~is_live] == 0)
+    assert np.all(codes[~is_live] == 99) and np.all(np.isnan(scales[~is_live]))
+    # slots nobody names keep their bits
+    named = set(int(x) for x in slots[is_live])
+    for s_ in range(n_slots):
+        if s_ not in named:
+            np.testing.assert_array_equal(P[s_], pool[s_])
+    # live entries equal la_decode_step on the gathered states, bit for bit
+    S_g, o_g, codes_g, scales_g = _run_decode(c, d, pool[np.where(is_live, slots, 0)])
+    for b in np.nonzero(is_live)[0]:
+        np.testing.assert_array_equal(P[slots[b]], S_g[b])
+        np.testing.assert_array_equal(o[b], o_g[b])
+        np.testing.assert_array_equal(codes[b], codes_g[b])
+        np.testing.assert_array_equal(scales[b], scales_g[b])
+    # and the oracle's slot decode (unrotated domain)
+    pool_phys = gu.rotated_to_state(pool) if rot else pool.astype(np.float64)
+    o_r, pool_r = oracle.decode_slots(d["q"].f64, d["k"].f64, d["v"].f64, d["g"].f64, d["beta"].f64,
+                                      pool_phys, slots, gate=c.gate, qdq_mode=mode, group=group,
+                                      hadamard=had > 0)
+    assert gu.err(o, o_r) <= 1e-5
+    P_phys = gu.rotated_to_state(P) if rot else P.astype(np.float64)
+    for b in np.nonzero(is_live)[0]:
+        # one code step of difference at a near-tie moves an element by at most one grid step
+        assert gu.err(P_phys[slots[b]], pool_r[slots[b]]) <= (2.0 / 127 if mode == la.LA_QDQ_INT8_GROUP else 1.0 / 8)

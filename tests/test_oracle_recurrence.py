@@ -226,3 +226,38 @@ def test_qdq_points_and_output_reads_unrounded_state(oracle_mod):
     last = oracle.fwd(q[:, 16:], k[:, 16:], v[:, 16:], g[:, 16:], beta[:, 16:], ckq[:, :, 16])
     np.testing.assert_array_equal(ST[0, 0], oracle.qdq(last[1][0, 0], oracle.QDQ_INT8, 32)[0])
     np.testing.assert_array_equal(o[:, 16:], last[0])
+
+
+def test_decode_slots_padding_noop_and_permutation(oracle_mod):
+    """Slot-pool decode: entries naming slot 0 or an index outside the pool give o = 0 and touch
+    no slot; with beta = 0, g = 0 and exactly representable INT8 states, each live entry returns
+    S^T q of the slot it names (a matrix product, not the recurrence) and leaves the pool as it
+    was; permuting the entries together with their slots permutes the outputs and gives the
+    same pool."""
+    rng = np.random.default_rng(31)
+    B, H, dk, dv, n = 6, 2, 32, 32, 5
+    q, k, v, g, beta, _ = _rand_inputs(rng, B, 1, H, dk, dv)
+    codes = rng.integers(-127, 128, size=(n, H, dk, dv))
+    codes[..., ::32] = 127
+    pool = codes * 2.0 ** -8
+    slots = np.array([3, 0, 1, 7, -2, 4])
+    g0, b0 = np.zeros_like(g), np.zeros_like(beta)
+    o, pool2 = oracle.decode_slots(q, k, v, g0, b0, pool, slots, qdq_mode=oracle.QDQ_INT8, group=32)
+    np.testing.assert_array_equal(pool2, pool)
+    for b in range(B):
+        if 1 <= slots[b] < n:
+            np.testing.assert_allclose(o[b, 0], np.einsum("hij,hi->hj", pool[slots[b]], q[b, 0]), rtol=0, atol=1e-14)
+        else:
+            assert np.all(o[b] == 0)
+    # a real step: padding entries and unnamed slots (0 and 2) keep their states
+    o, pool3 = oracle.decode_slots(q, k, v, g, beta, pool, slots, qdq_mode=oracle.QDQ_INT8, group=32)
+    for sl in (0, 2):
+        np.testing.assert_array_equal(pool3[sl], pool[sl])
+    for sl in (1, 3, 4):
+        assert np.any(pool3[sl] != pool[sl])
+    assert np.all(o[1] == 0) and np.all(o[3] == 0) and np.all(o[4] == 0)
+    perm = np.array([5, 2, 0, 4, 1, 3])
+    op, poolp = oracle.decode_slots(q[perm], k[perm], v[perm], g[perm], beta[perm], pool, slots[perm],
+                                    qdq_mode=oracle.QDQ_INT8, group=32)
+    np.testing.assert_array_equal(op, o[perm])
+    np.testing.assert_array_equal(poolp, pool3)
