@@ -240,6 +240,40 @@ def bench_decode_slots(steps=100, warmup=150):
     }
 
 
+def bench_varlen(steps=3, warmup=1):
+    """Packed prefill: 64 sequences of lengths drawn uniformly from 1..1024 (seeded), H=16,
+    d=128, bf16 inputs, GDN with INT8 group-32 rounding after every token."""
+    import numpy as np
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    rng = np.random.default_rng(9)
+    lens = rng.integers(1, 1025, size=64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    w = synth.Workload("varlen", B=1, T=T, H=16, d_k=128, d_v=128, s0_sigma=0.0, config_id=9)
+    d = synth.generate(w)
+    dev = {k: _dev(d[k]) for k in ("q", "k", "v", "g", "beta")}
+    del d
+    o = torch.empty((T, w.H, w.d_v), device="cuda")
+    ST = torch.empty((len(lens), w.H, w.d_k, w.d_v), device="cuda")
+    cu_d = torch.from_numpy(cu).cuda()
+    c = la.Config(B=len(lens), T=T, H=w.H, d_k=w.d_k, d_v=w.d_v, qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=1)
+    stream = torch.cuda.current_stream()
+    t = _time_calls(lambda: la.la_recurrent_fwd_varlen(c, cu_d, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                                                       None, o, ST, stream=stream), steps, warmup, stream)
+    flops = 7.0 * w.d_k * w.d_v * w.H * T
+    return {
+        "workload": f"packed prefill, 64 GDN sequences of 1..1024 tokens ({T} in all), H=16, d=128, bf16 inputs, "
+                    "INT8 group-32 every token",
+        "kernel": "token (packed sequences)", "ms_per_call": t * 1e3, "updates_per_s": w.H * T / t,
+        "roofline": _fp32_roofline(flops, t, "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head); "
+                                             "the INT8 codec is not counted; the longest sequence sets the time"),
+    }
+
+
 def bench_wht_fwdbwd(steps=2, warmup=1):
     """GDN B=4 H=16 T=2048 d=128, bf16 inputs, Hadamard + INT8 group-32 every token: forward with
     64-token checkpoints, then the straight-through backward from them."""
@@ -381,7 +415,8 @@ def main():
     }
     if not args.no_extra:
         line["extra"] = {"long_sequence": bench_long_e4m3(), "kda_int8g64_tok": bench_kda_tok(),
-                         "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "decode_slots": bench_decode_slots()}
+                         "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "decode_slots": bench_decode_slots(),
+                         "varlen_prefill": bench_varlen()}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["d"], w)
     else:

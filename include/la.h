@@ -106,6 +106,22 @@ la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, c
                            float* S_T, float* ckpts, void* stream);
 
 /*
+ * Forward over packed sequences of different lengths (the packed sequence tails of the
+ * linear-attention state-QAT pages' GDN/KDA state QAT, serving prefill).  cfg->B is the
+ * number of sequences and cfg->T the packed length; sequence b is tokens
+ * cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of q, k [T][H][d_k], v, o [T][H][d_v], g [T][H]
+ * ([T][H][d_k] for per-key gates) and beta [T][H].  Each sequence starts from S0[b] (NULL =
+ * zeros), has its own rounding points (counted from its first token) and ends in S_T[b]
+ * (NULL = not written); S0 and S_T are [B][H][d_k][d_v].  cu_seqlens is int32 [B + 1] in
+ * device memory, non-decreasing from 0 to T; the kernel clamps every boundary to [0, T] (a
+ * sequence whose boundaries are out of order is empty).  No checkpoints; the per-token kernel
+ * serves every configuration.
+ */
+la_status la_recurrent_fwd_varlen(const la_config* cfg, const int32_t* cu_seqlens, const void* q,
+                                  const void* k, const void* v, const void* g, const void* beta,
+                                  const float* S0, void* o, float* S_T, void* stream);
+
+/*
  * One decode token (cfg->T must be 1): S [B][H][d_k][d_v] is read, updated, quantized at
  * the token (a single-token call always ends on a quantization point) and written back in
  * place.  codes/scales are optional (NULL = not written):

@@ -140,6 +140,34 @@ def fwd(q, k, v, g, beta, S0=None, *, gate=GATE_SCALAR, qdq_mode=QDQ_NONE, group
     return o, ST, ck
 
 
+def fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, gate=GATE_SCALAR, qdq_mode=QDQ_NONE, group=32,
+               hadamard=False, qdq_interval=1):
+    """Forward over packed sequences (the pages' packed sequence tails): q, k, v, g, beta hold the
+    tokens of all sequences one after another ([T, H, ...], no batch axis), sequence b being
+    tokens cu_seqlens[b] .. cu_seqlens[b + 1] - 1 (boundaries clamped to [0, T], an inverted
+    pair is an empty sequence).  Each sequence is the forward above on its own tokens, from
+    S0[b] (zeros when S0 is None), with its own rounding points.  Returns (o [T, H, d_v],
+    S_T [B, H, d_k, d_v]), float64; tokens outside every sequence give o = 0."""
+    q, k, v, g, beta = map(_d, (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    B = len(cu_seqlens) - 1
+    o = np.zeros((T, H, dv))
+    ST = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        t0 = min(max(int(cu_seqlens[b]), 0), T)
+        t1 = min(max(int(cu_seqlens[b + 1]), t0), T)
+        S0b = None if S0 is None else _d(S0)[b:b + 1]
+        if t1 == t0:
+            ST[b] = 0.0 if S0b is None else S0b[0]
+            continue
+        ob, STb, _ = fwd(q[None, t0:t1], k[None, t0:t1], v[None, t0:t1], g[None, t0:t1], beta[None, t0:t1], S0b,
+                         gate=gate, qdq_mode=qdq_mode, group=group, hadamard=hadamard, qdq_interval=qdq_interval)
+        o[t0:t1] = ob[0]
+        ST[b] = STb[0]
+    return o, ST
+
+
 def decode_slots(q, k, v, g, beta, S_pool, slots, *, gate=GATE_SCALAR, qdq_mode=QDQ_NONE, group=32,
                  hadamard=False):
     """One decode token over a pool of state slots (the serving adapter's paged cache with index

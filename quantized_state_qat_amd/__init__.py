@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_decode_step.argtypes = [cp] + [vp] * 10
         lib.la_recurrent_bwd_ste.restype = ctypes.c_int
         lib.la_recurrent_bwd_ste.argtypes = [cp] + [vp] * 16 + [ctypes.c_size_t, vp]
+        lib.la_recurrent_fwd_varlen.restype = ctypes.c_int
+        lib.la_recurrent_fwd_varlen.argtypes = [cp] + [vp] * 10
         lib.la_decode_step_slots.restype = ctypes.c_int
         lib.la_decode_step_slots.argtypes = [cp] + [vp] * 7 + [ctypes.c_int32] + [vp] * 4
         lib.la_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -122,6 +124,13 @@ def la_recurrent_fwd(cfg: Config, q, k, v, g, beta, S0, o, S_T=None, ckpts=None,
     c = cfg.c()
     _check(lib.la_recurrent_fwd(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                 _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ckpts), _stream(stream)))
+
+
+def la_recurrent_fwd_varlen(cfg: Config, cu_seqlens, q, k, v, g, beta, S0, o, S_T=None, stream=None) -> None:
+    lib = load_library()
+    c = cfg.c()
+    _check(lib.la_recurrent_fwd_varlen(ctypes.byref(c), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                       _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream)))
 
 
 def la_decode_step(cfg: Config, q, k, v, g, beta, S, o, codes=None, scales=None, stream=None) -> None:

@@ -34,13 +34,33 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int T = p.T, H = p.H, DV = p.dv;
+    const int H = p.H, DV = p.dv;
+    int T = p.T;
+    size_t tok0 = static_cast<size_t>(b) * T * H + h;  // token 0 of this (b, h)
+    if (a.cu_seqlens) {
+        // packed sequences: this one's tokens, clamped to the packed length
+        const int t_begin = min(max(a.cu_seqlens[b], 0), p.T);
+        const int t_end = min(max(a.cu_seqlens[b + 1], t_begin), p.T);
+        T = t_end - t_begin;
+        tok0 = static_cast<size_t>(t_begin) * H + h;
+    }
     const int col = blk * TC + lane % TC;
     const int r0 = tok_row0<S>(w, lane);
     const size_t bh = static_cast<size_t>(b) * H + h;
     const size_t state_off = bh * DK * DV;
-    const size_t tok0 = static_cast<size_t>(b) * T * H + h;  // token 0 of this (b, h)
     const TokInputs in{a.q, a.k, a.v, a.g, a.beta, nullptr};
+    if (T == 0) {
+        // an empty packed sequence hands its initial state through unchanged (no rotation
+        // round trip); uniform over the workgroup
+        if (a.ST) {
+#pragma unroll
+            for (int m = 0; m < R; m++) {
+                const size_t e = state_off + static_cast<size_t>(r0 + m) * DV + col;
+                a.ST[e] = a.S0 ? a.S0[e] : 0.0f;
+            }
+        }
+        return;
+    }
 
     TokFetch<S, KDA, false> f;
     auto fetch = [&](int u) __attribute__((always_inline)) {

@@ -157,6 +157,33 @@ la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, c
     return hip_status(la::launch_fwd(c, a, s), "la_recurrent_fwd launch");
 }
 
+la_status la_recurrent_fwd_varlen(const la_config* cfg, const int32_t* cu_seqlens, const void* q,
+                                  const void* k, const void* v, const void* g, const void* beta,
+                                  const float* S0, void* o, float* S_T, void* stream) {
+    CHECK(check_config(cfg, false));
+    const la_config& c = *cfg;
+    const bool units = c.B > 0 && c.H > 0;
+    const bool work = units && c.T > 0;
+    CHECK(check_ptr(cu_seqlens, "cu_seqlens", units));
+    CHECK(check_ptr(q, "q", work));
+    CHECK(check_ptr(k, "k", work));
+    CHECK(check_ptr(v, "v", work));
+    CHECK(check_ptr(g, "g", work));
+    CHECK(check_ptr(beta, "beta", work));
+    CHECK(check_ptr(o, "o", work));
+    CHECK(check_ptr(S0, "S0", false));
+    CHECK(check_ptr(S_T, "S_T", false));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!units) return ok();
+    if (c.T == 0) {
+        if (!S_T) return ok();
+        return hip_status(la::launch_copy_state(c, S0, S_T, s), "copy S0 -> S_T");
+    }
+    la::FwdArgs a{q, k, v, g, beta, S0, o, S_T, nullptr};
+    a.cu_seqlens = cu_seqlens;
+    return hip_status(la::launch_fwd_tok(c, a, s), "la_recurrent_fwd_varlen launch");
+}
+
 la_status la_decode_step(const la_config* cfg, const void* q, const void* k, const void* v,
                          const void* g, const void* beta, float* S, void* o, void* codes,
                          float* scales, void* stream) {

@@ -19,6 +19,9 @@ struct FwdArgs {
     void* o;        // may be null (backward recompute)
     float* ST;      // may be null
     float* ckpts;   // may be null
+    // packed sequences (token kernel only): sequence b is tokens cu_seqlens[b] .. [b + 1] of
+    // a [T][H][...] layout; null = the batched [B][T][H][...] layout
+    const int32_t* cu_seqlens = nullptr;
 };
 
 struct DecodeArgs {

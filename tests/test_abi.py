@@ -21,7 +21,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     lib = la.load_library()
     names = header_functions()
-    assert set(names) == {"la_recurrent_fwd", "la_decode_step", "la_decode_step_slots",
+    assert set(names) == {"la_recurrent_fwd", "la_recurrent_fwd_varlen", "la_decode_step", "la_decode_step_slots",
                           "la_recurrent_bwd_ste", "la_bwd_workspace_bytes", "la_fwd_kernel_name",
                           "la_status_string", "la_last_error"}
     for n in names:

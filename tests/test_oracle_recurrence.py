@@ -261,3 +261,43 @@ def test_decode_slots_padding_noop_and_permutation(oracle_mod):
                                     qdq_mode=oracle.QDQ_INT8, group=32)
     np.testing.assert_array_equal(op, o[perm])
     np.testing.assert_array_equal(poolp, pool3)
+
+
+def test_fwd_varlen_structure(oracle_mod):
+    """Packed sequences: an empty sequence hands its S_0 through; a sequence's outputs and final
+    state depend on its own tokens only (changing another sequence's tokens changes nothing);
+    reordering the sequences in the packing reorders the results; with one sequence per call
+    and equal lengths, the rows of the packed result are the batched forward's rows (the packing
+    moves data only)."""
+    rng = np.random.default_rng(41)
+    H, dk, dv = 2, 16, 16
+    lens = [5, 0, 3, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, k, v, g, beta, _ = _rand_inputs(rng, 1, T, H, dk, dv)
+    q, k, v, g, beta = q[0], k[0], v[0], g[0], beta[0]
+    S0 = rng.standard_normal((4, H, dk, dv)) * 0.3
+    kw = dict(qdq_mode=oracle.QDQ_INT8, group=16, qdq_interval=2)
+    o, ST = oracle.fwd_varlen(q, k, v, g, beta, cu, S0, **kw)
+    np.testing.assert_array_equal(ST[1], S0[1])
+    v2 = v.copy()
+    v2[cu[2]:cu[3]] += 1.0  # sequence 2's values
+    o2, ST2 = oracle.fwd_varlen(q, k, v2, g, beta, cu, S0, **kw)
+    for b in (0, 1, 3):
+        np.testing.assert_array_equal(ST2[b], ST[b])
+        np.testing.assert_array_equal(o2[cu[b]:cu[b + 1]], o[cu[b]:cu[b + 1]])
+    assert np.any(ST2[2] != ST[2])
+    order = [3, 0, 2, 1]
+    idx = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in order]).astype(int)
+    cu_p = np.concatenate([[0], np.cumsum([lens[b] for b in order])])
+    op, STp = oracle.fwd_varlen(q[idx], k[idx], v[idx], g[idx], beta[idx], cu_p, S0[order], **kw)
+    np.testing.assert_array_equal(op, o[idx])
+    np.testing.assert_array_equal(STp, ST[order])
+    # equal lengths: the packing is the batched layout with the batch axis folded into time
+    L = 6
+    qb, kb, vb, gb, bb, S0b = _rand_inputs(rng, 3, L, H, dk, dv)
+    ob, STb, _ = oracle.fwd(qb, kb, vb, gb, bb, S0b, **kw)
+    fold = lambda x: x.reshape((3 * L,) + x.shape[2:])
+    ov, STv = oracle.fwd_varlen(fold(qb), fold(kb), fold(vb), fold(gb), fold(bb), np.arange(4) * L, S0b, **kw)
+    np.testing.assert_array_equal(ov, fold(ob))
+    np.testing.assert_array_equal(STv, STb)
