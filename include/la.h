@@ -155,9 +155,11 @@ la_status la_decode_step_slots(const la_config* cfg, const void* q, const void* 
  * Straight-through backward of la_recurrent_fwd for the upstream gradients dout (o) and
  * dS_T (S_T; NULL = zero).  Recomputation runs in chunks of cfg->ckpt_interval (>= 1)
  * tokens from ckpts (the forward's checkpoints with the same interval); ckpts == NULL
- * recomputes them into the workspace first.  The workspace (device memory, at least
- * la_bwd_workspace_bytes(cfg) bytes, contents undefined on entry and exit) is owned by
- * the caller.  Writes every gradient output in full.
+ * recomputes them into the workspace first.  Where la_bwd_kernel_name(cfg) is "block", the
+ * states are instead recomputed from S0 with the block forward (the same arithmetic as
+ * la_recurrent_fwd's "block" kernel, so the same rounding decisions) and ckpts is not read.
+ * The workspace (device memory, at least la_bwd_workspace_bytes(cfg) bytes, contents
+ * undefined on entry and exit) is owned by the caller.  Writes every gradient output in full.
  */
 la_status la_recurrent_bwd_ste(const la_config* cfg, const void* q, const void* k,
                                const void* v, const void* g, const void* beta, const float* S0,
@@ -182,6 +184,17 @@ size_t la_bwd_workspace_bytes(const la_config* cfg);
  * order of floating-point operations; every one computes the same recurrence.
  */
 const char* la_fwd_kernel_name(const la_config* cfg);
+
+/*
+ * Which backward la_recurrent_bwd_ste runs for cfg (diagnostic; no GPU work, no state):
+ *   "block"  the configurations of the "block" forward with d_v a multiple of 64: the state
+ *            entering every 16-token block is recomputed into the workspace, then the blocks
+ *            are walked last to first on the matrix cores (the block form of the adjoint);
+ *   "token"  every other valid configuration: chunks of ckpt_interval tokens recomputed from
+ *            the checkpoints and walked token by token.
+ * Returns "" (and sets la_last_error) for an invalid cfg.
+ */
+const char* la_bwd_kernel_name(const la_config* cfg);
 
 /* Static description of a status code. */
 const char* la_status_string(la_status s);

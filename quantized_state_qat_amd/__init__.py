@@ -91,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_last_error.argtypes = []
         lib.la_fwd_kernel_name.restype = ctypes.c_char_p
         lib.la_fwd_kernel_name.argtypes = [cp]
+        lib.la_bwd_kernel_name.restype = ctypes.c_char_p
+        lib.la_bwd_kernel_name.argtypes = [cp]
         _lib = lib
     return _lib
 
@@ -168,6 +170,12 @@ def la_fwd_kernel_name(cfg: Config) -> str:
     """Which forward kernel serves cfg: "block", "wave", "fast" or "token" ("" if invalid)."""
     c = cfg.c()
     return load_library().la_fwd_kernel_name(ctypes.byref(c)).decode()
+
+
+def la_bwd_kernel_name(cfg: Config) -> str:
+    """Which backward serves cfg: "block" or "token" ("" if invalid)."""
+    c = cfg.c()
+    return load_library().la_bwd_kernel_name(ctypes.byref(c)).decode()
 
 
 def la_status_string(status: int) -> str:

@@ -1,0 +1,565 @@
+// Straight-through backward on the matrix cores, for the configurations the block forward
+// serves: scalar gate, no rotation, d_k = 128, bf16 keys, queries and values, every rounding
+// point on a 16-token block end.
+//
+// Three launches.  (1) The block forward (fwd_mfma.hip) with a checkpoint every 16 tokens
+// into the workspace: the state entering every block, rounding points included.  (2) This
+// file's block kernel walks the blocks last to first with dS = dL/dS carried in registers.
+// (3) A reduction finishes the key, query and gate gradients.  The quantizer passes the
+// gradient through unchanged, so a block's adjoint is that of the exact recurrence.
+//
+// Block algebra (16 tokens, local index j; G_j the inclusive sum of the log gates inside the
+// block, gamma_j = exp(G_j), rho_j = exp(G_15 - G_j), r_ji = exp(G_j - G_i) for i <= j: every
+// factor is the decay the recurrence itself applies between two tokens, so no range guard):
+//   A_ji = r_ji k_j . k_i (i < j),  C_ji = r_ji q_j . k_i (i <= j),  N = (I + diag(beta) A)^-1
+//   W = V - diag(gamma) K S_0,  Delta = N diag(beta) W          (Delta_j = the token's delta)
+//   O = diag(gamma) Q S_0 + C Delta,  S_16 = gamma_15 S_0 + sum_i rho_i k_i delta_i^T.
+// Adjoint, given dO and dS' = dL/dS_16:
+//   dDelta = C^T dO + diag(rho) K dS',  lambda = N^T dDelta,  dv = beta lambda,  dU = -dv
+//   dbeta_j = lambda_j . (W - A Delta)_j,  dA_ji = -beta_j lambda_j . delta_i,  dC_ji = dO_j . delta_i
+//   dS_0 = gamma_15 dS' + Q^T diag(gamma) dO + K^T diag(gamma) dU
+//   dk = diag(gamma) dU S_0^T + diag(rho) Delta dS'^T + (Ab + Ab^T) K + Cb^T Q,  Ab = dA o r, Cb = dC o r
+//   dq = diag(gamma) dO S_0^T + Cb K
+//   dG_j = (gamma U)_j . dU_j - rho_j (K dS')_j . delta_j + rowsum_j(E) - colsum_j(E) + q_j . (dq_j from S_0)
+//          + [j = 15] (gamma_15 <dS', S_0> + sum_i rho_i (K dS')_i . delta_i),   E = dA o A + dC o C
+//   dg_l = sum_{j >= l} dG_j  (G_j sums the gates of tokens <= j).
+// Per wave (16 value columns; lane 16 g + c): the state slices in the forward's layout
+// (state_row), 16 x 16 token matrices in the accumulator layout of the 16x16 MFMAs ("D": lane
+// (g, c) holds rows 4 g .. 4 g + 3 of column c) or transposed ("T": lane (g, c) holds row c,
+// columns 4 g .. 4 g + 3).  Products over the 128 key rows use bf16 MFMAs of the raw keys and
+// queries (exact) with the other operand split exactly into three bf16 parts; products over 16
+// tokens or 16 columns use fp32 MFMAs (16x16x4).  The four waves of a workgroup sum their
+// partial key/query/gate sums (over their columns) in LDS; the reduction kernel adds the
+// workgroups of a head in a fixed order and applies the Gram-matrix terms once per head.
+#include "la_device.hpp"
+#include "la_internal.hpp"
+#include "la_mfma.hpp"
+#include "la_wave.hpp"
+
+namespace la {
+
+namespace {
+
+constexpr int kBwWaves = 4;
+constexpr int kBwThreads = kBwWaves * 64;  // 64 value columns per workgroup
+constexpr int kBwDK = 128;
+constexpr int kDppRowShr = 0x110;  // row_shr:n = kDppRowShr + n
+
+// Partial record of one (sequence, head, block, 64-column slice), in floats.
+constexpr int kRecDk = 0;      // [16 tokens][128 rows]: diag(gamma) dU S_0^T + diag(rho) Delta dS'^T
+constexpr int kRecDq = 2048;   // [16][128]: diag(gamma) dO S_0^T
+constexpr int kRecA = 4096;    // [16][16]: Ab
+constexpr int kRecC = 4352;    // [16][16]: Cb
+constexpr int kRecGr = 4608;   // [16]: dG terms collected by token row
+constexpr int kRecGc = 4624;   // [16]: dG terms collected by token column
+constexpr int kRecB = 4640;    // [16]: dbeta
+constexpr int kRec = 4672;     // record stride (256-byte multiple)
+
+struct BwParams {
+    int T, H, dv, nb;
+};
+
+// Per-wave LDS.
+struct BwShared {
+    uint16_t kN[kBlk][kKeyRow];  // the block's keys, [token][row] (transposed reads of the update)
+    uint16_t qN[kBlk][kKeyRow];  // and queries
+    float SdS[2][kBwDK][16];     // S_0 and dS' by [row][column]; then this wave's partial sums
+    float small[5][64][4];       // small partial sums for the cross-wave reduction
+    float AmT[kBlk][20];         // [i][j] = A_ji
+    float dd[4][kBlk][4];        // solve: stage values of tokens 4 g + r, [g][column][r]
+    float Ns[kBlk][20];          // [c][j] = N_jc
+    float XD[kBlk][20];          // Delta by [token][column]
+    float XL[kBlk][20];          // lambda by [token][column]
+    float G[kBlk], beta[kBlk];
+};
+
+// Inclusive prefix sum over each row of 16 lanes.
+__device__ __forceinline__ float row_prefix_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowShr + 1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowShr + 2, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowShr + 4, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowShr + 8, 0xF, 0xF, false));
+    return x;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+}
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// Product over key rows: lane (g, c) register r = sum_rows key_{4g+r}[row] x[row][c], with the
+// keys of token c as loaded (kv[i] = rows state_row(8 i .. 8 i + 7, g)) and x in the state layout.
+__device__ __forceinline__ f4 project(const float (&x)[32], const u4 (&kv)[4]) {
+    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+        uint32_t hh[4], ll[4], l2[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) split3_pair(x[8 * st + 2 * i], x[8 * st + 2 * i + 1], hh[i], ll[i], l2[i]);
+        const bf8 ak = __builtin_bit_cast(bf8, kv[st]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf8, u4{l2[0], l2[1], l2[2], l2[3]}), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf8, u4{ll[0], ll[1], ll[2], ll[3]}), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf8, u4{hh[0], hh[1], hh[2], hh[3]}), acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+}  // namespace
+
+template <bool GF32>
+__global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArgs a) {
+    constexpr int DK = kBwDK, R = 32;
+    constexpr int GB = GF32 ? 4 : 2;
+    __shared__ BwShared shw[kBwWaves];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int cw0 = blockIdx.x * 64 + w * 16;  // this wave's first value column
+    const int col = cw0 + c;
+    const int T = p.T, H = p.H, DV = p.dv, nb = p.nb;
+    const int nwg = gridDim.x;
+    const size_t bh = static_cast<size_t>(b) * H + h;
+    const size_t seq0 = static_cast<size_t>(b) * T * H;
+    const size_t seq_tok = static_cast<size_t>(T) * H;
+    BwShared& sh = shw[w];
+
+    // buffer resources over exactly this sequence's tokens (offsets < 2^31, checked on the host):
+    // reads past its last token return zero, stores there are dropped
+    const auto rk = make_rsrc(static_cast<const char*>(a.k) + seq0 * DK * 2, seq_tok * DK * 2);
+    const auto rq = make_rsrc(static_cast<const char*>(a.q) + seq0 * DK * 2, seq_tok * DK * 2);
+    const auto rv = make_rsrc(static_cast<const char*>(a.v) + seq0 * DV * 2, seq_tok * DV * 2);
+    const auto rgt = make_rsrc(static_cast<const char*>(a.g) + seq0 * GB, seq_tok * GB);
+    const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
+    const auto rdo = make_rsrc(a.dout + seq0 * DV, seq_tok * DV * 4);
+    const auto rdv = make_rsrc(a.dv + seq0 * DV, seq_tok * DV * 4);
+    const float* dense = a.ws_states + bh * static_cast<size_t>(nb) * DK * DV;
+
+    float dS[R];
+#pragma unroll
+    for (int m = 0; m < R; m++)
+        dS[m] = a.dST ? a.dST[bh * DK * DV + static_cast<size_t>(state_row(m, g)) * DV + col] : 0.0f;
+
+    const int voff_kq = (c * H * DK + 8 * g) * 2;  // token c, rows 32 i + 8 g .. + 7 (load i)
+    const int voff_v = (4 * g * H * DV + col) * 2;  // token 4 g + r (soffset), column col
+    const int voff_do = (4 * g * H * DV + col) * 4;
+    const int voff_doT = (c * H * DV + cw0 + 4 * g) * 4;  // token c, columns cw0 + 4 g .. + 3
+    const int voff_gate = c * H * GB;
+
+#pragma unroll 1
+    for (int blk = nb - 1; blk >= 0; blk--) {
+        const int t0 = blk * kBlk;
+        // ------------------------------------------------------------ inputs
+        u4 kk[4], qq[4];
+        const int so_kq = (t0 * H + h) * DK * 2;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            kk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so_kq, 0);
+            qq[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so_kq, 0);
+        }
+        float V4[4];
+        f4 dO4;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            V4[r] = bf_lo(__builtin_amdgcn_raw_buffer_load_b16(rv, voff_v, ((t0 + r) * H + h) * DV * 2, 0));
+            dO4[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdo, voff_do, ((t0 + r) * H + h) * DV * 4, 0));
+        }
+        const f4 dOT = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rdo, voff_doT, (t0 * H + h) * DV * 4, 0));
+        const int so_g = (t0 * H + h) * GB;
+        uint32_t gw, bw;
+        if (GF32) {
+            gw = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gate, so_g, 0);
+            bw = __builtin_amdgcn_raw_buffer_load_b32(rbt, voff_gate, so_g, 0);
+        } else {
+            gw = __builtin_amdgcn_raw_buffer_load_b16(rgt, voff_gate, so_g, 0);
+            bw = __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, so_g, 0);
+        }
+        float s[R];  // S_0: the state entering the block
+        {
+            const float* src = dense + static_cast<size_t>(blk) * DK * DV + col;
+#pragma unroll
+            for (int m = 0; m < R; m++) s[m] = src[static_cast<size_t>(state_row(m, g)) * DV];
+        }
+
+        // ------------------------------------------------------------ Gram matrices, gates
+        // gk (lane (g, c), register r) = k_{4g+r} . k_c, gqk = q_{4g+r} . k_c
+        f4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gqk = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const bf8 ak = __builtin_bit_cast(bf8, kk[i]), aq = __builtin_bit_cast(bf8, qq[i]);
+            gk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, ak, gk, 0, 0, 0);
+            gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, ak, gqk, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            *reinterpret_cast<u4*>(&sh.kN[c][32 * i + 8 * g]) = kk[i];
+            *reinterpret_cast<u4*>(&sh.qN[c][32 * i + 8 * g]) = qq[i];
+        }
+        // lane (g, c): token t0 + c; tokens past the end take gate 0 and beta 0
+        const bool valid = t0 + c < T;
+        const float gv = valid ? (GF32 ? __uint_as_float(gw) : bf_lo(gw)) : 0.0f;
+        const float bv = valid ? (GF32 ? __uint_as_float(bw) : bf_lo(bw)) : 0.0f;
+        const float Gc = row_prefix_sum(gv);  // G_c
+        const float G15 = lane_of(Gc, kBlk - 1);
+        if (g == 0) {
+            sh.G[c] = Gc;
+            sh.beta[c] = bv;
+        }
+        wave_lds_sync();
+        const f4 G4 = *reinterpret_cast<const f4*>(&sh.G[4 * g]);
+        const f4 b4 = *reinterpret_cast<const f4*>(&sh.beta[4 * g]);
+        const float gam15 = expf(G15);
+        const float gam_c = expf(Gc), rho_c = expf(G15 - Gc);
+        f4 gam4, rho4, Rr, a4, c4, aT4;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int j = 4 * g + r;
+            gam4[r] = expf(G4[r]);
+            rho4[r] = expf(G15 - G4[r]);
+            Rr[r] = c <= j ? expf(c <= j ? G4[r] - Gc : 0.0f) : 0.0f;     // r_{j c}
+            const float rt = j < c ? expf(j < c ? Gc - G4[r] : 0.0f) : 0.0f;  // r_{c j}
+            a4[r] = c < j ? Rr[r] * gk[r] : 0.0f;   // A_{j c}
+            c4[r] = Rr[r] * gqk[r];                 // C_{j c}
+            aT4[r] = rt * gk[r];                    // A_{c j}
+        }
+
+        // ------------------------------------------------------------ N = (I + diag(beta) A)^-1
+        // Lane (g, c) solves column c for tokens 4 g .. 4 g + 3 in four stages; after stage st,
+        // lane group st's values are final and one MFMA adds their contribution to later tokens.
+        *reinterpret_cast<f4*>(&sh.AmT[c][4 * g]) = a4;  // AmT[i][j] = A_ji
+        wave_lds_sync();
+        const float c10 = sh.AmT[4 * g][4 * g + 1], c20 = sh.AmT[4 * g][4 * g + 2];
+        const float c21 = sh.AmT[4 * g + 1][4 * g + 2], c30 = sh.AmT[4 * g][4 * g + 3];
+        const float c31 = sh.AmT[4 * g + 1][4 * g + 3], c32 = sh.AmT[4 * g + 2][4 * g + 3];
+        f4 dm = {0.0f, 0.0f, 0.0f, 0.0f}, nsel = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            const float e0 = 4 * g == c ? 1.0f : 0.0f, e1 = 4 * g + 1 == c ? 1.0f : 0.0f;
+            const float e2 = 4 * g + 2 == c ? 1.0f : 0.0f, e3 = 4 * g + 3 == c ? 1.0f : 0.0f;
+            const float x0 = e0 - b4[0] * dm[0];
+            const float x1 = e1 - b4[1] * (dm[1] + c10 * x0);
+            const float x2 = e2 - b4[2] * (dm[2] + c20 * x0 + c21 * x1);
+            const float x3 = e3 - b4[3] * (dm[3] + c30 * x0 + c31 * x1 + c32 * x2);
+            if (g == st) nsel = f4{x0, x1, x2, x3};
+            if (st < 3) {
+                *reinterpret_cast<f4*>(&sh.dd[g][c][0]) = f4{x0, x1, x2, x3};
+                wave_lds_sync();
+                // A: lane (kk, j) = A_{j, 4 st + kk} for tokens j of later groups; B: N_{4 st + kk, c}
+                const float ast = c >= 4 * st + 4 ? sh.AmT[4 * st + g][c] : 0.0f;
+                dm = mfma4(ast, sh.dd[st][c][g], dm);
+                wave_lds_sync();
+            }
+        }
+        *reinterpret_cast<f4*>(&sh.Ns[c][4 * g]) = nsel;  // Ns[c][j] = N_jc
+        wave_lds_sync();
+
+        // ------------------------------------------------------------ forward quantities
+        const f4 P4 = project(s, kk);   // (K S_0)_{4g+r, c}
+        const f4 Z4 = project(dS, kk);  // (K dS')_{4g+r, c}
+        f4 W4;
+#pragma unroll
+        for (int r = 0; r < 4; r++) W4[r] = V4[r] - gam4[r] * P4[r];
+        // Delta = N diag(beta) W: slice s pairs token 4 g + s; A = N_{c, 4g+s}, B = beta W
+        f4 D4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int sl = 0; sl < 4; sl++) D4 = mfma4(sh.Ns[4 * g + sl][c], b4[sl] * W4[sl], D4);
+
+        // ------------------------------------------------------------ adjoint of the block
+        f4 dD4;
+#pragma unroll
+        for (int r = 0; r < 4; r++) dD4[r] = rho4[r] * Z4[r];
+#pragma unroll
+        for (int sl = 0; sl < 4; sl++) dD4 = mfma4(c4[sl], dO4[sl], dD4);  // + C^T dO
+        f4 L4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int sl = 0; sl < 4; sl++) L4 = mfma4(nsel[sl], dD4[sl], L4);  // lambda = N^T dDelta
+        f4 AD4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int sl = 0; sl < 4; sl++) AD4 = mfma4(aT4[sl], D4[sl], AD4);  // A Delta
+        f4 dV4, dU4;
+        float e1[4], e2[4], db[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            dV4[r] = b4[r] * L4[r];
+            dU4[r] = -dV4[r];
+            db[r] = group_sum<16>(L4[r] * (W4[r] - AD4[r]));
+            e1[r] = group_sum<16>(gam4[r] * P4[r] * dU4[r]);
+            e2[r] = group_sum<16>(rho4[r] * Z4[r] * D4[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dV4[r]), rdv, voff_do, ((t0 + r) * H + h) * DV * 4, 0);
+        float sd = 0.0f;
+#pragma unroll
+        for (int m = 0; m < R; m++) sd += dS[m] * s[m];
+        const float sdot = wave_sum(sd);                           // <dS', S_0> over this wave's columns
+        const float e2tot = rows_sum(e2[0] + e2[1] + e2[2] + e2[3]);  // sum over the block's tokens
+
+        // Delta and lambda to the T layout
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            sh.XD[4 * g + r][c] = D4[r];
+            sh.XL[4 * g + r][c] = L4[r];
+        }
+        wave_lds_sync();
+        const f4 DT = *reinterpret_cast<const f4*>(&sh.XD[c][4 * g]);
+        const f4 LT = *reinterpret_cast<const f4*>(&sh.XL[c][4 * g]);
+        // dC = dO Delta^T, lambda Delta^T: slice s pairs column 4 g + s
+        f4 dC4 = {0.0f, 0.0f, 0.0f, 0.0f}, dAr4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int sl = 0; sl < 4; sl++) {
+            dC4 = mfma4(dOT[sl], DT[sl], dC4);
+            dAr4 = mfma4(LT[sl], DT[sl], dAr4);
+        }
+        f4 Ab4, Cb4, dgr4;
+        float ecol = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int j = 4 * g + r;
+            const float dA = c < j ? -b4[r] * dAr4[r] : 0.0f;
+            const float dC = c <= j ? dC4[r] : 0.0f;
+            Ab4[r] = dA * Rr[r];
+            Cb4[r] = dC * Rr[r];
+            const float E = dA * a4[r] + dC * c4[r];
+            ecol += E;
+            dgr4[r] = e1[r] - e2[r] + group_sum<16>(E) + (j == kBlk - 1 ? gam15 * sdot + e2tot : 0.0f);
+        }
+        const float dgc = -rows_sum(ecol);
+
+        // ------------------------------------------------------------ key/query partials
+        // over this wave's columns: dk_S[i][row] = sum_col X1[i][col] S_0[row][col] +
+        // X2[i][col] dS'[row][col], dq_S with X3; X1 = gamma dU, X2 = rho Delta, X3 = gamma dO
+        // (T layout: lane (g, c) is token c).  Tile tau = rows 16 tau .. 16 tau + 15; slice s
+        // pairs column 4 g + s.
+#pragma unroll
+        for (int m = 0; m < R; m++) {
+            sh.SdS[0][state_row(m, g)][c] = s[m];
+            sh.SdS[1][state_row(m, g)][c] = dS[m];
+        }
+        const f4 X1T = (-gam_c * bv) * LT, X2T = rho_c * DT, X3T = gam_c * dOT;
+        wave_lds_sync();
+        f4 dka[8], dqa[8];
+#pragma unroll
+        for (int tau = 0; tau < 8; tau++) {
+            const f4 Sf = *reinterpret_cast<const f4*>(&sh.SdS[0][16 * tau + c][4 * g]);
+            const f4 dSf = *reinterpret_cast<const f4*>(&sh.SdS[1][16 * tau + c][4 * g]);
+            f4 ak = {0.0f, 0.0f, 0.0f, 0.0f}, aq = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int sl = 0; sl < 4; sl++) {
+                ak = mfma4(X1T[sl], Sf[sl], ak);
+                ak = mfma4(X2T[sl], dSf[sl], ak);
+                aq = mfma4(X3T[sl], Sf[sl], aq);
+            }
+            dka[tau] = ak;
+            dqa[tau] = aq;
+        }
+
+        // ------------------------------------------------------------ dS_0
+        // gamma_15 dS' + K^T (gamma dU) + Q^T (gamma dO): tile tau = dS[4 tau .. 4 tau + 3]
+        // (accumulator row 4 g' + r = key row state_row(4 tau + r, g')), A = keys or queries
+        // read transposed from LDS, B = the token vectors in three bf16 parts.
+        {
+            f4 x1, x3;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                x1[r] = gam4[r] * dU4[r];
+                x3[r] = gam4[r] * dO4[r];
+            }
+            bf4 h1, l1, m1, h3, l3, m3;
+            split3<4>(x1, h1, l1, m1);
+            split3<4>(x3, h3, l3, m3);
+#pragma unroll
+            for (int tau = 0; tau < 8; tau++) {
+                const s4 kr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(&sh.kN[0][0] + tr_offset(g, c, tau)));
+                const s4 qr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(&sh.qN[0][0] + tr_offset(g, c, tau)));
+                f4 st = {gam15 * dS[4 * tau], gam15 * dS[4 * tau + 1], gam15 * dS[4 * tau + 2], gam15 * dS[4 * tau + 3]};
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr, __builtin_bit_cast(s4, m1), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qr, __builtin_bit_cast(s4, m3), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr, __builtin_bit_cast(s4, l1), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qr, __builtin_bit_cast(s4, l3), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr, __builtin_bit_cast(s4, h1), st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qr, __builtin_bit_cast(s4, h3), st, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; r++) dS[4 * tau + r] = st[r];
+            }
+        }
+
+        // ------------------------------------------------------------ cross-wave sums
+        // This wave's 64 partial registers (dk tiles, then dq tiles) go over its own S_0/dS'
+        // copy, register quad q of lane L at float (q * 64 + L) * 4; wave w' sums quads
+        // 4 w' .. 4 w' + 3 over the four waves and stores them.
+        wave_lds_sync();
+        {
+            float* flat = &sh.SdS[0][0][0];
+#pragma unroll
+            for (int q = 0; q < 16; q++)
+                *reinterpret_cast<f4*>(flat + (q * 64 + lane) * 4) = q < 8 ? dka[q] : dqa[q - 8];
+            *reinterpret_cast<f4*>(&sh.small[0][lane][0]) = Ab4;
+            *reinterpret_cast<f4*>(&sh.small[1][lane][0]) = Cb4;
+            *reinterpret_cast<f4*>(&sh.small[2][lane][0]) = dgr4;
+            *reinterpret_cast<f4*>(&sh.small[3][lane][0]) = f4{db[0], db[1], db[2], db[3]};
+            *reinterpret_cast<f4*>(&sh.small[4][lane][0]) = f4{dgc, 0.0f, 0.0f, 0.0f};
+        }
+        __syncthreads();
+        {
+            float* rec = a.ws_part + ((bh * nb + blk) * nwg + blockIdx.x) * static_cast<size_t>(kRec);
+#pragma unroll
+            for (int qq4 = 0; qq4 < 4; qq4++) {
+                const int q = 4 * w + qq4;
+                f4 acc = *reinterpret_cast<const f4*>(&shw[0].SdS[0][0][0] + (q * 64 + lane) * 4);
+#pragma unroll
+                for (int ww = 1; ww < kBwWaves; ww++) acc += *reinterpret_cast<const f4*>(&shw[ww].SdS[0][0][0] + (q * 64 + lane) * 4);
+                float* dst = rec + (q < 8 ? kRecDk : kRecDq) + 16 * (q & 7) + c;
+#pragma unroll
+                for (int r = 0; r < 4; r++) dst[(4 * g + r) * DK] = acc[r];
+            }
+            f4 sm = *reinterpret_cast<const f4*>(&shw[0].small[w][lane][0]);
+#pragma unroll
+            for (int ww = 1; ww < kBwWaves; ww++) sm += *reinterpret_cast<const f4*>(&shw[ww].small[w][lane][0]);
+            if (w < 2) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) rec[(w == 0 ? kRecA : kRecC) + (4 * g + r) * kBlk + c] = sm[r];
+            } else if (c == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) rec[(w == 2 ? kRecGr : kRecB) + 4 * g + r] = sm[r];
+            }
+            if (w == 0 && g == 0) {
+                float x = shw[0].small[4][lane][0];
+#pragma unroll
+                for (int ww = 1; ww < kBwWaves; ww++) x += shw[ww].small[4][lane][0];
+                rec[kRecGc + c] = x;
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int m = 0; m < R; m++) a.dS0[bh * DK * DV + static_cast<size_t>(state_row(m, g)) * DV + col] = dS[m];
+}
+
+// Per (block, head, sequence): the workgroups' partial records summed in slice order, the
+// Gram-matrix terms (Ab + Ab^T) K + Cb^T Q and Cb K, the query term of dG, and dg as the
+// suffix sum of dG over the block's tokens.
+__global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArgs a, int nwg) {
+    constexpr int DK = kBwDK;
+    __shared__ float Kf[kBlk][DK + 4], Qf[kBlk][DK + 4];
+    __shared__ float Ab[kBlk][kBlk + 1], Cb[kBlk][kBlk + 1];
+    __shared__ float dG[kBlk], qd[kBlk];
+    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int T = p.T, H = p.H, nb = p.nb;
+    const int t0 = blk * kBlk;
+    const size_t bh = static_cast<size_t>(b) * H + h;
+    const float* rec0 = a.ws_part + (bh * nb + blk) * nwg * static_cast<size_t>(kRec);
+    const uint16_t* kb = static_cast<const uint16_t*>(a.k);
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q);
+    for (int e = tid; e < kBlk * DK; e += 256) {
+        const int i = e / DK, row = e % DK;
+        const bool ok = t0 + i < T;
+        const size_t idx = ((static_cast<size_t>(b) * T + t0 + i) * H + h) * DK + row;
+        Kf[i][row] = ok ? bf16_bits_to_f32(kb[idx]) : 0.0f;
+        Qf[i][row] = ok ? bf16_bits_to_f32(qb[idx]) : 0.0f;
+    }
+    {
+        float sa = 0.0f, sc = 0.0f;
+        for (int wg = 0; wg < nwg; wg++) {
+            sa += rec0[wg * static_cast<size_t>(kRec) + kRecA + tid];
+            sc += rec0[wg * static_cast<size_t>(kRec) + kRecC + tid];
+        }
+        Ab[tid / kBlk][tid % kBlk] = sa;
+        Cb[tid / kBlk][tid % kBlk] = sc;
+    }
+    if (tid < kBlk) {
+        float sg = 0.0f, sb = 0.0f;
+        for (int wg = 0; wg < nwg; wg++) {
+            const float* r = rec0 + wg * static_cast<size_t>(kRec);
+            sg += r[kRecGr + tid] + r[kRecGc + tid];
+            sb += r[kRecB + tid];
+        }
+        dG[tid] = sg;
+        if (t0 + tid < T) a.dbeta[(static_cast<size_t>(b) * T + t0 + tid) * H + h] = sb;
+    }
+    __syncthreads();
+    const int i = tid >> 4, rc = tid & 15;  // token i, rows 8 rc .. 8 rc + 7
+    float ca[kBlk], cq[kBlk], cc[kBlk];
+#pragma unroll
+    for (int j = 0; j < kBlk; j++) {
+        ca[j] = Ab[i][j] + Ab[j][i];
+        cq[j] = Cb[j][i];
+        cc[j] = Cb[i][j];
+    }
+    const bool ok = t0 + i < T;
+    const size_t o = ((static_cast<size_t>(b) * T + t0 + i) * H + h) * DK + 8 * rc;
+    float qdot = 0.0f;
+#pragma unroll 2
+    for (int e = 0; e < 8; e++) {
+        const int row = 8 * rc + e;
+        float dks = 0.0f, dqs = 0.0f;
+        for (int wg = 0; wg < nwg; wg++) {
+            const float* r = rec0 + wg * static_cast<size_t>(kRec);
+            dks += r[kRecDk + i * DK + row];
+            dqs += r[kRecDq + i * DK + row];
+        }
+        qdot += Qf[i][row] * dqs;
+        float xk = 0.0f, xq = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kBlk; j++) {
+            xk += ca[j] * Kf[j][row] + cq[j] * Qf[j][row];
+            xq += cc[j] * Kf[j][row];
+        }
+        if (ok) {
+            a.dk[o + e] = dks + xk;
+            a.dq[o + e] = dqs + xq;
+        }
+    }
+    qdot = group_sum<16>(qdot);
+    if (rc == 0) qd[i] = qdot;
+    __syncthreads();
+    if (tid < kBlk && t0 + tid < T) {
+        float x = 0.0f;
+        for (int j = kBlk - 1; j >= tid; j--) x += dG[j] + qd[j];
+        a.dg[(static_cast<size_t>(b) * T + t0 + tid) * H + h] = x;
+    }
+}
+
+bool bwd_mfma_eligible(const la_config& c) {
+    if (c.d_v % 64 != 0) return false;
+    la_config c16 = c;
+    c16.ckpt_interval = kBlk;
+    if (!fwd_mfma_eligible(c16)) return false;
+    // 32-bit buffer offsets over one sequence's upstream gradient (its last block included)
+    const size_t span = static_cast<size_t>(c.T + kBlk) * c.H * c.d_v * 4;
+    return span < (static_cast<size_t>(1) << 31);
+}
+
+size_t bwd_mfma_state_bytes(const la_config& c) {
+    return static_cast<size_t>(c.B) * c.H * ((c.T + kBlk - 1) / kBlk) * c.d_k * c.d_v * sizeof(float);
+}
+
+size_t bwd_mfma_part_bytes(const la_config& c) {
+    return static_cast<size_t>(c.B) * c.H * ((c.T + kBlk - 1) / kBlk) * (c.d_v / 64) * kRec * sizeof(float);
+}
+
+hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs& a, hipStream_t s) {
+    la_config c16 = c;
+    c16.ckpt_interval = kBlk;
+    hipError_t e = launch_fwd_mfma(c16, fa, s);
+    if (e != hipSuccess) return e;
+    const BwParams p{c.T, c.H, c.d_v, (c.T + kBlk - 1) / kBlk};
+    dim3 grid(c.d_v / 64, c.H, c.B);
+    if (c.gate_dtype == LA_F32)
+        hipLaunchKernelGGL((bwd_mfma_kernel<true>), grid, dim3(kBwThreads), 0, s, p, a);
+    else
+        hipLaunchKernelGGL((bwd_mfma_kernel<false>), grid, dim3(kBwThreads), 0, s, p, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_mfma_reduce_kernel, dim3(p.nb, c.H, c.B), dim3(256), 0, s, p, a, c.d_v / 64);
+    return hipGetLastError();
+}
+
+}  // namespace la

@@ -32,6 +32,7 @@
 // inputs and beta = 0 and leave the state unchanged; their outputs are dropped.
 #include "la_device.hpp"
 #include "la_internal.hpp"
+#include "la_mfma.hpp"
 #include "la_recur.hpp"
 #include "la_wave.hpp"
 
@@ -41,54 +42,9 @@ Params make_params(const la_config& c);
 
 namespace {
 
-constexpr int kBlk = 16;                       // tokens per block
 constexpr int kMThreads = kWaveTileWaves * 64;  // 4 waves = 64 value columns
 constexpr float kGammaLo = 0x1p-60f, kGammaHi = 0x1p60f;
 constexpr int kDppRowShr = 0x110;              // row_shr:n = kDppRowShr + n
-// LDS row of one token's 128 keys, in bf16 elements: 320 bytes, so that the transposed reads of
-// the update (four tokens 320 bytes apart, four 16-byte row offsets) hit distinct banks
-constexpr int kKeyRow = 160;
-
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef float f8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-typedef short s4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-
-typedef float f2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-
-// x = hi + lo + lo2 exactly, each part a bf16 (nearest at each step): the residual of rounding
-// an fp32 value to bf16 is exact in fp32 and has at most 16 significant bits, the residual of
-// that at most 8, which bf16 holds exactly.  Products of exact bf16 inputs with the parts are
-// exact in fp32, so an MFMA over the three parts forms fp32 products (summed in fp32).
-// Two values at a time: one packed conversion per part, whose halves widen back by a shift
-// and a mask (11 operations per pair).
-__device__ __forceinline__ void split3_pair(float x0, float x1, uint32_t& hi, uint32_t& lo, uint32_t& lo2) {
-    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x0, x1}, bf2));
-    const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
-    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{r0, r1}, bf2));
-    const float q0 = r0 - __uint_as_float(lo << 16), q1 = r1 - __uint_as_float(lo & 0xFFFF0000u);
-    lo2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{q0, q1}, bf2));
-}
-template <int N, typename FV, typename BV>
-__device__ __forceinline__ void split3(const FV& x, BV& hi, BV& lo, BV& lo2) {
-    typedef uint32_t uv __attribute__((ext_vector_type(N / 2)));
-    uv h, l, l2;
-#pragma unroll
-    for (int i = 0; i < N / 2; i++) {
-        uint32_t a, b, c;
-        split3_pair(x[2 * i], x[2 * i + 1], a, b, c);
-        h[i] = a;
-        l[i] = b;
-        l2[i] = c;
-    }
-    hi = __builtin_bit_cast(BV, h);
-    lo = __builtin_bit_cast(BV, l);
-    lo2 = __builtin_bit_cast(BV, l2);
-}
-
 // Per-wave LDS of one block.
 struct BlockShared {
     float Gk[kBlk][kBlk];    // [j][i] = k_i . k_j
@@ -97,16 +53,11 @@ struct BlockShared {
     float gam[kBlk], rgam[kBlk], beta[kBlk];
 };
 
-// Key row held in s[m] by lane group g.
-__device__ __forceinline__ int state_row(int m, int g) { return 32 * (m >> 3) + 8 * g + (m & 7); }
-
 // Product with identity-filled lanes: x[lane - n] of the same row of 16, 1.0 below the row.
 template <int N>
 __device__ __forceinline__ float row_shr_or_one(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x), kDppRowShr + N, 0xF, 0xF, false));
 }
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 
 }  // namespace
 
@@ -380,11 +331,7 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             // S_0 + K^T DD, tile tau = s[4 tau .. 4 tau + 3]: accumulator row i = 4 g' + r is
             // key row state_row(4 tau + r, g'); A (row i = c, tokens 4 g .. 4 g + 3) = the keys
             // of those tokens there; B (tokens 4 g + j, column c) = dd, in three bf16 parts.
-            // A comes from the gfx950 transposed LDS read: within each group of 16 lanes, slot j
-            // of lane i is element i % 4 of the 8 bytes addressed by lane 4 j + i / 4.  The rows
-            // lanes 4 a .. 4 a + 3 need are consecutive (32 (tau / 2) + 8 a + 4 (tau % 2) + b), so
-            // lane s of group g addresses token 4 g + s / 4 at the first of lane group
-            // s % 4's rows, and slot j of lane c receives token 4 g + j at row(c).
+            // A comes from the gfx950 transposed LDS read (tr_offset).
             const f4 ddv = {sel[0], sel[1], sel[2], sel[3]};
             bf4 dh, dl, dl2;
             split3<4>(ddv, dh, dl, dl2);
@@ -392,9 +339,7 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
             for (int tau = 0; tau < 8; tau++) {
-                const int off = (4 * g + (c >> 2)) * kKeyRow + 32 * (tau >> 1) + 8 * (c & 3) + 4 * (tau & 1);
-                typedef __attribute__((address_space(3))) s4 lds_s4;
-                const s4 kr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(&kN[w][0][0] + off));
+                const s4 kr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(&kN[w][0][0] + tr_offset(g, c, tau)));
                 f4 st = {s[4 * tau], s[4 * tau + 1], s[4 * tau + 2], s[4 * tau + 3]};
                 st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr, __builtin_bit_cast(s4, dl2), st, 0, 0, 0);
                 st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr, __builtin_bit_cast(s4, dl), st, 0, 0, 0);

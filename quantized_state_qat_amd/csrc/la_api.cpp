@@ -97,6 +97,14 @@ struct WsLayout {
 
 WsLayout ws_layout(const la_config& c) {
     WsLayout L;
+    if (la::bwd_mfma_eligible(c)) {
+        // block backward: the state entering every 16-token block, then the partial records
+        L.states = 0;
+        L.part = round_up(la::bwd_mfma_state_bytes(c));
+        L.ckpts = L.part + round_up(la::bwd_mfma_part_bytes(c));
+        L.total = L.ckpts;
+        return L;
+    }
     // the backward runs in the token layout: tiles of tok_tile_cols value columns
     const size_t tc = static_cast<size_t>(la::tok_tile_cols(c.d_k, c.qdq, c.group));
     const size_t tiles = static_cast<size_t>(la::tok_tiles(c));
@@ -129,6 +137,11 @@ const char* la_last_error(void) { return g_err; }
 const char* la_fwd_kernel_name(const la_config* cfg) {
     if (check_config(cfg, false) != LA_OK) return "";
     return la::fwd_kernel_name(*cfg);
+}
+
+const char* la_bwd_kernel_name(const la_config* cfg) {
+    if (check_config(cfg, false) != LA_OK) return "";
+    return la::bwd_mfma_eligible(*cfg) ? "block" : "token";
 }
 
 la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, const void* v,
@@ -271,6 +284,13 @@ la_status la_recurrent_bwd_ste(const la_config* cfg, const void* q, const void* 
         return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                     workspace ? ws_bytes : static_cast<size_t>(0));
     char* ws = static_cast<char*>(workspace);
+    if (la::bwd_mfma_eligible(c)) {
+        float* dense = reinterpret_cast<float*>(ws + L.states);
+        la::FwdArgs fa{q, k, v, g, beta, S0, nullptr, nullptr, dense};
+        la::BwdArgs a{q, k, v, g, beta, dense, dout, dS_T, dq, dk, dv, dg, dbeta, dS0,
+                      dense, reinterpret_cast<float*>(ws + L.part)};
+        return hip_status(la::launch_bwd_mfma(c, fa, a, s), "la_recurrent_bwd_ste launch");
+    }
     const float* ck = ckpts;
     if (!ck) {
         float* ckw = reinterpret_cast<float*>(ws + L.ckpts);

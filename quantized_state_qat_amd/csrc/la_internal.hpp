@@ -86,5 +86,12 @@ hipError_t launch_fwd_wave(const la_config& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_tok(const la_config& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_copy_state(const la_config& c, const float* src, float* dst, hipStream_t s);
 hipError_t launch_bwd(const la_config& c, const BwdArgs& a, hipStream_t s);
+// Block backward (bwd_mfma.hip): the block forward with a checkpoint every 16 tokens into
+// a.ws_states (fa.ckpts), the block kernel writing partial records to a.ws_part, then their
+// reduction.  Workspace: bwd_mfma_state_bytes + bwd_mfma_part_bytes.
+bool bwd_mfma_eligible(const la_config& c);
+size_t bwd_mfma_state_bytes(const la_config& c);
+size_t bwd_mfma_part_bytes(const la_config& c);
+hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs& a, hipStream_t s);
 
 }  // namespace la

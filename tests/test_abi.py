@@ -22,7 +22,7 @@ def test_library_exports_every_declared_function():
     lib = la.load_library()
     names = header_functions()
     assert set(names) == {"la_recurrent_fwd", "la_recurrent_fwd_varlen", "la_decode_step", "la_decode_step_slots",
-                          "la_recurrent_bwd_ste", "la_bwd_workspace_bytes", "la_fwd_kernel_name",
+                          "la_recurrent_bwd_ste", "la_bwd_workspace_bytes", "la_fwd_kernel_name", "la_bwd_kernel_name",
                           "la_status_string", "la_last_error"}
     for n in names:
         assert hasattr(lib, n), n
@@ -169,6 +169,43 @@ def test_fwd_kernel_selection(kw, name):
     base = dict(B=2, T=100, H=2, d_k=128, d_v=128)
     base.update(kw)
     assert la.la_fwd_kernel_name(la.Config(**base)) == name
+
+
+@pytest.mark.parametrize("kw,name", [
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64), "block"),
+    (dict(qdq=la.LA_QDQ_NONE, ckpt_interval=64, gate_dtype=la.LA_BF16), "block"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=16, ckpt_interval=5), "block"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=16, qdq_interval=32, ckpt_interval=64, d_v=192), "block"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=1, ckpt_interval=64), "token"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=24, ckpt_interval=24), "token"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=64, hadamard=1), "token"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, gate=la.LA_GATE_KEY), "token"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, qkv_dtype=la.LA_F32), "token"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, d_k=64), "token"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=64, qdq_interval=48, ckpt_interval=16, d_v=64), "block"),
+])
+def test_bwd_kernel_selection(kw, name):
+    """Which backward serves a configuration: the block form needs the block forward's
+    configurations (the user's checkpoint spacing aside: it recomputes every block's state)
+    and whole 64-column workgroups."""
+    base = dict(B=2, T=100, H=2, d_k=128, d_v=128)
+    base.update(kw)
+    assert la.la_bwd_kernel_name(la.Config(**base)) == name
+
+
+def test_bwd_block_workspace():
+    """Block backward workspace: the state entering every 16-token block (fp32 d_k x d_v per
+    unit and block), then one partial record of 4672 floats per unit, block and 64-column
+    slice (two 16 x 128 key/query sums, two 16 x 16 Gram-term matrices, three 16-token
+    vectors, padded)."""
+    c = la.Config(B=3, T=100, H=2, d_k=128, d_v=192, qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64,
+                  ckpt_interval=64)
+    assert la.la_bwd_kernel_name(c) == "block"
+    nb = 7
+    states = 3 * 2 * nb * 128 * 192 * 4
+    part = 3 * 2 * nb * 3 * 4672 * 4
+    n = la.la_bwd_workspace_bytes(c)
+    assert n >= states + part and n < states + part + 2 * 256
 
 
 def test_fwd_kernel_name_invalid():
