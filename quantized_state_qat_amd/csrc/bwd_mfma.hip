@@ -138,7 +138,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
     const auto rdo = make_rsrc(a.dout + seq0 * DV, seq_tok * DV * 4);
     const auto rdv = make_rsrc(a.dv + seq0 * DV, seq_tok * DV * 4);
-    const float* dense = a.ws_states + bh * static_cast<size_t>(nb) * DK * DV;
+    // this unit's block-start states (the eligibility check keeps their offsets below 2^31)
+    const auto rst = make_rsrc(a.ws_states + bh * static_cast<size_t>(nb) * DK * DV, static_cast<size_t>(nb) * DK * DV * 4);
+    const int voff_st = (state_row(0, g) * DV + col) * 4;
 
     float dS[R];
 #pragma unroll
@@ -151,40 +153,71 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     const int voff_doT = (c * H * DV + cw0 + 4 * g) * 4;  // token c, columns cw0 + 4 g .. + 3
     const int voff_gate = c * H * GB;
 
+    // A block's inputs (lane (g, c)): keys and queries of token t0 + c at rows
+    // state_row(8 i .. 8 i + 7, g) (load i); values and dO of tokens t0 + 4 g + r at column col;
+    // dO of token t0 + c at columns cw0 + 4 g .. + 3; gate and beta of token t0 + c; the state
+    // entering the block in the state layout.  The next block (in walking order) is fetched
+    // while this one is processed.
+    struct BlockIn {
+        u4 k[4], q[4];
+        uint32_t v[4];
+        f4 dO, dOT;
+        uint32_t g, b;
+        float s[R];
+    };
+    // the loads of a block in three parts (keys and queries; values, dO, gate and beta; the
+    // state), spread over the previous block's steps so that no burst fills the address queue
+    auto fetch_part = [&](BlockIn& in, int blk, int part) __attribute__((always_inline)) {
+        const int t0 = blk * kBlk;
+        if (part == 0) {
+            const int so_kq = (t0 * H + h) * DK * 2;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                in.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so_kq, 0);
+                in.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so_kq, 0);
+            }
+        } else if (part == 1) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                in.v[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff_v, ((t0 + r) * H + h) * DV * 2, 0);
+                in.dO[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdo, voff_do, ((t0 + r) * H + h) * DV * 4, 0));
+            }
+            in.dOT = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rdo, voff_doT, (t0 * H + h) * DV * 4, 0));
+            const int so_g = (t0 * H + h) * GB;
+            if (GF32) {
+                in.g = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gate, so_g, 0);
+                in.b = __builtin_amdgcn_raw_buffer_load_b32(rbt, voff_gate, so_g, 0);
+            } else {
+                in.g = __builtin_amdgcn_raw_buffer_load_b16(rgt, voff_gate, so_g, 0);
+                in.b = __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, so_g, 0);
+            }
+        } else {
+            // rows state_row(m, g) = state_row(0, g) + 32 (m / 8) + m % 8: the row step is uniform
+            const int so = blk * DK * DV * 4;
+#pragma unroll
+            for (int m = 0; m < R; m++)
+                in.s[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rst, voff_st, so + (32 * (m >> 3) + (m & 7)) * DV * 4, 0));
+        }
+    };
+
+    BlockIn cur, nxt;
+    fetch_part(cur, nb - 1, 0);
+    fetch_part(cur, nb - 1, 1);
+    fetch_part(cur, nb - 1, 2);
 #pragma unroll 1
     for (int blk = nb - 1; blk >= 0; blk--) {
         const int t0 = blk * kBlk;
-        // ------------------------------------------------------------ inputs
-        u4 kk[4], qq[4];
-        const int so_kq = (t0 * H + h) * DK * 2;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            kk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so_kq, 0);
-            qq[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so_kq, 0);
-        }
+        // the block walked next (block 0 again after the last: no branch, so the compiler's
+        // waits for this block's loads do not also wait for the next block's)
+        const int bn = blk > 0 ? blk - 1 : 0;
+        const u4(&kk)[4] = cur.k;
+        const u4(&qq)[4] = cur.q;
+        const float(&s)[R] = cur.s;
+        const f4 dO4 = cur.dO, dOT = cur.dOT;
+        const uint32_t gw = cur.g, bw = cur.b;
         float V4[4];
-        f4 dO4;
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            V4[r] = bf_lo(__builtin_amdgcn_raw_buffer_load_b16(rv, voff_v, ((t0 + r) * H + h) * DV * 2, 0));
-            dO4[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdo, voff_do, ((t0 + r) * H + h) * DV * 4, 0));
-        }
-        const f4 dOT = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rdo, voff_doT, (t0 * H + h) * DV * 4, 0));
-        const int so_g = (t0 * H + h) * GB;
-        uint32_t gw, bw;
-        if (GF32) {
-            gw = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gate, so_g, 0);
-            bw = __builtin_amdgcn_raw_buffer_load_b32(rbt, voff_gate, so_g, 0);
-        } else {
-            gw = __builtin_amdgcn_raw_buffer_load_b16(rgt, voff_gate, so_g, 0);
-            bw = __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, so_g, 0);
-        }
-        float s[R];  // S_0: the state entering the block
-        {
-            const float* src = dense + static_cast<size_t>(blk) * DK * DV + col;
-#pragma unroll
-            for (int m = 0; m < R; m++) s[m] = src[static_cast<size_t>(state_row(m, g)) * DV];
-        }
+        for (int r = 0; r < 4; r++) V4[r] = bf_lo(cur.v[r]);
 
         // ------------------------------------------------------------ Gram matrices, gates
         // gk (lane (g, c), register r) = k_{4g+r} . k_c, gqk = q_{4g+r} . k_c
@@ -195,6 +228,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
             gk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, ak, gk, 0, 0, 0);
             gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, ak, gqk, 0, 0, 0);
         }
+        fetch_part(nxt, bn, 0);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             *reinterpret_cast<u4*>(&sh.kN[c][32 * i + 8 * g]) = kk[i];
@@ -257,10 +291,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
         }
         *reinterpret_cast<f4*>(&sh.Ns[c][4 * g]) = nsel;  // Ns[c][j] = N_jc
         wave_lds_sync();
+        fetch_part(nxt, bn, 1);
 
         // ------------------------------------------------------------ forward quantities
         const f4 P4 = project(s, kk);   // (K S_0)_{4g+r, c}
         const f4 Z4 = project(dS, kk);  // (K dS')_{4g+r, c}
+        fetch_part(nxt, bn, 2);
         f4 W4;
 #pragma unroll
         for (int r = 0; r < 4; r++) W4[r] = V4[r] - gam4[r] * P4[r];
@@ -436,6 +472,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
             }
         }
         __syncthreads();
+        cur = nxt;
     }
 
 #pragma unroll
@@ -444,7 +481,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
 
 // Per (block, head, sequence): the workgroups' partial records summed in slice order, the
 // Gram-matrix terms (Ab + Ab^T) K + Cb^T Q and Cb K, the query term of dG, and dg as the
-// suffix sum of dG over the block's tokens.
+// suffix sum of dG over the block's tokens.  Thread (i, rc) owns token i, rows 8 rc .. 8 rc + 7
+// (16-byte loads and stores; the 16 threads of a token cover its 512-byte row).
 __global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArgs a, int nwg) {
     constexpr int DK = kBwDK;
     __shared__ float Kf[kBlk][DK + 4], Qf[kBlk][DK + 4];
@@ -456,14 +494,22 @@ __global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArg
     const int t0 = blk * kBlk;
     const size_t bh = static_cast<size_t>(b) * H + h;
     const float* rec0 = a.ws_part + (bh * nb + blk) * nwg * static_cast<size_t>(kRec);
-    const uint16_t* kb = static_cast<const uint16_t*>(a.k);
-    const uint16_t* qb = static_cast<const uint16_t*>(a.q);
-    for (int e = tid; e < kBlk * DK; e += 256) {
-        const int i = e / DK, row = e % DK;
-        const bool ok = t0 + i < T;
-        const size_t idx = ((static_cast<size_t>(b) * T + t0 + i) * H + h) * DK + row;
-        Kf[i][row] = ok ? bf16_bits_to_f32(kb[idx]) : 0.0f;
-        Qf[i][row] = ok ? bf16_bits_to_f32(qb[idx]) : 0.0f;
+    const int i = tid >> 4, rc = tid & 15;
+    const bool ok = t0 + i < T;
+    const size_t o = ((static_cast<size_t>(b) * T + t0 + i) * H + h) * DK + 8 * rc;
+    {
+        u4 kw = {0u, 0u, 0u, 0u}, qw = {0u, 0u, 0u, 0u};
+        if (ok) {
+            kw = *reinterpret_cast<const u4*>(static_cast<const uint16_t*>(a.k) + o);
+            qw = *reinterpret_cast<const u4*>(static_cast<const uint16_t*>(a.q) + o);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            Kf[i][8 * rc + 2 * e] = __uint_as_float(kw[e] << 16);
+            Kf[i][8 * rc + 2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
+            Qf[i][8 * rc + 2 * e] = __uint_as_float(qw[e] << 16);
+            Qf[i][8 * rc + 2 * e + 1] = __uint_as_float(qw[e] & 0xFFFF0000u);
+        }
     }
     {
         float sa = 0.0f, sc = 0.0f;
@@ -484,37 +530,41 @@ __global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArg
         dG[tid] = sg;
         if (t0 + tid < T) a.dbeta[(static_cast<size_t>(b) * T + t0 + tid) * H + h] = sb;
     }
-    __syncthreads();
-    const int i = tid >> 4, rc = tid & 15;  // token i, rows 8 rc .. 8 rc + 7
-    float ca[kBlk], cq[kBlk], cc[kBlk];
+    // the slices' key/query sums for this thread's eight rows
+    f4 dks[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    f4 dqs[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    for (int wg = 0; wg < nwg; wg++) {
+        const float* r = rec0 + wg * static_cast<size_t>(kRec) + i * DK + 8 * rc;
 #pragma unroll
-    for (int j = 0; j < kBlk; j++) {
-        ca[j] = Ab[i][j] + Ab[j][i];
-        cq[j] = Cb[j][i];
-        cc[j] = Cb[i][j];
+        for (int hh = 0; hh < 2; hh++) {
+            dks[hh] += *reinterpret_cast<const f4*>(r + kRecDk + 4 * hh);
+            dqs[hh] += *reinterpret_cast<const f4*>(r + kRecDq + 4 * hh);
+        }
     }
-    const bool ok = t0 + i < T;
-    const size_t o = ((static_cast<size_t>(b) * T + t0 + i) * H + h) * DK + 8 * rc;
+    __syncthreads();
     float qdot = 0.0f;
-#pragma unroll 2
-    for (int e = 0; e < 8; e++) {
-        const int row = 8 * rc + e;
-        float dks = 0.0f, dqs = 0.0f;
-        for (int wg = 0; wg < nwg; wg++) {
-            const float* r = rec0 + wg * static_cast<size_t>(kRec);
-            dks += r[kRecDk + i * DK + row];
-            dqs += r[kRecDq + i * DK + row];
-        }
-        qdot += Qf[i][row] * dqs;
-        float xk = 0.0f, xq = 0.0f;
+    f4 dko[2] = {dks[0], dks[1]}, dqo[2] = {dqs[0], dqs[1]};
 #pragma unroll
-        for (int j = 0; j < kBlk; j++) {
-            xk += ca[j] * Kf[j][row] + cq[j] * Qf[j][row];
-            xq += cc[j] * Kf[j][row];
+    for (int hh = 0; hh < 2; hh++) {
+        const f4 qv = *reinterpret_cast<const f4*>(&Qf[i][8 * rc + 4 * hh]);
+        qdot += qv[0] * dqs[hh][0] + qv[1] * dqs[hh][1] + qv[2] * dqs[hh][2] + qv[3] * dqs[hh][3];
+    }
+#pragma unroll 4
+    for (int j = 0; j < kBlk; j++) {
+        const float ca = Ab[i][j] + Ab[j][i], cq = Cb[j][i], cc = Cb[i][j];
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            const f4 kv = *reinterpret_cast<const f4*>(&Kf[j][8 * rc + 4 * hh]);
+            const f4 qv = *reinterpret_cast<const f4*>(&Qf[j][8 * rc + 4 * hh]);
+            dko[hh] += ca * kv + cq * qv;
+            dqo[hh] += cc * kv;
         }
-        if (ok) {
-            a.dk[o + e] = dks + xk;
-            a.dq[o + e] = dqs + xq;
+    }
+    if (ok) {
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            *reinterpret_cast<f4*>(a.dk + o + 4 * hh) = dko[hh];
+            *reinterpret_cast<f4*>(a.dq + o + 4 * hh) = dqo[hh];
         }
     }
     qdot = group_sum<16>(qdot);
