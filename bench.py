@@ -103,7 +103,8 @@ def bench_decode(steps, warmup):
 
 
 def bench_long_e4m3(steps=3, warmup=1):
-    """GDN B=8 H=16 T=4096 d=128, E4M3 tile QDQ every 64 tokens."""
+    """GDN B=8 H=16 T=4096 d=128, E4M3 tile QDQ every 64 tokens: the forward alone, then the
+    training pair (forward with 64-token checkpoints, straight-through backward)."""
     import numpy as np
     import torch
 
@@ -111,11 +112,11 @@ def bench_long_e4m3(steps=3, warmup=1):
     import synth
 
     w = synth.WORKLOADS[2]
-    d = synth.generate(w)
+    d = synth.generate(w, with_do=True)
     dev = {}
     for k in ("q", "k", "v"):
         dev[k] = torch.from_numpy(d[k].bits.astype(np.int16)).view(torch.bfloat16).cuda()
-    for k in ("g", "beta"):
+    for k in ("g", "beta", "do"):
         dev[k] = torch.from_numpy(d[k].f32).cuda()
     del d
     o = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
@@ -125,14 +126,39 @@ def bench_long_e4m3(steps=3, warmup=1):
     stream = torch.cuda.current_stream()
     t = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
                                                 ST, stream=stream), steps, warmup, stream)
-    flops = 7.0 * w.d_k * w.d_v * w.B * w.H * w.T
-    return {
+    unit = w.d_k * w.d_v * w.B * w.H * w.T
+    fwd = {
         "workload": "gdn_long_e4m3_64 B=8 H=16 T=4096 d_k=d_v=128 bf16 q/k/v, fp32 g/beta/state, E4M3 tile QDQ every 64 tokens",
         "kernel": la.la_fwd_kernel_name(c), "ms_per_call": t * 1e3, "updates_per_s": w.B * w.H * w.T / t,
-        "roofline": _fp32_roofline(flops, t, "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head) "
-                                             "against the FP32 peak; the block kernel forms it on the matrix cores "
-                                             "from exact bf16 products with fp32 sums"),
+        "roofline": _fp32_roofline(7.0 * unit, t, "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head) "
+                                                  "against the FP32 peak; the block kernel forms it on the matrix cores "
+                                                  "from exact bf16 products with fp32 sums"),
     }
+
+    c.ckpt_interval = 64
+    ck = torch.empty((w.B, w.H, w.T // 64, w.d_k, w.d_v), device="cuda")
+    grads = [torch.empty((w.B, w.T, w.H, n), device="cuda") for n in (w.d_k, w.d_k, w.d_v)]
+    dg = torch.empty((w.B, w.T, w.H), device="cuda")
+    dbeta = torch.empty((w.B, w.T, w.H), device="cuda")
+    dS0 = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    nbytes = la.la_bwd_workspace_bytes(c)
+    ws = torch.empty((nbytes + 255) // 4, dtype=torch.float32, device="cuda")
+    t_f = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
+                                                  ST, ck, stream=stream), steps, warmup, stream)
+    t_b = _time_calls(lambda: la.la_recurrent_bwd_ste(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, ck,
+                                                      dev["do"], None, grads[0], grads[1], grads[2], dg, dbeta, dS0,
+                                                      ws, nbytes, stream=stream), steps, warmup, stream)
+    fwdbwd = {
+        "workload": "gdn_long_e4m3_64 training pair: forward with 64-token checkpoints, then the straight-through "
+                    "backward (same inputs, fp32 upstream gradient of o)",
+        "kernel_fwd": la.la_fwd_kernel_name(c), "kernel_bwd": la.la_bwd_kernel_name(c),
+        "ms_fwd": t_f * 1e3, "ms_bwd": t_b * 1e3, "workspace_bytes": nbytes,
+        "updates_per_s": w.B * w.H * w.T / (t_f + t_b),
+        "roofline_bwd": _fp32_roofline(22.0 * unit, t_b, "backward only: recompute 7 + adjoint 15 d_k d_v flops per "
+                                                         "token-head (the block path also recomputes every block's "
+                                                         "entering state with the block forward, not counted)"),
+    }
+    return fwd, fwdbwd
 
 
 def _dev(t):
@@ -414,7 +440,8 @@ def main():
         },
     }
     if not args.no_extra:
-        line["extra"] = {"long_sequence": bench_long_e4m3(), "kda_int8g64_tok": bench_kda_tok(),
+        long_fwd, long_fwdbwd = bench_long_e4m3()
+        line["extra"] = {"long_sequence": long_fwd, "long_sequence_fwdbwd": long_fwdbwd, "kda_int8g64_tok": bench_kda_tok(),
                          "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "decode_slots": bench_decode_slots(),
                          "varlen_prefill": bench_varlen()}
     if not args.no_cpu:

@@ -28,9 +28,10 @@
 // (g, c) holds rows 4 g .. 4 g + 3 of column c) or transposed ("T": lane (g, c) holds row c,
 // columns 4 g .. 4 g + 3).  Products over the 128 key rows use bf16 MFMAs of the raw keys and
 // queries (exact) with the other operand split exactly into three bf16 parts; products over 16
-// tokens or 16 columns use fp32 MFMAs (16x16x4).  The four waves of a workgroup sum their
-// partial key/query/gate sums (over their columns) in LDS; the reduction kernel adds the
-// workgroups of a head in a fixed order and applies the Gram-matrix terms once per head.
+// tokens or 16 columns use fp32 MFMAs (16x16x4).  The key/query sums over value columns are
+// formed per workgroup (each wave reads the other waves' rows from LDS and takes 32 key rows),
+// the small per-token sums are added across the four waves in LDS; the reduction kernel adds
+// the workgroups of a head in a fixed order and applies the Gram-matrix terms once per head.
 #include "la_device.hpp"
 #include "la_internal.hpp"
 #include "la_mfma.hpp"
@@ -63,7 +64,7 @@ struct BwParams {
 struct BwShared {
     uint16_t kN[kBlk][kKeyRow];  // the block's keys, [token][row] (transposed reads of the update)
     uint16_t qN[kBlk][kKeyRow];  // and queries
-    float SdS[2][kBwDK][16];     // S_0 and dS' by [row][column]; then this wave's partial sums
+    float SdS[2][kBwDK][16];     // S_0 and dS' by [row][column]
     float small[5][64][4];       // small partial sums for the cross-wave reduction
     float AmT[kBlk][20];         // [i][j] = A_ji
     float dd[4][kBlk][4];        // solve: stage values of tokens 4 g + r, [g][column][r]
@@ -150,7 +151,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     const int voff_kq = (c * H * DK + 8 * g) * 2;  // token c, rows 32 i + 8 g .. + 7 (load i)
     const int voff_v = (4 * g * H * DV + col) * 2;  // token 4 g + r (soffset), column col
     const int voff_do = (4 * g * H * DV + col) * 4;
-    const int voff_doT = (c * H * DV + cw0 + 4 * g) * 4;  // token c, columns cw0 + 4 g .. + 3
+    // token c, columns 64 x + 16 ww + 4 g .. + 3 for the four waves ww of the workgroup
+    const int voff_doT = (c * H * DV + blockIdx.x * 64 + 4 * g) * 4;
     const int voff_gate = c * H * GB;
 
     // A block's inputs (lane (g, c)): keys and queries of token t0 + c at rows
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     struct BlockIn {
         u4 k[4], q[4];
         uint32_t v[4];
-        f4 dO, dOT;
+        f4 dO, dOT[kBwWaves];
         uint32_t g, b;
         float s[R];
     };
@@ -182,7 +184,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
                 in.v[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff_v, ((t0 + r) * H + h) * DV * 2, 0);
                 in.dO[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdo, voff_do, ((t0 + r) * H + h) * DV * 4, 0));
             }
-            in.dOT = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rdo, voff_doT, (t0 * H + h) * DV * 4, 0));
+#pragma unroll
+            for (int ww = 0; ww < kBwWaves; ww++)
+                in.dOT[ww] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rdo, voff_doT + 64 * ww, (t0 * H + h) * DV * 4, 0));
             const int so_g = (t0 * H + h) * GB;
             if (GF32) {
                 in.g = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gate, so_g, 0);
@@ -213,7 +217,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
         const u4(&kk)[4] = cur.k;
         const u4(&qq)[4] = cur.q;
         const float(&s)[R] = cur.s;
-        const f4 dO4 = cur.dO, dOT = cur.dOT;
+        const f4 dO4 = cur.dO;
+        const f4 dOT = w == 0 ? cur.dOT[0] : w == 1 ? cur.dOT[1] : w == 2 ? cur.dOT[2] : cur.dOT[3];  // this wave's columns
         const uint32_t gw = cur.g, bw = cur.b;
         float V4[4];
 #pragma unroll
@@ -367,38 +372,21 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
         }
         const float dgc = -rows_sum(ecol);
 
-        // ------------------------------------------------------------ key/query partials
-        // over this wave's columns: dk_S[i][row] = sum_col X1[i][col] S_0[row][col] +
-        // X2[i][col] dS'[row][col], dq_S with X3; X1 = gamma dU, X2 = rho Delta, X3 = gamma dO
-        // (T layout: lane (g, c) is token c).  Tile tau = rows 16 tau .. 16 tau + 15; slice s
-        // pairs column 4 g + s.
+        // ------------------------------------------------------------ dS_0
+        // gamma_15 dS' + K^T (gamma dU) + Q^T (gamma dO): tile tau = dS[4 tau .. 4 tau + 3]
+        // (accumulator row 4 g' + r = key row state_row(4 tau + r, g')), A = keys or queries
+        // read transposed from LDS, B = the token vectors in three bf16 parts.  S_0 and dS'
+        // (before the update) go to LDS first, for the key/query sums below.
 #pragma unroll
         for (int m = 0; m < R; m++) {
             sh.SdS[0][state_row(m, g)][c] = s[m];
             sh.SdS[1][state_row(m, g)][c] = dS[m];
         }
-        const f4 X1T = (-gam_c * bv) * LT, X2T = rho_c * DT, X3T = gam_c * dOT;
-        wave_lds_sync();
-        f4 dka[8], dqa[8];
-#pragma unroll
-        for (int tau = 0; tau < 8; tau++) {
-            const f4 Sf = *reinterpret_cast<const f4*>(&sh.SdS[0][16 * tau + c][4 * g]);
-            const f4 dSf = *reinterpret_cast<const f4*>(&sh.SdS[1][16 * tau + c][4 * g]);
-            f4 ak = {0.0f, 0.0f, 0.0f, 0.0f}, aq = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int sl = 0; sl < 4; sl++) {
-                ak = mfma4(X1T[sl], Sf[sl], ak);
-                ak = mfma4(X2T[sl], dSf[sl], ak);
-                aq = mfma4(X3T[sl], Sf[sl], aq);
-            }
-            dka[tau] = ak;
-            dqa[tau] = aq;
-        }
-
-        // ------------------------------------------------------------ dS_0
-        // gamma_15 dS' + K^T (gamma dU) + Q^T (gamma dO): tile tau = dS[4 tau .. 4 tau + 3]
-        // (accumulator row 4 g' + r = key row state_row(4 tau + r, g')), A = keys or queries
-        // read transposed from LDS, B = the token vectors in three bf16 parts.
+        *reinterpret_cast<f4*>(&sh.small[0][lane][0]) = Ab4;
+        *reinterpret_cast<f4*>(&sh.small[1][lane][0]) = Cb4;
+        *reinterpret_cast<f4*>(&sh.small[2][lane][0]) = dgr4;
+        *reinterpret_cast<f4*>(&sh.small[3][lane][0]) = f4{db[0], db[1], db[2], db[3]};
+        *reinterpret_cast<f4*>(&sh.small[4][lane][0]) = f4{dgc, 0.0f, 0.0f, 0.0f};
         {
             f4 x1, x3;
 #pragma unroll
@@ -424,36 +412,60 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
                 for (int r = 0; r < 4; r++) dS[4 * tau + r] = st[r];
             }
         }
-
-        // ------------------------------------------------------------ cross-wave sums
-        // This wave's 64 partial registers (dk tiles, then dq tiles) go over its own S_0/dS'
-        // copy, register quad q of lane L at float (q * 64 + L) * 4; wave w' sums quads
-        // 4 w' .. 4 w' + 3 over the four waves and stores them.
-        wave_lds_sync();
-        {
-            float* flat = &sh.SdS[0][0][0];
-#pragma unroll
-            for (int q = 0; q < 16; q++)
-                *reinterpret_cast<f4*>(flat + (q * 64 + lane) * 4) = q < 8 ? dka[q] : dqa[q - 8];
-            *reinterpret_cast<f4*>(&sh.small[0][lane][0]) = Ab4;
-            *reinterpret_cast<f4*>(&sh.small[1][lane][0]) = Cb4;
-            *reinterpret_cast<f4*>(&sh.small[2][lane][0]) = dgr4;
-            *reinterpret_cast<f4*>(&sh.small[3][lane][0]) = f4{db[0], db[1], db[2], db[3]};
-            *reinterpret_cast<f4*>(&sh.small[4][lane][0]) = f4{dgc, 0.0f, 0.0f, 0.0f};
-        }
         __syncthreads();
+
+        // ------------------------------------------------------------ key/query sums
+        // over the workgroup's 64 columns, wave w taking key rows 32 w .. 32 w + 31 (tiles u = 0,
+        // 1 of 16 rows): dk_S[i][row] = sum_col X1[i][col] S_0[row][col] + X2[i][col] dS'[row][col],
+        // dq_S with X3; X1 = gamma dU = -gamma beta lambda, X2 = rho Delta, X3 = gamma dO, all
+        // row-scaled per token i (lane (g, c): token c).  Source wave ww, slice s pairs column
+        // 16 ww + 4 g + s: A from its lambda / Delta rows (XL, XD) or the dO load, B from its
+        // S_0 / dS' rows.  The sums are over the workgroup's columns: no cross-wave step.
         {
+            const float k1 = -gam_c * bv;
+            f4 ak[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+            f4 aq[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+            // operands of source wave ww: lambda and Delta rows of token c, then S_0 and dS' at
+            // rows 32 w + 16 u + c; the next wave's are read while this one's MFMAs run
+            struct TileOps {
+                f4 l, d, S[2], dS[2];
+            };
+            auto read_ops = [&](TileOps& t, int ww) __attribute__((always_inline)) {
+                t.l = *reinterpret_cast<const f4*>(&shw[ww].XL[c][4 * g]);
+                t.d = *reinterpret_cast<const f4*>(&shw[ww].XD[c][4 * g]);
+#pragma unroll
+                for (int u = 0; u < 2; u++) {
+                    t.S[u] = *reinterpret_cast<const f4*>(&shw[ww].SdS[0][32 * w + 16 * u + c][4 * g]);
+                    t.dS[u] = *reinterpret_cast<const f4*>(&shw[ww].SdS[1][32 * w + 16 * u + c][4 * g]);
+                }
+            };
+            TileOps ops[2];
+            read_ops(ops[0], 0);
+#pragma unroll
+            for (int ww = 0; ww < kBwWaves; ww++) {
+                if (ww + 1 < kBwWaves) read_ops(ops[(ww + 1) & 1], ww + 1);
+                const TileOps& t = ops[ww & 1];
+                const f4 x1 = k1 * t.l, x2 = rho_c * t.d, x3 = gam_c * cur.dOT[ww];
+#pragma unroll
+                for (int sl = 0; sl < 4; sl++) {
+#pragma unroll
+                    for (int u = 0; u < 2; u++) {
+                        ak[u] = mfma4(x1[sl], t.S[u][sl], ak[u]);
+                        aq[u] = mfma4(x3[sl], t.S[u][sl], aq[u]);
+                        ak[u] = mfma4(x2[sl], t.dS[u][sl], ak[u]);
+                    }
+                }
+            }
             float* rec = a.ws_part + ((bh * nb + blk) * nwg + blockIdx.x) * static_cast<size_t>(kRec);
 #pragma unroll
-            for (int qq4 = 0; qq4 < 4; qq4++) {
-                const int q = 4 * w + qq4;
-                f4 acc = *reinterpret_cast<const f4*>(&shw[0].SdS[0][0][0] + (q * 64 + lane) * 4);
+            for (int u = 0; u < 2; u++) {
 #pragma unroll
-                for (int ww = 1; ww < kBwWaves; ww++) acc += *reinterpret_cast<const f4*>(&shw[ww].SdS[0][0][0] + (q * 64 + lane) * 4);
-                float* dst = rec + (q < 8 ? kRecDk : kRecDq) + 16 * (q & 7) + c;
-#pragma unroll
-                for (int r = 0; r < 4; r++) dst[(4 * g + r) * DK] = acc[r];
+                for (int r = 0; r < 4; r++) {
+                    rec[kRecDk + (4 * g + r) * DK + 32 * w + 16 * u + c] = ak[u][r];
+                    rec[kRecDq + (4 * g + r) * DK + 32 * w + 16 * u + c] = aq[u][r];
+                }
             }
+            // the small sums: wave w adds slot w of the four waves (wave 0 also slot 4)
             f4 sm = *reinterpret_cast<const f4*>(&shw[0].small[w][lane][0]);
 #pragma unroll
             for (int ww = 1; ww < kBwWaves; ww++) sm += *reinterpret_cast<const f4*>(&shw[ww].small[w][lane][0]);
