@@ -175,11 +175,13 @@ size_t la_bwd_workspace_bytes(const la_config* cfg);
  * Which forward kernel la_recurrent_fwd runs for cfg (diagnostic; no GPU work, no state):
  *   "block"  GDN, d_k = 128, bf16 q/k/v, rounding at most every 16 tokens (interval and
  *            checkpoint spacing multiples of 16): 16-token blocks on the matrix cores;
- *   "wave"   GDN, no Hadamard, interval and checkpoint spacing multiples of 8: one wave per
- *            16 value columns, no barrier per token;
+ *   "wave"   GDN or KDA, no Hadamard, interval and checkpoint spacing multiples of 8 (and
+ *            no rounding point strictly inside a checkpoint chunk): one wave per 16 value
+ *            columns, no barrier per token;
  *   "fast"   GDN, no Hadamard, rounding at most every 2 tokens, no rounding point strictly
  *            inside a checkpoint chunk: eight waves per 64 columns, rescaled state;
- *   "token"  every other valid configuration (KDA, Hadamard, rounding every token).
+ *   "token"  every other valid configuration (Hadamard, rounding every token, KDA with an
+ *            interval or checkpoint spacing that is not a multiple of 8).
  * Returns "" (and sets la_last_error) for an invalid cfg.  The kernels differ only in the
  * order of floating-point operations; every one computes the same recurrence.
  */

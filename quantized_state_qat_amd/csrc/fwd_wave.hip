@@ -21,6 +21,10 @@
 //    past the end of the tensor return zero and are never used).
 // Rounding points and checkpoints fall on block boundaries, where the state is folded
 // (F = 1) before it is rounded or stored.
+// Per-key gates (KDA): each token's gates a = exp(g) arrive spread over the row group's lanes
+// like its keys, and a third DPP pass scales the state rows (S~ = diag(a) S) before the two
+// FMA passes; no rescale is carried (a per-row gate cannot be folded into one scalar), so
+// every block runs the same way and the gate windows only supply beta.
 #include "la_device.hpp"
 #include "la_internal.hpp"
 #include "la_recur.hpp"
@@ -39,7 +43,7 @@ constexpr float kFoldLo = 0x1p-30f, kFoldHi = 0x1p30f;
 
 }  // namespace
 
-template <int DK, int QMODE, int G, bool BF16, bool GF32, bool OBF16>
+template <int DK, int QMODE, int G, bool BF16, bool GF32, bool OBF16, bool KDA>
 __global__ __launch_bounds__(kWaveThreads) void fwd_wave_kernel(Params p, FwdArgs a) {
     constexpr int R = DK / 4;                       // state rows per lane
     constexpr int KPL = R >= 32 ? 2 : 1;            // key (query) values per lane
@@ -47,6 +51,7 @@ __global__ __launch_bounds__(kWaveThreads) void fwd_wave_kernel(Params p, FwdArg
     constexpr int IB = BF16 ? 2 : 4;                // input element bytes
     constexpr int OB = OBF16 ? 2 : 4;
     constexpr int GB = GF32 ? 4 : 2;
+    constexpr int NWG = (KPL == 2 && GF32) ? 2 : 1;  // raw words per lane of a token's key gates (KDA)
 
     __shared__ WaveQdqShared<DK, QMODE, G> qsh;
 
@@ -67,13 +72,15 @@ __global__ __launch_bounds__(kWaveThreads) void fwd_wave_kernel(Params p, FwdArg
     const auto rk = make_rsrc(static_cast<const char*>(a.k) + seq0 * DK * IB, seq_tok * DK * IB);
     const auto rq = make_rsrc(static_cast<const char*>(a.q) + seq0 * DK * IB, seq_tok * DK * IB);
     const auto rv = make_rsrc(static_cast<const char*>(a.v) + seq0 * DV * IB, seq_tok * DV * IB);
-    const auto rgt = make_rsrc(static_cast<const char*>(a.g) + seq0 * GB, seq_tok * GB);
+    // scalar gates [B][T][H]; per-key gates [B][T][H][d_k]
+    const auto rgt = make_rsrc(static_cast<const char*>(a.g) + seq0 * (KDA ? DK : 1) * GB, seq_tok * (KDA ? DK : 1) * GB);
     const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
     const bool has_o = a.o != nullptr;
     const auto ro = make_rsrc(has_o ? static_cast<const char*>(a.o) + seq0 * DV * OB : nullptr,
                               has_o ? seq_tok * DV * OB : 0);
     // this lane's key element(s) within a token's row, its value column, its output slot
     const int voff_k = (KPL == 2 ? 2 * lane : rg * R + (c % R)) * IB;
+    const int voff_gk = (KPL == 2 ? 2 * lane : rg * R + (c % R)) * GB;  // the same key rows' gates (KDA)
     const int voff_v = col * IB;
     const int voff_o = (rg * H * DV + col) * OB;  // row group r stores token t4 + r
 
@@ -89,6 +96,7 @@ __global__ __launch_bounds__(kWaveThreads) void fwd_wave_kernel(Params p, FwdArg
     // ---------------------------------------------------------------- inputs
     struct Raw {
         uint32_t k[NW], q[NW], v;
+        uint32_t gk[NWG];  // KDA only
     };
     auto fetch = [&](Raw& r, int tt) {
         const int so_k = (tt * H + h) * (DK * IB);
@@ -107,6 +115,31 @@ __global__ __launch_bounds__(kWaveThreads) void fwd_wave_kernel(Params p, FwdArg
         }
         if (BF16) r.v = __builtin_amdgcn_raw_buffer_load_b16(rv, voff_v, so_v, 0);
         else r.v = __builtin_amdgcn_raw_buffer_load_b32(rv, voff_v, so_v, 0);
+        if constexpr (KDA) {
+            const int so_g = (tt * H + h) * (DK * GB);
+            if (KPL == 2 && GF32) {
+                r.gk[0] = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gk, so_g, 0);
+                r.gk[NWG - 1] = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gk + 4, so_g, 0);
+            } else if (KPL == 2 || GF32) {
+                r.gk[0] = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gk, so_g, 0);
+            } else {
+                r.gk[0] = __builtin_amdgcn_raw_buffer_load_b16(rgt, voff_gk, so_g, 0);
+            }
+        }
+    };
+    // a = exp(g) of this lane's key rows (a1 only for two rows per lane); tokens past the end
+    // read g = 0 (and beta = 0, so they leave the state unchanged)
+    auto key_gates = [&](const Raw& r, float& a0, float& a1) {
+        float g0, g1 = 0.0f;
+        if (GF32) {
+            g0 = __uint_as_float(r.gk[0]);
+            if (KPL == 2) g1 = __uint_as_float(r.gk[NWG - 1]);
+        } else {
+            g0 = __uint_as_float(r.gk[0] << 16);
+            if (KPL == 2) g1 = __uint_as_float(r.gk[0] & 0xFFFF0000u);
+        }
+        a0 = expf(g0);
+        a1 = KPL == 2 ? expf(g1) : 1.0f;
     };
 
     // ---------------------------------------------------------------- gate windows
@@ -116,10 +149,10 @@ __global__ __launch_bounds__(kWaveThreads) void fwd_wave_kernel(Params p, FwdArg
         const int so = (w0n * H + h) * GB;  // wave-uniform part
         const int vo = lane * H * GB;       // lane i: token w0n + i
         if (GF32) {
-            graw = __builtin_amdgcn_raw_buffer_load_b32(rgt, vo, so, 0);
+            if (!KDA) graw = __builtin_amdgcn_raw_buffer_load_b32(rgt, vo, so, 0);
             braw = __builtin_amdgcn_raw_buffer_load_b32(rbt, vo, so, 0);
         } else {
-            graw = __builtin_amdgcn_raw_buffer_load_b16(rgt, vo, so, 0);
+            if (!KDA) graw = __builtin_amdgcn_raw_buffer_load_b16(rgt, vo, so, 0);
             braw = __builtin_amdgcn_raw_buffer_load_b16(rbt, vo, so, 0);
         }
     };
@@ -223,6 +256,69 @@ __global__ __launch_bounds__(kWaveThreads) void fwd_wave_kernel(Params p, FwdArg
         }
     };
 
+    if constexpr (KDA) {
+        // S~ = diag(a) S, P = S~^T k, Q = S~^T q, delta = beta (v - P), S' = S~ + k delta^T,
+        // o = Q + delta (k . q)
+        auto token_kda = [&](const Keys& x, float a0, float a1, uint32_t vraw, float kq, float bt) {
+            const float vj = BF16 ? __uint_as_float(vraw << 16) : __uint_as_float(vraw);
+            decay_pass<R>(s, a0, a1);
+            float pk, pq, P, Q;
+            dot_pass<R>(s, x.k0, x.k1, x.q0, x.q1, pk, pq);
+            rows_sum2(pk, pq, P, Q);
+            const float delta = bt * (vj - P);
+            const float o = __builtin_fmaf(delta, kq, Q);
+            update_pass<R>(s, x.k0, x.k1, delta);
+            return o;
+        };
+#pragma unroll 1
+        for (int t = 0; t < T; t += kRing) {
+            if (t == w_next) {
+                w0 = t;
+                w_next = t + kWin;
+                open_window(w0);
+                fetch_window(w_next);
+            }
+            if (t == ck_next) {
+                float* dst = a.ckpts + (bh * p.nck + t / p.ckpt_interval) * DK * DV;
+#pragma unroll
+                for (int m = 0; m < R; m++) dst[static_cast<size_t>(rg * R + m) * DV + col] = s[m];
+                ck_next += p.ckpt_interval;
+            }
+            const int tw = t - w0;
+            float o_acc = 0.0f;
+#pragma unroll
+            for (int j0 = 0; j0 < kRing; j0 += 4) {
+                __builtin_amdgcn_sched_barrier(0);
+                Keys x[4];
+                uint32_t vr[4];
+                float ga[4], gb[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    x[i] = widen(ring[j0 + i]);
+                    vr[i] = ring[j0 + i].v;
+                    key_gates(ring[j0 + i], ga[i], gb[i]);
+                    fetch(ring[j0 + i], t + j0 + i + kRing);
+                }
+                const float kq4 = sum4_by_rows(kq_part(x[0]), kq_part(x[1]), kq_part(x[2]), kq_part(x[3]));
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float o = token_kda(x[i], ga[i], gb[i], vr[i], kq4, lane_of(beta_w, tw + j0 + i));
+                    o_acc = rg == i ? o : o_acc;
+                }
+                store_o(t + j0, o_acc);
+            }
+            if (min(t + kRing, T) - 1 == q_next) {
+                quantize();
+                q_next = q_next + qi <= T - 1 ? q_next + qi : (q_next < T - 1 ? T - 1 : T);
+            }
+        }
+        if (a.ST) {
+#pragma unroll
+            for (int m = 0; m < R; m++) a.ST[state_off + static_cast<size_t>(rg * R + m) * DV + col] = s[m];
+        }
+        return;
+    }
+
     int t = 0;
 #pragma unroll 1
     while (t < T) {
@@ -319,16 +415,22 @@ __global__ __launch_bounds__(kWaveThreads) void fwd_wave_kernel(Params p, FwdArg
 
 namespace {
 
-template <int DK, int QMODE, int G, bool BF16, bool GF32>
-hipError_t launch_wave_o(const la_config& c, const FwdArgs& a, hipStream_t s) {
+template <int DK, int QMODE, int G, bool BF16, bool GF32, bool KDA>
+hipError_t launch_wave_k(const la_config& c, const FwdArgs& a, hipStream_t s) {
     dim3 grid(c.d_v / kTileCols, c.H, c.B);
     if (c.out_dtype == LA_BF16)
-        hipLaunchKernelGGL((fwd_wave_kernel<DK, QMODE, G, BF16, GF32, true>), grid, dim3(kWaveThreads), 0, s,
+        hipLaunchKernelGGL((fwd_wave_kernel<DK, QMODE, G, BF16, GF32, true, KDA>), grid, dim3(kWaveThreads), 0, s,
                            make_params(c), a);
     else
-        hipLaunchKernelGGL((fwd_wave_kernel<DK, QMODE, G, BF16, GF32, false>), grid, dim3(kWaveThreads), 0, s,
+        hipLaunchKernelGGL((fwd_wave_kernel<DK, QMODE, G, BF16, GF32, false, KDA>), grid, dim3(kWaveThreads), 0, s,
                            make_params(c), a);
     return hipGetLastError();
+}
+
+template <int DK, int QMODE, int G, bool BF16, bool GF32>
+hipError_t launch_wave_o(const la_config& c, const FwdArgs& a, hipStream_t s) {
+    if (c.gate == LA_GATE_KEY) return launch_wave_k<DK, QMODE, G, BF16, GF32, true>(c, a, s);
+    return launch_wave_k<DK, QMODE, G, BF16, GF32, false>(c, a, s);
 }
 
 template <int DK, int QMODE, int G>
@@ -354,7 +456,15 @@ hipError_t launch_wave_dk(const la_config& c, const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 bool fwd_wave_eligible(const la_config& c) {
-    if (!fwd_fast_eligible(c)) return false;
+    if (c.gate == LA_GATE_KEY) {
+        // per-key gates: the scalar-gate kernels' rounding conditions, without the rescale
+        if (c.hadamard) return false;
+        if (c.qdq != LA_QDQ_NONE &&
+            (c.qdq_interval < 2 || (c.ckpt_interval > 0 && c.qdq_interval % c.ckpt_interval != 0)))
+            return false;
+    } else if (!fwd_fast_eligible(c)) {
+        return false;
+    }
     if (c.qdq != LA_QDQ_NONE && c.qdq_interval % kRing != 0) return false;
     if (c.ckpt_interval > 0 && c.ckpt_interval % kRing != 0) return false;
     // 32-bit buffer offsets within one sequence, ring prefetch included

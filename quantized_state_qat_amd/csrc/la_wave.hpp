@@ -87,6 +87,41 @@ __device__ __forceinline__ void dot_pass(const float* s, float k0, float k1, flo
     Q = pq0 + pq1;
 }
 
+// Single DPP multiply for the small key sizes: x = a[lane L of this lane's row of 16] * x.
+template <int L>
+__device__ __forceinline__ void mul_bcast(float& x, float a) {
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 row_newbcast:%2 row_mask:0xf bank_mask:0xf" : "+v"(x) : "v"(a), "n"(L));
+}
+
+// d_k = 128: S[row] *= a[row] with lane L holding the gates of rows 2L (a0) and 2L+1 (a1).
+// Operands: %0..%31 = the 32 state rows (in/out); %32, %33 = a0, a1.
+#define LA_DEC2(L, E, O) LA_DPP(v_mul_f32_dpp, E, 32, E, L) LA_DPP(v_mul_f32_dpp, O, 33, O, L)
+// d_k = 64: lane L holds the gate of row L.  %0..%15 = state rows; %16 = a.
+#define LA_DEC1(L) LA_DPP(v_mul_f32_dpp, L, 16, L, L)
+
+// Per-key gate (KDA): S[row] *= a[row] over this lane's R rows, the gates spread over the row
+// group's lanes like the keys.
+template <int R>
+__device__ __forceinline__ void decay_pass(float* s, float a0, float a1) {
+    if constexpr (R == 32) {
+        asm("s_nop 1\n\t"
+            LA_DEC2(0, 0, 1) LA_DEC2(1, 2, 3) LA_DEC2(2, 4, 5) LA_DEC2(3, 6, 7) LA_DEC2(4, 8, 9)
+            LA_DEC2(5, 10, 11) LA_DEC2(6, 12, 13) LA_DEC2(7, 14, 15) LA_DEC2(8, 16, 17) LA_DEC2(9, 18, 19)
+            LA_DEC2(10, 20, 21) LA_DEC2(11, 22, 23) LA_DEC2(12, 24, 25) LA_DEC2(13, 26, 27)
+            LA_DEC2(14, 28, 29) LA_DEC2(15, 30, 31)
+            : LA_S32(s) : "v"(a0), "v"(a1));
+    } else if constexpr (R == 16) {
+        asm("s_nop 1\n\t"
+            LA_DEC1(0) LA_DEC1(1) LA_DEC1(2) LA_DEC1(3) LA_DEC1(4) LA_DEC1(5) LA_DEC1(6) LA_DEC1(7)
+            LA_DEC1(8) LA_DEC1(9) LA_DEC1(10) LA_DEC1(11) LA_DEC1(12) LA_DEC1(13) LA_DEC1(14) LA_DEC1(15)
+            : LA_S16(s) : "v"(a0));
+    } else {
+        (void)a1;
+        [&]<int... M>(std::integer_sequence<int, M...>) { (mul_bcast<M>(s[M], a0), ...); }(
+            std::make_integer_sequence<int, R>{});
+    }
+}
+
 // Shat[row] += k[row] * dd over this lane's R rows.
 template <int R>
 __device__ __forceinline__ void update_pass(float* s, float k0, float k1, float dd) {

@@ -1,8 +1,8 @@
 """Every forward kernel against the float64 oracle, teacher forced per rounding interval.
 
 la_recurrent_fwd selects one of four kernels from the configuration (la_fwd_kernel_name):
-the block kernel (16-token blocks on the matrix cores), the single-wave kernel, the
-eight-wave kernel and the per-token kernel.  Each case below is chosen to land on one of them
+the block kernel (16-token blocks on the matrix cores), the single-wave kernel (scalar or
+per-key gates), the eight-wave kernel and the per-token kernel.  Each case below is chosen to land on one of them
 (asserted), runs with checkpoints at the rounding interval, and then, for every unit and every
 interval, the oracle advances the GPU's checkpoint over that interval in float64 and rounds it
 with the FP32 codec ("GDN state/W QAT foundation", "Torch GDN/KDA decode QAT + INT8": What
@@ -36,7 +36,18 @@ CASES = [
     ("wave_int8g16_dk32_i24", W("wdk32", B=2, T=60, H=1, d_k=32, d_v=64, s0_sigma=0.2, config_id=45), INT8, 16, 24, "wave"),
     ("fast_int8g16_i3", W("fi8", B=1, T=40, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=46), INT8, 16, 3, "fast"),
     ("fast_e4m3_dk16_i5", W("fe4", B=2, T=33, H=2, d_k=16, d_v=64, s0_sigma=0.2, config_id=47), E4M3, 64, 5, "fast"),
-    ("token_kda_e4m3_i16", W("tk", B=1, T=40, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=48), E4M3, 64, 16, "token"),
+    ("wave_kda_e4m3_dk64_i16", W("tk", B=1, T=40, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=48), E4M3, 64, 16, "wave"),
+    ("wave_kda_int8g32_dk128_i64", W("wk1", B=2, T=150, H=2, d_k=128, d_v=128, gate="key", s0_sigma=0.2, config_id=60),
+     INT8, 32, 64, "wave"),
+    ("wave_kda_fp32_noqdq_dk128_i8", W("wk2", B=1, T=45, H=2, d_k=128, d_v=64, gate="key", qkv_dtype="f32",
+                                        gate_dtype="f32", s0_sigma=0.2, config_id=61), NONE, 32, 8, "wave"),
+    # nine units (92K codes): the near-tie budget is a fraction, and on 20K codes a single
+    # seed's handful of fp32-against-float64 flips already exceeds it
+    ("wave_kda_int8g16_dk32_i8", W("wk3", B=3, T=37, H=3, d_k=32, d_v=64, gate="key", s0_sigma=0.2, config_id=62),
+     INT8, 16, 8, "wave"),
+    ("wave_kda_e4m3_bf16gate_dk128_i24", W("wk4", B=1, T=70, H=3, d_k=128, d_v=192, gate="key", s0_sigma=0.1,
+                                            config_id=63), E4M3, 64, 24, "wave"),
+    ("token_kda_e4m3_i12", W("tk2", B=1, T=40, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=64), E4M3, 64, 12, "token"),
 ]
 
 
@@ -110,8 +121,12 @@ STEEP = [
     ("wave_e4m3_dk64_i64", W("swe4", B=1, T=150, H=2, d_k=64, d_v=128, s0_sigma=0.2, config_id=52), E4M3, 64, 64, "wave"),
     ("wave_int8g64_i8", W("swi8", B=1, T=85, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=53), INT8, 64, 8, "wave"),
     ("fast_int8g16_i3", W("sfi8", B=1, T=80, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=54), INT8, 16, 3, "fast"),
-    ("token_kda_int8g32_i16", W("stk", B=1, T=80, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=55),
-     INT8, 32, 16, "token"),
+    ("wave_kda_int8g32_i16", W("stk", B=1, T=80, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=55),
+     INT8, 32, 16, "wave"),
+    ("wave_kda_e4m3_dk128_i64", W("swk", B=1, T=150, H=2, d_k=128, d_v=128, gate="key", gate_dtype="f32",
+                                   s0_sigma=0.2, config_id=65), E4M3, 64, 64, "wave"),
+    ("token_kda_int8g32_i12", W("stk2", B=1, T=80, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=66),
+     INT8, 32, 12, "token"),
 ]
 
 
