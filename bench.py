@@ -161,6 +161,48 @@ def bench_long_e4m3(steps=3, warmup=1):
     return fwd, fwdbwd
 
 
+def bench_kda_long(steps=3, warmup=1):
+    """KDA B=8 H=16 T=4096 d=128, bf16 q/k/v, fp32 per-key gates and beta, E4M3 tile QDQ every
+    64 tokens: the forward (single-wave kernel) and the straight-through backward."""
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    w = synth.Workload("kda_long_e4m3_64", B=8, T=4096, H=16, d_k=128, d_v=128, gate="key", gate_dtype="f32",
+                       config_id=2)
+    d = synth.generate(w, with_do=True)
+    dev = {k: _dev(d[k]) for k in ("q", "k", "v", "g", "beta", "do")}
+    del d
+    c = la.Config(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v, gate=la.LA_GATE_KEY, qdq=la.LA_QDQ_E4M3_TILE, group=64,
+                  qdq_interval=64, ckpt_interval=64, gate_dtype=la.LA_F32)
+    o = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
+    ST = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    ck = torch.empty((w.B, w.H, w.T // 64, w.d_k, w.d_v), device="cuda")
+    grads = [torch.empty((w.B, w.T, w.H, w.d_k), device="cuda") for _ in range(4)]
+    dv = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
+    dbeta = torch.empty((w.B, w.T, w.H), device="cuda")
+    dS0 = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    nbytes = la.la_bwd_workspace_bytes(c)
+    ws = torch.empty((nbytes + 255) // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    t_f = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o, ST,
+                                                  ck, stream=stream), steps, warmup, stream)
+    t_b = _time_calls(lambda: la.la_recurrent_bwd_ste(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, ck,
+                                                      dev["do"], None, grads[0], grads[1], dv, grads[2], dbeta, dS0,
+                                                      ws, nbytes, stream=stream), steps, warmup, stream)
+    unit = w.d_k * w.d_v * w.B * w.H * w.T
+    return {
+        "workload": "kda_long_e4m3_64 B=8 H=16 T=4096 d_k=d_v=128 bf16 q/k/v, fp32 per-key gates and beta, E4M3 tile "
+                    "QDQ every 64 tokens, 64-token checkpoints",
+        "kernel_fwd": la.la_fwd_kernel_name(c), "kernel_bwd": la.la_bwd_kernel_name(c),
+        "ms_fwd": t_f * 1e3, "ms_bwd": t_b * 1e3, "updates_per_s_fwd": w.B * w.H * w.T / t_f,
+        "roofline_fwd": _fp32_roofline(7.0 * unit, t_f, "forward: 7 d_k d_v flops per token-head (the per-key decay "
+                                                        "adds d_k d_v multiplies, not counted)"),
+        "roofline_bwd": _fp32_roofline(22.0 * unit, t_b, "backward: recompute 7 + adjoint 15 d_k d_v per token-head"),
+    }
+
+
 def _dev(t):
     """Device copy of a generated tensor in its storage dtype."""
     import numpy as np
@@ -441,7 +483,8 @@ def main():
     }
     if not args.no_extra:
         long_fwd, long_fwdbwd = bench_long_e4m3()
-        line["extra"] = {"long_sequence": long_fwd, "long_sequence_fwdbwd": long_fwdbwd, "kda_int8g64_tok": bench_kda_tok(),
+        line["extra"] = {"long_sequence": long_fwd, "long_sequence_fwdbwd": long_fwdbwd, "kda_long_e4m3": bench_kda_long(),
+                         "kda_int8g64_tok": bench_kda_tok(),
                          "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "decode_slots": bench_decode_slots(),
                          "varlen_prefill": bench_varlen()}
     if not args.no_cpu:
