@@ -3,7 +3,8 @@
 // point on a 16-token block end.
 //
 // Three launches.  (1) The block forward (fwd_mfma.hip) with a checkpoint every 16 tokens
-// into the workspace: the state entering every block, rounding points included.  (2) This
+// into the workspace: the state entering every block, rounding points included, written in
+// the kernels' register order (each lane's 32 values contiguous).  (2) This
 // file's block kernel walks the blocks last to first with dS = dL/dS carried in registers.
 // (3) A reduction finishes the key, query and gate gradients.  The quantizer passes the
 // gradient through unchanged, so a block's adjoint is that of the exact recurrence.
@@ -92,20 +93,17 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
-// Product over key rows: lane (g, c) register r = sum_rows key_{4g+r}[row] x[row][c], with the
-// keys of token c as loaded (kv[i] = rows state_row(8 i .. 8 i + 7, g)) and x in the state layout.
-__device__ __forceinline__ f4 project(const float (&x)[32], const u4 (&kv)[4]) {
-    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+// Slice st of a product over key rows: lane (g, c) register r += sum over rows
+// state_row(8 st .. 8 st + 7, g') of key_{4g+r}[row] x[row][c], with the keys of token c as
+// loaded (kv[st] = those rows) and x in the state layout, x in three exact bf16 parts.
+__device__ __forceinline__ f4 project_slice(f4 acc, const float (&x)[32], const u4 (&kv)[4], int st) {
+    uint32_t hh[4], ll[4], l2[4];
 #pragma unroll
-    for (int st = 0; st < 4; st++) {
-        uint32_t hh[4], ll[4], l2[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) split3_pair(x[8 * st + 2 * i], x[8 * st + 2 * i + 1], hh[i], ll[i], l2[i]);
-        const bf8 ak = __builtin_bit_cast(bf8, kv[st]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf8, u4{l2[0], l2[1], l2[2], l2[3]}), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf8, u4{ll[0], ll[1], ll[2], ll[3]}), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf8, u4{hh[0], hh[1], hh[2], hh[3]}), acc, 0, 0, 0);
-    }
+    for (int i = 0; i < 4; i++) split3_pair(x[8 * st + 2 * i], x[8 * st + 2 * i + 1], hh[i], ll[i], l2[i]);
+    const bf8 ak = __builtin_bit_cast(bf8, kv[st]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf8, u4{l2[0], l2[1], l2[2], l2[3]}), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf8, u4{ll[0], ll[1], ll[2], ll[3]}), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, __builtin_bit_cast(bf8, u4{hh[0], hh[1], hh[2], hh[3]}), acc, 0, 0, 0);
     return acc;
 }
 
@@ -139,9 +137,10 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
     const auto rdo = make_rsrc(a.dout + seq0 * DV, seq_tok * DV * 4);
     const auto rdv = make_rsrc(a.dv + seq0 * DV, seq_tok * DV * 4);
-    // this unit's block-start states (the eligibility check keeps their offsets below 2^31)
+    // this unit's block-start states, lane-major per 16-column wave slice (the recompute's
+    // order; the eligibility check keeps their offsets below 2^31)
     const auto rst = make_rsrc(a.ws_states + bh * static_cast<size_t>(nb) * DK * DV, static_cast<size_t>(nb) * DK * DV * 4);
-    const int voff_st = (state_row(0, g) * DV + col) * 4;
+    const int voff_st = ((col >> 4) * 64 + lane) * 32 * 4;  // lane-major block-start states
 
     float dS[R];
 #pragma unroll
@@ -196,11 +195,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
                 in.b = __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, so_g, 0);
             }
         } else {
-            // rows state_row(m, g) = state_row(0, g) + 32 (m / 8) + m % 8: the row step is uniform
+            // the recompute wrote the states lane-major: this lane's 32 values are 128 bytes
             const int so = blk * DK * DV * 4;
 #pragma unroll
-            for (int m = 0; m < R; m++)
-                in.s[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rst, voff_st, so + (32 * (m >> 3) + (m & 7)) * DV * 4, 0));
+            for (int i = 0; i < R / 4; i++) {
+                const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rst, voff_st + 16 * i, so, 0);
+#pragma unroll
+                for (int e = 0; e < 4; e++) in.s[4 * i + e] = __uint_as_float(x[e]);
+            }
         }
     };
 
@@ -275,6 +277,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
         const float c10 = sh.AmT[4 * g][4 * g + 1], c20 = sh.AmT[4 * g][4 * g + 2];
         const float c21 = sh.AmT[4 * g + 1][4 * g + 2], c30 = sh.AmT[4 * g][4 * g + 3];
         const float c31 = sh.AmT[4 * g + 1][4 * g + 3], c32 = sh.AmT[4 * g + 2][4 * g + 3];
+        // the projections K S_0 and K dS' (independent of the solve) go slice by slice between
+        // its stages, so that their MFMAs run while a stage waits on LDS
+        f4 P4 = {0.0f, 0.0f, 0.0f, 0.0f}, Z4 = {0.0f, 0.0f, 0.0f, 0.0f};  // (K S_0), (K dS')_{4g+r, c}
         f4 dm = {0.0f, 0.0f, 0.0f, 0.0f}, nsel = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < 4; st++) {
@@ -285,8 +290,10 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
             const float x2 = e2 - b4[2] * (dm[2] + c20 * x0 + c21 * x1);
             const float x3 = e3 - b4[3] * (dm[3] + c30 * x0 + c31 * x1 + c32 * x2);
             if (g == st) nsel = f4{x0, x1, x2, x3};
+            if (st < 3) *reinterpret_cast<f4*>(&sh.dd[g][c][0]) = f4{x0, x1, x2, x3};
+            P4 = project_slice(P4, s, kk, st);
+            Z4 = project_slice(Z4, dS, kk, st);
             if (st < 3) {
-                *reinterpret_cast<f4*>(&sh.dd[g][c][0]) = f4{x0, x1, x2, x3};
                 wave_lds_sync();
                 // A: lane (kk, j) = A_{j, 4 st + kk} for tokens j of later groups; B: N_{4 st + kk, c}
                 const float ast = c >= 4 * st + 4 ? sh.AmT[4 * st + g][c] : 0.0f;
@@ -299,9 +306,6 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
         fetch_part(nxt, bn, 1);
 
         // ------------------------------------------------------------ forward quantities
-        const f4 P4 = project(s, kk);   // (K S_0)_{4g+r, c}
-        const f4 Z4 = project(dS, kk);  // (K dS')_{4g+r, c}
-        fetch_part(nxt, bn, 2);
         f4 W4;
 #pragma unroll
         for (int r = 0; r < 4; r++) W4[r] = V4[r] - gam4[r] * P4[r];
@@ -341,6 +345,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
         const float sdot = wave_sum(sd);                           // <dS', S_0> over this wave's columns
         const float e2tot = rows_sum(e2[0] + e2[1] + e2[2] + e2[3]);  // sum over the block's tokens
 
+        fetch_part(nxt, bn, 2);
         // Delta and lambda to the T layout
 #pragma unroll
         for (int r = 0; r < 4; r++) {
@@ -610,7 +615,9 @@ size_t bwd_mfma_part_bytes(const la_config& c) {
 hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs& a, hipStream_t s) {
     la_config c16 = c;
     c16.ckpt_interval = kBlk;
-    hipError_t e = launch_fwd_mfma(c16, fa, s);
+    FwdArgs fl = fa;
+    fl.ckpt_lane_major = 1;
+    hipError_t e = launch_fwd_mfma(c16, fl, s);
     if (e != hipSuccess) return e;
     const BwParams p{c.T, c.H, c.d_v, (c.T + kBlk - 1) / kBlk};
     dim3 grid(c.d_v / 64, c.H, c.B);

@@ -172,12 +172,22 @@ __global__ __launch_bounds__(kMThreads) void fwd_mfma_kernel(Params p, FwdArgs a
 #pragma unroll 1
     for (int t0 = 0; t0 < T; t0 += kBlk) {
         if (t0 == ck_next) {
-            // rows state_row(m, g) = state_row(0, g) + 32 (m / 8) + m % 8: the row step is uniform
             const int so = t0 / p.ckpt_interval * DK * DV * 4;
+            if (a.ckpt_lane_major) {
+                // lane-major: s[0..31] of lane L of wave slice col / 16 at float (slice 64 + L) 32
+                const int vo = ((col >> 4) * 64 + lane) * R * 4;
 #pragma unroll
-            for (int m = 0; m < R; m++)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s[m]), rck, voff_ck,
-                                                      so + (32 * (m >> 3) + (m & 7)) * DV * 4, 0);
+                for (int i = 0; i < R / 4; i++)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u4{__float_as_uint(s[4 * i]), __float_as_uint(s[4 * i + 1]), __float_as_uint(s[4 * i + 2]),
+                           __float_as_uint(s[4 * i + 3])}, rck, vo + 16 * i, so, 0);
+            } else {
+                // rows state_row(m, g) = state_row(0, g) + 32 (m / 8) + m % 8: the row step is uniform
+#pragma unroll
+                for (int m = 0; m < R; m++)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s[m]), rck, voff_ck,
+                                                          so + (32 * (m >> 3) + (m & 7)) * DV * 4, 0);
+            }
             ck_next += p.ckpt_interval;
         }
 

@@ -22,6 +22,10 @@ struct FwdArgs {
     // packed sequences (token kernel only): sequence b is tokens cu_seqlens[b] .. [b + 1] of
     // a [T][H][...] layout; null = the batched [B][T][H][...] layout
     const int32_t* cu_seqlens = nullptr;
+    // block kernel only: checkpoints in the kernels' register order (lane-major: each lane's
+    // 32 state values contiguous, per 16-column wave slice) instead of [d_k][d_v]; set by the
+    // block backward for its own recompute, never seen by a caller
+    int ckpt_lane_major = 0;
 };
 
 struct DecodeArgs {
