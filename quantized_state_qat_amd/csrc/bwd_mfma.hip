@@ -61,8 +61,8 @@ struct BwParams {
     int T, H, dv, nb;
 };
 
-// Per-wave LDS.
-struct BwShared {
+// Per-wave LDS (16-byte aligned for the 16-byte accesses).
+struct alignas(16) BwShared {
     uint16_t kN[kBlk][kKeyRow];  // the block's keys, [token][row] (transposed reads of the update)
     uint16_t qN[kBlk][kKeyRow];  // and queries
     float SdS[2][kBwDK][16];     // S_0 and dS' by [row][column]
