@@ -42,8 +42,8 @@ namespace la {
 
 namespace {
 
-constexpr int kBwWaves = 4;
-constexpr int kBwThreads = kBwWaves * 64;  // 64 value columns per workgroup
+constexpr int kBwWaves = 4;                   // column waves: 64 value columns per workgroup
+constexpr int kBwThreads = (kBwWaves + 1) * 64;  // and one producer wave
 constexpr int kBwDK = 128;
 constexpr int kDppRowShr = 0x110;  // row_shr:n = kDppRowShr + n
 
@@ -61,18 +61,32 @@ struct BwParams {
     int T, H, dv, nb;
 };
 
-// Per-wave LDS (16-byte aligned for the 16-byte accesses).
+// Per column wave LDS (16-byte aligned for the 16-byte accesses).
 struct alignas(16) BwShared {
-    uint16_t kN[kBlk][kKeyRow];  // the block's keys, [token][row] (transposed reads of the update)
-    uint16_t qN[kBlk][kKeyRow];  // and queries
     float SdS[2][kBwDK][16];     // S_0 and dS' by [row][column]
     float small[5][64][4];       // small partial sums for the cross-wave reduction
-    float AmT[kBlk][20];         // [i][j] = A_ji
-    float dd[4][kBlk][4];        // solve: stage values of tokens 4 g + r, [g][column][r]
-    float Ns[kBlk][20];          // [c][j] = N_jc
     float XD[kBlk][20];          // Delta by [token][column]
     float XL[kBlk][20];          // lambda by [token][column]
-    float G[kBlk], beta[kBlk];
+    float XO[kBlk][16];          // dO by [token][column]
+};
+// One block's state-independent data, written by the producer wave one block ahead.  The
+// 16 x 16 token matrices are stored so that lane (g, c) reads its four values (rows 4 g .. 4 g + 3
+// of column c) as one 16-byte word at [c][4 g].
+struct alignas(16) BwSlot {
+    uint16_t kN[kBlk][kKeyRow];  // keys [token][row] (projection operands, transposed update reads)
+    uint16_t qN[kBlk][kKeyRow];  // queries
+    float RR[kBlk][kBlk];        // [c][j] = r_{j c} (0 for c > j)
+    float A4[kBlk][kBlk];        // [c][j] = A_{j c}
+    float C4[kBlk][kBlk];        // [c][j] = C_{j c}
+    float AT[kBlk][kBlk];        // [c][j] = A_{c j}
+    float Ns[kBlk][20];          // [c][j] = N_{j c}
+    float G[kBlk], beta[kBlk];   // G_j and beta_j (0 past the end)
+    float GAM[kBlk], RHO[kBlk];  // exp(G_j), exp(G_15 - G_j)
+};
+// The producer's own staging for the solve.
+struct alignas(16) BwProd {
+    float AmT[kBlk][20];  // [i][j] = A_ji
+    float dd[4][kBlk][4]; // stage values of tokens 4 g + r, [g][column][r]
 };
 
 // Inclusive prefix sum over each row of 16 lanes.
@@ -114,27 +128,149 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     constexpr int DK = kBwDK, R = 32;
     constexpr int GB = GF32 ? 4 : 2;
     __shared__ BwShared shw[kBwWaves];
+    __shared__ BwSlot slots[2];
+    __shared__ BwProd prod;
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
     const int h = blockIdx.y, b = blockIdx.z;
-    const int cw0 = blockIdx.x * 64 + w * 16;  // this wave's first value column
-    const int col = cw0 + c;
     const int T = p.T, H = p.H, DV = p.dv, nb = p.nb;
     const int nwg = gridDim.x;
     const size_t bh = static_cast<size_t>(b) * H + h;
     const size_t seq0 = static_cast<size_t>(b) * T * H;
     const size_t seq_tok = static_cast<size_t>(T) * H;
-    BwShared& sh = shw[w];
 
     // buffer resources over exactly this sequence's tokens (offsets < 2^31, checked on the host):
     // reads past its last token return zero, stores there are dropped
     const auto rk = make_rsrc(static_cast<const char*>(a.k) + seq0 * DK * 2, seq_tok * DK * 2);
     const auto rq = make_rsrc(static_cast<const char*>(a.q) + seq0 * DK * 2, seq_tok * DK * 2);
+
+    if (w == kBwWaves) {
+        // ------------------------------------------------------------ producer
+        // Block blk - 1 (the next in walking order) while the column waves run block blk, its
+        // loads one block further ahead (block 0 again at the end: no branch in the loop).
+        const auto rgt = make_rsrc(static_cast<const char*>(a.g) + seq0 * GB, seq_tok * GB);
+        const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
+        const int voff_kq = (c * H * DK + 8 * g) * 2;  // token c, rows 32 i + 8 g .. + 7 (load i)
+        const int voff_gate = c * H * GB;
+        struct ProdIn {
+            u4 k[4], q[4];
+            uint32_t g, b;
+        };
+        auto pfetch = [&](ProdIn& in, int blk) __attribute__((always_inline)) {
+            const int t0 = blk * kBlk;
+            const int so_kq = (t0 * H + h) * DK * 2;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                in.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so_kq, 0);
+                in.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so_kq, 0);
+            }
+            const int so_g = (t0 * H + h) * GB;
+            if (GF32) {
+                in.g = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gate, so_g, 0);
+                in.b = __builtin_amdgcn_raw_buffer_load_b32(rbt, voff_gate, so_g, 0);
+            } else {
+                in.g = __builtin_amdgcn_raw_buffer_load_b16(rgt, voff_gate, so_g, 0);
+                in.b = __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, so_g, 0);
+            }
+        };
+        auto produce = [&](const ProdIn& in, int blk, BwSlot& sl) __attribute__((always_inline)) {
+            const int t0 = blk * kBlk;
+            // gk (lane (g, c), register r) = k_{4g+r} . k_c, gqk = q_{4g+r} . k_c
+            f4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gqk = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const bf8 ak = __builtin_bit_cast(bf8, in.k[i]), aq = __builtin_bit_cast(bf8, in.q[i]);
+                gk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, ak, gk, 0, 0, 0);
+                gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, ak, gqk, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                *reinterpret_cast<u4*>(&sl.kN[c][32 * i + 8 * g]) = in.k[i];
+                *reinterpret_cast<u4*>(&sl.qN[c][32 * i + 8 * g]) = in.q[i];
+            }
+            // lane (g, c): token t0 + c; tokens past the end take gate 0 and beta 0
+            const bool valid = t0 + c < T;
+            const float gv = valid ? (GF32 ? __uint_as_float(in.g) : bf_lo(in.g)) : 0.0f;
+            const float bv = valid ? (GF32 ? __uint_as_float(in.b) : bf_lo(in.b)) : 0.0f;
+            const float Gc = row_prefix_sum(gv);  // G_c
+            const float G15 = lane_of(Gc, kBlk - 1);
+            if (g == 0) {
+                sl.G[c] = Gc;
+                sl.beta[c] = bv;
+                sl.GAM[c] = expf(Gc);
+                sl.RHO[c] = expf(G15 - Gc);
+            }
+            wave_lds_sync();
+            const f4 G4 = *reinterpret_cast<const f4*>(&sl.G[4 * g]);
+            const f4 b4 = *reinterpret_cast<const f4*>(&sl.beta[4 * g]);
+            f4 Rr, a4, c4, aT4;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int j = 4 * g + r;
+                Rr[r] = c <= j ? expf(c <= j ? G4[r] - Gc : 0.0f) : 0.0f;     // r_{j c}
+                const float rt = j < c ? expf(j < c ? Gc - G4[r] : 0.0f) : 0.0f;  // r_{c j}
+                a4[r] = c < j ? Rr[r] * gk[r] : 0.0f;   // A_{j c}
+                c4[r] = Rr[r] * gqk[r];                 // C_{j c}
+                aT4[r] = rt * gk[r];                    // A_{c j}
+            }
+            *reinterpret_cast<f4*>(&sl.RR[c][4 * g]) = Rr;
+            *reinterpret_cast<f4*>(&sl.A4[c][4 * g]) = a4;
+            *reinterpret_cast<f4*>(&sl.C4[c][4 * g]) = c4;
+            *reinterpret_cast<f4*>(&sl.AT[c][4 * g]) = aT4;
+            // N = (I + diag(beta) A)^-1: lane (g, c) solves column c for tokens 4 g .. 4 g + 3 in
+            // four stages; after stage st, lane group st's values are final and one MFMA adds
+            // their contribution to later tokens
+            *reinterpret_cast<f4*>(&prod.AmT[c][4 * g]) = a4;  // AmT[i][j] = A_ji
+            wave_lds_sync();
+            const float c10 = prod.AmT[4 * g][4 * g + 1], c20 = prod.AmT[4 * g][4 * g + 2];
+            const float c21 = prod.AmT[4 * g + 1][4 * g + 2], c30 = prod.AmT[4 * g][4 * g + 3];
+            const float c31 = prod.AmT[4 * g + 1][4 * g + 3], c32 = prod.AmT[4 * g + 2][4 * g + 3];
+            f4 dm = {0.0f, 0.0f, 0.0f, 0.0f}, nsel = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; st++) {
+                const float e0 = 4 * g == c ? 1.0f : 0.0f, e1 = 4 * g + 1 == c ? 1.0f : 0.0f;
+                const float e2 = 4 * g + 2 == c ? 1.0f : 0.0f, e3 = 4 * g + 3 == c ? 1.0f : 0.0f;
+                const float x0 = e0 - b4[0] * dm[0];
+                const float x1 = e1 - b4[1] * (dm[1] + c10 * x0);
+                const float x2 = e2 - b4[2] * (dm[2] + c20 * x0 + c21 * x1);
+                const float x3 = e3 - b4[3] * (dm[3] + c30 * x0 + c31 * x1 + c32 * x2);
+                if (g == st) nsel = f4{x0, x1, x2, x3};
+                if (st < 3) {
+                    *reinterpret_cast<f4*>(&prod.dd[g][c][0]) = f4{x0, x1, x2, x3};
+                    wave_lds_sync();
+                    // A: lane (kk, j) = A_{j, 4 st + kk} for tokens j of later groups; B: N_{4 st + kk, c}
+                    const float ast = c >= 4 * st + 4 ? prod.AmT[4 * st + g][c] : 0.0f;
+                    dm = mfma4(ast, prod.dd[st][c][g], dm);
+                    wave_lds_sync();
+                }
+            }
+            *reinterpret_cast<f4*>(&sl.Ns[c][4 * g]) = nsel;  // Ns[c][j] = N_jc
+        };
+
+        ProdIn cur, nxt;
+        pfetch(cur, nb - 1);
+        pfetch(nxt, nb > 1 ? nb - 2 : 0);
+        produce(cur, nb - 1, slots[(nb - 1) & 1]);
+        cur = nxt;
+        __syncthreads();  // the last block's slot is ready
+#pragma unroll 1
+        for (int blk = nb - 1; blk >= 0; blk--) {
+            pfetch(nxt, blk > 1 ? blk - 2 : 0);
+            if (blk > 0) produce(cur, blk - 1, slots[(blk - 1) & 1]);
+            __syncthreads();  // the column waves' first barrier of the block
+            __syncthreads();  // and their second: the slots change hands
+            cur = nxt;
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------------- column waves
+    const int cw0 = blockIdx.x * 64 + w * 16;  // this wave's first value column
+    const int col = cw0 + c;
+    BwShared& sh = shw[w];
     const auto rv = make_rsrc(static_cast<const char*>(a.v) + seq0 * DV * 2, seq_tok * DV * 2);
-    const auto rgt = make_rsrc(static_cast<const char*>(a.g) + seq0 * GB, seq_tok * GB);
-    const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
     const auto rdo = make_rsrc(a.dout + seq0 * DV, seq_tok * DV * 4);
     const auto rdv = make_rsrc(a.dv + seq0 * DV, seq_tok * DV * 4);
     // this unit's block-start states, lane-major per 16-column wave slice (the recompute's
@@ -147,53 +283,28 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     for (int m = 0; m < R; m++)
         dS[m] = a.dST ? a.dST[bh * DK * DV + static_cast<size_t>(state_row(m, g)) * DV + col] : 0.0f;
 
-    const int voff_kq = (c * H * DK + 8 * g) * 2;  // token c, rows 32 i + 8 g .. + 7 (load i)
     const int voff_v = (4 * g * H * DV + col) * 2;  // token 4 g + r (soffset), column col
     const int voff_do = (4 * g * H * DV + col) * 4;
-    // token c, columns 64 x + 16 ww + 4 g .. + 3 for the four waves ww of the workgroup
-    const int voff_doT = (c * H * DV + blockIdx.x * 64 + 4 * g) * 4;
-    const int voff_gate = c * H * GB;
+    const int voff_doT = (c * H * DV + cw0 + 4 * g) * 4;  // token c, columns cw0 + 4 g .. + 3
 
-    // A block's inputs (lane (g, c)): keys and queries of token t0 + c at rows
-    // state_row(8 i .. 8 i + 7, g) (load i); values and dO of tokens t0 + 4 g + r at column col;
-    // dO of token t0 + c at columns cw0 + 4 g .. + 3; gate and beta of token t0 + c; the state
-    // entering the block in the state layout.  The next block (in walking order) is fetched
-    // while this one is processed.
+    // A block's own inputs (lane (g, c)): values and dO of tokens t0 + 4 g + r at column col;
+    // dO of token t0 + c at columns cw0 + 4 g .. + 3; the state entering the block in the
+    // state layout.  The next block (in walking order) is fetched while this one is processed,
+    // in two parts.
     struct BlockIn {
-        u4 k[4], q[4];
         uint32_t v[4];
-        f4 dO, dOT[kBwWaves];
-        uint32_t g, b;
+        f4 dO, dOT;
         float s[R];
     };
-    // the loads of a block in three parts (keys and queries; values, dO, gate and beta; the
-    // state), spread over the previous block's steps so that no burst fills the address queue
     auto fetch_part = [&](BlockIn& in, int blk, int part) __attribute__((always_inline)) {
         const int t0 = blk * kBlk;
         if (part == 0) {
-            const int so_kq = (t0 * H + h) * DK * 2;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                in.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so_kq, 0);
-                in.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so_kq, 0);
-            }
-        } else if (part == 1) {
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 in.v[r] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff_v, ((t0 + r) * H + h) * DV * 2, 0);
                 in.dO[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdo, voff_do, ((t0 + r) * H + h) * DV * 4, 0));
             }
-#pragma unroll
-            for (int ww = 0; ww < kBwWaves; ww++)
-                in.dOT[ww] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rdo, voff_doT + 64 * ww, (t0 * H + h) * DV * 4, 0));
-            const int so_g = (t0 * H + h) * GB;
-            if (GF32) {
-                in.g = __builtin_amdgcn_raw_buffer_load_b32(rgt, voff_gate, so_g, 0);
-                in.b = __builtin_amdgcn_raw_buffer_load_b32(rbt, voff_gate, so_g, 0);
-            } else {
-                in.g = __builtin_amdgcn_raw_buffer_load_b16(rgt, voff_gate, so_g, 0);
-                in.b = __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, so_g, 0);
-            }
+            in.dOT = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rdo, voff_doT, (t0 * H + h) * DV * 4, 0));
         } else {
             // the recompute wrote the states lane-major: this lane's 32 values are 128 bytes
             const int so = blk * DK * DV * 4;
@@ -209,110 +320,52 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     BlockIn cur, nxt;
     fetch_part(cur, nb - 1, 0);
     fetch_part(cur, nb - 1, 1);
-    fetch_part(cur, nb - 1, 2);
+    __syncthreads();  // the last block's slot is ready
 #pragma unroll 1
     for (int blk = nb - 1; blk >= 0; blk--) {
         const int t0 = blk * kBlk;
         // the block walked next (block 0 again after the last: no branch, so the compiler's
         // waits for this block's loads do not also wait for the next block's)
         const int bn = blk > 0 ? blk - 1 : 0;
-        const u4(&kk)[4] = cur.k;
-        const u4(&qq)[4] = cur.q;
+        const BwSlot& sl = slots[blk & 1];
         const float(&s)[R] = cur.s;
         const f4 dO4 = cur.dO;
-        const f4 dOT = w == 0 ? cur.dOT[0] : w == 1 ? cur.dOT[1] : w == 2 ? cur.dOT[2] : cur.dOT[3];  // this wave's columns
-        const uint32_t gw = cur.g, bw = cur.b;
+        const f4 dOT = cur.dOT;
         float V4[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) V4[r] = bf_lo(cur.v[r]);
-
-        // ------------------------------------------------------------ Gram matrices, gates
-        // gk (lane (g, c), register r) = k_{4g+r} . k_c, gqk = q_{4g+r} . k_c
-        f4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gqk = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const bf8 ak = __builtin_bit_cast(bf8, kk[i]), aq = __builtin_bit_cast(bf8, qq[i]);
-            gk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, ak, gk, 0, 0, 0);
-            gqk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, ak, gqk, 0, 0, 0);
-        }
         fetch_part(nxt, bn, 0);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            *reinterpret_cast<u4*>(&sh.kN[c][32 * i + 8 * g]) = kk[i];
-            *reinterpret_cast<u4*>(&sh.qN[c][32 * i + 8 * g]) = qq[i];
-        }
-        // lane (g, c): token t0 + c; tokens past the end take gate 0 and beta 0
-        const bool valid = t0 + c < T;
-        const float gv = valid ? (GF32 ? __uint_as_float(gw) : bf_lo(gw)) : 0.0f;
-        const float bv = valid ? (GF32 ? __uint_as_float(bw) : bf_lo(bw)) : 0.0f;
-        const float Gc = row_prefix_sum(gv);  // G_c
-        const float G15 = lane_of(Gc, kBlk - 1);
-        if (g == 0) {
-            sh.G[c] = Gc;
-            sh.beta[c] = bv;
-        }
-        wave_lds_sync();
-        const f4 G4 = *reinterpret_cast<const f4*>(&sh.G[4 * g]);
-        const f4 b4 = *reinterpret_cast<const f4*>(&sh.beta[4 * g]);
-        const float gam15 = expf(G15);
-        const float gam_c = expf(Gc), rho_c = expf(G15 - Gc);
-        f4 gam4, rho4, Rr, a4, c4, aT4;
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int j = 4 * g + r;
-            gam4[r] = expf(G4[r]);
-            rho4[r] = expf(G15 - G4[r]);
-            Rr[r] = c <= j ? expf(c <= j ? G4[r] - Gc : 0.0f) : 0.0f;     // r_{j c}
-            const float rt = j < c ? expf(j < c ? Gc - G4[r] : 0.0f) : 0.0f;  // r_{c j}
-            a4[r] = c < j ? Rr[r] * gk[r] : 0.0f;   // A_{j c}
-            c4[r] = Rr[r] * gqk[r];                 // C_{j c}
-            aT4[r] = rt * gk[r];                    // A_{c j}
-        }
 
-        // ------------------------------------------------------------ N = (I + diag(beta) A)^-1
-        // Lane (g, c) solves column c for tokens 4 g .. 4 g + 3 in four stages; after stage st,
-        // lane group st's values are final and one MFMA adds their contribution to later tokens.
-        *reinterpret_cast<f4*>(&sh.AmT[c][4 * g]) = a4;  // AmT[i][j] = A_ji
-        wave_lds_sync();
-        const float c10 = sh.AmT[4 * g][4 * g + 1], c20 = sh.AmT[4 * g][4 * g + 2];
-        const float c21 = sh.AmT[4 * g + 1][4 * g + 2], c30 = sh.AmT[4 * g][4 * g + 3];
-        const float c31 = sh.AmT[4 * g + 1][4 * g + 3], c32 = sh.AmT[4 * g + 2][4 * g + 3];
-        // the projections K S_0 and K dS' (independent of the solve) go slice by slice between
-        // its stages, so that their MFMAs run while a stage waits on LDS
-        f4 P4 = {0.0f, 0.0f, 0.0f, 0.0f}, Z4 = {0.0f, 0.0f, 0.0f, 0.0f};  // (K S_0), (K dS')_{4g+r, c}
-        f4 dm = {0.0f, 0.0f, 0.0f, 0.0f}, nsel = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int st = 0; st < 4; st++) {
-            const float e0 = 4 * g == c ? 1.0f : 0.0f, e1 = 4 * g + 1 == c ? 1.0f : 0.0f;
-            const float e2 = 4 * g + 2 == c ? 1.0f : 0.0f, e3 = 4 * g + 3 == c ? 1.0f : 0.0f;
-            const float x0 = e0 - b4[0] * dm[0];
-            const float x1 = e1 - b4[1] * (dm[1] + c10 * x0);
-            const float x2 = e2 - b4[2] * (dm[2] + c20 * x0 + c21 * x1);
-            const float x3 = e3 - b4[3] * (dm[3] + c30 * x0 + c31 * x1 + c32 * x2);
-            if (g == st) nsel = f4{x0, x1, x2, x3};
-            if (st < 3) *reinterpret_cast<f4*>(&sh.dd[g][c][0]) = f4{x0, x1, x2, x3};
-            P4 = project_slice(P4, s, kk, st);
-            Z4 = project_slice(Z4, dS, kk, st);
-            if (st < 3) {
-                wave_lds_sync();
-                // A: lane (kk, j) = A_{j, 4 st + kk} for tokens j of later groups; B: N_{4 st + kk, c}
-                const float ast = c >= 4 * st + 4 ? sh.AmT[4 * st + g][c] : 0.0f;
-                dm = mfma4(ast, sh.dd[st][c][g], dm);
-                wave_lds_sync();
-            }
-        }
-        *reinterpret_cast<f4*>(&sh.Ns[c][4 * g]) = nsel;  // Ns[c][j] = N_jc
-        wave_lds_sync();
-        fetch_part(nxt, bn, 1);
+        // ------------------------------------------------------------ the block's slot
+        const f4 b4 = *reinterpret_cast<const f4*>(&sl.beta[4 * g]);
+        const f4 gam4 = *reinterpret_cast<const f4*>(&sl.GAM[4 * g]);
+        const f4 rho4 = *reinterpret_cast<const f4*>(&sl.RHO[4 * g]);
+        const float gam15 = sl.GAM[kBlk - 1];
+        const float gam_c = sl.GAM[c], rho_c = sl.RHO[c], bv = sl.beta[c];
+        const f4 Rr = *reinterpret_cast<const f4*>(&sl.RR[c][4 * g]);
+        const f4 a4 = *reinterpret_cast<const f4*>(&sl.A4[c][4 * g]);
+        const f4 c4 = *reinterpret_cast<const f4*>(&sl.C4[c][4 * g]);
+        const f4 aT4 = *reinterpret_cast<const f4*>(&sl.AT[c][4 * g]);
+        const f4 nsel = *reinterpret_cast<const f4*>(&sl.Ns[c][4 * g]);  // N_{4g+r, c}
 
         // ------------------------------------------------------------ forward quantities
+        // P = K S_0, Z = K dS' (lane (g, c), register r: token 4 g + r, column c), the keys of
+        // token c from the slot (the rows of slice st), the state and dS' in three bf16 parts
+        f4 P4 = {0.0f, 0.0f, 0.0f, 0.0f}, Z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+            u4 kv[4];
+            kv[st] = *reinterpret_cast<const u4*>(&sl.kN[c][32 * st + 8 * g]);
+            P4 = project_slice(P4, s, kv, st);
+            Z4 = project_slice(Z4, dS, kv, st);
+        }
         f4 W4;
 #pragma unroll
         for (int r = 0; r < 4; r++) W4[r] = V4[r] - gam4[r] * P4[r];
         // Delta = N diag(beta) W: slice s pairs token 4 g + s; A = N_{c, 4g+s}, B = beta W
         f4 D4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int sl = 0; sl < 4; sl++) D4 = mfma4(sh.Ns[4 * g + sl][c], b4[sl] * W4[sl], D4);
+        for (int sl_ = 0; sl_ < 4; sl_++) D4 = mfma4(sl.Ns[4 * g + sl_][c], b4[sl_] * W4[sl_], D4);
 
         // ------------------------------------------------------------ adjoint of the block
         f4 dD4;
@@ -345,13 +398,13 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
         const float sdot = wave_sum(sd);                           // <dS', S_0> over this wave's columns
         const float e2tot = rows_sum(e2[0] + e2[1] + e2[2] + e2[3]);  // sum over the block's tokens
 
-        fetch_part(nxt, bn, 2);
         // Delta and lambda to the T layout
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             sh.XD[4 * g + r][c] = D4[r];
             sh.XL[4 * g + r][c] = L4[r];
         }
+        *reinterpret_cast<f4*>(&sh.XO[c][4 * g]) = dOT;  // for the other waves' key/query sums
         wave_lds_sync();
         const f4 DT = *reinterpret_cast<const f4*>(&sh.XD[c][4 * g]);
         const f4 LT = *reinterpret_cast<const f4*>(&sh.XL[c][4 * g]);
@@ -404,8 +457,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
             split3<4>(x3, h3, l3, m3);
 #pragma unroll
             for (int tau = 0; tau < 8; tau++) {
-                const s4 kr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(&sh.kN[0][0] + tr_offset(g, c, tau)));
-                const s4 qr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(&sh.qN[0][0] + tr_offset(g, c, tau)));
+                const s4 kr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(&sl.kN[0][0] + tr_offset(g, c, tau)));
+                const s4 qr = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(&sl.qN[0][0] + tr_offset(g, c, tau)));
                 f4 st = {gam15 * dS[4 * tau], gam15 * dS[4 * tau + 1], gam15 * dS[4 * tau + 2], gam15 * dS[4 * tau + 3]};
                 st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr, __builtin_bit_cast(s4, m1), st, 0, 0, 0);
                 st = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qr, __builtin_bit_cast(s4, m3), st, 0, 0, 0);
@@ -417,6 +470,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
                 for (int r = 0; r < 4; r++) dS[4 * tau + r] = st[r];
             }
         }
+        // the next block's state: this block's is in LDS now, so the two are never both live
+        fetch_part(nxt, bn, 1);
         __syncthreads();
 
         // ------------------------------------------------------------ key/query sums
@@ -424,40 +479,29 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
         // 1 of 16 rows): dk_S[i][row] = sum_col X1[i][col] S_0[row][col] + X2[i][col] dS'[row][col],
         // dq_S with X3; X1 = gamma dU = -gamma beta lambda, X2 = rho Delta, X3 = gamma dO, all
         // row-scaled per token i (lane (g, c): token c).  Source wave ww, slice s pairs column
-        // 16 ww + 4 g + s: A from its lambda / Delta rows (XL, XD) or the dO load, B from its
-        // S_0 / dS' rows.  The sums are over the workgroup's columns: no cross-wave step.
+        // 16 ww + 4 g + s: A from its lambda / Delta / dO rows (XL, XD, XO), B from its S_0 /
+        // dS' rows.  The sums are over the workgroup's columns: no cross-wave step.
         {
             const float k1 = -gam_c * bv;
             f4 ak[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
             f4 aq[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-            // operands of source wave ww: lambda and Delta rows of token c, then S_0 and dS' at
-            // rows 32 w + 16 u + c; the next wave's are read while this one's MFMAs run
-            struct TileOps {
-                f4 l, d, S[2], dS[2];
-            };
-            auto read_ops = [&](TileOps& t, int ww) __attribute__((always_inline)) {
-                t.l = *reinterpret_cast<const f4*>(&shw[ww].XL[c][4 * g]);
-                t.d = *reinterpret_cast<const f4*>(&shw[ww].XD[c][4 * g]);
-#pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    t.S[u] = *reinterpret_cast<const f4*>(&shw[ww].SdS[0][32 * w + 16 * u + c][4 * g]);
-                    t.dS[u] = *reinterpret_cast<const f4*>(&shw[ww].SdS[1][32 * w + 16 * u + c][4 * g]);
-                }
-            };
-            TileOps ops[2];
-            read_ops(ops[0], 0);
+            // operands of source wave ww: lambda, Delta and dO rows of token c, then S_0 and dS'
+            // at rows 32 w + 16 u + c
 #pragma unroll
             for (int ww = 0; ww < kBwWaves; ww++) {
-                if (ww + 1 < kBwWaves) read_ops(ops[(ww + 1) & 1], ww + 1);
-                const TileOps& t = ops[ww & 1];
-                const f4 x1 = k1 * t.l, x2 = rho_c * t.d, x3 = gam_c * cur.dOT[ww];
+                const f4 x1 = k1 * *reinterpret_cast<const f4*>(&shw[ww].XL[c][4 * g]);
+                const f4 x2 = rho_c * *reinterpret_cast<const f4*>(&shw[ww].XD[c][4 * g]);
+                const f4 x3 = gam_c * *reinterpret_cast<const f4*>(&shw[ww].XO[c][4 * g]);
 #pragma unroll
-                for (int sl = 0; sl < 4; sl++) {
+                for (int u = 0; u < 2; u++) {
+                    const int row = 32 * w + 16 * u + c;
+                    const f4 Sf = *reinterpret_cast<const f4*>(&shw[ww].SdS[0][row][4 * g]);
+                    const f4 dSf = *reinterpret_cast<const f4*>(&shw[ww].SdS[1][row][4 * g]);
 #pragma unroll
-                    for (int u = 0; u < 2; u++) {
-                        ak[u] = mfma4(x1[sl], t.S[u][sl], ak[u]);
-                        aq[u] = mfma4(x3[sl], t.S[u][sl], aq[u]);
-                        ak[u] = mfma4(x2[sl], t.dS[u][sl], ak[u]);
+                    for (int sl_ = 0; sl_ < 4; sl_++) {
+                        ak[u] = mfma4(x1[sl_], Sf[sl_], ak[u]);
+                        aq[u] = mfma4(x3[sl_], Sf[sl_], aq[u]);
+                        ak[u] = mfma4(x2[sl_], dSf[sl_], ak[u]);
                     }
                 }
             }
