@@ -173,8 +173,9 @@ size_t la_bwd_workspace_bytes(const la_config* cfg);
 
 /*
  * Which forward kernel la_recurrent_fwd runs for cfg (diagnostic; no GPU work, no state):
- *   "block"  GDN, d_k = 128, bf16 q/k/v, rounding at most every 16 tokens (interval and
- *            checkpoint spacing multiples of 16): 16-token blocks on the matrix cores;
+ *   "block"  GDN or KDA, no Hadamard, d_k = 128, bf16 q/k/v, rounding at most every 16 tokens
+ *            (interval and checkpoint spacing multiples of 16; KDA: no rounding point strictly
+ *            inside a checkpoint chunk): 16-token blocks on the matrix cores;
  *   "wave"   GDN or KDA, no Hadamard, interval and checkpoint spacing multiples of 8 (and
  *            no rounding point strictly inside a checkpoint chunk): one wave per 16 value
  *            columns, no barrier per token;
@@ -189,7 +190,7 @@ const char* la_fwd_kernel_name(const la_config* cfg);
 
 /*
  * Which backward la_recurrent_bwd_ste runs for cfg (diagnostic; no GPU work, no state):
- *   "block"  the configurations of the "block" forward with d_v a multiple of 64: the state
+ *   "block"  the GDN configurations of the "block" forward: the state
  *            entering every 16-token block is recomputed into the workspace, then the blocks
  *            are walked last to first on the matrix cores (the block form of the adjoint);
  *   "token"  every other valid configuration: chunks of ckpt_interval tokens recomputed from

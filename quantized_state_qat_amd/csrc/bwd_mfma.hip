@@ -639,7 +639,7 @@ __global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArg
 }
 
 bool bwd_mfma_eligible(const la_config& c) {
-    if (c.d_v % 64 != 0) return false;
+    if (c.gate != LA_GATE_SCALAR || c.d_v % 64 != 0) return false;
     la_config c16 = c;
     c16.ckpt_interval = kBlk;
     if (!fwd_mfma_eligible(c16)) return false;

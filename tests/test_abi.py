@@ -160,7 +160,8 @@ def test_bwd_workspace_and_checks():
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=12, ckpt_interval=0), "fast"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=1, ckpt_interval=0), "token"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=64, hadamard=1), "token"),
-    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, gate=la.LA_GATE_KEY), "wave"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, gate=la.LA_GATE_KEY), "block"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=24, ckpt_interval=24, gate=la.LA_GATE_KEY), "wave"),
     (dict(qdq=la.LA_QDQ_NONE, ckpt_interval=8, gate=la.LA_GATE_KEY, qkv_dtype=la.LA_F32), "wave"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=64, qdq_interval=1, ckpt_interval=64, gate=la.LA_GATE_KEY), "token"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=64, qdq_interval=12, ckpt_interval=12, gate=la.LA_GATE_KEY), "token"),

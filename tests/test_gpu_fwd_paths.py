@@ -1,8 +1,8 @@
 """Every forward kernel against the float64 oracle, teacher forced per rounding interval.
 
 la_recurrent_fwd selects one of four kernels from the configuration (la_fwd_kernel_name):
-the block kernel (16-token blocks on the matrix cores), the single-wave kernel (scalar or
-per-key gates), the eight-wave kernel and the per-token kernel.  Each case below is chosen to land on one of them
+the block kernel (16-token blocks on the matrix cores, scalar or per-key gates), the
+single-wave kernel (scalar or per-key gates), the eight-wave kernel and the per-token kernel.  Each case below is chosen to land on one of them
 (asserted), runs with checkpoints at the rounding interval, and then, for every unit and every
 interval, the oracle advances the GPU's checkpoint over that interval in float64 and rounds it
 with the FP32 codec ("GDN state/W QAT foundation", "Torch GDN/KDA decode QAT + INT8": What
@@ -37,8 +37,12 @@ CASES = [
     ("fast_int8g16_i3", W("fi8", B=1, T=40, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=46), INT8, 16, 3, "fast"),
     ("fast_e4m3_dk16_i5", W("fe4", B=2, T=33, H=2, d_k=16, d_v=64, s0_sigma=0.2, config_id=47), E4M3, 64, 5, "fast"),
     ("wave_kda_e4m3_dk64_i16", W("tk", B=1, T=40, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=48), E4M3, 64, 16, "wave"),
-    ("wave_kda_int8g32_dk128_i64", W("wk1", B=2, T=150, H=2, d_k=128, d_v=128, gate="key", s0_sigma=0.2, config_id=60),
-     INT8, 32, 64, "wave"),
+    ("block_kda_int8g32_i64", W("wk1", B=2, T=150, H=2, d_k=128, d_v=128, gate="key", s0_sigma=0.2, config_id=60),
+     INT8, 32, 64, "block"),
+    ("block_kda_e4m3_i16_dv192", W("bk2", B=1, T=77, H=2, d_k=128, d_v=192, gate="key", s0_sigma=0.2, config_id=67),
+     E4M3, 64, 16, "block"),
+    ("block_kda_noqdq_f32gate_i16", W("bk3", B=2, T=40, H=1, d_k=128, d_v=64, gate="key", gate_dtype="f32",
+                                       s0_sigma=0.2, config_id=68), NONE, 32, 16, "block"),
     ("wave_kda_fp32_noqdq_dk128_i8", W("wk2", B=1, T=45, H=2, d_k=128, d_v=64, gate="key", qkv_dtype="f32",
                                         gate_dtype="f32", s0_sigma=0.2, config_id=61), NONE, 32, 8, "wave"),
     # nine units (92K codes): the near-tie budget is a fraction, and on 20K codes a single
@@ -123,8 +127,8 @@ STEEP = [
     ("fast_int8g16_i3", W("sfi8", B=1, T=80, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=54), INT8, 16, 3, "fast"),
     ("wave_kda_int8g32_i16", W("stk", B=1, T=80, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=55),
      INT8, 32, 16, "wave"),
-    ("wave_kda_e4m3_dk128_i64", W("swk", B=1, T=150, H=2, d_k=128, d_v=128, gate="key", gate_dtype="f32",
-                                   s0_sigma=0.2, config_id=65), E4M3, 64, 64, "wave"),
+    ("block_kda_e4m3_i64", W("swk", B=1, T=150, H=2, d_k=128, d_v=128, gate="key", gate_dtype="f32",
+                              s0_sigma=0.2, config_id=65), E4M3, 64, 64, "block"),
     ("token_kda_int8g32_i12", W("stk2", B=1, T=80, H=2, d_k=64, d_v=64, gate="key", s0_sigma=0.2, config_id=66),
      INT8, 32, 12, "token"),
 ]
