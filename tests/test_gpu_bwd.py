@@ -57,6 +57,10 @@ CASES = [
      la.LA_QDQ_INT8_GROUP, 32, 2, 1, 32, True),
     ("kda_int8g64_tok", synth.Workload("k", B=2, T=100, H=2, d_k=128, d_v=128, gate="key", config_id=32),
      la.LA_QDQ_INT8_GROUP, 64, 0, 1, 64, False),
+    # checkpoints from the KDA block forward, recomputed by the token backward
+    ("kda_e4m3_64_block_ckpts", synth.Workload("kb", B=1, T=150, H=2, d_k=128, d_v=128, gate="key", gate_dtype="f32",
+                                               s0_sigma=0.1, config_id=40),
+     la.LA_QDQ_E4M3_TILE, 64, 0, 64, 64, True),
     ("gdn_e4m3_64", synth.Workload("e", B=2, T=150, H=2, d_k=128, d_v=128, gate_dtype="f32", config_id=33),
      la.LA_QDQ_E4M3_TILE, 64, 0, 64, 64, True),
     ("gdn_fp32_noqdq_dk64", synth.Workload("n", B=1, T=50, H=3, d_k=64, d_v=64, qkv_dtype="f32",
