@@ -407,9 +407,12 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kernel(Params p, FwdArgs 
 // (Delta holds the tokens' true deltas; every entry of A and C and every Kt factor is a decay
 // the recurrence itself applies between two tokens).  None of the scaled operands is a bf16
 // value, so each product takes the six significant pairs of the two three-part splits.  The
-// producer forms the scaled operands, their parts, both Gram products and M; the consumers run
-// the projections, Delta, the outputs and the update.  Blocks whose gate sums leave
-// [-60, 60] run token by token with the gates applied to the state.
+// exponentials and splits are most of a block's vector work, so two producer waves share them,
+// each taking half of the key rows: it forms the scaled operands of its rows, their parts and
+// its partial Gram products.  Each consumer adds the partial Grams (in a fixed order), solves
+// M itself (no barrier between the producers is needed) and runs the projections, Delta, the
+// outputs and the update.  Blocks whose gate sums leave [-60, 60] run token by token with the
+// gates applied to the state.
 namespace {
 
 constexpr float kKdaGLim = 60.0f;
@@ -418,12 +421,19 @@ struct alignas(16) KdaSlot {
     uint16_t Kb[3][kBlk][kKeyRow];  // the three bf16 parts of Kb, [token][row]
     uint16_t Qb[3][kBlk][kKeyRow];  // of Qb
     uint16_t Kt[3][kBlk][kKeyRow];  // of Kt (transposed reads of the update)
-    float Ms[kBlk][20];             // [c][j] = M[j][c]
-    float GQ[kBlk][kBlk];           // [c][4 g + r] = Kh_{4g+r} . Qb_c
+    float GK[2][kBlk][kBlk];        // per producer (its 64 key rows): [c][4 g + r] = Kb_{4g+r} . Kh_c
+    float GQ[2][kBlk][kBlk];        // [c][4 g + r] = Kh_{4g+r} . Qb_c
     float eG15[128];                // exp(G_15) per key row
     float beta[kBlk];
-    int in_range;
+    int ok[2];                      // per producer: its gate sums stay in range
 };
+// A column wave's staging for its solve of M.
+struct alignas(16) KdaSolve {
+    float AmT[kBlk][20];   // [i][j] = A_ji
+    float dd[4][kBlk][4];  // stage values of tokens 4 g + r, [g][column][r]
+    float Ms[kBlk][20];    // [c][j] = M[j][c]
+};
+constexpr int kKdaThreads = (kWaveTileWaves + 2) * 64;  // four column waves + two producers
 
 // e^x for |x| <= 60 (the block's gate-sum range): e^x = 2^(x log2 e), with x log2 e carried as
 // an fp32 sum hi + lo (the product's rounding error recovered by one FMA, plus the low part of
@@ -459,7 +469,7 @@ __device__ __forceinline__ f4 mfma6_32(const bf8 (&a)[3], const bf8 (&b)[3], f4 
 }  // namespace
 
 template <int QMODE, int G, bool GF32, bool OBF16>
-__global__ __launch_bounds__(kPcThreads) void fwd_mfma_kda_kernel(Params p, FwdArgs a) {
+__global__ __launch_bounds__(kKdaThreads) void fwd_mfma_kda_kernel(Params p, FwdArgs a) {
     constexpr int DK = 128, R = 32;
     constexpr int GB = GF32 ? 4 : 2, OB = OBF16 ? 2 : 4;
     constexpr int kQBar = (QMODE == LA_QDQ_E4M3_TILE || (QMODE == LA_QDQ_INT8_GROUP && G > kWaveCols)) ? 1 : 0;
@@ -467,7 +477,7 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kda_kernel(Params p, FwdA
 
     __shared__ WaveQdqShared<DK, QMODE, G> qsh;
     __shared__ KdaSlot slots[2];
-    __shared__ PcProd prod;
+    __shared__ KdaSolve solve[kWaveTileWaves];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -487,29 +497,32 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kda_kernel(Params p, FwdA
     // this lane's gate words of one token: rows 32 i + 8 g .. + 7 of slice i (GF32: two words)
     auto gate_word_off = [&](int i, int half) { return (32 * i + 8 * g) * GB + 16 * half; };
 
-    if (w == kWaveTileWaves) {
-        // ------------------------------------------------------------ producer
+    if (w >= kWaveTileWaves) {
+        // ------------------------------------------------------------ producers
+        // producer pw takes key rows 64 pw .. 64 pw + 63 (slices 2 pw and 2 pw + 1); producer 0
+        // also reads beta
+        const int pw = w - kWaveTileWaves;
         const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
-        const int voff_kq = (c * H * DK + 8 * g) * 2;
+        const int voff_kq = (c * H * DK + 64 * pw + 8 * g) * 2;
         const int voff_g = c * H * DK * GB;
         const int voff_gate = c * H * GB;
         struct ProdIn {
-            u4 k[4], q[4], gw[NGW];
+            u4 k[2], q[2], gw[NGW / 2];
             uint32_t b;
         };
         auto pfetch = [&](ProdIn& in, int t0) __attribute__((always_inline)) {
             const int so = (t0 * H + h) * DK * 2;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
+            for (int i = 0; i < 2; i++) {
                 in.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so, 0);
                 in.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so, 0);
             }
             const int sg = (t0 * H + h) * DK * GB;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+            for (int i = 0; i < 2; i++)
 #pragma unroll
                 for (int hf = 0; hf < NGW / 4; hf++)
-                    in.gw[i * (NGW / 4) + hf] = __builtin_amdgcn_raw_buffer_load_b128(rgk, voff_g + gate_word_off(i, hf), sg, 0);
+                    in.gw[i * (NGW / 4) + hf] = __builtin_amdgcn_raw_buffer_load_b128(rgk, voff_g + gate_word_off(2 * pw + i, hf), sg, 0);
             const int sb = (t0 * H + h) * GB;
             in.b = GF32 ? __builtin_amdgcn_raw_buffer_load_b32(rbt, voff_gate, sb, 0)
                         : __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, sb, 0);
@@ -519,27 +532,28 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kda_kernel(Params p, FwdA
             bool ok = true;
             f4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int st = 0; st < 4; st++) {
+            for (int i = 0; i < 2; i++) {
+                const int st = 2 * pw + i;
                 // this lane's 8 key rows of slice st: token c's keys, queries and gates
                 float kf[8], qf[8], gf[8];
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    kf[2 * e] = __uint_as_float(in.k[st][e] << 16);
-                    kf[2 * e + 1] = __uint_as_float(in.k[st][e] & 0xFFFF0000u);
-                    qf[2 * e] = __uint_as_float(in.q[st][e] << 16);
-                    qf[2 * e + 1] = __uint_as_float(in.q[st][e] & 0xFFFF0000u);
+                    kf[2 * e] = __uint_as_float(in.k[i][e] << 16);
+                    kf[2 * e + 1] = __uint_as_float(in.k[i][e] & 0xFFFF0000u);
+                    qf[2 * e] = __uint_as_float(in.q[i][e] << 16);
+                    qf[2 * e + 1] = __uint_as_float(in.q[i][e] & 0xFFFF0000u);
                 }
                 if (GF32) {
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        gf[e] = __uint_as_float(in.gw[2 * st][e]);
-                        gf[4 + e] = __uint_as_float(in.gw[2 * st + 1][e]);
+                        gf[e] = __uint_as_float(in.gw[2 * i][e]);
+                        gf[4 + e] = __uint_as_float(in.gw[2 * i + 1][e]);
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        gf[2 * e] = __uint_as_float(in.gw[st][e] << 16);
-                        gf[2 * e + 1] = __uint_as_float(in.gw[st][e] & 0xFFFF0000u);
+                        gf[2 * e] = __uint_as_float(in.gw[i][e] << 16);
+                        gf[2 * e + 1] = __uint_as_float(in.gw[i][e] & 0xFFFF0000u);
                     }
                 }
                 float kb[8], qb[8], kh[8], kt[8], e15[8];
@@ -577,7 +591,8 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kda_kernel(Params p, FwdA
                     *reinterpret_cast<f4*>(&sl.eG15[32 * st + 8 * g]) = f4{e15[0], e15[1], e15[2], e15[3]};
                     *reinterpret_cast<f4*>(&sl.eG15[32 * st + 8 * g + 4]) = f4{e15[4], e15[5], e15[6], e15[7]};
                 }
-                // A (gk, lane (g, c) register r) = Kb_{4g+r} . Kh_c; Kh_{4g+r} . Qb_c (gq)
+                // lane (g, c) register r: Kb_{4g+r} . Kh_c (gk) and Kh_{4g+r} . Qb_c (gq) over
+                // this producer's key rows
                 const bf8 akb[3] = {parts_bf8(kbp[0]), parts_bf8(kbp[1]), parts_bf8(kbp[2])};
                 const bf8 akh[3] = {parts_bf8(khp[0]), parts_bf8(khp[1]), parts_bf8(khp[2])};
                 const bf8 aqb[3] = {parts_bf8(qbp[0]), parts_bf8(qbp[1]), parts_bf8(qbp[2])};
@@ -585,39 +600,10 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kda_kernel(Params p, FwdA
                 gq = mfma6_32(akh, aqb, gq);
             }
             const bool in_range = __all(ok);
-            const float bv = GF32 ? __uint_as_float(in.b) : bf_lo(in.b);
-            if (g == 0) sl.beta[c] = valid ? bv : 0.0f;
-            if (lane == 0) sl.in_range = in_range ? 1 : 0;
-            *reinterpret_cast<f4*>(&sl.GQ[c][4 * g]) = gq;
-            *reinterpret_cast<f4*>(&prod.Gk[c][4 * g]) = gk;  // [c][j] = A_{j c}
-            pc_wave_sync();
-            if (!in_range) return;
-            // M = (I + diag(beta) A)^{-1} diag(beta) on the identity in four stages (A is not
-            // symmetric here: A_{j i} = Gk[i][j])
-            const f4 beta4 = *reinterpret_cast<const f4*>(&sl.beta[4 * g]);
-            const float c01 = prod.Gk[4 * g][4 * g + 1], c02 = prod.Gk[4 * g][4 * g + 2];
-            const float c12 = prod.Gk[4 * g + 1][4 * g + 2], c03 = prod.Gk[4 * g][4 * g + 3];
-            const float c13 = prod.Gk[4 * g + 1][4 * g + 3], c23 = prod.Gk[4 * g + 2][4 * g + 3];
-            f4 dm = {0.0f, 0.0f, 0.0f, 0.0f}, selm = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int st = 0; st < 4; st++) {
-                const float e0 = 4 * g == c ? 1.0f : 0.0f, e1 = 4 * g + 1 == c ? 1.0f : 0.0f;
-                const float e2 = 4 * g + 2 == c ? 1.0f : 0.0f, e3 = 4 * g + 3 == c ? 1.0f : 0.0f;
-                const float x0 = beta4[0] * (e0 - dm[0]);
-                const float x1 = beta4[1] * (e1 - __builtin_fmaf(c01, x0, dm[1]));
-                const float x2 = beta4[2] * (e2 - __builtin_fmaf(c12, x1, __builtin_fmaf(c02, x0, dm[2])));
-                const float x3 = beta4[3] * (e3 - __builtin_fmaf(c23, x2, __builtin_fmaf(c13, x1, __builtin_fmaf(c03, x0, dm[3]))));
-                if (g == st) selm = f4{x0, x1, x2, x3};
-                if (st < 3) {
-                    *reinterpret_cast<f4*>(&prod.dd[g][c][0]) = f4{x0, x1, x2, x3};
-                    pc_wave_sync();
-                    // A: lane (kk, j) = A_{j, 4 st + kk} = Gk[4 st + kk][j] for tokens j of later groups
-                    const float ast = c >= 4 * st + 4 ? prod.Gk[4 * st + g][c] : 0.0f;
-                    dm = __builtin_amdgcn_mfma_f32_16x16x4f32(ast, prod.dd[st][c][g], dm, 0, 0, 0);
-                    pc_wave_sync();
-                }
-            }
-            *reinterpret_cast<f4*>(&sl.Ms[c][4 * g]) = selm;
+            if (pw == 0 && g == 0) sl.beta[c] = valid ? (GF32 ? __uint_as_float(in.b) : bf_lo(in.b)) : 0.0f;
+            if (lane == 0) sl.ok[pw] = in_range ? 1 : 0;
+            *reinterpret_cast<f4*>(&sl.GK[pw][c][4 * g]) = gk;
+            *reinterpret_cast<f4*>(&sl.GQ[pw][c][4 * g]) = gq;
         };
 
         int q_next = QMODE != LA_QDQ_NONE ? min(qi, T) - 1 : T;
@@ -692,7 +678,7 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kda_kernel(Params p, FwdA
             ck_next += p.ckpt_interval;
         }
 
-        if (__builtin_expect(__builtin_amdgcn_readfirstlane(sl.in_range) != 0, 1)) {
+        if (__builtin_expect(__builtin_amdgcn_readfirstlane(sl.ok[0] & sl.ok[1]) != 0, 1)) {
             // P' = Kb S_0, Q' = Qb S_0 (lane (g, c), register r: token 4 g + r, column c)
             f4 dk = {0.0f, 0.0f, 0.0f, 0.0f}, dq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -710,13 +696,44 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kda_kernel(Params p, FwdA
                 dk = mfma6_32(akb, bs, dk);
                 dq = mfma6_32(aqb, bs, dq);
             }
+            // M = (I + diag(beta) A)^{-1} diag(beta), solved by each wave on the identity in four
+            // stages (lane group g: tokens 4 g .. 4 g + 3 of column c; after each stage one fp32
+            // MFMA adds its values to the later tokens).  A_{j i} is the sum of the producers'
+            // partial products GK[.][i][j]; A is not symmetric here.
+            KdaSolve& sv = solve[w];
+            auto gkc = [&](int i, int j) __attribute__((always_inline)) { return sl.GK[0][i][j] + sl.GK[1][i][j]; };
+            const f4 beta4 = *reinterpret_cast<const f4*>(&sl.beta[4 * g]);
+            const float c01 = gkc(4 * g, 4 * g + 1), c02 = gkc(4 * g, 4 * g + 2);
+            const float c12 = gkc(4 * g + 1, 4 * g + 2), c03 = gkc(4 * g, 4 * g + 3);
+            const float c13 = gkc(4 * g + 1, 4 * g + 3), c23 = gkc(4 * g + 2, 4 * g + 3);
+            f4 dm = {0.0f, 0.0f, 0.0f, 0.0f}, selm = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; st++) {
+                const float e0 = 4 * g == c ? 1.0f : 0.0f, e1 = 4 * g + 1 == c ? 1.0f : 0.0f;
+                const float e2 = 4 * g + 2 == c ? 1.0f : 0.0f, e3 = 4 * g + 3 == c ? 1.0f : 0.0f;
+                const float x0 = beta4[0] * (e0 - dm[0]);
+                const float x1 = beta4[1] * (e1 - __builtin_fmaf(c01, x0, dm[1]));
+                const float x2 = beta4[2] * (e2 - __builtin_fmaf(c12, x1, __builtin_fmaf(c02, x0, dm[2])));
+                const float x3 = beta4[3] * (e3 - __builtin_fmaf(c23, x2, __builtin_fmaf(c13, x1, __builtin_fmaf(c03, x0, dm[3]))));
+                if (g == st) selm = f4{x0, x1, x2, x3};
+                if (st < 3) {
+                    *reinterpret_cast<f4*>(&sv.dd[g][c][0]) = f4{x0, x1, x2, x3};
+                    pc_wave_sync();
+                    // A: lane (kk, j) = A_{j, 4 st + kk} for tokens j of later groups
+                    const float ast = c >= 4 * st + 4 ? gkc(4 * st + g, c) : 0.0f;
+                    dm = __builtin_amdgcn_mfma_f32_16x16x4f32(ast, sv.dd[st][c][g], dm, 0, 0, 0);
+                    pc_wave_sync();
+                }
+            }
+            *reinterpret_cast<f4*>(&sv.Ms[c][4 * g]) = selm;
+            pc_wave_sync();
             // Delta = M (V - P'): slice s pairs token 4 g + s
             f4 ddm = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int sl_ = 0; sl_ < 4; sl_++)
-                ddm = __builtin_amdgcn_mfma_f32_16x16x4f32(sl.Ms[4 * g + sl_][c], bf_lo(vcur[sl_]) - dk[sl_], ddm, 0, 0, 0);
+                ddm = __builtin_amdgcn_mfma_f32_16x16x4f32(sv.Ms[4 * g + sl_][c], bf_lo(vcur[sl_]) - dk[sl_], ddm, 0, 0, 0);
             // o_i = Q'_i + sum_{j <= i} (Kh_j . Qb_i) delta_j
-            const f4 gq = *reinterpret_cast<const f4*>(&sl.GQ[c][4 * g]);
+            const f4 gq = *reinterpret_cast<const f4*>(&sl.GQ[0][c][4 * g]) + *reinterpret_cast<const f4*>(&sl.GQ[1][c][4 * g]);
             f4 ov = dq;
 #pragma unroll
             for (int kp = 0; kp < 4; kp++) {
@@ -829,9 +846,9 @@ hipError_t launch_mfma_o(const la_config& c, const FwdArgs& a, hipStream_t s) {
     dim3 grid(c.d_v / kTileCols, c.H, c.B);
     if (c.gate == LA_GATE_KEY) {
         if (c.out_dtype == LA_BF16)
-            hipLaunchKernelGGL((fwd_mfma_kda_kernel<QMODE, G, GF32, true>), grid, dim3(kPcThreads), 0, s, make_params(c), a);
+            hipLaunchKernelGGL((fwd_mfma_kda_kernel<QMODE, G, GF32, true>), grid, dim3(kKdaThreads), 0, s, make_params(c), a);
         else
-            hipLaunchKernelGGL((fwd_mfma_kda_kernel<QMODE, G, GF32, false>), grid, dim3(kPcThreads), 0, s, make_params(c), a);
+            hipLaunchKernelGGL((fwd_mfma_kda_kernel<QMODE, G, GF32, false>), grid, dim3(kKdaThreads), 0, s, make_params(c), a);
     } else if (c.out_dtype == LA_BF16) {
         hipLaunchKernelGGL((fwd_mfma_kernel<QMODE, G, GF32, true>), grid, dim3(kPcThreads), 0, s, make_params(c), a);
     } else {
