@@ -417,15 +417,17 @@ namespace {
 
 constexpr float kKdaGLim = 60.0f;
 
+constexpr int kKdaProd = 2;                  // producer waves
+constexpr int kKdaSlices = 4 / kKdaProd;     // 32-row key slices per producer
 struct alignas(16) KdaSlot {
     uint16_t Kb[3][kBlk][kKeyRow];  // the three bf16 parts of Kb, [token][row]
     uint16_t Qb[3][kBlk][kKeyRow];  // of Qb
     uint16_t Kt[3][kBlk][kKeyRow];  // of Kt (transposed reads of the update)
-    float GK[2][kBlk][kBlk];        // per producer (its 64 key rows): [c][4 g + r] = Kb_{4g+r} . Kh_c
-    float GQ[2][kBlk][kBlk];        // [c][4 g + r] = Kh_{4g+r} . Qb_c
+    float GK[kKdaProd][kBlk][kBlk];  // per producer (its key rows): [c][4 g + r] = Kb_{4g+r} . Kh_c
+    float GQ[kKdaProd][kBlk][kBlk];  // [c][4 g + r] = Kh_{4g+r} . Qb_c
     float eG15[128];                // exp(G_15) per key row
     float beta[kBlk];
-    int ok[2];                      // per producer: its gate sums stay in range
+    int ok[kKdaProd];               // per producer: its gate sums stay in range
 };
 // A column wave's staging for its solve of M.
 struct alignas(16) KdaSolve {
@@ -433,7 +435,7 @@ struct alignas(16) KdaSolve {
     float dd[4][kBlk][4];  // stage values of tokens 4 g + r, [g][column][r]
     float Ms[kBlk][20];    // [c][j] = M[j][c]
 };
-constexpr int kKdaThreads = (kWaveTileWaves + 2) * 64;  // four column waves + two producers
+constexpr int kKdaThreads = (kWaveTileWaves + kKdaProd) * 64;  // four column waves + the producers
 
 // e^x for |x| <= 60 (the block's gate-sum range): e^x = 2^(x log2 e), with x log2 e carried as
 // an fp32 sum hi + lo (the product's rounding error recovered by one FMA, plus the low part of
@@ -499,30 +501,30 @@ __global__ __launch_bounds__(kKdaThreads) void fwd_mfma_kda_kernel(Params p, Fwd
 
     if (w >= kWaveTileWaves) {
         // ------------------------------------------------------------ producers
-        // producer pw takes key rows 64 pw .. 64 pw + 63 (slices 2 pw and 2 pw + 1); producer 0
-        // also reads beta
+        // producer pw takes key slices kKdaSlices pw ..  kKdaSlices (pw + 1) - 1 (32 rows each);
+        // producer 0 also writes beta
         const int pw = w - kWaveTileWaves;
         const auto rbt = make_rsrc(static_cast<const char*>(a.beta) + seq0 * GB, seq_tok * GB);
-        const int voff_kq = (c * H * DK + 64 * pw + 8 * g) * 2;
+        const int voff_kq = (c * H * DK + 32 * kKdaSlices * pw + 8 * g) * 2;
         const int voff_g = c * H * DK * GB;
         const int voff_gate = c * H * GB;
         struct ProdIn {
-            u4 k[2], q[2], gw[NGW / 2];
+            u4 k[kKdaSlices], q[kKdaSlices], gw[NGW / 4 * kKdaSlices];
             uint32_t b;
         };
         auto pfetch = [&](ProdIn& in, int t0) __attribute__((always_inline)) {
             const int so = (t0 * H + h) * DK * 2;
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
+            for (int i = 0; i < kKdaSlices; i++) {
                 in.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_kq + 64 * i, so, 0);
                 in.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, voff_kq + 64 * i, so, 0);
             }
             const int sg = (t0 * H + h) * DK * GB;
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < kKdaSlices; i++)
 #pragma unroll
                 for (int hf = 0; hf < NGW / 4; hf++)
-                    in.gw[i * (NGW / 4) + hf] = __builtin_amdgcn_raw_buffer_load_b128(rgk, voff_g + gate_word_off(2 * pw + i, hf), sg, 0);
+                    in.gw[i * (NGW / 4) + hf] = __builtin_amdgcn_raw_buffer_load_b128(rgk, voff_g + gate_word_off(kKdaSlices * pw + i, hf), sg, 0);
             const int sb = (t0 * H + h) * GB;
             in.b = GF32 ? __builtin_amdgcn_raw_buffer_load_b32(rbt, voff_gate, sb, 0)
                         : __builtin_amdgcn_raw_buffer_load_b16(rbt, voff_gate, sb, 0);
@@ -532,8 +534,8 @@ __global__ __launch_bounds__(kKdaThreads) void fwd_mfma_kda_kernel(Params p, Fwd
             bool ok = true;
             f4 gk = {0.0f, 0.0f, 0.0f, 0.0f}, gq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int st = 2 * pw + i;
+            for (int i = 0; i < kKdaSlices; i++) {
+                const int st = kKdaSlices * pw + i;
                 // this lane's 8 key rows of slice st: token c's keys, queries and gates
                 float kf[8], qf[8], gf[8];
 #pragma unroll
@@ -678,7 +680,10 @@ __global__ __launch_bounds__(kKdaThreads) void fwd_mfma_kda_kernel(Params p, Fwd
             ck_next += p.ckpt_interval;
         }
 
-        if (__builtin_expect(__builtin_amdgcn_readfirstlane(sl.ok[0] & sl.ok[1]) != 0, 1)) {
+        int in_range = sl.ok[0];
+#pragma unroll
+        for (int pw = 1; pw < kKdaProd; pw++) in_range &= sl.ok[pw];
+        if (__builtin_expect(__builtin_amdgcn_readfirstlane(in_range) != 0, 1)) {
             // P' = Kb S_0, Q' = Qb S_0 (lane (g, c), register r: token 4 g + r, column c)
             f4 dk = {0.0f, 0.0f, 0.0f, 0.0f}, dq = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -701,7 +706,12 @@ __global__ __launch_bounds__(kKdaThreads) void fwd_mfma_kda_kernel(Params p, Fwd
             // MFMA adds its values to the later tokens).  A_{j i} is the sum of the producers'
             // partial products GK[.][i][j]; A is not symmetric here.
             KdaSolve& sv = solve[w];
-            auto gkc = [&](int i, int j) __attribute__((always_inline)) { return sl.GK[0][i][j] + sl.GK[1][i][j]; };
+            auto gkc = [&](int i, int j) __attribute__((always_inline)) {
+                float x = sl.GK[0][i][j];
+#pragma unroll
+                for (int pw = 1; pw < kKdaProd; pw++) x += sl.GK[pw][i][j];
+                return x;
+            };
             const f4 beta4 = *reinterpret_cast<const f4*>(&sl.beta[4 * g]);
             const float c01 = gkc(4 * g, 4 * g + 1), c02 = gkc(4 * g, 4 * g + 2);
             const float c12 = gkc(4 * g + 1, 4 * g + 2), c03 = gkc(4 * g, 4 * g + 3);
@@ -733,7 +743,9 @@ __global__ __launch_bounds__(kKdaThreads) void fwd_mfma_kda_kernel(Params p, Fwd
             for (int sl_ = 0; sl_ < 4; sl_++)
                 ddm = __builtin_amdgcn_mfma_f32_16x16x4f32(sv.Ms[4 * g + sl_][c], bf_lo(vcur[sl_]) - dk[sl_], ddm, 0, 0, 0);
             // o_i = Q'_i + sum_{j <= i} (Kh_j . Qb_i) delta_j
-            const f4 gq = *reinterpret_cast<const f4*>(&sl.GQ[0][c][4 * g]) + *reinterpret_cast<const f4*>(&sl.GQ[1][c][4 * g]);
+            f4 gq = *reinterpret_cast<const f4*>(&sl.GQ[0][c][4 * g]);
+#pragma unroll
+            for (int pw = 1; pw < kKdaProd; pw++) gq += *reinterpret_cast<const f4*>(&sl.GQ[pw][c][4 * g]);
             f4 ov = dq;
 #pragma unroll
             for (int kp = 0; kp < 4; kp++) {
