@@ -163,7 +163,7 @@ def bench_long_e4m3(steps=3, warmup=1):
 
 def bench_kda_long(steps=3, warmup=1):
     """KDA B=8 H=16 T=4096 d=128, bf16 q/k/v, fp32 per-key gates and beta, E4M3 tile QDQ every
-    64 tokens: the forward (single-wave kernel) and the straight-through backward."""
+    64 tokens: the forward (block kernel) and the straight-through backward (token kernel)."""
     import torch
 
     import quantized_state_qat_amd as la

@@ -125,6 +125,29 @@ def e4m3_codes_from_state(X: np.ndarray, tile: int = 64):
     return out
 
 
+# Non-negative E4M3FN values in increasing order, from the format's definition: subnormals
+# m 2^-9 (m = 0..7), normals (1 + m/8) 2^(e-7) for e = 1..15 (e = 15, m = 7 is NaN; max 448).
+E4M3_GRID = np.array([m * 2.0 ** -9 for m in range(8)]
+                     + [(1 + m / 8) * 2.0 ** (e - 7) for e in range(1, 16) for m in range(8) if (e, m) != (15, 7)])
+
+
+def compare_e4m3_values(yg: np.ndarray, yo: np.ndarray, tally: "CodeTally") -> None:
+    """Add one quantization point's E4M3 grid values (GPU yg, oracle yo) to the tally; every
+    mismatch must be a pair of neighbouring grid values of one sign (a near-tie decided the
+    other way), or zero against the smallest subnormal."""
+    yg = np.asarray(yg, dtype=np.float64)
+    yo = np.asarray(yo, dtype=np.float64)
+    bad = yg != yo
+    tally.add(int(bad.sum()), yg.size)
+    if bad.any():
+        a, b = yg[bad], yo[bad]
+        same_side = (np.sign(a) == np.sign(b)) | (a == 0) | (b == 0)
+        ia = np.searchsorted(E4M3_GRID, np.abs(a))
+        ib = np.searchsorted(E4M3_GRID, np.abs(b))
+        assert np.all(E4M3_GRID[ia] == np.abs(a)) and np.all(E4M3_GRID[ib] == np.abs(b)), "values off the grid"
+        assert np.all(same_side & (np.abs(ia - ib) == 1)), list(zip(a[:8], b[:8]))
+
+
 def hadamard_n(n: int) -> np.ndarray:
     H = np.array([[1.0]])
     while H.shape[0] < n:
