@@ -37,9 +37,12 @@
  *   o          [B][T][H][d_v]          dtype out_dtype
  *   S0, S_T, S [B][H][d_k][d_v]        float32
  *   ckpts      [B][H][ceil(T/ckpt_interval)][d_k][d_v] float32: the carried state entering
- *              tokens 0, n, 2n, ... (n = ckpt_interval).  In Hadamard mode the carried state
- *              is kept, and checkpointed, in its rotated form Y = Hu S (Hu the unnormalized
- *              Sylvester matrix, Hu Hu = d_k I), on which the INT8 codes act; S = Hu Y / d_k.
+ *              tokens 0, n, 2n, ... (n = ckpt_interval).  In Hadamard mode with the scalar
+ *              gate the carried state is kept, and checkpointed, in its rotated form
+ *              Y = Hu S (Hu the unnormalized Sylvester matrix, Hu Hu = d_k I), on which the
+ *              INT8 codes act; S = Hu Y / d_k.  With per-key gates (a row decay does not
+ *              commute with the rotation) S is carried and checkpointed unrotated and rotated
+ *              to Hu S' only at each rounding point, where the codes act on it.
  *   dout       [B][T][H][d_v]          float32
  *   dq, dk     [B][T][H][d_k], dv [B][T][H][d_v], dg like g, dbeta [B][T][H],
  *   dS_T, dS0  [B][H][d_k][d_v]        all float32
@@ -53,7 +56,8 @@
  * return LA_ERR_UNSUPPORTED; there is no fallback path.
  *
  * Supported: d_k in {16, 32, 64, 128}; d_v a multiple of 64 up to 4096; INT8 group 16, 32
- * or 64; E4M3 tile width 64; Hadamard with the scalar gate only.
+ * or 64; E4M3 tile width 64; Hadamard with INT8, for either gate (state_rotated = 1 with the
+ * scalar gate only).
  */
 #ifndef LA_H
 #define LA_H
@@ -89,11 +93,12 @@ typedef struct la_config {
     int32_t qkv_dtype;     /* la_dtype of q, k, v */
     int32_t gate_dtype;    /* la_dtype of g, beta */
     int32_t out_dtype;     /* la_dtype of o */
-    int32_t state_rotated; /* Hadamard mode only.  0: S0, S_T, S (decode), dS_T and dS0 hold the
-                              state S.  1: they hold the rotated state Y = Hu S (and the
-                              gradients dL/dY), the representation the codes act on; chained
-                              calls then resume bit for bit and a decode step rotates only the
-                              key and query vectors, never the state. */
+    int32_t state_rotated; /* Hadamard mode with the scalar gate only.  0: S0, S_T, S (decode),
+                              dS_T and dS0 hold the state S.  1: they hold the rotated state
+                              Y = Hu S (and the gradients dL/dY), the representation the
+                              codes act on; chained calls then resume bit for bit and a
+                              decode step rotates only the key and query vectors, never the
+                              state. */
 } la_config;
 
 /*

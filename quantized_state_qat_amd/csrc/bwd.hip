@@ -109,6 +109,9 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     using S = TokShape<DK, QMODE, G>;
     constexpr int R = S::R, TC = S::TC;
     constexpr int PW = PartLayout<DK, KDA>::PW;
+    // Hadamard mode: rotated carry for the scalar gate (RC), rotation around each rounding
+    // point of the recompute for per-key gates (RQ; the adjoint is then the plain one)
+    constexpr bool RC = HAD && !KDA, RQ = HAD && KDA;
     __shared__ TokRing<S, KDA, true> ring;
     __shared__ float2 red[2][kTokWaves][TC];
     __shared__ TokQdqShared<S> qsh;
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
 #pragma unroll
     for (int m = 0; m < R; m++)
         lam[m] = a.dST ? a.dST[state_off + static_cast<size_t>(r0 + m) * DV + col] : 0.0f;
-    if (HAD && !p.rot) tok_rotate<S>(lam, tile, w, lane, 1.0f / DK);  // dL/dY = Hu dL/dS / d_k
+    if (RC && !p.rot) tok_rotate<S>(lam, tile, w, lane, 1.0f / DK);  // dL/dY = Hu dL/dS / d_k
 
     // Blocks in processing order: chunk c from last to first; in each, phase A over blocks
     // j = 0 .. nb-1, then phase B over j = nb-1 .. 0.  The inputs of the next block in this
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     // publish block (c, j) from the fetched words, fetch (nc, nj), make the records visible
     auto publish = [&](int nt, int nc, int nj) __attribute__((always_inline)) {
         __syncthreads();  // the previous block's records are no longer read
-        if (w < nt) f.template publish<HAD>(ring, w, p, lane);
+        if (w < nt) f.template publish<RC>(ring, w, p, lane);
         fetch(nc, nj);
         __syncthreads();
     };
@@ -189,11 +192,11 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                     TokOps<S, KDA> op;
                     tok_read<S, KDA, true>(op, ring, i, w, lane);
                     float u, dl, o;
-                    tok_step<S, KDA, HAD>(s, op, red[rp], w, lane, u, dl, o);
+                    tok_step<S, KDA, RC>(s, op, red[rp], w, lane, u, dl, o);
                     rp ^= 1;
                     const int t = tb + i;
                     if (QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1))
-                        tok_qdq<S>(s, qsh, w, lane);
+                        tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
                 }
             }
         }
@@ -228,11 +231,11 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                         TokOps<S, KDA> op;
                         tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
                         float o;
-                        tok_step<S, KDA, HAD>(s, op, red[rp], w, lane, uu[i], dd[i], o);
+                        tok_step<S, KDA, RC>(s, op, red[rp], w, lane, uu[i], dd[i], o);
                         rp ^= 1;
                         const int t = tb + i0 + i;
                         if (QMODE != LA_QDQ_NONE && i + 1 < n && (((t + 1) % p.qdq_interval) == 0 || t == T - 1))
-                            tok_qdq<S>(s, qsh, w, lane);
+                            tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
                     }
                 }
 #pragma unroll
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                         tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
                         const size_t tok = tok0 + static_cast<size_t>(tb + i0 + i) * H;
                         float* part = a.ws_part + (static_cast<size_t>(blk) * ntok + tok) * PW;
-                        tok_adjoint<S, KDA, HAD>(st[i], uu[i], dd[i], op, ring.ga[i0 + i], lam, red[rp], w, lane,
+                        tok_adjoint<S, KDA, RC>(st[i], uu[i], dd[i], op, ring.ga[i0 + i], lam, red[rp], w, lane,
                                                   part, a.dv + tok * DV + col, w == i0 + i);
                         rp ^= 1;
                     }
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
             }
         }
     }
-    if (HAD && !p.rot) tok_rotate<S>(lam, tile, w, lane, 1.0f);  // dL/dS = Hu dL/dY
+    if (RC && !p.rot) tok_rotate<S>(lam, tile, w, lane, 1.0f);  // dL/dS = Hu dL/dY
 #pragma unroll
     for (int m = 0; m < R; m++) a.dS0[state_off + static_cast<size_t>(r0 + m) * DV + col] = lam[m];
 }
@@ -340,7 +343,7 @@ hipError_t launch_bwd_t(const la_config& c, const BwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const size_t ntok = static_cast<size_t>(c.B) * c.T * c.H;
     if (ntok == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_reduce_kernel<DK, HAD, KDA>), dim3(static_cast<unsigned>(ntok)), dim3(64), 0, s, p, a,
+    hipLaunchKernelGGL((bwd_reduce_kernel<DK, HAD && !KDA, KDA>), dim3(static_cast<unsigned>(ntok)), dim3(64), 0, s, p, a,
                        c.d_v / TC);
     return hipGetLastError();
 }
@@ -360,7 +363,8 @@ hipError_t launch_bwd_q(const la_config& c, const BwdArgs& a, hipStream_t s) {
 
 template <int DK>
 hipError_t launch_bwd_dk(const la_config& c, const BwdArgs& a, hipStream_t s) {
-    if (c.hadamard) return launch_bwd_q<DK, true, false>(c, a, s);
+    if (c.hadamard)
+        return c.gate == LA_GATE_KEY ? launch_bwd_q<DK, true, true>(c, a, s) : launch_bwd_q<DK, true, false>(c, a, s);
     if (c.gate == LA_GATE_KEY) return launch_bwd_q<DK, false, true>(c, a, s);
     return launch_bwd_q<DK, false, false>(c, a, s);
 }

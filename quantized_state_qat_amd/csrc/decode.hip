@@ -134,7 +134,7 @@ __global__ __launch_bounds__(16 * (DK / R)) void decode_kernel(DecParams p, Deco
         float kqp = wave_sum(tid < DK ? kk * qv : 0.0f);
         if (lane == 0) sm.kqp[w] = kqp;
     }
-    if (HAD && p.rot) {
+    if (HAD && !KDA && p.rot) {  // (per-key gates take only the unrotated state)
         // state held as Y = Hu S: rotate the key and query instead of the state.
         // u = Y~^T (Hu k) / d_k, Y' = Y~ + (Hu k) delta^T, o = Y~^T (Hu q) / d_k + delta (k . q).
 #pragma unroll 1
@@ -336,9 +336,12 @@ static hipError_t launch_dec_dk(const la_config& c, const DecodeArgs& a, hipStre
                    : launch_dec_t<DK, LA_QDQ_E4M3_TILE, 64, false, false>(c, a, s);
     if (c.hadamard) {
         switch (c.group) {
-            case 16: return launch_dec_t<DK, LA_QDQ_INT8_GROUP, 16, true, false>(c, a, s);
-            case 32: return launch_dec_t<DK, LA_QDQ_INT8_GROUP, 32, true, false>(c, a, s);
-            default: return launch_dec_t<DK, LA_QDQ_INT8_GROUP, 64, true, false>(c, a, s);
+            case 16: return kda ? launch_dec_t<DK, LA_QDQ_INT8_GROUP, 16, true, true>(c, a, s)
+                                : launch_dec_t<DK, LA_QDQ_INT8_GROUP, 16, true, false>(c, a, s);
+            case 32: return kda ? launch_dec_t<DK, LA_QDQ_INT8_GROUP, 32, true, true>(c, a, s)
+                                : launch_dec_t<DK, LA_QDQ_INT8_GROUP, 32, true, false>(c, a, s);
+            default: return kda ? launch_dec_t<DK, LA_QDQ_INT8_GROUP, 64, true, true>(c, a, s)
+                                : launch_dec_t<DK, LA_QDQ_INT8_GROUP, 64, true, false>(c, a, s);
         }
     }
     switch (c.group) {

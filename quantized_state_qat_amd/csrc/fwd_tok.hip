@@ -26,6 +26,9 @@ template <int DK, int QMODE, int G, bool HAD, bool KDA>
 __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdArgs a) {
     using S = TokShape<DK, QMODE, G>;
     constexpr int R = S::R, TC = S::TC;
+    // Hadamard mode: the scalar gate carries Y = Hu S (RC); per-key gates carry S and rotate
+    // around each rounding point (RQ)
+    constexpr bool RC = HAD && !KDA, RQ = HAD && KDA;
     __shared__ TokRing<S, KDA, false> ring;
     __shared__ float2 red[2][kTokWaves][TC];
     __shared__ TokQdqShared<S> qsh;
@@ -67,14 +70,14 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
         if (u < T) f.fetch(in, p, tok0 + static_cast<size_t>(u) * H, col, lane);
     };
     auto publish = [&](int u) __attribute__((always_inline)) {
-        if (u < T) f.template publish<HAD>(ring, u % kTokRing, p, lane);
+        if (u < T) f.template publish<RC>(ring, u % kTokRing, p, lane);
     };
 
     float s[R];
 #pragma unroll
     for (int m = 0; m < R; m++)
         s[m] = a.S0 ? a.S0[state_off + static_cast<size_t>(r0 + m) * DV + col] : 0.0f;
-    if (HAD && !p.rot) tok_rotate<S>(s, tile, w, lane, 1.0f);
+    if (RC && !p.rot) tok_rotate<S>(s, tile, w, lane, 1.0f);
 
     fetch(w);
     publish(w);
@@ -106,13 +109,13 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
             ck_next += p.ckpt_interval;
         }
         float u, delta, o;
-        tok_step<S, KDA, HAD>(s, op, red[t & 1], w, lane, u, delta, o);
+        tok_step<S, KDA, RC>(s, op, red[t & 1], w, lane, u, delta, o);
         if (a.o && w == (t & (kTokWaves - 1)) && lane < TC) store_elem(a.o, tok * DV + col, p.out_dt, o);
         if (t + 1 < T) tok_read<S, KDA, false>(op_next, ring, (t + 1) % kTokRing, w, lane);
         if (t == q_next) {
             q_next = min(q_next + p.qdq_interval, T - 1);
             if (q_next == t) q_next = T;
-            tok_qdq<S>(s, qsh, w, lane);
+            tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
         }
     };
 #pragma unroll 1
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
         if (t + 1 < T) token(t + 1, opB, opA);
     }
     if (a.ST) {
-        if (HAD && !p.rot) tok_rotate<S>(s, tile, w, lane, 1.0f / DK);
+        if (RC && !p.rot) tok_rotate<S>(s, tile, w, lane, 1.0f / DK);
 #pragma unroll
         for (int m = 0; m < R; m++) a.ST[state_off + static_cast<size_t>(r0 + m) * DV + col] = s[m];
     }
@@ -151,7 +154,8 @@ hipError_t launch_tok_q(const la_config& c, const FwdArgs& a, hipStream_t s) {
 
 template <int DK>
 hipError_t launch_tok_dk(const la_config& c, const FwdArgs& a, hipStream_t s) {
-    if (c.hadamard) return launch_tok_q<DK, true, false>(c, a, s);
+    if (c.hadamard)
+        return c.gate == LA_GATE_KEY ? launch_tok_q<DK, true, true>(c, a, s) : launch_tok_q<DK, true, false>(c, a, s);
     if (c.gate == LA_GATE_KEY) return launch_tok_q<DK, false, true>(c, a, s);
     return launch_tok_q<DK, false, false>(c, a, s);
 }

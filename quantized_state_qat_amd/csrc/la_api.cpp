@@ -56,8 +56,9 @@ la_status check_config(const la_config* c, bool decode) {
         case LA_QDQ_INT8_GROUP:
             if (c->group != 16 && c->group != 32 && c->group != 64)
                 return fail(LA_ERR_UNSUPPORTED, "INT8 group must be 16, 32 or 64 (group=%d)", c->group);
-            if (c->hadamard && c->gate == LA_GATE_KEY)
-                return fail(LA_ERR_UNSUPPORTED, "Hadamard rotation is implemented for the scalar gate only");
+            if (c->hadamard && c->gate == LA_GATE_KEY && c->state_rotated)
+                return fail(LA_ERR_UNSUPPORTED,
+                            "state_rotated is implemented for the scalar gate only (per-key gates carry S)");
             if (c->qdq_interval < 1) return fail(LA_ERR_INVALID_ARG, "qdq_interval must be >= 1");
             break;
         case LA_QDQ_E4M3_TILE:

@@ -515,4 +515,16 @@ __device__ __forceinline__ void tok_rotate(float (&s)[S::R], float* tile, int w,
     __syncthreads();
 }
 
+// A rounding point.  ROT (Hadamard mode with per-key gates, whose state is carried unrotated:
+// a per-row decay does not commute with the key-axis rotation): the codes are those of Hu S'
+// and the state carried on is Hu Q(Hu S') / d_k, which is Hn Q(Hn S') because the codecs
+// commute with a common scale of their group up to the rounding of that scale (the same
+// reading as the rotated carry of the scalar gate).  Every thread of the workgroup calls it.
+template <class S, bool ROT>
+__device__ __forceinline__ void tok_qdq_at(float (&s)[S::R], TokQdqShared<S>& sh, float* tile, int w, int lane) {
+    if constexpr (ROT) tok_rotate<S>(s, tile, w, lane, 1.0f);
+    tok_qdq<S>(s, sh, w, lane);
+    if constexpr (ROT) tok_rotate<S>(s, tile, w, lane, 1.0f / S::DK);
+}
+
 }  // namespace la

@@ -53,7 +53,7 @@ def fwd(c, **ptrs):
     (dict(d_v=96), la.LA_ERR_UNSUPPORTED, "d_v"),
     (dict(group=8), la.LA_ERR_UNSUPPORTED, "group"),
     (dict(qdq=la.LA_QDQ_E4M3_TILE, group=32), la.LA_ERR_UNSUPPORTED, "E4M3"),
-    (dict(hadamard=1, gate=la.LA_GATE_KEY), la.LA_ERR_UNSUPPORTED, "Hadamard"),
+    (dict(hadamard=1, gate=la.LA_GATE_KEY, state_rotated=1), la.LA_ERR_UNSUPPORTED, "state_rotated"),
     (dict(hadamard=1, qdq=la.LA_QDQ_NONE), la.LA_ERR_INVALID_ARG, "hadamard"),
     (dict(qdq_interval=0), la.LA_ERR_INVALID_ARG, "qdq_interval"),
     (dict(qdq=7), la.LA_ERR_INVALID_ARG, "qdq"),
@@ -160,6 +160,8 @@ def test_bwd_workspace_and_checks():
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=12, ckpt_interval=0), "fast"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=1, ckpt_interval=0), "token"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=64, hadamard=1), "token"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=64, hadamard=1,
+          gate=la.LA_GATE_KEY), "token"),
     (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, gate=la.LA_GATE_KEY), "block"),
     (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=24, ckpt_interval=24, gate=la.LA_GATE_KEY), "wave"),
     (dict(qdq=la.LA_QDQ_NONE, ckpt_interval=8, gate=la.LA_GATE_KEY, qkv_dtype=la.LA_F32), "wave"),

@@ -26,8 +26,9 @@ def _check_against_oracle(c, d, S0, do, dST, g_gpu, tol):
     """S0 and dST are given in the representation the call used (rotated when
     c.state_rotated); the oracle works on the unrotated state."""
     had, rot = bool(c.hadamard), bool(c.state_rotated)
+    rc = had and c.gate == la.LA_GATE_SCALAR  # per-key gates carry the unrotated state
     _, ST, states = gu.run_fwd(c, d, S0=S0, ckpt_interval=1)
-    states = gu.rotated_to_state(states) if had else states.astype(np.float64)
+    states = gu.rotated_to_state(states) if rc else states.astype(np.float64)
     S0_phys = None if S0 is None else (gu.rotated_to_state(S0) if rot else S0.astype(np.float64))
     dST_phys = None
     if dST is not None:
@@ -57,6 +58,12 @@ CASES = [
      la.LA_QDQ_INT8_GROUP, 32, 2, 1, 32, True),
     ("kda_int8g64_tok", synth.Workload("k", B=2, T=100, H=2, d_k=128, d_v=128, gate="key", config_id=32),
      la.LA_QDQ_INT8_GROUP, 64, 0, 1, 64, False),
+    ("kda_wht_int8g32_tok", synth.Workload("kw", B=1, T=70, H=2, d_k=128, d_v=128, gate="key", s0_sigma=0.2,
+                                           config_id=41),
+     la.LA_QDQ_INT8_GROUP, 32, 1, 1, 32, True),
+    ("kda_wht_int8g64_i2_ckpt12", synth.Workload("kw2", B=2, T=41, H=1, d_k=128, d_v=64, gate="key", s0_sigma=0.2,
+                                                 config_id=42),
+     la.LA_QDQ_INT8_GROUP, 64, 1, 2, 12, True),
     # checkpoints from the KDA block forward, recomputed by the token backward
     ("kda_e4m3_64_block_ckpts", synth.Workload("kb", B=1, T=150, H=2, d_k=128, d_v=128, gate="key", gate_dtype="f32",
                                                s0_sigma=0.1, config_id=40),

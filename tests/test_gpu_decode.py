@@ -62,6 +62,7 @@ CASES = [
     ("int8g64_kda", 2, 2, 128, 128, "key", la.LA_QDQ_INT8_GROUP, 64, 0),
     ("e4m3", 2, 3, 128, 128, "scalar", la.LA_QDQ_E4M3_TILE, 64, 0),
     ("wht_int8g32", 2, 2, 128, 128, "scalar", la.LA_QDQ_INT8_GROUP, 32, 1),
+    ("wht_int8g64_kda", 2, 2, 128, 128, "key", la.LA_QDQ_INT8_GROUP, 64, 1),
     ("wht_int8g16_rotated_state", 2, 3, 128, 128, "scalar", la.LA_QDQ_INT8_GROUP, 16, 2),
     ("none_dk32", 2, 2, 32, 64, "scalar", la.LA_QDQ_NONE, 32, 0),
     ("int8g32_dk16", 1, 3, 16, 64, "scalar", la.LA_QDQ_INT8_GROUP, 32, 0),

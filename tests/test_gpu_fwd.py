@@ -38,16 +38,18 @@ def _oracle_kw(c):
 
 def per_token_teacher_forced(c, d, ck, ST, o_gpu, tol, tally=None):
     """Compare every token: GPU state entering token t -> oracle one step -> GPU state after
-    token t (codes) and o_t.  In Hadamard mode the checkpoints hold the rotated state
-    (c.state_rotated decides whether S_T does too).  Returns (max output error, tally)."""
+    token t (codes) and o_t.  In Hadamard mode with the scalar gate the checkpoints hold the
+    rotated state (c.state_rotated decides whether S_T does too); per-key gates carry and
+    checkpoint the unrotated state.  Returns (max output error, tally)."""
     T = c.T
     had = bool(c.hadamard)
+    rc = had and c.gate == la.LA_GATE_SCALAR
     tally = tally if tally is not None else gu.CodeTally()
     worst_o = 0.0
     for t in range(T):
-        S_in = gu.rotated_to_state(ck[:, :, t]) if had else ck[:, :, t].astype(np.float64)
+        S_in = gu.rotated_to_state(ck[:, :, t]) if rc else ck[:, :, t].astype(np.float64)
         if t + 1 < T:
-            S_out, out_rotated = ck[:, :, t + 1], had
+            S_out, out_rotated = ck[:, :, t + 1], rc
         else:
             S_out, out_rotated = ST, had and bool(c.state_rotated)
         o_t, Sp, _ = oracle.fwd(d["q"].f64[:, t:t + 1], d["k"].f64[:, t:t + 1], d["v"].f64[:, t:t + 1],
@@ -79,6 +81,11 @@ PER_TOKEN = [
      la.LA_QDQ_INT8_GROUP, 64, 0),
     ("gdn_wht_int8g32_ragged", synth.Workload("wht", B=2, T=70, H=2, d_k=128, d_v=128, config_id=22),
      la.LA_QDQ_INT8_GROUP, 32, 1),
+    # per-key gates with the rotation: the state is carried unrotated, rotated at each rounding
+    ("kda_wht_int8g32_ragged", synth.Workload("kwh", B=2, T=70, H=2, d_k=128, d_v=128, gate="key", config_id=27),
+     la.LA_QDQ_INT8_GROUP, 32, 1),
+    ("kda_wht_int8g16_dk64", synth.Workload("kw6", B=1, T=33, H=2, d_k=64, d_v=128, gate="key", config_id=28),
+     la.LA_QDQ_INT8_GROUP, 16, 1),
     ("gdn_int8g16_dk32_dv128", synth.Workload("g16", B=1, T=33, H=3, d_k=32, d_v=128, config_id=23),
      la.LA_QDQ_INT8_GROUP, 16, 0),
     ("kda_e4m3_tok_dk64", synth.Workload("e4t", B=1, T=20, H=2, d_k=64, d_v=64, gate="key", config_id=24),

@@ -155,8 +155,6 @@ QCASES = [(oracle.QDQ_INT8, 32, False, 1), (oracle.QDQ_INT8, 16, False, 1),
 def test_power_of_two_and_sign_equivariance(oracle_mod, mode, group, had, interval, gate):
     """The recurrence is jointly linear in (S_0, v) and every quantizer commutes with 2^m
     scaling and with negation, so (2^m v, 2^m S_0) gives exactly 2^m o and 2^m S."""
-    if had and gate == "key":
-        pytest.skip("Hadamard cases use the scalar gate")
     rng = np.random.default_rng(10 + mode + group)
     q, k, v, g, beta, S0 = _rand_inputs(rng, 1, 70, 2, 64, 64, gate)
     kw = dict(gate=1 if gate == "key" else 0, qdq_mode=mode, group=group, hadamard=had,
