@@ -251,12 +251,18 @@ def bench_kda_tok(steps=3, warmup=1):
     stream = torch.cuda.current_stream()
     t = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
                                                 ST, stream=stream), steps, warmup, stream)
+    c.hadamard = 1
+    t_h = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
+                                                  ST, stream=stream), steps, warmup, stream)
     flops = 7.0 * w.d_k * w.d_v * w.B * w.H * w.T
     return {
         "workload": "kda_int8g64_tok B=4 H=32 T=2048 d_k=d_v=128 bf16 inputs, KDA gate, INT8 group-64 QDQ every token",
         "kernel": la.la_fwd_kernel_name(c), "ms_per_call": t * 1e3, "updates_per_s": w.B * w.H * w.T / t,
         "roofline": _fp32_roofline(flops, t, "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head); "
                                              "the INT8 codec is not counted"),
+        "ms_per_call_hadamard": t_h * 1e3,
+        "note_hadamard": "the same call with the key-axis Hadamard rotation around every rounding (per-key gates "
+                         "carry the state unrotated: two rotations of the state per token)",
     }
 
 

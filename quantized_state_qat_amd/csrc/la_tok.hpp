@@ -489,30 +489,44 @@ __device__ __forceinline__ void tok_qdq(float (&s)[S::R], TokQdqShared<S>& sh, i
 }
 
 // ------------------------------------------------------------------ state rotation
-// s <- (Hu s) * scale along the key axis, through an LDS tile of DK x TC floats.  Every
-// thread of the workgroup calls it.
+// s <- (Hu s) * scale along the key axis (Sylvester butterflies over row bits 1, 2, 4, ...
+// in that order).  A lane's R rows are consecutive and R-aligned, so the stages over row bits
+// below R stay in registers; each higher stage exchanges rows with the lane or wave that holds
+// the partner rows through an LDS tile of DK x TC floats.  Every thread of the workgroup calls
+// it (uniformly).
 template <class S>
 __device__ __forceinline__ void tok_rotate(float (&s)[S::R], float* tile, int w, int lane, float scale) {
-    constexpr int DK = S::DK, TC = S::TC;
+    constexpr int DK = S::DK, TC = S::TC, R = S::R;
     const int r0 = tok_row0<S>(w, lane), c = lane % TC;
-    __syncthreads();
 #pragma unroll
-    for (int m = 0; m < S::R; m++) tile[(r0 + m) * TC + c] = s[m];
-#pragma unroll 1
-    for (int h = 1; h < DK; h <<= 1) {
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < (DK / 2) * TC; idx += kTokThreads) {
-            const int cc = idx % TC, pr = idx / TC;
-            const int i = (pr / h) * 2 * h + (pr % h);
-            const float x = tile[i * TC + cc], y = tile[(i + h) * TC + cc];
-            tile[i * TC + cc] = x + y;
-            tile[(i + h) * TC + cc] = x - y;
+    for (int h = 1; h < R; h <<= 1) {
+#pragma unroll
+        for (int m = 0; m < R; m++) {
+            if ((m & h) == 0) {
+                const float x = s[m], y = s[m + h];
+                s[m] = x + y;
+                s[m + h] = x - y;
+            }
         }
     }
-    __syncthreads();
 #pragma unroll
-    for (int m = 0; m < S::R; m++) s[m] = tile[(r0 + m) * TC + c] * scale;
-    __syncthreads();
+    for (int h = R; h < DK; h <<= 1) {
+        __syncthreads();  // the previous stage's reads are done
+#pragma unroll
+        for (int m = 0; m < R; m++) tile[(r0 + m) * TC + c] = s[m];
+        __syncthreads();
+        // every row of this lane has the same bit h (h >= R): the lower rows add the partner,
+        // the upper rows subtract themselves from it
+        const bool upper = (r0 & h) != 0;
+#pragma unroll
+        for (int m = 0; m < R; m++) {
+            const float p = tile[((r0 + m) ^ h) * TC + c];
+            s[m] = upper ? p - s[m] : s[m] + p;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < R; m++) s[m] *= scale;
+    __syncthreads();  // the tile is free for its next use
 }
 
 // A rounding point.  ROT (Hadamard mode with per-key gates, whose state is carried unrotated:
