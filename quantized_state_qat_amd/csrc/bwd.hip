@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     __shared__ TokRing<S, KDA, true> ring;
     __shared__ float2 red[2][kTokWaves][TC];
     __shared__ TokQdqShared<S> qsh;
-    __shared__ float tile[HAD ? DK * TC : 1];
+    __shared__ float tile[HAD ? 2 * DK * TC : 1];  // tok_rotate's two tiles
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

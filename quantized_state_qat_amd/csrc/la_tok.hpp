@@ -492,8 +492,9 @@ __device__ __forceinline__ void tok_qdq(float (&s)[S::R], TokQdqShared<S>& sh, i
 // s <- (Hu s) * scale along the key axis (Sylvester butterflies over row bits 1, 2, 4, ...
 // in that order).  A lane's R rows are consecutive and R-aligned, so the stages over row bits
 // below R stay in registers; each higher stage exchanges rows with the lane or wave that holds
-// the partner rows through an LDS tile of DK x TC floats.  Every thread of the workgroup calls
-// it (uniformly).
+// the partner rows through one of two LDS tiles of DK x TC floats, used in turn: a stage
+// writes the tile whose reads ended before the previous stage's barrier, so one barrier per
+// stage (and one on entry) suffices.  Every thread of the workgroup calls it (uniformly).
 template <class S>
 __device__ __forceinline__ void tok_rotate(float (&s)[S::R], float* tile, int w, int lane, float scale) {
     constexpr int DK = S::DK, TC = S::TC, R = S::R;
@@ -509,24 +510,26 @@ __device__ __forceinline__ void tok_rotate(float (&s)[S::R], float* tile, int w,
             }
         }
     }
+    __syncthreads();  // the tiles' previous readers are done
+    int buf = 0;
 #pragma unroll
     for (int h = R; h < DK; h <<= 1) {
-        __syncthreads();  // the previous stage's reads are done
+        float* tb = tile + buf * DK * TC;
+        buf ^= 1;
 #pragma unroll
-        for (int m = 0; m < R; m++) tile[(r0 + m) * TC + c] = s[m];
+        for (int m = 0; m < R; m++) tb[(r0 + m) * TC + c] = s[m];
         __syncthreads();
         // every row of this lane has the same bit h (h >= R): the lower rows add the partner,
         // the upper rows subtract themselves from it
         const bool upper = (r0 & h) != 0;
 #pragma unroll
         for (int m = 0; m < R; m++) {
-            const float p = tile[((r0 + m) ^ h) * TC + c];
+            const float p = tb[((r0 + m) ^ h) * TC + c];
             s[m] = upper ? p - s[m] : s[m] + p;
         }
     }
 #pragma unroll
     for (int m = 0; m < R; m++) s[m] *= scale;
-    __syncthreads();  // the tile is free for its next use
 }
 
 // A rounding point.  ROT (Hadamard mode with per-key gates, whose state is carried unrotated:
