@@ -175,6 +175,7 @@ SLOT_CASES = [
     ("int8g32", 6, 2, 128, 128, "scalar", la.LA_QDQ_INT8_GROUP, 32, 0),
     ("e4m3_kda_dk64", 5, 3, 64, 128, "key", la.LA_QDQ_E4M3_TILE, 64, 0),
     ("wht_int8g16_rotated_state", 4, 2, 128, 64, "scalar", la.LA_QDQ_INT8_GROUP, 16, 2),
+    ("wht_int8g32_kda", 4, 2, 128, 128, "key", la.LA_QDQ_INT8_GROUP, 32, 1),
 ]
 
 

@@ -47,6 +47,7 @@ CASES = [
     # an interval that is not a multiple of 8 keeps the single-sequence calls on the token kernel
     ("kda_e4m3_i12", 64, 128, "key", la.LA_QDQ_E4M3_TILE, 64, 0, 12),
     ("gdn_wht_int8g16_tok", 128, 64, "scalar", la.LA_QDQ_INT8_GROUP, 16, 1, 1),
+    ("kda_wht_int8g32_tok", 128, 128, "key", la.LA_QDQ_INT8_GROUP, 32, 1, 1),
 ]
 
 
