@@ -98,6 +98,7 @@ def _torch_ste_forward(q, k, v, g, beta, S0, gate, mode, group, had, interval):
     (1, oracle.QDQ_INT8, 64, False, 1),
     (0, oracle.QDQ_E4M3, 64, False, 4),
     (0, oracle.QDQ_INT8, 32, True, 1),
+    (1, oracle.QDQ_INT8, 32, True, 1),
 ])
 def test_matches_torch_autograd_ste(oracle_mod, gate, mode, group, had, interval):
     rng = np.random.default_rng(50 + mode)
