@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X FP32 (vector, packed; equal to the FP32 matrix peak)
+BF16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix peak
 METRIC = "token·head state updates/s + % of HBM/VALU roofline, GDN/KDA d=128 QDQ"
 
 
@@ -127,12 +128,36 @@ def bench_long_e4m3(steps=3, warmup=1):
     t = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
                                                 ST, stream=stream), steps, warmup, stream)
     unit = w.d_k * w.d_v * w.B * w.H * w.T
+    workload = "gdn_long_e4m3_64 B=8 H=16 T=4096 d_k=d_v=128 bf16 q/k/v, fp32 g/beta/state, E4M3 tile QDQ every 64 tokens"
+    # matrix-core work the block kernel issues per (workgroup, 16-token block): each of the four
+    # column waves 24 bf16 16x16x32 (projections of the split state), 24 bf16 16x16x16 (the
+    # rank-16 update of the split deltas) and 8 fp32 16x16x4 (deltas and outputs); the producer
+    # 8 bf16 16x16x32 (Gram matrices) and 4 fp32 16x16x4 (the solve)
+    mfma_per_wg_block = 4 * (24 * 2 * 16 * 16 * 32 + 24 * 2 * 16 * 16 * 16 + 8 * 2 * 16 * 16 * 4) \
+        + 8 * 2 * 16 * 16 * 32 + 4 * 2 * 16 * 16 * 4
+    mfma_flops = mfma_per_wg_block * w.B * w.H * (w.d_v // 64) * (w.T // 16)
     fwd = {
-        "workload": "gdn_long_e4m3_64 B=8 H=16 T=4096 d_k=d_v=128 bf16 q/k/v, fp32 g/beta/state, E4M3 tile QDQ every 64 tokens",
+        "workload": workload,
         "kernel": la.la_fwd_kernel_name(c), "ms_per_call": t * 1e3, "updates_per_s": w.B * w.H * w.T / t,
-        "roofline": _fp32_roofline(7.0 * unit, t, "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head) "
-                                                  "against the FP32 peak; the block kernel forms it on the matrix cores "
-                                                  "from exact bf16 products with fp32 sums"),
+        "roofline": _fp32_roofline(7.0 * unit, t, "the chunked (16-token block) form on the matrix cores: algorithmic "
+                                                  "fp32 work of the recurrence (7 d_k d_v per token-head) against the "
+                                                  "FP32 peak, formed from exact bf16 products with fp32 sums"),
+        "mfma_pipe": {"issued_flops_per_call": mfma_flops, "achieved": mfma_flops / t / 1e12, "unit": "TFLOP/s",
+                      "peak_bf16_dense": BF16_MFMA_PEAK_TFLOPS, "frac": mfma_flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                      "note": "matrix-core work actually issued (exact three-part bf16 splits of fp32 operands), "
+                              "against the dense bf16 peak"},
+    }
+    # the same workload on the VALU-only recurrence (single-wave kernel: no matrix cores)
+    cv = la.Config(**{**c.__dict__, "kernel": la.LA_KERNEL_WAVE})
+    t_v = _time_calls(lambda: la.la_recurrent_fwd(cv, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
+                                                  ST, stream=stream), steps, warmup, stream)
+    valu = {
+        "workload": workload,
+        "kernel": la.la_fwd_kernel_name(cv), "ms_per_call": t_v * 1e3, "updates_per_s": w.B * w.H * w.T / t_v,
+        "roofline": _fp32_roofline(7.0 * unit, t_v, "VALU recurrence, one token at a time: 7 d_k d_v flops per "
+                                                    "token-head against the FP32 vector peak (which needs packed "
+                                                    "FP32 FMAs; this build issues unpacked FP32, whose peak is half)"),
+        "frac_of_unpacked_valu_peak": 7.0 * unit / t_v / 1e12 / (FP32_VALU_PEAK_TFLOPS / 2),
     }
 
     c.ckpt_interval = 64
@@ -158,7 +183,7 @@ def bench_long_e4m3(steps=3, warmup=1):
                                                          "token-head (the block path also recomputes every block's "
                                                          "entering state with the block forward, not counted)"),
     }
-    return fwd, fwdbwd
+    return fwd, fwdbwd, valu
 
 
 def bench_kda_long(steps=3, warmup=1):
@@ -397,24 +422,76 @@ def bench_wht_fwdbwd(steps=2, warmup=1):
     }
 
 
-def cpu_baseline(d, w, budget_s=12.0):
-    """The float64 oracle's decode step on the host cores (same generated inputs), repeated on
-    the full batch until about budget_s seconds of CPU time."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed_oracle(run, units_per_run, threads, reps=3):
+    """Median over `reps` runs of the oracle at `threads` OpenMP threads: units per second."""
+    import oracle
+    oracle.set_num_threads(threads)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    med = times[len(times) // 2]
+    return {"threads": threads, "median_s": med, "runs_s": times, "value": units_per_run / med}
+
+
+def cpu_baseline(d, w):
+    """The float64 oracle's decode step on the host cores (same generated inputs): the full
+    B x H batch, median of three runs at all threads (ten steps a run) and at one thread (one
+    step a run)."""
     import oracle
     oracle.build()
+    all_threads = oracle.num_threads()
     args = [d[k].f64 for k in ("q", "k", "v", "g", "beta")]
     S0 = d["S0"].f64
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.fwd(*args, S0, qdq_mode=oracle.QDQ_INT8, group=32, qdq_interval=1)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 5000:
-            break
-    rate = reps * w.B * w.H / el
-    return {"value": rate, "unit": "token·head updates/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} full decode steps of the B={w.B} H={w.H} d={w.d_k} batch in {el:.1f} s "
-                      "(float64 oracle, OpenMP over (sequence, head) units)"}
+
+    def steps(n):
+        return lambda: [oracle.fwd(*args, S0, qdq_mode=oracle.QDQ_INT8, group=32, qdq_interval=1) for _ in range(n)]
+
+    r_all = _timed_oracle(steps(10), 10 * w.B * w.H, all_threads)
+    r_one = _timed_oracle(steps(1), w.B * w.H, 1)
+    oracle.set_num_threads(all_threads)
+    return {"value": r_all["value"], "unit": "token·head updates/s", "cores": all_threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "threads_all": r_all, "threads_1": r_one,
+            "sample": f"decode steps of the full B={w.B} H={w.H} d={w.d_k} batch, INT8 g32: median of 3 runs of "
+                      f"10 steps at {all_threads} threads and of 3 runs of 1 step at 1 thread (float64 oracle, "
+                      "OpenMP over (sequence, head) units)"}
+
+
+def cpu_baseline_long():
+    """The oracle on a bounded sample of the long-sequence E4M3 workload (same generator):
+    all 128 units over the first 256 tokens at all threads, 8 units over the first 256 tokens
+    at one thread; median of three runs each."""
+    import numpy as np
+
+    import oracle
+    import synth
+    oracle.build()
+    all_threads = oracle.num_threads()
+    w = synth.Workload("gdn_long_e4m3_64", B=8, T=256, H=16, d_k=128, d_v=128, gate_dtype="f32", config_id=2)
+    d = synth.generate(w)
+    args = [d[k].f64 for k in ("q", "k", "v", "g", "beta")]
+    one = [np.ascontiguousarray(a[:1, :, :8]) for a in args]
+    kw = dict(qdq_mode=oracle.QDQ_E4M3, group=64, qdq_interval=64)
+    r_all = _timed_oracle(lambda: oracle.fwd(*args, None, **kw), w.B * w.H * w.T, all_threads)
+    r_one = _timed_oracle(lambda: oracle.fwd(*one, None, **kw), 8 * w.T, 1)
+    oracle.set_num_threads(all_threads)
+    return {"value": r_all["value"], "unit": "token·head updates/s", "cores": all_threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "threads_all": r_all, "threads_1": r_one,
+            "sample": "the long-sequence E4M3 workload's first 256 tokens (generator of B=8 H=16 T=4096 d=128, "
+                      "E4M3 every 64 tokens): all 128 units at all threads, 8 units at 1 thread; median of 3 runs"}
 
 
 def profile_mode(steps):
@@ -488,8 +565,11 @@ def main():
         },
     }
     if not args.no_extra:
-        long_fwd, long_fwdbwd = bench_long_e4m3()
-        line["extra"] = {"long_sequence": long_fwd, "long_sequence_fwdbwd": long_fwdbwd, "kda_long_e4m3": bench_kda_long(),
+        long_fwd, long_fwdbwd, long_valu = bench_long_e4m3()
+        if not args.no_cpu:
+            long_valu["cpu_baseline"] = cpu_baseline_long()
+        line["extra"] = {"long_sequence_valu": long_valu, "long_sequence": long_fwd,
+                         "long_sequence_fwdbwd": long_fwdbwd, "kda_long_e4m3": bench_kda_long(),
                          "kda_int8g64_tok": bench_kda_tok(),
                          "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "decode_slots": bench_decode_slots(),
                          "varlen_prefill": bench_varlen()}

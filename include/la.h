@@ -81,6 +81,14 @@ typedef enum {
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 typedef enum { LA_GATE_SCALAR = 0, LA_GATE_KEY = 1 } la_gate;
 typedef enum { LA_QDQ_NONE = 0, LA_QDQ_INT8_GROUP = 1, LA_QDQ_E4M3_TILE = 2 } la_qdq;
+/* Forward kernel choice (see la_fwd_kernel_name): automatic, or one kernel by name. */
+typedef enum {
+    LA_KERNEL_AUTO = 0,
+    LA_KERNEL_BLOCK = 1,
+    LA_KERNEL_WAVE = 2,
+    LA_KERNEL_FAST = 3,
+    LA_KERNEL_TOKEN = 4
+} la_kernel;
 
 typedef struct la_config {
     int32_t B, T, H, d_k, d_v;
@@ -99,12 +107,24 @@ typedef struct la_config {
                               codes act on; chained calls then resume bit for bit and a
                               decode step rotates only the key and query vectors, never the
                               state. */
+    int32_t kernel;        /* la_kernel.  LA_KERNEL_AUTO: the first kernel of la_fwd_kernel_name's
+                              list that serves cfg.  Any other value runs that forward kernel
+                              (la_recurrent_fwd, and the backward's recompute) or returns
+                              LA_ERR_UNSUPPORTED where it cannot serve cfg; the kernels differ
+                              only in the order of floating-point operations between rounding
+                              points.  la_recurrent_fwd_varlen accepts AUTO and TOKEN only;
+                              the decode steps accept AUTO only. */
 } la_config;
 
 /*
- * Forward recurrence over T tokens for every (b, h).
+ * Forward recurrence over T tokens for every (b, h): the training forward of the state QAT
+ * ("GDN state/W QAT foundation", What does this PR do?: the recurrence with per-tile E4M3
+ * state QDQ at 64-token boundaries; "Torch GDN/KDA decode QAT + INT8", What does this PR do?:
+ * the GDN/KDA recurrent path with token state QDQ, INT8 groups and the Hadamard mode).
  * S0 may be NULL (zero initial state).  S_T may be NULL (not written).  ckpts may be NULL;
  * when non-NULL, cfg->ckpt_interval must be >= 1.  T == 0 writes S_T = S0.
+ * Errors: LA_ERR_INVALID_ARG / LA_ERR_UNSUPPORTED / LA_ERR_ALIGNMENT from the host checks
+ * (nothing is enqueued), LA_ERR_HIP if a launch fails.
  */
 la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, const void* v,
                            const void* g, const void* beta, const float* S0, void* o,
@@ -127,9 +147,12 @@ la_status la_recurrent_fwd_varlen(const la_config* cfg, const int32_t* cu_seqlen
                                   const float* S0, void* o, float* S_T, void* stream);
 
 /*
- * One decode token (cfg->T must be 1): S [B][H][d_k][d_v] is read, updated, quantized at
- * the token (a single-token call always ends on a quantization point) and written back in
- * place.  codes/scales are optional (NULL = not written):
+ * One decode token (cfg->T must be 1): the serving-side recurrent step with token state QDQ
+ * ("Torch GDN/KDA decode QAT + INT8", What does this PR do?: the recurrent decode takes BF16
+ * inputs and works in FP32; "Fused Triton GDN/KDA decode QAT", What does this PR do?: the
+ * fused token update with FP8 or INT8 state QDQ).  S [B][H][d_k][d_v] is read, updated,
+ * quantized at the token (a single-token call always ends on a quantization point) and
+ * written back in place; the caller owns S.  codes/scales are optional (NULL = not written):
  *   INT8:  codes int8 [B][H][d_k][d_v], scales float [B][H][d_k][d_v/group]
  *          (Hadamard: codes and scales of H S' with H the unnormalized Sylvester matrix,
  *          i.e. scales are sqrt(d_k) times those of the normalized rotation)
@@ -157,7 +180,10 @@ la_status la_decode_step_slots(const la_config* cfg, const void* q, const void* 
                                int32_t n_slots, void* o, void* codes, float* scales, void* stream);
 
 /*
- * Straight-through backward of la_recurrent_fwd for the upstream gradients dout (o) and
+ * Straight-through backward of la_recurrent_fwd ("GDN state/W QAT foundation", What does
+ * this PR do?: identity straight-through gradients through the state QDQ; "Fused Triton
+ * GDN/KDA decode QAT", What does this PR do?: a checkpointed custom backward with a
+ * differentiable continuation carry, i.e. dS0) for the upstream gradients dout (o) and
  * dS_T (S_T; NULL = zero).  Recomputation runs in chunks of cfg->ckpt_interval (>= 1)
  * tokens from ckpts (the forward's checkpoints with the same interval); ckpts == NULL
  * recomputes them into the workspace first.  Where la_bwd_kernel_name(cfg) is "block", the
@@ -188,14 +214,16 @@ size_t la_bwd_workspace_bytes(const la_config* cfg);
  *            inside a checkpoint chunk: eight waves per 64 columns, rescaled state;
  *   "token"  every other valid configuration (Hadamard, rounding every token, KDA with an
  *            interval or checkpoint spacing that is not a multiple of 8).
- * Returns "" (and sets la_last_error) for an invalid cfg.  The kernels differ only in the
- * order of floating-point operations; every one computes the same recurrence.
+ * With cfg->kernel other than LA_KERNEL_AUTO the named kernel is returned if it serves cfg.
+ * Returns "" (and sets la_last_error) for an invalid cfg or a requested kernel that cannot
+ * serve it.  The kernels differ only in the order of floating-point operations; every one
+ * computes the same recurrence.
  */
 const char* la_fwd_kernel_name(const la_config* cfg);
 
 /*
  * Which backward la_recurrent_bwd_ste runs for cfg (diagnostic; no GPU work, no state):
- *   "block"  the GDN configurations of the "block" forward: the state
+ *   "block"  the GDN configurations whose forward runs the "block" kernel: the state
  *            entering every 16-token block is recomputed into the workspace, then the blocks
  *            are walked last to first on the matrix cores (the block form of the adjoint);
  *   "token"  every other valid configuration: chunks of ckpt_interval tokens recomputed from

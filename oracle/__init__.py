@@ -52,6 +52,8 @@ def _load():
         dp = ctypes.POINTER(ctypes.c_double)
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
         lib.oracle_e4m3_code.restype = ctypes.c_int
@@ -80,6 +82,11 @@ def _d(a) -> np.ndarray:
 def num_threads() -> int:
     """Threads the oracle's parallel loops over (sequence, head) units use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for later calls (OpenMP); the CPU baseline times the oracle at 1 and at all."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def e4m3_value(code: int) -> float:

@@ -59,6 +59,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Sets the number of threads for later calls (no effect without OpenMP). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* FP8 E4M3FN value table                                                                */
 /* ------------------------------------------------------------------------------------ */

@@ -24,6 +24,7 @@ typedef struct {
 } oracle_cfg;
 
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 double oracle_e4m3_value(int code);
 int oracle_e4m3_code(double y);
 void oracle_hadamard(int dk, int dv, const double* X, double* Y);

@@ -20,6 +20,7 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_ALIGNMENT, LA_ERR_WORKSPAC
 LA_F32, LA_BF16 = 0, 1
 LA_GATE_SCALAR, LA_GATE_KEY = 0, 1
 LA_QDQ_NONE, LA_QDQ_INT8_GROUP, LA_QDQ_E4M3_TILE = 0, 1, 2
+LA_KERNEL_AUTO, LA_KERNEL_BLOCK, LA_KERNEL_WAVE, LA_KERNEL_FAST, LA_KERNEL_TOKEN = range(5)
 
 
 class LaError(RuntimeError):
@@ -31,7 +32,7 @@ class LaError(RuntimeError):
 class la_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "H", "d_k", "d_v", "gate", "qdq", "group", "hadamard", "qdq_interval",
-                 "ckpt_interval", "qkv_dtype", "gate_dtype", "out_dtype", "state_rotated")]
+                 "ckpt_interval", "qkv_dtype", "gate_dtype", "out_dtype", "state_rotated", "kernel")]
 
 
 @dataclasses.dataclass
@@ -51,6 +52,7 @@ class Config:
     gate_dtype: int = LA_BF16
     out_dtype: int = LA_F32
     state_rotated: int = 0
+    kernel: int = LA_KERNEL_AUTO
 
     def c(self) -> la_config:
         return la_config(*[int(getattr(self, f.name)) for f in dataclasses.fields(self)])
@@ -108,6 +110,57 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _torch_dtype(code: int):
+    import torch
+    return torch.bfloat16 if code == LA_BF16 else torch.float32
+
+
+def _arg(t, name: str, numel: int, dtypes=None) -> Optional[int]:
+    """Address of a device tensor argument after checking, on the host, that it lives on a
+    GPU, has one of the expected dtypes and holds at least `numel` elements: a host tensor,
+    a wrong dtype or a short buffer would otherwise reach the kernels.  Raw integer
+    addresses are passed through unchecked."""
+    if t is None or isinstance(t, int):
+        return _ptr(t)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if dtypes is not None:
+        dts = dtypes if isinstance(dtypes, (tuple, list)) else (dtypes,)
+        if t.dtype not in dts:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dts)}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the configuration needs {numel}")
+    return _ptr(t)
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _gate_numel(cfg: Config, tokens: int) -> int:
+    return tokens * cfg.H * (cfg.d_k if cfg.gate == LA_GATE_KEY else 1)
+
+
+def _state_numel(cfg: Config, units: int) -> int:
+    return units * cfg.H * cfg.d_k * cfg.d_v
+
+
+def _inputs(cfg: Config, tokens: int, q, k, v, g, beta):
+    """Checked addresses of q, k, v, g, beta for `tokens` token positions per head."""
+    qd, gd = _torch_dtype(cfg.qkv_dtype), _torch_dtype(cfg.gate_dtype)
+    return (_arg(q, "q", tokens * cfg.H * cfg.d_k, qd), _arg(k, "k", tokens * cfg.H * cfg.d_k, qd),
+            _arg(v, "v", tokens * cfg.H * cfg.d_v, qd), _arg(g, "g", _gate_numel(cfg, tokens), gd),
+            _arg(beta, "beta", tokens * cfg.H, gd))
+
+
+def _codes_scales(cfg: Config, codes, scales):
+    import torch
+    n = _state_numel(cfg, cfg.B)
+    nsc = cfg.B * cfg.H * (cfg.d_k * (cfg.d_v // cfg.group) if cfg.qdq == LA_QDQ_INT8_GROUP else cfg.d_v // 64)
+    return (_arg(codes, "codes", n, (torch.int8, torch.uint8)), _arg(scales, "scales", nsc, _f32()))
+
+
 def _stream(stream) -> Optional[int]:
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -124,31 +177,46 @@ def _check(status: int) -> None:
 def la_recurrent_fwd(cfg: Config, q, k, v, g, beta, S0, o, S_T=None, ckpts=None, stream=None) -> None:
     lib = load_library()
     c = cfg.c()
-    _check(lib.la_recurrent_fwd(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ckpts), _stream(stream)))
+    tok = cfg.B * cfg.T
+    nck = (cfg.T + cfg.ckpt_interval - 1) // cfg.ckpt_interval if cfg.ckpt_interval > 0 else 0
+    args = _inputs(cfg, tok, q, k, v, g, beta)
+    _check(lib.la_recurrent_fwd(ctypes.byref(c), *args, _arg(S0, "S0", _state_numel(cfg, cfg.B), _f32()),
+                                _arg(o, "o", tok * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
+                                _arg(S_T, "S_T", _state_numel(cfg, cfg.B), _f32()),
+                                _arg(ckpts, "ckpts", _state_numel(cfg, cfg.B) * nck, _f32()), _stream(stream)))
 
 
 def la_recurrent_fwd_varlen(cfg: Config, cu_seqlens, q, k, v, g, beta, S0, o, S_T=None, stream=None) -> None:
+    import torch
     lib = load_library()
     c = cfg.c()
-    _check(lib.la_recurrent_fwd_varlen(ctypes.byref(c), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                       _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _stream(stream)))
+    args = _inputs(cfg, cfg.T, q, k, v, g, beta)
+    _check(lib.la_recurrent_fwd_varlen(ctypes.byref(c), _arg(cu_seqlens, "cu_seqlens", cfg.B + 1, torch.int32),
+                                       *args, _arg(S0, "S0", _state_numel(cfg, cfg.B), _f32()),
+                                       _arg(o, "o", cfg.T * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
+                                       _arg(S_T, "S_T", _state_numel(cfg, cfg.B), _f32()), _stream(stream)))
 
 
 def la_decode_step(cfg: Config, q, k, v, g, beta, S, o, codes=None, scales=None, stream=None) -> None:
     lib = load_library()
     c = cfg.c()
-    _check(lib.la_decode_step(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                              _ptr(S), _ptr(o), _ptr(codes), _ptr(scales), _stream(stream)))
+    args = _inputs(cfg, cfg.B, q, k, v, g, beta)
+    _check(lib.la_decode_step(ctypes.byref(c), *args, _arg(S, "S", _state_numel(cfg, cfg.B), _f32()),
+                              _arg(o, "o", cfg.B * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
+                              *_codes_scales(cfg, codes, scales), _stream(stream)))
 
 
 def la_decode_step_slots(cfg: Config, q, k, v, g, beta, S_pool, slots, n_slots: int, o, codes=None,
                          scales=None, stream=None) -> None:
+    import torch
     lib = load_library()
     c = cfg.c()
-    _check(lib.la_decode_step_slots(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                    _ptr(S_pool), _ptr(slots), int(n_slots), _ptr(o), _ptr(codes),
-                                    _ptr(scales), _stream(stream)))
+    args = _inputs(cfg, cfg.B, q, k, v, g, beta)
+    _check(lib.la_decode_step_slots(ctypes.byref(c), *args,
+                                    _arg(S_pool, "S_pool", _state_numel(cfg, max(int(n_slots), 0)), _f32()),
+                                    _arg(slots, "slots", cfg.B, torch.int32), int(n_slots),
+                                    _arg(o, "o", cfg.B * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
+                                    *_codes_scales(cfg, codes, scales), _stream(stream)))
 
 
 def la_bwd_workspace_bytes(cfg: Config) -> int:
@@ -160,10 +228,24 @@ def la_recurrent_bwd_ste(cfg: Config, q, k, v, g, beta, S0, ckpts, dout, dS_T, d
                          dbeta, dS0, workspace, ws_bytes: int, stream=None) -> None:
     lib = load_library()
     c = cfg.c()
-    _check(lib.la_recurrent_bwd_ste(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                    _ptr(S0), _ptr(ckpts), _ptr(dout), _ptr(dS_T), _ptr(dq), _ptr(dk),
-                                    _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dS0), _ptr(workspace),
-                                    int(ws_bytes), _stream(stream)))
+    f32 = _f32()
+    tok = cfg.B * cfg.T
+    nck = (cfg.T + cfg.ckpt_interval - 1) // cfg.ckpt_interval if cfg.ckpt_interval > 0 else 0
+    nst = _state_numel(cfg, cfg.B)
+    args = _inputs(cfg, tok, q, k, v, g, beta)
+    if workspace is not None and not isinstance(workspace, int):
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a GPU tensor")
+        if workspace.numel() * workspace.element_size() < int(ws_bytes):
+            raise ValueError(f"workspace holds fewer than the {int(ws_bytes)} bytes passed as ws_bytes")
+    _check(lib.la_recurrent_bwd_ste(ctypes.byref(c), *args, _arg(S0, "S0", nst, f32),
+                                    _arg(ckpts, "ckpts", nst * nck, f32),
+                                    _arg(dout, "dout", tok * cfg.H * cfg.d_v, f32), _arg(dS_T, "dS_T", nst, f32),
+                                    _arg(dq, "dq", tok * cfg.H * cfg.d_k, f32),
+                                    _arg(dk, "dk", tok * cfg.H * cfg.d_k, f32),
+                                    _arg(dv, "dv", tok * cfg.H * cfg.d_v, f32),
+                                    _arg(dg, "dg", _gate_numel(cfg, tok), f32), _arg(dbeta, "dbeta", tok * cfg.H, f32),
+                                    _arg(dS0, "dS0", nst, f32), _ptr(workspace), int(ws_bytes), _stream(stream)))
 
 
 def la_fwd_kernel_name(cfg: Config) -> str:

@@ -640,8 +640,12 @@ __global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArg
 
 bool bwd_mfma_eligible(const la_config& c) {
     if (c.gate != LA_GATE_SCALAR || c.d_v % 64 != 0) return false;
+    // the caller's forward must itself have run on the block kernel, so that the recompute
+    // (the block kernel with 16-token checkpoints) meets the forward's rounding decisions
+    if (fwd_kernel(c) != LA_KERNEL_BLOCK) return false;
     la_config c16 = c;
     c16.ckpt_interval = kBlk;
+    c16.kernel = LA_KERNEL_AUTO;
     if (!fwd_mfma_eligible(c16)) return false;
     // 32-bit buffer offsets over one sequence's upstream gradient (its last block included)
     const size_t span = static_cast<size_t>(c.T + kBlk) * c.H * c.d_v * 4;

@@ -22,18 +22,38 @@ Params make_params(const la_config& c) {
     return p;
 }
 
+la_kernel fwd_kernel(const la_config& c) {
+    switch (c.kernel) {
+        case LA_KERNEL_BLOCK: return fwd_mfma_eligible(c) ? LA_KERNEL_BLOCK : LA_KERNEL_AUTO;
+        case LA_KERNEL_WAVE: return fwd_wave_eligible(c) ? LA_KERNEL_WAVE : LA_KERNEL_AUTO;
+        case LA_KERNEL_FAST: return fwd_fast_eligible(c) ? LA_KERNEL_FAST : LA_KERNEL_AUTO;
+        case LA_KERNEL_TOKEN: return LA_KERNEL_TOKEN;  // serves every valid configuration
+        default: break;
+    }
+    if (fwd_mfma_eligible(c)) return LA_KERNEL_BLOCK;
+    if (fwd_wave_eligible(c)) return LA_KERNEL_WAVE;
+    if (fwd_fast_eligible(c)) return LA_KERNEL_FAST;
+    return LA_KERNEL_TOKEN;
+}
+
 const char* fwd_kernel_name(const la_config& c) {
-    if (fwd_mfma_eligible(c)) return "block";
-    if (fwd_wave_eligible(c)) return "wave";
-    if (fwd_fast_eligible(c)) return "fast";
-    return "token";
+    switch (fwd_kernel(c)) {
+        case LA_KERNEL_BLOCK: return "block";
+        case LA_KERNEL_WAVE: return "wave";
+        case LA_KERNEL_FAST: return "fast";
+        case LA_KERNEL_TOKEN: return "token";
+        default: return "";
+    }
 }
 
 hipError_t launch_fwd(const la_config& c, const FwdArgs& a, hipStream_t s) {
-    if (fwd_mfma_eligible(c)) return launch_fwd_mfma(c, a, s);
-    if (fwd_wave_eligible(c)) return launch_fwd_wave(c, a, s);
-    if (fwd_fast_eligible(c)) return launch_fwd_fast(c, a, s);
-    return launch_fwd_tok(c, a, s);
+    switch (fwd_kernel(c)) {
+        case LA_KERNEL_BLOCK: return launch_fwd_mfma(c, a, s);
+        case LA_KERNEL_WAVE: return launch_fwd_wave(c, a, s);
+        case LA_KERNEL_FAST: return launch_fwd_fast(c, a, s);
+        case LA_KERNEL_TOKEN: return launch_fwd_tok(c, a, s);
+        default: return hipErrorInvalidValue;  // rejected by the ABI before any launch
+    }
 }
 
 hipError_t launch_copy_state(const la_config& c, const float* src, float* dst, hipStream_t s) {

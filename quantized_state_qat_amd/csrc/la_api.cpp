@@ -49,6 +49,10 @@ la_status check_config(const la_config* c, bool decode) {
         return fail(LA_ERR_INVALID_ARG, "state_rotated must be 0 or 1");
     if (c->state_rotated && !c->hadamard)
         return fail(LA_ERR_INVALID_ARG, "state_rotated needs the Hadamard rotation");
+    if (c->kernel < LA_KERNEL_AUTO || c->kernel > LA_KERNEL_TOKEN)
+        return fail(LA_ERR_INVALID_ARG, "unknown kernel %d", c->kernel);
+    if (decode && c->kernel != LA_KERNEL_AUTO)
+        return fail(LA_ERR_INVALID_ARG, "the decode steps choose their kernel themselves (kernel must be 0)");
     switch (c->qdq) {
         case LA_QDQ_NONE:
             if (c->hadamard) return fail(LA_ERR_INVALID_ARG, "hadamard needs the INT8 quantizer");
@@ -117,11 +121,7 @@ WsLayout ws_layout(const la_config& c) {
     return L;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* la_status_string(la_status s) {
+const char* la_status_string_impl(la_status s) {
     switch (s) {
         case LA_OK: return "ok";
         case LA_ERR_INVALID_ARG: return "invalid argument";
@@ -133,15 +133,28 @@ const char* la_status_string(la_status s) {
     return "unknown status";
 }
 
+
+la_status check_kernel(const la_config& c) {
+    if (la::fwd_kernel(c) == LA_KERNEL_AUTO)
+        return fail(LA_ERR_UNSUPPORTED, "the requested forward kernel (%d) cannot serve this configuration", c.kernel);
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_string(la_status s) { return la_status_string_impl(s); }
+
 const char* la_last_error(void) { return g_err; }
 
 const char* la_fwd_kernel_name(const la_config* cfg) {
-    if (check_config(cfg, false) != LA_OK) return "";
+    if (check_config(cfg, false) != LA_OK || check_kernel(*cfg) != LA_OK) return "";
     return la::fwd_kernel_name(*cfg);
 }
 
 const char* la_bwd_kernel_name(const la_config* cfg) {
-    if (check_config(cfg, false) != LA_OK) return "";
+    if (check_config(cfg, false) != LA_OK || check_kernel(*cfg) != LA_OK) return "";
     return la::bwd_mfma_eligible(*cfg) ? "block" : "token";
 }
 
@@ -150,6 +163,7 @@ la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, c
                            float* S_T, float* ckpts, void* stream) {
     CHECK(check_config(cfg, false));
     const la_config& c = *cfg;
+    CHECK(check_kernel(c));
     const bool work = c.B > 0 && c.H > 0 && c.T > 0;
     CHECK(check_ptr(q, "q", work));
     CHECK(check_ptr(k, "k", work));
@@ -176,6 +190,8 @@ la_status la_recurrent_fwd_varlen(const la_config* cfg, const int32_t* cu_seqlen
                                   const float* S0, void* o, float* S_T, void* stream) {
     CHECK(check_config(cfg, false));
     const la_config& c = *cfg;
+    if (c.kernel != LA_KERNEL_AUTO && c.kernel != LA_KERNEL_TOKEN)
+        return fail(LA_ERR_UNSUPPORTED, "packed sequences run on the per-token kernel only (kernel=%d)", c.kernel);
     const bool units = c.B > 0 && c.H > 0;
     const bool work = units && c.T > 0;
     CHECK(check_ptr(cu_seqlens, "cu_seqlens", units));
@@ -247,7 +263,7 @@ la_status la_decode_step_slots(const la_config* cfg, const void* q, const void* 
 }
 
 size_t la_bwd_workspace_bytes(const la_config* cfg) {
-    if (check_config(cfg, false) != LA_OK || cfg->ckpt_interval < 1) return 0;
+    if (check_config(cfg, false) != LA_OK || check_kernel(*cfg) != LA_OK || cfg->ckpt_interval < 1) return 0;
     return ws_layout(*cfg).total;
 }
 
@@ -258,6 +274,7 @@ la_status la_recurrent_bwd_ste(const la_config* cfg, const void* q, const void* 
                                float* dS0, void* workspace, size_t ws_bytes, void* stream) {
     CHECK(check_config(cfg, false));
     const la_config& c = *cfg;
+    CHECK(check_kernel(c));
     if (c.ckpt_interval < 1) return fail(LA_ERR_INVALID_ARG, "backward needs ckpt_interval >= 1");
     const bool units = c.B > 0 && c.H > 0;
     const bool work = units && c.T > 0;

@@ -79,6 +79,10 @@ inline int part_width(const la_config& c) { return 2 * c.d_k + (c.gate == LA_GAT
 inline int n_sub_states(const la_config& c) { return (c.ckpt_interval + 3) / 4; }
 
 hipError_t launch_decode(const la_config& c, const DecodeArgs& a, hipStream_t s);
+// The forward kernel that serves c: c.kernel if it is not LA_KERNEL_AUTO and that kernel
+// serves c (else LA_KERNEL_AUTO: none), otherwise the first of block, wave, fast, token that
+// does.
+la_kernel fwd_kernel(const la_config& c);
 hipError_t launch_fwd(const la_config& c, const FwdArgs& a, hipStream_t s);
 const char* fwd_kernel_name(const la_config& c);
 bool fwd_fast_eligible(const la_config& c);

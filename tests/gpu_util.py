@@ -4,8 +4,10 @@ C ABI, the error metric and the quantization-code comparison protocol.
 Error metric: e(x, ref) = max|x - ref| / max|ref| over a whole tensor.
 Code protocol (teacher forced): at a quantization point the GPU's carried state and the
 oracle's must agree code for code; the only allowed differences are +-1 at near-ties
-(where the oracle's pre-rounding value lies within TIE_WINDOW of a rounding boundary),
-on at most 1e-4 of the codes.
+(where the oracle's pre-rounding value lies within TIE_WINDOW of a rounding boundary; for
+E4M3, neighbouring grid values of one sign with the oracle's x/s within TIE_WINDOW of a grid
+step from their midpoint), on at most 1e-4 of the codes of a whole test (of
+CODE_MIN_SAMPLE codes for smaller tests).
 """
 from __future__ import annotations
 
@@ -19,6 +21,10 @@ import synth
 
 TIE_WINDOW = 2e-3          # distance of x/s to a rounding boundary, in code units
 CODE_MISMATCH_MAX = 1e-4   # fraction of codes allowed to differ (by one, at near-ties)
+# A fraction of 1e-4 cannot resolve a handful of near-tie flips on a small sample, so a
+# tally of fewer codes than this is held to the budget of this many (ten mismatches); every
+# mismatch must still be one step at a near-tie.
+CODE_MIN_SAMPLE = 100_000
 TOL_BF16 = 2e-3            # output/state error bound with bf16 inputs
 TOL_F32 = 1e-5             # output/state error bound with fp32 inputs
 
@@ -148,6 +154,54 @@ def compare_e4m3_values(yg: np.ndarray, yo: np.ndarray, tally: "CodeTally") -> N
         assert np.all(same_side & (np.abs(ia - ib) == 1)), list(zip(a[:8], b[:8]))
 
 
+_E4M3_TABLE = None
+
+
+def e4m3_table() -> np.ndarray:
+    """Value of every E4M3FN code 0..255 from the oracle's code table (0x7F/0xFF, NaN in the
+    format, are never produced and map to the table's own value)."""
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = np.array([oracle.e4m3_value(c) for c in range(256)])
+    return _E4M3_TABLE
+
+
+def e4m3_grid_of_state(X: np.ndarray, tile: int = 64) -> np.ndarray:
+    """Grid values y (E4M3 values, float64) of a dequantized E4M3 tile state [..., d_k, d_v]:
+    per tile of all d_k rows x `tile` columns the largest magnitude is 448 s, so X/s lies
+    within fp32 rounding of a grid value; asserts that it does and returns that value."""
+    X = np.asarray(X, dtype=np.float64)
+    dk, dv = X.shape[-2:]
+    T = X.reshape(*X.shape[:-1], dv // tile, tile)
+    amax = np.abs(T).max(axis=(-3, -1), keepdims=True)
+    s = np.where(amax > 0, amax / 448.0, 1.0)
+    y = (T / s).reshape(X.shape)
+    a = np.abs(y)
+    i = np.clip(np.searchsorted(E4M3_GRID, a), 1, len(E4M3_GRID) - 1)
+    lo, hi = E4M3_GRID[i - 1], E4M3_GRID[i]
+    near = np.where(a - lo <= hi - a, lo, hi)
+    assert np.all(np.abs(a - near) <= 1e-5 * np.maximum(near, 2.0 ** -9)), "state is not on the E4M3 grid"
+    return np.copysign(near, y)
+
+
+def compare_e4m3_point(gpu_state, ora_codes, ora_ypre, tally: "CodeTally", tile: int = 64) -> None:
+    """Teacher-forced comparison of one E4M3 quantization point: the GPU's dequantized state
+    [.., d_k, d_v] against the oracle's codes and pre-rounding values y = x/s for the same
+    entering state.  Every mismatch must be a pair of neighbouring grid values of one sign
+    (or zero against the smallest subnormal) with the oracle's y within TIE_WINDOW of a grid
+    step from their midpoint; counts go to `tally`."""
+    yg = e4m3_grid_of_state(gpu_state, tile)
+    yo = e4m3_table()[np.asarray(ora_codes, dtype=np.int64) & 0xFF]
+    bad = yg != yo
+    tally.add(int(bad.sum()), yg.size)
+    if bad.any():
+        compare_e4m3_values(yg, yo, CodeTally())
+        a, b = np.abs(yg[bad]), np.abs(yo[bad])
+        y = np.abs(np.asarray(ora_ypre, dtype=np.float64)[bad])
+        dist = np.abs(y - 0.5 * (a + b)) / np.abs(a - b)
+        assert dist.max() <= TIE_WINDOW, f"E4M3 mismatch away from a tie (distance {dist.max()} of a step)"
+
+
 def hadamard_n(n: int) -> np.ndarray:
     H = np.array([[1.0]])
     while H.shape[0] < n:
@@ -172,8 +226,9 @@ class CodeTally:
         return self.mismatches / self.total if self.total else 0.0
 
     def check(self) -> float:
-        assert self.fraction <= CODE_MISMATCH_MAX, \
-            f"code mismatch fraction {self.fraction} ({self.mismatches} of {self.total})"
+        allowed = CODE_MISMATCH_MAX * max(self.total, CODE_MIN_SAMPLE)
+        assert self.mismatches <= allowed, \
+            f"code mismatch fraction {self.fraction} ({self.mismatches} of {self.total}, {allowed:.0f} allowed)"
         return self.fraction
 
 

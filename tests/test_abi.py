@@ -181,8 +181,12 @@ def test_fwd_kernel_selection(kw, name):
 @pytest.mark.parametrize("kw,name", [
     (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64), "block"),
     (dict(qdq=la.LA_QDQ_NONE, ckpt_interval=64, gate_dtype=la.LA_BF16), "block"),
-    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=16, ckpt_interval=5), "block"),
-    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=16, qdq_interval=32, ckpt_interval=64, d_v=192), "block"),
+    # the forward of this configuration runs the per-token kernel (a rounding point falls
+    # inside a 5-token checkpoint chunk), so the backward recomputes with it as well
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=16, ckpt_interval=5), "token"),
+    # rounding every 32 tokens inside 64-token checkpoint chunks: the per-token forward
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=16, qdq_interval=32, ckpt_interval=64, d_v=192), "token"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=16, qdq_interval=64, ckpt_interval=32, d_v=192), "block"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=1, ckpt_interval=64), "token"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=24, ckpt_interval=24), "token"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=64, hadamard=1), "token"),
@@ -231,3 +235,90 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([sys.executable, "-c", prog], cwd=root, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.split()[0] == "1", out.stdout
+
+
+@pytest.mark.parametrize("kernel,kw,name", [
+    (la.LA_KERNEL_WAVE, dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64), "wave"),
+    (la.LA_KERNEL_FAST, dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64), "fast"),
+    (la.LA_KERNEL_TOKEN, dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64), "token"),
+    (la.LA_KERNEL_BLOCK, dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64), "block"),
+    (la.LA_KERNEL_TOKEN, dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=1, hadamard=1), "token"),
+    (la.LA_KERNEL_BLOCK, dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=1), ""),
+    (la.LA_KERNEL_WAVE, dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=12), ""),
+    (la.LA_KERNEL_FAST, dict(gate=la.LA_GATE_KEY, qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=16), ""),
+])
+def test_forced_kernel(kernel, kw, name):
+    """A requested forward kernel serves the configuration or is reported unsupported."""
+    base = dict(B=2, T=100, H=2, d_k=128, d_v=128, kernel=kernel)
+    base.update(kw)
+    c = la.Config(**base)
+    assert la.la_fwd_kernel_name(c) == name
+    if name == "":
+        assert "cannot serve" in la.la_last_error()
+        with pytest.raises(la.LaError) as ei:
+            fwd(c)
+        assert ei.value.status == la.LA_ERR_UNSUPPORTED
+        assert la.la_bwd_workspace_bytes(c) == 0
+    elif name != "block":
+        # the block backward needs the block forward's rounding decisions
+        assert la.la_bwd_kernel_name(c) == "token"
+
+
+def test_kernel_field_checks():
+    with pytest.raises(la.LaError) as ei:
+        fwd(cfg(kernel=9))
+    assert ei.value.status == la.LA_ERR_INVALID_ARG
+    with pytest.raises(la.LaError) as ei:
+        la.la_decode_step(cfg(T=1, kernel=la.LA_KERNEL_TOKEN), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == la.LA_ERR_INVALID_ARG
+    with pytest.raises(la.LaError) as ei:
+        la.la_recurrent_fwd_varlen(cfg(kernel=la.LA_KERNEL_BLOCK), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                   stream=0)
+    assert ei.value.status == la.LA_ERR_UNSUPPORTED
+
+
+class FakeDeviceTensor:
+    """Stands in for a GPU tensor in the binding's host-side checks; its address is never
+    dereferenced because every call below is rejected before the library is called."""
+
+    def __init__(self, numel, dtype):
+        self._n, self.dtype, self.is_cuda = numel, dtype, True
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 4
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return FAKE
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    c = cfg(qkv_dtype=la.LA_BF16, gate_dtype=la.LA_BF16)
+    n_qk = c.B * c.T * c.H * c.d_k
+    good = dict(q=FakeDeviceTensor(n_qk, torch.bfloat16), k=FakeDeviceTensor(n_qk, torch.bfloat16),
+                v=FakeDeviceTensor(n_qk, torch.bfloat16), g=FakeDeviceTensor(c.B * c.T * c.H, torch.bfloat16),
+                beta=FakeDeviceTensor(c.B * c.T * c.H, torch.bfloat16), o=FakeDeviceTensor(n_qk, torch.float32))
+    # a host tensor
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fwd(c, **{**good, "q": torch.zeros(n_qk, dtype=torch.bfloat16)})
+    # wrong dtype
+    with pytest.raises(ValueError, match="dtype"):
+        fwd(c, **{**good, "k": FakeDeviceTensor(n_qk, torch.float32)})
+    # too few elements
+    with pytest.raises(ValueError, match="elements"):
+        fwd(c, **{**good, "v": FakeDeviceTensor(n_qk - 1, torch.bfloat16)})
+    with pytest.raises(ValueError, match="elements"):
+        fwd(c, **{**good, "S0": FakeDeviceTensor(c.B * c.H * c.d_k * c.d_v - 1, torch.float32)})
+    with pytest.raises(ValueError, match="dtype"):
+        la.la_decode_step(cfg(T=1), good["q"], good["k"], good["v"], good["g"], good["beta"],
+                          FakeDeviceTensor(c.B * c.H * c.d_k * c.d_v, torch.bfloat16), good["o"], stream=0)
+    with pytest.raises(ValueError, match="int32"):
+        la.la_decode_step_slots(cfg(T=1), good["q"], good["k"], good["v"], good["g"], good["beta"],
+                                FakeDeviceTensor(3 * c.H * c.d_k * c.d_v, torch.float32),
+                                FakeDeviceTensor(c.B, torch.int64), 3, good["o"], stream=0)

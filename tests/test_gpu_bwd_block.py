@@ -106,8 +106,8 @@ def test_block_bwd_steep_gates():
 
 def test_block_bwd_full_size_sampled_unit():
     """GDN B=8 H=16 T=4096 d=128, E4M3 tiles every 64 tokens (the long-sequence workload):
-    the full-size backward, then one unit re-run alone (bit-identical by batch independence)
-    and compared with the oracle over all 4096 tokens."""
+    the full-size backward, then four units spread over the batch and the heads re-run alone
+    (bit-identical by batch independence) and compared with the oracle over all 4096 tokens."""
     w = synth.WORKLOADS[2]
     d = synth.generate(w, with_do=True)
     c = gu.cfg_for(w, d, qdq=E4M3, group=64, qdq_interval=64, ckpt_interval=64)
@@ -115,20 +115,24 @@ def test_block_bwd_full_size_sampled_unit():
     g = gu.run_bwd(c, d, d["do"].f32)
     for n in GRADS:
         assert np.all(np.isfinite(g[n])), n
-    b, h = 5, 11
-    dd = sl(d, b, b + 1, 0, w.T, h, h + 1)
-    dd["do"] = synth.Tensor(f32=np.ascontiguousarray(d["do"].f32[b:b + 1, :, h:h + 1]), dtype="f32")
+    units = [(5, 11), (0, 0), (7, 15), (3, 4)]
+    sub = {(b, h): sl(d, b, b + 1, 0, w.T, h, h + 1) for (b, h) in units}
+    for (b, h) in units:
+        sub[(b, h)]["do"] = synth.Tensor(f32=np.ascontiguousarray(d["do"].f32[b:b + 1, :, h:h + 1]), dtype="f32")
     del d
-    cu = gu.cfg_for(w, dd, qdq=E4M3, group=64, qdq_interval=64, ckpt_interval=64)
-    cu.B, cu.H = 1, 1
-    gu1 = gu.run_bwd(cu, dd, dd["do"].f32)
-    for n in ["dq", "dk", "dv", "dbeta", "dg"]:
-        np.testing.assert_array_equal(gu1[n][0, :, 0], g[n][b, :, h])
-    np.testing.assert_array_equal(gu1["dS0"][0, 0], g["dS0"][b, h])
-    states = block_states(cu, dd, None)
-    ref = oracle.bwd(dd["q"].f64, dd["k"].f64, dd["v"].f64, dd["g"].f64, dd["beta"].f64, None,
-                     dd["do"].f32.astype(np.float64), None, states=states, qdq_mode=E4M3, group=64,
-                     qdq_interval=64)
-    errs = {n: gu.err(gu1[n], ref[n]) for n in GRADS}
-    print(f"unit ({b},{h})", {k: f"{v:.2e}" for k, v in errs.items()})
-    assert max(errs.values()) <= TOL, errs
+    for (b, h) in units:
+        dd = sub[(b, h)]
+        cu = gu.cfg_for(w, dd, qdq=E4M3, group=64, qdq_interval=64, ckpt_interval=64)
+        cu.B, cu.H = 1, 1
+        gu1 = gu.run_bwd(cu, dd, dd["do"].f32)
+        for n in ["dq", "dk", "dv", "dbeta", "dg"]:
+            np.testing.assert_array_equal(gu1[n][0, :, 0], g[n][b, :, h])
+        np.testing.assert_array_equal(gu1["dS0"][0, 0], g["dS0"][b, h])
+        states = block_states(cu, dd, None)
+        ref = oracle.bwd(dd["q"].f64, dd["k"].f64, dd["v"].f64, dd["g"].f64, dd["beta"].f64, None,
+                         dd["do"].f32.astype(np.float64), None, states=states, qdq_mode=E4M3, group=64,
+                         qdq_interval=64)
+        del states
+        errs = {n: gu.err(gu1[n], ref[n]) for n in GRADS}
+        print(f"unit ({b},{h})", {k: f"{v:.2e}" for k, v in errs.items()})
+        assert max(errs.values()) <= TOL, errs
