@@ -102,7 +102,7 @@ def test_decode_matches_oracle(name, B, H, dk, dv, gate, mode, group, had):
             vg = np.vectorize(oracle.e4m3_value)(codes[mism].astype(np.int64))
             vo = np.vectorize(oracle.e4m3_value)(codes_r[mism].astype(np.int64))
             mid = (vg + vo) / 2
-            assert np.all(np.abs(ypre[mism] - mid) <= gu.TIE_WINDOW * np.abs(vg - vo))
+            assert np.all(np.abs(np.abs(ypre[mism]) - np.abs(mid)) <= gu.E4M3_TIE_WINDOW)
         np.testing.assert_allclose(scales.reshape(-1), scales_r.reshape(-1), rtol=2 ** -22)
         assert gu.err(S, Xh) <= (1e-5 if not mism.any() else 1.0 / 8)
 
