@@ -198,6 +198,25 @@ la_status la_recurrent_bwd_ste(const la_config* cfg, const void* q, const void* 
                                float* dq, float* dk, float* dv, float* dg, float* dbeta,
                                float* dS0, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * la_recurrent_bwd_ste without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The workspace is a fixed device array inside the library, la_noalloc_workspace_limit()
+ * bytes (128 MiB) on each GPU the library runs on, held until the process ends.  A cfg whose
+ * la_bwd_workspace_bytes exceeds it returns LA_ERR_WORKSPACE before any HIP call.  The call
+ * allocates nothing.  Every call on a GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (several streams or threads) race and must be serialized by the caller.
+ * Arguments, results and other errors are those of la_recurrent_bwd_ste.
+ */
+la_status la_recurrent_bwd_ste_noalloc(const la_config* cfg, const void* q, const void* k,
+                                       const void* v, const void* g, const void* beta,
+                                       const float* S0, const float* ckpts, const float* dout,
+                                       const float* dS_T, float* dq, float* dk, float* dv,
+                                       float* dg, float* dbeta, float* dS0, void* stream);
+
+/* Bytes of la_recurrent_bwd_ste_noalloc's device array. */
+size_t la_noalloc_workspace_limit(void);
+
 /* Workspace bytes la_recurrent_bwd_ste needs for cfg (0 for an invalid cfg; the requirement
  * includes room for recomputed checkpoints, so it does not depend on whether ckpts is NULL). */
 size_t la_bwd_workspace_bytes(const la_config* cfg);

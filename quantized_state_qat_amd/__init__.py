@@ -85,6 +85,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_recurrent_fwd_varlen.argtypes = [cp] + [vp] * 10
         lib.la_decode_step_slots.restype = ctypes.c_int
         lib.la_decode_step_slots.argtypes = [cp] + [vp] * 7 + [ctypes.c_int32] + [vp] * 4
+        if hasattr(lib, "la_recurrent_bwd_ste_noalloc"):
+            lib.la_recurrent_bwd_ste_noalloc.restype = ctypes.c_int
+            lib.la_recurrent_bwd_ste_noalloc.argtypes = [cp] + [vp] * 16
+            lib.la_noalloc_workspace_limit.restype = ctypes.c_size_t
+            lib.la_noalloc_workspace_limit.argtypes = []
         lib.la_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.la_bwd_workspace_bytes.argtypes = [cp]
         lib.la_status_string.restype = ctypes.c_char_p
@@ -246,6 +251,33 @@ def la_recurrent_bwd_ste(cfg: Config, q, k, v, g, beta, S0, ckpts, dout, dS_T, d
                                     _arg(dv, "dv", tok * cfg.H * cfg.d_v, f32),
                                     _arg(dg, "dg", _gate_numel(cfg, tok), f32), _arg(dbeta, "dbeta", tok * cfg.H, f32),
                                     _arg(dS0, "dS0", nst, f32), _ptr(workspace), int(ws_bytes), _stream(stream)))
+
+
+def la_recurrent_bwd_ste_noalloc(cfg: Config, q, k, v, g, beta, S0, ckpts, dout, dS_T, dq, dk, dv, dg,
+                                 dbeta, dS0, stream=None) -> None:
+    """la_recurrent_bwd_ste with the library's fixed device array as its workspace (no
+    allocation; the workspace must fit la_noalloc_workspace_limit() bytes)."""
+    lib = load_library()
+    c = cfg.c()
+    f32 = _f32()
+    tok = cfg.B * cfg.T
+    nck = (cfg.T + cfg.ckpt_interval - 1) // cfg.ckpt_interval if cfg.ckpt_interval > 0 else 0
+    nst = _state_numel(cfg, cfg.B)
+    args = _inputs(cfg, tok, q, k, v, g, beta)
+    _check(lib.la_recurrent_bwd_ste_noalloc(ctypes.byref(c), *args, _arg(S0, "S0", nst, f32),
+                                            _arg(ckpts, "ckpts", nst * nck, f32),
+                                            _arg(dout, "dout", tok * cfg.H * cfg.d_v, f32),
+                                            _arg(dS_T, "dS_T", nst, f32),
+                                            _arg(dq, "dq", tok * cfg.H * cfg.d_k, f32),
+                                            _arg(dk, "dk", tok * cfg.H * cfg.d_k, f32),
+                                            _arg(dv, "dv", tok * cfg.H * cfg.d_v, f32),
+                                            _arg(dg, "dg", _gate_numel(cfg, tok), f32),
+                                            _arg(dbeta, "dbeta", tok * cfg.H, f32), _arg(dS0, "dS0", nst, f32),
+                                            _stream(stream)))
+
+
+def la_noalloc_workspace_limit() -> int:
+    return int(load_library().la_noalloc_workspace_limit())
 
 
 def la_fwd_kernel_name(cfg: Config) -> str:

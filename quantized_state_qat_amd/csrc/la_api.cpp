@@ -272,6 +272,18 @@ la_status la_recurrent_bwd_ste(const la_config* cfg, const void* q, const void* 
                                const float* ckpts, const float* dout, const float* dS_T,
                                float* dq, float* dk, float* dv, float* dg, float* dbeta,
                                float* dS0, void* workspace, size_t ws_bytes, void* stream) {
+    return la::bwd_ste(cfg, q, k, v, g, beta, S0, ckpts, dout, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace,
+                       ws_bytes, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace la {
+
+la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* S0, const float* ckpts, const float* dout,
+                  const float* dS_T, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                  float* dS0, void* workspace, size_t ws_bytes, WorkspaceProvider provide, void* stream) {
     CHECK(check_config(cfg, false));
     const la_config& c = *cfg;
     CHECK(check_kernel(c));
@@ -298,6 +310,14 @@ la_status la_recurrent_bwd_ste(const la_config* cfg, const void* q, const void* 
     if (!units) return ok();
     if (c.T == 0) return hip_status(la::launch_copy_state(c, dS_T, dS0, s), "copy dS_T -> dS0");
     const WsLayout L = ws_layout(c);
+    if (provide) {
+        // the allocation-free entry point: its fixed device array must hold the workspace
+        if (ws_bytes < L.total)
+            return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, the allocation-free entry point's "
+                        "device array holds %zu", L.total, ws_bytes);
+        CHECK(hip_status(provide(&workspace), "device array of the allocation-free entry point"));
+        CHECK(check_ptr(workspace, "device array", true));
+    }
     if (!workspace || ws_bytes < L.total)
         return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                     workspace ? ws_bytes : static_cast<size_t>(0));
@@ -322,4 +342,4 @@ la_status la_recurrent_bwd_ste(const la_config* cfg, const void* q, const void* 
     return hip_status(la::launch_bwd(c, a, s), "la_recurrent_bwd_ste launch");
 }
 
-}  // extern "C"
+}  // namespace la

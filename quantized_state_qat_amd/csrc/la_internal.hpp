@@ -102,4 +102,14 @@ size_t bwd_mfma_state_bytes(const la_config& c);
 size_t bwd_mfma_part_bytes(const la_config& c);
 hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs& a, hipStream_t s);
 
+// The straight-through backward behind both backward entry points: host checks, workspace
+// layout, launches.  With provide == nullptr the caller's workspace (ws_bytes) is used; else,
+// after every host check and the size check against ws_bytes, provide() supplies the
+// workspace (the allocation-free entry point's device array).
+using WorkspaceProvider = hipError_t (*)(void** workspace);
+la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* S0, const float* ckpts, const float* dout,
+                  const float* dS_T, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                  float* dS0, void* workspace, size_t ws_bytes, WorkspaceProvider provide, void* stream);
+
 }  // namespace la
