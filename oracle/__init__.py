@@ -38,7 +38,7 @@ def build(force: bool = False) -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
                 ("B", "T", "H", "dk", "dv", "gate", "qdq", "group", "hadamard", "qdq_interval",
-                 "ckpt_interval")]
+                 "ckpt_interval", "replay")]
 
 
 _lib = None
@@ -65,6 +65,10 @@ def _load():
                                                        ctypes.c_void_p]
         lib.oracle_fwd.restype = ctypes.c_int
         lib.oracle_fwd.argtypes = [ctypes.POINTER(_Cfg)] + [ctypes.c_void_p] * 9
+        lib.oracle_fwd_ex.restype = ctypes.c_int
+        lib.oracle_fwd_ex.argtypes = [ctypes.POINTER(_Cfg)] + [ctypes.c_void_p] * 11
+        lib.oracle_bf16.restype = ctypes.c_double
+        lib.oracle_bf16.argtypes = [ctypes.c_double]
         lib.oracle_bwd.restype = ctypes.c_int
         lib.oracle_bwd.argtypes = [ctypes.POINTER(_Cfg)] + [ctypes.c_void_p] * 15
         _lib = lib
@@ -123,28 +127,39 @@ def qdq(X: np.ndarray, mode: int, group: int, hadamard: bool = False):
     return Xh, codes, scales, ypre
 
 
-def _cfg(B, T, H, dk, dv, gate, qdq_mode, group, hadamard, qdq_interval, ckpt_interval):
-    return _Cfg(B, T, H, dk, dv, gate, qdq_mode, group, int(hadamard), qdq_interval, ckpt_interval)
+def _cfg(B, T, H, dk, dv, gate, qdq_mode, group, hadamard, qdq_interval, ckpt_interval, replay=False):
+    return _Cfg(B, T, H, dk, dv, gate, qdq_mode, group, int(hadamard), qdq_interval, ckpt_interval, int(replay))
+
+
+def bf16(x: float) -> float:
+    """Nearest BF16 value to fl32(x) (ties to even), the replay windows' entry encoding."""
+    return _load().oracle_bf16(float(x))
 
 
 def fwd(q, k, v, g, beta, S0=None, *, gate=GATE_SCALAR, qdq_mode=QDQ_NONE, group=32,
-        hadamard=False, qdq_interval=1, ckpt_interval=0):
-    """Forward recurrence.  Returns (o, S_T, ckpts or None), all float64."""
+        hadamard=False, qdq_interval=1, ckpt_interval=0, replay=False, dhat=None, return_deltas=False):
+    """Forward recurrence.  Returns (o, S_T, ckpts or None), all float64, and the deltas of
+    every token [B, T, H, d_v] as a fourth item when return_deltas.  replay: replay windows of
+    qdq_interval tokens (BF16 key and update entries between rounding points); dhat
+    [B, T, H, d_v]: the update entries to use at the tokens that are not rounding points (NaN:
+    encode the oracle's own delta), for teacher forcing."""
     q, k, v, g, beta = map(_d, (q, k, v, g, beta))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     S0 = None if S0 is None else _d(S0)
+    dhat = None if dhat is None else _d(dhat)
     o = np.zeros((B, T, H, dv))
     ST = np.zeros((B, H, dk, dv))
+    deltas = np.zeros((B, T, H, dv)) if return_deltas else None
     ck = None
     if ckpt_interval > 0:
         ck = np.zeros((B, H, (T + ckpt_interval - 1) // ckpt_interval, dk, dv))
-    c = _cfg(B, T, H, dk, dv, gate, qdq_mode, group, hadamard, qdq_interval, ckpt_interval)
-    rc = _load().oracle_fwd(ctypes.byref(c), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(o),
-                            _p(ST), _p(ck))
+    c = _cfg(B, T, H, dk, dv, gate, qdq_mode, group, hadamard, qdq_interval, ckpt_interval, replay)
+    rc = _load().oracle_fwd_ex(ctypes.byref(c), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0), _p(o),
+                               _p(ST), _p(ck), _p(dhat), _p(deltas))
     if rc:
         raise ValueError("oracle_fwd rejected its configuration")
-    return o, ST, ck
+    return (o, ST, ck, deltas) if return_deltas else (o, ST, ck)
 
 
 def fwd_varlen(q, k, v, g, beta, cu_seqlens, S0=None, *, gate=GATE_SCALAR, qdq_mode=QDQ_NONE, group=32,
@@ -201,7 +216,7 @@ def decode_slots(q, k, v, g, beta, S_pool, slots, *, gate=GATE_SCALAR, qdq_mode=
 
 
 def bwd(q, k, v, g, beta, S0, dout, dST=None, states=None, *, gate=GATE_SCALAR,
-        qdq_mode=QDQ_NONE, group=32, hadamard=False, qdq_interval=1):
+        qdq_mode=QDQ_NONE, group=32, hadamard=False, qdq_interval=1, replay=False):
     """Straight-through backward.  Returns dict of dq, dk, dv, dg, dbeta, dS0 (float64)."""
     q, k, v, g, beta, dout = map(_d, (q, k, v, g, beta, dout))
     B, T, H, dk = q.shape
@@ -213,7 +228,7 @@ def bwd(q, k, v, g, beta, S0, dout, dST=None, states=None, *, gate=GATE_SCALAR,
         "dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
         "dg": np.zeros_like(g), "dbeta": np.zeros_like(beta), "dS0": np.zeros((B, H, dk, dv)),
     }
-    c = _cfg(B, T, H, dk, dv, gate, qdq_mode, group, hadamard, qdq_interval, 0)
+    c = _cfg(B, T, H, dk, dv, gate, qdq_mode, group, hadamard, qdq_interval, 0, replay)
     rc = _load().oracle_bwd(ctypes.byref(c), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
                             _p(states), _p(dout), _p(dST), _p(out["dq"]), _p(out["dk"]),
                             _p(out["dv"]), _p(out["dg"]), _p(out["dbeta"]), _p(out["dS0"]))

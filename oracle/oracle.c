@@ -36,6 +36,16 @@
  *    sqrt(d_k); the INT8 codec acts on fl32(Y); the carried state is Hn Yhat.
  *  - Backward: identity straight-through gradient through Q (and through the rotations,
  *    since Hn Hn = I); the upstream gradient is dO and optionally dS_T.
+ *  - Replay windows ("Torch GDN/KDA decode QAT + INT8", What does this PR do?: a window of
+ *    one token checkpoints every token; longer windows keep BF16 key and update entries and
+ *    refresh at the window boundary; "Fused Triton GDN/KDA decode QAT", What does this PR
+ *    do?: replay with encode-once factors): the rounding points are those of qdq_interval =
+ *    W (window ends, and the call's last token); at every other token the carried state takes
+ *    the token's rank-1 update from its factors encoded once to BF16,
+ *    S_t = S~ + bf16(k) bf16(delta)^T, each factor rounded from its FP32 value to nearest
+ *    even; the output reads the token's own unencoded update (o_t = S'^T q_t, as always), and
+ *    a window end rounds S' itself (the refresh absorbs its token without an entry).  The
+ *    backward passes straight through the encoding as it does through Q.
  *
  * All functions are reentrant; none allocates beyond plain malloc scratch freed on return.
  */
@@ -98,6 +108,17 @@ int oracle_e4m3_code(double y) {
     else if (dhi < dlo) c = hi;
     else c = (lo % 2 == 0) ? lo : hi;
     return (neg ? 0x80 : 0) | c;
+}
+
+/* Nearest BF16 value to fl32(x), ties to the even significand (x finite). */
+double oracle_bf16(double x) {
+    float f = (float)x;
+    uint32_t b;
+    memcpy(&b, &f, sizeof b);
+    uint32_t lsb = (b >> 16) & 1u;
+    b = (b + 0x7FFFu + lsb) & 0xFFFF0000u;
+    memcpy(&f, &b, sizeof f);
+    return (double)f;
 }
 
 /* ------------------------------------------------------------------------------------ */
@@ -227,6 +248,8 @@ static int check_cfg(const oracle_cfg* c) {
         if (c->hadamard && (c->qdq != ORACLE_QDQ_INT8 || (c->dk & (c->dk - 1)))) return -1;
     }
     if (c->ckpt_interval < 0) return -1;
+    if (c->replay != 0 && c->replay != 1) return -1;
+    if (c->replay && c->qdq == ORACLE_QDQ_NONE) return -1; /* replay windows end in a checkpoint codec */
     return 0;
 }
 
@@ -263,10 +286,31 @@ static void gate_factors(const oracle_cfg* c, const double* g, int b, int t, int
     }
 }
 
+/* The carried state after token t (0-based) from S~, S' = S~ + k delta^T and the token's
+ * factors: Q(S') at a rounding point; in replay mode S~ + bf16(k) dhat^T elsewhere, with dhat
+ * the given entry (dhat_t, when not NULL and not NaN) or bf16(delta); else S'. */
+static void carry(const oracle_cfg* c, int t, const double* St, const double* Sp, const double* kt,
+                  const double* delta, const double* dhat_t, double* S) {
+    const int dk = c->dk, dv = c->dv;
+    if (is_qdq_point(c, t)) {
+        oracle_qdq(c->qdq, c->group, c->hadamard, dk, dv, Sp, S, NULL, NULL, NULL);
+    } else if (c->replay) {
+        for (int i = 0; i < dk; i++) {
+            double kh = oracle_bf16(kt[i]);
+            for (int j = 0; j < dv; j++) {
+                double dh = (dhat_t && !isnan(dhat_t[j])) ? dhat_t[j] : oracle_bf16(delta[j]);
+                S[i * dv + j] = St[i * dv + j] + kh * dh;
+            }
+        }
+    } else {
+        memcpy(S, Sp, sizeof(double) * (size_t)dk * dv);
+    }
+}
+
 /* Forward pass of one (sequence, head) unit. */
 static void unit_fwd(const oracle_cfg* c, int b, int h, const double* q, const double* k,
                      const double* v, const double* g, const double* beta, const double* S0,
-                     double* o, double* ST, double* ckpts) {
+                     double* o, double* ST, double* ckpts, const double* dhat_in, double* delta_out) {
     const int T = c->T, H = c->H, dk = c->dk, dv = c->dv;
     const size_t n = (size_t)dk * dv;
     const int nck = (c->ckpt_interval > 0) ? (T + c->ckpt_interval - 1) / c->ckpt_interval : 0;
@@ -286,25 +330,29 @@ static void unit_fwd(const oracle_cfg* c, int b, int h, const double* q, const d
         gate_factors(c, g, b, t, h, a);
         token_step(dk, dv, S, a, k + tok * dk, q + tok * dk, v + tok * dv, beta[tok], St, Sp, u,
                    delta, o + tok * dv);
-        if (is_qdq_point(c, t))
-            oracle_qdq(c->qdq, c->group, c->hadamard, dk, dv, Sp, S, NULL, NULL, NULL);
-        else
-            memcpy(S, Sp, sizeof(double) * n);
+        if (delta_out) memcpy(delta_out + tok * dv, delta, sizeof(double) * dv);
+        carry(c, t, St, Sp, k + tok * dk, delta, dhat_in ? dhat_in + tok * dv : NULL, S);
     }
     if (ST) memcpy(ST + ((size_t)b * H + h) * n, S, sizeof(double) * n);
     free(S); free(St); free(Sp); free(u); free(delta); free(a);
 }
 
 /* Units are independent, so they are spread over OpenMP threads (when built with it). */
-int oracle_fwd(const oracle_cfg* c, const double* q, const double* k, const double* v,
-               const double* g, const double* beta, const double* S0, double* o, double* ST,
-               double* ckpts) {
+int oracle_fwd_ex(const oracle_cfg* c, const double* q, const double* k, const double* v,
+                  const double* g, const double* beta, const double* S0, double* o, double* ST,
+                  double* ckpts, const double* dhat_in, double* delta_out) {
     if (check_cfg(c)) return -1;
     const int units = c->B * c->H;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int unit = 0; unit < units; unit++)
-        unit_fwd(c, unit / c->H, unit % c->H, q, k, v, g, beta, S0, o, ST, ckpts);
+        unit_fwd(c, unit / c->H, unit % c->H, q, k, v, g, beta, S0, o, ST, ckpts, dhat_in, delta_out);
     return 0;
+}
+
+int oracle_fwd(const oracle_cfg* c, const double* q, const double* k, const double* v,
+               const double* g, const double* beta, const double* S0, double* o, double* ST,
+               double* ckpts) {
+    return oracle_fwd_ex(c, q, k, v, g, beta, S0, o, ST, ckpts, NULL, NULL);
 }
 
 /* ------------------------------------------------------------------------------------ */
@@ -342,10 +390,7 @@ static void unit_bwd(const oracle_cfg* c, int b, int h, const double* q, const d
             gate_factors(c, g, b, t, h, a);
             token_step(dk, dv, S, a, k + tok * dk, q + tok * dk, v + tok * dv, beta[tok], St, Sp,
                        u, delta, otmp);
-            if (is_qdq_point(c, t))
-                oracle_qdq(c->qdq, c->group, c->hadamard, dk, dv, Sp, S, NULL, NULL, NULL);
-            else
-                memcpy(S, Sp, sizeof(double) * n);
+            carry(c, t, St, Sp, k + tok * dk, delta, NULL, S);
         }
         Sprev_base = traj;
     }

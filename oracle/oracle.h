@@ -21,6 +21,8 @@ typedef struct {
     int hadamard;      /* 1: normalized Walsh-Hadamard rotation of the key axis around INT8 */
     int qdq_interval;  /* 1: every token; n: after tokens n, 2n, ... and after the last */
     int ckpt_interval; /* 0: no checkpoints */
+    int replay;        /* 1: replay windows of qdq_interval tokens (BF16 key/update entries
+                          between rounding points); 0: off */
 } oracle_cfg;
 
 int oracle_num_threads(void);
@@ -33,6 +35,13 @@ int oracle_qdq(int qdq, int group, int hadamard, int dk, int dv, const double* X
 int oracle_fwd(const oracle_cfg* c, const double* q, const double* k, const double* v,
                const double* g, const double* beta, const double* S0, double* o, double* ST,
                double* ckpts);
+/* oracle_fwd with two optional arrays [B][T][H][dv]: dhat_in, in replay mode, gives the BF16
+ * update entry to use at each token that is not a rounding point (a NaN entry: encode the
+ * oracle's own delta); delta_out receives every token's delta (float64). */
+int oracle_fwd_ex(const oracle_cfg* c, const double* q, const double* k, const double* v,
+                  const double* g, const double* beta, const double* S0, double* o, double* ST,
+                  double* ckpts, const double* dhat_in, double* delta_out);
+double oracle_bf16(double x);
 int oracle_bwd(const oracle_cfg* c, const double* q, const double* k, const double* v,
                const double* g, const double* beta, const double* S0, const double* states,
                const double* dout, const double* dST, double* dq, double* dk, double* dv,
