@@ -422,6 +422,48 @@ def bench_wht_fwdbwd(steps=2, warmup=1):
     }
 
 
+def bench_replay(steps=2, warmup=1):
+    """Replay windows of 16 tokens on the Hadamard workload's shape (GDN B=4 H=16 T=2048 d=128,
+    bf16 inputs, Hadamard + INT8 group-32 refresh every 16 tokens, BF16 update entries in
+    between): forward with 64-token checkpoints, then the straight-through backward."""
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    w = synth.WORKLOADS[4]
+    d = synth.generate(w, with_do=True)
+    dev = {k: _dev(d[k]) for k in ("q", "k", "v", "g", "beta")}
+    dout = _dev(d["do"])
+    del d
+    c = la.Config(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v, qdq=la.LA_QDQ_INT8_GROUP, group=32, hadamard=1,
+                  qdq_interval=16, replay=1, ckpt_interval=64)
+    o = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
+    ST = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    ck = torch.empty((w.B, w.H, (w.T + 63) // 64, w.d_k, w.d_v), device="cuda")
+    grads = [torch.empty((w.B, w.T, w.H, n), device="cuda") for n in (w.d_k, w.d_k, w.d_v)]
+    dg = torch.empty((w.B, w.T, w.H), device="cuda")
+    dbeta = torch.empty((w.B, w.T, w.H), device="cuda")
+    dS0 = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    nbytes = la.la_bwd_workspace_bytes(c)
+    ws = torch.empty((nbytes + 255) // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    t_f = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
+                                                  ST, ck, stream=stream), steps, warmup, stream)
+    t_b = _time_calls(lambda: la.la_recurrent_bwd_ste(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, ck,
+                                                      dout, None, grads[0], grads[1], grads[2], dg, dbeta, dS0, ws,
+                                                      nbytes, stream=stream), steps, warmup, stream)
+    unit = w.d_k * w.d_v * w.B * w.H * w.T
+    return {
+        "workload": "gdn_fwdbwd_wht_int8g32 shape with replay windows of 16 tokens: Hadamard + INT8 group-32 "
+                    "refresh every 16 tokens, BF16 update entries in between, 64-token checkpoints",
+        "kernel": la.la_fwd_kernel_name(c), "ms_fwd": t_f * 1e3, "ms_bwd": t_b * 1e3,
+        "updates_per_s": w.B * w.H * w.T / (t_f + t_b),
+        "roofline_fwd": _fp32_roofline(7.0 * unit, t_f, "forward: 7 d_k d_v flops per token-head"),
+        "roofline_bwd": _fp32_roofline(22.0 * unit, t_b, "backward: recompute 7 + adjoint 15 d_k d_v per token-head"),
+    }
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -571,7 +613,8 @@ def main():
         line["extra"] = {"long_sequence_valu": long_valu, "long_sequence": long_fwd,
                          "long_sequence_fwdbwd": long_fwdbwd, "kda_long_e4m3": bench_kda_long(),
                          "kda_int8g64_tok": bench_kda_tok(),
-                         "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "decode_slots": bench_decode_slots(),
+                         "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "replay_w16_wht_int8g32": bench_replay(),
+                         "decode_slots": bench_decode_slots(),
                          "varlen_prefill": bench_varlen()}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["d"], w)

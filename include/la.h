@@ -114,6 +114,17 @@ typedef struct la_config {
                               only in the order of floating-point operations between rounding
                               points.  la_recurrent_fwd_varlen accepts AUTO and TOKEN only;
                               the decode steps accept AUTO only. */
+    int32_t replay;        /* 0 | 1: replay windows of qdq_interval tokens ("Torch GDN/KDA decode
+                              QAT + INT8", What does this PR do?: larger windows keep BF16 key and
+                              update entries and refresh at the window boundary; "Fused Triton
+                              GDN/KDA decode QAT": encode-once factors).  The rounding points
+                              stay those of qdq_interval; at every other token the carried state
+                              takes the token's update from its key and delta each rounded once
+                              to BF16 (nearest, ties to even), S_t = S~ + bf16(k) bf16(delta)^T,
+                              while o_t reads the unrounded update.  A window of one token is
+                              rounding after every token.  Needs a quantizer and bf16 q/k/v
+                              (keys are then their own BF16 entries); runs the per-token kernel.
+                              The backward passes straight through the encoding as through Q. */
 } la_config;
 
 /*
@@ -129,6 +140,18 @@ typedef struct la_config {
 la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, const void* v,
                            const void* g, const void* beta, const float* S0, void* o,
                            float* S_T, float* ckpts, void* stream);
+
+/*
+ * la_recurrent_fwd in replay mode (cfg->replay = 1) that also writes every token's update
+ * entry: entries [B][T][H][d_v] bf16 bit patterns, delta_t rounded once to BF16 (nearest,
+ * ties to even), the value the carried state takes at every token that is not a rounding
+ * point (written for the rounding points' tokens too, whose refresh uses delta itself).  For
+ * inspection of the replay encoding; runs the per-token kernel.  LA_ERR_INVALID_ARG without
+ * replay.
+ */
+la_status la_recurrent_fwd_entries(const la_config* cfg, const void* q, const void* k, const void* v,
+                                   const void* g, const void* beta, const float* S0, void* o, float* S_T,
+                                   float* ckpts, void* entries, void* stream);
 
 /*
  * Forward over packed sequences of different lengths (the packed sequence tails of the

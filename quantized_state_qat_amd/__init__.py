@@ -32,7 +32,7 @@ class LaError(RuntimeError):
 class la_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "H", "d_k", "d_v", "gate", "qdq", "group", "hadamard", "qdq_interval",
-                 "ckpt_interval", "qkv_dtype", "gate_dtype", "out_dtype", "state_rotated", "kernel")]
+                 "ckpt_interval", "qkv_dtype", "gate_dtype", "out_dtype", "state_rotated", "kernel", "replay")]
 
 
 @dataclasses.dataclass
@@ -53,6 +53,7 @@ class Config:
     out_dtype: int = LA_F32
     state_rotated: int = 0
     kernel: int = LA_KERNEL_AUTO
+    replay: int = 0
 
     def c(self) -> la_config:
         return la_config(*[int(getattr(self, f.name)) for f in dataclasses.fields(self)])
@@ -81,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_decode_step.argtypes = [cp] + [vp] * 10
         lib.la_recurrent_bwd_ste.restype = ctypes.c_int
         lib.la_recurrent_bwd_ste.argtypes = [cp] + [vp] * 16 + [ctypes.c_size_t, vp]
+        lib.la_recurrent_fwd_entries.restype = ctypes.c_int
+        lib.la_recurrent_fwd_entries.argtypes = [cp] + [vp] * 11
         lib.la_recurrent_fwd_varlen.restype = ctypes.c_int
         lib.la_recurrent_fwd_varlen.argtypes = [cp] + [vp] * 10
         lib.la_decode_step_slots.restype = ctypes.c_int
@@ -189,6 +192,23 @@ def la_recurrent_fwd(cfg: Config, q, k, v, g, beta, S0, o, S_T=None, ckpts=None,
                                 _arg(o, "o", tok * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
                                 _arg(S_T, "S_T", _state_numel(cfg, cfg.B), _f32()),
                                 _arg(ckpts, "ckpts", _state_numel(cfg, cfg.B) * nck, _f32()), _stream(stream)))
+
+
+def la_recurrent_fwd_entries(cfg: Config, q, k, v, g, beta, S0, o, S_T, ckpts, entries, stream=None) -> None:
+    """la_recurrent_fwd in replay mode, also writing each token's BF16 update entry
+    (entries: bf16 [B, T, H, d_v])."""
+    import torch
+    lib = load_library()
+    c = cfg.c()
+    tok = cfg.B * cfg.T
+    nck = (cfg.T + cfg.ckpt_interval - 1) // cfg.ckpt_interval if cfg.ckpt_interval > 0 else 0
+    args = _inputs(cfg, tok, q, k, v, g, beta)
+    _check(lib.la_recurrent_fwd_entries(ctypes.byref(c), *args, _arg(S0, "S0", _state_numel(cfg, cfg.B), _f32()),
+                                        _arg(o, "o", tok * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
+                                        _arg(S_T, "S_T", _state_numel(cfg, cfg.B), _f32()),
+                                        _arg(ckpts, "ckpts", _state_numel(cfg, cfg.B) * nck, _f32()),
+                                        _arg(entries, "entries", tok * cfg.H * cfg.d_v, (torch.bfloat16, torch.int16)),
+                                        _stream(stream)))
 
 
 def la_recurrent_fwd_varlen(cfg: Config, cu_seqlens, q, k, v, g, beta, S0, o, S_T=None, stream=None) -> None:

@@ -192,11 +192,11 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                     TokOps<S, KDA> op;
                     tok_read<S, KDA, true>(op, ring, i, w, lane);
                     float u, dl, o;
-                    tok_step<S, KDA, RC>(s, op, red[rp], w, lane, u, dl, o);
-                    rp ^= 1;
                     const int t = tb + i;
-                    if (QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1))
-                        tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
+                    const bool qpt = QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1);
+                    tok_step<S, KDA, RC>(s, op, red[rp], w, lane, u, dl, o, p.replay && !qpt);
+                    rp ^= 1;
+                    if (qpt) tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
                 }
             }
         }
@@ -231,11 +231,11 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                         TokOps<S, KDA> op;
                         tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
                         float o;
-                        tok_step<S, KDA, RC>(s, op, red[rp], w, lane, uu[i], dd[i], o);
-                        rp ^= 1;
                         const int t = tb + i0 + i;
-                        if (QMODE != LA_QDQ_NONE && i + 1 < n && (((t + 1) % p.qdq_interval) == 0 || t == T - 1))
-                            tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
+                        const bool qpt = QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1);
+                        tok_step<S, KDA, RC>(s, op, red[rp], w, lane, uu[i], dd[i], o, p.replay && !qpt);
+                        rp ^= 1;
+                        if (qpt && i + 1 < n) tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
                     }
                 }
 #pragma unroll

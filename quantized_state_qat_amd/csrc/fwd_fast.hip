@@ -289,6 +289,7 @@ static hipError_t launch_fast_dk(const la_config& c, const FwdArgs& a, hipStream
 
 bool fwd_fast_eligible(const la_config& c) {
     if (c.gate != LA_GATE_SCALAR || c.hadamard) return false;
+    if (c.replay && c.qdq_interval > 1) return false;  // encoded updates: token by token
     if (c.qdq == LA_QDQ_NONE) return true;
     // no rounding decision may fall strictly inside a checkpoint chunk, so that a backward
     // recompute (which uses the general kernel) meets the same decisions at chunk ends

@@ -878,6 +878,7 @@ hipError_t launch_mfma_t(const la_config& c, const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 bool fwd_mfma_eligible(const la_config& c) {
+    if (c.replay && c.qdq_interval > 1) return false;  // encoded updates: token by token
     if (c.gate == LA_GATE_KEY) {
         // per-key gates: the scalar-gate kernels' rounding conditions, without their rescale
         if (c.hadamard) return false;

@@ -19,6 +19,7 @@ TokParams make_tok_params(const la_config& c) {
     p.ckpt_interval = c.ckpt_interval > 0 ? c.ckpt_interval : 1;
     p.nck = n_ckpts(c);
     p.rot = c.hadamard && c.state_rotated;
+    p.replay = c.replay && c.qdq != LA_QDQ_NONE;
     return p;
 }
 
@@ -109,8 +110,10 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
             ck_next += p.ckpt_interval;
         }
         float u, delta, o;
-        tok_step<S, KDA, RC>(s, op, red[t & 1], w, lane, u, delta, o);
+        tok_step<S, KDA, RC>(s, op, red[t & 1], w, lane, u, delta, o, p.replay && t != q_next);
         if (a.o && w == (t & (kTokWaves - 1)) && lane < TC) store_elem(a.o, tok * DV + col, p.out_dt, o);
+        if (a.entries && w == (t & (kTokWaves - 1)) && lane < TC)
+            a.entries[tok * DV + col] = static_cast<uint16_t>(__float_as_uint(bf16_rne(delta)) >> 16);
         if (t + 1 < T) tok_read<S, KDA, false>(op_next, ring, (t + 1) % kTokRing, w, lane);
         if (t == q_next) {
             q_next = min(q_next + p.qdq_interval, T - 1);

@@ -456,6 +456,7 @@ hipError_t launch_wave_dk(const la_config& c, const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 bool fwd_wave_eligible(const la_config& c) {
+    if (c.replay && c.qdq_interval > 1) return false;  // encoded updates: token by token
     if (c.gate == LA_GATE_KEY) {
         // per-key gates: the scalar-gate kernels' rounding conditions, without the rescale
         if (c.hadamard) return false;

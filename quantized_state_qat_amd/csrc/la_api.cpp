@@ -51,6 +51,11 @@ la_status check_config(const la_config* c, bool decode) {
         return fail(LA_ERR_INVALID_ARG, "state_rotated needs the Hadamard rotation");
     if (c->kernel < LA_KERNEL_AUTO || c->kernel > LA_KERNEL_TOKEN)
         return fail(LA_ERR_INVALID_ARG, "unknown kernel %d", c->kernel);
+    if (c->replay != 0 && c->replay != 1) return fail(LA_ERR_INVALID_ARG, "replay must be 0 or 1");
+    if (c->replay && c->qdq == LA_QDQ_NONE)
+        return fail(LA_ERR_INVALID_ARG, "replay windows end in a rounding point: they need a quantizer");
+    if (c->replay && c->qkv_dtype != LA_BF16)
+        return fail(LA_ERR_UNSUPPORTED, "replay windows take bf16 q/k/v (the keys are their own BF16 entries)");
     if (decode && c->kernel != LA_KERNEL_AUTO)
         return fail(LA_ERR_INVALID_ARG, "the decode steps choose their kernel themselves (kernel must be 0)");
     switch (c->qdq) {
@@ -183,6 +188,36 @@ la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, c
     }
     la::FwdArgs a{q, k, v, g, beta, S0, o, S_T, ckpts};
     return hip_status(la::launch_fwd(c, a, s), "la_recurrent_fwd launch");
+}
+
+la_status la_recurrent_fwd_entries(const la_config* cfg, const void* q, const void* k, const void* v,
+                                   const void* g, const void* beta, const float* S0, void* o, float* S_T,
+                                   float* ckpts, void* entries, void* stream) {
+    CHECK(check_config(cfg, false));
+    const la_config& c = *cfg;
+    if (!c.replay) return fail(LA_ERR_INVALID_ARG, "update entries exist in replay mode only (cfg->replay = 1)");
+    CHECK(check_kernel(c));
+    const bool work = c.B > 0 && c.H > 0 && c.T > 0;
+    CHECK(check_ptr(q, "q", work));
+    CHECK(check_ptr(k, "k", work));
+    CHECK(check_ptr(v, "v", work));
+    CHECK(check_ptr(g, "g", work));
+    CHECK(check_ptr(beta, "beta", work));
+    CHECK(check_ptr(o, "o", work));
+    CHECK(check_ptr(entries, "entries", work));
+    CHECK(check_ptr(S0, "S0", false));
+    CHECK(check_ptr(S_T, "S_T", false));
+    CHECK(check_ptr(ckpts, "ckpts", false));
+    if (ckpts && c.ckpt_interval < 1) return fail(LA_ERR_INVALID_ARG, "ckpts given but ckpt_interval < 1");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (c.B == 0 || c.H == 0) return ok();
+    if (c.T == 0) {
+        if (!S_T) return ok();
+        return hip_status(la::launch_copy_state(c, S0, S_T, s), "copy S0 -> S_T");
+    }
+    la::FwdArgs a{q, k, v, g, beta, S0, o, S_T, ckpts};
+    a.entries = static_cast<uint16_t*>(entries);
+    return hip_status(la::launch_fwd_tok(c, a, s), "la_recurrent_fwd_entries launch");
 }
 
 la_status la_recurrent_fwd_varlen(const la_config* cfg, const int32_t* cu_seqlens, const void* q,

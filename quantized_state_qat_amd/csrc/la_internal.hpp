@@ -26,6 +26,9 @@ struct FwdArgs {
     // 32 state values contiguous, per 16-column wave slice) instead of [d_k][d_v]; set by the
     // block backward for its own recompute, never seen by a caller
     int ckpt_lane_major = 0;
+    // token kernel only (replay windows): bf16 bits [B][T][H][d_v] of every token's delta
+    // rounded to BF16, the update entry the replay encoding uses; null = not written
+    uint16_t* entries = nullptr;
 };
 
 struct DecodeArgs {

@@ -35,8 +35,17 @@ struct TokParams {
     int B, T, H, dk, dv;
     int qkv_dt, gate_dt, out_dt;
     int qdq_interval, ckpt_interval, nck;
-    int rot;  // state tensors hold the rotated state (Hadamard mode)
+    int rot;     // state tensors hold the rotated state (Hadamard mode)
+    int replay;  // replay windows: updates between rounding points from BF16-encoded deltas
 };
+
+// Nearest BF16 value of x (ties to the even significand), as a float: the replay windows'
+// once-only encoding of a token's update.  x finite.
+__device__ __forceinline__ float bf16_rne(float x) {
+    uint32_t b = __float_as_uint(x);
+    b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+    return __uint_as_float(b);
+}
 
 // ------------------------------------------------------------------ lane reduce-scatter
 // Reduce N values per lane (x[0..N-1], value i belonging to row i) over aligned groups of
@@ -376,11 +385,13 @@ __device__ __forceinline__ float tok_rows_combine(float x) {
 
 // ------------------------------------------------------------------ one token
 // s: the state entering the token (this lane's rows of its column), advanced in place to
-// S' = a S + ku delta^T (before rounding).  red: this token's reduction buffer (kTokWaves x TC
-// float2).  Returns u = S~^T k, delta and o = S'^T q for the column.
+// S' = a S + ku delta^T (before rounding), or, with enc (a replay-window token that is not a
+// rounding point), to a S + ku bf16(delta)^T.  red: this token's reduction buffer (kTokWaves
+// x TC float2).  Returns u = S~^T k, delta and o = S'^T q for the column (from the unencoded
+// delta).
 template <class S, bool KDA, bool HAD>
 __device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>& op, float2 (*red)[S::TC],
-                                         int w, int lane, float& u, float& delta, float& o) {
+                                         int w, int lane, float& u, float& delta, float& o, bool enc = false) {
     float pk = 0.0f, pq = 0.0f;
 #pragma unroll
     for (int m = 0; m < S::R; m++) {
@@ -409,8 +420,9 @@ __device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>&
     delta = op.beta * (op.vj - P);
     o = __builtin_fmaf(delta, op.kq, Q);
     u = P;
+    const float du = enc ? bf16_rne(delta) : delta;
 #pragma unroll
-    for (int m = 0; m < S::R; m++) s[m] = __builtin_fmaf(op.kr[m], delta, s[m]);
+    for (int m = 0; m < S::R; m++) s[m] = __builtin_fmaf(op.kr[m], du, s[m]);
 }
 
 // ------------------------------------------------------------------ codecs
