@@ -339,6 +339,64 @@ def bench_decode_slots(steps=100, warmup=150):
     }
 
 
+def bench_decode_replay(windows=6, warmup_windows=4, W=16):
+    """Serving decode in replay mode: the decode workload's B=256 x H=16 states as checkpoints
+    with a log of BF16 entries, windows of 16 tokens (Hadamard + INT8 group-32 refresh at each
+    window end, entries appended at the other steps), three (checkpoint, log) sets in rotation
+    so that every step streams its checkpoint from HBM.  Reported per step, averaged over whole
+    windows."""
+    import numpy as np
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    w = synth.WORKLOADS[1]
+    d = synth.generate(w)
+    dev = {k: torch.from_numpy(d[k].bits.astype(np.int16)).view(torch.bfloat16).cuda()
+           for k in ("q", "k", "v", "g", "beta")}
+    B, H, dk, dv = w.B, w.H, w.d_k, w.d_v
+    sets = [dict(S=torch.from_numpy(d["S0"].f32).cuda(),
+                 lk=torch.zeros((B, H, W - 1, dk), dtype=torch.int16, device="cuda"),
+                 ld=torch.zeros((B, H, W - 1, dv), dtype=torch.int16, device="cuda"),
+                 lg=torch.zeros((B, H, W - 1), dtype=torch.float32, device="cuda")) for _ in range(3)]
+    pos = [torch.full((B,), p, dtype=torch.int32, device="cuda") for p in range(W)]
+    o = torch.empty((B, 1, H, dv), device="cuda")
+    c = la.Config(B=B, T=1, H=H, d_k=dk, d_v=dv, qdq=la.LA_QDQ_INT8_GROUP, group=32, hadamard=1, qdq_interval=W,
+                  replay=1)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        st = sets[i % 3]
+        la.la_decode_step_replay(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], st["S"], st["lk"], st["ld"],
+                                 st["lg"], pos[(i // 3) % W], o, stream=stream)
+    n_warm, n = 3 * W * warmup_windows, 3 * W * windows
+    for i in range(n_warm):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / n
+    # algorithmic bytes per step, averaged over a window: the checkpoint read, the window's
+    # entries read (on average (W - 1) / 2 per step), one entry written or (once per window)
+    # the checkpoint written, the token's inputs and output
+    entry = (dk + dv) * 2 + 4
+    per_head = (4 * dk * dv + (W - 1) / 2 * entry + (W - 1) / W * entry + 4 * dk * dv / W
+                + 2 * (2 * dk + dv) + 4 + 4 * dv)
+    nbytes = per_head * B * H
+    return {
+        "workload": f"gdn_decode_int8g32 shape in replay mode: B={B} H={H} d={dk}, windows of {W} tokens, Hadamard "
+                    "+ INT8 group-32 refresh at window ends, BF16 entries between, 3 (checkpoint, log) sets in rotation",
+        "kernel": "decode (replay)", "us_per_step": t * 1e6, "updates_per_s": B * H / t,
+        "roofline": {"bound": "hbm", "achieved": nbytes / t / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nbytes / t / 1e9 / HBM_PEAK_GBS, "bytes_per_step_avg": nbytes},
+    }
+
+
 def bench_varlen(steps=3, warmup=1):
     """Packed prefill: 64 sequences of lengths drawn uniformly from 1..1024 (seeded), H=16,
     d=128, bf16 inputs, GDN with INT8 group-32 rounding after every token."""
@@ -364,7 +422,19 @@ def bench_varlen(steps=3, warmup=1):
     t = _time_calls(lambda: la.la_recurrent_fwd_varlen(c, cu_d, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
                                                        None, o, ST, stream=stream), steps, warmup, stream)
     flops = 7.0 * w.d_k * w.d_v * w.H * T
+    # the packed straight-through backward (checkpoints every 64 tokens recomputed inside)
+    c.ckpt_interval = 64
+    dout = torch.randn((T, w.H, w.d_v), device="cuda")
+    gq, gk, gv = (torch.empty((T, w.H, n), device="cuda") for n in (w.d_k, w.d_k, w.d_v))
+    gg, gb = torch.empty((T, w.H), device="cuda"), torch.empty((T, w.H), device="cuda")
+    dS0 = torch.empty((len(lens), w.H, w.d_k, w.d_v), device="cuda")
+    nbytes = la.la_bwd_varlen_workspace_bytes(c)
+    ws = torch.empty((nbytes + 255) // 4, dtype=torch.float32, device="cuda")
+    t_b = _time_calls(lambda: la.la_recurrent_bwd_ste_varlen(c, cu_d, dev["q"], dev["k"], dev["v"], dev["g"],
+                                                             dev["beta"], None, dout, None, gq, gk, gv, gg, gb, dS0,
+                                                             ws, nbytes, stream=stream), steps, warmup, stream)
     return {
+        "ms_bwd": t_b * 1e3,
         "workload": f"packed prefill, 64 GDN sequences of 1..1024 tokens ({T} in all), H=16, d=128, bf16 inputs, "
                     "INT8 group-32 every token",
         "kernel": "token (packed sequences)", "ms_per_call": t * 1e3, "updates_per_s": w.H * T / t,
@@ -614,7 +684,7 @@ def main():
                          "long_sequence_fwdbwd": long_fwdbwd, "kda_long_e4m3": bench_kda_long(),
                          "kda_int8g64_tok": bench_kda_tok(),
                          "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "replay_w16_wht_int8g32": bench_replay(),
-                         "decode_slots": bench_decode_slots(),
+                         "decode_slots": bench_decode_slots(), "decode_replay_w16": bench_decode_replay(),
                          "varlen_prefill": bench_varlen()}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["d"], w)

@@ -170,6 +170,54 @@ la_status la_recurrent_fwd_varlen(const la_config* cfg, const int32_t* cu_seqlen
                                   const float* S0, void* o, float* S_T, void* stream);
 
 /*
+ * Packed sequences with a per-sequence prefix/suffix boundary ("Torch GDN/KDA decode QAT +
+ * INT8", What does this PR do?: an explicit per-sequence boundary selects a chunked prefill
+ * prefix and a recurrent suffix; suffix gradients flow through the handoff into prefill).
+ * Layouts as in la_recurrent_fwd_varlen (cfg->B sequences packed into cfg->T tokens).  Sequence
+ * b's first prefix_len[b] tokens (int32 [B], device memory, clamped to the sequence) run with
+ * prefix_cfg from S0[b] (NULL = zeros), its rounding points counted from its first token and
+ * the prefix's last token a rounding point; the state there, S_mid[b] (float32
+ * [B][H][d_k][d_v], written, the handoff the backward needs), starts the remaining tokens,
+ * which run with suffix_cfg and end in S_T[b] (NULL = not written).  The two configurations
+ * must agree in B, T, H, d_k, d_v, gate and dtypes; their quantizers, intervals, Hadamard and
+ * replay settings may differ; state_rotated must be 0 in both.  Per-token kernel, two launches.
+ */
+la_status la_recurrent_fwd_split(const la_config* prefix_cfg, const la_config* suffix_cfg,
+                                 const int32_t* cu_seqlens, const int32_t* prefix_len, const void* q,
+                                 const void* k, const void* v, const void* g, const void* beta,
+                                 const float* S0, void* o, float* S_mid, float* S_T, void* stream);
+
+/*
+ * Straight-through backward of la_recurrent_fwd_varlen for the upstream gradients dout
+ * ([T][H][d_v]) and dS_T ([B][H][d_k][d_v]; NULL = zero): every gradient in the packed layout,
+ * dS0 per sequence.  Chunks of cfg->ckpt_interval (>= 1) tokens are recomputed from
+ * checkpoints that the call first recomputes into the workspace (at least
+ * la_bwd_varlen_workspace_bytes(cfg) bytes).  Tokens outside every sequence get zero gradients.
+ */
+la_status la_recurrent_bwd_ste_varlen(const la_config* cfg, const int32_t* cu_seqlens, const void* q,
+                                      const void* k, const void* v, const void* g, const void* beta,
+                                      const float* S0, const float* dout, const float* dS_T, float* dq,
+                                      float* dk, float* dv, float* dg, float* dbeta, float* dS0,
+                                      void* workspace, size_t ws_bytes, void* stream);
+size_t la_bwd_varlen_workspace_bytes(const la_config* cfg);
+
+/*
+ * Straight-through backward of la_recurrent_fwd_split: the suffix backward from S_mid (the
+ * forward's handoff states) for dout and dS_T, whose dS0 is the gradient at the handoff; then
+ * the prefix backward from S0 with that gradient as its dS_T.  Each part recomputes with its
+ * own configuration (ckpt_interval >= 1 in both).  Workspace: at least
+ * la_bwd_split_workspace_bytes(prefix_cfg, suffix_cfg) bytes.
+ */
+la_status la_recurrent_bwd_ste_split(const la_config* prefix_cfg, const la_config* suffix_cfg,
+                                     const int32_t* cu_seqlens, const int32_t* prefix_len, const void* q,
+                                     const void* k, const void* v, const void* g, const void* beta,
+                                     const float* S0, const float* S_mid, const float* dout,
+                                     const float* dS_T, float* dq, float* dk, float* dv, float* dg,
+                                     float* dbeta, float* dS0, void* workspace, size_t ws_bytes,
+                                     void* stream);
+size_t la_bwd_split_workspace_bytes(const la_config* prefix_cfg, const la_config* suffix_cfg);
+
+/*
  * One decode token (cfg->T must be 1): the serving-side recurrent step with token state QDQ
  * ("Torch GDN/KDA decode QAT + INT8", What does this PR do?: the recurrent decode takes BF16
  * inputs and works in FP32; "Fused Triton GDN/KDA decode QAT", What does this PR do?: the
@@ -201,6 +249,30 @@ la_status la_decode_step(const la_config* cfg, const void* q, const void* k, con
 la_status la_decode_step_slots(const la_config* cfg, const void* q, const void* k, const void* v,
                                const void* g, const void* beta, float* S_pool, const int32_t* slots,
                                int32_t n_slots, void* o, void* codes, float* scales, void* stream);
+
+/*
+ * One decode token of a serving batch in replay mode (cfg->replay = 1, cfg->T = 1, window
+ * W = cfg->qdq_interval): the serving side of replay windows ("Torch GDN/KDA decode QAT +
+ * INT8", What does this PR do?: the runtime reconstructs its state from BF16 key/update entries
+ * and refreshes the checkpoint at the window boundary, promoting working values to FP32).
+ * Per sequence b the decode state is the window's checkpoint S[b] [H][d_k][d_v] (float32,
+ * unrotated) and a log of the window's earlier tokens, entries 0 .. pos[b] - 1:
+ *   log_k  bf16 [B][H][W - 1][d_k]   the keys' BF16 bits
+ *   log_d  bf16 [B][H][W - 1][d_v]   the updates delta rounded once to BF16
+ *   log_g  float [B][H][W - 1] (scalar gate) or [B][H][W - 1][d_k] (per-key gates): g
+ *   pos    int32 [B] in device memory: entries already logged (clamped to [0, W - 1])
+ * The call reconstructs the state entering the token in FP32 from the checkpoint and the
+ * entries (S <- diag(exp g_i) S + k_i d_i^T in log order), advances it by the token and writes
+ * o.  If pos[b] < W - 1 the token's entries are appended at index pos[b] and S[b] is left
+ * unchanged; if pos[b] == W - 1 the token ends the window: S[b] <- Q(S') in place (codes and
+ * scales as in la_decode_step, written only then).  The caller advances pos (pos + 1, or 0
+ * after a window end).  Tokens of a window evolve exactly as la_recurrent_fwd's replay
+ * tokens with the same window.  The log pointers may be NULL when W == 1.
+ */
+la_status la_decode_step_replay(const la_config* cfg, const void* q, const void* k, const void* v,
+                                const void* g, const void* beta, float* S, void* log_k, void* log_d,
+                                float* log_g, const int32_t* pos, void* o, void* codes, float* scales,
+                                void* stream);
 
 /*
  * Straight-through backward of la_recurrent_fwd ("GDN state/W QAT foundation", What does

@@ -235,3 +235,102 @@ def bwd(q, k, v, g, beta, S0, dout, dST=None, states=None, *, gate=GATE_SCALAR,
     if rc:
         raise ValueError("oracle_bwd rejected its configuration")
     return out
+
+
+def _seq_range(cu_seqlens, b, T):
+    t0 = min(max(int(cu_seqlens[b]), 0), T)
+    t1 = min(max(int(cu_seqlens[b + 1]), t0), T)
+    return t0, t1
+
+
+def bwd_varlen(q, k, v, g, beta, cu_seqlens, S0, dout, dST=None, *, gate=GATE_SCALAR, qdq_mode=QDQ_NONE, group=32,
+               hadamard=False, qdq_interval=1, replay=False, states=None):
+    """Straight-through backward of fwd_varlen: each sequence's backward on its own tokens
+    ([T, H, ...] packing, sequence b = tokens cu_seqlens[b] .. cu_seqlens[b + 1] - 1, clamped),
+    from S0[b] and dST[b].  states: optional [T, H, d_k, d_v], the carried state entering each
+    packed token (teacher forcing).  Tokens outside every sequence get zero gradients; an empty
+    sequence hands dST through as dS0.  Returns the gradients (packed) and dS0 [B, H, d_k, d_v]."""
+    q, k, v, g, beta, dout = map(_d, (q, k, v, g, beta, dout))
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    B = len(cu_seqlens) - 1
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v), "dg": np.zeros_like(g),
+           "dbeta": np.zeros_like(beta), "dS0": np.zeros((B, H, dk, dv))}
+    for b in range(B):
+        t0, t1 = _seq_range(cu_seqlens, b, T)
+        S0b = None if S0 is None else _d(S0)[b:b + 1]
+        dSTb = None if dST is None else _d(dST)[b:b + 1]
+        if t1 == t0:
+            out["dS0"][b] = 0.0 if dSTb is None else dSTb[0]
+            continue
+        st = None if states is None else _d(states)[None, t0:t1].transpose(0, 2, 1, 3, 4)
+        r = bwd(q[None, t0:t1], k[None, t0:t1], v[None, t0:t1], g[None, t0:t1], beta[None, t0:t1], S0b,
+                dout[None, t0:t1], dSTb, states=st, gate=gate, qdq_mode=qdq_mode, group=group, hadamard=hadamard,
+                qdq_interval=qdq_interval, replay=replay)
+        for n in ("dq", "dk", "dv", "dg", "dbeta"):
+            out[n][t0:t1] = r[n][0]
+        out["dS0"][b] = r["dS0"][0]
+    return out
+
+
+def _split_ranges(cu_seqlens, prefix_len, T):
+    B = len(cu_seqlens) - 1
+    pre, suf = [], []
+    for b in range(B):
+        t0, t1 = _seq_range(cu_seqlens, b, T)
+        mid = min(max(t0 + int(prefix_len[b]), t0), t1)
+        pre.append((t0, mid))
+        suf.append((mid, t1))
+    return pre, suf
+
+
+def _ranges_to_cu(ranges, T):
+    """Packing of sub-ranges into a token index list and a cumulative offset array."""
+    idx = np.concatenate([np.arange(a, b) for a, b in ranges]) if ranges else np.zeros(0, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum([b - a for a, b in ranges])]).astype(np.int64)
+    return idx.astype(np.int64), cu
+
+
+def fwd_split(q, k, v, g, beta, cu_seqlens, prefix_len, S0, prefix_kw, suffix_kw, *, gate=GATE_SCALAR):
+    """Packed sequences cut at a per-sequence boundary (the pages' chunked-prefill prefix and
+    recurrent suffix with the state handed over between them): sequence b's first
+    prefix_len[b] tokens (clamped) run fwd with prefix_kw from S0[b], the rest with suffix_kw
+    from the prefix's final state S_mid[b].  Returns (o [T, H, d_v], S_mid, S_T), float64."""
+    q, k, v, g, beta = map(_d, (q, k, v, g, beta))
+    T, H, dk = q.shape
+    pre, suf = _split_ranges(cu_seqlens, prefix_len, T)
+    o = np.zeros((T, H, v.shape[-1]))
+    ip, cp = _ranges_to_cu(pre, T)
+    o_p, S_mid = fwd_varlen(q[ip], k[ip], v[ip], g[ip], beta[ip], cp, S0, gate=gate, **prefix_kw)
+    o[ip] = o_p
+    is_, cs = _ranges_to_cu(suf, T)
+    o_s, S_T = fwd_varlen(q[is_], k[is_], v[is_], g[is_], beta[is_], cs, S_mid, gate=gate, **suffix_kw)
+    o[is_] = o_s
+    return o, S_mid, S_T
+
+
+def bwd_split(q, k, v, g, beta, cu_seqlens, prefix_len, S0, S_mid, dout, dST, prefix_kw, suffix_kw, *,
+              gate=GATE_SCALAR, states=None):
+    """Straight-through backward of fwd_split: the suffixes' backward from S_mid for dout and
+    dST, whose dS0 is the gradient at the handoff; then the prefixes' backward from S0 with it
+    as their dST.  states: optional [T, H, d_k, d_v] carried states entering each token
+    (teacher forcing).  Returns the packed gradients and dS0."""
+    q, k, v, g, beta, dout = map(_d, (q, k, v, g, beta, dout))
+    T = q.shape[0]
+    pre, suf = _split_ranges(cu_seqlens, prefix_len, T)
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v), "dg": np.zeros_like(g),
+           "dbeta": np.zeros_like(beta)}
+    is_, cs = _ranges_to_cu(suf, T)
+    st_s = None if states is None else _d(states)[is_]
+    r_s = bwd_varlen(q[is_], k[is_], v[is_], g[is_], beta[is_], cs, S_mid, dout[is_], dST, gate=gate, states=st_s,
+                     **suffix_kw)
+    ip, cp = _ranges_to_cu(pre, T)
+    st_p = None if states is None else _d(states)[ip]
+    r_p = bwd_varlen(q[ip], k[ip], v[ip], g[ip], beta[ip], cp, S0, dout[ip], r_s["dS0"], gate=gate, states=st_p,
+                     **prefix_kw)
+    for n in out:
+        out[n][is_] = r_s[n]
+        out[n][ip] = r_p[n]
+    out["dS0"] = r_p["dS0"]
+    out["dS_mid"] = r_s["dS0"]
+    return out

@@ -86,6 +86,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_recurrent_fwd_entries.argtypes = [cp] + [vp] * 11
         lib.la_recurrent_fwd_varlen.restype = ctypes.c_int
         lib.la_recurrent_fwd_varlen.argtypes = [cp] + [vp] * 10
+        lib.la_recurrent_fwd_split.restype = ctypes.c_int
+        lib.la_recurrent_fwd_split.argtypes = [cp, cp] + [vp] * 12
+        lib.la_recurrent_bwd_ste_varlen.restype = ctypes.c_int
+        lib.la_recurrent_bwd_ste_varlen.argtypes = [cp] + [vp] * 16 + [ctypes.c_size_t, vp]
+        lib.la_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_bwd_varlen_workspace_bytes.argtypes = [cp]
+        lib.la_recurrent_bwd_ste_split.restype = ctypes.c_int
+        lib.la_recurrent_bwd_ste_split.argtypes = [cp, cp] + [vp] * 18 + [ctypes.c_size_t, vp]
+        lib.la_bwd_split_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_bwd_split_workspace_bytes.argtypes = [cp, cp]
+        lib.la_decode_step_replay.restype = ctypes.c_int
+        lib.la_decode_step_replay.argtypes = [cp] + [vp] * 14
         lib.la_decode_step_slots.restype = ctypes.c_int
         lib.la_decode_step_slots.argtypes = [cp] + [vp] * 7 + [ctypes.c_int32] + [vp] * 4
         if hasattr(lib, "la_recurrent_bwd_ste_noalloc"):
@@ -229,6 +241,104 @@ def la_decode_step(cfg: Config, q, k, v, g, beta, S, o, codes=None, scales=None,
     _check(lib.la_decode_step(ctypes.byref(c), *args, _arg(S, "S", _state_numel(cfg, cfg.B), _f32()),
                               _arg(o, "o", cfg.B * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
                               *_codes_scales(cfg, codes, scales), _stream(stream)))
+
+
+def _packed_grads(cfg: Config, dq, dk, dv, dg, dbeta, dS0):
+    f32 = _f32()
+    tok = cfg.T
+    return (_arg(dq, "dq", tok * cfg.H * cfg.d_k, f32), _arg(dk, "dk", tok * cfg.H * cfg.d_k, f32),
+            _arg(dv, "dv", tok * cfg.H * cfg.d_v, f32), _arg(dg, "dg", _gate_numel(cfg, tok), f32),
+            _arg(dbeta, "dbeta", tok * cfg.H, f32), _arg(dS0, "dS0", _state_numel(cfg, cfg.B), f32))
+
+
+def _workspace(workspace, ws_bytes):
+    if workspace is not None and not isinstance(workspace, int):
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a GPU tensor")
+        if workspace.numel() * workspace.element_size() < int(ws_bytes):
+            raise ValueError(f"workspace holds fewer than the {int(ws_bytes)} bytes passed as ws_bytes")
+    return _ptr(workspace)
+
+
+def la_recurrent_fwd_split(prefix_cfg: Config, suffix_cfg: Config, cu_seqlens, prefix_len, q, k, v, g, beta, S0, o,
+                           S_mid, S_T=None, stream=None) -> None:
+    """Packed sequences, each cut into a prefix (prefix_cfg) and a suffix (suffix_cfg) at
+    prefix_len[b] tokens; S_mid receives the handoff states."""
+    import torch
+    lib = load_library()
+    cp, cs = prefix_cfg.c(), suffix_cfg.c()
+    cfg = prefix_cfg
+    args = _inputs(cfg, cfg.T, q, k, v, g, beta)
+    n = _state_numel(cfg, cfg.B)
+    _check(lib.la_recurrent_fwd_split(ctypes.byref(cp), ctypes.byref(cs),
+                                      _arg(cu_seqlens, "cu_seqlens", cfg.B + 1, torch.int32),
+                                      _arg(prefix_len, "prefix_len", cfg.B, torch.int32), *args,
+                                      _arg(S0, "S0", n, _f32()),
+                                      _arg(o, "o", cfg.T * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
+                                      _arg(S_mid, "S_mid", n, _f32()), _arg(S_T, "S_T", n, _f32()), _stream(stream)))
+
+
+def la_bwd_varlen_workspace_bytes(cfg: Config) -> int:
+    c = cfg.c()
+    return int(load_library().la_bwd_varlen_workspace_bytes(ctypes.byref(c)))
+
+
+def la_recurrent_bwd_ste_varlen(cfg: Config, cu_seqlens, q, k, v, g, beta, S0, dout, dS_T, dq, dk, dv, dg, dbeta,
+                                dS0, workspace, ws_bytes: int, stream=None) -> None:
+    import torch
+    lib = load_library()
+    c = cfg.c()
+    n = _state_numel(cfg, cfg.B)
+    args = _inputs(cfg, cfg.T, q, k, v, g, beta)
+    _check(lib.la_recurrent_bwd_ste_varlen(ctypes.byref(c), _arg(cu_seqlens, "cu_seqlens", cfg.B + 1, torch.int32),
+                                           *args, _arg(S0, "S0", n, _f32()),
+                                           _arg(dout, "dout", cfg.T * cfg.H * cfg.d_v, _f32()),
+                                           _arg(dS_T, "dS_T", n, _f32()),
+                                           *_packed_grads(cfg, dq, dk, dv, dg, dbeta, dS0),
+                                           _workspace(workspace, ws_bytes), int(ws_bytes), _stream(stream)))
+
+
+def la_bwd_split_workspace_bytes(prefix_cfg: Config, suffix_cfg: Config) -> int:
+    cp, cs = prefix_cfg.c(), suffix_cfg.c()
+    return int(load_library().la_bwd_split_workspace_bytes(ctypes.byref(cp), ctypes.byref(cs)))
+
+
+def la_recurrent_bwd_ste_split(prefix_cfg: Config, suffix_cfg: Config, cu_seqlens, prefix_len, q, k, v, g, beta, S0,
+                               S_mid, dout, dS_T, dq, dk, dv, dg, dbeta, dS0, workspace, ws_bytes: int,
+                               stream=None) -> None:
+    import torch
+    lib = load_library()
+    cp, cs = prefix_cfg.c(), suffix_cfg.c()
+    cfg = prefix_cfg
+    n = _state_numel(cfg, cfg.B)
+    args = _inputs(cfg, cfg.T, q, k, v, g, beta)
+    _check(lib.la_recurrent_bwd_ste_split(ctypes.byref(cp), ctypes.byref(cs),
+                                          _arg(cu_seqlens, "cu_seqlens", cfg.B + 1, torch.int32),
+                                          _arg(prefix_len, "prefix_len", cfg.B, torch.int32), *args,
+                                          _arg(S0, "S0", n, _f32()), _arg(S_mid, "S_mid", n, _f32()),
+                                          _arg(dout, "dout", cfg.T * cfg.H * cfg.d_v, _f32()),
+                                          _arg(dS_T, "dS_T", n, _f32()),
+                                          *_packed_grads(cfg, dq, dk, dv, dg, dbeta, dS0),
+                                          _workspace(workspace, ws_bytes), int(ws_bytes), _stream(stream)))
+
+
+def la_decode_step_replay(cfg: Config, q, k, v, g, beta, S, log_k, log_d, log_g, pos, o, codes=None, scales=None,
+                          stream=None) -> None:
+    """One decode token in replay mode: S holds the window's checkpoint, log_k/log_d (bf16)
+    and log_g (float32) the entries of its earlier tokens, pos (int32 [B]) how many."""
+    import torch
+    lib = load_library()
+    c = cfg.c()
+    W1 = max(cfg.qdq_interval - 1, 0)
+    args = _inputs(cfg, cfg.B, q, k, v, g, beta)
+    nl = cfg.B * cfg.H * W1
+    _check(lib.la_decode_step_replay(ctypes.byref(c), *args, _arg(S, "S", _state_numel(cfg, cfg.B), _f32()),
+                                     _arg(log_k, "log_k", nl * cfg.d_k, (torch.bfloat16, torch.int16)),
+                                     _arg(log_d, "log_d", nl * cfg.d_v, (torch.bfloat16, torch.int16)),
+                                     _arg(log_g, "log_g", nl * (cfg.d_k if cfg.gate == LA_GATE_KEY else 1), _f32()),
+                                     _arg(pos, "pos", cfg.B, torch.int32),
+                                     _arg(o, "o", cfg.B * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
+                                     *_codes_scales(cfg, codes, scales), _stream(stream)))
 
 
 def la_decode_step_slots(cfg: Config, q, k, v, g, beta, S_pool, slots, n_slots: int, o, codes=None,

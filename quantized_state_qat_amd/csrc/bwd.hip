@@ -120,15 +120,35 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int T = p.T, H = p.H, DV = p.dv, C = p.ckpt_interval;
+    const int H = p.H, DV = p.dv, C = p.ckpt_interval;
     const int NB = DV / TC;
     const int col = blk * TC + lane % TC;
     const int r0 = tok_row0<S>(w, lane);
     const size_t bh = static_cast<size_t>(b) * H + h;
     const size_t state_off = bh * DK * DV;
     const size_t wg = bh * NB + blk;
-    const size_t ntok = static_cast<size_t>(p.B) * T * H;
-    const size_t tok0 = static_cast<size_t>(b) * T * H + h;
+    const size_t ntok = static_cast<size_t>(p.ntok);
+    int T = p.T;
+    size_t tok0 = static_cast<size_t>(b) * T * H + h;
+    size_t ck0 = bh * p.nck;  // this unit's first checkpoint
+    if (a.cu_seqlens) {
+        // packed sequences: this one's token range (or one part of it) and checkpoint slots
+        int t_begin, t_end;
+        packed_range(a.cu_seqlens, a.split, a.split_part, b, p.T, t_begin, t_end);
+        T = t_end - t_begin;
+        tok0 = static_cast<size_t>(t_begin) * H + h;
+        ck0 = static_cast<size_t>(h) * p.nck + b + t_begin / C;
+        if (T == 0) {
+            // nothing to walk: dS0 = dS_T (uniform over the workgroup)
+#pragma unroll
+            for (int m = 0; m < R; m++) {
+                const size_t e = state_off + static_cast<size_t>(r0 + m) * DV + col;
+                a.dS0[e] = a.dST ? a.dST[e] : 0.0f;
+            }
+            return;
+        }
+    }
+    const int nck = (T + C - 1) / C;
     const int nsub = (C + kSubTok - 1) / kSubTok;
     float* wsS = a.ws_states + wg * static_cast<size_t>(nsub) * DK * TC;
     const TokInputs in{a.q, a.k, a.v, a.g, a.beta, a.dout};
@@ -157,11 +177,11 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
         __syncthreads();
     };
 
-    fetch(p.nck - 1, 0);
+    fetch(nck - 1, 0);
     __builtin_amdgcn_s_waitcnt(0);
     int rp = 0;
 #pragma unroll 1
-    for (int c = p.nck - 1; c >= 0; c--) {
+    for (int c = nck - 1; c >= 0; c--) {
         const int t0 = c * C, t1 = min(T, t0 + C);
         const int nb = nblocks(c);
         const int last_sub = ((t1 - t0 - 1) / kSubTok) * kSubTok;  // chunk offset of the last stored state
@@ -170,7 +190,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
         // every fourth token (the chunk's first state is its checkpoint)
         {
             float s[R];
-            const float* ck = a.ckpts + (bh * p.nck + c) * DK * DV;
+            const float* ck = a.ckpts + (ck0 + c) * DK * DV;
 #pragma unroll
             for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
 #pragma unroll 1
@@ -213,7 +233,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                 const int i0 = kSubTok * hh, n = min(kSubTok, nt - i0);
                 float s[R];
                 if (j == 0 && hh == 0) {
-                    const float* ck = a.ckpts + (bh * p.nck + c) * DK * DV;
+                    const float* ck = a.ckpts + (ck0 + c) * DK * DV;
 #pragma unroll
                     for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
                 } else {
@@ -266,7 +286,52 @@ __global__ __launch_bounds__(64) void bwd_reduce_kernel(TokParams p, BwdArgs a, 
     constexpr int NV = (DK + 63) / 64;
     const int lane = threadIdx.x;
     const size_t tok = blockIdx.x;
-    const size_t ntok = static_cast<size_t>(p.B) * p.T * p.H;
+    const size_t ntok = static_cast<size_t>(p.ntok);
+    if (a.cu_seqlens) {
+        // packed sequences: the sequence holding this token (the first, should ranges overlap);
+        // a token of no sequence gets zero gradients (from the prefix pass of a split call), a
+        // token outside this call's part is left to the other part's pass
+        const int t = static_cast<int>(tok / p.H);
+        int owner = -1;
+        bool in_part = false;
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            const int bb = b0 + lane;
+            bool hit = false, hitp = false;
+            if (bb < p.B) {
+                int beg, end;
+                packed_range(a.cu_seqlens, nullptr, 0, bb, p.T, beg, end);
+                hit = t >= beg && t < end;
+                if (hit && a.split) {
+                    packed_range(a.cu_seqlens, a.split, a.split_part, bb, p.T, beg, end);
+                    hitp = t >= beg && t < end;
+                } else {
+                    hitp = hit;
+                }
+            }
+            const uint64_t m = __ballot(hit);
+            if (m) {
+                const int first = __builtin_ctzll(m);
+                owner = b0 + first;
+                in_part = __shfl(static_cast<int>(hitp), first) != 0;
+                break;
+            }
+        }
+        if (owner < 0) {
+            if (a.split && a.split_part != 0) return;
+            for (int i = lane; i < DK; i += 64) {
+                a.dq[tok * DK + i] = 0.0f;
+                a.dk[tok * DK + i] = 0.0f;
+                if (KDA) a.dg[tok * DK + i] = 0.0f;
+            }
+            for (int i = lane; i < p.dv; i += 64) a.dv[tok * p.dv + i] = 0.0f;
+            if (lane == 0) {
+                if (!KDA) a.dg[tok] = 0.0f;
+                a.dbeta[tok] = 0.0f;
+            }
+            return;
+        }
+        if (!in_part) return;
+    }
     float x1[NV], x2[NV];
 #pragma unroll
     for (int j = 0; j < NV; j++) {
@@ -335,13 +400,17 @@ namespace {
 
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
 hipError_t launch_bwd_t(const la_config& c, const BwdArgs& a, hipStream_t s) {
-    const TokParams p = make_tok_params(c);
+    TokParams p = make_tok_params(c);
+    if (a.cu_seqlens) {
+        p.nck = varlen_ckpt_slots(c);
+        p.ntok = static_cast<long>(c.T) * c.H;
+    }
     constexpr int TC = tok_tile_cols(DK, QMODE, G);
     dim3 grid(c.d_v / TC, c.H, c.B);
     hipLaunchKernelGGL((bwd_tok_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(kTokThreads), 0, s, p, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t ntok = static_cast<size_t>(c.B) * c.T * c.H;
+    const size_t ntok = static_cast<size_t>(p.ntok);
     if (ntok == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_reduce_kernel<DK, HAD && !KDA, KDA>), dim3(static_cast<unsigned>(ntok)), dim3(64), 0, s, p, a,
                        c.d_v / TC);

@@ -112,11 +112,11 @@ __global__ __launch_bounds__(16 * (DK / R)) void decode_kernel(DecParams p, Deco
     float* Srow = a.S + (stok * DK + static_cast<size_t>(rg) * R) * DV + col0;
 
     // token vectors first, so that waiting for them does not wait for the state
-    float kk = 0.f, qv = 0.f, ai = 0.f;
+    float kk = 0.f, qv = 0.f, ai = 0.f, gv = 0.f;
     if (tid < DK) {
         kk = load_elem(a.k, tok * DK + tid, p.qkv_dt);
         qv = load_elem(a.q, tok * DK + tid, p.qkv_dt);
-        float gv = KDA ? load_elem(a.g, tok * DK + tid, p.gate_dt) : load_elem(a.g, tok, p.gate_dt);
+        gv = KDA ? load_elem(a.g, tok * DK + tid, p.gate_dt) : load_elem(a.g, tok, p.gate_dt);
         ai = expf(gv);
     }
     const float beta = load_elem(a.beta, tok, p.gate_dt);
@@ -124,6 +124,64 @@ __global__ __launch_bounds__(16 * (DK / R)) void decode_kernel(DecParams p, Deco
     float4 s[R];
 #pragma unroll
     for (int m = 0; m < R; m++) s[m] = load_nt(Srow + static_cast<size_t>(m) * DV);
+
+    // replay windows: the state entering the token is the window's checkpoint advanced by the
+    // logged entries of its earlier tokens, S <- diag(exp g_i) S + k_i d_i^T in log order
+    // (the carried update of the forward's replay tokens); pos is uniform per workgroup
+    const int W1 = a.window - 1;
+    const int pos = a.pos ? min(max(a.pos[b], 0), W1) : W1;
+    const int npos = a.pos ? pos : 0;
+    const size_t lbase = tok * static_cast<size_t>(W1 > 0 ? W1 : 1);
+    // one entry's operands for this thread: its R rows of the key (R consecutive bf16 values,
+    // one load), its four columns of the update (one 8-byte load) and the gate(s); loaded one
+    // entry ahead of use so the loads overlap the previous entry's arithmetic
+    struct Ent {
+        uint32_t kw[(R + 1) / 2];
+        uint2 dw;
+        float g[KDA ? R : 1];
+    };
+    auto load_ent = [&](int i, Ent& en) __attribute__((always_inline)) {
+        const size_t e = lbase + i;
+        const uint16_t* kp = a.log_k + e * DK + rg * R;
+        if constexpr (R == 8) {
+            const uint4 x = *reinterpret_cast<const uint4*>(kp);
+            en.kw[0] = x.x; en.kw[1] = x.y; en.kw[2] = x.z; en.kw[3] = x.w;
+        } else if constexpr (R == 4) {
+            const uint2 x = *reinterpret_cast<const uint2*>(kp);
+            en.kw[0] = x.x; en.kw[1] = x.y;
+        } else if constexpr (R == 2) {
+            en.kw[0] = *reinterpret_cast<const uint32_t*>(kp);
+        } else {
+            en.kw[0] = *kp;
+        }
+        en.dw = *reinterpret_cast<const uint2*>(a.log_d + e * DV + col0);
+        if constexpr (KDA) {
+#pragma unroll
+            for (int m = 0; m < R; m++) en.g[m] = a.log_g[e * DK + rg * R + m];
+        } else {
+            en.g[0] = a.log_g[e];
+        }
+    };
+    Ent cur, nxt;
+    if (npos > 0) load_ent(0, cur);
+#pragma unroll 1
+    for (int i = 0; i < npos; i++) {
+        if (i + 1 < npos) load_ent(i + 1, nxt);
+        const float4 dh = make_float4(bf16_bits_to_f32(cur.dw.x & 0xFFFFu), bf16_bits_to_f32(cur.dw.x >> 16),
+                                      bf16_bits_to_f32(cur.dw.y & 0xFFFFu), bf16_bits_to_f32(cur.dw.y >> 16));
+        const float ga = KDA ? 1.0f : expf(cur.g[0]);
+#pragma unroll
+        for (int m = 0; m < R; m++) {
+            const float ar = KDA ? expf(cur.g[m]) : ga;
+            const uint32_t kb = R == 1 ? cur.kw[0] : ((m & 1) ? (cur.kw[m / 2] >> 16) : (cur.kw[m / 2] & 0xFFFFu));
+            const float kr = bf16_bits_to_f32(kb);
+            s[m].x = __builtin_fmaf(kr, dh.x, ar * s[m].x);
+            s[m].y = __builtin_fmaf(kr, dh.y, ar * s[m].y);
+            s[m].z = __builtin_fmaf(kr, dh.z, ar * s[m].z);
+            s[m].w = __builtin_fmaf(kr, dh.w, ar * s[m].w);
+        }
+        cur = nxt;
+    }
 
     if (tid < DK) {
         sm.k[tid] = kk;
@@ -194,6 +252,23 @@ __global__ __launch_bounds__(16 * (DK / R)) void decode_kernel(DecParams p, Deco
         const float4 o = make_float4(__builtin_fmaf(dl.x, kq, r.x), __builtin_fmaf(dl.y, kq, r.y),
                                      __builtin_fmaf(dl.z, kq, r.z), __builtin_fmaf(dl.w, kq, r.w));
         store4(a.o, tok * DV + col0, p.out_dt, o);
+    }
+    if (a.pos && pos < W1) {
+        // a replay token inside the window: append its entries (delta rounded once to BF16, the
+        // key's BF16 bits, the log gate); the checkpoint is left as it is
+        const size_t e = lbase + pos;
+        if (rg == 0) {
+            uint2 dw;
+            dw.x = static_cast<uint32_t>(f32_to_bf16_bits(dl.x)) | (static_cast<uint32_t>(f32_to_bf16_bits(dl.y)) << 16);
+            dw.y = static_cast<uint32_t>(f32_to_bf16_bits(dl.z)) | (static_cast<uint32_t>(f32_to_bf16_bits(dl.w)) << 16);
+            *reinterpret_cast<uint2*>(a.log_d + e * DV + col0) = dw;
+        }
+        if (blk == 0 && tid < DK) {
+            a.log_k[e * DK + tid] = f32_to_bf16_bits(kk);
+            if (KDA) a.log_g[e * DK + tid] = gv;
+            else if (tid == 0) a.log_g[e] = gv;
+        }
+        return;
     }
 
     // S' = diag(a) S + k delta^T

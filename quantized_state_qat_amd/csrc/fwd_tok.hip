@@ -20,6 +20,7 @@ TokParams make_tok_params(const la_config& c) {
     p.nck = n_ckpts(c);
     p.rot = c.hadamard && c.state_rotated;
     p.replay = c.replay && c.qdq != LA_QDQ_NONE;
+    p.ntok = static_cast<long>(c.B) * c.T * c.H;
     return p;
 }
 
@@ -41,12 +42,15 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
     const int H = p.H, DV = p.dv;
     int T = p.T;
     size_t tok0 = static_cast<size_t>(b) * T * H + h;  // token 0 of this (b, h)
+    size_t ck0 = (static_cast<size_t>(b) * H + h) * p.nck;  // its first checkpoint
     if (a.cu_seqlens) {
-        // packed sequences: this one's tokens, clamped to the packed length
-        const int t_begin = min(max(a.cu_seqlens[b], 0), p.T);
-        const int t_end = min(max(a.cu_seqlens[b + 1], t_begin), p.T);
+        // packed sequences: this one's tokens (or one part of them), clamped to the packed
+        // length; checkpoints in the packed slot layout
+        int t_begin, t_end;
+        packed_range(a.cu_seqlens, a.split, a.split_part, b, p.T, t_begin, t_end);
         T = t_end - t_begin;
         tok0 = static_cast<size_t>(t_begin) * H + h;
+        ck0 = static_cast<size_t>(h) * p.nck + b + t_begin / p.ckpt_interval;
     }
     const int col = blk * TC + lane % TC;
     const int r0 = tok_row0<S>(w, lane);
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
         }
         if (t == ck_next) {
             // checkpoints hold the carried state as the loop carries it (rotated in Hadamard mode)
-            float* dst = a.ckpts + (bh * p.nck + t / p.ckpt_interval) * DK * DV;
+            float* dst = a.ckpts + (ck0 + t / p.ckpt_interval) * DK * DV;
 #pragma unroll
             for (int m = 0; m < R; m++) dst[static_cast<size_t>(r0 + m) * DV + col] = s[m];
             ck_next += p.ckpt_interval;
@@ -138,7 +142,12 @@ namespace {
 template <int DK, int QMODE, int G, bool HAD, bool KDA>
 hipError_t launch_tok_t(const la_config& c, const FwdArgs& a, hipStream_t s) {
     dim3 grid(c.d_v / tok_tile_cols(DK, QMODE, G), c.H, c.B);
-    hipLaunchKernelGGL((fwd_tok_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(kTokThreads), 0, s, make_tok_params(c), a);
+    TokParams p = make_tok_params(c);
+    if (a.cu_seqlens) {
+        p.nck = varlen_ckpt_slots(c);
+        p.ntok = static_cast<long>(c.T) * c.H;
+    }
+    hipLaunchKernelGGL((fwd_tok_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(kTokThreads), 0, s, p, a);
     return hipGetLastError();
 }
 

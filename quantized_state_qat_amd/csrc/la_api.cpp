@@ -126,6 +126,20 @@ WsLayout ws_layout(const la_config& c) {
     return L;
 }
 
+// Packed sequences (token backward only): sub-states per workgroup (B sequences), partial
+// row sums per value tile and packed token-head, checkpoints in the packed slot layout.
+WsLayout ws_layout_varlen(const la_config& c) {
+    WsLayout L;
+    const size_t tc = static_cast<size_t>(la::tok_tile_cols(c.d_k, c.qdq, c.group));
+    const size_t tiles = static_cast<size_t>(la::tok_tiles(c));
+    const size_t nwg = static_cast<size_t>(c.B) * c.H * tiles;
+    L.states = 0;
+    L.part = round_up(nwg * static_cast<size_t>(la::n_sub_states(c)) * c.d_k * tc * sizeof(float));
+    L.ckpts = L.part + round_up(tiles * static_cast<size_t>(c.T) * c.H * la::part_width(c) * sizeof(float));
+    L.total = L.ckpts + round_up(static_cast<size_t>(c.H) * la::varlen_ckpt_slots(c) * c.d_k * c.d_v * sizeof(float));
+    return L;
+}
+
 const char* la_status_string_impl(la_status s) {
     switch (s) {
         case LA_OK: return "ok";
@@ -297,6 +311,126 @@ la_status la_decode_step_slots(const la_config* cfg, const void* q, const void* 
     return hip_status(la::launch_decode(c, a, static_cast<hipStream_t>(stream)), "la_decode_step_slots launch");
 }
 
+la_status la_decode_step_replay(const la_config* cfg, const void* q, const void* k, const void* v,
+                                const void* g, const void* beta, float* S, void* log_k, void* log_d,
+                                float* log_g, const int32_t* pos, void* o, void* codes, float* scales,
+                                void* stream) {
+    CHECK(check_config(cfg, true));
+    const la_config& c = *cfg;
+    if (!c.replay) return fail(LA_ERR_INVALID_ARG, "la_decode_step_replay needs cfg->replay = 1");
+    if (c.hadamard && c.state_rotated)
+        return fail(LA_ERR_UNSUPPORTED, "replay decode carries the unrotated state (state_rotated must be 0)");
+    const bool work = c.B > 0 && c.H > 0;
+    const bool logs = work && c.qdq_interval > 1;
+    CHECK(check_ptr(q, "q", work));
+    CHECK(check_ptr(k, "k", work));
+    CHECK(check_ptr(v, "v", work));
+    CHECK(check_ptr(g, "g", work));
+    CHECK(check_ptr(beta, "beta", work));
+    CHECK(check_ptr(S, "S", work));
+    CHECK(check_ptr(o, "o", work));
+    CHECK(check_ptr(pos, "pos", work));
+    CHECK(check_ptr(log_k, "log_k", logs));
+    CHECK(check_ptr(log_d, "log_d", logs));
+    CHECK(check_ptr(log_g, "log_g", logs));
+    CHECK(check_ptr(codes, "codes", false));
+    CHECK(check_ptr(scales, "scales", false));
+    if (!work) return ok();
+    la::DecodeArgs a{q, k, v, g, beta, S, o, codes, scales};
+    a.pos = pos;
+    a.log_k = static_cast<uint16_t*>(log_k);
+    a.log_d = static_cast<uint16_t*>(log_d);
+    a.log_g = log_g;
+    a.window = c.qdq_interval;
+    return hip_status(la::launch_decode(c, a, static_cast<hipStream_t>(stream)), "la_decode_step_replay launch");
+}
+
+size_t la_bwd_varlen_workspace_bytes(const la_config* cfg) {
+    if (check_config(cfg, false) != LA_OK || cfg->ckpt_interval < 1) return 0;
+    if (cfg->kernel != LA_KERNEL_AUTO && cfg->kernel != LA_KERNEL_TOKEN) return 0;
+    return ws_layout_varlen(*cfg).total;
+}
+
+la_status la_recurrent_bwd_ste_varlen(const la_config* cfg, const int32_t* cu_seqlens, const void* q,
+                                      const void* k, const void* v, const void* g, const void* beta,
+                                      const float* S0, const float* dout, const float* dS_T, float* dq,
+                                      float* dk, float* dv, float* dg, float* dbeta, float* dS0,
+                                      void* workspace, size_t ws_bytes, void* stream) {
+    CHECK(check_config(cfg, false));
+    return la::bwd_varlen(*cfg, cu_seqlens, nullptr, 0, q, k, v, g, beta, S0, dout, dS_T, dq, dk, dv, dg, dbeta,
+                          dS0, workspace, ws_bytes, stream);
+}
+
+la_status la_recurrent_fwd_split(const la_config* prefix_cfg, const la_config* suffix_cfg,
+                                 const int32_t* cu_seqlens, const int32_t* prefix_len, const void* q,
+                                 const void* k, const void* v, const void* g, const void* beta,
+                                 const float* S0, void* o, float* S_mid, float* S_T, void* stream) {
+    CHECK(la::check_split(prefix_cfg, suffix_cfg));
+    const la_config& c = *prefix_cfg;
+    const bool units = c.B > 0 && c.H > 0;
+    const bool work = units && c.T > 0;
+    CHECK(check_ptr(cu_seqlens, "cu_seqlens", units));
+    CHECK(check_ptr(prefix_len, "prefix_len", units));
+    CHECK(check_ptr(q, "q", work));
+    CHECK(check_ptr(k, "k", work));
+    CHECK(check_ptr(v, "v", work));
+    CHECK(check_ptr(g, "g", work));
+    CHECK(check_ptr(beta, "beta", work));
+    CHECK(check_ptr(o, "o", work));
+    CHECK(check_ptr(S0, "S0", false));
+    CHECK(check_ptr(S_mid, "S_mid", units));
+    CHECK(check_ptr(S_T, "S_T", false));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!units) return ok();
+    la::FwdArgs a{q, k, v, g, beta, S0, o, S_mid, nullptr};
+    a.cu_seqlens = cu_seqlens;
+    a.split = prefix_len;
+    a.split_part = 0;
+    CHECK(hip_status(la::launch_fwd_tok(c, a, s), "la_recurrent_fwd_split prefix launch"));
+    la::FwdArgs b{q, k, v, g, beta, S_mid, o, S_T, nullptr};
+    b.cu_seqlens = cu_seqlens;
+    b.split = prefix_len;
+    b.split_part = 1;
+    return hip_status(la::launch_fwd_tok(*suffix_cfg, b, s), "la_recurrent_fwd_split suffix launch");
+}
+
+size_t la_bwd_split_workspace_bytes(const la_config* prefix_cfg, const la_config* suffix_cfg) {
+    if (la::check_split(prefix_cfg, suffix_cfg) != LA_OK) return 0;
+    if (prefix_cfg->ckpt_interval < 1 || suffix_cfg->ckpt_interval < 1) return 0;
+    const size_t a = ws_layout_varlen(*prefix_cfg).total, b = ws_layout_varlen(*suffix_cfg).total;
+    const la_config& c = *prefix_cfg;
+    return round_up(static_cast<size_t>(c.B) * c.H * c.d_k * c.d_v * sizeof(float)) + (a > b ? a : b);
+}
+
+la_status la_recurrent_bwd_ste_split(const la_config* prefix_cfg, const la_config* suffix_cfg,
+                                     const int32_t* cu_seqlens, const int32_t* prefix_len, const void* q,
+                                     const void* k, const void* v, const void* g, const void* beta,
+                                     const float* S0, const float* S_mid, const float* dout,
+                                     const float* dS_T, float* dq, float* dk, float* dv, float* dg,
+                                     float* dbeta, float* dS0, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+    CHECK(la::check_split(prefix_cfg, suffix_cfg));
+    const la_config& c = *prefix_cfg;
+    const bool units = c.B > 0 && c.H > 0;
+    CHECK(check_ptr(S_mid, "S_mid", units));
+    CHECK(check_ptr(prefix_len, "prefix_len", units));
+    CHECK(check_ptr(workspace, "workspace", false));
+    if (!units) return ok();
+    const size_t need = la_bwd_split_workspace_bytes(prefix_cfg, suffix_cfg);
+    if (need == 0) return fail(LA_ERR_INVALID_ARG, "backward needs ckpt_interval >= 1 in both configurations");
+    if (!workspace || ws_bytes < need)
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? ws_bytes : static_cast<size_t>(0));
+    // suffix first: its dS0 is the gradient at the handoff, the prefix's dS_T
+    const size_t mid_bytes = round_up(static_cast<size_t>(c.B) * c.H * c.d_k * c.d_v * sizeof(float));
+    float* dS_mid = static_cast<float*>(workspace);
+    void* ws = static_cast<char*>(workspace) + mid_bytes;
+    CHECK(la::bwd_varlen(*suffix_cfg, cu_seqlens, prefix_len, 1, q, k, v, g, beta, S_mid, dout, dS_T, dq, dk, dv, dg,
+                         dbeta, dS_mid, ws, ws_bytes - mid_bytes, stream));
+    return la::bwd_varlen(*prefix_cfg, cu_seqlens, prefix_len, 0, q, k, v, g, beta, S0, dout, dS_mid, dq, dk, dv, dg,
+                          dbeta, dS0, ws, ws_bytes - mid_bytes, stream);
+}
+
 size_t la_bwd_workspace_bytes(const la_config* cfg) {
     if (check_config(cfg, false) != LA_OK || check_kernel(*cfg) != LA_OK || cfg->ckpt_interval < 1) return 0;
     return ws_layout(*cfg).total;
@@ -375,6 +509,72 @@ la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void
     la::BwdArgs a{q, k, v, g, beta, ck, dout, dS_T, dq, dk, dv, dg, dbeta, dS0,
                   reinterpret_cast<float*>(ws + L.states), reinterpret_cast<float*>(ws + L.part)};
     return hip_status(la::launch_bwd(c, a, s), "la_recurrent_bwd_ste launch");
+}
+
+}  // namespace la
+
+namespace la {
+
+la_status check_split(const la_config* a, const la_config* b) {
+    CHECK(check_config(a, false));
+    CHECK(check_config(b, false));
+    if (a->B != b->B || a->T != b->T || a->H != b->H || a->d_k != b->d_k || a->d_v != b->d_v ||
+        a->gate != b->gate || a->qkv_dtype != b->qkv_dtype || a->gate_dtype != b->gate_dtype ||
+        a->out_dtype != b->out_dtype)
+        return fail(LA_ERR_INVALID_ARG, "prefix and suffix configurations differ in shape, gate or dtypes");
+    if (a->state_rotated || b->state_rotated)
+        return fail(LA_ERR_UNSUPPORTED, "the handoff state is the unrotated S (state_rotated must be 0)");
+    for (const la_config* c : {a, b})
+        if (c->kernel != LA_KERNEL_AUTO && c->kernel != LA_KERNEL_TOKEN)
+            return fail(LA_ERR_UNSUPPORTED, "packed sequences run on the per-token kernel only (kernel=%d)", c->kernel);
+    return LA_OK;
+}
+
+la_status bwd_varlen(const la_config& c, const int32_t* cu_seqlens, const int32_t* split, int part, const void* q,
+                     const void* k, const void* v, const void* g, const void* beta, const float* S0,
+                     const float* dout, const float* dS_T, float* dq, float* dk, float* dv, float* dg,
+                     float* dbeta, float* dS0, void* workspace, size_t ws_bytes, void* stream) {
+    if (c.kernel != LA_KERNEL_AUTO && c.kernel != LA_KERNEL_TOKEN)
+        return fail(LA_ERR_UNSUPPORTED, "packed sequences run on the per-token kernel only (kernel=%d)", c.kernel);
+    if (c.ckpt_interval < 1) return fail(LA_ERR_INVALID_ARG, "backward needs ckpt_interval >= 1");
+    const bool units = c.B > 0 && c.H > 0;
+    const bool work = units && c.T > 0;
+    CHECK(check_ptr(cu_seqlens, "cu_seqlens", units));
+    CHECK(check_ptr(q, "q", work));
+    CHECK(check_ptr(k, "k", work));
+    CHECK(check_ptr(v, "v", work));
+    CHECK(check_ptr(g, "g", work));
+    CHECK(check_ptr(beta, "beta", work));
+    CHECK(check_ptr(dout, "dout", work));
+    CHECK(check_ptr(dq, "dq", work));
+    CHECK(check_ptr(dk, "dk", work));
+    CHECK(check_ptr(dv, "dv", work));
+    CHECK(check_ptr(dg, "dg", work));
+    CHECK(check_ptr(dbeta, "dbeta", work));
+    CHECK(check_ptr(dS0, "dS0", units));
+    CHECK(check_ptr(S0, "S0", false));
+    CHECK(check_ptr(dS_T, "dS_T", false));
+    CHECK(check_ptr(workspace, "workspace", false));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!units) return ok();
+    if (c.T == 0) return hip_status(launch_copy_state(c, dS_T, dS0, s), "copy dS_T -> dS0");
+    const WsLayout L = ws_layout_varlen(c);
+    if (!workspace || ws_bytes < L.total)
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                    workspace ? ws_bytes : static_cast<size_t>(0));
+    char* ws = static_cast<char*>(workspace);
+    float* ckw = reinterpret_cast<float*>(ws + L.ckpts);
+    FwdArgs fa{q, k, v, g, beta, S0, nullptr, nullptr, ckw};
+    fa.cu_seqlens = cu_seqlens;
+    fa.split = split;
+    fa.split_part = part;
+    CHECK(hip_status(launch_fwd_tok(c, fa, s), "checkpoint recompute launch"));
+    BwdArgs a{q, k, v, g, beta, ckw, dout, dS_T, dq, dk, dv, dg, dbeta, dS0,
+              reinterpret_cast<float*>(ws + L.states), reinterpret_cast<float*>(ws + L.part)};
+    a.cu_seqlens = cu_seqlens;
+    a.split = split;
+    a.split_part = part;
+    return hip_status(launch_bwd(c, a, s), "packed backward launch");
 }
 
 }  // namespace la

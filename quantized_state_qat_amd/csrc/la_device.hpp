@@ -27,6 +27,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// The nearest BF16 value of x as a float (ties to even): the replay windows' encoding.
+__device__ __forceinline__ float bf16_rne(float x) {
+    return __uint_as_float(static_cast<uint32_t>(f32_to_bf16_bits(x)) << 16);
+}
+
 __device__ __forceinline__ void store_elem(void* p, size_t idx, int dtype, float x) {
     if (dtype == 0) static_cast<float*>(p)[idx] = x;
     else static_cast<uint16_t*>(p)[idx] = f32_to_bf16_bits(x);

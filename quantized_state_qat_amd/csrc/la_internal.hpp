@@ -22,6 +22,10 @@ struct FwdArgs {
     // packed sequences (token kernel only): sequence b is tokens cu_seqlens[b] .. [b + 1] of
     // a [T][H][...] layout; null = the batched [B][T][H][...] layout
     const int32_t* cu_seqlens = nullptr;
+    // packed sequences cut in two (la_recurrent_fwd_split): split[b] is sequence b's prefix
+    // length (clamped to the sequence); split_part 0 runs the prefixes, 1 the suffixes
+    const int32_t* split = nullptr;
+    int split_part = 0;
     // block kernel only: checkpoints in the kernels' register order (lane-major: each lane's
     // 32 state values contiguous, per 16-column wave slice) instead of [d_k][d_v]; set by the
     // block backward for its own recompute, never seen by a caller
@@ -43,6 +47,13 @@ struct DecodeArgs {
     float* scales;  // may be null
     const int32_t* slots = nullptr;  // null: entry b is state b; else the state slot of entry b
     int n_slots = 0;                 // slots outside [1, n_slots) are padding
+    // replay windows of `window` tokens (la_decode_step_replay): S holds the window's
+    // checkpoint; entries 0 .. pos[b] - 1 of the log are the window's earlier tokens
+    const int32_t* pos = nullptr;    // [B]; null: no replay
+    uint16_t* log_k = nullptr;       // [B][H][window - 1][d_k] bf16
+    uint16_t* log_d = nullptr;       // [B][H][window - 1][d_v] bf16
+    float* log_g = nullptr;          // [B][H][window - 1] (scalar gate) or [..][d_k] (per key)
+    int window = 1;
 };
 
 struct BwdArgs {
@@ -62,7 +73,19 @@ struct BwdArgs {
     float* dS0;
     float* ws_states;    // per workgroup: the state entering every 4th token of a chunk (d_k x tile columns)
     float* ws_part;      // per value tile and token: partial row sums
+    // packed sequences (la_recurrent_bwd_ste_varlen / _split), as in FwdArgs; the checkpoints
+    // are then in the packed slot layout (varlen_ckpt_slots)
+    const int32_t* cu_seqlens = nullptr;
+    const int32_t* split = nullptr;
+    int split_part = 0;
 };
+
+// Packed sequences with checkpoints: sequence b's chunks occupy slots b + begin_b / C + c
+// (begin_b its first token, C the checkpoint spacing), disjoint across sequences; a head's
+// slots are [H][slots][d_k][d_v].  slots = B + T / C + 1 bounds them for any packing of T.
+inline int varlen_ckpt_slots(const la_config& c) {
+    return c.ckpt_interval > 0 ? c.B + c.T / c.ckpt_interval + 1 : 0;
+}
 
 // Host-side layout helpers (shared by the ABI and the launchers).
 inline int n_value_blocks(const la_config& c) { return c.d_v / 64; }
@@ -97,6 +120,8 @@ hipError_t launch_fwd_wave(const la_config& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_tok(const la_config& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_copy_state(const la_config& c, const float* src, float* dst, hipStream_t s);
 hipError_t launch_bwd(const la_config& c, const BwdArgs& a, hipStream_t s);
+// Token range [begin, end) of packed sequence b (part of it when split is given), on the
+// host side's terms: the device computes the same from cu_seqlens.
 // Block backward (bwd_mfma.hip): the block forward with a checkpoint every 16 tokens into
 // a.ws_states (fa.ckpts), the block kernel writing partial records to a.ws_part, then their
 // reduction.  Workspace: bwd_mfma_state_bytes + bwd_mfma_part_bytes.
@@ -109,6 +134,14 @@ hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs&
 // layout, launches.  With provide == nullptr the caller's workspace (ws_bytes) is used; else,
 // after every host check and the size check against ws_bytes, provide() supplies the
 // workspace (the allocation-free entry point's device array).
+// Prefix and suffix configurations of la_recurrent_fwd_split / la_recurrent_bwd_ste_split.
+la_status check_split(const la_config* prefix, const la_config* suffix);
+// The packed-sequence backward (all sequences, or one part of each with split): checkpoints
+// recomputed into the workspace, then the token backward and the reduction.
+la_status bwd_varlen(const la_config& c, const int32_t* cu_seqlens, const int32_t* split, int part, const void* q,
+                     const void* k, const void* v, const void* g, const void* beta, const float* S0,
+                     const float* dout, const float* dS_T, float* dq, float* dk, float* dv, float* dg,
+                     float* dbeta, float* dS0, void* workspace, size_t ws_bytes, void* stream);
 using WorkspaceProvider = hipError_t (*)(void** workspace);
 la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void* v, const void* g,
                   const void* beta, const float* S0, const float* ckpts, const float* dout,

@@ -37,15 +37,23 @@ struct TokParams {
     int qdq_interval, ckpt_interval, nck;
     int rot;     // state tensors hold the rotated state (Hadamard mode)
     int replay;  // replay windows: updates between rounding points from BF16-encoded deltas
+    long ntok;   // token-heads of the call: B T H, or T H for packed sequences
 };
 
-// Nearest BF16 value of x (ties to the even significand), as a float: the replay windows'
-// once-only encoding of a token's update.  x finite.
-__device__ __forceinline__ float bf16_rne(float x) {
-    uint32_t b = __float_as_uint(x);
-    b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
-    return __uint_as_float(b);
+// Token range [begin, end) of packed sequence b: cu_seqlens[b] .. cu_seqlens[b + 1], clamped
+// to [0, T_total] (an inverted pair is empty), then, with split, the prefix of split[b]
+// tokens (part 0) or the rest (part 1).
+__device__ __forceinline__ void packed_range(const int32_t* cu, const int32_t* split, int part, int b, int T_total,
+                                             int& begin, int& end) {
+    begin = min(max(cu[b], 0), T_total);
+    end = min(max(cu[b + 1], begin), T_total);
+    if (split) {
+        const int mid = min(max(begin + split[b], begin), end);
+        if (part == 0) end = mid;
+        else begin = mid;
+    }
 }
+
 
 // ------------------------------------------------------------------ lane reduce-scatter
 // Reduce N values per lane (x[0..N-1], value i belonging to row i) over aligned groups of

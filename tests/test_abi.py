@@ -24,7 +24,9 @@ def test_library_exports_every_declared_function():
     assert set(names) == {"la_recurrent_fwd", "la_recurrent_fwd_varlen", "la_decode_step", "la_decode_step_slots",
                           "la_recurrent_bwd_ste", "la_bwd_workspace_bytes", "la_fwd_kernel_name", "la_bwd_kernel_name",
                           "la_status_string", "la_last_error", "la_recurrent_bwd_ste_noalloc",
-                          "la_noalloc_workspace_limit", "la_recurrent_fwd_entries"}
+                          "la_noalloc_workspace_limit", "la_recurrent_fwd_entries", "la_decode_step_replay",
+                          "la_recurrent_fwd_split", "la_recurrent_bwd_ste_varlen", "la_bwd_varlen_workspace_bytes",
+                          "la_recurrent_bwd_ste_split", "la_bwd_split_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 

@@ -226,3 +226,115 @@ def test_replay_backward(name, w, mode, group, had, W, ckpt):
         np.testing.assert_array_equal(g1[n], g2[n])
     errs = _check_against_oracle(c, d, S0, d["do"].f32, dST, g1, gu.TOL_F32)
     print(name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+DECODE = [
+    # name, gate, quantizer, group, hadamard, window, d_k
+    ("gdn_wht_int8g32_w4", "scalar", INT8, 32, 1, 4, 128),
+    ("gdn_int8g32_w16", "scalar", INT8, 32, 0, 16, 128),
+    ("kda_int8g64_w4", "key", INT8, 64, 0, 4, 128),
+    ("kda_wht_int8g32_w16", "key", INT8, 32, 1, 16, 64),
+    ("gdn_e4m3_w8", "scalar", E4M3, 64, 0, 8, 128),
+    ("gdn_int8g16_w1", "scalar", INT8, 16, 0, 1, 64),
+]
+
+
+@pytest.mark.parametrize("name,gate,mode,group,had,W,dk", DECODE, ids=[x[0] for x in DECODE])
+def test_replay_decode_against_oracle(name, gate, mode, group, had, W, dk):
+    """Serving decode in replay mode, token after token over two windows and a half: every
+    output against the oracle (the window run from the GPU's checkpoint with the GPU's logged
+    entries forced), every appended entry against the oracle's encoding of its delta (near-tie
+    protocol), the logged key and gate bits exactly, the checkpoint untouched inside a window,
+    and at each window end the refreshed checkpoint's codes (near-tie protocol) and the codes
+    and scales outputs."""
+    torch = gu.torch_mod()
+    B, H, dv = 3, 2, 128
+    T = 2 * W + W // 2 + 1
+    w = W_("rd", B=B, T=T, H=H, d_k=dk, d_v=dv, gate=gate, s0_sigma=0.05, config_id=101)
+    d = synth.generate(w)
+    dev = {n: gu.dev(d[n]) for n in ("q", "k", "v", "g", "beta")}
+    c = gu.cfg_for(w, d, qdq=mode, group=group, hadamard=had, qdq_interval=W, replay=1)
+    c.T = 1
+    W1 = max(W - 1, 1)
+    log_k = torch.zeros((B, H, W1, dk), dtype=torch.int16, device="cuda")
+    log_d = torch.zeros((B, H, W1, dv), dtype=torch.int16, device="cuda")
+    log_g = torch.zeros((B, H, W1) + ((dk,) if gate == "key" else ()), dtype=torch.float32, device="cuda")
+    S = torch.from_numpy(d["S0"].f32.copy()).cuda()
+    C_win = d["S0"].f32.copy()       # checkpoint entering the current window (host copy)
+    tally_e, tally_c = gu.CodeTally(), gu.CodeTally()
+    worst_o = 0.0
+    for t in range(T):
+        p = t % W
+        w0 = t - p
+        pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+        o = gu.nan_like(torch, (B, 1, H, dv))
+        codes = torch.full((B, H, dk, dv), 99, dtype=torch.int8 if mode == INT8 else torch.uint8, device="cuda")
+        nsc = (B, H, dk, dv // group) if mode == INT8 else (B, H, dv // 64)
+        scales = gu.nan_like(torch, nsc)
+        tk = {n: dev[n][:, t:t + 1].contiguous() for n in dev}
+        la.la_decode_step_replay(c, tk["q"], tk["k"], tk["v"], tk["g"], tk["beta"], S, log_k, log_d, log_g, pos,
+                                 o, codes, scales)
+        torch.cuda.synchronize()
+        o = o.cpu().numpy()
+        # oracle: the window so far from the GPU's checkpoint, the GPU's entries forced
+        dd = sl(d, 0, B, w0, t + 1, 0, H)
+        ents = bits_to_f64(log_d.cpu().numpy())                      # [B, H, W1, dv]
+        dhat = np.full((B, p + 1, H, dv), np.nan)
+        for i in range(p):
+            dhat[:, i] = ents[:, :, i]
+        o_r, _, ck_r, dl_r = oracle.fwd(dd["q"].f64, dd["k"].f64, dd["v"].f64, dd["g"].f64, dd["beta"].f64,
+                                        C_win.astype(np.float64), gate=c.gate, qdq_mode=mode, group=group,
+                                        hadamard=bool(had), qdq_interval=W, replay=True, dhat=dhat,
+                                        ckpt_interval=1, return_deltas=True)
+        worst_o = max(worst_o, gu.err(o[:, 0], o_r[:, p]))
+        if p < W - 1:
+            # an entry was appended; the checkpoint is unchanged
+            np.testing.assert_array_equal(S.cpu().numpy(), C_win)
+            compare_entries(ents[:, :, p], dl_r[:, p], tally_e)
+            kb = log_k.cpu().numpy()[:, :, p].view(np.uint16)
+            np.testing.assert_array_equal(kb, d["k"].bits[:, t])
+            gl = log_g.cpu().numpy()[:, :, p]
+            np.testing.assert_array_equal(gl, d["g"].f32[:, t])
+        else:
+            # window end: the refreshed checkpoint against the oracle's rounding of S'
+            S_new = S.cpu().numpy()
+            dl = sl(d, 0, B, t, t + 1, 0, H)
+            _, Sp, _ = oracle.fwd(dl["q"].f64, dl["k"].f64, dl["v"].f64, dl["g"].f64, dl["beta"].f64,
+                                  ck_r[:, :, p], gate=c.gate)
+            cg, sg = codes.cpu().numpy(), scales.cpu().numpy()
+            for b in range(B):
+                for h in range(H):
+                    _, cr, sr, ypre = oracle.qdq(Sp[b, h], mode, group, bool(had))
+                    if mode == INT8:
+                        gu.compare_int8_codes(S_new[b, h], cr, ypre, group, hadamard=bool(had), tally=tally_c)
+                        mism = cg[b, h].astype(np.int32) != cr
+                        if not mism.any() and not had:
+                            # a scale is its group's largest magnitude over 127: it carries that
+                            # element's fp32 error, accumulated over the window's reconstruction
+                            np.testing.assert_allclose(sg[b, h].reshape(-1), sr, rtol=2e-6)
+                    else:
+                        gu.compare_e4m3_point(S_new[b, h], cr, ypre, tally_c)
+            C_win = S_new.copy()
+    assert worst_o <= gu.TOL_F32, worst_o
+    tally_c.check()
+    tally_e.check()
+    print(f"{name}: output {worst_o:.2e}, codes {tally_c.mismatches}/{tally_c.total}, "
+          f"entries {tally_e.mismatches}/{tally_e.total}")
+
+
+def test_replay_decode_window_of_one_is_the_decode_step():
+    torch = gu.torch_mod()
+    w = W_("rd1", B=4, T=1, H=2, d_k=128, d_v=128, s0_sigma=0.05, config_id=102)
+    d = synth.generate(w)
+    dev = {n: gu.dev(d[n]) for n in ("q", "k", "v", "g", "beta")}
+    c = gu.cfg_for(w, d, qdq=INT8, group=32, hadamard=1, qdq_interval=1, replay=1)
+    S1 = torch.from_numpy(d["S0"].f32.copy()).cuda()
+    S2 = S1.clone()
+    o1, o2 = gu.nan_like(torch, (4, 1, 2, 128)), gu.nan_like(torch, (4, 1, 2, 128))
+    pos = torch.zeros((4,), dtype=torch.int32, device="cuda")
+    la.la_decode_step_replay(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], S1, None, None, None, pos, o1)
+    c0 = gu.cfg_for(w, d, qdq=INT8, group=32, hadamard=1, qdq_interval=1)
+    la.la_decode_step(c0, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], S2, o2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o1.cpu().numpy(), o2.cpu().numpy())
+    np.testing.assert_array_equal(S1.cpu().numpy(), S2.cpu().numpy())
