@@ -626,6 +626,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the long-sequence, KDA and Hadamard forward/backward measurements")
+    ap.add_argument("--only", default="",
+                    help="comma-separated extra measurements to run alone (e.g. long_sequence_fwdbwd), "
+                         "printing their JSON only: for profiling one workload")
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection mode: a few decode launches and one plain copy of a "
                          "256 MiB state buffer (the calibration kernel for HBM byte counters); no JSON")
@@ -643,6 +646,20 @@ def main():
 
     if args.profile:
         profile_mode(min(args.steps, 5))
+        return
+    if args.only:
+        extras = {
+            "long_sequence_valu": lambda: bench_long_e4m3()[2], "long_sequence": lambda: bench_long_e4m3()[0],
+            "long_sequence_fwdbwd": lambda: bench_long_e4m3()[1], "kda_long_e4m3": bench_kda_long,
+            "kda_int8g64_tok": bench_kda_tok, "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd,
+            "replay_w16_wht_int8g32": bench_replay, "decode_slots": bench_decode_slots,
+            "decode_replay_w16": bench_decode_replay, "varlen_prefill": bench_varlen,
+        }
+        out = {}
+        for name in args.only.split(","):
+            out[name] = extras[name]()
+            print(f"done {name}", file=sys.stderr, flush=True)
+        print(json.dumps(out), flush=True)
         return
 
     r = bench_decode(args.steps, args.warmup)

@@ -282,8 +282,10 @@ la_status la_decode_step_replay(const la_config* cfg, const void* q, const void*
  * dS_T (S_T; NULL = zero).  Recomputation runs in chunks of cfg->ckpt_interval (>= 1)
  * tokens from ckpts (the forward's checkpoints with the same interval); ckpts == NULL
  * recomputes them into the workspace first.  Where la_bwd_kernel_name(cfg) is "block", the
- * states are instead recomputed from S0 with the block forward (the same arithmetic as
- * la_recurrent_fwd's "block" kernel, so the same rounding decisions) and ckpts is not read.
+ * sequence is walked in segments, last first: the state entering every 16-token block of a
+ * segment is recomputed from ckpts, all checkpoint chunks in parallel, with the block
+ * forward's own arithmetic (no rounding point lies inside a chunk there), then the segment's
+ * blocks are walked backwards on the matrix cores.
  * The workspace (device memory, at least la_bwd_workspace_bytes(cfg) bytes, contents
  * undefined on entry and exit) is owned by the caller.  Writes every gradient output in full.
  */
@@ -337,9 +339,10 @@ const char* la_fwd_kernel_name(const la_config* cfg);
 
 /*
  * Which backward la_recurrent_bwd_ste runs for cfg (diagnostic; no GPU work, no state):
- *   "block"  the GDN configurations whose forward runs the "block" kernel: the state
- *            entering every 16-token block is recomputed into the workspace, then the blocks
- *            are walked last to first on the matrix cores (the block form of the adjoint);
+ *   "block"  the GDN configurations whose forward runs the "block" kernel: segment by
+ *            segment (last first), the state entering every 16-token block is recomputed from
+ *            the checkpoints into the workspace, then the blocks are walked last to first on
+ *            the matrix cores (the block form of the adjoint);
  *   "token"  every other valid configuration: chunks of ckpt_interval tokens recomputed from
  *            the checkpoints and walked token by token.
  * Returns "" (and sets la_last_error) for an invalid cfg.

@@ -57,8 +57,10 @@ constexpr int kRecGc = 4624;   // [16]: dG terms collected by token column
 constexpr int kRecB = 4640;    // [16]: dbeta
 constexpr int kRec = 4672;     // record stride (256-byte multiple)
 
+// One segment [t_off, t_off + T) of sequences stride_T tokens long; nb = its 16-token blocks.
 struct BwParams {
     int T, H, dv, nb;
+    int stride_T, t_off;
 };
 
 // Per column wave LDS (16-byte aligned for the 16-byte accesses).
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     const int T = p.T, H = p.H, DV = p.dv, nb = p.nb;
     const int nwg = gridDim.x;
     const size_t bh = static_cast<size_t>(b) * H + h;
-    const size_t seq0 = static_cast<size_t>(b) * T * H;
+    const size_t seq0 = (static_cast<size_t>(b) * p.stride_T + p.t_off) * H;  // the segment's first token
     const size_t seq_tok = static_cast<size_t>(T) * H;
 
     // buffer resources over exactly this sequence's tokens (offsets < 2^31, checked on the host):
@@ -276,7 +278,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
     // this unit's block-start states, lane-major per 16-column wave slice (the recompute's
     // order; the eligibility check keeps their offsets below 2^31)
     const auto rst = make_rsrc(a.ws_states + bh * static_cast<size_t>(nb) * DK * DV, static_cast<size_t>(nb) * DK * DV * 4);
-    const int voff_st = ((col >> 4) * 64 + lane) * 32 * 4;  // lane-major block-start states
+    // block-start states per 16-column wave slice, register quad i of lane l at (i 64 + l) 16 bytes
+    const int voff_st = ((col >> 4) * (R / 4) * 64 + lane) * 16;
 
     float dS[R];
 #pragma unroll
@@ -306,11 +309,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_mfma_kernel(BwParams p, BwdArg
             }
             in.dOT = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rdo, voff_doT, (t0 * H + h) * DV * 4, 0));
         } else {
-            // the recompute wrote the states lane-major: this lane's 32 values are 128 bytes
+            // the recompute wrote the states in register order: this lane's 32 values as eight
+            // 16-byte quads, each quad of the 64 lanes one contiguous kilobyte
             const int so = blk * DK * DV * 4;
 #pragma unroll
             for (int i = 0; i < R / 4; i++) {
-                const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rst, voff_st + 16 * i, so, 0);
+                const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rst, voff_st + 1024 * i, so, 0);
 #pragma unroll
                 for (int e = 0; e < 4; e++) in.s[4 * i + e] = __uint_as_float(x[e]);
             }
@@ -557,7 +561,8 @@ __global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArg
     const float* rec0 = a.ws_part + (bh * nb + blk) * nwg * static_cast<size_t>(kRec);
     const int i = tid >> 4, rc = tid & 15;
     const bool ok = t0 + i < T;
-    const size_t o = ((static_cast<size_t>(b) * T + t0 + i) * H + h) * DK + 8 * rc;
+    const size_t tseq = static_cast<size_t>(b) * p.stride_T + p.t_off;  // the segment's first token
+    const size_t o = ((tseq + t0 + i) * H + h) * DK + 8 * rc;
     {
         u4 kw = {0u, 0u, 0u, 0u}, qw = {0u, 0u, 0u, 0u};
         if (ok) {
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArg
             sb += r[kRecB + tid];
         }
         dG[tid] = sg;
-        if (t0 + tid < T) a.dbeta[(static_cast<size_t>(b) * T + t0 + tid) * H + h] = sb;
+        if (t0 + tid < T) a.dbeta[(tseq + t0 + tid) * H + h] = sb;
     }
     // the slices' key/query sums for this thread's eight rows
     f4 dks[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
@@ -634,7 +639,7 @@ __global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArg
     if (tid < kBlk && t0 + tid < T) {
         float x = 0.0f;
         for (int j = kBlk - 1; j >= tid; j--) x += dG[j] + qd[j];
-        a.dg[(static_cast<size_t>(b) * T + t0 + tid) * H + h] = x;
+        a.dg[(tseq + t0 + tid) * H + h] = x;
     }
 }
 
@@ -652,31 +657,76 @@ bool bwd_mfma_eligible(const la_config& c) {
     return span < (static_cast<size_t>(1) << 31);
 }
 
+// Tokens per segment: a multiple of the checkpoint spacing, sized so that a segment's
+// block-start states and partial records take about 256 MiB (at least one chunk, at most
+// the sequence).
+int bwd_mfma_segment(const la_config& c) {
+    const size_t units = static_cast<size_t>(c.B) * c.H;
+    const size_t per_tok = units * (static_cast<size_t>(c.d_k) * c.d_v * 4 + (c.d_v / 64) * kRec * 4) / kBlk;
+    const int C = c.ckpt_interval;
+    size_t L = (static_cast<size_t>(256) << 20) / (per_tok > 0 ? per_tok : 1);
+    L = L / C * C;
+    const size_t Tr = (static_cast<size_t>(c.T) + C - 1) / C * C;
+    if (L < static_cast<size_t>(C)) L = C;
+    if (L > Tr) L = Tr;
+    return static_cast<int>(L);
+}
+
 size_t bwd_mfma_state_bytes(const la_config& c) {
-    return static_cast<size_t>(c.B) * c.H * ((c.T + kBlk - 1) / kBlk) * c.d_k * c.d_v * sizeof(float);
+    return static_cast<size_t>(c.B) * c.H * ((bwd_mfma_segment(c) + kBlk - 1) / kBlk) * c.d_k * c.d_v * sizeof(float);
 }
 
 size_t bwd_mfma_part_bytes(const la_config& c) {
-    return static_cast<size_t>(c.B) * c.H * ((c.T + kBlk - 1) / kBlk) * (c.d_v / 64) * kRec * sizeof(float);
+    return static_cast<size_t>(c.B) * c.H * ((bwd_mfma_segment(c) + kBlk - 1) / kBlk) * (c.d_v / 64) * kRec *
+           sizeof(float);
 }
 
-hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs& a, hipStream_t s) {
-    la_config c16 = c;
-    c16.ckpt_interval = kBlk;
-    FwdArgs fl = fa;
-    fl.ckpt_lane_major = 1;
-    hipError_t e = launch_fwd_mfma(c16, fl, s);
-    if (e != hipSuccess) return e;
-    const BwParams p{c.T, c.H, c.d_v, (c.T + kBlk - 1) / kBlk};
-    dim3 grid(c.d_v / 64, c.H, c.B);
-    if (c.gate_dtype == LA_F32)
-        hipLaunchKernelGGL((bwd_mfma_kernel<true>), grid, dim3(kBwThreads), 0, s, p, a);
-    else
-        hipLaunchKernelGGL((bwd_mfma_kernel<false>), grid, dim3(kBwThreads), 0, s, p, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_mfma_reduce_kernel, dim3(p.nb, c.H, c.B), dim3(256), 0, s, p, a, c.d_v / 64);
-    return hipGetLastError();
+// Segments last to first: (1) the state entering every 16-token block of the segment,
+// recomputed from the forward's checkpoints, every checkpoint chunk in parallel (the block
+// forward in chunk mode; the caller's checkpoints, or when none are given, the block forward's
+// own first written into ck_room); (2) the block adjoint over the segment, dS carried between
+// segments in `carry` (in place: each workgroup reads and writes its own elements); (3) the
+// reduction of the segment's records.
+hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs& a, float* carry, float* ck_room,
+                           hipStream_t s) {
+    const float* ck = a.ckpts;
+    if (!ck) {
+        FwdArgs f = fa;
+        f.o = nullptr;
+        f.ST = nullptr;
+        f.ckpts = ck_room;
+        hipError_t e = launch_fwd_mfma(c, f, s);
+        if (e != hipSuccess) return e;
+        ck = ck_room;
+    }
+    const int L = bwd_mfma_segment(c);
+    const int nseg = (c.T + L - 1) / L;
+    for (int sg = nseg - 1; sg >= 0; sg--) {
+        const int s0 = sg * L, s1 = min(c.T, s0 + L), n = s1 - s0;
+        FwdArgs f = fa;
+        f.S0 = ck;
+        f.o = nullptr;
+        f.ST = nullptr;
+        f.ckpts = a.ws_states;
+        f.ckpt_lane_major = 1;
+        hipError_t e = launch_fwd_mfma_chunks(c, f, s0, s1, s);
+        if (e != hipSuccess) return e;
+        const BwParams p{n, c.H, c.d_v, (n + kBlk - 1) / kBlk, c.T, s0};
+        BwdArgs b = a;
+        b.dST = sg == nseg - 1 ? a.dST : carry;
+        b.dS0 = sg == 0 ? a.dS0 : carry;
+        dim3 grid(c.d_v / 64, c.H, c.B);
+        if (c.gate_dtype == LA_F32)
+            hipLaunchKernelGGL((bwd_mfma_kernel<true>), grid, dim3(kBwThreads), 0, s, p, b);
+        else
+            hipLaunchKernelGGL((bwd_mfma_kernel<false>), grid, dim3(kBwThreads), 0, s, p, b);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(bwd_mfma_reduce_kernel, dim3(p.nb, c.H, c.B), dim3(256), 0, s, p, b, c.d_v / 64);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace la

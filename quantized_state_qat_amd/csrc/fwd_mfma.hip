@@ -104,11 +104,23 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kernel(Params p, FwdArgs 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int T = p.T, H = p.H, DV = p.dv;
+    const int h = blockIdx.y;
+    const int H = p.H, DV = p.dv;
+    const bool chunked = p.chunk > 0;
+    int b = blockIdx.z, T = p.T;
+    size_t seq0 = static_cast<size_t>(b) * T * H;
+    size_t s0_off = 0, ck_off = 0;
+    if (chunked) {
+        // one checkpoint chunk of the block backward's recompute (Params: chunk)
+        b = blockIdx.z / p.nch;
+        const int t_start = p.t_off + (blockIdx.z - b * p.nch) * p.chunk;
+        T = min(p.chunk, p.t_end - t_start);
+        seq0 = (static_cast<size_t>(b) * p.stride_T + t_start) * H;
+        s0_off = ((static_cast<size_t>(b) * H + h) * p.nck_in + t_start / p.chunk) * DK * DV;
+        ck_off = ((static_cast<size_t>(b) * H + h) * p.nck + (t_start - p.t_off) / kBlk) * DK * DV;
+    }
     const int nblk = (T + kBlk - 1) / kBlk;
     const size_t bh = static_cast<size_t>(b) * H + h;
-    const size_t seq0 = static_cast<size_t>(b) * T * H;
     const size_t seq_tok = static_cast<size_t>(T) * H;
     const int qi = p.qdq_interval;
     // last token of the next rounding interval (T: none); the same schedule in every wave
@@ -210,7 +222,7 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kernel(Params p, FwdArgs 
             *reinterpret_cast<f4*>(&sl.Ms[c][4 * g]) = selm;
         };
 
-        int q_next = QMODE != LA_QDQ_NONE ? min(qi, T) - 1 : T;
+        int q_next = QMODE != LA_QDQ_NONE && !chunked ? min(qi, T) - 1 : T;
         ProdIn cur, nxt;
         pfetch(cur, 0);
         pfetch(nxt, kBlk);
@@ -238,17 +250,18 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kernel(Params p, FwdArgs 
     const int col = blockIdx.x * kTileCols + w * kWaveCols + c;
     const size_t state_off = bh * DK * DV;
     const auto rv = make_rsrc(static_cast<const char*>(a.v) + seq0 * DV * 2, seq_tok * DV * 2);
-    const size_t ck_unit = static_cast<size_t>(p.nck) * DK * DV;
-    const auto rck = make_rsrc(a.ckpts ? a.ckpts + bh * ck_unit : nullptr, a.ckpts ? ck_unit * 4 : 0);
+    const size_t ck_unit = static_cast<size_t>(chunked ? nblk : p.nck) * DK * DV;
+    const auto rck = make_rsrc(a.ckpts ? a.ckpts + (chunked ? ck_off : bh * ck_unit) : nullptr, a.ckpts ? ck_unit * 4 : 0);
     const int voff_ck = (state_row(0, g) * DV + col) * 4;
     const bool has_o = a.o != nullptr;
     const auto ro = make_rsrc(has_o ? static_cast<const char*>(a.o) + seq0 * DV * OB : nullptr,
                               has_o ? seq_tok * DV * OB : 0);
 
     float s[R];
+    const size_t s0_base = chunked ? s0_off : state_off;
 #pragma unroll
     for (int m = 0; m < R; m++)
-        s[m] = a.S0 ? a.S0[state_off + static_cast<size_t>(state_row(m, g)) * DV + col] : 0.0f;
+        s[m] = a.S0 ? a.S0[s0_base + static_cast<size_t>(state_row(m, g)) * DV + col] : 0.0f;
     __builtin_amdgcn_s_waitcnt(0);
 
     // values of tokens t0 + 4 g .. 4 g + 3 at this lane's column
@@ -265,7 +278,7 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kernel(Params p, FwdArgs 
     };
 
     int qpar = 0;
-    int q_next = QMODE != LA_QDQ_NONE ? min(qi, T) - 1 : T;
+    int q_next = QMODE != LA_QDQ_NONE && !chunked ? min(qi, T) - 1 : T;
     int ck_next = a.ckpts ? 0 : T;
     uint32_t vcur[4], vnxt[4];
     vfetch(vcur, 0);
@@ -278,12 +291,14 @@ __global__ __launch_bounds__(kPcThreads) void fwd_mfma_kernel(Params p, FwdArgs 
         if (t0 == ck_next) {
             const int so = t0 / p.ckpt_interval * DK * DV * 4;
             if (a.ckpt_lane_major) {
-                const int vo = ((col >> 4) * 64 + lane) * R * 4;
+                // per 16-column wave slice, register quad i of lane l at (i * 64 + l) * 16 bytes:
+                // every store instruction writes one contiguous kilobyte
+                const int vo = ((col >> 4) * (R / 4) * 64 + lane) * 16;
 #pragma unroll
                 for (int i = 0; i < R / 4; i++)
                     __builtin_amdgcn_raw_buffer_store_b128(
                         u4{__float_as_uint(s[4 * i]), __float_as_uint(s[4 * i + 1]), __float_as_uint(s[4 * i + 2]),
-                           __float_as_uint(s[4 * i + 3])}, rck, vo + 16 * i, so, 0);
+                           __float_as_uint(s[4 * i + 3])}, rck, vo + 1024 * i, so, 0);
             } else {
 #pragma unroll
                 for (int m = 0; m < R; m++)
@@ -875,7 +890,37 @@ hipError_t launch_mfma_t(const la_config& c, const FwdArgs& a, hipStream_t s) {
     return launch_mfma_o<QMODE, G, false>(c, a, s);
 }
 
+template <int QMODE, int G>
+hipError_t launch_chunks_t(const la_config& c, const FwdArgs& a, const Params& p, hipStream_t s) {
+    dim3 grid(c.d_v / kTileCols, c.H, c.B * p.nch);
+    if (c.gate_dtype == LA_F32)
+        hipLaunchKernelGGL((fwd_mfma_kernel<QMODE, G, true, false>), grid, dim3(kPcThreads), 0, s, p, a);
+    else
+        hipLaunchKernelGGL((fwd_mfma_kernel<QMODE, G, false, false>), grid, dim3(kPcThreads), 0, s, p, a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_fwd_mfma_chunks(const la_config& c, const FwdArgs& a, int t_off, int t_end, hipStream_t s) {
+    la_config cc = c;
+    cc.ckpt_interval = kBlk;
+    Params p = make_params(cc);
+    p.chunk = c.ckpt_interval;
+    p.nch = (t_end - t_off + p.chunk - 1) / p.chunk;
+    p.t_off = t_off;
+    p.t_end = t_end;
+    p.stride_T = c.T;
+    p.nck_in = n_ckpts(c);
+    p.nck = (t_end - t_off + kBlk - 1) / kBlk;
+    if (c.qdq == LA_QDQ_NONE) return launch_chunks_t<LA_QDQ_NONE, 1>(c, a, p, s);
+    if (c.qdq == LA_QDQ_E4M3_TILE) return launch_chunks_t<LA_QDQ_E4M3_TILE, 64>(c, a, p, s);
+    switch (c.group) {
+        case 16: return launch_chunks_t<LA_QDQ_INT8_GROUP, 16>(c, a, p, s);
+        case 32: return launch_chunks_t<LA_QDQ_INT8_GROUP, 32>(c, a, p, s);
+        default: return launch_chunks_t<LA_QDQ_INT8_GROUP, 64>(c, a, p, s);
+    }
+}
 
 bool fwd_mfma_eligible(const la_config& c) {
     if (c.replay && c.qdq_interval > 1) return false;  // encoded updates: token by token

@@ -103,16 +103,20 @@ size_t round_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
     size_t states, part, ckpts, total;
+    size_t carry = 0;  // block backward: dS between segments
 };
 
 WsLayout ws_layout(const la_config& c) {
     WsLayout L;
     if (la::bwd_mfma_eligible(c)) {
-        // block backward: the state entering every 16-token block, then the partial records
+        // block backward, per segment: the state entering every 16-token block, the partial
+        // records; then dS carried between segments and room for the forward's checkpoints
+        // (used when the caller gives none)
         L.states = 0;
         L.part = round_up(la::bwd_mfma_state_bytes(c));
-        L.ckpts = L.part + round_up(la::bwd_mfma_part_bytes(c));
-        L.total = L.ckpts;
+        L.carry = L.part + round_up(la::bwd_mfma_part_bytes(c));
+        L.ckpts = L.carry + round_up(static_cast<size_t>(c.B) * c.H * c.d_k * c.d_v * sizeof(float));
+        L.total = L.ckpts + round_up(static_cast<size_t>(c.B) * c.H * la::n_ckpts(c) * c.d_k * c.d_v * sizeof(float));
         return L;
     }
     // the backward runs in the token layout: tiles of tok_tile_cols value columns
@@ -492,11 +496,13 @@ la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void
                     workspace ? ws_bytes : static_cast<size_t>(0));
     char* ws = static_cast<char*>(workspace);
     if (la::bwd_mfma_eligible(c)) {
-        float* dense = reinterpret_cast<float*>(ws + L.states);
-        la::FwdArgs fa{q, k, v, g, beta, S0, nullptr, nullptr, dense};
-        la::BwdArgs a{q, k, v, g, beta, dense, dout, dS_T, dq, dk, dv, dg, dbeta, dS0,
-                      dense, reinterpret_cast<float*>(ws + L.part)};
-        return hip_status(la::launch_bwd_mfma(c, fa, a, s), "la_recurrent_bwd_ste launch");
+        float* states = reinterpret_cast<float*>(ws + L.states);
+        la::FwdArgs fa{q, k, v, g, beta, S0, nullptr, nullptr, nullptr};
+        la::BwdArgs a{q, k, v, g, beta, ckpts, dout, dS_T, dq, dk, dv, dg, dbeta, dS0,
+                      states, reinterpret_cast<float*>(ws + L.part)};
+        return hip_status(la::launch_bwd_mfma(c, fa, a, reinterpret_cast<float*>(ws + L.carry),
+                                              reinterpret_cast<float*>(ws + L.ckpts), s),
+                          "la_recurrent_bwd_ste launch");
     }
     const float* ck = ckpts;
     if (!ck) {

@@ -26,8 +26,8 @@ struct FwdArgs {
     // length (clamped to the sequence); split_part 0 runs the prefixes, 1 the suffixes
     const int32_t* split = nullptr;
     int split_part = 0;
-    // block kernel only: checkpoints in the kernels' register order (lane-major: each lane's
-    // 32 state values contiguous, per 16-column wave slice) instead of [d_k][d_v]; set by the
+    // block kernel only: checkpoints in the kernels' register order (per 16-column wave slice,
+    // register quad i of lane l at (i 64 + l) 16 bytes) instead of [d_k][d_v]; set by the
     // block backward for its own recompute, never seen by a caller
     int ckpt_lane_major = 0;
     // token kernel only (replay windows): bf16 bits [B][T][H][d_v] of every token's delta
@@ -122,13 +122,21 @@ hipError_t launch_copy_state(const la_config& c, const float* src, float* dst, h
 hipError_t launch_bwd(const la_config& c, const BwdArgs& a, hipStream_t s);
 // Token range [begin, end) of packed sequence b (part of it when split is given), on the
 // host side's terms: the device computes the same from cu_seqlens.
-// Block backward (bwd_mfma.hip): the block forward with a checkpoint every 16 tokens into
-// a.ws_states (fa.ckpts), the block kernel writing partial records to a.ws_part, then their
-// reduction.  Workspace: bwd_mfma_state_bytes + bwd_mfma_part_bytes.
+// Block forward in chunk mode (la_recur.hpp Params::chunk): from checkpoints a.S0 (spacing
+// c.ckpt_interval), the state entering every 16-token block of tokens [t_off, t_end) into
+// a.ckpts, lane-major, every checkpoint chunk in parallel.
+hipError_t launch_fwd_mfma_chunks(const la_config& c, const FwdArgs& a, int t_off, int t_end, hipStream_t s);
+// Block backward (bwd_mfma.hip), segment by segment: a segment's block-start states (chunk
+// recompute from a.ckpts, or from the forward's checkpoints recomputed into ck_room) into
+// a.ws_states, the block kernel writing partial records to a.ws_part, their reduction; dS is
+// carried between segments in `carry` ([B][H][d_k][d_v]).  Workspace: bwd_mfma_state_bytes
+// + bwd_mfma_part_bytes (one segment each) + carry + checkpoint room.
 bool bwd_mfma_eligible(const la_config& c);
+int bwd_mfma_segment(const la_config& c);
 size_t bwd_mfma_state_bytes(const la_config& c);
 size_t bwd_mfma_part_bytes(const la_config& c);
-hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs& a, float* carry, float* ck_room,
+                           hipStream_t s);
 
 // The straight-through backward behind both backward entry points: host checks, workspace
 // layout, launches.  With provide == nullptr the caller's workspace (ws_bytes) is used; else,

@@ -208,18 +208,31 @@ def test_bwd_kernel_selection(kw, name):
 
 
 def test_bwd_block_workspace():
-    """Block backward workspace: the state entering every 16-token block (fp32 d_k x d_v per
-    unit and block), then one partial record of 4672 floats per unit, block and 64-column
-    slice (two 16 x 128 key/query sums, two 16 x 16 Gram-term matrices, three 16-token
-    vectors, padded)."""
+    """Block backward workspace, for one segment of the sequence (here the whole sequence,
+    rounded up to the checkpoint spacing: 128 tokens, 8 blocks): the state entering every
+    16-token block (fp32 d_k x d_v per unit and block), one partial record of 4672 floats per
+    unit, block and 64-column slice (two 16 x 128 key/query sums, two 16 x 16 Gram-term
+    matrices, three 16-token vectors, padded), dS carried between segments, and room for the
+    forward's checkpoints."""
     c = la.Config(B=3, T=100, H=2, d_k=128, d_v=192, qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64,
                   ckpt_interval=64)
     assert la.la_bwd_kernel_name(c) == "block"
-    nb = 7
+    nb = 8
     states = 3 * 2 * nb * 128 * 192 * 4
     part = 3 * 2 * nb * 3 * 4672 * 4
+    carry = 3 * 2 * 128 * 192 * 4
+    ckpts = 3 * 2 * 2 * 128 * 192 * 4
     n = la.la_bwd_workspace_bytes(c)
-    assert n >= states + part and n < states + part + 2 * 256
+    assert n >= states + part + carry + ckpts and n < states + part + carry + ckpts + 4 * 256
+
+
+def test_bwd_block_workspace_long_sequence_under_1gb():
+    """The long-sequence workload's backward walks segments of 512 tokens: its workspace stays
+    below 1 GB (with room for the forward's checkpoints)."""
+    c = la.Config(B=8, T=4096, H=16, d_k=128, d_v=128, qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64,
+                  ckpt_interval=64, gate_dtype=la.LA_F32)
+    assert la.la_bwd_kernel_name(c) == "block"
+    assert la.la_bwd_workspace_bytes(c) < 10 ** 9
 
 
 def test_fwd_kernel_name_invalid():
