@@ -158,6 +158,8 @@ def bench_long_e4m3(steps=3, warmup=1):
                                                     "token-head against the FP32 vector peak (which needs packed "
                                                     "FP32 FMAs; this build issues unpacked FP32, whose peak is half)"),
         "frac_of_unpacked_valu_peak": 7.0 * unit / t_v / 1e12 / (FP32_VALU_PEAK_TFLOPS / 2),
+        "issue_floor": _issue_roofline(3.0 + 8.0 / 64, unit, t_v, "two FMA passes (projections) and one FMA update per "
+                                                               "element and token, the E4M3 codec (8) every 64 tokens"),
     }
 
     c.ckpt_interval = 64
@@ -242,6 +244,21 @@ def _fp32_roofline(flops, t, what):
             "frac": flops / t / 1e12 / FP32_VALU_PEAK_TFLOPS, "flops_per_call": flops, "note": what}
 
 
+# VALU issue rate of the chip: one wave64 instruction per CU per cycle (four 16-lane SIMDs, four
+# cycles per wave instruction), i.e. 64 element operations per CU per cycle.
+VALU_ELEM_OPS_PEAK = 64 * 256 * 2.4e9
+
+
+def _issue_roofline(ops_per_elem, elems, t, what):
+    """Algorithmic VALU issue floor: ops_per_elem element operations per state element and token
+    (the recurrence's decay, projections and update, plus the codec and the rotations where they
+    run) over `elems` state-element-tokens, against the chip's VALU issue rate."""
+    ops = ops_per_elem * elems
+    return {"bound": "alu", "achieved": ops / t / 1e12, "peak": VALU_ELEM_OPS_PEAK / 1e12,
+            "unit": "T element-ops/s", "frac": ops / t / VALU_ELEM_OPS_PEAK, "ops_per_element_token": ops_per_elem,
+            "note": what}
+
+
 def _time_calls(fn, steps, warmup, stream):
     import torch
     for _ in range(warmup):
@@ -285,7 +302,13 @@ def bench_kda_tok(steps=3, warmup=1):
         "kernel": la.la_fwd_kernel_name(c), "ms_per_call": t * 1e3, "updates_per_s": w.B * w.H * w.T / t,
         "roofline": _fp32_roofline(flops, t, "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head); "
                                              "the INT8 codec is not counted"),
+        "issue_floor": _issue_roofline(12.0, w.d_k * w.d_v * w.B * w.H * w.T, t,
+                                       "decay, two projections and the update (4) plus the INT8 codec (8) per element "
+                                       "and token"),
         "ms_per_call_hadamard": t_h * 1e3,
+        "issue_floor_hadamard": _issue_roofline(26.0, w.d_k * w.d_v * w.B * w.H * w.T, t_h,
+                                                "as above plus two 7-stage butterfly rotations of the state (14) per "
+                                                "element and token"),
         "note_hadamard": "the same call with the key-axis Hadamard rotation around every rounding (per-key gates "
                          "carry the state unrotated: two rotations of the state per token)",
     }
@@ -440,6 +463,9 @@ def bench_varlen(steps=3, warmup=1):
         "kernel": "token (packed sequences)", "ms_per_call": t * 1e3, "updates_per_s": w.H * T / t,
         "roofline": _fp32_roofline(flops, t, "algorithmic fp32 work of the recurrence (7 d_k d_v per token-head); "
                                              "the INT8 codec is not counted; the longest sequence sets the time"),
+        "issue_floor": _issue_roofline(12.0, w.d_k * w.d_v * w.H * T, t, "token step (4) and INT8 codec (8) per "
+                                                                       "element and token"),
+        "issue_floor_bwd": _issue_roofline(33.0, w.d_k * w.d_v * w.H * T, t_b, "recompute twice (24) and adjoint (9)"),
     }
 
 
@@ -489,6 +515,11 @@ def bench_wht_fwdbwd(steps=2, warmup=1):
                                    "rotations and the codec are not counted"),
         "roofline_fwd": _fp32_roofline(7.0 * unit, t_f, "forward only"),
         "roofline_bwd": _fp32_roofline(22.0 * unit, t_b, "backward only (recompute + adjoint)"),
+        "issue_floor_fwd": _issue_roofline(12.0, unit, t_f, "decay, projections, update (4) and the INT8 codec (8) "
+                                                            "per element and token (the state is carried rotated)"),
+        "issue_floor_bwd": _issue_roofline(33.0, unit, t_b, "the forward token step with its codec twice (recompute "
+                                                            "of the chunk, then of each group of four: 24) and the "
+                                                            "adjoint (9) per element and token"),
     }
 
 
