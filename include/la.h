@@ -87,8 +87,12 @@ typedef enum {
     LA_KERNEL_BLOCK = 1,
     LA_KERNEL_WAVE = 2,
     LA_KERNEL_FAST = 3,
-    LA_KERNEL_TOKEN = 4
+    LA_KERNEL_TOKEN = 4,
+    LA_KERNEL_CHUNK = 5  /* the 64-token chunk form (la_recurrent_fwd_chunk): d_k = 128 */
 } la_kernel;
+/* The chunk form's triangular solve ("Experimental GDN/KDA approximate-inverse QAT", What does
+   this PR do?: exact solve by default, or an explicit Neumann polynomial degree). */
+typedef enum { LA_SOLVE_EXACT = 0, LA_SOLVE_NEUMANN = 1 } la_solve;
 
 typedef struct la_config {
     int32_t B, T, H, d_k, d_v;
@@ -125,6 +129,15 @@ typedef struct la_config {
                               rounding after every token.  Needs a quantizer and bf16 q/k/v
                               (keys are then their own BF16 entries); runs the per-token kernel.
                               The backward passes straight through the encoding as through Q. */
+    int32_t solve;         /* la_solve.  LA_SOLVE_EXACT (0): the recurrence above, on any kernel.
+                              LA_SOLVE_NEUMANN (1): the 64-token chunk form in which each chunk's
+                              (I + A)^-1 is replaced by the Neumann polynomial
+                              sum_{n=0}^{degree} (-A)^n ("Experimental GDN/KDA approximate-inverse
+                              QAT", What does this PR do?), a different function of the inputs;
+                              runs on the chunk kernel only (la_recurrent_fwd_chunk), whose
+                              comment states the chunk form. */
+    int32_t degree;        /* Neumann degree, 3 | 7 | 15 | 31 with LA_SOLVE_NEUMANN, else 0.  It is
+                              used as given: never raised, lowered or replaced by the exact solve. */
 } la_config;
 
 /*
@@ -140,6 +153,37 @@ typedef struct la_config {
 la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, const void* v,
                            const void* g, const void* beta, const float* S0, void* o,
                            float* S_T, float* ckpts, void* stream);
+
+/*
+ * Forward over 64-token chunks ("GDN state/W QAT foundation", What does this PR do?: the state
+ * rounded at 64-token chunk boundaries; "Experimental GDN/KDA approximate-inverse QAT", What
+ * does this PR do?: the chunk's triangular solve exact or by a Neumann polynomial).  Tokens are
+ * cut into chunks of 64 from the start of the call; a chunk of L tokens entering with the
+ * carried state S, with cumulative log decays G_r = g_0 + ... + g_r per key (the scalar gate's
+ * value on every key), computes
+ *     A_ri  = beta_r sum_k k_r[k] k_i[k] exp(G_r[k] - G_i[k])   (i < r; 0 elsewhere)
+ *     M_ri  = sum_k q_r[k] k_i[k] exp(G_r[k] - G_i[k])          (i <= r; 0 elsewhere)
+ *     P     = (I + A)^-1 (solve = EXACT) or sum_{n=0}^{degree} (-A)^n (solve = NEUMANN)
+ *     Delta = P diag(beta) (V - (K o E) S),  E_r = exp(G_r)
+ *     O     = (Q o E) S + M Delta
+ *     S_end = diag(exp(G_{L-1})) S + (K o F)^T Delta,  F_r = exp(G_{L-1} - G_r)
+ * and S_end is rounded when the chunk ends on a rounding point.  With the exact solve this is
+ * the recurrence in the header comment (up to the order of floating-point operations).
+ * cfg->kernel must be LA_KERNEL_CHUNK, or LA_KERNEL_AUTO with solve = NEUMANN.  Needs d_k = 128,
+ * no Hadamard rotation and no replay windows, qdq_interval a multiple of 64 with a quantizer,
+ * ckpt_interval 0 or a multiple of 64.  workspace: device memory of at least
+ * la_chunk_workspace_bytes(cfg) bytes (the chunks' matrices), owned by the caller, contents
+ * ignored on entry and undefined on return.  Other arguments and errors as la_recurrent_fwd;
+ * LA_ERR_WORKSPACE when the workspace is missing or too small.
+ */
+la_status la_recurrent_fwd_chunk(const la_config* cfg, const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta, const float* S0, void* o,
+                                 float* S_T, float* ckpts, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/* Workspace bytes la_recurrent_fwd_chunk needs for cfg (0 if cfg is invalid or not served by
+   the chunk kernel). */
+size_t la_chunk_workspace_bytes(const la_config* cfg);
 
 /*
  * la_recurrent_fwd in replay mode (cfg->replay = 1) that also writes every token's update
@@ -329,7 +373,10 @@ size_t la_bwd_workspace_bytes(const la_config* cfg);
  *   "fast"   GDN, no Hadamard, rounding at most every 2 tokens, no rounding point strictly
  *            inside a checkpoint chunk: eight waves per 64 columns, rescaled state;
  *   "token"  every other valid configuration (Hadamard, rounding every token, KDA with an
- *            interval or checkpoint spacing that is not a multiple of 8).
+ *            interval or checkpoint spacing that is not a multiple of 8);
+ *   "chunk"  cfg->kernel = LA_KERNEL_CHUNK, or solve = LA_SOLVE_NEUMANN (never chosen by
+ *            LA_KERNEL_AUTO for the exact solve): the 64-token chunk form, run by
+ *            la_recurrent_fwd_chunk only (la_recurrent_fwd returns LA_ERR_UNSUPPORTED).
  * With cfg->kernel other than LA_KERNEL_AUTO the named kernel is returned if it serves cfg.
  * Returns "" (and sets la_last_error) for an invalid cfg or a requested kernel that cannot
  * serve it.  The kernels differ only in the order of floating-point operations; every one

@@ -20,7 +20,8 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_ALIGNMENT, LA_ERR_WORKSPAC
 LA_F32, LA_BF16 = 0, 1
 LA_GATE_SCALAR, LA_GATE_KEY = 0, 1
 LA_QDQ_NONE, LA_QDQ_INT8_GROUP, LA_QDQ_E4M3_TILE = 0, 1, 2
-LA_KERNEL_AUTO, LA_KERNEL_BLOCK, LA_KERNEL_WAVE, LA_KERNEL_FAST, LA_KERNEL_TOKEN = range(5)
+LA_KERNEL_AUTO, LA_KERNEL_BLOCK, LA_KERNEL_WAVE, LA_KERNEL_FAST, LA_KERNEL_TOKEN, LA_KERNEL_CHUNK = range(6)
+LA_SOLVE_EXACT, LA_SOLVE_NEUMANN = 0, 1
 
 
 class LaError(RuntimeError):
@@ -32,7 +33,8 @@ class LaError(RuntimeError):
 class la_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "H", "d_k", "d_v", "gate", "qdq", "group", "hadamard", "qdq_interval",
-                 "ckpt_interval", "qkv_dtype", "gate_dtype", "out_dtype", "state_rotated", "kernel", "replay")]
+                 "ckpt_interval", "qkv_dtype", "gate_dtype", "out_dtype", "state_rotated", "kernel", "replay", "solve",
+                 "degree")]
 
 
 @dataclasses.dataclass
@@ -54,6 +56,8 @@ class Config:
     state_rotated: int = 0
     kernel: int = LA_KERNEL_AUTO
     replay: int = 0
+    solve: int = LA_SOLVE_EXACT
+    degree: int = 0
 
     def c(self) -> la_config:
         return la_config(*[int(getattr(self, f.name)) for f in dataclasses.fields(self)])
@@ -82,6 +86,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.la_decode_step.argtypes = [cp] + [vp] * 10
         lib.la_recurrent_bwd_ste.restype = ctypes.c_int
         lib.la_recurrent_bwd_ste.argtypes = [cp] + [vp] * 16 + [ctypes.c_size_t, vp]
+        lib.la_recurrent_fwd_chunk.restype = ctypes.c_int
+        lib.la_recurrent_fwd_chunk.argtypes = [cp] + [vp] * 10 + [ctypes.c_size_t, vp]
+        lib.la_chunk_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_chunk_workspace_bytes.argtypes = [cp]
         lib.la_recurrent_fwd_entries.restype = ctypes.c_int
         lib.la_recurrent_fwd_entries.argtypes = [cp] + [vp] * 11
         lib.la_recurrent_fwd_varlen.restype = ctypes.c_int
@@ -204,6 +212,26 @@ def la_recurrent_fwd(cfg: Config, q, k, v, g, beta, S0, o, S_T=None, ckpts=None,
                                 _arg(o, "o", tok * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
                                 _arg(S_T, "S_T", _state_numel(cfg, cfg.B), _f32()),
                                 _arg(ckpts, "ckpts", _state_numel(cfg, cfg.B) * nck, _f32()), _stream(stream)))
+
+
+def la_chunk_workspace_bytes(cfg: Config) -> int:
+    c = cfg.c()
+    return int(load_library().la_chunk_workspace_bytes(ctypes.byref(c)))
+
+
+def la_recurrent_fwd_chunk(cfg: Config, q, k, v, g, beta, S0, o, S_T, ckpts, workspace, ws_bytes: int,
+                           stream=None) -> None:
+    """The 64-token chunk form (exact or Neumann solve); workspace of la_chunk_workspace_bytes."""
+    lib = load_library()
+    c = cfg.c()
+    tok = cfg.B * cfg.T
+    nck = (cfg.T + cfg.ckpt_interval - 1) // cfg.ckpt_interval if cfg.ckpt_interval > 0 else 0
+    args = _inputs(cfg, tok, q, k, v, g, beta)
+    _check(lib.la_recurrent_fwd_chunk(ctypes.byref(c), *args, _arg(S0, "S0", _state_numel(cfg, cfg.B), _f32()),
+                                      _arg(o, "o", tok * cfg.H * cfg.d_v, _torch_dtype(cfg.out_dtype)),
+                                      _arg(S_T, "S_T", _state_numel(cfg, cfg.B), _f32()),
+                                      _arg(ckpts, "ckpts", _state_numel(cfg, cfg.B) * nck, _f32()),
+                                      _workspace(workspace, ws_bytes), int(ws_bytes), _stream(stream)))
 
 
 def la_recurrent_fwd_entries(cfg: Config, q, k, v, g, beta, S0, o, S_T, ckpts, entries, stream=None) -> None:
@@ -411,7 +439,7 @@ def la_noalloc_workspace_limit() -> int:
 
 
 def la_fwd_kernel_name(cfg: Config) -> str:
-    """Which forward kernel serves cfg: "block", "wave", "fast" or "token" ("" if invalid)."""
+    """Which forward kernel serves cfg: "block", "wave", "fast", "token" or "chunk" ("" if invalid)."""
     c = cfg.c()
     return load_library().la_fwd_kernel_name(ctypes.byref(c)).decode()
 

@@ -1,0 +1,390 @@
+// 64-token chunk path, forward: the chunk-parallel prep kernel (one workgroup per sequence,
+// head and chunk) and the state pass (one workgroup per sequence, head and 64 value columns).
+// The formulas and the state pass's register layout are those of la_chunk.hpp.
+#include "la_chunk.hpp"
+
+namespace la {
+
+ChunkParams make_chunk_params(const la_config& c) {
+    ChunkParams p;
+    p.B = c.B; p.T = c.T; p.H = c.H; p.dv = c.d_v;
+    p.nch = (c.T + kCh - 1) / kCh;
+    p.ntile = c.d_v / 64;
+    p.qkv_dt = c.qkv_dtype; p.gate_dt = c.gate_dtype; p.out_dt = c.out_dtype;
+    p.qdq_interval = c.qdq == LA_QDQ_NONE ? 1 : c.qdq_interval;
+    p.ckpt_interval = c.ckpt_interval > 0 ? c.ckpt_interval : 1;
+    p.nck = n_ckpts(c);
+    p.degree = c.solve == LA_SOLVE_NEUMANN ? c.degree : 0;
+    return p;
+}
+
+bool chunk_eligible(const la_config& c) {
+    if (c.d_k != kChDk || c.hadamard || c.replay || c.state_rotated) return false;
+    if (c.qdq != LA_QDQ_NONE && c.qdq_interval % kCh != 0) return false;
+    if (c.ckpt_interval > 0 && c.ckpt_interval % kCh != 0) return false;
+    return true;
+}
+
+size_t chunk_fwd_workspace_bytes(const la_config& c) {
+    const size_t nch = (static_cast<size_t>(c.T) + kCh - 1) / kCh;
+    return static_cast<size_t>(c.B) * c.H * nch * RecF::SIZE * sizeof(float);
+}
+
+namespace {
+
+constexpr int kPW = 68;   // pitch of the prep kernel's 64 x 64 work matrices
+constexpr int kPT = 132;  // pitch of its token-by-key arrays
+
+// C = A B (+ Cadd) for 64 x 64 fp32 matrices in LDS (pitch kPW) on the matrix cores; wave w
+// forms rows 16 w .. 16 w + 15.  The barrier between the products and the stores lets C alias
+// A, B or Cadd.  Every thread of the workgroup must call it.
+__device__ void mm64(const float* A, const float* B, float* C, const float* Cadd) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    f4 acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[ct][r] = Cadd ? Cadd[(16 * w + 4 * g + r) * kPW + 16 * ct + c] : 0.0f;
+#pragma unroll 4
+    for (int s = 0; s < 16; s++) {
+        const float a = A[(16 * w + c) * kPW + 4 * s + g];
+#pragma unroll
+        for (int ct = 0; ct < 4; ct++) acc[ct] = mfma4(a, B[(4 * s + g) * kPW + 16 * ct + c], acc[ct]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) C[(16 * w + 4 * g + r) * kPW + 16 * ct + c] = acc[ct][r];
+    __syncthreads();
+}
+
+// Prep: A, M, the solve P, Kp, Qp, Kd, E_L of one chunk into its record (forward or backward
+// layout).  Tokens past the sequence's end are zero rows (their beta, k and q are zero).
+template <bool KDA, bool BWD>
+__global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p, ChunkIn in, float* __restrict__ rec) {
+    __shared__ __align__(16) float big[3 * kCh * kPT];
+    __shared__ float Am[kCh * kPW], Mm[kCh * kPW];
+    __shared__ float bS[kCh], gS[kCh];
+    float* kS = big;
+    float* qS = big + kCh * kPT;
+    float* GS = big + 2 * kCh * kPT;
+    const int t = threadIdx.x;
+    const int cc = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int H = p.H, T = p.T;
+    const int t0 = cc * kCh, L = min(kCh, T - t0);
+    const size_t tok0 = (static_cast<size_t>(b) * T + t0) * H + h;
+    float* R = rec + ((static_cast<size_t>(b) * H + h) * p.nch + cc) * (BWD ? RecB::SIZE : RecF::SIZE);
+
+    for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
+        const int r = idx >> 7, kk = idx & 127;
+        float kv = 0.0f, qv = 0.0f;
+        if (r < L) {
+            const size_t e = (tok0 + static_cast<size_t>(r) * H) * kChDk + kk;
+            kv = load_elem(in.k, e, p.qkv_dt);
+            qv = load_elem(in.q, e, p.qkv_dt);
+        }
+        kS[r * kPT + kk] = kv;
+        qS[r * kPT + kk] = qv;
+    }
+    if (t < kCh) {
+        const bool ok = t < L;
+        bS[t] = ok ? load_elem(in.beta, tok0 + static_cast<size_t>(t) * H, p.gate_dt) : 0.0f;
+        if (!KDA) gS[t] = ok ? load_elem(in.g, tok0 + static_cast<size_t>(t) * H, p.gate_dt) : 0.0f;
+    }
+    if (KDA) {
+        // cumulative log decays per key; rows past the end repeat G_{L-1}
+        if (t < kChDk) {
+            float run = 0.0f;
+#pragma unroll 8
+            for (int r = 0; r < kCh; r++) {
+                if (r < L) run += load_elem(in.g, (tok0 + static_cast<size_t>(r) * H) * kChDk + t, p.gate_dt);
+                GS[r * kPT + t] = run;
+            }
+        }
+    } else {
+        __syncthreads();
+        if (t == 0) {
+            float run = 0.0f;
+            for (int r = 0; r < kCh; r++) {
+                if (r < L) run += gS[r];
+                gS[r] = run;
+            }
+        }
+    }
+    __syncthreads();
+    auto Gof = [&](int r, int kk) __attribute__((always_inline)) { return KDA ? GS[r * kPT + kk] : gS[r]; };
+
+    // decayed keys and queries
+    for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
+        const int r = idx >> 7, kk = idx & 127;
+        const float G = Gof(r, kk);
+        const float E = expf(G);
+        const float kv = kS[r * kPT + kk], qv = qS[r * kPT + kk];
+        if (BWD) {
+            const float F = expf(Gof(L - 1, kk) - G);
+            R[RecB::KP + r * RecB::PK + kk] = kv * E;
+            R[RecB::QP + r * RecB::PK + kk] = qv * E;
+            R[RecB::KD + r * RecB::PKD + kk] = kv * F;
+        } else {
+            R[RecF::KP + r * RecF::PK + kk] = kv * E;
+            R[RecF::QP + r * RecF::PK + kk] = qv * E;
+        }
+    }
+    if (!BWD) {
+        for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
+            const int kk = idx >> 6, r = idx & 63;
+            R[RecF::KDT + kk * RecF::PD + r] = kS[r * kPT + kk] * expf(Gof(L - 1, kk) - Gof(r, kk));
+        }
+    }
+    if (t < kChDk) R[(BWD ? RecB::EL : RecF::EL) + t] = expf(Gof(L - 1, t));
+
+    // A (strictly lower) and M (lower with the diagonal)
+    if (KDA) {
+        // per-key decays inside the sums: thread t forms rows r1 = t / 8 and r2 = 63 - r1 at
+        // columns (t % 8) + 8 j, so every thread has 65 row-column pairs' worth of work
+        const int r1 = t >> 3, r2 = 63 - r1, i0 = t & 7;
+        float a1[8], m1[8], a2[8], m2[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) a1[j] = m1[j] = a2[j] = m2[j] = 0.0f;
+#pragma unroll 2
+        for (int kk = 0; kk < kChDk; kk++) {
+            const float k1 = kS[r1 * kPT + kk], q1 = qS[r1 * kPT + kk], G1 = GS[r1 * kPT + kk];
+            const float k2 = kS[r2 * kPT + kk], q2 = qS[r2 * kPT + kk], G2 = GS[r2 * kPT + kk];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int i = i0 + 8 * j;
+                const float ki = kS[i * kPT + kk], Gi = GS[i * kPT + kk];
+                const float kd1 = ki * __expf(i <= r1 ? G1 - Gi : 0.0f);
+                const float kd2 = ki * __expf(i <= r2 ? G2 - Gi : 0.0f);
+                a1[j] = __builtin_fmaf(k1, kd1, a1[j]);
+                m1[j] = __builtin_fmaf(q1, kd1, m1[j]);
+                a2[j] = __builtin_fmaf(k2, kd2, a2[j]);
+                m2[j] = __builtin_fmaf(q2, kd2, m2[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int i = i0 + 8 * j;
+            Am[r1 * kPW + i] = i < r1 ? bS[r1] * a1[j] : 0.0f;
+            Mm[r1 * kPW + i] = i <= r1 ? m1[j] : 0.0f;
+            Am[r2 * kPW + i] = i < r2 ? bS[r2] * a2[j] : 0.0f;
+            Mm[r2 * kPW + i] = i <= r2 ? m2[j] : 0.0f;
+        }
+    } else {
+        // one decay per token pair: K K^T and Q K^T on the matrix cores, then the decay
+        const int lane = t & 63, w = t >> 6, g = lane >> 4, c = lane & 15;
+        for (int tl = w; tl < 16; tl += 4) {
+            const int rt = tl >> 2, ct = tl & 3;
+            f4 ak = {0.0f, 0.0f, 0.0f, 0.0f}, aq = ak;
+            if (rt >= ct) {
+#pragma unroll 4
+                for (int s = 0; s < 32; s++) {
+                    const float bk = kS[(16 * ct + c) * kPT + 4 * s + g];
+                    ak = mfma4(kS[(16 * rt + c) * kPT + 4 * s + g], bk, ak);
+                    aq = mfma4(qS[(16 * rt + c) * kPT + 4 * s + g], bk, aq);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = 16 * rt + 4 * g + r, i = 16 * ct + c;
+                const float gam = i <= row ? expf(gS[row] - gS[i]) : 0.0f;
+                Am[row * kPW + i] = i < row ? bS[row] * (gam * ak[r]) : 0.0f;
+                Mm[row * kPW + i] = gam * aq[r];
+            }
+        }
+    }
+    __syncthreads();
+
+    // the solve, in the token arrays' space
+    float* W0 = big;
+    float* W1 = big + kCh * kPW;
+    float* red = big + 2 * kCh * kPW;
+    const float* Pm;
+    if (p.degree == 0) {
+        // (I + A)^-1 by forward substitution, one row at a time, four partial sums per column
+        const int j = t & 63, part = t >> 6;
+        for (int r = 0; r < kCh; r++) {
+            float acc = 0.0f;
+            for (int i = part; i < r; i += 4) acc = __builtin_fmaf(Am[r * kPW + i], W0[i * kPW + j], acc);
+            red[part * kCh + j] = acc;
+            __syncthreads();
+            if (part == 0)
+                W0[r * kPW + j] = (j == r ? 1.0f : 0.0f) - ((red[j] + red[kCh + j]) + (red[2 * kCh + j] + red[3 * kCh + j]));
+            __syncthreads();
+        }
+        Pm = W0;
+    } else {
+        // sum_{n <= d} X^n, X = -A, d = 2^m - 1, as (I + X)(I + X^2)(I + X^4) ...: Z holds X^(2^j),
+        // P the product so far
+        for (int idx = t; idx < kCh * kCh; idx += kChThreads) {
+            const int r = idx >> 6, i = idx & 63;
+            const float x = -Am[r * kPW + i];
+            W0[r * kPW + i] = x;
+            W1[r * kPW + i] = r == i ? 1.0f + x : x;
+        }
+        __syncthreads();
+        for (int done = 1; done < p.degree; done = 2 * done + 1) {
+            mm64(W0, W0, W0, nullptr);  // Z <- Z Z
+            mm64(W1, W0, W1, W1);       // P <- P + P Z
+        }
+        Pm = W1;
+    }
+
+    for (int idx = t; idx < kCh * kCh; idx += kChThreads) {
+        const int r = idx >> 6, i = idx & 63;
+        if (BWD) {
+            R[RecB::P + r * RecB::PP + i] = Pm[r * kPW + i];
+            R[RecB::M + r * RecB::PP + i] = Mm[r * kPW + i];
+            R[RecB::A + r * RecB::PA + i] = Am[r * kPW + i];
+        } else {
+            R[RecF::P + r * RecF::PP + i] = Pm[r * kPW + i];
+            R[RecF::M + r * RecF::PP + i] = Mm[r * kPW + i];
+        }
+    }
+}
+
+// State pass: chunks in order, the state of 64 value columns in registers (la_chunk.hpp map);
+// outputs, checkpoints every ckpt_interval tokens, rounding at the chunk ends that are
+// rounding points, the final state.
+template <int QMODE, int G>
+__global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p, ChunkIn in, const float* __restrict__ S0,
+                                                                  void* o, float* ST, float* ckpts,
+                                                                  const float* __restrict__ rec) {
+    __shared__ __align__(16) float R[RecF::SIZE];
+    __shared__ WaveQdqShared<kChDk, QMODE, G> qsh;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    int tile, bh;
+    chunk_tile_of(blockIdx.x, p.ntile, tile, bh);
+    if (bh >= p.B * p.H) return;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int dv = p.dv, col = tile * 64 + 16 * w + c;
+    const size_t soff = static_cast<size_t>(bh) * kChDk * dv + col;
+    float s[32];
+#pragma unroll
+    for (int m = 0; m < 32; m++) s[m] = S0 ? S0[soff + static_cast<size_t>(kmap(m, g)) * dv] : 0.0f;
+    int qpar = 0;
+    for (int cc = 0; cc < p.nch; cc++) {
+        const int t0 = cc * kCh, L = min(kCh, p.T - t0);
+        if (ckpts && t0 % p.ckpt_interval == 0) {
+            float* dst = ckpts + (static_cast<size_t>(bh) * p.nck + t0 / p.ckpt_interval) * kChDk * dv + col;
+#pragma unroll
+            for (int m = 0; m < 32; m++) dst[static_cast<size_t>(kmap(m, g)) * dv] = s[m];
+        }
+        __syncthreads();  // every wave is done with the previous record
+        copy_to_lds(R, rec + (static_cast<size_t>(bh) * p.nch + cc) * RecF::SIZE, RecF::SIZE);
+        const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
+        float vv[16], bb[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int tk = kmap(i, g);
+            const bool ok = tk < L;
+            const size_t e = tok0 + static_cast<size_t>(tk) * p.H;
+            vv[i] = ok ? load_elem(in.v, e * dv + col, p.qkv_dt) : 0.0f;
+            bb[i] = ok ? load_elem(in.beta, e, p.gate_dt) : 0.0f;
+        }
+        __syncthreads();
+
+        // X = Kp S, Y = Qp S
+        f4 X[4], Y[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; rt++) X[rt] = Y[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 32; m++) {
+            const int key = kmap(m, g);
+#pragma unroll
+            for (int rt = 0; rt < 4; rt++) {
+                const int row = cmap(rt, c) * RecF::PK + key;
+                X[rt] = mfma4(R[RecF::KP + row], s[m], X[rt]);
+                Y[rt] = mfma4(R[RecF::QP + row], s[m], Y[rt]);
+            }
+        }
+        // beta (V - X), then Delta = P (beta (V - X))
+        float rv[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) rv[i] = bb[i] * (vv[i] - X[i >> 2][i & 3]);
+        f4 D[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; rt++) D[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            const int tk = kmap(m, g);
+#pragma unroll
+            for (int rt = 0; rt < 4; rt++) D[rt] = mfma4(R[RecF::P + cmap(rt, c) * RecF::PP + tk], rv[m], D[rt]);
+        }
+        // O = Y + M Delta
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            const int tk = kmap(m, g);
+            const float dm = D[m >> 2][m & 3];
+#pragma unroll
+            for (int rt = 0; rt < 4; rt++) Y[rt] = mfma4(R[RecF::M + cmap(rt, c) * RecF::PP + tk], dm, Y[rt]);
+        }
+        if (o) {
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int tk = kmap(i, g);
+                if (tk < L) store_elem(o, (tok0 + static_cast<size_t>(tk) * p.H) * dv + col, p.out_dt, Y[i >> 2][i & 3]);
+            }
+        }
+        // S_end = diag(E_L) S + Kd^T Delta
+#pragma unroll
+        for (int kt = 0; kt < 8; kt++) {
+            f4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[r] = R[RecF::EL + 16 * kt + 4 * r + g] * s[4 * kt + r];
+#pragma unroll
+            for (int m = 0; m < 16; m++)
+                acc = mfma4(R[RecF::KDT + cmap(kt, c) * RecF::PD + kmap(m, g)], D[m >> 2][m & 3], acc);
+#pragma unroll
+            for (int r = 0; r < 4; r++) s[4 * kt + r] = acc[r];
+        }
+        if (QMODE != LA_QDQ_NONE && ((t0 + L) % p.qdq_interval == 0 || t0 + L == p.T))
+            wave_quantize<32, QMODE, G, kChDk>(s, qsh, lane, w, qpar);
+    }
+    if (ST) {
+#pragma unroll
+        for (int m = 0; m < 32; m++) ST[soff + static_cast<size_t>(kmap(m, g)) * dv] = s[m];
+    }
+}
+
+template <int QMODE, int G>
+hipError_t launch_chunk_state(const la_config& c, const ChunkParams& p, const ChunkIn& in, const float* S0, void* o,
+                              float* ST, float* ckpts, const float* rec, hipStream_t s) {
+    hipLaunchKernelGGL((chunk_fwd_kernel<QMODE, G>), dim3(chunk_tile_blocks(c.B * c.H, p.ntile)), dim3(kChThreads), 0,
+                       s, p, in, S0, o, ST, ckpts, rec);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_prep(const la_config& c, const ChunkIn& in, float* rec, bool bwd, hipStream_t s) {
+    const ChunkParams p = make_chunk_params(c);
+    const dim3 grid(p.nch, c.H, c.B);
+    const bool kda = c.gate == LA_GATE_KEY;
+    if (bwd) {
+        if (kda) hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(kChThreads), 0, s, p, in, rec);
+        else hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(kChThreads), 0, s, p, in, rec);
+    } else {
+        if (kda) hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(kChThreads), 0, s, p, in, rec);
+        else hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(kChThreads), 0, s, p, in, rec);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_fwd(const la_config& c, const FwdArgs& a, float* rec, hipStream_t s) {
+    const ChunkParams p = make_chunk_params(c);
+    const ChunkIn in{a.q, a.k, a.v, a.g, a.beta};
+    hipError_t e = launch_chunk_prep(c, in, rec, false, s);
+    if (e != hipSuccess) return e;
+    if (c.qdq == LA_QDQ_NONE) return launch_chunk_state<LA_QDQ_NONE, 1>(c, p, in, a.S0, a.o, a.ST, a.ckpts, rec, s);
+    if (c.qdq == LA_QDQ_E4M3_TILE)
+        return launch_chunk_state<LA_QDQ_E4M3_TILE, 64>(c, p, in, a.S0, a.o, a.ST, a.ckpts, rec, s);
+    switch (c.group) {
+        case 16: return launch_chunk_state<LA_QDQ_INT8_GROUP, 16>(c, p, in, a.S0, a.o, a.ST, a.ckpts, rec, s);
+        case 32: return launch_chunk_state<LA_QDQ_INT8_GROUP, 32>(c, p, in, a.S0, a.o, a.ST, a.ckpts, rec, s);
+        default: return launch_chunk_state<LA_QDQ_INT8_GROUP, 64>(c, p, in, a.S0, a.o, a.ST, a.ckpts, rec, s);
+    }
+}
+
+}  // namespace la

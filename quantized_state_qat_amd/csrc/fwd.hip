@@ -23,6 +23,9 @@ Params make_params(const la_config& c) {
 }
 
 la_kernel fwd_kernel(const la_config& c) {
+    // the Neumann solve defines a different function: the chunk kernel or nothing
+    if (c.solve == LA_SOLVE_NEUMANN || c.kernel == LA_KERNEL_CHUNK)
+        return chunk_eligible(c) ? LA_KERNEL_CHUNK : LA_KERNEL_AUTO;
     switch (c.kernel) {
         case LA_KERNEL_BLOCK: return fwd_mfma_eligible(c) ? LA_KERNEL_BLOCK : LA_KERNEL_AUTO;
         case LA_KERNEL_WAVE: return fwd_wave_eligible(c) ? LA_KERNEL_WAVE : LA_KERNEL_AUTO;
@@ -42,6 +45,7 @@ const char* fwd_kernel_name(const la_config& c) {
         case LA_KERNEL_WAVE: return "wave";
         case LA_KERNEL_FAST: return "fast";
         case LA_KERNEL_TOKEN: return "token";
+        case LA_KERNEL_CHUNK: return "chunk";
         default: return "";
     }
 }

@@ -49,8 +49,16 @@ la_status check_config(const la_config* c, bool decode) {
         return fail(LA_ERR_INVALID_ARG, "state_rotated must be 0 or 1");
     if (c->state_rotated && !c->hadamard)
         return fail(LA_ERR_INVALID_ARG, "state_rotated needs the Hadamard rotation");
-    if (c->kernel < LA_KERNEL_AUTO || c->kernel > LA_KERNEL_TOKEN)
+    if (c->kernel < LA_KERNEL_AUTO || c->kernel > LA_KERNEL_CHUNK)
         return fail(LA_ERR_INVALID_ARG, "unknown kernel %d", c->kernel);
+    if (c->solve != LA_SOLVE_EXACT && c->solve != LA_SOLVE_NEUMANN)
+        return fail(LA_ERR_INVALID_ARG, "unknown solve %d", c->solve);
+    if (c->solve == LA_SOLVE_NEUMANN && c->degree != 3 && c->degree != 7 && c->degree != 15 && c->degree != 31)
+        return fail(LA_ERR_INVALID_ARG, "Neumann degree must be 3, 7, 15 or 31 (degree=%d)", c->degree);
+    if (c->solve == LA_SOLVE_EXACT && c->degree != 0)
+        return fail(LA_ERR_INVALID_ARG, "degree is the Neumann solve's (set solve = 1) and must be 0 otherwise");
+    if (decode && c->solve != LA_SOLVE_EXACT)
+        return fail(LA_ERR_INVALID_ARG, "the decode steps have no chunks: solve must be exact");
     if (c->replay != 0 && c->replay != 1) return fail(LA_ERR_INVALID_ARG, "replay must be 0 or 1");
     if (c->replay && c->qdq == LA_QDQ_NONE)
         return fail(LA_ERR_INVALID_ARG, "replay windows end in a rounding point: they need a quantizer");
@@ -178,6 +186,7 @@ const char* la_fwd_kernel_name(const la_config* cfg) {
 
 const char* la_bwd_kernel_name(const la_config* cfg) {
     if (check_config(cfg, false) != LA_OK || check_kernel(*cfg) != LA_OK) return "";
+    if (la::fwd_kernel(*cfg) == LA_KERNEL_CHUNK) return "chunk";
     return la::bwd_mfma_eligible(*cfg) ? "block" : "token";
 }
 
@@ -187,6 +196,8 @@ la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, c
     CHECK(check_config(cfg, false));
     const la_config& c = *cfg;
     CHECK(check_kernel(c));
+    if (la::fwd_kernel(c) == LA_KERNEL_CHUNK)
+        return fail(LA_ERR_UNSUPPORTED, "the chunk kernel needs a workspace: call la_recurrent_fwd_chunk");
     const bool work = c.B > 0 && c.H > 0 && c.T > 0;
     CHECK(check_ptr(q, "q", work));
     CHECK(check_ptr(k, "k", work));
@@ -206,6 +217,46 @@ la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, c
     }
     la::FwdArgs a{q, k, v, g, beta, S0, o, S_T, ckpts};
     return hip_status(la::launch_fwd(c, a, s), "la_recurrent_fwd launch");
+}
+
+size_t la_chunk_workspace_bytes(const la_config* cfg) {
+    if (check_config(cfg, false) != LA_OK || la::fwd_kernel(*cfg) != LA_KERNEL_CHUNK) return 0;
+    return la::chunk_fwd_workspace_bytes(*cfg);
+}
+
+la_status la_recurrent_fwd_chunk(const la_config* cfg, const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta, const float* S0, void* o,
+                                 float* S_T, float* ckpts, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+    CHECK(check_config(cfg, false));
+    const la_config& c = *cfg;
+    if (la::fwd_kernel(c) != LA_KERNEL_CHUNK)
+        return fail(LA_ERR_UNSUPPORTED, "the chunk kernel needs kernel = LA_KERNEL_CHUNK (or the Neumann solve), "
+                    "d_k = 128, no rotation or replay, rounding points and checkpoints on multiples of 64");
+    const bool work = c.B > 0 && c.H > 0 && c.T > 0;
+    CHECK(check_ptr(q, "q", work));
+    CHECK(check_ptr(k, "k", work));
+    CHECK(check_ptr(v, "v", work));
+    CHECK(check_ptr(g, "g", work));
+    CHECK(check_ptr(beta, "beta", work));
+    CHECK(check_ptr(o, "o", work));
+    CHECK(check_ptr(S0, "S0", false));
+    CHECK(check_ptr(S_T, "S_T", false));
+    CHECK(check_ptr(ckpts, "ckpts", false));
+    CHECK(check_ptr(workspace, "workspace", false));
+    if (ckpts && c.ckpt_interval < 1) return fail(LA_ERR_INVALID_ARG, "ckpts given but ckpt_interval < 1");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (c.B == 0 || c.H == 0) return ok();
+    if (c.T == 0) {
+        if (!S_T) return ok();
+        return hip_status(la::launch_copy_state(c, S0, S_T, s), "copy S0 -> S_T");
+    }
+    const size_t need = la::chunk_fwd_workspace_bytes(c);
+    if (!workspace || ws_bytes < need)
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? ws_bytes : static_cast<size_t>(0));
+    la::FwdArgs a{q, k, v, g, beta, S0, o, S_T, ckpts};
+    return hip_status(la::launch_chunk_fwd(c, a, static_cast<float*>(workspace), s), "la_recurrent_fwd_chunk launch");
 }
 
 la_status la_recurrent_fwd_entries(const la_config* cfg, const void* q, const void* k, const void* v,
@@ -243,8 +294,9 @@ la_status la_recurrent_fwd_varlen(const la_config* cfg, const int32_t* cu_seqlen
                                   const float* S0, void* o, float* S_T, void* stream) {
     CHECK(check_config(cfg, false));
     const la_config& c = *cfg;
-    if (c.kernel != LA_KERNEL_AUTO && c.kernel != LA_KERNEL_TOKEN)
-        return fail(LA_ERR_UNSUPPORTED, "packed sequences run on the per-token kernel only (kernel=%d)", c.kernel);
+    if ((c.kernel != LA_KERNEL_AUTO && c.kernel != LA_KERNEL_TOKEN) || c.solve != LA_SOLVE_EXACT)
+        return fail(LA_ERR_UNSUPPORTED, "packed sequences run on the per-token kernel only (kernel=%d, solve=%d)",
+                    c.kernel, c.solve);
     const bool units = c.B > 0 && c.H > 0;
     const bool work = units && c.T > 0;
     CHECK(check_ptr(cu_seqlens, "cu_seqlens", units));
@@ -351,7 +403,7 @@ la_status la_decode_step_replay(const la_config* cfg, const void* q, const void*
 
 size_t la_bwd_varlen_workspace_bytes(const la_config* cfg) {
     if (check_config(cfg, false) != LA_OK || cfg->ckpt_interval < 1) return 0;
-    if (cfg->kernel != LA_KERNEL_AUTO && cfg->kernel != LA_KERNEL_TOKEN) return 0;
+    if ((cfg->kernel != LA_KERNEL_AUTO && cfg->kernel != LA_KERNEL_TOKEN) || cfg->solve != LA_SOLVE_EXACT) return 0;
     return ws_layout_varlen(*cfg).total;
 }
 
@@ -437,6 +489,7 @@ la_status la_recurrent_bwd_ste_split(const la_config* prefix_cfg, const la_confi
 
 size_t la_bwd_workspace_bytes(const la_config* cfg) {
     if (check_config(cfg, false) != LA_OK || check_kernel(*cfg) != LA_OK || cfg->ckpt_interval < 1) return 0;
+    if (la::fwd_kernel(*cfg) == LA_KERNEL_CHUNK) return 0;
     return ws_layout(*cfg).total;
 }
 
@@ -460,6 +513,8 @@ la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void
     CHECK(check_config(cfg, false));
     const la_config& c = *cfg;
     CHECK(check_kernel(c));
+    if (la::fwd_kernel(c) == LA_KERNEL_CHUNK)
+        return fail(LA_ERR_UNSUPPORTED, "the chunk form's backward is not available");
     if (c.ckpt_interval < 1) return fail(LA_ERR_INVALID_ARG, "backward needs ckpt_interval >= 1");
     const bool units = c.B > 0 && c.H > 0;
     const bool work = units && c.T > 0;
@@ -531,8 +586,9 @@ la_status check_split(const la_config* a, const la_config* b) {
     if (a->state_rotated || b->state_rotated)
         return fail(LA_ERR_UNSUPPORTED, "the handoff state is the unrotated S (state_rotated must be 0)");
     for (const la_config* c : {a, b})
-        if (c->kernel != LA_KERNEL_AUTO && c->kernel != LA_KERNEL_TOKEN)
-            return fail(LA_ERR_UNSUPPORTED, "packed sequences run on the per-token kernel only (kernel=%d)", c->kernel);
+        if ((c->kernel != LA_KERNEL_AUTO && c->kernel != LA_KERNEL_TOKEN) || c->solve != LA_SOLVE_EXACT)
+            return fail(LA_ERR_UNSUPPORTED, "packed sequences run on the per-token kernel only (kernel=%d, solve=%d)",
+                        c->kernel, c->solve);
     return LA_OK;
 }
 
@@ -540,8 +596,9 @@ la_status bwd_varlen(const la_config& c, const int32_t* cu_seqlens, const int32_
                      const void* k, const void* v, const void* g, const void* beta, const float* S0,
                      const float* dout, const float* dS_T, float* dq, float* dk, float* dv, float* dg,
                      float* dbeta, float* dS0, void* workspace, size_t ws_bytes, void* stream) {
-    if (c.kernel != LA_KERNEL_AUTO && c.kernel != LA_KERNEL_TOKEN)
-        return fail(LA_ERR_UNSUPPORTED, "packed sequences run on the per-token kernel only (kernel=%d)", c.kernel);
+    if ((c.kernel != LA_KERNEL_AUTO && c.kernel != LA_KERNEL_TOKEN) || c.solve != LA_SOLVE_EXACT)
+        return fail(LA_ERR_UNSUPPORTED, "packed sequences run on the per-token kernel only (kernel=%d, solve=%d)",
+                    c.kernel, c.solve);
     if (c.ckpt_interval < 1) return fail(LA_ERR_INVALID_ARG, "backward needs ckpt_interval >= 1");
     const bool units = c.B > 0 && c.H > 0;
     const bool work = units && c.T > 0;

@@ -118,6 +118,12 @@ hipError_t launch_fwd_mfma(const la_config& c, const FwdArgs& a, hipStream_t s);
 bool fwd_wave_eligible(const la_config& c);
 hipError_t launch_fwd_wave(const la_config& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_tok(const la_config& c, const FwdArgs& a, hipStream_t s);
+// 64-token chunk path (chunk_fwd.hip): d_k = 128, no rotation, no replay, rounding points and
+// checkpoints on chunk ends.  The forward prepares every chunk's matrices into `records`
+// (chunk_fwd_workspace_bytes) and then runs the state pass.
+bool chunk_eligible(const la_config& c);
+size_t chunk_fwd_workspace_bytes(const la_config& c);
+hipError_t launch_chunk_fwd(const la_config& c, const FwdArgs& a, float* records, hipStream_t s);
 hipError_t launch_copy_state(const la_config& c, const float* src, float* dst, hipStream_t s);
 hipError_t launch_bwd(const la_config& c, const BwdArgs& a, hipStream_t s);
 // Token range [begin, end) of packed sequence b (part of it when split is given), on the

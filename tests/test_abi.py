@@ -26,7 +26,8 @@ def test_library_exports_every_declared_function():
                           "la_status_string", "la_last_error", "la_recurrent_bwd_ste_noalloc",
                           "la_noalloc_workspace_limit", "la_recurrent_fwd_entries", "la_decode_step_replay",
                           "la_recurrent_fwd_split", "la_recurrent_bwd_ste_varlen", "la_bwd_varlen_workspace_bytes",
-                          "la_recurrent_bwd_ste_split", "la_bwd_split_workspace_bytes"}
+                          "la_recurrent_bwd_ste_split", "la_bwd_split_workspace_bytes", "la_recurrent_fwd_chunk",
+                          "la_chunk_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -338,3 +339,71 @@ def test_binding_rejects_bad_tensors():
         la.la_decode_step_slots(cfg(T=1), good["q"], good["k"], good["v"], good["g"], good["beta"],
                                 FakeDeviceTensor(3 * c.H * c.d_k * c.d_v, torch.float32),
                                 FakeDeviceTensor(c.B, torch.int64), 3, good["o"], stream=0)
+
+
+CHUNK_OK = dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64)
+
+
+def chunk_fwd(c, ws=FAKE, ws_bytes=1 << 40):
+    return la.la_recurrent_fwd_chunk(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, ws, ws_bytes, stream=0)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(solve=1, degree=5), la.LA_ERR_INVALID_ARG, "Neumann degree"),
+    (dict(solve=1, degree=63), la.LA_ERR_INVALID_ARG, "Neumann degree"),
+    (dict(solve=0, degree=3), la.LA_ERR_INVALID_ARG, "degree"),
+    (dict(solve=2), la.LA_ERR_INVALID_ARG, "solve"),
+])
+def test_solve_field_checks(kw, status, msg):
+    base = dict(CHUNK_OK)
+    base.update(kw)
+    with pytest.raises(la.LaError) as e:
+        chunk_fwd(cfg(**base))
+    assert e.value.status == status and msg in str(e.value)
+
+
+def test_chunk_kernel_selection_and_workspace():
+    for solve, degree, kernel in ((la.LA_SOLVE_NEUMANN, 7, la.LA_KERNEL_AUTO), (la.LA_SOLVE_EXACT, 0, la.LA_KERNEL_CHUNK)):
+        c = cfg(T=150, solve=solve, degree=degree, kernel=kernel, **CHUNK_OK)
+        assert la.la_fwd_kernel_name(c) == "chunk"
+        assert la.la_chunk_workspace_bytes(c) == c.B * c.H * 3 * 34432 * 4
+        # the plain forward has no workspace argument: the chunk kernel is refused there
+        with pytest.raises(la.LaError) as e:
+            fwd(c)
+        assert e.value.status == la.LA_ERR_UNSUPPORTED and "la_recurrent_fwd_chunk" in str(e.value)
+        with pytest.raises(la.LaError) as e:
+            chunk_fwd(c, ws=None, ws_bytes=0)
+        assert e.value.status == la.LA_ERR_WORKSPACE
+        with pytest.raises(la.LaError) as e:
+            chunk_fwd(c, ws_bytes=la.la_chunk_workspace_bytes(c) - 1)
+        assert e.value.status == la.LA_ERR_WORKSPACE
+    # the exact solve with automatic choice never picks the chunk kernel
+    c = cfg(T=150, **CHUNK_OK)
+    assert la.la_fwd_kernel_name(c) != "chunk" and la.la_chunk_workspace_bytes(c) == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(d_k=64), dict(qdq_interval=32), dict(ckpt_interval=16), dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, hadamard=1),
+    dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, replay=1),
+])
+def test_chunk_kernel_cannot_serve(kw):
+    base = dict(CHUNK_OK)
+    base.update(kw)
+    c = cfg(T=150, solve=la.LA_SOLVE_NEUMANN, degree=3, **base)
+    assert la.la_fwd_kernel_name(c) == ""
+    assert la.la_chunk_workspace_bytes(c) == 0
+    with pytest.raises(la.LaError) as e:
+        chunk_fwd(c)
+    assert e.value.status == la.LA_ERR_UNSUPPORTED
+
+
+def test_token_only_entries_refuse_the_neumann_solve():
+    c = cfg(T=1, solve=la.LA_SOLVE_NEUMANN, degree=3, **CHUNK_OK)
+    with pytest.raises(la.LaError) as e:
+        la.la_decode_step(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == la.LA_ERR_INVALID_ARG
+    c = cfg(T=150, solve=la.LA_SOLVE_NEUMANN, degree=3, **CHUNK_OK)
+    with pytest.raises(la.LaError) as e:
+        la.la_recurrent_fwd_varlen(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, stream=0)
+    assert e.value.status == la.LA_ERR_UNSUPPORTED
+    assert la.la_bwd_varlen_workspace_bytes(c) == 0
