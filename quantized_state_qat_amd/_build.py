@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblaqat.so")
 SOURCES = ["la_api.cpp", "fwd.hip", "fwd_fast.hip", "fwd_wave.hip", "fwd_mfma.hip", "fwd_tok.hip", "decode.hip", "bwd.hip",
-           "bwd_mfma.hip", "noalloc.hip", "chunk_fwd.hip"]
+           "bwd_mfma.hip", "noalloc.hip", "chunk_fwd.hip", "chunk_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

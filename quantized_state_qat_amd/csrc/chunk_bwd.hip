@@ -1,0 +1,643 @@
+// 64-token chunk path, straight-through backward (the chain rule through each chunk's terms of
+// la_chunk.hpp, identity through every rounding; "Experimental GDN/KDA approximate-inverse QAT",
+// What does this PR do?: the backward differentiates the polynomial actually used).  From the
+// forward's checkpoints (one per chunk), four launches:
+//   prep      the chunk records in the backward layout (chunk_fwd.hip's prep kernel);
+//   recompute U = V - Kp S and Delta = P diag(beta) U of every chunk, all chunks in parallel;
+//   dstate    per (sequence, head, 64 value columns), chunks last to first: dS carried in
+//             registers, dDelta = Kd dS_end + M^T dO, dR = P^T dDelta, dv = beta dR, the partial
+//             beta gradient, dS <- E_L dS + Qp^T dO - Kp^T dv; dS0 at the end;
+//   grad      per (sequence, head, chunk): the products over value columns (dP = dDelta R^T,
+//             dM = dO Delta^T, dQp = dO S^T, dKp = -dv S^T, dKd = Delta dS_end^T, dE_L), the
+//             backward of the solve, the decays and the pair sums, and the gate gradient as a
+//             suffix sum of the cumulative-decay gradient.
+#include "la_chunk.hpp"
+
+namespace la {
+
+ChunkParams make_chunk_params(const la_config& c);
+hipError_t launch_chunk_prep(const la_config& c, const ChunkIn& in, float* rec, bool bwd, hipStream_t s);
+
+namespace {
+
+constexpr int kSP = 20;             // pitch of the gradient kernel's 16-column slabs
+constexpr int kTK = kCh * 132;      // one token-by-key array (pitch 132)
+constexpr int kWM = kCh * kPW;      // one 64 x 64 work matrix
+constexpr int kBig = 6 * kWM;       // the gradient kernel's phase-shared LDS (floats)
+static_assert(5 * kCh * kSP + 2 * kChDk * kSP <= 3 * kWM, "slabs overlap the dP buffer");
+static_assert(3 * kTK <= kBig && 2 * kTK + kWM <= kBig, "phase buffers exceed the shared array");
+
+struct ChunkBwdPtrs {
+    const float* ckpts;   // [B][H][nch][128][d_v], the state entering every chunk
+    const float* dout;
+    const float* dST;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dg;
+    float* dbeta;
+    float* dS0;
+    float* rec;           // [B H nch] backward records
+    float* U;             // [B H nch][64][d_v]
+    float* D;             // Delta, same layout
+    float* dD;            // dDelta, same layout
+    float* dSe;           // [B H nch][128][d_v]: dL/d(state after the chunk)
+    float* dbp;           // [ntile][B H nch][64]: beta-gradient partial per value tile
+    float* dGw;           // [B H nch][64][128]: cumulative-decay gradient of the elementwise terms
+};
+
+// U and Delta of one (sequence, head, chunk, 64 columns) from the chunk's checkpoint.
+__global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams p, ChunkIn in, ChunkBwdPtrs a) {
+    __shared__ __align__(16) float Kp_s[kCh * RecB::PK];
+    __shared__ __align__(16) float P_s[kCh * RecB::PP];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    const int tile = blockIdx.x % p.ntile, rest = blockIdx.x / p.ntile;
+    const int cc = rest % p.nch, bh = rest / p.nch;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int dv = p.dv, col = tile * 64 + 16 * w + c;
+    const size_t ch = static_cast<size_t>(bh) * p.nch + cc;
+    const float* R = a.rec + ch * RecB::SIZE;
+    copy_to_lds(Kp_s, R + RecB::KP, kCh * RecB::PK);
+    copy_to_lds(P_s, R + RecB::P, kCh * RecB::PP);
+    const float* S = a.ckpts + ch * kChDk * dv + col;
+    float s[32];
+#pragma unroll
+    for (int m = 0; m < 32; m++) s[m] = S[static_cast<size_t>(kmap(m, g)) * dv];
+    const int t0 = cc * kCh, L = min(kCh, p.T - t0);
+    const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
+    float vv[16], bb[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int tk = kmap(i, g);
+        const bool ok = tk < L;
+        const size_t e = tok0 + static_cast<size_t>(tk) * p.H;
+        vv[i] = ok ? load_elem(in.v, e * dv + col, p.qkv_dt) : 0.0f;
+        bb[i] = ok ? load_elem(in.beta, e, p.gate_dt) : 0.0f;
+    }
+    __syncthreads();
+    f4 X[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; rt++) X[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < 32; m++) {
+        const int key = kmap(m, g);
+#pragma unroll
+        for (int rt = 0; rt < 4; rt++) X[rt] = mfma4(Kp_s[cmap(rt, c) * RecB::PK + key], s[m], X[rt]);
+        if ((m & 3) == 3) sched_fence();
+    }
+    float u[16], rv[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        u[i] = vv[i] - X[i >> 2][i & 3];
+        rv[i] = bb[i] * u[i];
+    }
+    f4 D[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; rt++) D[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < 16; m++) {
+        const int tk = kmap(m, g);
+#pragma unroll
+        for (int rt = 0; rt < 4; rt++) D[rt] = mfma4(P_s[cmap(rt, c) * RecB::PP + tk], rv[m], D[rt]);
+        if ((m & 3) == 3) sched_fence();
+    }
+    float* Ub = a.U + ch * kCh * dv + col;
+    float* Db = a.D + ch * kCh * dv + col;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const size_t o = static_cast<size_t>(kmap(i, g)) * dv;
+        Ub[o] = u[i];
+        Db[o] = D[i >> 2][i & 3];
+    }
+}
+
+// dS carried through the chunks, last to first, for 64 value columns (la_chunk.hpp map).
+__global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams p, ChunkIn in, ChunkBwdPtrs a) {
+    __shared__ __align__(16) float R[RecB::LDS_SIZE];
+    __shared__ float red[4][kCh];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g0 = lane >> 4, c0 = lane & 15;
+    int tile, bh;
+    chunk_tile_of(blockIdx.x, p.ntile, tile, bh);
+    const int BH = p.B * p.H;
+    if (bh >= BH) return;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int dv = p.dv, col = tile * 64 + 16 * w + c0;
+    const size_t soff = static_cast<size_t>(bh) * kChDk * dv + col;
+    float ds[32];
+#pragma unroll
+    for (int m = 0; m < 32; m++) ds[m] = a.dST ? a.dST[soff + static_cast<size_t>(kmap(m, g0)) * dv] : 0.0f;
+    for (int cc = p.nch - 1; cc >= 0; cc--) {
+        const int g = opaque(g0), c = opaque(c0);
+        const int t0 = cc * kCh, L = min(kCh, p.T - t0);
+        const size_t ch = static_cast<size_t>(bh) * p.nch + cc;
+        const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
+        float* dse = a.dSe + ch * kChDk * dv + col;
+#pragma unroll
+        for (int m = 0; m < 32; m++) dse[static_cast<size_t>(kmap(m, g)) * dv] = ds[m];
+        __syncthreads();
+        copy_to_lds(R, a.rec + ch * RecB::SIZE, RecB::LDS_SIZE);
+        float dO[16], uu[16], bb[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int tk = kmap(i, g);
+            const bool ok = tk < L;
+            const size_t e = tok0 + static_cast<size_t>(tk) * p.H;
+            dO[i] = ok ? a.dout[e * dv + col] : 0.0f;
+            bb[i] = ok ? load_elem(in.beta, e, p.gate_dt) : 0.0f;
+            uu[i] = a.U[(ch * kCh + tk) * dv + col];
+        }
+        __syncthreads();
+        // dDelta = Kd dS_end + M^T dO
+        f4 DD[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; rt++) DD[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 32; m++) {
+            const int key = kmap(m, g);
+#pragma unroll
+            for (int rt = 0; rt < 4; rt++) DD[rt] = mfma4(R[RecB::KD + cmap(rt, c) * RecB::PKD + key], ds[m], DD[rt]);
+            if ((m & 3) == 3) sched_fence();
+        }
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            const int tk = kmap(m, g);
+#pragma unroll
+            for (int rt = 0; rt < 4; rt++) DD[rt] = mfma4(R[RecB::M + tk * RecB::PP + cmap(rt, c)], dO[m], DD[rt]);
+            if ((m & 3) == 3) sched_fence();
+        }
+        // dR = P^T dDelta
+        f4 dR[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; rt++) dR[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            const int tk = kmap(m, g);
+            const float dm = DD[m >> 2][m & 3];
+#pragma unroll
+            for (int rt = 0; rt < 4; rt++) dR[rt] = mfma4(R[RecB::P + tk * RecB::PP + cmap(rt, c)], dm, dR[rt]);
+            if ((m & 3) == 3) sched_fence();
+        }
+        float* dDb = a.dD + ch * kCh * dv + col;
+        float du[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int tk = kmap(i, g);
+            dDb[static_cast<size_t>(tk) * dv] = DD[i >> 2][i & 3];
+            du[i] = bb[i] * dR[i >> 2][i & 3];
+            if (tk < L) a.dv[(tok0 + static_cast<size_t>(tk) * p.H) * dv + col] = du[i];
+        }
+        // beta gradient of R = beta U, summed over this tile's columns
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const float v = group_sum<16>(dR[i >> 2][i & 3] * uu[i]);
+            if (c == i) red[w][kmap(i, g)] = v;
+        }
+        __syncthreads();
+        if (threadIdx.x < kCh) {
+            const int t = threadIdx.x;
+            a.dbp[(static_cast<size_t>(tile) * BH * p.nch + ch) * kCh + t] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+        }
+        // dS <- E_L dS + Qp^T dO - Kp^T dv
+#pragma unroll
+        for (int kt = 0; kt < 8; kt++) {
+            f4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[r] = R[RecB::EL + 16 * kt + 4 * r + g] * ds[4 * kt + r];
+#pragma unroll
+            for (int m = 0; m < 16; m++) {
+                const int tk = kmap(m, g);
+                acc = mfma4(R[RecB::QP + tk * RecB::PK + cmap(kt, c)], dO[m], acc);
+                acc = mfma4(R[RecB::KP + tk * RecB::PK + cmap(kt, c)], -du[m], acc);
+                if ((m & 3) == 3) sched_fence();
+            }
+#pragma unroll
+            for (int r = 0; r < 4; r++) ds[4 * kt + r] = acc[r];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 32; m++) a.dS0[soff + static_cast<size_t>(kmap(m, g0)) * dv] = ds[m];
+}
+
+// The ten 16 x 16 tiles of a 64 x 64 lower-triangular matrix.
+__device__ __forceinline__ void low_tile(int i, int& rt, int& ct) {
+    rt = i < 1 ? 0 : i < 3 ? 1 : i < 6 ? 2 : 3;
+    ct = i - (rt * (rt + 1)) / 2;
+}
+
+// Gradients of one (sequence, head, chunk).
+template <bool KDA>
+__global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p, ChunkIn in, ChunkBwdPtrs a) {
+    __shared__ __align__(16) float big[kBig];
+    __shared__ float dAs[kWM], dMs[kWM];
+    __shared__ float bS[kCh], gS[kCh], elS[kChDk];
+    __shared__ float bpart[4][kCh];  // beta's pair term per wave and token
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, g0 = lane >> 4, c0 = lane & 15;
+    const int g = g0, c = c0;
+    const int cc = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int bh = b * p.H + h, BH = p.B * p.H;
+    const int dv = p.dv, t0 = cc * kCh, L = min(kCh, p.T - t0);
+    const size_t ch = static_cast<size_t>(bh) * p.nch + cc;
+    const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
+    const float* R = a.rec + ch * RecB::SIZE;
+    float* dPs = big + 3 * kWM;
+    for (int i = t; i < kWM; i += kChThreads) dPs[i] = dMs[i] = 0.0f;
+    bpart[w][lane] = 0.0f;
+    if (t < kCh) bS[t] = t < L ? load_elem(in.beta, tok0 + static_cast<size_t>(t) * p.H, p.gate_dt) : 0.0f;
+
+    // ---- products over the value columns, 16 at a time
+    float* dDs = big;
+    float* Rs = dDs + kCh * kSP;
+    float* dOs = Rs + kCh * kSP;
+    float* Ds = dOs + kCh * kSP;
+    float* dUs = Ds + kCh * kSP;
+    float* S0s = dUs + kCh * kSP;
+    float* dSes = S0s + kChDk * kSP;
+    f4 accQ[8], accK[8], accD[8], accPM[5];
+#pragma unroll
+    for (int j = 0; j < 8; j++) accQ[j] = accK[j] = accD[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < 5; u++) accPM[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    float el = 0.0f;
+    const float* Sck = a.ckpts + ch * kChDk * dv;
+    const float* dSe = a.dSe + ch * kChDk * dv;
+    for (int sb = 0; sb < dv / 16; sb++) {
+        const int g = opaque(g0), c = opaque(c0);
+        __syncthreads();
+        {
+            const int tk = t >> 2, j4 = (t & 3) << 2, c0 = 16 * sb + j4;
+            const size_t wrow = (ch * kCh + tk) * dv + c0;
+            const bool ok = tk < L;
+            const size_t grow = (tok0 + static_cast<size_t>(tk) * p.H) * dv + c0;
+            const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            float4 u4 = *reinterpret_cast<const float4*>(a.U + wrow);
+            const float bt = bS[tk];
+            u4.x *= bt; u4.y *= bt; u4.z *= bt; u4.w *= bt;
+            *reinterpret_cast<float4*>(Rs + tk * kSP + j4) = u4;
+            *reinterpret_cast<float4*>(dDs + tk * kSP + j4) = *reinterpret_cast<const float4*>(a.dD + wrow);
+            *reinterpret_cast<float4*>(Ds + tk * kSP + j4) = *reinterpret_cast<const float4*>(a.D + wrow);
+            *reinterpret_cast<float4*>(dOs + tk * kSP + j4) = ok ? *reinterpret_cast<const float4*>(a.dout + grow) : z;
+            *reinterpret_cast<float4*>(dUs + tk * kSP + j4) = ok ? *reinterpret_cast<const float4*>(a.dv + grow) : z;
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                const int idx = t + kChThreads * u, key = idx >> 2, k4 = (idx & 3) << 2;
+                const size_t kr = static_cast<size_t>(key) * dv + 16 * sb + k4;
+                *reinterpret_cast<float4*>(S0s + key * kSP + k4) = *reinterpret_cast<const float4*>(Sck + kr);
+                *reinterpret_cast<float4*>(dSes + key * kSP + k4) = *reinterpret_cast<const float4*>(dSe + kr);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const int kc = 4 * s + g;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int rt = j & 3, kt = w + 4 * (j >> 2);
+                const int ar = (16 * rt + c) * kSP + kc, br = (16 * kt + c) * kSP + kc;
+                accQ[j] = mfma4(dOs[ar], S0s[br], accQ[j]);
+                accK[j] = mfma4(dUs[ar], S0s[br], accK[j]);
+                accD[j] = mfma4(Ds[ar], dSes[br], accD[j]);
+                if ((j & 1) == 1) sched_fence();
+            }
+#pragma unroll
+            for (int u = 0; u < 5; u++) {
+                // tiles w + 4 u of dP (0..9) and dM (10..19); the choice is uniform over the wave
+                const int idx = w + 4 * u;
+                int rt, ct;
+                low_tile(idx % 10, rt, ct);
+                const float* Ao = idx < 10 ? dDs : dOs;
+                const float* Bo = idx < 10 ? Rs : Ds;
+                accPM[u] = mfma4(Ao[(16 * rt + c) * kSP + kc], Bo[(16 * ct + c) * kSP + kc], accPM[u]);
+            }
+        }
+        if (t < kChDk) {
+#pragma unroll
+            for (int j = 0; j < 16; j++) el = __builtin_fmaf(dSes[t * kSP + j], S0s[t * kSP + j], el);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 5; u++) {
+        const int idx = w + 4 * u;
+        int rt, ct;
+        low_tile(idx % 10, rt, ct);
+        float* dst = idx < 10 ? dPs : dMs;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int row = 16 * rt + 4 * g + r, cl = 16 * ct + c;
+            if (cl <= row) dst[row * kPW + cl] = accPM[u][r];
+        }
+    }
+    if (t < kChDk) elS[t] = el;
+    __syncthreads();
+
+    // ---- backward of the solve: dA (strictly lower) from dP
+    {
+        float* Xb = big;
+        float* Zb = big + kWM;
+        float* Pb = big + 2 * kWM;
+        float* Gb = dPs;
+        float* dZn = big + 4 * kWM;
+        float* dZb = big + 5 * kWM;
+        if (p.degree == 0) {
+            // P = (I + A)^-1: dA = -P^T dP P^T
+            for (int i = t; i < kCh * kCh; i += kChThreads) Xb[(i >> 6) * kPW + (i & 63)] = R[RecB::P + (i >> 6) * RecB::PP + (i & 63)];
+            __syncthreads();
+            mm64<true, false>(Xb, Gb, Zb, nullptr);
+            mm64<false, true>(Zb, Xb, Zb, nullptr);
+            dZn = Zb;
+        } else {
+            // P = (I + Z_0)(I + Z_1) ... (I + Z_{m-1}), Z_j = X^(2^j), X = -A.  Reverse sweep
+            // over the factors with G the gradient of the running product: dZ_j = P_{j-1}^T G
+            // plus the squaring's dZ_{j+1} Z_j^T + Z_j^T dZ_{j+1}, then G <- G (I + Z_j)^T;
+            // Z_j and the prefix P_{j-1} are recomputed from X at every step.
+            int m = 0;
+            while ((1 << m) - 1 < p.degree) m++;
+            for (int i = t; i < kCh * kCh; i += kChThreads) Xb[(i >> 6) * kPW + (i & 63)] = -R[RecB::A + (i >> 6) * RecB::PA + (i & 63)];
+            for (int j = m - 1; j >= 0; j--) {
+                __syncthreads();
+                for (int i = t; i < kCh * kCh; i += kChThreads) {
+                    const int r = i >> 6, q = i & 63;
+                    Zb[r * kPW + q] = Xb[r * kPW + q];
+                    Pb[r * kPW + q] = r == q ? 1.0f : 0.0f;
+                }
+                __syncthreads();
+                for (int i = 0; i < j; i++) {
+                    mm64<false, false>(Pb, Zb, Pb, Pb);
+                    mm64<false, false>(Zb, Zb, Zb, nullptr);
+                }
+                mm64<true, false>(Pb, Gb, dZb, nullptr);
+                if (j < m - 1) {
+                    mm64<false, true>(dZn, Zb, dZb, dZb);
+                    mm64<true, false>(Zb, dZn, dZb, dZb);
+                }
+                if (j > 0) mm64<false, true>(Gb, Zb, Gb, Gb);
+                float* tmp = dZn;
+                dZn = dZb;
+                dZb = tmp;
+            }
+        }
+        // exact: dA = -(P^T dP P^T); Neumann: dA = -dX (X = -A)
+        __syncthreads();
+        for (int i = t; i < kCh * kCh; i += kChThreads) {
+            const int r = i >> 6, q = i & 63;
+            dAs[r * kPW + q] = q < r ? -dZn[r * kPW + q] : 0.0f;
+        }
+    }
+
+    // ---- cumulative log decays
+    float* Gs = big + 2 * kTK;
+    if (KDA) {
+        if (t < kChDk) {
+            float run = 0.0f;
+#pragma unroll 8
+            for (int r = 0; r < kCh; r++) {
+                if (r < L) run += load_elem(in.g, (tok0 + static_cast<size_t>(r) * p.H) * kChDk + t, p.gate_dt);
+                Gs[r * 132 + t] = run;
+            }
+        }
+    } else if (t == 0) {
+        float run = 0.0f;
+        for (int r = 0; r < kCh; r++) {
+            if (r < L) run += load_elem(in.g, tok0 + static_cast<size_t>(r) * p.H, p.gate_dt);
+            gS[r] = run;
+        }
+    }
+    __syncthreads();
+    auto Gof = [&](int r, int kk) __attribute__((always_inline)) { return KDA ? Gs[r * 132 + kk] : gS[r]; };
+
+    // ---- elementwise terms of Kp = k E, Qp = q E, Kd = k F and E_L
+    {
+        float colsum[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
+            const float GL = Gof(L - 1, key);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = 16 * rt + 4 * g + r;
+                const float G = Gof(row, key);
+                const float E = expf(G), F = expf(GL - G);
+                const float Kp = R[RecB::KP + row * RecB::PK + key], Qp = R[RecB::QP + row * RecB::PK + key];
+                const float Kd = R[RecB::KD + row * RecB::PKD + key];
+                const float dQp = accQ[j][r], dKp = -accK[j][r], dKd = accD[j][r];
+                accQ[j][r] = E * dQp;
+                accK[j][r] = __builtin_fmaf(E, dKp, F * dKd);
+                accD[j][r] = __builtin_fmaf(dKp, Kp, __builtin_fmaf(dQp, Qp, -dKd * Kd));
+                colsum[j >> 2] = __builtin_fmaf(dKd, Kd, colsum[j >> 2]);
+            }
+            sched_fence();
+        }
+        colsum[0] = rows_sum(colsum[0]);
+        colsum[1] = rows_sum(colsum[1]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = 16 * rt + 4 * g + r;
+                if (row == L - 1) accD[j][r] += colsum[j >> 2] + elS[key] * expf(Gof(L - 1, key));
+                if (row < L) {
+                    const size_t e = (tok0 + static_cast<size_t>(row) * p.H) * kChDk + key;
+                    a.dq[e] = accQ[j][r];
+                    a.dk[e] = accK[j][r];
+                    a.dGw[(ch * kCh + row) * kChDk + key] = accD[j][r];
+                }
+            }
+        }
+    }
+
+    // ---- pair sums through A and M
+    float* kS = big;
+    float* qS = big + kTK;
+    __syncthreads();
+    for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
+        const int r = idx >> 7, kk = idx & 127;
+        float kv = 0.0f, qv = 0.0f;
+        if (r < L) {
+            const size_t e = (tok0 + static_cast<size_t>(r) * p.H) * kChDk + kk;
+            kv = load_elem(in.k, e, p.qkv_dt);
+            qv = load_elem(in.q, e, p.qkv_dt);
+        }
+        kS[r * 132 + kk] = kv;
+        qS[r * 132 + kk] = qv;
+    }
+    __syncthreads();
+    if (KDA) {
+        // thread: key kk, rows rh + 2 jj; decays exp(G_r - G_i) per key inside the sums
+        const int kk = t & 127, rh = t >> 7;
+        for (int jj = 0; jj < 32; jj++) {
+            const int r = rh + 2 * jj;
+            const float Gr = Gs[r * 132 + kk], kr = kS[r * 132 + kk], qr = qS[r * 132 + kk];
+            float T1 = 0.0f, T2 = 0.0f, T3 = 0.0f;
+            for (int i = 0; i <= r; i++) {
+                const float kd = kS[i * 132 + kk] * __expf(Gr - Gs[i * 132 + kk]);
+                T1 = __builtin_fmaf(dAs[r * kPW + i], kd, T1);
+                T2 = __builtin_fmaf(dMs[r * kPW + i], kd, T2);
+            }
+            for (int s2 = r; s2 < kCh; s2++) {
+                const float d = __expf(Gs[s2 * 132 + kk] - Gr);
+                const float wk = bS[s2] * dAs[s2 * kPW + r] * kS[s2 * 132 + kk];
+                T3 = __builtin_fmaf(__builtin_fmaf(dMs[s2 * kPW + r], qS[s2 * 132 + kk], wk), d, T3);
+            }
+            const float bt = bS[r];
+            // the rows are uniform over the wave: its 64 keys' share of beta's pair term
+            const float bsum = wave_sum(kr * T1);
+            if (lane == 0) bpart[w][r] = bsum;
+            if (r < L) {
+                const size_t e = (tok0 + static_cast<size_t>(r) * p.H) * kChDk + kk;
+                a.dq[e] += T2;
+                a.dk[e] += __builtin_fmaf(bt, T1, T3);
+                a.dGw[(ch * kCh + r) * kChDk + kk] += __builtin_fmaf(bt * kr, T1, __builtin_fmaf(qr, T2, -kr * T3));
+            }
+        }
+    } else {
+        // one decay per pair: dA o Gamma, dM o Gamma and beta dA o Gamma, then products with K, Q
+        float* dABG = big + 2 * kTK;
+        for (int i = t; i < kCh * kCh; i += kChThreads) {
+            const int r = i >> 6, q = i & 63;
+            const float gam = q <= r ? expf(gS[r] - gS[q]) : 0.0f;
+            const float da = dAs[r * kPW + q] * gam;
+            dAs[r * kPW + q] = da;
+            dMs[r * kPW + q] *= gam;
+            dABG[r * kPW + q] = bS[r] * da;
+        }
+        __syncthreads();
+        f4 T1[8], T2[8], T3[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) T1[j] = T2[j] = T3[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+        for (int s = 0; s < 16; s++) {
+            const int tk = 4 * s + g;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int rt = j & 3, kt = w + 4 * (j >> 2);
+                const float bk = kS[tk * 132 + 16 * kt + c], bq = qS[tk * 132 + 16 * kt + c];
+                T1[j] = mfma4(dAs[(16 * rt + c) * kPW + tk], bk, T1[j]);
+                T2[j] = mfma4(dMs[(16 * rt + c) * kPW + tk], bk, T2[j]);
+                T3[j] = mfma4(dABG[tk * kPW + 16 * rt + c], bk, T3[j]);
+                T3[j] = mfma4(dMs[tk * kPW + 16 * rt + c], bq, T3[j]);
+            }
+        }
+        float bc[4][4];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = 16 * rt + 4 * g + r;
+                const float kr = kS[row * 132 + key], qr = qS[row * 132 + key], bt = bS[row];
+                const float t1 = T1[j][r], t2 = T2[j][r], t3 = T3[j][r];
+                bc[rt][r] = (j < 4 ? 0.0f : bc[rt][r]) + kr * t1;
+                if (row < L) {
+                    const size_t e = (tok0 + static_cast<size_t>(row) * p.H) * kChDk + key;
+                    a.dq[e] += t2;
+                    a.dk[e] += __builtin_fmaf(bt, t1, t3);
+                    a.dGw[(ch * kCh + row) * kChDk + key] += __builtin_fmaf(bt * kr, t1, __builtin_fmaf(qr, t2, -kr * t3));
+                }
+            }
+        }
+        // beta's pair term: this wave's 32 keys of every row, summed over the 16 lanes of a row
+#pragma unroll
+        for (int rt = 0; rt < 4; rt++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float v = group_sum<16>(bc[rt][r]);
+                if (c == 0) bpart[w][16 * rt + 4 * g + r] = v;
+            }
+    }
+
+    // ---- gate and beta gradients
+    float* dGs = big;           // [64][132]: total cumulative-decay gradient
+    __syncthreads();
+    for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
+        const int r = idx >> 7, kk = idx & 127;
+        dGs[r * 132 + kk] = r < L ? a.dGw[(ch * kCh + r) * kChDk + kk] : 0.0f;
+    }
+    __syncthreads();
+    if (KDA) {
+        // dg_r = sum_{r' >= r} dG_r' per key (G is the running sum of g)
+        if (t < kChDk) {
+            float acc = 0.0f;
+            for (int r = L - 1; r >= 0; r--) {
+                acc += dGs[r * 132 + t];
+                a.dg[(tok0 + static_cast<size_t>(r) * p.H) * kChDk + t] = acc;
+            }
+        }
+    } else {
+        if (t < kCh) {
+            float rs = 0.0f;
+            for (int kk = 0; kk < kChDk; kk++) rs += dGs[t * 132 + kk];
+            elS[t] = rs;
+        }
+        __syncthreads();
+        if (t < L) {
+            float acc = 0.0f;
+            for (int r = L - 1; r >= t; r--) acc += elS[r];
+            a.dg[tok0 + static_cast<size_t>(t) * p.H] = acc;
+        }
+    }
+    if (t < L) {
+        float sbt = (bpart[0][t] + bpart[1][t]) + (bpart[2][t] + bpart[3][t]);
+        for (int tl = 0; tl < p.ntile; tl++) sbt += a.dbp[(static_cast<size_t>(tl) * BH * p.nch + ch) * kCh + t];
+        a.dbeta[tok0 + static_cast<size_t>(t) * p.H] = sbt;
+    }
+}
+
+}  // namespace
+
+ChunkBwdLayout chunk_bwd_layout(const la_config& c) {
+    auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+    const size_t nch = (static_cast<size_t>(c.T) + kCh - 1) / kCh;
+    const size_t units = static_cast<size_t>(c.B) * c.H * nch;
+    ChunkBwdLayout L;
+    L.rec = 0;
+    L.ckpts = L.rec + up(units * RecB::SIZE * sizeof(float));
+    L.U = L.ckpts + up(units * kChDk * c.d_v * sizeof(float));
+    L.D = L.U + up(units * kCh * c.d_v * sizeof(float));
+    L.dD = L.D + up(units * kCh * c.d_v * sizeof(float));
+    L.dSe = L.dD + up(units * kCh * c.d_v * sizeof(float));
+    L.dbp = L.dSe + up(units * kChDk * c.d_v * sizeof(float));
+    L.dGw = L.dbp + up(static_cast<size_t>(c.d_v / 64) * units * kCh * sizeof(float));
+    L.total = L.dGw + up(units * kCh * kChDk * sizeof(float));
+    return L;
+}
+
+hipError_t launch_chunk_bwd(const la_config& c, const FwdArgs& fa, const BwdArgs& ba, char* ws, hipStream_t s) {
+    const ChunkParams p = make_chunk_params(c);
+    const ChunkIn in{fa.q, fa.k, fa.v, fa.g, fa.beta};
+    const ChunkBwdLayout L = chunk_bwd_layout(c);
+    float* rec = reinterpret_cast<float*>(ws + L.rec);
+    const float* ck = ba.ckpts;
+    hipError_t e;
+    if (!ck) {
+        // checkpoints from the chunk forward (its records in the backward records' room)
+        float* room = reinterpret_cast<float*>(ws + L.ckpts);
+        FwdArgs f = fa;
+        f.o = nullptr;
+        f.ST = nullptr;
+        f.ckpts = room;
+        e = launch_chunk_fwd(c, f, rec, s);
+        if (e != hipSuccess) return e;
+        ck = room;
+    }
+    e = launch_chunk_prep(c, in, rec, true, s);
+    if (e != hipSuccess) return e;
+    ChunkBwdPtrs a{ck, ba.dout, ba.dST, ba.dq, ba.dk, ba.dv, ba.dg, ba.dbeta, ba.dS0, rec,
+                   reinterpret_cast<float*>(ws + L.U), reinterpret_cast<float*>(ws + L.D),
+                   reinterpret_cast<float*>(ws + L.dD), reinterpret_cast<float*>(ws + L.dSe),
+                   reinterpret_cast<float*>(ws + L.dbp), reinterpret_cast<float*>(ws + L.dGw)};
+    const unsigned units = static_cast<unsigned>(c.B) * c.H * p.nch;
+    hipLaunchKernelGGL(chunk_recompute_kernel, dim3(units * p.ntile), dim3(kChThreads), 0, s, p, in, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_dstate_kernel, dim3(chunk_tile_blocks(c.B * c.H, p.ntile)), dim3(kChThreads), 0, s, p,
+                       in, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 grid(p.nch, c.H, c.B);
+    if (c.gate == LA_GATE_KEY) hipLaunchKernelGGL(chunk_grad_kernel<true>, grid, dim3(kChThreads), 0, s, p, in, a);
+    else hipLaunchKernelGGL(chunk_grad_kernel<false>, grid, dim3(kChThreads), 0, s, p, in, a);
+    return hipGetLastError();
+}
+
+}  // namespace la

@@ -32,32 +32,7 @@ size_t chunk_fwd_workspace_bytes(const la_config& c) {
 
 namespace {
 
-constexpr int kPW = 68;   // pitch of the prep kernel's 64 x 64 work matrices
-constexpr int kPT = 132;  // pitch of its token-by-key arrays
-
-// C = A B (+ Cadd) for 64 x 64 fp32 matrices in LDS (pitch kPW) on the matrix cores; wave w
-// forms rows 16 w .. 16 w + 15.  The barrier between the products and the stores lets C alias
-// A, B or Cadd.  Every thread of the workgroup must call it.
-__device__ void mm64(const float* A, const float* B, float* C, const float* Cadd) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-    f4 acc[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ct++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) acc[ct][r] = Cadd ? Cadd[(16 * w + 4 * g + r) * kPW + 16 * ct + c] : 0.0f;
-#pragma unroll 4
-    for (int s = 0; s < 16; s++) {
-        const float a = A[(16 * w + c) * kPW + 4 * s + g];
-#pragma unroll
-        for (int ct = 0; ct < 4; ct++) acc[ct] = mfma4(a, B[(4 * s + g) * kPW + 16 * ct + c], acc[ct]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ct = 0; ct < 4; ct++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) C[(16 * w + 4 * g + r) * kPW + 16 * ct + c] = acc[ct][r];
-    __syncthreads();
-}
+constexpr int kPT = 132;  // pitch of the prep kernel's token-by-key arrays
 
 // Prep: A, M, the solve P, Kp, Qp, Kd, E_L of one chunk into its record (forward or backward
 // layout).  Tokens past the sequence's end are zero rows (their beta, k and q are zero).
@@ -225,8 +200,8 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
         }
         __syncthreads();
         for (int done = 1; done < p.degree; done = 2 * done + 1) {
-            mm64(W0, W0, W0, nullptr);  // Z <- Z Z
-            mm64(W1, W0, W1, W1);       // P <- P + P Z
+            mm64<false, false>(W0, W0, W0, nullptr);  // Z <- Z Z
+            mm64<false, false>(W1, W0, W1, W1);       // P <- P + P Z
         }
         Pm = W1;
     }
@@ -253,18 +228,19 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
                                                                   const float* __restrict__ rec) {
     __shared__ __align__(16) float R[RecF::SIZE];
     __shared__ WaveQdqShared<kChDk, QMODE, G> qsh;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g0 = lane >> 4, c0 = lane & 15;
     int tile, bh;
     chunk_tile_of(blockIdx.x, p.ntile, tile, bh);
     if (bh >= p.B * p.H) return;
     const int b = bh / p.H, h = bh - b * p.H;
-    const int dv = p.dv, col = tile * 64 + 16 * w + c;
+    const int dv = p.dv, col = tile * 64 + 16 * w + c0;
     const size_t soff = static_cast<size_t>(bh) * kChDk * dv + col;
     float s[32];
 #pragma unroll
-    for (int m = 0; m < 32; m++) s[m] = S0 ? S0[soff + static_cast<size_t>(kmap(m, g)) * dv] : 0.0f;
+    for (int m = 0; m < 32; m++) s[m] = S0 ? S0[soff + static_cast<size_t>(kmap(m, g0)) * dv] : 0.0f;
     int qpar = 0;
     for (int cc = 0; cc < p.nch; cc++) {
+        const int g = opaque(g0), c = opaque(c0);
         const int t0 = cc * kCh, L = min(kCh, p.T - t0);
         if (ckpts && t0 % p.ckpt_interval == 0) {
             float* dst = ckpts + (static_cast<size_t>(bh) * p.nck + t0 / p.ckpt_interval) * kChDk * dv + col;
@@ -298,6 +274,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
                 X[rt] = mfma4(R[RecF::KP + row], s[m], X[rt]);
                 Y[rt] = mfma4(R[RecF::QP + row], s[m], Y[rt]);
             }
+            if ((m & 3) == 3) sched_fence();
         }
         // beta (V - X), then Delta = P (beta (V - X))
         float rv[16];
@@ -311,6 +288,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
             const int tk = kmap(m, g);
 #pragma unroll
             for (int rt = 0; rt < 4; rt++) D[rt] = mfma4(R[RecF::P + cmap(rt, c) * RecF::PP + tk], rv[m], D[rt]);
+            if ((m & 3) == 3) sched_fence();
         }
         // O = Y + M Delta
 #pragma unroll
@@ -319,6 +297,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
             const float dm = D[m >> 2][m & 3];
 #pragma unroll
             for (int rt = 0; rt < 4; rt++) Y[rt] = mfma4(R[RecF::M + cmap(rt, c) * RecF::PP + tk], dm, Y[rt]);
+            if ((m & 3) == 3) sched_fence();
         }
         if (o) {
 #pragma unroll
@@ -334,8 +313,10 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[r] = R[RecF::EL + 16 * kt + 4 * r + g] * s[4 * kt + r];
 #pragma unroll
-            for (int m = 0; m < 16; m++)
+            for (int m = 0; m < 16; m++) {
                 acc = mfma4(R[RecF::KDT + cmap(kt, c) * RecF::PD + kmap(m, g)], D[m >> 2][m & 3], acc);
+                if ((m & 7) == 7) sched_fence();
+            }
 #pragma unroll
             for (int r = 0; r < 4; r++) s[4 * kt + r] = acc[r];
         }
@@ -344,7 +325,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
     }
     if (ST) {
 #pragma unroll
-        for (int m = 0; m < 32; m++) ST[soff + static_cast<size_t>(kmap(m, g)) * dv] = s[m];
+        for (int m = 0; m < 32; m++) ST[soff + static_cast<size_t>(kmap(m, g0)) * dv] = s[m];
     }
 }
 

@@ -489,7 +489,8 @@ la_status la_recurrent_bwd_ste_split(const la_config* prefix_cfg, const la_confi
 
 size_t la_bwd_workspace_bytes(const la_config* cfg) {
     if (check_config(cfg, false) != LA_OK || check_kernel(*cfg) != LA_OK || cfg->ckpt_interval < 1) return 0;
-    if (la::fwd_kernel(*cfg) == LA_KERNEL_CHUNK) return 0;
+    if (la::fwd_kernel(*cfg) == LA_KERNEL_CHUNK)
+        return cfg->ckpt_interval == la::kChunkTokens ? la::chunk_bwd_layout(*cfg).total : 0;
     return ws_layout(*cfg).total;
 }
 
@@ -513,8 +514,9 @@ la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void
     CHECK(check_config(cfg, false));
     const la_config& c = *cfg;
     CHECK(check_kernel(c));
-    if (la::fwd_kernel(c) == LA_KERNEL_CHUNK)
-        return fail(LA_ERR_UNSUPPORTED, "the chunk form's backward is not available");
+    const bool chunk = la::fwd_kernel(c) == LA_KERNEL_CHUNK;
+    if (chunk && c.ckpt_interval != la::kChunkTokens)
+        return fail(LA_ERR_UNSUPPORTED, "the chunk form's backward takes a checkpoint per chunk (ckpt_interval = 64)");
     if (c.ckpt_interval < 1) return fail(LA_ERR_INVALID_ARG, "backward needs ckpt_interval >= 1");
     const bool units = c.B > 0 && c.H > 0;
     const bool work = units && c.T > 0;
@@ -537,7 +539,8 @@ la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!units) return ok();
     if (c.T == 0) return hip_status(la::launch_copy_state(c, dS_T, dS0, s), "copy dS_T -> dS0");
-    const WsLayout L = ws_layout(c);
+    WsLayout L = ws_layout(c);
+    if (chunk) L.total = la::chunk_bwd_layout(c).total;
     if (provide) {
         // the allocation-free entry point: its fixed device array must hold the workspace
         if (ws_bytes < L.total)
@@ -550,6 +553,11 @@ la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void
         return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                     workspace ? ws_bytes : static_cast<size_t>(0));
     char* ws = static_cast<char*>(workspace);
+    if (chunk) {
+        la::FwdArgs fa{q, k, v, g, beta, S0, nullptr, nullptr, nullptr};
+        la::BwdArgs a{q, k, v, g, beta, ckpts, dout, dS_T, dq, dk, dv, dg, dbeta, dS0, nullptr, nullptr};
+        return hip_status(la::launch_chunk_bwd(c, fa, a, ws, s), "la_recurrent_bwd_ste chunk launch");
+    }
     if (la::bwd_mfma_eligible(c)) {
         float* states = reinterpret_cast<float*>(ws + L.states);
         la::FwdArgs fa{q, k, v, g, beta, S0, nullptr, nullptr, nullptr};

@@ -69,8 +69,51 @@ static_assert(RecF::SIZE % 64 == 0 && RecB::SIZE % 64 == 0 && RecB::LDS_SIZE % 4
 __device__ __forceinline__ int cmap(int blk, int x) { return 16 * blk + 4 * (x & 3) + (x >> 2); }
 __device__ __forceinline__ int kmap(int m, int g) { return 16 * (m >> 2) + 4 * (m & 3) + g; }
 
+// Compiler-only fence (no instruction): loads are not moved across it, which bounds how many
+// LDS operands of an unrolled product loop the scheduler hoists (and keeps live) at once.
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+
+// The same value, opaque to the compiler: lane indices passed through it at the top of a loop
+// body keep the addresses derived from them inside the body.  Otherwise every LDS address of
+// the unrolled products, being loop-invariant, is hoisted out of the chunk loop and held in
+// registers for its whole length.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+constexpr int kPW = 68;  // pitch of the 64 x 64 work matrices in LDS
+
+// C = op(A) op(B) (+ Cadd) for 64 x 64 fp32 matrices in LDS (pitch kPW) on the matrix cores,
+// op = transpose when TA / TB; wave w forms rows 16 w .. 16 w + 15.  The barrier between the
+// products and the stores lets C alias A, B or Cadd.  Every thread of the workgroup must call it.
+template <bool TA, bool TB>
+__device__ void mm64(const float* A, const float* B, float* C, const float* Cadd) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    f4 acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[ct][r] = Cadd ? Cadd[(16 * w + 4 * g + r) * kPW + 16 * ct + c] : 0.0f;
+#pragma unroll 4
+    for (int s = 0; s < 16; s++) {
+        const float a = TA ? A[(4 * s + g) * kPW + 16 * w + c] : A[(16 * w + c) * kPW + 4 * s + g];
+#pragma unroll
+        for (int ct = 0; ct < 4; ct++) {
+            const float b = TB ? B[(16 * ct + c) * kPW + 4 * s + g] : B[(4 * s + g) * kPW + 16 * ct + c];
+            acc[ct] = mfma4(a, b, acc[ct]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) C[(16 * w + 4 * g + r) * kPW + 16 * ct + c] = acc[ct][r];
+    __syncthreads();
 }
 
 // Copy n floats (a multiple of four, 16-byte aligned) from global memory into LDS.

@@ -121,9 +121,18 @@ hipError_t launch_fwd_tok(const la_config& c, const FwdArgs& a, hipStream_t s);
 // 64-token chunk path (chunk_fwd.hip): d_k = 128, no rotation, no replay, rounding points and
 // checkpoints on chunk ends.  The forward prepares every chunk's matrices into `records`
 // (chunk_fwd_workspace_bytes) and then runs the state pass.
+constexpr int kChunkTokens = 64;
 bool chunk_eligible(const la_config& c);
 size_t chunk_fwd_workspace_bytes(const la_config& c);
 hipError_t launch_chunk_fwd(const la_config& c, const FwdArgs& a, float* records, hipStream_t s);
+// Backward of the chunk form (chunk_bwd.hip), from checkpoints every 64 tokens (ba.ckpts, or
+// recomputed into the workspace's room when null).  Workspace regions, byte offsets:
+struct ChunkBwdLayout {
+    size_t rec, ckpts, U, D, dD, dSe, dbp, dGw, total;
+};
+ChunkBwdLayout chunk_bwd_layout(const la_config& c);
+struct BwdArgs;
+hipError_t launch_chunk_bwd(const la_config& c, const FwdArgs& fa, const BwdArgs& ba, char* ws, hipStream_t s);
 hipError_t launch_copy_state(const la_config& c, const float* src, float* dst, hipStream_t s);
 hipError_t launch_bwd(const la_config& c, const BwdArgs& a, hipStream_t s);
 // Token range [begin, end) of packed sequence b (part of it when split is given), on the

@@ -187,3 +187,108 @@ def test_chunk_empty_call_hands_the_state_through():
     la.la_recurrent_fwd_chunk(c, None, None, None, None, None, S0, None, ST, None, None, 0)
     torch.cuda.synchronize()
     assert torch.equal(ST, S0)
+
+
+# ---------------------------------------------------------------- backward
+
+def run_chunk_bwd(c, d, S0, ck, do, dST, dev_inputs=None):
+    torch = gu.torch_mod()
+    di = dev_inputs or {k: gu.dev(d[k]) for k in ("q", "k", "v", "g", "beta")}
+    f = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    gshape = (c.B, c.T, c.H, c.d_k) if c.gate == la.LA_GATE_KEY else (c.B, c.T, c.H)
+    out = {"dq": gu.nan_like(torch, (c.B, c.T, c.H, c.d_k)), "dk": gu.nan_like(torch, (c.B, c.T, c.H, c.d_k)),
+           "dv": gu.nan_like(torch, (c.B, c.T, c.H, c.d_v)), "dg": gu.nan_like(torch, gshape),
+           "dbeta": gu.nan_like(torch, (c.B, c.T, c.H)), "dS0": gu.nan_like(torch, (c.B, c.H, c.d_k, c.d_v))}
+    nbytes = la.la_bwd_workspace_bytes(c)
+    assert nbytes > 0, la.la_last_error()
+    ws = torch.full((nbytes // 4 + 1,), float("nan"), device="cuda")
+    la.la_recurrent_bwd_ste(c, di["q"], di["k"], di["v"], di["g"], di["beta"], f(S0), f(ck), f(do), f(dST),
+                            out["dq"], out["dk"], out["dv"], out["dg"], out["dbeta"], out["dS0"], ws, nbytes)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def oracle_bwd_units(c, d, S0, ck, do, dST, units):
+    """The chunked oracle's backward of each (b, h) unit, teacher forced with the GPU's
+    checkpoints (the states entering every chunk)."""
+    out = {}
+    for b, h in units:
+        args = [d[n].f64[b:b + 1, :, h:h + 1] for n in ("q", "k", "v", "g", "beta")]
+        r = oc.bwd(*args, None if S0 is None else S0[b:b + 1, h:h + 1], do[b:b + 1, :, h:h + 1],
+                   None if dST is None else dST[b:b + 1, h:h + 1], qdq_mode=c.qdq, group=c.group,
+                   qdq_interval=c.qdq_interval, chunk_states=ck[b:b + 1, h:h + 1].astype(np.float64),
+                   **oracle_kw(c))
+        out[(b, h)] = r
+    return out
+
+
+GRADS = ("dq", "dk", "dv", "dg", "dbeta")
+BCASES = [
+    # name, gate, quantizer kw, solve, degree, T, d_v
+    ("gdn_plain_exact", "scalar", {}, la.LA_SOLVE_EXACT, 0, 150, 128),
+    ("kda_plain_exact", "key", {}, la.LA_SOLVE_EXACT, 0, 150, 128),
+    ("gdn_e4m3_n3", "scalar", dict(qdq=E4M3, group=64, qdq_interval=64), la.LA_SOLVE_NEUMANN, 3, 150, 128),
+    ("kda_e4m3_n7", "key", dict(qdq=E4M3, group=64, qdq_interval=64), la.LA_SOLVE_NEUMANN, 7, 150, 128),
+    ("gdn_int8g32_n31_dv192", "scalar", dict(qdq=INT8, group=32, qdq_interval=128), la.LA_SOLVE_NEUMANN, 31, 200, 192),
+    ("kda_e4m3_n15_dv64", "key", dict(qdq=E4M3, group=64, qdq_interval=64), la.LA_SOLVE_NEUMANN, 15, 130, 64),
+    ("kda_int8g16_exact", "key", dict(qdq=INT8, group=16, qdq_interval=64), la.LA_SOLVE_EXACT, 0, 100, 128),
+]
+
+
+@pytest.mark.parametrize("name,gate,qkw,solve,degree,T,dv", BCASES, ids=[b[0] for b in BCASES])
+def test_chunk_backward_against_oracle(name, gate, qkw, solve, degree, T, dv):
+    B, H = 2, 2
+    w = synth.Workload(name, B=B, T=T, H=H, d_k=128, d_v=dv, gate=gate, config_id=400 + degree + T)
+    d = synth.generate(w, with_do=True)
+    rng = np.random.default_rng(400 + T)
+    S0 = (rng.standard_normal((B, H, 128, dv)) * 0.3).astype(np.float32)
+    dST = rng.standard_normal((B, H, 128, dv)).astype(np.float32)
+    c = chunk_cfg(w, d, solve, degree, **qkw)
+    o, ST, ck = run_chunk(c, d, S0, ckpt_interval=64)
+    do = d["do"].f32
+    r = run_chunk_bwd(c, d, S0, ck, do, dST)
+    ref = oracle_bwd_units(c, d, S0, ck, do.astype(np.float64), dST.astype(np.float64),
+                           [(b, h) for b in range(B) for h in range(H)])
+    errs = {}
+    for n in GRADS + ("dS0",):
+        got = np.stack([r[n][b, :, h] if n != "dS0" else r[n][b, h] for (b, h) in ref])
+        want = np.stack([ref[(b, h)][n][0, :, 0] if n != "dS0" else ref[(b, h)][n][0, 0] for (b, h) in ref])
+        errs[n] = gu.err(got, want)
+    assert max(errs.values()) <= gu.TOL_F32, errs
+    # the backward without checkpoints recomputes the same ones: bit-identical gradients
+    r2 = run_chunk_bwd(c, d, S0, None, do, dST)
+    for n in r:
+        np.testing.assert_array_equal(r[n], r2[n], err_msg=n)
+
+
+@pytest.mark.parametrize("T", [1, 64, 65])
+def test_chunk_backward_edge_lengths(T):
+    w = synth.Workload("chunk_bwd_edge", B=1, T=T, H=2, d_k=128, d_v=128, gate="key", config_id=450 + T)
+    d = synth.generate(w, with_do=True)
+    c = chunk_cfg(w, d, la.LA_SOLVE_NEUMANN, 3, qdq=E4M3, group=64, qdq_interval=64)
+    o, ST, ck = run_chunk(c, d, None, ckpt_interval=64)
+    do = d["do"].f32
+    r = run_chunk_bwd(c, d, None, ck, do, None)
+    ref = oracle_bwd_units(c, d, None, ck, do.astype(np.float64), None, [(0, 0), (0, 1)])
+    for (b, h), rr in ref.items():
+        for n in GRADS:
+            assert gu.err(r[n][b, :, h], rr[n][0, :, 0]) <= gu.TOL_F32, (n, T)
+        assert gu.err(r["dS0"][b, h], rr["dS0"][0, 0]) <= gu.TOL_F32
+
+
+@pytest.mark.parametrize("gate,degree", [("scalar", 7), ("key", 31)])
+def test_chunk_backward_long_sequence_sampled(gate, degree):
+    """B=8 H=16 T=4096 with E4M3 tiles every 64 tokens: sampled units against the oracle."""
+    w = synth.Workload("chunk_long", B=8, T=4096, H=16, d_k=128, d_v=128, gate=gate, gate_dtype="f32", config_id=2)
+    d = synth.generate(w, with_do=True)
+    c = chunk_cfg(w, d, la.LA_SOLVE_NEUMANN, degree, qdq=E4M3, group=64, qdq_interval=64)
+    o, ST, ck = run_chunk(c, d, None, ckpt_interval=64)
+    do = d["do"].f32
+    r = run_chunk_bwd(c, d, None, ck, do, None)
+    units = [(0, 0), (5, 11)]
+    ref = oracle_bwd_units(c, d, None, ck, do.astype(np.float64), None, units)
+    for (b, h), rr in ref.items():
+        for n in GRADS:
+            assert gu.err(r[n][b, :, h], rr[n][0, :, 0]) <= gu.TOL_F32, n
+    for n in r:
+        assert np.all(np.isfinite(r[n])), n
