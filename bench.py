@@ -230,6 +230,68 @@ def bench_kda_long(steps=3, warmup=1):
     }
 
 
+def bench_chunk(steps=3, warmup=1):
+    """The 64-token chunk form on the long-sequence shape (B=8 H=16 T=4096 d=128, bf16 q/k/v, fp32
+    gates and beta, E4M3 tile QDQ every 64 tokens, a checkpoint per chunk): forward and
+    straight-through backward with the exact solve and with Neumann polynomials, GDN and KDA."""
+    import torch
+
+    import quantized_state_qat_amd as la
+    import synth
+
+    out = {"workload": "B=8 H=16 T=4096 d_k=d_v=128 bf16 q/k/v, fp32 gates and beta, E4M3 tile QDQ every 64 tokens, "
+                       "64-token chunks and checkpoints",
+           "flops_note": "fp32 matrix work counted per chunk and head: state pass 2 (2*64*128 + 2*64*64 + 128*64) per "
+                         "value column; prep 2*2*(64*65/2)*128 for A and M, 2*64^3/3 for the exact solve or "
+                         "2*(2 log2(d+1) - 2)*64^3 for the Neumann product"}
+    for gate in ("scalar", "key"):
+        w = synth.Workload("chunk_long", B=8, T=4096, H=16, d_k=128, d_v=128, gate=gate, gate_dtype="f32", config_id=2)
+        d = synth.generate(w, with_do=True)
+        dev = {k: _dev(d[k]) for k in ("q", "k", "v", "g", "beta", "do")}
+        del d
+        o = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
+        ST = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+        ck = torch.empty((w.B, w.H, w.T // 64, w.d_k, w.d_v), device="cuda")
+        gshape = (w.B, w.T, w.H, w.d_k) if gate == "key" else (w.B, w.T, w.H)
+        dq, dk = (torch.empty((w.B, w.T, w.H, w.d_k), device="cuda") for _ in range(2))
+        dv = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
+        dg = torch.empty(gshape, device="cuda")
+        dbeta = torch.empty((w.B, w.T, w.H), device="cuda")
+        dS0 = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+        stream = torch.cuda.current_stream()
+        for solve, degree in ((la.LA_SOLVE_EXACT, 0), (la.LA_SOLVE_NEUMANN, 3), (la.LA_SOLVE_NEUMANN, 31)):
+            if gate == "key" and degree == 31:
+                continue
+            c = la.Config(B=w.B, T=w.T, H=w.H, d_k=w.d_k, d_v=w.d_v,
+                          gate=la.LA_GATE_KEY if gate == "key" else la.LA_GATE_SCALAR, qdq=la.LA_QDQ_E4M3_TILE,
+                          group=64, qdq_interval=64, ckpt_interval=64, gate_dtype=la.LA_F32,
+                          kernel=la.LA_KERNEL_CHUNK, solve=solve, degree=degree)
+            nf = la.la_chunk_workspace_bytes(c)
+            nb = la.la_bwd_workspace_bytes(c)
+            ws = torch.empty((max(nf, nb) + 255) // 4, dtype=torch.float32, device="cuda")
+            t_f = _time_calls(lambda: la.la_recurrent_fwd_chunk(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                                                                None, o, ST, ck, ws, nf, stream=stream),
+                              steps, warmup, stream)
+            t_b = _time_calls(lambda: la.la_recurrent_bwd_ste(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                                                              None, ck, dev["do"], None, dq, dk, dv, dg, dbeta, dS0,
+                                                              ws, nb, stream=stream), steps, warmup, stream)
+            nch = w.T // 64
+            m = (degree + 1).bit_length() - 1
+            solve_fl = 2 * 64 ** 3 / 3 if degree == 0 else 2 * (2 * m - 2) * 64 ** 3
+            per_chunk = 2 * (2 * 64 * 128 + 2 * 64 * 64 + 128 * 64) * w.d_v + 2 * 2 * (64 * 65 / 2) * 128 + solve_fl
+            fl = per_chunk * nch * w.B * w.H
+            key = f"{'kda' if gate == 'key' else 'gdn'}_{'exact' if degree == 0 else 'neumann%d' % degree}"
+            out[key] = {"ms_fwd": t_f * 1e3, "ms_bwd": t_b * 1e3, "updates_per_s_fwd": w.B * w.H * w.T / t_f,
+                        "workspace_bytes_fwd": nf, "workspace_bytes_bwd": nb,
+                        "roofline_fwd": {"bound": "mfma", "achieved": fl / t_f / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": fl / t_f / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                                         "flops_per_call": fl, "note": "fp32 matrix cores (16x16x4 f32), dense peak"}}
+            del ws
+            torch.cuda.empty_cache()
+        del dev
+    return out
+
+
 def _dev(t):
     """Device copy of a generated tensor in its storage dtype."""
     import numpy as np
@@ -684,7 +746,7 @@ def main():
             "long_sequence_fwdbwd": lambda: bench_long_e4m3()[1], "kda_long_e4m3": bench_kda_long,
             "kda_int8g64_tok": bench_kda_tok, "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd,
             "replay_w16_wht_int8g32": bench_replay, "decode_slots": bench_decode_slots,
-            "decode_replay_w16": bench_decode_replay, "varlen_prefill": bench_varlen,
+            "decode_replay_w16": bench_decode_replay, "varlen_prefill": bench_varlen, "chunk_prefill": bench_chunk,
         }
         out = {}
         for name in args.only.split(","):
@@ -733,7 +795,7 @@ def main():
                          "kda_int8g64_tok": bench_kda_tok(),
                          "gdn_fwdbwd_wht_int8g32": bench_wht_fwdbwd(), "replay_w16_wht_int8g32": bench_replay(),
                          "decode_slots": bench_decode_slots(), "decode_replay_w16": bench_decode_replay(),
-                         "varlen_prefill": bench_varlen()}
+                         "varlen_prefill": bench_varlen(), "chunk_prefill": bench_chunk()}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["d"], w)
     else:

@@ -43,7 +43,8 @@ struct ChunkBwdPtrs {
     float* dD;            // dDelta, same layout
     float* dSe;           // [B H nch][128][d_v]: dL/d(state after the chunk)
     float* dbp;           // [ntile][B H nch][64]: beta-gradient partial per value tile
-    float* dGw;           // [B H nch][64][128]: cumulative-decay gradient of the elementwise terms
+    float* gsc;           // [B H nch][3][64][128]: dQp, dKp, dKd of the products over columns,
+                          // then (in the dKd slot) the cumulative-decay gradient
 };
 
 // U and Delta of one (sequence, head, chunk, 64 columns) from the chunk's checkpoint.
@@ -57,8 +58,8 @@ __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams
     const int dv = p.dv, col = tile * 64 + 16 * w + c;
     const size_t ch = static_cast<size_t>(bh) * p.nch + cc;
     const float* R = a.rec + ch * RecB::SIZE;
-    copy_to_lds(Kp_s, R + RecB::KP, kCh * RecB::PK);
-    copy_to_lds(P_s, R + RecB::P, kCh * RecB::PP);
+    lds_dma(Kp_s, R + RecB::KP, kCh * RecB::PK);
+    lds_dma(P_s, R + RecB::P, kCh * RecB::PP);
     const float* S = a.ckpts + ch * kChDk * dv + col;
     float s[32];
 #pragma unroll
@@ -74,6 +75,7 @@ __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams
         vv[i] = ok ? load_elem(in.v, e * dv + col, p.qkv_dt) : 0.0f;
         bb[i] = ok ? load_elem(in.beta, e, p.gate_dt) : 0.0f;
     }
+    wait_all_mem();
     __syncthreads();
     f4 X[4];
 #pragma unroll
@@ -113,8 +115,11 @@ __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams
 
 // dS carried through the chunks, last to first, for 64 value columns (la_chunk.hpp map).
 __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams p, ChunkIn in, ChunkBwdPtrs a) {
-    __shared__ __align__(16) float R[RecB::LDS_SIZE];
+    __shared__ __align__(16) float RA[RecB::PART2];                    // Kd, M
+    __shared__ __align__(16) float RB[RecB::LDS_SIZE - RecB::PART2];   // P, Qp, Kp, E_L
     __shared__ float red[4][kCh];
+    constexpr int bP = RecB::P - RecB::PART2, bQP = RecB::QP - RecB::PART2, bKP = RecB::KP - RecB::PART2,
+                  bEL = RecB::EL - RecB::PART2;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g0 = lane >> 4, c0 = lane & 15;
     int tile, bh;
     chunk_tile_of(blockIdx.x, p.ntile, tile, bh);
@@ -126,6 +131,8 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
     float ds[32];
 #pragma unroll
     for (int m = 0; m < 32; m++) ds[m] = a.dST ? a.dST[soff + static_cast<size_t>(kmap(m, g0)) * dv] : 0.0f;
+    const float* recu = a.rec + static_cast<size_t>(bh) * p.nch * RecB::SIZE;
+    lds_dma(RA, recu + static_cast<size_t>(p.nch - 1) * RecB::SIZE, RecB::PART2);
     for (int cc = p.nch - 1; cc >= 0; cc--) {
         const int g = opaque(g0), c = opaque(c0);
         const int t0 = cc * kCh, L = min(kCh, p.T - t0);
@@ -134,8 +141,10 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
         float* dse = a.dSe + ch * kChDk * dv + col;
 #pragma unroll
         for (int m = 0; m < 32; m++) dse[static_cast<size_t>(kmap(m, g)) * dv] = ds[m];
+        // part 1 of this chunk's record is here, part 2 of the later chunk free: load part 2
+        wait_all_mem();
         __syncthreads();
-        copy_to_lds(R, a.rec + ch * RecB::SIZE, RecB::LDS_SIZE);
+        lds_dma(RB, recu + static_cast<size_t>(cc) * RecB::SIZE + RecB::PART2, RecB::LDS_SIZE - RecB::PART2);
         float dO[16], uu[16], bb[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
@@ -146,7 +155,6 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
             bb[i] = ok ? load_elem(in.beta, e, p.gate_dt) : 0.0f;
             uu[i] = a.U[(ch * kCh + tk) * dv + col];
         }
-        __syncthreads();
         // dDelta = Kd dS_end + M^T dO
         f4 DD[4];
 #pragma unroll
@@ -155,16 +163,20 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
         for (int m = 0; m < 32; m++) {
             const int key = kmap(m, g);
 #pragma unroll
-            for (int rt = 0; rt < 4; rt++) DD[rt] = mfma4(R[RecB::KD + cmap(rt, c) * RecB::PKD + key], ds[m], DD[rt]);
+            for (int rt = 0; rt < 4; rt++) DD[rt] = mfma4(RA[RecB::KD + cmap(rt, c) * RecB::PKD + key], ds[m], DD[rt]);
             if ((m & 3) == 3) sched_fence();
         }
 #pragma unroll
         for (int m = 0; m < 16; m++) {
             const int tk = kmap(m, g);
 #pragma unroll
-            for (int rt = 0; rt < 4; rt++) DD[rt] = mfma4(R[RecB::M + tk * RecB::PP + cmap(rt, c)], dO[m], DD[rt]);
+            for (int rt = 0; rt < 4; rt++) DD[rt] = mfma4(RA[RecB::M + tk * RecB::PP + cmap(rt, c)], dO[m], DD[rt]);
             if ((m & 3) == 3) sched_fence();
         }
+        // part 2 is here and part 1 free: load the previous chunk's part 1
+        wait_all_mem();
+        __syncthreads();
+        if (cc > 0) lds_dma(RA, recu + static_cast<size_t>(cc - 1) * RecB::SIZE, RecB::PART2);
         // dR = P^T dDelta
         f4 dR[4];
 #pragma unroll
@@ -174,7 +186,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
             const int tk = kmap(m, g);
             const float dm = DD[m >> 2][m & 3];
 #pragma unroll
-            for (int rt = 0; rt < 4; rt++) dR[rt] = mfma4(R[RecB::P + tk * RecB::PP + cmap(rt, c)], dm, dR[rt]);
+            for (int rt = 0; rt < 4; rt++) dR[rt] = mfma4(RB[bP + tk * RecB::PP + cmap(rt, c)], dm, dR[rt]);
             if ((m & 3) == 3) sched_fence();
         }
         float* dDb = a.dD + ch * kCh * dv + col;
@@ -202,12 +214,12 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
         for (int kt = 0; kt < 8; kt++) {
             f4 acc;
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[r] = R[RecB::EL + 16 * kt + 4 * r + g] * ds[4 * kt + r];
+            for (int r = 0; r < 4; r++) acc[r] = RB[bEL + 16 * kt + 4 * r + g] * ds[4 * kt + r];
 #pragma unroll
             for (int m = 0; m < 16; m++) {
                 const int tk = kmap(m, g);
-                acc = mfma4(R[RecB::QP + tk * RecB::PK + cmap(kt, c)], dO[m], acc);
-                acc = mfma4(R[RecB::KP + tk * RecB::PK + cmap(kt, c)], -du[m], acc);
+                acc = mfma4(RB[bQP + tk * RecB::PK + cmap(kt, c)], dO[m], acc);
+                acc = mfma4(RB[bKP + tk * RecB::PK + cmap(kt, c)], -du[m], acc);
                 if ((m & 3) == 3) sched_fence();
             }
 #pragma unroll
@@ -231,6 +243,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     __shared__ float dAs[kWM], dMs[kWM];
     __shared__ float bS[kCh], gS[kCh], elS[kChDk];
     __shared__ float bpart[4][kCh];  // beta's pair term per wave and token
+    __shared__ float elS2[2 * kChDk];  // column sums of dKd Kd (KDA: two row halves)
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, g0 = lane >> 4, c0 = lane & 15;
     const int g = g0, c = c0;
     const int cc = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -328,6 +341,18 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
         }
     }
     if (t < kChDk) elS[t] = el;
+    float* gsc = a.gsc + ch * 3 * kCh * kChDk;  // [3][64][128]
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int rt = j & 3, kt = w + 4 * (j >> 2);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int o = (16 * rt + 4 * g + r) * kChDk + 16 * kt + c;
+            gsc[o] = accQ[j][r];
+            gsc[kCh * kChDk + o] = -accK[j][r];
+            gsc[2 * kCh * kChDk + o] = accD[j][r];
+        }
+    }
     __syncthreads();
 
     // ---- backward of the solve: dA (strictly lower) from dP
@@ -384,90 +409,115 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
         }
     }
 
-    // ---- cumulative log decays
+    // ---- k, q and the cumulative log decays in LDS (rows past the end are zero; G repeats G_{L-1})
+    float* kS = big;
+    float* qS = big + kTK;
     float* Gs = big + 2 * kTK;
+    __syncthreads();
+    load_rows_lds(kS, in.k, tok0, p.H, L, p.qkv_dt);
+    load_rows_lds(qS, in.q, tok0, p.H, L, p.qkv_dt);
+    if (KDA) load_rows_lds(Gs, in.g, tok0, p.H, L, p.gate_dt);
+    else if (t < kCh) gS[t] = t < L ? load_elem(in.g, tok0 + static_cast<size_t>(t) * p.H, p.gate_dt) : 0.0f;
+    __syncthreads();
     if (KDA) {
         if (t < kChDk) {
             float run = 0.0f;
-#pragma unroll 8
             for (int r = 0; r < kCh; r++) {
-                if (r < L) run += load_elem(in.g, (tok0 + static_cast<size_t>(r) * p.H) * kChDk + t, p.gate_dt);
+                run += Gs[r * 132 + t];
                 Gs[r * 132 + t] = run;
             }
         }
     } else if (t == 0) {
         float run = 0.0f;
         for (int r = 0; r < kCh; r++) {
-            if (r < L) run += load_elem(in.g, tok0 + static_cast<size_t>(r) * p.H, p.gate_dt);
+            run += gS[r];
             gS[r] = run;
         }
     }
     __syncthreads();
     auto Gof = [&](int r, int kk) __attribute__((always_inline)) { return KDA ? Gs[r * 132 + kk] : gS[r]; };
+    float* dABG = big + 2 * kTK;  // scalar gate only (no per-key decays in LDS then)
+    if (!KDA) {
+        // one decay per pair: dA o Gamma, dM o Gamma and beta dA o Gamma
+        for (int i = t; i < kCh * kCh; i += kChThreads) {
+            const int r = i >> 6, q = i & 63;
+            const float gam = q <= r ? expf(gS[r] - gS[q]) : 0.0f;
+            const float da = dAs[r * kPW + q] * gam;
+            dAs[r * kPW + q] = da;
+            dMs[r * kPW + q] *= gam;
+            dABG[r * kPW + q] = bS[r] * da;
+        }
+        __syncthreads();
+    }
 
-    // ---- elementwise terms of Kp = k E, Qp = q E, Kd = k F and E_L
-    {
+    // ---- the pair sums through A and M (D: the decays)
+    //   T1 = sum_{i<r} dA_ri k_i D_ri,  T2 = sum_{i<=r} dM_ri k_i D_ri,
+    //   T3 = sum_{s>r} beta_s dA_sr k_s D_sr + sum_{s>=r} dM_sr q_s D_sr,
+    // with the elementwise terms of Kp = k E, Qp = q E, Kd = k F: the outputs dq, dk and the
+    // cumulative-decay gradient dG (into the gsc dKd slot), and beta's pair term k_r T1
+    float* gKd = gsc + 2 * kCh * kChDk;
+    auto finish = [&](int row, int key, float t1, float t2, float t3) __attribute__((always_inline)) {
+        const int o = row * kChDk + key;
+        const float dQp = gsc[o], dKp = gsc[kCh * kChDk + o], dKd = gKd[o];
+        const float G = Gof(row, key), GL = Gof(L - 1, key);
+        const float E = expf(G), F = expf(GL - G);
+        const float kv = kS[row * 132 + key], qv = qS[row * 132 + key], bt = bS[row];
+        const float Kp = kv * E, Qp = qv * E, Kd = kv * F;
+        if (row < L) {
+            const size_t e = (tok0 + static_cast<size_t>(row) * p.H) * kChDk + key;
+            a.dq[e] = __builtin_fmaf(E, dQp, t2);
+            a.dk[e] = __builtin_fmaf(E, dKp, __builtin_fmaf(F, dKd, __builtin_fmaf(bt, t1, t3)));
+        }
+        gKd[o] = __builtin_fmaf(dKp, Kp, __builtin_fmaf(dQp, Qp, -dKd * Kd)) +
+                 __builtin_fmaf(bt * kv, t1, __builtin_fmaf(qv, t2, -kv * t3));
+        return dKd * Kd;  // this element's share of dG_{L-1} through F and its k t1 below
+    };
+    if (!KDA) {
+        // tiles (rt, kt) of this wave on the matrix cores, one decay per pair folded into dA, dM
         float colsum[2] = {0.0f, 0.0f};
+        float bc[4][4];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
-            const float GL = Gof(L - 1, key);
+            f4 T1 = {0.0f, 0.0f, 0.0f, 0.0f}, T2 = T1, T3 = T1;
+#pragma unroll 4
+            for (int s = 0; s < 16; s++) {
+                const int tk = 4 * s + g;
+                const float bk = kS[tk * 132 + key], bq = qS[tk * 132 + key];
+                T1 = mfma4(dAs[(16 * rt + c) * kPW + tk], bk, T1);
+                T2 = mfma4(dMs[(16 * rt + c) * kPW + tk], bk, T2);
+                T3 = mfma4(dABG[tk * kPW + 16 * rt + c], bk, T3);
+                T3 = mfma4(dMs[tk * kPW + 16 * rt + c], bq, T3);
+            }
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int row = 16 * rt + 4 * g + r;
-                const float G = Gof(row, key);
-                const float E = expf(G), F = expf(GL - G);
-                const float Kp = R[RecB::KP + row * RecB::PK + key], Qp = R[RecB::QP + row * RecB::PK + key];
-                const float Kd = R[RecB::KD + row * RecB::PKD + key];
-                const float dQp = accQ[j][r], dKp = -accK[j][r], dKd = accD[j][r];
-                accQ[j][r] = E * dQp;
-                accK[j][r] = __builtin_fmaf(E, dKp, F * dKd);
-                accD[j][r] = __builtin_fmaf(dKp, Kp, __builtin_fmaf(dQp, Qp, -dKd * Kd));
-                colsum[j >> 2] = __builtin_fmaf(dKd, Kd, colsum[j >> 2]);
+                colsum[j >> 2] += finish(row, key, T1[r], T2[r], T3[r]);
+                bc[rt][r] = (j < 4 ? 0.0f : bc[rt][r]) + kS[row * 132 + key] * T1[r];
             }
             sched_fence();
         }
+        // colsum: over this lane group's rows, then the four groups; key 16 kt + c
         colsum[0] = rows_sum(colsum[0]);
         colsum[1] = rows_sum(colsum[1]);
+        if (g == 0) {
+            elS2[16 * w + c] = colsum[0];
+            elS2[16 * (w + 4) + c] = colsum[1];
+        }
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
+        for (int rt = 0; rt < 4; rt++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int row = 16 * rt + 4 * g + r;
-                if (row == L - 1) accD[j][r] += colsum[j >> 2] + elS[key] * expf(Gof(L - 1, key));
-                if (row < L) {
-                    const size_t e = (tok0 + static_cast<size_t>(row) * p.H) * kChDk + key;
-                    a.dq[e] = accQ[j][r];
-                    a.dk[e] = accK[j][r];
-                    a.dGw[(ch * kCh + row) * kChDk + key] = accD[j][r];
-                }
+                const float v = group_sum<16>(bc[rt][r]);
+                if (c == 0) bpart[w][16 * rt + 4 * g + r] = v;
             }
-        }
-    }
-
-    // ---- pair sums through A and M
-    float* kS = big;
-    float* qS = big + kTK;
-    __syncthreads();
-    for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
-        const int r = idx >> 7, kk = idx & 127;
-        float kv = 0.0f, qv = 0.0f;
-        if (r < L) {
-            const size_t e = (tok0 + static_cast<size_t>(r) * p.H) * kChDk + kk;
-            kv = load_elem(in.k, e, p.qkv_dt);
-            qv = load_elem(in.q, e, p.qkv_dt);
-        }
-        kS[r * 132 + kk] = kv;
-        qS[r * 132 + kk] = qv;
-    }
-    __syncthreads();
-    if (KDA) {
-        // thread: key kk, rows rh + 2 jj; decays exp(G_r - G_i) per key inside the sums
+    } else {
+        // thread: key kk, rows rh + 2 jj (uniform over the wave); per-key decays in the sums
         const int kk = t & 127, rh = t >> 7;
+        float cs = 0.0f;
         for (int jj = 0; jj < 32; jj++) {
             const int r = rh + 2 * jj;
-            const float Gr = Gs[r * 132 + kk], kr = kS[r * 132 + kk], qr = qS[r * 132 + kk];
+            const float Gr = Gs[r * 132 + kk], kr = kS[r * 132 + kk];
             float T1 = 0.0f, T2 = 0.0f, T3 = 0.0f;
             for (int i = 0; i <= r; i++) {
                 const float kd = kS[i * 132 + kk] * __expf(Gr - Gs[i * 132 + kk]);
@@ -479,79 +529,23 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
                 const float wk = bS[s2] * dAs[s2 * kPW + r] * kS[s2 * 132 + kk];
                 T3 = __builtin_fmaf(__builtin_fmaf(dMs[s2 * kPW + r], qS[s2 * 132 + kk], wk), d, T3);
             }
-            const float bt = bS[r];
-            // the rows are uniform over the wave: its 64 keys' share of beta's pair term
+            cs += finish(r, kk, T1, T2, T3);
             const float bsum = wave_sum(kr * T1);
             if (lane == 0) bpart[w][r] = bsum;
-            if (r < L) {
-                const size_t e = (tok0 + static_cast<size_t>(r) * p.H) * kChDk + kk;
-                a.dq[e] += T2;
-                a.dk[e] += __builtin_fmaf(bt, T1, T3);
-                a.dGw[(ch * kCh + r) * kChDk + kk] += __builtin_fmaf(bt * kr, T1, __builtin_fmaf(qr, T2, -kr * T3));
-            }
         }
-    } else {
-        // one decay per pair: dA o Gamma, dM o Gamma and beta dA o Gamma, then products with K, Q
-        float* dABG = big + 2 * kTK;
-        for (int i = t; i < kCh * kCh; i += kChThreads) {
-            const int r = i >> 6, q = i & 63;
-            const float gam = q <= r ? expf(gS[r] - gS[q]) : 0.0f;
-            const float da = dAs[r * kPW + q] * gam;
-            dAs[r * kPW + q] = da;
-            dMs[r * kPW + q] *= gam;
-            dABG[r * kPW + q] = bS[r] * da;
-        }
-        __syncthreads();
-        f4 T1[8], T2[8], T3[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) T1[j] = T2[j] = T3[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 2
-        for (int s = 0; s < 16; s++) {
-            const int tk = 4 * s + g;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int rt = j & 3, kt = w + 4 * (j >> 2);
-                const float bk = kS[tk * 132 + 16 * kt + c], bq = qS[tk * 132 + 16 * kt + c];
-                T1[j] = mfma4(dAs[(16 * rt + c) * kPW + tk], bk, T1[j]);
-                T2[j] = mfma4(dMs[(16 * rt + c) * kPW + tk], bk, T2[j]);
-                T3[j] = mfma4(dABG[tk * kPW + 16 * rt + c], bk, T3[j]);
-                T3[j] = mfma4(dMs[tk * kPW + 16 * rt + c], bq, T3[j]);
-            }
-        }
-        float bc[4][4];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int row = 16 * rt + 4 * g + r;
-                const float kr = kS[row * 132 + key], qr = qS[row * 132 + key], bt = bS[row];
-                const float t1 = T1[j][r], t2 = T2[j][r], t3 = T3[j][r];
-                bc[rt][r] = (j < 4 ? 0.0f : bc[rt][r]) + kr * t1;
-                if (row < L) {
-                    const size_t e = (tok0 + static_cast<size_t>(row) * p.H) * kChDk + key;
-                    a.dq[e] += t2;
-                    a.dk[e] += __builtin_fmaf(bt, t1, t3);
-                    a.dGw[(ch * kCh + row) * kChDk + key] += __builtin_fmaf(bt * kr, t1, __builtin_fmaf(qr, t2, -kr * t3));
-                }
-            }
-        }
-        // beta's pair term: this wave's 32 keys of every row, summed over the 16 lanes of a row
-#pragma unroll
-        for (int rt = 0; rt < 4; rt++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float v = group_sum<16>(bc[rt][r]);
-                if (c == 0) bpart[w][16 * rt + 4 * g + r] = v;
-            }
+        // the two row halves of key kk sit in waves w and w ^ 2
+        elS2[t] = cs;
     }
 
-    // ---- gate and beta gradients
-    float* dGs = big;           // [64][132]: total cumulative-decay gradient
+    // ---- gate and beta gradients: dG from gsc into LDS (the key array is no longer read)
+    float* dGs = big;
     __syncthreads();
     for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
         const int r = idx >> 7, kk = idx & 127;
-        dGs[r * 132 + kk] = r < L ? a.dGw[(ch * kCh + r) * kChDk + kk] : 0.0f;
+        float v = gKd[r * kChDk + kk];
+        // F_i = exp(G_{L-1} - G_i) and E_L = exp(G_{L-1}) feed dG_{L-1} as well
+        if (r == L - 1) v += (KDA ? elS2[kk] + elS2[kk + kChDk] : elS2[kk]) + elS[kk] * expf(Gof(L - 1, kk));
+        dGs[r * 132 + kk] = r < L ? v : 0.0f;
     }
     __syncthreads();
     if (KDA) {
@@ -597,8 +591,8 @@ ChunkBwdLayout chunk_bwd_layout(const la_config& c) {
     L.dD = L.D + up(units * kCh * c.d_v * sizeof(float));
     L.dSe = L.dD + up(units * kCh * c.d_v * sizeof(float));
     L.dbp = L.dSe + up(units * kChDk * c.d_v * sizeof(float));
-    L.dGw = L.dbp + up(static_cast<size_t>(c.d_v / 64) * units * kCh * sizeof(float));
-    L.total = L.dGw + up(units * kCh * kChDk * sizeof(float));
+    L.gsc = L.dbp + up(static_cast<size_t>(c.d_v / 64) * units * kCh * sizeof(float));
+    L.total = L.gsc + up(units * 3 * kCh * kChDk * sizeof(float));
     return L;
 }
 
@@ -625,7 +619,7 @@ hipError_t launch_chunk_bwd(const la_config& c, const FwdArgs& fa, const BwdArgs
     ChunkBwdPtrs a{ck, ba.dout, ba.dST, ba.dq, ba.dk, ba.dv, ba.dg, ba.dbeta, ba.dS0, rec,
                    reinterpret_cast<float*>(ws + L.U), reinterpret_cast<float*>(ws + L.D),
                    reinterpret_cast<float*>(ws + L.dD), reinterpret_cast<float*>(ws + L.dSe),
-                   reinterpret_cast<float*>(ws + L.dbp), reinterpret_cast<float*>(ws + L.dGw)};
+                   reinterpret_cast<float*>(ws + L.dbp), reinterpret_cast<float*>(ws + L.gsc)};
     const unsigned units = static_cast<unsigned>(c.B) * c.H * p.nch;
     hipLaunchKernelGGL(chunk_recompute_kernel, dim3(units * p.ntile), dim3(kChThreads), 0, s, p, in, a);
     e = hipGetLastError();

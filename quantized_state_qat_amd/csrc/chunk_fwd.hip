@@ -51,29 +51,22 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
     const size_t tok0 = (static_cast<size_t>(b) * T + t0) * H + h;
     float* R = rec + ((static_cast<size_t>(b) * H + h) * p.nch + cc) * (BWD ? RecB::SIZE : RecF::SIZE);
 
-    for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
-        const int r = idx >> 7, kk = idx & 127;
-        float kv = 0.0f, qv = 0.0f;
-        if (r < L) {
-            const size_t e = (tok0 + static_cast<size_t>(r) * H) * kChDk + kk;
-            kv = load_elem(in.k, e, p.qkv_dt);
-            qv = load_elem(in.q, e, p.qkv_dt);
-        }
-        kS[r * kPT + kk] = kv;
-        qS[r * kPT + kk] = qv;
-    }
+    load_rows_lds(kS, in.k, tok0, H, L, p.qkv_dt);
+    load_rows_lds(qS, in.q, tok0, H, L, p.qkv_dt);
+    if (KDA) load_rows_lds(GS, in.g, tok0, H, L, p.gate_dt);
     if (t < kCh) {
         const bool ok = t < L;
         bS[t] = ok ? load_elem(in.beta, tok0 + static_cast<size_t>(t) * H, p.gate_dt) : 0.0f;
         if (!KDA) gS[t] = ok ? load_elem(in.g, tok0 + static_cast<size_t>(t) * H, p.gate_dt) : 0.0f;
     }
     if (KDA) {
-        // cumulative log decays per key; rows past the end repeat G_{L-1}
+        // cumulative log decays per key (rows past the end repeat G_{L-1}): one thread per key
+        // sums down its column of the gates loaded above
+        __syncthreads();
         if (t < kChDk) {
             float run = 0.0f;
-#pragma unroll 8
             for (int r = 0; r < kCh; r++) {
-                if (r < L) run += load_elem(in.g, (tok0 + static_cast<size_t>(r) * H) * kChDk + t, p.gate_dt);
+                run += GS[r * kPT + t];
                 GS[r * kPT + t] = run;
             }
         }
@@ -174,18 +167,42 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
     // the solve, in the token arrays' space
     float* W0 = big;
     float* W1 = big + kCh * kPW;
-    float* red = big + 2 * kCh * kPW;
+    float* Ys = big + 2 * kCh * kPW;  // four 16 x 16 wave-private tiles
     const float* Pm;
     if (p.degree == 0) {
-        // (I + A)^-1 by forward substitution, one row at a time, four partial sums per column
-        const int j = t & 63, part = t >> 6;
-        for (int r = 0; r < kCh; r++) {
-            float acc = 0.0f;
-            for (int i = part; i < r; i += 4) acc = __builtin_fmaf(Am[r * kPW + i], W0[i * kPW + j], acc);
-            red[part * kCh + j] = acc;
-            __syncthreads();
-            if (part == 0)
-                W0[r * kPW + j] = (j == r ? 1.0f : 0.0f) - ((red[j] + red[kCh + j]) + (red[2 * kCh + j] + red[3 * kCh + j]));
+        // (I + A)^-1 in 16 x 16 blocks.  Diagonal blocks by forward substitution, wave w
+        // inverting block w (lane (g, c) holds column c and sums rows i = g mod 4; a row's
+        // values are read back by the same wave, whose LDS accesses are in order).  Then block
+        // rows k = 1..3: T_kj = -T_kk sum_{l=j}^{k-1} A_kl T_lj, tile (k, j) on wave j.
+        for (int idx = t; idx < kCh * kCh; idx += kChThreads) W0[(idx >> 6) * kPW + (idx & 63)] = 0.0f;
+        __syncthreads();
+        const int lane = t & 63, w = t >> 6, g = lane >> 4, c = lane & 15, o = 16 * w;
+        for (int r = 0; r < 16; r++) {
+            float part = 0.0f;
+            for (int i = g; i < r; i += 4)
+                part = __builtin_fmaf(Am[(o + r) * kPW + o + i], W0[(o + i) * kPW + o + c], part);
+            const float sum = rows_sum(part);
+            if (g == 0) W0[(o + r) * kPW + o + c] = (r == c ? 1.0f : 0.0f) - sum;
+        }
+        __syncthreads();
+        float* Y = Ys + 256 * w;
+        for (int k = 1; k < 4; k++) {
+            if (w < k) {
+                f4 y = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int l = w; l < k; l++) {
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; s2++)
+                        y = mfma4(Am[(16 * k + c) * kPW + 16 * l + 4 * s2 + g], W0[(16 * l + 4 * s2 + g) * kPW + o + c], y);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r++) Y[(4 * g + r) * 16 + c] = y[r];
+                f4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s2 = 0; s2 < 4; s2++)
+                    z = mfma4(W0[(16 * k + c) * kPW + 16 * k + 4 * s2 + g], Y[(4 * s2 + g) * 16 + c], z);
+#pragma unroll
+                for (int r = 0; r < 4; r++) W0[(16 * k + 4 * g + r) * kPW + o + c] = -z[r];
+            }
             __syncthreads();
         }
         Pm = W0;
@@ -226,8 +243,11 @@ template <int QMODE, int G>
 __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p, ChunkIn in, const float* __restrict__ S0,
                                                                   void* o, float* ST, float* ckpts,
                                                                   const float* __restrict__ rec) {
-    __shared__ __align__(16) float R[RecF::SIZE];
+    __shared__ __align__(16) float RA[RecF::PART2];               // Kp, Qp
+    __shared__ __align__(16) float RB[RecF::SIZE - RecF::PART2];  // P, M, Kd^T, E_L
     __shared__ WaveQdqShared<kChDk, QMODE, G> qsh;
+    constexpr int bP = RecF::P - RecF::PART2, bM = RecF::M - RecF::PART2, bKDT = RecF::KDT - RecF::PART2,
+                  bEL = RecF::EL - RecF::PART2;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g0 = lane >> 4, c0 = lane & 15;
     int tile, bh;
     chunk_tile_of(blockIdx.x, p.ntile, tile, bh);
@@ -239,6 +259,8 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
 #pragma unroll
     for (int m = 0; m < 32; m++) s[m] = S0 ? S0[soff + static_cast<size_t>(kmap(m, g0)) * dv] : 0.0f;
     int qpar = 0;
+    const float* recu = rec + static_cast<size_t>(bh) * p.nch * RecF::SIZE;
+    lds_dma(RA, recu, RecF::PART2);
     for (int cc = 0; cc < p.nch; cc++) {
         const int g = opaque(g0), c = opaque(c0);
         const int t0 = cc * kCh, L = min(kCh, p.T - t0);
@@ -247,8 +269,11 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
 #pragma unroll
             for (int m = 0; m < 32; m++) dst[static_cast<size_t>(kmap(m, g)) * dv] = s[m];
         }
-        __syncthreads();  // every wave is done with the previous record
-        copy_to_lds(R, rec + (static_cast<size_t>(bh) * p.nch + cc) * RecF::SIZE, RecF::SIZE);
+        // part 1 of this chunk's record has arrived and every wave is done with part 2 of the
+        // previous one: load part 2 while the first products run
+        wait_all_mem();
+        __syncthreads();
+        lds_dma(RB, recu + static_cast<size_t>(cc) * RecF::SIZE + RecF::PART2, RecF::SIZE - RecF::PART2);
         const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
         float vv[16], bb[16];
 #pragma unroll
@@ -259,7 +284,6 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
             vv[i] = ok ? load_elem(in.v, e * dv + col, p.qkv_dt) : 0.0f;
             bb[i] = ok ? load_elem(in.beta, e, p.gate_dt) : 0.0f;
         }
-        __syncthreads();
 
         // X = Kp S, Y = Qp S
         f4 X[4], Y[4];
@@ -271,11 +295,15 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
 #pragma unroll
             for (int rt = 0; rt < 4; rt++) {
                 const int row = cmap(rt, c) * RecF::PK + key;
-                X[rt] = mfma4(R[RecF::KP + row], s[m], X[rt]);
-                Y[rt] = mfma4(R[RecF::QP + row], s[m], Y[rt]);
+                X[rt] = mfma4(RA[RecF::KP + row], s[m], X[rt]);
+                Y[rt] = mfma4(RA[RecF::QP + row], s[m], Y[rt]);
             }
             if ((m & 3) == 3) sched_fence();
         }
+        // part 2 has arrived and part 1 is free: load the next chunk's part 1
+        wait_all_mem();
+        __syncthreads();
+        if (cc + 1 < p.nch) lds_dma(RA, recu + static_cast<size_t>(cc + 1) * RecF::SIZE, RecF::PART2);
         // beta (V - X), then Delta = P (beta (V - X))
         float rv[16];
 #pragma unroll
@@ -287,7 +315,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
         for (int m = 0; m < 16; m++) {
             const int tk = kmap(m, g);
 #pragma unroll
-            for (int rt = 0; rt < 4; rt++) D[rt] = mfma4(R[RecF::P + cmap(rt, c) * RecF::PP + tk], rv[m], D[rt]);
+            for (int rt = 0; rt < 4; rt++) D[rt] = mfma4(RB[bP + cmap(rt, c) * RecF::PP + tk], rv[m], D[rt]);
             if ((m & 3) == 3) sched_fence();
         }
         // O = Y + M Delta
@@ -296,7 +324,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
             const int tk = kmap(m, g);
             const float dm = D[m >> 2][m & 3];
 #pragma unroll
-            for (int rt = 0; rt < 4; rt++) Y[rt] = mfma4(R[RecF::M + cmap(rt, c) * RecF::PP + tk], dm, Y[rt]);
+            for (int rt = 0; rt < 4; rt++) Y[rt] = mfma4(RB[bM + cmap(rt, c) * RecF::PP + tk], dm, Y[rt]);
             if ((m & 3) == 3) sched_fence();
         }
         if (o) {
@@ -311,10 +339,10 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
         for (int kt = 0; kt < 8; kt++) {
             f4 acc;
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[r] = R[RecF::EL + 16 * kt + 4 * r + g] * s[4 * kt + r];
+            for (int r = 0; r < 4; r++) acc[r] = RB[bEL + 16 * kt + 4 * r + g] * s[4 * kt + r];
 #pragma unroll
             for (int m = 0; m < 16; m++) {
-                acc = mfma4(R[RecF::KDT + cmap(kt, c) * RecF::PD + kmap(m, g)], D[m >> 2][m & 3], acc);
+                acc = mfma4(RB[bKDT + cmap(kt, c) * RecF::PD + kmap(m, g)], D[m >> 2][m & 3], acc);
                 if ((m & 7) == 7) sched_fence();
             }
 #pragma unroll

@@ -49,22 +49,84 @@ struct ChunkIn {
 };
 
 // Record of one (sequence, head, chunk), fp32, in the state pass's LDS layout.  Row pitches
-// are chosen so that the A-operand reads of 16 rows x 4 k-indices hit 64 distinct banks.
-// Forward: P, M [64][68]; Kp, Qp [token][132]; Kd transposed [key][68]; E_L [128].
+// are chosen so that the A-operand reads of 16 rows x 4 k-indices hit 64 distinct banks.  Each
+// record is two parts in the order the pass consumes them (part 1 is free once its first
+// products are done, part 2 at the chunk's end), so that the next chunk's parts can be loaded
+// into LDS while the current one is still being used.
+// Forward: part 1 Kp, Qp [token][132]; part 2 P, M [64][68], Kd transposed [key][68], E_L [128].
 struct RecF {
     static constexpr int PP = 68, PK = 132, PD = 68;
-    static constexpr int P = 0, M = P + kCh * PP, KP = M + kCh * PP, QP = KP + kCh * PK, KDT = QP + kCh * PK;
-    static constexpr int EL = KDT + kChDk * PD, SIZE = EL + kChDk;
+    static constexpr int KP = 0, QP = KP + kCh * PK, PART2 = QP + kCh * PK;
+    static constexpr int P = PART2, M = P + kCh * PP, KDT = M + kCh * PP, EL = KDT + kChDk * PD, SIZE = EL + kChDk;
 };
 // Backward: the state gradient pass reads P and M transposed and Kp, Qp, Kd by token rows:
-// P, M [64][80]; Kp, Qp [token][144]; Kd [token][132]; E_L [128] (the pass's LDS prefix), then
+// part 1 Kd [token][132], M [64][80]; part 2 P [64][80], Qp, Kp [token][144], E_L [128]; then
 // A [64][68] for the gradient kernel.
 struct RecB {
     static constexpr int PP = 80, PK = 144, PKD = 132, PA = 68;
-    static constexpr int P = 0, M = P + kCh * PP, KP = M + kCh * PP, QP = KP + kCh * PK, KD = QP + kCh * PK;
-    static constexpr int EL = KD + kCh * PKD, LDS_SIZE = EL + kChDk, A = LDS_SIZE, SIZE = A + kCh * PA;
+    static constexpr int KD = 0, M = KD + kCh * PKD, PART2 = M + kCh * PP;
+    static constexpr int P = PART2, QP = P + kCh * PP, KP = QP + kCh * PK, EL = KP + kCh * PK;
+    static constexpr int LDS_SIZE = EL + kChDk, A = LDS_SIZE, SIZE = A + kCh * PA;
 };
 static_assert(RecF::SIZE % 64 == 0 && RecB::SIZE % 64 == 0 && RecB::LDS_SIZE % 4 == 0, "record alignment");
+static_assert(RecF::PART2 % 4 == 0 && RecB::PART2 % 4 == 0, "record parts start on 16-byte boundaries");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Start an asynchronous copy of n floats (a multiple of four, 16-byte aligned) from global
+// memory into LDS with direct-to-LDS loads: 16 bytes per lane, one kilobyte per wave
+// instruction, wave w taking kilobytes w, w + 4, ...  Complete after s_waitcnt vmcnt(0) in
+// every wave and a barrier.
+__device__ __forceinline__ void lds_dma(float* dst, const float* __restrict__ src, int n) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int full = n >> 8;
+    for (int i = w; i < full; i += 4)
+        __builtin_amdgcn_global_load_lds(src + (i << 8) + 4 * lane, (lds_void_t*)(dst + (i << 8)), 16,
+                                         0, 0);
+    const int rem = n & 255;
+    if (rem && w == (full & 3) && 4 * lane < rem)
+        __builtin_amdgcn_global_load_lds(src + (full << 8) + 4 * lane, (lds_void_t*)(dst + (full << 8)),
+                                         16, 0, 0);
+}
+
+// Rows 0 .. L-1 of a [token][128] input (token r at element (tok0 + r H) 128), widened to fp32,
+// into LDS dst[r * 132 + k]; rows L .. 63 zero.  A thread takes 8 consecutive elements of each
+// of four rows (one 16-byte load for bf16, two for fp32), all loads in flight together.
+__device__ __forceinline__ void load_rows_lds(float* dst, const void* src, size_t tok0, int H, int L, int dtype) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const int gi = threadIdx.x + kChThreads * u, r = gi >> 4, k8 = (gi & 15) * 8;
+        const size_t e = (tok0 + static_cast<size_t>(r) * H) * kChDk + k8;
+        if (r >= L) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) v[u][i] = 0.0f;
+        } else if (dtype == LA_BF16) {
+            const uint4 wv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + e);
+            const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                v[u][2 * i] = __uint_as_float(ws[i] << 16);
+                v[u][2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
+            }
+        } else {
+            const float4 a0 = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + e);
+            const float4 a1 = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + e + 4);
+            v[u][0] = a0.x; v[u][1] = a0.y; v[u][2] = a0.z; v[u][3] = a0.w;
+            v[u][4] = a1.x; v[u][5] = a1.y; v[u][6] = a1.z; v[u][7] = a1.w;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const int gi = threadIdx.x + kChThreads * u, r = gi >> 4, k8 = (gi & 15) * 8;
+        float4* d = reinterpret_cast<float4*>(dst + r * 132 + k8);
+        d[0] = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+        d[1] = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+    }
+}
+
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ int cmap(int blk, int x) { return 16 * blk + 4 * (x & 3) + (x >> 2); }
 __device__ __forceinline__ int kmap(int m, int g) { return 16 * (m >> 2) + 4 * (m & 3) + g; }
