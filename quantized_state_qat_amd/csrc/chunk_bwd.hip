@@ -472,14 +472,36 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
                  __builtin_fmaf(bt * kv, t1, __builtin_fmaf(qv, t2, -kv * t3));
         return dKd * Kd;  // this element's share of dG_{L-1} through F and its k t1 below
     };
-    if (!KDA) {
-        // tiles (rt, kt) of this wave on the matrix cores, one decay per pair folded into dA, dM
-        float colsum[2] = {0.0f, 0.0f};
-        float bc[4][4];
+    // KDA: a chunk whose gates could overflow a factored decay (a positive gate and a cumulative
+    // range above 80) takes the per-key sums over every block
+    __shared__ int unsafe;
+    if (KDA) {
+        if (t == 0) unsafe = 0;
+        __syncthreads();
+        if (t < kChDk) {
+            float gmin = 0.0f, gmax = 0.0f, prev = 0.0f;
+            bool pos = false;
+            for (int r = 0; r < L; r++) {
+                const float G = Gs[r * 132 + t];
+                pos = pos || G > prev;
+                prev = G;
+                gmin = fminf(gmin, G);
+                gmax = fmaxf(gmax, G);
+            }
+            if (pos && gmax - gmin > 80.0f) atomicOr(&unsafe, 1);
+        }
+        __syncthreads();
+    }
+    const bool fact = !KDA || unsafe == 0;
+    // tiles (rt, kt) of this wave: rows of block rt, keys 16 kt + c
+    float colsum[2] = {0.0f, 0.0f};
+    float bc[4][4];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
-            f4 T1 = {0.0f, 0.0f, 0.0f, 0.0f}, T2 = T1, T3 = T1;
+    for (int j = 0; j < 8; j++) {
+        const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
+        f4 T1 = {0.0f, 0.0f, 0.0f, 0.0f}, T2 = T1, T3 = T1;
+        if (!KDA) {
+            // one decay per pair, folded into dA and dM above
 #pragma unroll 4
             for (int s = 0; s < 16; s++) {
                 const int tk = 4 * s + g;
@@ -489,53 +511,90 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
                 T3 = mfma4(dABG[tk * kPW + 16 * rt + c], bk, T3);
                 T3 = mfma4(dMs[tk * kPW + 16 * rt + c], bq, T3);
             }
+        } else {
+            if (fact) {
+                // blocks I < rt: e^{G_r - G_i} = e^{G_r - ref} e^{ref - G_i}, ref = G at the end
+                // of block I; the products over block I's tokens on the matrix cores
+#pragma unroll
+                for (int I = 0; I < rt; I++) {
+                    const float rf = Gs[(16 * I + 15) * 132 + key];
+                    f4 P1 = {0.0f, 0.0f, 0.0f, 0.0f}, P2 = P1;
+#pragma unroll
+                    for (int s = 0; s < 4; s++) {
+                        const int tk = 16 * I + 4 * s + g;
+                        const float bl = kS[tk * 132 + key] * __expf(rf - Gs[tk * 132 + key]);
+                        P1 = mfma4(dAs[(16 * rt + c) * kPW + tk], bl, P1);
+                        P2 = mfma4(dMs[(16 * rt + c) * kPW + tk], bl, P2);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const float e = __expf(Gs[(16 * rt + 4 * g + r) * 132 + key] - rf);
+                        T1[r] = __builtin_fmaf(e, P1[r], T1[r]);
+                        T2[r] = __builtin_fmaf(e, P2[r], T2[r]);
+                    }
+                }
+                // blocks R > rt: e^{G_s - G_i} = e^{G_s - ref} e^{ref - G_i}, ref = G at the end of
+                // block rt; products over block R's tokens
+#pragma unroll
+                for (int R2 = rt + 1; R2 < 4; R2++) {
+                    const float rf = Gs[(16 * rt + 15) * 132 + key];
+                    f4 P3 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int s = 0; s < 4; s++) {
+                        const int tk = 16 * R2 + 4 * s + g;
+                        const float er = __expf(Gs[tk * 132 + key] - rf);
+                        P3 = mfma4(bS[tk] * dAs[tk * kPW + 16 * rt + c], kS[tk * 132 + key] * er, P3);
+                        P3 = mfma4(dMs[tk * kPW + 16 * rt + c], qS[tk * 132 + key] * er, P3);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        T3[r] = __builtin_fmaf(__expf(rf - Gs[(16 * rt + 4 * g + r) * 132 + key]), P3[r], T3[r]);
+                }
+            }
+            // per-key sums: block rt itself (every block when the factors are not safe); dA is zero
+            // on and above the diagonal and dM above it, and each term's decay is between the
+            // earlier and the later token
+            const int i_lo = fact ? 16 * rt : 0, i_hi = fact ? 16 * rt + 16 : kCh;
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int row = 16 * rt + 4 * g + r;
-                colsum[j >> 2] += finish(row, key, T1[r], T2[r], T3[r]);
-                bc[rt][r] = (j < 4 ? 0.0f : bc[rt][r]) + kS[row * 132 + key] * T1[r];
+                const float Gr = Gs[row * 132 + key];
+                float t1 = 0.0f, t2 = 0.0f, t3 = 0.0f;
+                for (int i = i_lo; i < i_hi; i++) {
+                    const float Gi = Gs[i * 132 + key], ki = kS[i * 132 + key];
+                    const float d = __expf(i <= row ? Gr - Gi : Gi - Gr);
+                    const float dl = i <= row ? d : 0.0f, du = i >= row ? d : 0.0f;  // no 0 * inf
+                    t1 = __builtin_fmaf(dAs[row * kPW + i] * ki, dl, t1);
+                    t2 = __builtin_fmaf(dMs[row * kPW + i] * ki, dl, t2);
+                    t3 = __builtin_fmaf(__builtin_fmaf(bS[i] * dAs[i * kPW + row], ki, dMs[i * kPW + row] * qS[i * 132 + key]), du, t3);
+                }
+                T1[r] += t1;
+                T2[r] += t2;
+                T3[r] += t3;
             }
-            sched_fence();
-        }
-        // colsum: over this lane group's rows, then the four groups; key 16 kt + c
-        colsum[0] = rows_sum(colsum[0]);
-        colsum[1] = rows_sum(colsum[1]);
-        if (g == 0) {
-            elS2[16 * w + c] = colsum[0];
-            elS2[16 * (w + 4) + c] = colsum[1];
         }
 #pragma unroll
-        for (int rt = 0; rt < 4; rt++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float v = group_sum<16>(bc[rt][r]);
-                if (c == 0) bpart[w][16 * rt + 4 * g + r] = v;
-            }
-    } else {
-        // thread: key kk, rows rh + 2 jj (uniform over the wave); per-key decays in the sums
-        const int kk = t & 127, rh = t >> 7;
-        float cs = 0.0f;
-        for (int jj = 0; jj < 32; jj++) {
-            const int r = rh + 2 * jj;
-            const float Gr = Gs[r * 132 + kk], kr = kS[r * 132 + kk];
-            float T1 = 0.0f, T2 = 0.0f, T3 = 0.0f;
-            for (int i = 0; i <= r; i++) {
-                const float kd = kS[i * 132 + kk] * __expf(Gr - Gs[i * 132 + kk]);
-                T1 = __builtin_fmaf(dAs[r * kPW + i], kd, T1);
-                T2 = __builtin_fmaf(dMs[r * kPW + i], kd, T2);
-            }
-            for (int s2 = r; s2 < kCh; s2++) {
-                const float d = __expf(Gs[s2 * 132 + kk] - Gr);
-                const float wk = bS[s2] * dAs[s2 * kPW + r] * kS[s2 * 132 + kk];
-                T3 = __builtin_fmaf(__builtin_fmaf(dMs[s2 * kPW + r], qS[s2 * 132 + kk], wk), d, T3);
-            }
-            cs += finish(r, kk, T1, T2, T3);
-            const float bsum = wave_sum(kr * T1);
-            if (lane == 0) bpart[w][r] = bsum;
+        for (int r = 0; r < 4; r++) {
+            const int row = 16 * rt + 4 * g + r;
+            colsum[j >> 2] += finish(row, key, T1[r], T2[r], T3[r]);
+            bc[rt][r] = (j < 4 ? 0.0f : bc[rt][r]) + kS[row * 132 + key] * T1[r];
         }
-        // the two row halves of key kk sit in waves w and w ^ 2
-        elS2[t] = cs;
+        sched_fence();
     }
+    // colsum: over this lane group's rows, then the four groups; key 16 kt + c
+    colsum[0] = rows_sum(colsum[0]);
+    colsum[1] = rows_sum(colsum[1]);
+    if (g == 0) {
+        elS2[16 * w + c] = colsum[0];
+        elS2[16 * (w + 4) + c] = colsum[1];
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; rt++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const float v = group_sum<16>(bc[rt][r]);
+            if (c == 0) bpart[w][16 * rt + 4 * g + r] = v;
+        }
 
     // ---- gate and beta gradients: dG from gsc into LDS (the key array is no longer read)
     float* dGs = big;
@@ -544,7 +603,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
         const int r = idx >> 7, kk = idx & 127;
         float v = gKd[r * kChDk + kk];
         // F_i = exp(G_{L-1} - G_i) and E_L = exp(G_{L-1}) feed dG_{L-1} as well
-        if (r == L - 1) v += (KDA ? elS2[kk] + elS2[kk + kChDk] : elS2[kk]) + elS[kk] * expf(Gof(L - 1, kk));
+        if (r == L - 1) v += elS2[kk] + elS[kk] * expf(Gof(L - 1, kk));
         dGs[r * 132 + kk] = r < L ? v : 0.0f;
     }
     __syncthreads();

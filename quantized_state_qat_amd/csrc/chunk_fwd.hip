@@ -109,35 +109,84 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
 
     // A (strictly lower) and M (lower with the diagonal)
     if (KDA) {
-        // per-key decays inside the sums: thread t forms rows r1 = t / 8 and r2 = 63 - r1 at
-        // columns (t % 8) + 8 j, so every thread has 65 row-column pairs' worth of work
-        const int r1 = t >> 3, r2 = 63 - r1, i0 = t & 7;
-        float a1[8], m1[8], a2[8], m2[8];
+        // Off-diagonal 16 x 16 tiles (rt > ct) on the matrix cores: with ref the cumulative
+        // gate of the last token of block ct, e^{G_r - G_i} = e^{G_r - ref} e^{ref - G_i}, and
+        // for gates <= 0 both factors are decays (<= 1), so neither overflows: A and M are
+        // (K o e^{G - ref}) (K o e^{ref - G})^T and (Q o e^{G - ref}) (K o e^{ref - G})^T.  A
+        // chunk whose gates could make a factor overflow (a positive gate and a cumulative
+        // range above 80) takes the per-key sums for every tile instead.  Diagonal tiles: the
+        // per-key sums, one thread per four (row, column) pairs.
+        const int lane = t & 63, w = t >> 6, g = lane >> 4, c = lane & 15;
+        __shared__ int unsafe;
+        if (t == 0) unsafe = 0;
+        for (int i = t; i < kCh * kPW; i += kChThreads) Am[i] = Mm[i] = 0.0f;
+        __syncthreads();
+        if (t < kChDk) {
+            float gmin = 0.0f, gmax = 0.0f, prev = 0.0f;
+            bool pos = false;
+            for (int r = 0; r < L; r++) {
+                const float G = GS[r * kPT + t];
+                pos = pos || G > prev;
+                prev = G;
+                gmin = fminf(gmin, G);
+                gmax = fmaxf(gmax, G);
+            }
+            if (pos && gmax - gmin > 80.0f) atomicOr(&unsafe, 1);
+        }
+        __syncthreads();
+        const bool fact = unsafe == 0;
+        if (fact) {
+            constexpr int PR[6] = {1, 2, 2, 3, 3, 3}, PC[6] = {0, 0, 1, 0, 1, 2};
+            for (int pi = w; pi < 6; pi += 4) {
+                const int rt = PR[pi], ct = PC[pi], ref = 16 * ct + 15;
+                f4 aA = {0.0f, 0.0f, 0.0f, 0.0f}, aM = aA;
+#pragma unroll 4
+                for (int s2 = 0; s2 < 32; s2++) {
+                    const int key = 4 * s2 + g;
+                    const float rf = GS[ref * kPT + key];
+                    const int ra = (16 * rt + c) * kPT + key, rb = (16 * ct + c) * kPT + key;
+                    const float er = __expf(GS[ra] - rf);
+                    const float bl = kS[rb] * __expf(rf - GS[rb]);
+                    aA = mfma4(kS[ra] * er, bl, aA);
+                    aM = mfma4(qS[ra] * er, bl, aM);
+                }
 #pragma unroll
-        for (int j = 0; j < 8; j++) a1[j] = m1[j] = a2[j] = m2[j] = 0.0f;
-#pragma unroll 2
-        for (int kk = 0; kk < kChDk; kk++) {
-            const float k1 = kS[r1 * kPT + kk], q1 = qS[r1 * kPT + kk], G1 = GS[r1 * kPT + kk];
-            const float k2 = kS[r2 * kPT + kk], q2 = qS[r2 * kPT + kk], G2 = GS[r2 * kPT + kk];
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int i = i0 + 8 * j;
-                const float ki = kS[i * kPT + kk], Gi = GS[i * kPT + kk];
-                const float kd1 = ki * __expf(i <= r1 ? G1 - Gi : 0.0f);
-                const float kd2 = ki * __expf(i <= r2 ? G2 - Gi : 0.0f);
-                a1[j] = __builtin_fmaf(k1, kd1, a1[j]);
-                m1[j] = __builtin_fmaf(q1, kd1, m1[j]);
-                a2[j] = __builtin_fmaf(k2, kd2, a2[j]);
-                m2[j] = __builtin_fmaf(q2, kd2, m2[j]);
+                for (int r = 0; r < 4; r++) {
+                    const int row = 16 * rt + 4 * g + r, col = 16 * ct + c;
+                    Am[row * kPW + col] = bS[row] * aA[r];
+                    Mm[row * kPW + col] = aM[r];
+                }
             }
         }
+        // the per-key sums: the diagonal tiles (wave w: tile w), and every lower tile of an
+        // unsafe chunk; lane: row 4 (lane / 16) + rr of the tile, column lane % 16
+        for (int tl = w; tl < (fact ? 4 : 10); tl += 4) {
+            int rt, ct;
+            if (fact) {
+                rt = ct = tl;
+            } else {
+                rt = tl < 1 ? 0 : tl < 3 ? 1 : tl < 6 ? 2 : 3;
+                ct = tl - (rt * (rt + 1)) / 2;
+            }
+            const int col = 16 * ct + c;
+            float aa[4] = {0.0f, 0.0f, 0.0f, 0.0f}, mm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+            for (int kk = 0; kk < kChDk; kk++) {
+                const float kc = kS[col * kPT + kk], Gc = GS[col * kPT + kk];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const int i = i0 + 8 * j;
-            Am[r1 * kPW + i] = i < r1 ? bS[r1] * a1[j] : 0.0f;
-            Mm[r1 * kPW + i] = i <= r1 ? m1[j] : 0.0f;
-            Am[r2 * kPW + i] = i < r2 ? bS[r2] * a2[j] : 0.0f;
-            Mm[r2 * kPW + i] = i <= r2 ? m2[j] : 0.0f;
+                for (int rr = 0; rr < 4; rr++) {
+                    const int row = 16 * rt + 4 * g + rr;
+                    const float kd = kc * __expf(col <= row ? GS[row * kPT + kk] - Gc : 0.0f);
+                    aa[rr] = __builtin_fmaf(kS[row * kPT + kk], kd, aa[rr]);
+                    mm[rr] = __builtin_fmaf(qS[row * kPT + kk], kd, mm[rr]);
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+                const int row = 16 * rt + 4 * g + rr;
+                Am[row * kPW + col] = col < row ? bS[row] * aa[rr] : 0.0f;
+                Mm[row * kPW + col] = col <= row ? mm[rr] : 0.0f;
+            }
         }
     } else {
         // one decay per token pair: K K^T and Q K^T on the matrix cores, then the decay

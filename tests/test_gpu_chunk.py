@@ -292,3 +292,38 @@ def test_chunk_backward_long_sequence_sampled(gate, degree):
             assert gu.err(r[n][b, :, h], rr[n][0, :, 0]) <= gu.TOL_F32, n
     for n in r:
         assert np.all(np.isfinite(r[n])), n
+
+
+@pytest.mark.parametrize("first_gate", [-20.0, -85.0], ids=["factored", "per_key_fallback"])
+def test_chunk_kda_positive_gates(first_gate):
+    """Gates above zero make the factored decays exceed one: with a cumulative range under 80 per
+    chunk the kernels keep the factored products, above it (first_gate = -85, then small
+    positive gates) they take the per-key sums for every block.  Forward and backward against
+    the chunked oracle.  The gates alternate +0.5 and -1.0 (factors above one inside a block,
+    a net decay like the workloads'), so the 1e-5 bar (fp32 against float64, relative to the
+    largest magnitude) applies as for the other cases; with gates near zero over a whole
+    chunk (no decay at all) A's entries grow and the solve's backward loses about one more
+    bit."""
+    T, B, H = 130, 1, 2
+    w = synth.Workload("chunk_posgate", B=B, T=T, H=H, d_k=128, d_v=128, gate="key", gate_dtype="f32", config_id=470)
+    d = synth.generate(w, with_do=True)
+    rng = np.random.default_rng(471)
+    alt = np.where(np.arange(T) % 2 == 0, 0.5, -1.0)[None, :, None, None]
+    g = alt + 0.05 * rng.standard_normal((B, T, H, 128))
+    g[:, ::64] = first_gate
+    d["g"] = synth.cast(g, "f32")
+    S0 = (rng.standard_normal((B, H, 128, 128)) * 0.3).astype(np.float32)
+    c = chunk_cfg(w, d, la.LA_SOLVE_NEUMANN, 7, qdq=E4M3, group=64, qdq_interval=64)
+    c.gate_dtype = la.LA_F32
+    o, ST, ck = run_chunk(c, d, S0, ckpt_interval=64)
+    tally = gu.CodeTally()
+    wo, ws = teacher_forced_chunks(c, d, ck, ST, o, tally)
+    assert wo <= gu.TOL_F32 and ws <= gu.TOL_F32, (wo, ws)
+    tally.check()
+    do = d["do"].f32
+    r = run_chunk_bwd(c, d, S0, ck, do, None)
+    ref = oracle_bwd_units(c, d, S0, ck, do.astype(np.float64), None, [(0, 0), (0, 1)])
+    for (b, h), rr in ref.items():
+        for n in GRADS:
+            assert gu.err(r[n][b, :, h], rr[n][0, :, 0]) <= gu.TOL_F32, n
+        assert gu.err(r["dS0"][b, h], rr["dS0"][0, 0]) <= gu.TOL_F32
