@@ -18,6 +18,20 @@ def pytest_runtest_setup(item):
         print(f"\n[gpu case] {item.nodeid}", flush=True)
 
 
+@pytest.fixture(autouse=True)
+def _float32_default():
+    """Every test starts from torch's float32 default; a test that needs float64 says so in its
+    tensors, and nothing it changes leaks into later tests."""
+    try:
+        import torch
+    except ImportError:
+        yield
+        return
+    torch.set_default_dtype(torch.float32)
+    yield
+    torch.set_default_dtype(torch.float32)
+
+
 @pytest.fixture(scope="session")
 def oracle_mod():
     import oracle

@@ -182,7 +182,7 @@ def test_chunk_short_and_edge_lengths(T):
 def test_chunk_empty_call_hands_the_state_through():
     torch = gu.torch_mod()
     c = la.Config(B=2, T=0, H=2, d_k=128, d_v=64, kernel=la.LA_KERNEL_CHUNK)
-    S0 = torch.randn(2, 2, 128, 64, device="cuda")
+    S0 = torch.randn(2, 2, 128, 64, device="cuda", dtype=torch.float32)
     ST = torch.full_like(S0, float("nan"))
     la.la_recurrent_fwd_chunk(c, None, None, None, None, None, S0, None, ST, None, None, 0)
     torch.cuda.synchronize()

@@ -24,7 +24,6 @@ import torch
 
 import oracle
 
-torch.set_default_dtype(torch.float64)
 
 
 def _rand_inputs(rng, B, T, H, dk, dv, gate="scalar", s0=0.3):
@@ -210,7 +209,7 @@ def _torch_replay_forward(q, k, v, g, beta, S0, gate, mode, group, had, W):
             M = S0[b, h].T
             ob = []
             for t in range(T):
-                a = torch.exp(g[b, t, h]) * torch.ones(dk) if gate == 0 else torch.exp(g[b, t, h])
+                a = torch.exp(g[b, t, h]) * torch.ones(dk, dtype=torch.float64) if gate == 0 else torch.exp(g[b, t, h])
                 kk = k[b, t, h]
                 Mt = M @ torch.diag(a)
                 delta = beta[b, t, h] * (v[b, t, h] - Mt @ kk)

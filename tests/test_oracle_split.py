@@ -130,7 +130,6 @@ def test_split_backward_matches_torch_autograd(oracle_mod, gate):
     """One sequence: E4M3 prefix rounding every 4 tokens, then an INT8 (Hadamard) suffix
     rounding every token, chained through the handoff state; torch float64 autograd with
     straight-through rounding in both parts."""
-    torch.set_default_dtype(torch.float64)
     rng = np.random.default_rng(6 + gate)
     T, pre, H, dk, dv = 11, 6, 2, 16, 32
     q, k, v, g, beta = _inputs(rng, T, H, dk, dv, "key" if gate else "scalar")
