@@ -17,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extr
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -190,7 +191,9 @@ def bench_long_e4m3(steps=3, warmup=1):
 
 def bench_kda_long(steps=3, warmup=1):
     """KDA B=8 H=16 T=4096 d=128, bf16 q/k/v, fp32 per-key gates and beta, E4M3 tile QDQ every
-    64 tokens: the forward (block kernel) and the straight-through backward (token kernel)."""
+    64 tokens: the forward (block kernel) and the straight-through backward from its checkpoints
+    (the chunk kernel: every rounding point is a checkpoint), with the per-token backward on the
+    same checkpoints beside it."""
     import torch
 
     import quantized_state_qat_amd as la
@@ -218,12 +221,19 @@ def bench_kda_long(steps=3, warmup=1):
     t_b = _time_calls(lambda: la.la_recurrent_bwd_ste(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, ck,
                                                       dev["do"], None, grads[0], grads[1], dv, grads[2], dbeta, dS0,
                                                       ws, nbytes, stream=stream), steps, warmup, stream)
+    ct = dataclasses.replace(c, kernel=la.LA_KERNEL_TOKEN)
+    nbt = la.la_bwd_workspace_bytes(ct)
+    wst = torch.empty((nbt + 255) // 4, dtype=torch.float32, device="cuda") if nbt > nbytes else ws
+    t_bt = _time_calls(lambda: la.la_recurrent_bwd_ste(ct, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None,
+                                                       ck, dev["do"], None, grads[0], grads[1], dv, grads[2], dbeta,
+                                                       dS0, wst, nbt, stream=stream), steps, warmup, stream)
     unit = w.d_k * w.d_v * w.B * w.H * w.T
     return {
         "workload": "kda_long_e4m3_64 B=8 H=16 T=4096 d_k=d_v=128 bf16 q/k/v, fp32 per-key gates and beta, E4M3 tile "
                     "QDQ every 64 tokens, 64-token checkpoints",
         "kernel_fwd": la.la_fwd_kernel_name(c), "kernel_bwd": la.la_bwd_kernel_name(c),
-        "ms_fwd": t_f * 1e3, "ms_bwd": t_b * 1e3, "updates_per_s_fwd": w.B * w.H * w.T / t_f,
+        "ms_fwd": t_f * 1e3, "ms_bwd": t_b * 1e3, "ms_bwd_token_kernel": t_bt * 1e3,
+        "workspace_bytes_bwd": nbytes, "updates_per_s_fwd": w.B * w.H * w.T / t_f,
         "roofline_fwd": _fp32_roofline(7.0 * unit, t_f, "forward: 7 d_k d_v flops per token-head (the per-key decay "
                                                         "adds d_k d_v multiplies, not counted)"),
         "roofline_bwd": _fp32_roofline(22.0 * unit, t_b, "backward: recompute 7 + adjoint 15 d_k d_v per token-head"),

@@ -44,13 +44,15 @@ struct ChunkBwdPtrs {
     float* dSe;           // [B H nch][128][d_v]: dL/d(state after the chunk)
     float* dbp;           // [ntile][B H nch][64]: beta-gradient partial per value tile
     float* gsc;           // [B H nch][3][64][128]: dQp, dKp, dKd of the products over columns,
-                          // then (in the dKd slot) the cumulative-decay gradient
+                          // then the Kd terms of the gate gradient (dQp slot) and the rest of
+                          // the cumulative-decay gradient (dKd slot)
 };
 
 // U and Delta of one (sequence, head, chunk, 64 columns) from the chunk's checkpoint.
 __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams p, ChunkIn in, ChunkBwdPtrs a) {
     __shared__ __align__(16) float Kp_s[kCh * RecB::PK];
     __shared__ __align__(16) float P_s[kCh * RecB::PP];
+    __shared__ __align__(16) float b_s[kCh];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
     const int tile = blockIdx.x % p.ntile, rest = blockIdx.x / p.ntile;
     const int cc = rest % p.nch, bh = rest / p.nch;
@@ -58,25 +60,31 @@ __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams
     const int dv = p.dv, col = tile * 64 + 16 * w + c;
     const size_t ch = static_cast<size_t>(bh) * p.nch + cc;
     const float* R = a.rec + ch * RecB::SIZE;
-    lds_dma(Kp_s, R + RecB::KP, kCh * RecB::PK);
-    lds_dma(P_s, R + RecB::P, kCh * RecB::PP);
+    const int t0 = cc * kCh, L = min(kCh, p.T - t0);
+    const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
+    // v first, while nothing else is in flight (a row past the end reads row 0, zeroed below)
+    uint32_t vr[16];
+    const size_t vrow = static_cast<size_t>(p.H) * dv;
+    load_raw<16>(vr, in.v, p.qkv_dt, [&](int i) {
+        const int tk = kmap(i, g);
+        return (tok0 * dv + col) + static_cast<size_t>(tk < L ? tk : 0) * vrow;
+    });
     const float* S = a.ckpts + ch * kChDk * dv + col;
     float s[32];
 #pragma unroll
     for (int m = 0; m < 32; m++) s[m] = S[static_cast<size_t>(kmap(m, g)) * dv];
-    const int t0 = cc * kCh, L = min(kCh, p.T - t0);
-    const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
+    lds_dma(Kp_s, R + RecB::KP, kCh * RecB::PK);
+    lds_dma(P_s, R + RecB::P, kCh * RecB::PP);
+    lds_dma(b_s, R + RecB::BT, kCh);
+    wait_all_mem();
+    __syncthreads();
     float vv[16], bb[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         const int tk = kmap(i, g);
-        const bool ok = tk < L;
-        const size_t e = tok0 + static_cast<size_t>(tk) * p.H;
-        vv[i] = ok ? load_elem(in.v, e * dv + col, p.qkv_dt) : 0.0f;
-        bb[i] = ok ? load_elem(in.beta, e, p.gate_dt) : 0.0f;
+        vv[i] = tk < L ? raw_f32(vr[i], p.qkv_dt) : 0.0f;
+        bb[i] = b_s[tk];
     }
-    wait_all_mem();
-    __syncthreads();
     f4 X[4];
 #pragma unroll
     for (int rt = 0; rt < 4; rt++) X[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -119,7 +127,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
     __shared__ __align__(16) float RB[RecB::LDS_SIZE - RecB::PART2];   // P, Qp, Kp, E_L
     __shared__ float red[4][kCh];
     constexpr int bP = RecB::P - RecB::PART2, bQP = RecB::QP - RecB::PART2, bKP = RecB::KP - RecB::PART2,
-                  bEL = RecB::EL - RecB::PART2;
+                  bEL = RecB::EL - RecB::PART2, bBT = RecB::BT - RecB::PART2;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g0 = lane >> 4, c0 = lane & 15;
     int tile, bh;
     chunk_tile_of(blockIdx.x, p.ntile, tile, bh);
@@ -145,14 +153,12 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
         wait_all_mem();
         __syncthreads();
         lds_dma(RB, recu + static_cast<size_t>(cc) * RecB::SIZE + RecB::PART2, RecB::LDS_SIZE - RecB::PART2);
-        float dO[16], uu[16], bb[16];
+        // upstream gradient (a row past the end reads row 0, zeroed where used) and U
+        float dOr[16], uu[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const int tk = kmap(i, g);
-            const bool ok = tk < L;
-            const size_t e = tok0 + static_cast<size_t>(tk) * p.H;
-            dO[i] = ok ? a.dout[e * dv + col] : 0.0f;
-            bb[i] = ok ? load_elem(in.beta, e, p.gate_dt) : 0.0f;
+            dOr[i] = a.dout[(tok0 + static_cast<size_t>(tk < L ? tk : 0) * p.H) * dv + col];
             uu[i] = a.U[(ch * kCh + tk) * dv + col];
         }
         // dDelta = Kd dS_end + M^T dO
@@ -166,6 +172,9 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
             for (int rt = 0; rt < 4; rt++) DD[rt] = mfma4(RA[RecB::KD + cmap(rt, c) * RecB::PKD + key], ds[m], DD[rt]);
             if ((m & 3) == 3) sched_fence();
         }
+        float dO[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) dO[i] = kmap(i, g) < L ? dOr[i] : 0.0f;
 #pragma unroll
         for (int m = 0; m < 16; m++) {
             const int tk = kmap(m, g);
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
         for (int i = 0; i < 16; i++) {
             const int tk = kmap(i, g);
             dDb[static_cast<size_t>(tk) * dv] = DD[i >> 2][i & 3];
-            du[i] = bb[i] * dR[i >> 2][i & 3];
+            du[i] = RB[bBT + tk] * dR[i >> 2][i & 3];
             if (tk < L) a.dv[(tok0 + static_cast<size_t>(tk) * p.H) * dv + col] = du[i];
         }
         // beta gradient of R = beta U, summed over this tile's columns
@@ -243,7 +252,6 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     __shared__ float dAs[kWM], dMs[kWM];
     __shared__ float bS[kCh], gS[kCh], elS[kChDk];
     __shared__ float bpart[4][kCh];  // beta's pair term per wave and token
-    __shared__ float elS2[2 * kChDk];  // column sums of dKd Kd (KDA: two row halves)
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, g0 = lane >> 4, c0 = lane & 15;
     const int g = g0, c = c0;
     const int cc = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     float* dPs = big + 3 * kWM;
     for (int i = t; i < kWM; i += kChThreads) dPs[i] = dMs[i] = 0.0f;
     bpart[w][lane] = 0.0f;
-    if (t < kCh) bS[t] = t < L ? load_elem(in.beta, tok0 + static_cast<size_t>(t) * p.H, p.gate_dt) : 0.0f;
+    if (t < kCh) bS[t] = R[RecB::BT + t];
 
     // ---- products over the value columns, 16 at a time
     float* dDs = big;
@@ -273,32 +281,52 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     float el = 0.0f;
     const float* Sck = a.ckpts + ch * kChDk * dv;
     const float* dSe = a.dSe + ch * kChDk * dv;
+    // slab sb: this thread's 16-byte pieces of U, dDelta, Delta, dO, dv (token t / 4) and of S,
+    // dS_end (keys t / 4 and 64 + t / 4); slab sb + 1 is loaded while slab sb is multiplied (a
+    // row past the end reads row 0 and is stored as zero)
+    struct Slab {
+        float4 u, dd, d, o, w, s0[2], se[2];
+    };
+    auto slab_load = [&](int sb, Slab& x) __attribute__((always_inline)) {
+        const int tk = t >> 2, cb = 16 * sb + ((t & 3) << 2);
+        const size_t wrow = (ch * kCh + tk) * dv + cb;
+        const size_t grow = (tok0 + static_cast<size_t>(tk < L ? tk : 0) * p.H) * dv + cb;
+        x.u = *reinterpret_cast<const float4*>(a.U + wrow);
+        x.dd = *reinterpret_cast<const float4*>(a.dD + wrow);
+        x.d = *reinterpret_cast<const float4*>(a.D + wrow);
+        x.o = *reinterpret_cast<const float4*>(a.dout + grow);
+        x.w = *reinterpret_cast<const float4*>(a.dv + grow);
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int idx = t + kChThreads * u, key = idx >> 2, k4 = (idx & 3) << 2;
+            const size_t kr = static_cast<size_t>(key) * dv + 16 * sb + k4;
+            x.s0[u] = *reinterpret_cast<const float4*>(Sck + kr);
+            x.se[u] = *reinterpret_cast<const float4*>(dSe + kr);
+        }
+    };
+    Slab nx;
+    slab_load(0, nx);
     for (int sb = 0; sb < dv / 16; sb++) {
         const int g = opaque(g0), c = opaque(c0);
         __syncthreads();
         {
-            const int tk = t >> 2, j4 = (t & 3) << 2, c0 = 16 * sb + j4;
-            const size_t wrow = (ch * kCh + tk) * dv + c0;
+            const int tk = t >> 2, j4 = (t & 3) << 2;
             const bool ok = tk < L;
-            const size_t grow = (tok0 + static_cast<size_t>(tk) * p.H) * dv + c0;
-            const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            float4 u4 = *reinterpret_cast<const float4*>(a.U + wrow);
             const float bt = bS[tk];
-            u4.x *= bt; u4.y *= bt; u4.z *= bt; u4.w *= bt;
-            *reinterpret_cast<float4*>(Rs + tk * kSP + j4) = u4;
-            *reinterpret_cast<float4*>(dDs + tk * kSP + j4) = *reinterpret_cast<const float4*>(a.dD + wrow);
-            *reinterpret_cast<float4*>(Ds + tk * kSP + j4) = *reinterpret_cast<const float4*>(a.D + wrow);
-            *reinterpret_cast<float4*>(dOs + tk * kSP + j4) = ok ? *reinterpret_cast<const float4*>(a.dout + grow) : z;
-            *reinterpret_cast<float4*>(dUs + tk * kSP + j4) = ok ? *reinterpret_cast<const float4*>(a.dv + grow) : z;
+            *reinterpret_cast<float4*>(Rs + tk * kSP + j4) = make_float4(nx.u.x * bt, nx.u.y * bt, nx.u.z * bt, nx.u.w * bt);
+            *reinterpret_cast<float4*>(dDs + tk * kSP + j4) = nx.dd;
+            *reinterpret_cast<float4*>(Ds + tk * kSP + j4) = nx.d;
+            *reinterpret_cast<float4*>(dOs + tk * kSP + j4) = keep_if(ok, nx.o);
+            *reinterpret_cast<float4*>(dUs + tk * kSP + j4) = keep_if(ok, nx.w);
 #pragma unroll
             for (int u = 0; u < 2; u++) {
                 const int idx = t + kChThreads * u, key = idx >> 2, k4 = (idx & 3) << 2;
-                const size_t kr = static_cast<size_t>(key) * dv + 16 * sb + k4;
-                *reinterpret_cast<float4*>(S0s + key * kSP + k4) = *reinterpret_cast<const float4*>(Sck + kr);
-                *reinterpret_cast<float4*>(dSes + key * kSP + k4) = *reinterpret_cast<const float4*>(dSe + kr);
+                *reinterpret_cast<float4*>(S0s + key * kSP + k4) = nx.s0[u];
+                *reinterpret_cast<float4*>(dSes + key * kSP + k4) = nx.se[u];
             }
         }
         __syncthreads();
+        slab_load(sb + 1 < dv / 16 ? sb + 1 : sb, nx);  // the last slab reloads itself
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             const int kc = 4 * s + g;
@@ -365,6 +393,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
         float* dZb = big + 5 * kWM;
         if (p.degree == 0) {
             // P = (I + A)^-1: dA = -P^T dP P^T
+#pragma unroll
             for (int i = t; i < kCh * kCh; i += kChThreads) Xb[(i >> 6) * kPW + (i & 63)] = R[RecB::P + (i >> 6) * RecB::PP + (i & 63)];
             __syncthreads();
             mm64<true, false>(Xb, Gb, Zb, nullptr);
@@ -377,6 +406,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
             // Z_j and the prefix P_{j-1} are recomputed from X at every step.
             int m = 0;
             while ((1 << m) - 1 < p.degree) m++;
+#pragma unroll
             for (int i = t; i < kCh * kCh; i += kChThreads) Xb[(i >> 6) * kPW + (i & 63)] = -R[RecB::A + (i >> 6) * RecB::PA + (i & 63)];
             for (int j = m - 1; j >= 0; j--) {
                 __syncthreads();
@@ -413,26 +443,24 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     float* kS = big;
     float* qS = big + kTK;
     float* Gs = big + 2 * kTK;
-    __syncthreads();
-    load_rows_lds(kS, in.k, tok0, p.H, L, p.qkv_dt);
-    load_rows_lds(qS, in.q, tok0, p.H, L, p.qkv_dt);
-    if (KDA) load_rows_lds(Gs, in.g, tok0, p.H, L, p.gate_dt);
-    else if (t < kCh) gS[t] = t < L ? load_elem(in.g, tok0 + static_cast<size_t>(t) * p.H, p.gate_dt) : 0.0f;
+    {
+        Rows rk, rq, rg;
+        rows_load(rk, in.k, tok0, p.H, L, p.qkv_dt);
+        rows_load(rq, in.q, tok0, p.H, L, p.qkv_dt);
+        if (KDA) rows_load(rg, in.g, tok0, p.H, L, p.gate_dt);
+        uint32_t gr[1];
+        if (!KDA) load_raw<1>(gr, in.g, p.gate_dt, [&](int) { return tok0 + static_cast<size_t>(t < L ? t & 63 : 0) * p.H; });
+        __syncthreads();
+        rows_store(kS, rk, L, p.qkv_dt);
+        rows_store(qS, rq, L, p.qkv_dt);
+        if (KDA) rows_store(Gs, rg, L, p.gate_dt);
+        else if (t < kCh) gS[t] = t < L ? raw_f32(gr[0], p.gate_dt) : 0.0f;
+    }
     __syncthreads();
     if (KDA) {
-        if (t < kChDk) {
-            float run = 0.0f;
-            for (int r = 0; r < kCh; r++) {
-                run += Gs[r * 132 + t];
-                Gs[r * 132 + t] = run;
-            }
-        }
-    } else if (t == 0) {
-        float run = 0.0f;
-        for (int r = 0; r < kCh; r++) {
-            run += gS[r];
-            gS[r] = run;
-        }
+        if (t < kChDk) cumsum_cols(Gs, t);
+    } else if (t < kCh) {
+        gS[t] = cumsum_lanes(gS[t]);  // zero past the end: those rows repeat G_{L-1}
     }
     __syncthreads();
     auto Gof = [&](int r, int kk) __attribute__((always_inline)) { return KDA ? Gs[r * 132 + kk] : gS[r]; };
@@ -456,9 +484,9 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     // with the elementwise terms of Kp = k E, Qp = q E, Kd = k F: the outputs dq, dk and the
     // cumulative-decay gradient dG (into the gsc dKd slot), and beta's pair term k_r T1
     float* gKd = gsc + 2 * kCh * kChDk;
-    auto finish = [&](int row, int key, float t1, float t2, float t3) __attribute__((always_inline)) {
+    auto finish = [&](int row, int key, float t1, float t2, float t3, float dQp, float dKp, float dKd)
+                      __attribute__((always_inline)) {
         const int o = row * kChDk + key;
-        const float dQp = gsc[o], dKp = gsc[kCh * kChDk + o], dKd = gKd[o];
         const float G = Gof(row, key), GL = Gof(L - 1, key);
         const float E = expf(G), F = expf(GL - G);
         const float kv = kS[row * 132 + key], qv = qS[row * 132 + key], bt = bS[row];
@@ -468,37 +496,29 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
             a.dq[e] = __builtin_fmaf(E, dQp, t2);
             a.dk[e] = __builtin_fmaf(E, dKp, __builtin_fmaf(F, dKd, __builtin_fmaf(bt, t1, t3)));
         }
-        gKd[o] = __builtin_fmaf(dKp, Kp, __builtin_fmaf(dQp, Qp, -dKd * Kd)) +
-                 __builtin_fmaf(bt * kv, t1, __builtin_fmaf(qv, t2, -kv * t3));
-        return dKd * Kd;  // this element's share of dG_{L-1} through F and its k t1 below
+        gKd[o] = __builtin_fmaf(dKp, Kp, dQp * Qp) + __builtin_fmaf(bt * kv, t1, __builtin_fmaf(qv, t2, -kv * t3));
+        // Kd = k F, F = e^{G_{L-1} - G}: its term reaches the gates of the tokens after this row
+        // only, summed below as a prefix (as the total at row L - 1 less a suffix it would
+        // cancel badly under steep decay, where the later rows dominate the total)
+        gsc[o] = dKd * Kd;
     };
-    // KDA: a chunk whose gates could overflow a factored decay (a positive gate and a cumulative
-    // range above 80) takes the per-key sums over every block
-    __shared__ int unsafe;
-    if (KDA) {
-        if (t == 0) unsafe = 0;
-        __syncthreads();
-        if (t < kChDk) {
-            float gmin = 0.0f, gmax = 0.0f, prev = 0.0f;
-            bool pos = false;
-            for (int r = 0; r < L; r++) {
-                const float G = Gs[r * 132 + t];
-                pos = pos || G > prev;
-                prev = G;
-                gmin = fminf(gmin, G);
-                gmax = fmaxf(gmax, G);
-            }
-            if (pos && gmax - gmin > 80.0f) atomicOr(&unsafe, 1);
-        }
-        __syncthreads();
-    }
-    const bool fact = !KDA || unsafe == 0;
+    // KDA: every decay factored on 16-token blocks (chunk_factorable), else per-key sums
+    __shared__ int flag;
+    const bool fact = !KDA || chunk_factorable(Gs, L, &flag);
     // tiles (rt, kt) of this wave: rows of block rt, keys 16 kt + c
-    float colsum[2] = {0.0f, 0.0f};
     float bc[4][4];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
+        // the products over columns for this tile's elements, loaded while the pair sums run
+        float pq[4], pk[4], pd[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int o = (16 * rt + 4 * g + r) * kChDk + key;
+            pq[r] = gsc[o];
+            pk[r] = gsc[kCh * kChDk + o];
+            pd[r] = gKd[o];
+        }
         f4 T1 = {0.0f, 0.0f, 0.0f, 0.0f}, T2 = T1, T3 = T1;
         if (!KDA) {
             // one decay per pair, folded into dA and dM above
@@ -513,56 +533,58 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
             }
         } else {
             if (fact) {
-                // blocks I < rt: e^{G_r - G_i} = e^{G_r - ref} e^{ref - G_i}, ref = G at the end
-                // of block I; the products over block I's tokens on the matrix cores
+                // blocks I <= rt: e^{G_r - G_i} = e^{G_r - ref} e^{ref - G_i}, ref = G at the end
+                // of block I (at the eighth token of block rt for I = rt, where dA and dM vanish
+                // on the pairs with i past r); the products over block I's tokens on the matrix
+                // cores
 #pragma unroll
-                for (int I = 0; I < rt; I++) {
-                    const float rf = Gs[(16 * I + 15) * 132 + key];
+                for (int I = 0; I <= rt; I++) {
+                    const float rf = Gs[(I < rt ? 16 * I + 15 : 16 * rt + 7) * 132 + key];
                     f4 P1 = {0.0f, 0.0f, 0.0f, 0.0f}, P2 = P1;
 #pragma unroll
                     for (int s = 0; s < 4; s++) {
                         const int tk = 16 * I + 4 * s + g;
-                        const float bl = kS[tk * 132 + key] * __expf(rf - Gs[tk * 132 + key]);
+                        const float bl = kS[tk * 132 + key] * expf(rf - Gs[tk * 132 + key]);
                         P1 = mfma4(dAs[(16 * rt + c) * kPW + tk], bl, P1);
                         P2 = mfma4(dMs[(16 * rt + c) * kPW + tk], bl, P2);
                     }
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        const float e = __expf(Gs[(16 * rt + 4 * g + r) * 132 + key] - rf);
+                        const float e = expf(Gs[(16 * rt + 4 * g + r) * 132 + key] - rf);
                         T1[r] = __builtin_fmaf(e, P1[r], T1[r]);
                         T2[r] = __builtin_fmaf(e, P2[r], T2[r]);
                     }
                 }
-                // blocks R > rt: e^{G_s - G_i} = e^{G_s - ref} e^{ref - G_i}, ref = G at the end of
-                // block rt; products over block R's tokens
+                // blocks R >= rt: e^{G_s - G_i} = e^{G_s - ref} e^{ref - G_i}, ref = G at the end of
+                // block rt (at its eighth token for R = rt); products over block R's tokens
 #pragma unroll
-                for (int R2 = rt + 1; R2 < 4; R2++) {
-                    const float rf = Gs[(16 * rt + 15) * 132 + key];
+                for (int R2 = rt; R2 < 4; R2++) {
+                    const float rf = Gs[(16 * rt + (R2 > rt ? 15 : 7)) * 132 + key];
                     f4 P3 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int s = 0; s < 4; s++) {
                         const int tk = 16 * R2 + 4 * s + g;
-                        const float er = __expf(Gs[tk * 132 + key] - rf);
+                        const float er = expf(Gs[tk * 132 + key] - rf);
                         P3 = mfma4(bS[tk] * dAs[tk * kPW + 16 * rt + c], kS[tk * 132 + key] * er, P3);
                         P3 = mfma4(dMs[tk * kPW + 16 * rt + c], qS[tk * 132 + key] * er, P3);
                     }
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        T3[r] = __builtin_fmaf(__expf(rf - Gs[(16 * rt + 4 * g + r) * 132 + key]), P3[r], T3[r]);
+                        T3[r] = __builtin_fmaf(expf(rf - Gs[(16 * rt + 4 * g + r) * 132 + key]), P3[r], T3[r]);
                 }
             }
-            // per-key sums: block rt itself (every block when the factors are not safe); dA is zero
-            // on and above the diagonal and dM above it, and each term's decay is between the
-            // earlier and the later token
-            const int i_lo = fact ? 16 * rt : 0, i_hi = fact ? 16 * rt + 16 : kCh;
+            // per-key sums over every token when the factors are not safe; dA is zero on and
+            // above the diagonal and dM above it, and each term's decay is between the earlier
+            // and the later token
+            const int i_hi = fact ? 0 : kCh;
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int row = 16 * rt + 4 * g + r;
                 const float Gr = Gs[row * 132 + key];
                 float t1 = 0.0f, t2 = 0.0f, t3 = 0.0f;
-                for (int i = i_lo; i < i_hi; i++) {
+                for (int i = 0; i < i_hi; i++) {
                     const float Gi = Gs[i * 132 + key], ki = kS[i * 132 + key];
-                    const float d = __expf(i <= row ? Gr - Gi : Gi - Gr);
+                    const float d = expf(i <= row ? Gr - Gi : Gi - Gr);
                     const float dl = i <= row ? d : 0.0f, du = i >= row ? d : 0.0f;  // no 0 * inf
                     t1 = __builtin_fmaf(dAs[row * kPW + i] * ki, dl, t1);
                     t2 = __builtin_fmaf(dMs[row * kPW + i] * ki, dl, t2);
@@ -576,17 +598,10 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int row = 16 * rt + 4 * g + r;
-            colsum[j >> 2] += finish(row, key, T1[r], T2[r], T3[r]);
+            finish(row, key, T1[r], T2[r], T3[r], pq[r], pk[r], pd[r]);
             bc[rt][r] = (j < 4 ? 0.0f : bc[rt][r]) + kS[row * 132 + key] * T1[r];
         }
         sched_fence();
-    }
-    // colsum: over this lane group's rows, then the four groups; key 16 kt + c
-    colsum[0] = rows_sum(colsum[0]);
-    colsum[1] = rows_sum(colsum[1]);
-    if (g == 0) {
-        elS2[16 * w + c] = colsum[0];
-        elS2[16 * (w + 4) + c] = colsum[1];
     }
 #pragma unroll
     for (int rt = 0; rt < 4; rt++)
@@ -596,37 +611,54 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
             if (c == 0) bpart[w][16 * rt + 4 * g + r] = v;
         }
 
-    // ---- gate and beta gradients: dG from gsc into LDS (the key array is no longer read)
+    // ---- gate and beta gradients: dG and the Kd terms from gsc into LDS (the key and query
+    // arrays are no longer read)
     float* dGs = big;
+    float* cS = big + kTK;
     __syncthreads();
+#pragma unroll
     for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
         const int r = idx >> 7, kk = idx & 127;
         float v = gKd[r * kChDk + kk];
-        // F_i = exp(G_{L-1} - G_i) and E_L = exp(G_{L-1}) feed dG_{L-1} as well
-        if (r == L - 1) v += elS2[kk] + elS[kk] * expf(Gof(L - 1, kk));
+        const float cv = gsc[r * kChDk + kk];
+        // E_L = exp(G_{L-1}) feeds dG_{L-1} as well
+        if (r == L - 1) v += elS[kk] * expf(Gof(L - 1, kk));
         dGs[r * 132 + kk] = r < L ? v : 0.0f;
+        cS[r * 132 + kk] = r < L ? cv : 0.0f;
     }
     __syncthreads();
     if (KDA) {
-        // dg_r = sum_{r' >= r} dG_r' per key (G is the running sum of g)
+        // dg_r = sum_{r' >= r} dG_r' + sum_{r' < r} dKd_r' Kd_r' per key (G is the running sum of g)
         if (t < kChDk) {
+            float pre = 0.0f;
+            for (int r = 0; r < L; r++) {
+                const float x = cS[r * 132 + t];
+                cS[r * 132 + t] = pre;
+                pre += x;
+            }
             float acc = 0.0f;
             for (int r = L - 1; r >= 0; r--) {
                 acc += dGs[r * 132 + t];
-                a.dg[(tok0 + static_cast<size_t>(r) * p.H) * kChDk + t] = acc;
+                a.dg[(tok0 + static_cast<size_t>(r) * p.H) * kChDk + t] = acc + cS[r * 132 + t];
             }
         }
     } else {
         if (t < kCh) {
-            float rs = 0.0f;
-            for (int kk = 0; kk < kChDk; kk++) rs += dGs[t * 132 + kk];
+            float rs = 0.0f, cs = 0.0f;
+            for (int kk = 0; kk < kChDk; kk++) {
+                rs += dGs[t * 132 + kk];
+                cs += cS[t * 132 + kk];
+            }
             elS[t] = rs;
+            const float inc = wave_prefix_sum(cs);
+            const float exc = __shfl_up(inc, 1, 64);
+            gS[t] = t > 0 ? exc : 0.0f;  // the cumulative gates are no longer read
         }
         __syncthreads();
         if (t < L) {
             float acc = 0.0f;
             for (int r = L - 1; r >= t; r--) acc += elS[r];
-            a.dg[tok0 + static_cast<size_t>(t) * p.H] = acc;
+            a.dg[tok0 + static_cast<size_t>(t) * p.H] = acc + gS[t];
         }
     }
     if (t < L) {
@@ -663,13 +695,15 @@ hipError_t launch_chunk_bwd(const la_config& c, const FwdArgs& fa, const BwdArgs
     const float* ck = ba.ckpts;
     hipError_t e;
     if (!ck) {
-        // checkpoints from the chunk forward (its records in the backward records' room)
+        // checkpoints from the forward kernel that serves c: the chunk forward (its records in
+        // the backward records' room), or the kernel the caller's forward ran, whose rounding
+        // decisions the checkpoints must repeat
         float* room = reinterpret_cast<float*>(ws + L.ckpts);
         FwdArgs f = fa;
         f.o = nullptr;
         f.ST = nullptr;
         f.ckpts = room;
-        e = launch_chunk_fwd(c, f, rec, s);
+        e = fwd_kernel(c) == LA_KERNEL_CHUNK ? launch_chunk_fwd(c, f, rec, s) : launch_fwd(c, f, s);
         if (e != hipSuccess) return e;
         ck = room;
     }

@@ -51,34 +51,32 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
     const size_t tok0 = (static_cast<size_t>(b) * T + t0) * H + h;
     float* R = rec + ((static_cast<size_t>(b) * H + h) * p.nch + cc) * (BWD ? RecB::SIZE : RecF::SIZE);
 
-    load_rows_lds(kS, in.k, tok0, H, L, p.qkv_dt);
-    load_rows_lds(qS, in.q, tok0, H, L, p.qkv_dt);
-    if (KDA) load_rows_lds(GS, in.g, tok0, H, L, p.gate_dt);
-    if (t < kCh) {
-        const bool ok = t < L;
-        bS[t] = ok ? load_elem(in.beta, tok0 + static_cast<size_t>(t) * H, p.gate_dt) : 0.0f;
-        if (!KDA) gS[t] = ok ? load_elem(in.g, tok0 + static_cast<size_t>(t) * H, p.gate_dt) : 0.0f;
+    {
+        // every load of the chunk's inputs in flight before any is used
+        Rows rk, rq, rg;
+        rows_load(rk, in.k, tok0, H, L, p.qkv_dt);
+        rows_load(rq, in.q, tok0, H, L, p.qkv_dt);
+        if (KDA) rows_load(rg, in.g, tok0, H, L, p.gate_dt);
+        uint32_t br[1], gr[1];
+        const size_t te = tok0 + static_cast<size_t>(t < L ? t & 63 : 0) * H;
+        load_raw<1>(br, in.beta, p.gate_dt, [&](int) { return te; });
+        if (!KDA) load_raw<1>(gr, in.g, p.gate_dt, [&](int) { return te; });
+        rows_store(kS, rk, L, p.qkv_dt);
+        rows_store(qS, rq, L, p.qkv_dt);
+        if (KDA) rows_store(GS, rg, L, p.gate_dt);
+        if (t < kCh) {
+            bS[t] = t < L ? raw_f32(br[0], p.gate_dt) : 0.0f;
+            if (!KDA) gS[t] = t < L ? raw_f32(gr[0], p.gate_dt) : 0.0f;
+        }
     }
     if (KDA) {
         // cumulative log decays per key (rows past the end repeat G_{L-1}): one thread per key
         // sums down its column of the gates loaded above
         __syncthreads();
-        if (t < kChDk) {
-            float run = 0.0f;
-            for (int r = 0; r < kCh; r++) {
-                run += GS[r * kPT + t];
-                GS[r * kPT + t] = run;
-            }
-        }
+        if (t < kChDk) cumsum_cols(GS, t);
     } else {
-        __syncthreads();
-        if (t == 0) {
-            float run = 0.0f;
-            for (int r = 0; r < kCh; r++) {
-                if (r < L) run += gS[r];
-                gS[r] = run;
-            }
-        }
+        // zero past the end, so those rows repeat G_{L-1}
+        if (t < kCh) gS[t] = cumsum_lanes(gS[t]);
     }
     __syncthreads();
     auto Gof = [&](int r, int kk) __attribute__((always_inline)) { return KDA ? GS[r * kPT + kk] : gS[r]; };
@@ -106,86 +104,72 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
         }
     }
     if (t < kChDk) R[(BWD ? RecB::EL : RecF::EL) + t] = expf(Gof(L - 1, t));
+    if (t < kCh) R[(BWD ? RecB::BT : RecF::BT) + t] = bS[t];
 
     // A (strictly lower) and M (lower with the diagonal)
     if (KDA) {
-        // Off-diagonal 16 x 16 tiles (rt > ct) on the matrix cores: with ref the cumulative
-        // gate of the last token of block ct, e^{G_r - G_i} = e^{G_r - ref} e^{ref - G_i}, and
-        // for gates <= 0 both factors are decays (<= 1), so neither overflows: A and M are
-        // (K o e^{G - ref}) (K o e^{ref - G})^T and (Q o e^{G - ref}) (K o e^{ref - G})^T.  A
-        // chunk whose gates could make a factor overflow (a positive gate and a cumulative
-        // range above 80) takes the per-key sums for every tile instead.  Diagonal tiles: the
-        // per-key sums, one thread per four (row, column) pairs.
+        // The ten lower 16 x 16 tiles (rt >= ct) on the matrix cores: with ref a cumulative gate
+        // (G at the end of block ct off the diagonal, at the eighth token of the block on it),
+        // e^{G_r - G_i} = e^{G_r - ref} e^{ref - G_i}, so A and M of the tile are
+        // (K o e^{G - ref}) (K o e^{ref - G})^T and (Q o e^{G - ref}) (K o e^{ref - G})^T.
+        // chunk_factorable checks that no factor overflows; a chunk that fails takes the per-key
+        // sums for every tile instead, one thread per four (row, column) pairs.
         const int lane = t & 63, w = t >> 6, g = lane >> 4, c = lane & 15;
-        __shared__ int unsafe;
-        if (t == 0) unsafe = 0;
-        for (int i = t; i < kCh * kPW; i += kChThreads) Am[i] = Mm[i] = 0.0f;
-        __syncthreads();
-        if (t < kChDk) {
-            float gmin = 0.0f, gmax = 0.0f, prev = 0.0f;
-            bool pos = false;
-            for (int r = 0; r < L; r++) {
-                const float G = GS[r * kPT + t];
-                pos = pos || G > prev;
-                prev = G;
-                gmin = fminf(gmin, G);
-                gmax = fmaxf(gmax, G);
-            }
-            if (pos && gmax - gmin > 80.0f) atomicOr(&unsafe, 1);
-        }
-        __syncthreads();
-        const bool fact = unsafe == 0;
+        __shared__ int flag;
+        const bool fact = chunk_factorable(GS, L, &flag);
         if (fact) {
-            constexpr int PR[6] = {1, 2, 2, 3, 3, 3}, PC[6] = {0, 0, 1, 0, 1, 2};
-            for (int pi = w; pi < 6; pi += 4) {
-                const int rt = PR[pi], ct = PC[pi], ref = 16 * ct + 15;
+            constexpr int PR[10] = {1, 2, 2, 3, 3, 3, 0, 1, 2, 3}, PC[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+            for (int pi = w; pi < 10; pi += 4) {
+                const int rt = PR[pi], ct = PC[pi], ref = rt == ct ? 16 * ct + 7 : 16 * ct + 15;
                 f4 aA = {0.0f, 0.0f, 0.0f, 0.0f}, aM = aA;
 #pragma unroll 4
                 for (int s2 = 0; s2 < 32; s2++) {
                     const int key = 4 * s2 + g;
                     const float rf = GS[ref * kPT + key];
                     const int ra = (16 * rt + c) * kPT + key, rb = (16 * ct + c) * kPT + key;
-                    const float er = __expf(GS[ra] - rf);
-                    const float bl = kS[rb] * __expf(rf - GS[rb]);
+                    const float er = expf(GS[ra] - rf);
+                    const float bl = kS[rb] * expf(rf - GS[rb]);
                     aA = mfma4(kS[ra] * er, bl, aA);
                     aM = mfma4(qS[ra] * er, bl, aM);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const int row = 16 * rt + 4 * g + r, col = 16 * ct + c;
-                    Am[row * kPW + col] = bS[row] * aA[r];
-                    Mm[row * kPW + col] = aM[r];
+                    Am[row * kPW + col] = col < row ? bS[row] * aA[r] : 0.0f;
+                    Mm[row * kPW + col] = col <= row ? aM[r] : 0.0f;
                 }
             }
-        }
-        // the per-key sums: the diagonal tiles (wave w: tile w), and every lower tile of an
-        // unsafe chunk; lane: row 4 (lane / 16) + rr of the tile, column lane % 16
-        for (int tl = w; tl < (fact ? 4 : 10); tl += 4) {
-            int rt, ct;
-            if (fact) {
-                rt = ct = tl;
-            } else {
-                rt = tl < 1 ? 0 : tl < 3 ? 1 : tl < 6 ? 2 : 3;
-                ct = tl - (rt * (rt + 1)) / 2;
+            // the tiles above the diagonal
+            for (int i = t; i < kCh * kCh; i += kChThreads) {
+                const int r = i >> 6, q = i & 63;
+                if ((q >> 4) > (r >> 4)) Am[r * kPW + q] = Mm[r * kPW + q] = 0.0f;
             }
-            const int col = 16 * ct + c;
-            float aa[4] = {0.0f, 0.0f, 0.0f, 0.0f}, mm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        } else {
+            for (int i = t; i < kCh * kPW; i += kChThreads) Am[i] = Mm[i] = 0.0f;
+            __syncthreads();
+            // lane: row 4 (lane / 16) + rr of the tile, column lane % 16
+            for (int tl = w; tl < 10; tl += 4) {
+                const int rt = tl < 1 ? 0 : tl < 3 ? 1 : tl < 6 ? 2 : 3;
+                const int ct = tl - (rt * (rt + 1)) / 2;
+                const int col = 16 * ct + c;
+                float aa[4] = {0.0f, 0.0f, 0.0f, 0.0f}, mm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 2
-            for (int kk = 0; kk < kChDk; kk++) {
-                const float kc = kS[col * kPT + kk], Gc = GS[col * kPT + kk];
+                for (int kk = 0; kk < kChDk; kk++) {
+                    const float kc = kS[col * kPT + kk], Gc = GS[col * kPT + kk];
+#pragma unroll
+                    for (int rr = 0; rr < 4; rr++) {
+                        const int row = 16 * rt + 4 * g + rr;
+                        const float kd = kc * expf(col <= row ? GS[row * kPT + kk] - Gc : 0.0f);
+                        aa[rr] = __builtin_fmaf(kS[row * kPT + kk], kd, aa[rr]);
+                        mm[rr] = __builtin_fmaf(qS[row * kPT + kk], kd, mm[rr]);
+                    }
+                }
 #pragma unroll
                 for (int rr = 0; rr < 4; rr++) {
                     const int row = 16 * rt + 4 * g + rr;
-                    const float kd = kc * __expf(col <= row ? GS[row * kPT + kk] - Gc : 0.0f);
-                    aa[rr] = __builtin_fmaf(kS[row * kPT + kk], kd, aa[rr]);
-                    mm[rr] = __builtin_fmaf(qS[row * kPT + kk], kd, mm[rr]);
+                    Am[row * kPW + col] = col < row ? bS[row] * aa[rr] : 0.0f;
+                    Mm[row * kPW + col] = col <= row ? mm[rr] : 0.0f;
                 }
-            }
-#pragma unroll
-            for (int rr = 0; rr < 4; rr++) {
-                const int row = 16 * rt + 4 * g + rr;
-                Am[row * kPW + col] = col < row ? bS[row] * aa[rr] : 0.0f;
-                Mm[row * kPW + col] = col <= row ? mm[rr] : 0.0f;
             }
         }
     } else {
@@ -296,7 +280,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
     __shared__ __align__(16) float RB[RecF::SIZE - RecF::PART2];  // P, M, Kd^T, E_L
     __shared__ WaveQdqShared<kChDk, QMODE, G> qsh;
     constexpr int bP = RecF::P - RecF::PART2, bM = RecF::M - RecF::PART2, bKDT = RecF::KDT - RecF::PART2,
-                  bEL = RecF::EL - RecF::PART2;
+                  bEL = RecF::EL - RecF::PART2, bBT = RecF::BT - RecF::PART2;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g0 = lane >> 4, c0 = lane & 15;
     int tile, bh;
     chunk_tile_of(blockIdx.x, p.ntile, tile, bh);
@@ -319,20 +303,20 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
             for (int m = 0; m < 32; m++) dst[static_cast<size_t>(kmap(m, g)) * dv] = s[m];
         }
         // part 1 of this chunk's record has arrived and every wave is done with part 2 of the
-        // previous one: load part 2 while the first products run
+        // previous one
         wait_all_mem();
         __syncthreads();
-        lds_dma(RB, recu + static_cast<size_t>(cc) * RecF::SIZE + RecF::PART2, RecF::SIZE - RecF::PART2);
+        // v of this lane's tokens (a row past the end reads row 0 and is zeroed where it is
+        // used), issued while nothing else is in flight: the dtype switch then costs no wait
         const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
-        float vv[16], bb[16];
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
+        uint32_t vr[16];
+        const size_t vrow = static_cast<size_t>(p.H) * dv;
+        load_raw<16>(vr, in.v, p.qkv_dt, [&](int i) {
             const int tk = kmap(i, g);
-            const bool ok = tk < L;
-            const size_t e = tok0 + static_cast<size_t>(tk) * p.H;
-            vv[i] = ok ? load_elem(in.v, e * dv + col, p.qkv_dt) : 0.0f;
-            bb[i] = ok ? load_elem(in.beta, e, p.gate_dt) : 0.0f;
-        }
+            return (tok0 * dv + col) + static_cast<size_t>(tk < L ? tk : 0) * vrow;
+        });
+        // part 2 while the first products run
+        lds_dma(RB, recu + static_cast<size_t>(cc) * RecF::SIZE + RecF::PART2, RecF::SIZE - RecF::PART2);
 
         // X = Kp S, Y = Qp S
         f4 X[4], Y[4];
@@ -356,7 +340,11 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
         // beta (V - X), then Delta = P (beta (V - X))
         float rv[16];
 #pragma unroll
-        for (int i = 0; i < 16; i++) rv[i] = bb[i] * (vv[i] - X[i >> 2][i & 3]);
+        for (int i = 0; i < 16; i++) {
+            const int tk = kmap(i, g);
+            const float vt = tk < L ? raw_f32(vr[i], p.qkv_dt) : 0.0f;
+            rv[i] = RB[bBT + tk] * (vt - X[i >> 2][i & 3]);
+        }
         f4 D[4];
 #pragma unroll
         for (int rt = 0; rt < 4; rt++) D[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};

@@ -39,6 +39,13 @@ la_kernel fwd_kernel(const la_config& c) {
     return LA_KERNEL_TOKEN;
 }
 
+la_kernel bwd_kernel(const la_config& c) {
+    if (fwd_kernel(c) == LA_KERNEL_CHUNK) return LA_KERNEL_CHUNK;
+    if (bwd_mfma_eligible(c)) return LA_KERNEL_BLOCK;
+    if (c.kernel != LA_KERNEL_TOKEN && c.ckpt_interval == kChunkTokens && chunk_eligible(c)) return LA_KERNEL_CHUNK;
+    return LA_KERNEL_TOKEN;
+}
+
 const char* fwd_kernel_name(const la_config& c) {
     switch (fwd_kernel(c)) {
         case LA_KERNEL_BLOCK: return "block";

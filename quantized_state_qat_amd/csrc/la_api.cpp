@@ -186,8 +186,11 @@ const char* la_fwd_kernel_name(const la_config* cfg) {
 
 const char* la_bwd_kernel_name(const la_config* cfg) {
     if (check_config(cfg, false) != LA_OK || check_kernel(*cfg) != LA_OK) return "";
-    if (la::fwd_kernel(*cfg) == LA_KERNEL_CHUNK) return "chunk";
-    return la::bwd_mfma_eligible(*cfg) ? "block" : "token";
+    switch (la::bwd_kernel(*cfg)) {
+        case LA_KERNEL_CHUNK: return "chunk";
+        case LA_KERNEL_BLOCK: return "block";
+        default: return "token";
+    }
 }
 
 la_status la_recurrent_fwd(const la_config* cfg, const void* q, const void* k, const void* v,
@@ -489,7 +492,7 @@ la_status la_recurrent_bwd_ste_split(const la_config* prefix_cfg, const la_confi
 
 size_t la_bwd_workspace_bytes(const la_config* cfg) {
     if (check_config(cfg, false) != LA_OK || check_kernel(*cfg) != LA_OK || cfg->ckpt_interval < 1) return 0;
-    if (la::fwd_kernel(*cfg) == LA_KERNEL_CHUNK)
+    if (la::bwd_kernel(*cfg) == LA_KERNEL_CHUNK)
         return cfg->ckpt_interval == la::kChunkTokens ? la::chunk_bwd_layout(*cfg).total : 0;
     return ws_layout(*cfg).total;
 }
@@ -514,7 +517,7 @@ la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void
     CHECK(check_config(cfg, false));
     const la_config& c = *cfg;
     CHECK(check_kernel(c));
-    const bool chunk = la::fwd_kernel(c) == LA_KERNEL_CHUNK;
+    const bool chunk = la::bwd_kernel(c) == LA_KERNEL_CHUNK;
     if (chunk && c.ckpt_interval != la::kChunkTokens)
         return fail(LA_ERR_UNSUPPORTED, "the chunk form's backward takes a checkpoint per chunk (ckpt_interval = 64)");
     if (c.ckpt_interval < 1) return fail(LA_ERR_INVALID_ARG, "backward needs ckpt_interval >= 1");
@@ -558,7 +561,7 @@ la_status bwd_ste(const la_config* cfg, const void* q, const void* k, const void
         la::BwdArgs a{q, k, v, g, beta, ckpts, dout, dS_T, dq, dk, dv, dg, dbeta, dS0, nullptr, nullptr};
         return hip_status(la::launch_chunk_bwd(c, fa, a, ws, s), "la_recurrent_bwd_ste chunk launch");
     }
-    if (la::bwd_mfma_eligible(c)) {
+    if (la::bwd_kernel(c) == LA_KERNEL_BLOCK) {
         float* states = reinterpret_cast<float*>(ws + L.states);
         la::FwdArgs fa{q, k, v, g, beta, S0, nullptr, nullptr, nullptr};
         la::BwdArgs a{q, k, v, g, beta, ckpts, dout, dS_T, dq, dk, dv, dg, dbeta, dS0,

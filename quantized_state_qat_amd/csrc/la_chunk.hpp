@@ -53,23 +53,26 @@ struct ChunkIn {
 // record is two parts in the order the pass consumes them (part 1 is free once its first
 // products are done, part 2 at the chunk's end), so that the next chunk's parts can be loaded
 // into LDS while the current one is still being used.
-// Forward: part 1 Kp, Qp [token][132]; part 2 P, M [64][68], Kd transposed [key][68], E_L [128].
+// Forward: part 1 Kp, Qp [token][132]; part 2 P, M [64][68], Kd transposed [key][68], E_L [128],
+// beta [64] (widened to fp32; zero past the sequence's end).
 struct RecF {
     static constexpr int PP = 68, PK = 132, PD = 68;
     static constexpr int KP = 0, QP = KP + kCh * PK, PART2 = QP + kCh * PK;
-    static constexpr int P = PART2, M = P + kCh * PP, KDT = M + kCh * PP, EL = KDT + kChDk * PD, SIZE = EL + kChDk;
+    static constexpr int P = PART2, M = P + kCh * PP, KDT = M + kCh * PP, EL = KDT + kChDk * PD, BT = EL + kChDk,
+                         SIZE = BT + kCh;
 };
 // Backward: the state gradient pass reads P and M transposed and Kp, Qp, Kd by token rows:
-// part 1 Kd [token][132], M [64][80]; part 2 P [64][80], Qp, Kp [token][144], E_L [128]; then
-// A [64][68] for the gradient kernel.
+// part 1 Kd [token][132], M [64][80]; part 2 P [64][80], Qp, Kp [token][144], E_L [128], beta
+// [64]; then A [64][68] for the gradient kernel.
 struct RecB {
     static constexpr int PP = 80, PK = 144, PKD = 132, PA = 68;
     static constexpr int KD = 0, M = KD + kCh * PKD, PART2 = M + kCh * PP;
-    static constexpr int P = PART2, QP = P + kCh * PP, KP = QP + kCh * PK, EL = KP + kCh * PK;
-    static constexpr int LDS_SIZE = EL + kChDk, A = LDS_SIZE, SIZE = A + kCh * PA;
+    static constexpr int P = PART2, QP = P + kCh * PP, KP = QP + kCh * PK, EL = KP + kCh * PK, BT = EL + kChDk;
+    static constexpr int LDS_SIZE = BT + kCh, A = LDS_SIZE, SIZE = A + kCh * PA;
 };
 static_assert(RecF::SIZE % 64 == 0 && RecB::SIZE % 64 == 0 && RecB::LDS_SIZE % 4 == 0, "record alignment");
-static_assert(RecF::PART2 % 4 == 0 && RecB::PART2 % 4 == 0, "record parts start on 16-byte boundaries");
+static_assert(RecF::PART2 % 4 == 0 && RecB::PART2 % 4 == 0 && RecB::BT % 4 == 0,
+              "record parts and the beta row start on 16-byte boundaries");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -89,41 +92,131 @@ __device__ __forceinline__ void lds_dma(float* dst, const float* __restrict__ sr
                                          16, 0, 0);
 }
 
-// Rows 0 .. L-1 of a [token][128] input (token r at element (tok0 + r H) 128), widened to fp32,
-// into LDS dst[r * 132 + k]; rows L .. 63 zero.  A thread takes 8 consecutive elements of each
-// of four rows (one 16-byte load for bf16, two for fp32), all loads in flight together.
-__device__ __forceinline__ void load_rows_lds(float* dst, const void* src, size_t tok0, int H, int L, int dtype) {
-    float v[4][8];
+// Rows 0 .. 63 of a [token][128] bf16 or fp32 input (token r at element (tok0 + r H) 128) in
+// 16-byte pieces: thread t holds pieces t + 256 u of the chunk (u < 4 for bf16, u < 8 for fp32;
+// piece pc is row pc / P, bytes 16 (pc % P) of it, P = 16 or 32 pieces per row).  rows_load
+// only issues loads (a row past the end reads row 0), so the pieces of several arrays can all
+// be in flight together; rows_store widens them into LDS dst[r * 132 + k], rows L .. 63 zero.
+struct Rows {
+    uint4 x[8];
+};
+__device__ __forceinline__ void rows_load(Rows& R, const void* src, size_t tok0, int H, int L, int dtype) {
+    const bool f32 = dtype == LA_F32;
+    const int sh = f32 ? 5 : 4, nu = f32 ? 8 : 4;
+    const size_t esz = f32 ? 4 : 2;
+    const char* base = static_cast<const char*>(src) + tok0 * kChDk * esz;
+    const size_t rstride = static_cast<size_t>(H) * kChDk * esz;
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-        const int gi = threadIdx.x + kChThreads * u, r = gi >> 4, k8 = (gi & 15) * 8;
-        const size_t e = (tok0 + static_cast<size_t>(r) * H) * kChDk + k8;
-        if (r >= L) {
-#pragma unroll
-            for (int i = 0; i < 8; i++) v[u][i] = 0.0f;
-        } else if (dtype == LA_BF16) {
-            const uint4 wv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + e);
-            const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                v[u][2 * i] = __uint_as_float(ws[i] << 16);
-                v[u][2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
-            }
-        } else {
-            const float4 a0 = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + e);
-            const float4 a1 = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + e + 4);
-            v[u][0] = a0.x; v[u][1] = a0.y; v[u][2] = a0.z; v[u][3] = a0.w;
-            v[u][4] = a1.x; v[u][5] = a1.y; v[u][6] = a1.z; v[u][7] = a1.w;
+    for (int u = 0; u < 8; u++) {
+        if (u < nu) {
+            const int pc = threadIdx.x + kChThreads * u, r = pc >> sh, o = pc & ((1 << sh) - 1);
+            R.x[u] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(r < L ? r : 0) * rstride + 16 * o);
         }
     }
+}
+__device__ __forceinline__ void rows_store(float* dst, const Rows& R, int L, int dtype) {
+    if (dtype == LA_F32) {
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-        const int gi = threadIdx.x + kChThreads * u, r = gi >> 4, k8 = (gi & 15) * 8;
-        float4* d = reinterpret_cast<float4*>(dst + r * 132 + k8);
-        d[0] = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
-        d[1] = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+        for (int u = 0; u < 8; u++) {
+            const int pc = threadIdx.x + kChThreads * u, r = pc >> 5, o = pc & 31;
+            const uint32_t m = r < L ? 0xFFFFFFFFu : 0u;
+            const uint4 x = R.x[u];
+            *reinterpret_cast<float4*>(dst + r * 132 + 4 * o) = make_float4(
+                __uint_as_float(x.x & m), __uint_as_float(x.y & m), __uint_as_float(x.z & m), __uint_as_float(x.w & m));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int pc = threadIdx.x + kChThreads * u, r = pc >> 4, o = pc & 15;
+            const uint32_t m = r < L ? 0xFFFFFFFFu : 0u;
+            const uint32_t w[4] = {R.x[u].x & m, R.x[u].y & m, R.x[u].z & m, R.x[u].w & m};
+            float4* d = reinterpret_cast<float4*>(dst + r * 132 + 8 * o);
+            d[0] = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                               __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u));
+            d[1] = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
+                               __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u));
+        }
     }
 }
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane l holds x), in six shift-and-add steps.
+template <typename F>
+__device__ __forceinline__ F wave_prefix_sum(F x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const F y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Cumulative log decays of a chunk, in float: per key G[r * 132 + key] in place (rows past the
+// end hold zero gates), one thread per key; for a scalar gate the 64 lanes of one wave, lane r
+// holding row r's gate.  Late in a chunk under steep decay these are large numbers whose
+// differences keep an absolute error of about |G| 2^-24 per step (rounding once from a double
+// sum does not help: the two rounded ends of a difference then err independently).
+__device__ __forceinline__ void cumsum_cols(float* G, int key) {
+    float run = 0.0f;
+    for (int r = 0; r < kCh; r++) {
+        run += G[r * 132 + key];
+        G[r * 132 + key] = run;
+    }
+}
+__device__ __forceinline__ float cumsum_lanes(float g) { return wave_prefix_sum(g); }
+
+// Whether a chunk's per-key cumulative log decays G (LDS, [token][132], rows past the end
+// repeating row L - 1) allow every decay e^{G_r - G_i} to be factored as e^{G_r - ref}
+// e^{ref - G_i} with no factor overflowing or underflowing: off-diagonal 16-token blocks take
+// ref = G at the end of the earlier block, so both factors are decays unless a gate is positive
+// (then the chunk's range must stay within 80); a diagonal block takes ref = G at its eighth
+// token, so every G of the block must lie within 80 of it.  Every thread of the workgroup
+// calls it (it synchronises); one thread per key does the scan.
+__device__ __forceinline__ bool chunk_factorable(const float* G, int L, int* flag) {
+    if (threadIdx.x == 0) *flag = 0;
+    __syncthreads();
+    if (threadIdx.x < kChDk) {
+        const int key = threadIdx.x;
+        float gmin = 0.0f, gmax = 0.0f, prev = 0.0f, spread = 0.0f;
+        bool pos = false;
+        for (int r = 0; r < L; r++) {
+            const float x = G[r * 132 + key];
+            pos = pos || x > prev;
+            prev = x;
+            gmin = fminf(gmin, x);
+            gmax = fmaxf(gmax, x);
+            spread = fmaxf(spread, fabsf(x - G[((r & ~15) + 7) * 132 + key]));
+        }
+        if ((pos && gmax - gmin > 80.0f) || !(spread <= 80.0f)) atomicOr(flag, 1);
+    }
+    __syncthreads();
+    return *flag == 0;
+}
+
+// x, or zero when !ok, component by component (a select between whole vectors can leave
+// them in private memory).
+__device__ __forceinline__ float4 keep_if(bool ok, float4 x) {
+    return make_float4(ok ? x.x : 0.0f, ok ? x.y : 0.0f, ok ? x.z : 0.0f, ok ? x.w : 0.0f);
+}
+
+// N elements idx(0) .. idx(N-1) of a bf16 or fp32 array as raw bits (bf16 zero-extended),
+// the dtype switch outside the loads.  Nothing here reads a loaded value, so all N loads are
+// in flight together; a conversion or a select on each value right after its load would make
+// every load wait for those before it (and for any other memory operation still in flight).
+// raw_f32 turns the bits into the float where the value is used.
+template <int N, typename Idx>
+__device__ __forceinline__ void load_raw(uint32_t (&r)[N], const void* p, int dtype, Idx idx) {
+    if (dtype == LA_F32) {
+        const uint32_t* s = static_cast<const uint32_t*>(p);
+#pragma unroll
+        for (int i = 0; i < N; i++) r[i] = s[idx(i)];
+    } else {
+        const uint16_t* s = static_cast<const uint16_t*>(p);
+#pragma unroll
+        for (int i = 0; i < N; i++) r[i] = s[idx(i)];
+    }
+}
+__device__ __forceinline__ float raw_f32(uint32_t r, int dtype) { return __uint_as_float(dtype == LA_F32 ? r : r << 16); }
 
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }

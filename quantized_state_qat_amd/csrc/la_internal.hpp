@@ -148,6 +148,12 @@ hipError_t launch_fwd_mfma_chunks(const la_config& c, const FwdArgs& a, int t_of
 // + bwd_mfma_part_bytes (one segment each) + carry + checkpoint room.
 bool bwd_mfma_eligible(const la_config& c);
 int bwd_mfma_segment(const la_config& c);
+// The backward kernel that serves c: the chunk form when the forward runs it; else the block
+// backward when eligible; else, unless c.kernel asks for the token kernel, the chunk backward
+// when every rounding point and checkpoint is a chunk end (ckpt_interval = 64: the checkpoints
+// then carry every rounding decision, and a missing set is recomputed by c's own forward
+// kernel); else the token backward.
+la_kernel bwd_kernel(const la_config& c);
 size_t bwd_mfma_state_bytes(const la_config& c);
 size_t bwd_mfma_part_bytes(const la_config& c);
 hipError_t launch_bwd_mfma(const la_config& c, const FwdArgs& fa, const BwdArgs& a, float* carry, float* ck_room,

@@ -194,15 +194,23 @@ def test_fwd_kernel_selection(kw, name):
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=1, ckpt_interval=64), "token"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=24, ckpt_interval=24), "token"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=32, qdq_interval=64, ckpt_interval=64, hadamard=1), "token"),
-    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, gate=la.LA_GATE_KEY), "token"),
-    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, qkv_dtype=la.LA_F32), "token"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, gate=la.LA_GATE_KEY), "chunk"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, qkv_dtype=la.LA_F32), "chunk"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=32, gate=la.LA_GATE_KEY), "token"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=64, qdq_interval=1, ckpt_interval=64, gate=la.LA_GATE_KEY), "token"),
+    (dict(qdq=la.LA_QDQ_INT8_GROUP, group=64, qdq_interval=128, ckpt_interval=64, gate=la.LA_GATE_KEY), "chunk"),
+    (dict(ckpt_interval=64, gate=la.LA_GATE_KEY), "chunk"),
+    (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, gate=la.LA_GATE_KEY,
+          kernel=la.LA_KERNEL_TOKEN), "token"),
     (dict(qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64, ckpt_interval=64, d_k=64), "token"),
     (dict(qdq=la.LA_QDQ_INT8_GROUP, group=64, qdq_interval=48, ckpt_interval=16, d_v=64), "block"),
 ])
 def test_bwd_kernel_selection(kw, name):
     """Which backward serves a configuration: the block form needs the block forward's
     configurations (the user's checkpoint spacing aside: it recomputes every block's state)
-    and whole 64-column workgroups."""
+    and whole 64-column workgroups; the chunk form serves the rest whose rounding points and
+    checkpoints all fall on 64-token chunk ends (d_k = 128, no rotation), unless the token
+    kernel is asked for; the token backward serves everything else."""
     base = dict(B=2, T=100, H=2, d_k=128, d_v=128)
     base.update(kw)
     assert la.la_bwd_kernel_name(la.Config(**base)) == name
@@ -276,9 +284,12 @@ def test_forced_kernel(kernel, kw, name):
             fwd(c)
         assert ei.value.status == la.LA_ERR_UNSUPPORTED
         assert la.la_bwd_workspace_bytes(c) == 0
-    elif name != "block":
-        # the block backward needs the block forward's rounding decisions
+    elif name == "token":
         assert la.la_bwd_kernel_name(c) == "token"
+    elif name != "block":
+        # the block backward needs the block forward's rounding decisions; with every rounding
+        # point on a checkpoint the chunk backward needs none
+        assert la.la_bwd_kernel_name(c) == "chunk"
 
 
 def test_kernel_field_checks():
@@ -366,7 +377,10 @@ def test_chunk_kernel_selection_and_workspace():
     for solve, degree, kernel in ((la.LA_SOLVE_NEUMANN, 7, la.LA_KERNEL_AUTO), (la.LA_SOLVE_EXACT, 0, la.LA_KERNEL_CHUNK)):
         c = cfg(T=150, solve=solve, degree=degree, kernel=kernel, **CHUNK_OK)
         assert la.la_fwd_kernel_name(c) == "chunk"
-        assert la.la_chunk_workspace_bytes(c) == c.B * c.H * 3 * 34432 * 4
+        # one forward record per chunk: Kp, Qp [64][132]; P, M [64][68]; Kd^T [128][68]; E_L [128];
+        # beta [64] (fp32)
+        rec = 2 * 64 * 132 + 2 * 64 * 68 + 128 * 68 + 128 + 64
+        assert la.la_chunk_workspace_bytes(c) == c.B * c.H * 3 * rec * 4
         # the plain forward has no workspace argument: the chunk kernel is refused there
         with pytest.raises(la.LaError) as e:
             fwd(c)

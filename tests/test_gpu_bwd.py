@@ -8,10 +8,13 @@ adjoint evaluated on the quantized trajectory.  The oracle is therefore fed the 
 carried state entering every token (forward with per-token checkpoints): teacher forcing
 of the trajectory; everything after that is float64.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
 import oracle
+from oracle import chunk as oc
 import quantized_state_qat_amd as la
 import synth
 from tests import gpu_util as gu
@@ -64,7 +67,8 @@ CASES = [
     ("kda_wht_int8g64_i2_ckpt12", synth.Workload("kw2", B=2, T=41, H=1, d_k=128, d_v=64, gate="key", s0_sigma=0.2,
                                                  config_id=42),
      la.LA_QDQ_INT8_GROUP, 64, 1, 2, 12, True),
-    # checkpoints from the KDA block forward, recomputed by the token backward
+    # checkpoints from the KDA block forward, used (or recomputed by that forward) by the chunk
+    # backward: every rounding point is a checkpoint
     ("kda_e4m3_64_block_ckpts", synth.Workload("kb", B=1, T=150, H=2, d_k=128, d_v=128, gate="key", gate_dtype="f32",
                                                s0_sigma=0.1, config_id=40),
      la.LA_QDQ_E4M3_TILE, 64, 0, 64, 64, True),
@@ -105,6 +109,8 @@ def test_bwd_matches_oracle(name, w, mode, group, had, interval, ckpt, with_dst)
     c.ckpt_interval = ckpt
     if name == "gdn_int8g32_i16_ckpt32":
         assert la.la_fwd_kernel_name(c) == "token" and la.la_bwd_kernel_name(c) == "token"
+    if name == "kda_e4m3_64_block_ckpts":
+        assert la.la_fwd_kernel_name(c) == "block" and la.la_bwd_kernel_name(c) == "chunk"
     g1 = gu.run_bwd(c, d, d["do"].f32, S0=S0, dST=dST)            # recomputes checkpoints
     _, _, ck = gu.run_fwd(c, d, S0=S0, ckpt_interval=ckpt)
     c.ckpt_interval = ckpt
@@ -118,6 +124,38 @@ def test_bwd_matches_oracle(name, w, mode, group, had, interval, ckpt, with_dst)
     # to every case (the 2e-3 bound for bf16 inputs is implied)
     errs = _check_against_oracle(c, d, S0, d["do"].f32, dST, g1, gu.TOL_F32)
     print(name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+def test_bwd_kda_chunk_and_token_backward_agree():
+    """KDA with E4M3 every 64 tokens from the block forward's checkpoints: the chunk backward
+    (what the configuration runs) and the per-token backward (asked for by kernel = token) take
+    every state from those checkpoints (each rounding point is one), so both meet the chunked
+    oracle's exact-solve backward teacher forced with the same checkpoints at the FP32 bound,
+    and each other within twice it."""
+    w = synth.Workload("kt", B=2, T=200, H=2, d_k=128, d_v=128, gate="key", gate_dtype="f32", s0_sigma=0.1,
+                       config_id=58)
+    d = synth.generate(w, with_do=True, with_dST=True)
+    c = gu.cfg_for(w, d, qdq=la.LA_QDQ_E4M3_TILE, group=64, qdq_interval=64)
+    c.ckpt_interval = 64
+    ct = dataclasses.replace(c, kernel=la.LA_KERNEL_TOKEN)
+    assert la.la_bwd_kernel_name(c) == "chunk" and la.la_bwd_kernel_name(ct) == "token"
+    S0, dST = d["S0"].f32, d["dST"].f32
+    _, _, ck = gu.run_fwd(c, d, S0=S0, ckpt_interval=64)
+    c.ckpt_interval = 64
+    gc = gu.run_bwd(c, d, d["do"].f32, S0=S0, dST=dST, ckpts=ck)
+    gt = gu.run_bwd(ct, d, d["do"].f32, S0=S0, dST=dST, ckpts=ck)
+    ref = oc.bwd(d["q"].f64, d["k"].f64, d["v"].f64, d["g"].f64, d["beta"].f64, S0.astype(np.float64),
+                 d["do"].f64, dST.astype(np.float64),
+                 gate=c.gate, qdq_mode=c.qdq, group=c.group, qdq_interval=c.qdq_interval,
+                 chunk_states=ck.astype(np.float64))
+    errs = {}
+    for name in GRADS:
+        for tag, g in (("chunk", gc), ("token", gt)):
+            assert np.all(np.isfinite(g[name])), (tag, name)
+            errs[f"{tag}_{name}"] = gu.err(g[name], ref[name])
+        assert gu.err(gc[name], gt[name].astype(np.float64)) <= 2 * gu.TOL_F32, name
+    assert max(errs.values()) <= gu.TOL_F32, errs
+    print({k: f"{v:.2e}" for k, v in errs.items()})
 
 
 def test_bwd_full_size_sampled_units():

@@ -294,6 +294,45 @@ def test_chunk_backward_long_sequence_sampled(gate, degree):
         assert np.all(np.isfinite(r[n])), n
 
 
+@pytest.mark.parametrize("case", ["steep"])
+def test_chunk_kda_steep_gates(case):
+    """Gates that stretch the factored decays.  steep: every gate about -4.5, so a 16-token
+    block spans about 72 of log decay and the diagonal blocks' factors reach about e^36 on
+    either side of the block's eighth token; the kernels keep the factored products.  spike:
+    the workloads' gates with one gate of -90 at the fourth token of every chunk, 90 away from
+    that block's reference: a factor could overflow and the kernels take the per-key sums for
+    every block.  Forward and backward against the chunked oracle at the fp32 bar.  (Steeper
+    uniform decay runs into the float cumulative log decays, whose differences late in a chunk
+    keep an absolute error of about |G| 2^-24 per step: at about -6 per token the gate gradient,
+    a suffix sum of largely cancelling terms, reaches 4e-5 of its largest magnitude.)"""
+    T, B, H = 150, 1, 2
+    w = synth.Workload("chunk_steep", B=B, T=T, H=H, d_k=128, d_v=128, gate="key", gate_dtype="f32", config_id=472)
+    d = synth.generate(w, with_do=True)
+    rng = np.random.default_rng(473)
+    if case == "steep":
+        g = -4.5 + 0.2 * rng.standard_normal((B, T, H, 128))
+    else:
+        g = d["g"].f64.copy()
+        g[:, 3::64] = -90.0
+    d["g"] = synth.cast(g, "f32")
+    S0 = (rng.standard_normal((B, H, 128, 128)) * 0.3).astype(np.float32)
+    c = chunk_cfg(w, d, la.LA_SOLVE_EXACT, 0, qdq=E4M3, group=64, qdq_interval=64)
+    c.gate_dtype = la.LA_F32
+    o, ST, ck = run_chunk(c, d, S0, ckpt_interval=64)
+    tally = gu.CodeTally()
+    wo, ws = teacher_forced_chunks(c, d, ck, ST, o, tally)
+    assert wo <= gu.TOL_F32 and ws <= gu.TOL_F32, (wo, ws)
+    tally.check()
+    do = d["do"].f32
+    r = run_chunk_bwd(c, d, S0, ck, do, None)
+    ref = oracle_bwd_units(c, d, S0, ck, do.astype(np.float64), None, [(0, 0), (0, 1)])
+    for (b, h), rr in ref.items():
+        for n in GRADS:
+            assert np.all(np.isfinite(r[n][b, :, h])), n
+            assert gu.err(r[n][b, :, h], rr[n][0, :, 0]) <= gu.TOL_F32, n
+        assert gu.err(r["dS0"][b, h], rr["dS0"][0, 0]) <= gu.TOL_F32
+
+
 @pytest.mark.parametrize("first_gate", [-20.0, -85.0], ids=["factored", "per_key_fallback"])
 def test_chunk_kda_positive_gates(first_gate):
     """Gates above zero make the factored decays exceed one: with a cumulative range under 80 per
