@@ -24,6 +24,8 @@ constexpr int kSP = 20;             // pitch of the gradient kernel's 16-column 
 constexpr int kTK = kCh * 132;      // one token-by-key array (pitch 132)
 constexpr int kWM = kCh * kPW;      // one 64 x 64 work matrix
 constexpr int kBig = 6 * kWM;       // the gradient kernel's phase-shared LDS (floats)
+constexpr int kGW = 8;              // the gradient kernel's waves (two per SIMD: its phases wait on
+constexpr int kGT = 64 * kGW;       // memory and LDS, and the second wave fills those gaps)
 static_assert(5 * kCh * kSP + 2 * kChDk * kSP <= 3 * kWM, "slabs overlap the dP buffer");
 static_assert(3 * kTK <= kBig && 2 * kTK + kWM <= kBig, "phase buffers exceed the shared array");
 
@@ -62,17 +64,26 @@ __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams
     const float* R = a.rec + ch * RecB::SIZE;
     const int t0 = cc * kCh, L = min(kCh, p.T - t0);
     const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
-    // v first, while nothing else is in flight (a row past the end reads row 0, zeroed below)
+    // v first, while nothing else is in flight (rows past the end are zeroed below)
+    const size_t ntok = static_cast<size_t>(p.B) * p.T * p.H;
     uint32_t vr[16];
-    const size_t vrow = static_cast<size_t>(p.H) * dv;
-    load_raw<16>(vr, in.v, p.qkv_dt, [&](int i) {
-        const int tk = kmap(i, g);
-        return (tok0 * dv + col) + static_cast<size_t>(tk < L ? tk : 0) * vrow;
-    });
-    const float* S = a.ckpts + ch * kChDk * dv + col;
+    {
+        const int ve = p.qkv_dt == LA_F32 ? 4 : 2;
+        const ChunkRows rv = chunk_rows(static_cast<const char*>(in.v) + tok0 * dv * ve, (ntok - tok0) * dv * ve,
+                                        p.H * dv, g, col, ve);
+        if (ve == 4) {
+#pragma unroll
+            for (int i = 0; i < 16; i++) vr[i] = rv.ld32(i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) vr[i] = rv.ld16(i);
+        }
+    }
+    const size_t slab = static_cast<size_t>(kChDk) * dv * 4, rows = static_cast<size_t>(kCh) * dv * 4;
+    const ChunkRows rs = chunk_rows(a.ckpts + ch * kChDk * dv, slab, dv, g, col, 4);
     float s[32];
 #pragma unroll
-    for (int m = 0; m < 32; m++) s[m] = S[static_cast<size_t>(kmap(m, g)) * dv];
+    for (int m = 0; m < 32; m++) s[m] = rs.ldf(m);
     lds_dma(Kp_s, R + RecB::KP, kCh * RecB::PK);
     lds_dma(P_s, R + RecB::P, kCh * RecB::PP);
     lds_dma(b_s, R + RecB::BT, kCh);
@@ -111,13 +122,12 @@ __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams
         for (int rt = 0; rt < 4; rt++) D[rt] = mfma4(P_s[cmap(rt, c) * RecB::PP + tk], rv[m], D[rt]);
         if ((m & 3) == 3) sched_fence();
     }
-    float* Ub = a.U + ch * kCh * dv + col;
-    float* Db = a.D + ch * kCh * dv + col;
+    const ChunkRows ru = chunk_rows(a.U + ch * kCh * dv, rows, dv, g, col, 4);
+    const ChunkRows rd = chunk_rows(a.D + ch * kCh * dv, rows, dv, g, col, 4);
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        const size_t o = static_cast<size_t>(kmap(i, g)) * dv;
-        Ub[o] = u[i];
-        Db[o] = D[i >> 2][i & 3];
+        ru.stf(i, u[i]);
+        rd.stf(i, D[i >> 2][i & 3]);
     }
 }
 
@@ -146,20 +156,24 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
         const int t0 = cc * kCh, L = min(kCh, p.T - t0);
         const size_t ch = static_cast<size_t>(bh) * p.nch + cc;
         const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
-        float* dse = a.dSe + ch * kChDk * dv + col;
+        const ChunkRows rse = chunk_rows(a.dSe + ch * kChDk * dv, static_cast<size_t>(kChDk) * dv * 4, dv, g, col, 4);
 #pragma unroll
-        for (int m = 0; m < 32; m++) dse[static_cast<size_t>(kmap(m, g)) * dv] = ds[m];
+        for (int m = 0; m < 32; m++) rse.stf(m, ds[m]);
         // part 1 of this chunk's record is here, part 2 of the later chunk free: load part 2
         wait_all_mem();
         __syncthreads();
         lds_dma(RB, recu + static_cast<size_t>(cc) * RecB::SIZE + RecB::PART2, RecB::LDS_SIZE - RecB::PART2);
-        // upstream gradient (a row past the end reads row 0, zeroed where used) and U
+        // upstream gradient (rows past the end are zeroed where used) and U
+        const size_t ntok = static_cast<size_t>(p.B) * p.T * p.H;
+        const ChunkRows rdo = chunk_rows(a.dout + tok0 * dv, (ntok - tok0) * dv * 4, p.H * dv, g, col, 4);
+        const ChunkRows rdv = chunk_rows(a.dv + tok0 * dv, (ntok - tok0) * dv * 4, p.H * dv, g, col, 4);
+        const ChunkRows ru = chunk_rows(a.U + ch * kCh * dv, static_cast<size_t>(kCh) * dv * 4, dv, g, col, 4);
+        const ChunkRows rdd = chunk_rows(a.dD + ch * kCh * dv, static_cast<size_t>(kCh) * dv * 4, dv, g, col, 4);
         float dOr[16], uu[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-            const int tk = kmap(i, g);
-            dOr[i] = a.dout[(tok0 + static_cast<size_t>(tk < L ? tk : 0) * p.H) * dv + col];
-            uu[i] = a.U[(ch * kCh + tk) * dv + col];
+            dOr[i] = rdo.ldf(i);
+            uu[i] = ru.ldf(i);
         }
         // dDelta = Kd dS_end + M^T dO
         f4 DD[4];
@@ -198,14 +212,13 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
             for (int rt = 0; rt < 4; rt++) dR[rt] = mfma4(RB[bP + tk * RecB::PP + cmap(rt, c)], dm, dR[rt]);
             if ((m & 3) == 3) sched_fence();
         }
-        float* dDb = a.dD + ch * kCh * dv + col;
         float du[16];
 #pragma unroll
         for (int i = 0; i < 16; i++) {
             const int tk = kmap(i, g);
-            dDb[static_cast<size_t>(tk) * dv] = DD[i >> 2][i & 3];
+            rdd.stf(i, DD[i >> 2][i & 3]);
             du[i] = RB[bBT + tk] * dR[i >> 2][i & 3];
-            if (tk < L) a.dv[(tok0 + static_cast<size_t>(tk) * p.H) * dv + col] = du[i];
+            if (tk < L) rdv.stf(i, du[i]);
         }
         // beta gradient of R = beta U, summed over this tile's columns
 #pragma unroll
@@ -245,13 +258,13 @@ __device__ __forceinline__ void low_tile(int i, int& rt, int& ct) {
     ct = i - (rt * (rt + 1)) / 2;
 }
 
-// Gradients of one (sequence, head, chunk).
+// Gradients of one (sequence, head, chunk), eight waves.
 template <bool KDA>
-__global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p, ChunkIn in, ChunkBwdPtrs a) {
+__global__ __launch_bounds__(kGT, 1) void chunk_grad_kernel(ChunkParams p, ChunkIn in, ChunkBwdPtrs a) {
     __shared__ __align__(16) float big[kBig];
     __shared__ float dAs[kWM], dMs[kWM];
     __shared__ float bS[kCh], gS[kCh], elS[kChDk];
-    __shared__ float bpart[4][kCh];  // beta's pair term per wave and token
+    __shared__ float bpart[kGW][kCh];  // beta's pair term per wave and token
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, g0 = lane >> 4, c0 = lane & 15;
     const int g = g0, c = c0;
     const int cc = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -261,7 +274,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
     const float* R = a.rec + ch * RecB::SIZE;
     float* dPs = big + 3 * kWM;
-    for (int i = t; i < kWM; i += kChThreads) dPs[i] = dMs[i] = 0.0f;
+    for (int i = t; i < kWM; i += kGT) dPs[i] = dMs[i] = 0.0f;
     bpart[w][lane] = 0.0f;
     if (t < kCh) bS[t] = R[RecB::BT + t];
 
@@ -273,36 +286,37 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     float* dUs = Ds + kCh * kSP;
     float* S0s = dUs + kCh * kSP;
     float* dSes = S0s + kChDk * kSP;
-    f4 accQ[8], accK[8], accD[8], accPM[5];
+    // wave w: tiles (rt, w) of dQp, dKp, dKd (rows of block rt, keys 16 w + c) and tiles
+    // w, w + 8, w + 16 (those below 20) of dP (0..9) and dM (10..19)
+    f4 accQ[4], accK[4], accD[4], accPM[3];
 #pragma unroll
-    for (int j = 0; j < 8; j++) accQ[j] = accK[j] = accD[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 4; j++) accQ[j] = accK[j] = accD[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int u = 0; u < 5; u++) accPM[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < 3; u++) accPM[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     float el = 0.0f;
     const float* Sck = a.ckpts + ch * kChDk * dv;
     const float* dSe = a.dSe + ch * kChDk * dv;
-    // slab sb: this thread's 16-byte pieces of U, dDelta, Delta, dO, dv (token t / 4) and of S,
-    // dS_end (keys t / 4 and 64 + t / 4); slab sb + 1 is loaded while slab sb is multiplied (a
+    // slab sb: the 16-byte pieces of S and dS_end of key t / 4 and, in waves 0-3, of U,
+    // dDelta, Delta, dO, dv of token t / 4; slab sb + 1 is loaded while slab sb is multiplied (a
     // row past the end reads row 0 and is stored as zero)
+    const bool tokw = t < 4 * kCh;  // uniform over a wave
     struct Slab {
-        float4 u, dd, d, o, w, s0[2], se[2];
+        float4 u, dd, d, o, w, s0, se;
     };
     auto slab_load = [&](int sb, Slab& x) __attribute__((always_inline)) {
-        const int tk = t >> 2, cb = 16 * sb + ((t & 3) << 2);
-        const size_t wrow = (ch * kCh + tk) * dv + cb;
-        const size_t grow = (tok0 + static_cast<size_t>(tk < L ? tk : 0) * p.H) * dv + cb;
-        x.u = *reinterpret_cast<const float4*>(a.U + wrow);
-        x.dd = *reinterpret_cast<const float4*>(a.dD + wrow);
-        x.d = *reinterpret_cast<const float4*>(a.D + wrow);
-        x.o = *reinterpret_cast<const float4*>(a.dout + grow);
-        x.w = *reinterpret_cast<const float4*>(a.dv + grow);
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int idx = t + kChThreads * u, key = idx >> 2, k4 = (idx & 3) << 2;
-            const size_t kr = static_cast<size_t>(key) * dv + 16 * sb + k4;
-            x.s0[u] = *reinterpret_cast<const float4*>(Sck + kr);
-            x.se[u] = *reinterpret_cast<const float4*>(dSe + kr);
+        const int tk = (t >> 2) & 63, cb = 16 * sb + ((t & 3) << 2);
+        if (tokw) {
+            const size_t wrow = (ch * kCh + tk) * dv + cb;
+            const size_t grow = (tok0 + static_cast<size_t>(tk < L ? tk : 0) * p.H) * dv + cb;
+            x.u = *reinterpret_cast<const float4*>(a.U + wrow);
+            x.dd = *reinterpret_cast<const float4*>(a.dD + wrow);
+            x.d = *reinterpret_cast<const float4*>(a.D + wrow);
+            x.o = *reinterpret_cast<const float4*>(a.dout + grow);
+            x.w = *reinterpret_cast<const float4*>(a.dv + grow);
         }
+        const size_t kr = static_cast<size_t>(t >> 2) * dv + cb;
+        x.s0 = *reinterpret_cast<const float4*>(Sck + kr);
+        x.se = *reinterpret_cast<const float4*>(dSe + kr);
     };
     Slab nx;
     slab_load(0, nx);
@@ -310,44 +324,45 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
         const int g = opaque(g0), c = opaque(c0);
         __syncthreads();
         {
-            const int tk = t >> 2, j4 = (t & 3) << 2;
-            const bool ok = tk < L;
-            const float bt = bS[tk];
-            *reinterpret_cast<float4*>(Rs + tk * kSP + j4) = make_float4(nx.u.x * bt, nx.u.y * bt, nx.u.z * bt, nx.u.w * bt);
-            *reinterpret_cast<float4*>(dDs + tk * kSP + j4) = nx.dd;
-            *reinterpret_cast<float4*>(Ds + tk * kSP + j4) = nx.d;
-            *reinterpret_cast<float4*>(dOs + tk * kSP + j4) = keep_if(ok, nx.o);
-            *reinterpret_cast<float4*>(dUs + tk * kSP + j4) = keep_if(ok, nx.w);
-#pragma unroll
-            for (int u = 0; u < 2; u++) {
-                const int idx = t + kChThreads * u, key = idx >> 2, k4 = (idx & 3) << 2;
-                *reinterpret_cast<float4*>(S0s + key * kSP + k4) = nx.s0[u];
-                *reinterpret_cast<float4*>(dSes + key * kSP + k4) = nx.se[u];
+            const int tk = (t >> 2) & 63, j4 = (t & 3) << 2;
+            if (tokw) {
+                const bool ok = tk < L;
+                const float bt = bS[tk];
+                *reinterpret_cast<float4*>(Rs + tk * kSP + j4) = make_float4(nx.u.x * bt, nx.u.y * bt, nx.u.z * bt, nx.u.w * bt);
+                *reinterpret_cast<float4*>(dDs + tk * kSP + j4) = nx.dd;
+                *reinterpret_cast<float4*>(Ds + tk * kSP + j4) = nx.d;
+                *reinterpret_cast<float4*>(dOs + tk * kSP + j4) = keep_if(ok, nx.o);
+                *reinterpret_cast<float4*>(dUs + tk * kSP + j4) = keep_if(ok, nx.w);
             }
+            *reinterpret_cast<float4*>(S0s + (t >> 2) * kSP + j4) = nx.s0;
+            *reinterpret_cast<float4*>(dSes + (t >> 2) * kSP + j4) = nx.se;
         }
         __syncthreads();
         slab_load(sb + 1 < dv / 16 ? sb + 1 : sb, nx);  // the last slab reloads itself
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             const int kc = 4 * s + g;
+            const int br = (16 * w + c) * kSP + kc;
+            const float bs = S0s[br], be = dSes[br];
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int rt = j & 3, kt = w + 4 * (j >> 2);
-                const int ar = (16 * rt + c) * kSP + kc, br = (16 * kt + c) * kSP + kc;
-                accQ[j] = mfma4(dOs[ar], S0s[br], accQ[j]);
-                accK[j] = mfma4(dUs[ar], S0s[br], accK[j]);
-                accD[j] = mfma4(Ds[ar], dSes[br], accD[j]);
+            for (int j = 0; j < 4; j++) {
+                const int ar = (16 * j + c) * kSP + kc;
+                accQ[j] = mfma4(dOs[ar], bs, accQ[j]);
+                accK[j] = mfma4(dUs[ar], bs, accK[j]);
+                accD[j] = mfma4(Ds[ar], be, accD[j]);
                 if ((j & 1) == 1) sched_fence();
             }
 #pragma unroll
-            for (int u = 0; u < 5; u++) {
-                // tiles w + 4 u of dP (0..9) and dM (10..19); the choice is uniform over the wave
-                const int idx = w + 4 * u;
-                int rt, ct;
-                low_tile(idx % 10, rt, ct);
-                const float* Ao = idx < 10 ? dDs : dOs;
-                const float* Bo = idx < 10 ? Rs : Ds;
-                accPM[u] = mfma4(Ao[(16 * rt + c) * kSP + kc], Bo[(16 * ct + c) * kSP + kc], accPM[u]);
+            for (int u = 0; u < 3; u++) {
+                // tiles w + 8 u below 20: the choice is uniform over the wave
+                const int idx = w + 8 * u;
+                if (idx < 20) {
+                    int rt, ct;
+                    low_tile(idx % 10, rt, ct);
+                    const float* Ao = idx < 10 ? dDs : dOs;
+                    const float* Bo = idx < 10 ? Rs : Ds;
+                    accPM[u] = mfma4(Ao[(16 * rt + c) * kSP + kc], Bo[(16 * ct + c) * kSP + kc], accPM[u]);
+                }
             }
         }
         if (t < kChDk) {
@@ -357,22 +372,24 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 5; u++) {
-        const int idx = w + 4 * u;
-        int rt, ct;
-        low_tile(idx % 10, rt, ct);
-        float* dst = idx < 10 ? dPs : dMs;
+    for (int u = 0; u < 3; u++) {
+        const int idx = w + 8 * u;
+        if (idx < 20) {
+            int rt, ct;
+            low_tile(idx % 10, rt, ct);
+            float* dst = idx < 10 ? dPs : dMs;
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int row = 16 * rt + 4 * g + r, cl = 16 * ct + c;
-            if (cl <= row) dst[row * kPW + cl] = accPM[u][r];
+            for (int r = 0; r < 4; r++) {
+                const int row = 16 * rt + 4 * g + r, cl = 16 * ct + c;
+                if (cl <= row) dst[row * kPW + cl] = accPM[u][r];
+            }
         }
     }
     if (t < kChDk) elS[t] = el;
     float* gsc = a.gsc + ch * 3 * kCh * kChDk;  // [3][64][128]
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int rt = j & 3, kt = w + 4 * (j >> 2);
+    for (int j = 0; j < 4; j++) {
+        const int rt = j, kt = w;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int o = (16 * rt + 4 * g + r) * kChDk + 16 * kt + c;
@@ -394,10 +411,10 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
         if (p.degree == 0) {
             // P = (I + A)^-1: dA = -P^T dP P^T
 #pragma unroll
-            for (int i = t; i < kCh * kCh; i += kChThreads) Xb[(i >> 6) * kPW + (i & 63)] = R[RecB::P + (i >> 6) * RecB::PP + (i & 63)];
+            for (int i = t; i < kCh * kCh; i += kGT) Xb[(i >> 6) * kPW + (i & 63)] = R[RecB::P + (i >> 6) * RecB::PP + (i & 63)];
             __syncthreads();
-            mm64<true, false>(Xb, Gb, Zb, nullptr);
-            mm64<false, true>(Zb, Xb, Zb, nullptr);
+            mm64<true, false, kGW>(Xb, Gb, Zb, nullptr);
+            mm64<false, true, kGW>(Zb, Xb, Zb, nullptr);
             dZn = Zb;
         } else {
             // P = (I + Z_0)(I + Z_1) ... (I + Z_{m-1}), Z_j = X^(2^j), X = -A.  Reverse sweep
@@ -407,25 +424,25 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
             int m = 0;
             while ((1 << m) - 1 < p.degree) m++;
 #pragma unroll
-            for (int i = t; i < kCh * kCh; i += kChThreads) Xb[(i >> 6) * kPW + (i & 63)] = -R[RecB::A + (i >> 6) * RecB::PA + (i & 63)];
+            for (int i = t; i < kCh * kCh; i += kGT) Xb[(i >> 6) * kPW + (i & 63)] = -R[RecB::A + (i >> 6) * RecB::PA + (i & 63)];
             for (int j = m - 1; j >= 0; j--) {
                 __syncthreads();
-                for (int i = t; i < kCh * kCh; i += kChThreads) {
+                for (int i = t; i < kCh * kCh; i += kGT) {
                     const int r = i >> 6, q = i & 63;
                     Zb[r * kPW + q] = Xb[r * kPW + q];
                     Pb[r * kPW + q] = r == q ? 1.0f : 0.0f;
                 }
                 __syncthreads();
                 for (int i = 0; i < j; i++) {
-                    mm64<false, false>(Pb, Zb, Pb, Pb);
-                    mm64<false, false>(Zb, Zb, Zb, nullptr);
+                    mm64<false, false, kGW>(Pb, Zb, Pb, Pb);
+                    mm64<false, false, kGW>(Zb, Zb, Zb, nullptr);
                 }
-                mm64<true, false>(Pb, Gb, dZb, nullptr);
+                mm64<true, false, kGW>(Pb, Gb, dZb, nullptr);
                 if (j < m - 1) {
-                    mm64<false, true>(dZn, Zb, dZb, dZb);
-                    mm64<true, false>(Zb, dZn, dZb, dZb);
+                    mm64<false, true, kGW>(dZn, Zb, dZb, dZb);
+                    mm64<true, false, kGW>(Zb, dZn, dZb, dZb);
                 }
-                if (j > 0) mm64<false, true>(Gb, Zb, Gb, Gb);
+                if (j > 0) mm64<false, true, kGW>(Gb, Zb, Gb, Gb);
                 float* tmp = dZn;
                 dZn = dZb;
                 dZb = tmp;
@@ -433,7 +450,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
         }
         // exact: dA = -(P^T dP P^T); Neumann: dA = -dX (X = -A)
         __syncthreads();
-        for (int i = t; i < kCh * kCh; i += kChThreads) {
+        for (int i = t; i < kCh * kCh; i += kGT) {
             const int r = i >> 6, q = i & 63;
             dAs[r * kPW + q] = q < r ? -dZn[r * kPW + q] : 0.0f;
         }
@@ -444,7 +461,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     float* qS = big + kTK;
     float* Gs = big + 2 * kTK;
     {
-        Rows rk, rq, rg;
+        Rows<kGT> rk, rq, rg;
         rows_load(rk, in.k, tok0, p.H, L, p.qkv_dt);
         rows_load(rq, in.q, tok0, p.H, L, p.qkv_dt);
         if (KDA) rows_load(rg, in.g, tok0, p.H, L, p.gate_dt);
@@ -467,9 +484,9 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     float* dABG = big + 2 * kTK;  // scalar gate only (no per-key decays in LDS then)
     if (!KDA) {
         // one decay per pair: dA o Gamma, dM o Gamma and beta dA o Gamma
-        for (int i = t; i < kCh * kCh; i += kChThreads) {
+        for (int i = t; i < kCh * kCh; i += kGT) {
             const int r = i >> 6, q = i & 63;
-            const float gam = q <= r ? expf(gS[r] - gS[q]) : 0.0f;
+            const float gam = q <= r ? exp_acc(gS[r] - gS[q]) : 0.0f;
             const float da = dAs[r * kPW + q] * gam;
             dAs[r * kPW + q] = da;
             dMs[r * kPW + q] *= gam;
@@ -484,17 +501,22 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     // with the elementwise terms of Kp = k E, Qp = q E, Kd = k F: the outputs dq, dk and the
     // cumulative-decay gradient dG (into the gsc dKd slot), and beta's pair term k_r T1
     float* gKd = gsc + 2 * kCh * kChDk;
+    const size_t ntok = static_cast<size_t>(p.B) * p.T * p.H;
+    const auto rdq = make_rsrc(a.dq + tok0 * kChDk, (ntok - tok0) * kChDk * 4);
+    const auto rdk = make_rsrc(a.dk + tok0 * kChDk, (ntok - tok0) * kChDk * 4);
     auto finish = [&](int row, int key, float t1, float t2, float t3, float dQp, float dKp, float dKd)
                       __attribute__((always_inline)) {
         const int o = row * kChDk + key;
         const float G = Gof(row, key), GL = Gof(L - 1, key);
-        const float E = expf(G), F = expf(GL - G);
+        const float E = exp_acc(G), F = exp_acc(GL - G);
         const float kv = kS[row * 132 + key], qv = qS[row * 132 + key], bt = bS[row];
         const float Kp = kv * E, Qp = qv * E, Kd = kv * F;
         if (row < L) {
-            const size_t e = (tok0 + static_cast<size_t>(row) * p.H) * kChDk + key;
-            a.dq[e] = __builtin_fmaf(E, dQp, t2);
-            a.dk[e] = __builtin_fmaf(E, dKp, __builtin_fmaf(F, dKd, __builtin_fmaf(bt, t1, t3)));
+            // row = 16 rt + 4 g + r: the lane part 4 g in the offset register, the rest scalar
+            const int voff = (4 * g * p.H * kChDk + key) * 4, soff = (row - 4 * g) * p.H * kChDk * 4;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__builtin_fmaf(E, dQp, t2)), rdq, voff, soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(__builtin_fmaf(E, dKp, __builtin_fmaf(F, dKd, __builtin_fmaf(bt, t1, t3)))), rdk, voff, soff, 0);
         }
         gKd[o] = __builtin_fmaf(dKp, Kp, dQp * Qp) + __builtin_fmaf(bt * kv, t1, __builtin_fmaf(qv, t2, -kv * t3));
         // Kd = k F, F = e^{G_{L-1} - G}: its term reaches the gates of the tokens after this row
@@ -505,11 +527,11 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     // KDA: every decay factored on 16-token blocks (chunk_factorable), else per-key sums
     __shared__ int flag;
     const bool fact = !KDA || chunk_factorable(Gs, L, &flag);
-    // tiles (rt, kt) of this wave: rows of block rt, keys 16 kt + c
+    // tiles (rt, w) of this wave: rows of block rt, keys 16 w + c
     float bc[4][4];
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int rt = j & 3, kt = w + 4 * (j >> 2), key = 16 * kt + c;
+    for (int j = 0; j < 4; j++) {
+        const int rt = j, key = 16 * w + c;
         // the products over columns for this tile's elements, loaded while the pair sums run
         float pq[4], pk[4], pd[4];
 #pragma unroll
@@ -544,13 +566,13 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
 #pragma unroll
                     for (int s = 0; s < 4; s++) {
                         const int tk = 16 * I + 4 * s + g;
-                        const float bl = kS[tk * 132 + key] * expf(rf - Gs[tk * 132 + key]);
+                        const float bl = kS[tk * 132 + key] * exp_acc(rf - Gs[tk * 132 + key]);
                         P1 = mfma4(dAs[(16 * rt + c) * kPW + tk], bl, P1);
                         P2 = mfma4(dMs[(16 * rt + c) * kPW + tk], bl, P2);
                     }
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        const float e = expf(Gs[(16 * rt + 4 * g + r) * 132 + key] - rf);
+                        const float e = exp_acc(Gs[(16 * rt + 4 * g + r) * 132 + key] - rf);
                         T1[r] = __builtin_fmaf(e, P1[r], T1[r]);
                         T2[r] = __builtin_fmaf(e, P2[r], T2[r]);
                     }
@@ -564,13 +586,13 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
 #pragma unroll
                     for (int s = 0; s < 4; s++) {
                         const int tk = 16 * R2 + 4 * s + g;
-                        const float er = expf(Gs[tk * 132 + key] - rf);
+                        const float er = exp_acc(Gs[tk * 132 + key] - rf);
                         P3 = mfma4(bS[tk] * dAs[tk * kPW + 16 * rt + c], kS[tk * 132 + key] * er, P3);
                         P3 = mfma4(dMs[tk * kPW + 16 * rt + c], qS[tk * 132 + key] * er, P3);
                     }
 #pragma unroll
                     for (int r = 0; r < 4; r++)
-                        T3[r] = __builtin_fmaf(expf(rf - Gs[(16 * rt + 4 * g + r) * 132 + key]), P3[r], T3[r]);
+                        T3[r] = __builtin_fmaf(exp_acc(rf - Gs[(16 * rt + 4 * g + r) * 132 + key]), P3[r], T3[r]);
                 }
             }
             // per-key sums over every token when the factors are not safe; dA is zero on and
@@ -584,7 +606,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
                 float t1 = 0.0f, t2 = 0.0f, t3 = 0.0f;
                 for (int i = 0; i < i_hi; i++) {
                     const float Gi = Gs[i * 132 + key], ki = kS[i * 132 + key];
-                    const float d = expf(i <= row ? Gr - Gi : Gi - Gr);
+                    const float d = exp_acc(i <= row ? Gr - Gi : Gi - Gr);
                     const float dl = i <= row ? d : 0.0f, du = i >= row ? d : 0.0f;  // no 0 * inf
                     t1 = __builtin_fmaf(dAs[row * kPW + i] * ki, dl, t1);
                     t2 = __builtin_fmaf(dMs[row * kPW + i] * ki, dl, t2);
@@ -599,7 +621,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
         for (int r = 0; r < 4; r++) {
             const int row = 16 * rt + 4 * g + r;
             finish(row, key, T1[r], T2[r], T3[r], pq[r], pk[r], pd[r]);
-            bc[rt][r] = (j < 4 ? 0.0f : bc[rt][r]) + kS[row * 132 + key] * T1[r];
+            bc[rt][r] = kS[row * 132 + key] * T1[r];
         }
         sched_fence();
     }
@@ -617,12 +639,12 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
     float* cS = big + kTK;
     __syncthreads();
 #pragma unroll
-    for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
+    for (int idx = t; idx < kCh * kChDk; idx += kGT) {
         const int r = idx >> 7, kk = idx & 127;
         float v = gKd[r * kChDk + kk];
         const float cv = gsc[r * kChDk + kk];
         // E_L = exp(G_{L-1}) feeds dG_{L-1} as well
-        if (r == L - 1) v += elS[kk] * expf(Gof(L - 1, kk));
+        if (r == L - 1) v += elS[kk] * exp_acc(Gof(L - 1, kk));
         dGs[r * 132 + kk] = r < L ? v : 0.0f;
         cS[r * 132 + kk] = r < L ? cv : 0.0f;
     }
@@ -662,7 +684,8 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_grad_kernel(ChunkParams p
         }
     }
     if (t < L) {
-        float sbt = (bpart[0][t] + bpart[1][t]) + (bpart[2][t] + bpart[3][t]);
+        float sbt = ((bpart[0][t] + bpart[1][t]) + (bpart[2][t] + bpart[3][t])) +
+                    ((bpart[4][t] + bpart[5][t]) + (bpart[6][t] + bpart[7][t]));
         for (int tl = 0; tl < p.ntile; tl++) sbt += a.dbp[(static_cast<size_t>(tl) * BH * p.nch + ch) * kCh + t];
         a.dbeta[tok0 + static_cast<size_t>(t) * p.H] = sbt;
     }
@@ -722,8 +745,8 @@ hipError_t launch_chunk_bwd(const la_config& c, const FwdArgs& fa, const BwdArgs
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid(p.nch, c.H, c.B);
-    if (c.gate == LA_GATE_KEY) hipLaunchKernelGGL(chunk_grad_kernel<true>, grid, dim3(kChThreads), 0, s, p, in, a);
-    else hipLaunchKernelGGL(chunk_grad_kernel<false>, grid, dim3(kChThreads), 0, s, p, in, a);
+    if (c.gate == LA_GATE_KEY) hipLaunchKernelGGL(chunk_grad_kernel<true>, grid, dim3(kGT), 0, s, p, in, a);
+    else hipLaunchKernelGGL(chunk_grad_kernel<false>, grid, dim3(kGT), 0, s, p, in, a);
     return hipGetLastError();
 }
 

@@ -33,11 +33,13 @@ size_t chunk_fwd_workspace_bytes(const la_config& c) {
 namespace {
 
 constexpr int kPT = 132;  // pitch of the prep kernel's token-by-key arrays
+constexpr int kPrepW = 8;  // the prep kernel's waves (two per SIMD: its phases mostly wait on
+constexpr int kPrepT = 64 * kPrepW;  // memory and LDS, and the second wave fills those gaps)
 
 // Prep: A, M, the solve P, Kp, Qp, Kd, E_L of one chunk into its record (forward or backward
 // layout).  Tokens past the sequence's end are zero rows (their beta, k and q are zero).
 template <bool KDA, bool BWD>
-__global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p, ChunkIn in, float* __restrict__ rec) {
+__global__ __launch_bounds__(kPrepT, 1) void chunk_prep_kernel(ChunkParams p, ChunkIn in, float* __restrict__ rec) {
     __shared__ __align__(16) float big[3 * kCh * kPT];
     __shared__ float Am[kCh * kPW], Mm[kCh * kPW];
     __shared__ float bS[kCh], gS[kCh];
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
 
     {
         // every load of the chunk's inputs in flight before any is used
-        Rows rk, rq, rg;
+        Rows<kPrepT> rk, rq, rg;
         rows_load(rk, in.k, tok0, H, L, p.qkv_dt);
         rows_load(rq, in.q, tok0, H, L, p.qkv_dt);
         if (KDA) rows_load(rg, in.g, tok0, H, L, p.gate_dt);
@@ -82,13 +84,13 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
     auto Gof = [&](int r, int kk) __attribute__((always_inline)) { return KDA ? GS[r * kPT + kk] : gS[r]; };
 
     // decayed keys and queries
-    for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
+    for (int idx = t; idx < kCh * kChDk; idx += kPrepT) {
         const int r = idx >> 7, kk = idx & 127;
         const float G = Gof(r, kk);
-        const float E = expf(G);
+        const float E = exp_acc(G);
         const float kv = kS[r * kPT + kk], qv = qS[r * kPT + kk];
         if (BWD) {
-            const float F = expf(Gof(L - 1, kk) - G);
+            const float F = exp_acc(Gof(L - 1, kk) - G);
             R[RecB::KP + r * RecB::PK + kk] = kv * E;
             R[RecB::QP + r * RecB::PK + kk] = qv * E;
             R[RecB::KD + r * RecB::PKD + kk] = kv * F;
@@ -98,12 +100,12 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
         }
     }
     if (!BWD) {
-        for (int idx = t; idx < kCh * kChDk; idx += kChThreads) {
+        for (int idx = t; idx < kCh * kChDk; idx += kPrepT) {
             const int kk = idx >> 6, r = idx & 63;
-            R[RecF::KDT + kk * RecF::PD + r] = kS[r * kPT + kk] * expf(Gof(L - 1, kk) - Gof(r, kk));
+            R[RecF::KDT + kk * RecF::PD + r] = kS[r * kPT + kk] * exp_acc(Gof(L - 1, kk) - Gof(r, kk));
         }
     }
-    if (t < kChDk) R[(BWD ? RecB::EL : RecF::EL) + t] = expf(Gof(L - 1, t));
+    if (t < kChDk) R[(BWD ? RecB::EL : RecF::EL) + t] = exp_acc(Gof(L - 1, t));
     if (t < kCh) R[(BWD ? RecB::BT : RecF::BT) + t] = bS[t];
 
     // A (strictly lower) and M (lower with the diagonal)
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
         const bool fact = chunk_factorable(GS, L, &flag);
         if (fact) {
             constexpr int PR[10] = {1, 2, 2, 3, 3, 3, 0, 1, 2, 3}, PC[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-            for (int pi = w; pi < 10; pi += 4) {
+            for (int pi = w; pi < 10; pi += kPrepW) {
                 const int rt = PR[pi], ct = PC[pi], ref = rt == ct ? 16 * ct + 7 : 16 * ct + 15;
                 f4 aA = {0.0f, 0.0f, 0.0f, 0.0f}, aM = aA;
 #pragma unroll 4
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
                     const int key = 4 * s2 + g;
                     const float rf = GS[ref * kPT + key];
                     const int ra = (16 * rt + c) * kPT + key, rb = (16 * ct + c) * kPT + key;
-                    const float er = expf(GS[ra] - rf);
-                    const float bl = kS[rb] * expf(rf - GS[rb]);
+                    const float er = exp_acc(GS[ra] - rf);
+                    const float bl = kS[rb] * exp_acc(rf - GS[rb]);
                     aA = mfma4(kS[ra] * er, bl, aA);
                     aM = mfma4(qS[ra] * er, bl, aM);
                 }
@@ -140,15 +142,15 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
                 }
             }
             // the tiles above the diagonal
-            for (int i = t; i < kCh * kCh; i += kChThreads) {
+            for (int i = t; i < kCh * kCh; i += kPrepT) {
                 const int r = i >> 6, q = i & 63;
                 if ((q >> 4) > (r >> 4)) Am[r * kPW + q] = Mm[r * kPW + q] = 0.0f;
             }
         } else {
-            for (int i = t; i < kCh * kPW; i += kChThreads) Am[i] = Mm[i] = 0.0f;
+            for (int i = t; i < kCh * kPW; i += kPrepT) Am[i] = Mm[i] = 0.0f;
             __syncthreads();
             // lane: row 4 (lane / 16) + rr of the tile, column lane % 16
-            for (int tl = w; tl < 10; tl += 4) {
+            for (int tl = w; tl < 10; tl += kPrepW) {
                 const int rt = tl < 1 ? 0 : tl < 3 ? 1 : tl < 6 ? 2 : 3;
                 const int ct = tl - (rt * (rt + 1)) / 2;
                 const int col = 16 * ct + c;
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
 #pragma unroll
                     for (int rr = 0; rr < 4; rr++) {
                         const int row = 16 * rt + 4 * g + rr;
-                        const float kd = kc * expf(col <= row ? GS[row * kPT + kk] - Gc : 0.0f);
+                        const float kd = kc * exp_acc(col <= row ? GS[row * kPT + kk] - Gc : 0.0f);
                         aa[rr] = __builtin_fmaf(kS[row * kPT + kk], kd, aa[rr]);
                         mm[rr] = __builtin_fmaf(qS[row * kPT + kk], kd, mm[rr]);
                     }
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
     } else {
         // one decay per token pair: K K^T and Q K^T on the matrix cores, then the decay
         const int lane = t & 63, w = t >> 6, g = lane >> 4, c = lane & 15;
-        for (int tl = w; tl < 16; tl += 4) {
+        for (int tl = w; tl < 16; tl += kPrepW) {
             const int rt = tl >> 2, ct = tl & 3;
             f4 ak = {0.0f, 0.0f, 0.0f, 0.0f}, aq = ak;
             if (rt >= ct) {
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int row = 16 * rt + 4 * g + r, i = 16 * ct + c;
-                const float gam = i <= row ? expf(gS[row] - gS[i]) : 0.0f;
+                const float gam = i <= row ? exp_acc(gS[row] - gS[i]) : 0.0f;
                 Am[row * kPW + i] = i < row ? bS[row] * (gam * ak[r]) : 0.0f;
                 Mm[row * kPW + i] = gam * aq[r];
             }
@@ -207,15 +209,17 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
         // inverting block w (lane (g, c) holds column c and sums rows i = g mod 4; a row's
         // values are read back by the same wave, whose LDS accesses are in order).  Then block
         // rows k = 1..3: T_kj = -T_kk sum_{l=j}^{k-1} A_kl T_lj, tile (k, j) on wave j.
-        for (int idx = t; idx < kCh * kCh; idx += kChThreads) W0[(idx >> 6) * kPW + (idx & 63)] = 0.0f;
+        for (int idx = t; idx < kCh * kCh; idx += kPrepT) W0[(idx >> 6) * kPW + (idx & 63)] = 0.0f;
         __syncthreads();
         const int lane = t & 63, w = t >> 6, g = lane >> 4, c = lane & 15, o = 16 * w;
-        for (int r = 0; r < 16; r++) {
-            float part = 0.0f;
-            for (int i = g; i < r; i += 4)
-                part = __builtin_fmaf(Am[(o + r) * kPW + o + i], W0[(o + i) * kPW + o + c], part);
-            const float sum = rows_sum(part);
-            if (g == 0) W0[(o + r) * kPW + o + c] = (r == c ? 1.0f : 0.0f) - sum;
+        if (w < 4) {
+            for (int r = 0; r < 16; r++) {
+                float part = 0.0f;
+                for (int i = g; i < r; i += 4)
+                    part = __builtin_fmaf(Am[(o + r) * kPW + o + i], W0[(o + i) * kPW + o + c], part);
+                const float sum = rows_sum(part);
+                if (g == 0) W0[(o + r) * kPW + o + c] = (r == c ? 1.0f : 0.0f) - sum;
+            }
         }
         __syncthreads();
         float* Y = Ys + 256 * w;
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
     } else {
         // sum_{n <= d} X^n, X = -A, d = 2^m - 1, as (I + X)(I + X^2)(I + X^4) ...: Z holds X^(2^j),
         // P the product so far
-        for (int idx = t; idx < kCh * kCh; idx += kChThreads) {
+        for (int idx = t; idx < kCh * kCh; idx += kPrepT) {
             const int r = idx >> 6, i = idx & 63;
             const float x = -Am[r * kPW + i];
             W0[r * kPW + i] = x;
@@ -250,13 +254,13 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_prep_kernel(ChunkParams p
         }
         __syncthreads();
         for (int done = 1; done < p.degree; done = 2 * done + 1) {
-            mm64<false, false>(W0, W0, W0, nullptr);  // Z <- Z Z
-            mm64<false, false>(W1, W0, W1, W1);       // P <- P + P Z
+            mm64<false, false, kPrepW>(W0, W0, W0, nullptr);  // Z <- Z Z
+            mm64<false, false, kPrepW>(W1, W0, W1, W1);       // P <- P + P Z
         }
         Pm = W1;
     }
 
-    for (int idx = t; idx < kCh * kCh; idx += kChThreads) {
+    for (int idx = t; idx < kCh * kCh; idx += kPrepT) {
         const int r = idx >> 6, i = idx & 63;
         if (BWD) {
             R[RecB::P + r * RecB::PP + i] = Pm[r * kPW + i];
@@ -298,9 +302,10 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
         const int g = opaque(g0), c = opaque(c0);
         const int t0 = cc * kCh, L = min(kCh, p.T - t0);
         if (ckpts && t0 % p.ckpt_interval == 0) {
-            float* dst = ckpts + (static_cast<size_t>(bh) * p.nck + t0 / p.ckpt_interval) * kChDk * dv + col;
+            const ChunkRows ck = chunk_rows(ckpts + (static_cast<size_t>(bh) * p.nck + t0 / p.ckpt_interval) * kChDk * dv,
+                                            static_cast<size_t>(kChDk) * dv * 4, dv, g, col, 4);
 #pragma unroll
-            for (int m = 0; m < 32; m++) dst[static_cast<size_t>(kmap(m, g)) * dv] = s[m];
+            for (int m = 0; m < 32; m++) ck.stf(m, s[m]);
         }
         // part 1 of this chunk's record has arrived and every wave is done with part 2 of the
         // previous one
@@ -309,12 +314,20 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
         // v of this lane's tokens (a row past the end reads row 0 and is zeroed where it is
         // used), issued while nothing else is in flight: the dtype switch then costs no wait
         const size_t tok0 = (static_cast<size_t>(b) * p.T + t0) * p.H + h;
+        const size_t ntok = static_cast<size_t>(p.B) * p.T * p.H;  // tokens x heads in the inputs
         uint32_t vr[16];
-        const size_t vrow = static_cast<size_t>(p.H) * dv;
-        load_raw<16>(vr, in.v, p.qkv_dt, [&](int i) {
-            const int tk = kmap(i, g);
-            return (tok0 * dv + col) + static_cast<size_t>(tk < L ? tk : 0) * vrow;
-        });
+        {
+            const int ve = p.qkv_dt == LA_F32 ? 4 : 2;
+            const ChunkRows rv = chunk_rows(static_cast<const char*>(in.v) + tok0 * dv * ve, (ntok - tok0) * dv * ve,
+                                            p.H * dv, g, col, ve);
+            if (ve == 4) {
+#pragma unroll
+                for (int i = 0; i < 16; i++) vr[i] = rv.ld32(i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; i++) vr[i] = rv.ld16(i);
+            }
+        }
         // part 2 while the first products run
         lds_dma(RB, recu + static_cast<size_t>(cc) * RecF::SIZE + RecF::PART2, RecF::SIZE - RecF::PART2);
 
@@ -365,10 +378,15 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
             if ((m & 3) == 3) sched_fence();
         }
         if (o) {
+            const int oe = p.out_dt == LA_F32 ? 4 : 2;
+            const ChunkRows ro = chunk_rows(static_cast<char*>(o) + tok0 * dv * oe, (ntok - tok0) * dv * oe, p.H * dv, g,
+                                            col, oe);
 #pragma unroll
             for (int i = 0; i < 16; i++) {
-                const int tk = kmap(i, g);
-                if (tk < L) store_elem(o, (tok0 + static_cast<size_t>(tk) * p.H) * dv + col, p.out_dt, Y[i >> 2][i & 3]);
+                if (kmap(i, g) < L) {
+                    if (oe == 4) ro.stf(i, Y[i >> 2][i & 3]);
+                    else ro.st16(i, f32_to_bf16_bits(Y[i >> 2][i & 3]));
+                }
             }
         }
         // S_end = diag(E_L) S + Kd^T Delta
@@ -409,11 +427,11 @@ hipError_t launch_chunk_prep(const la_config& c, const ChunkIn& in, float* rec, 
     const dim3 grid(p.nch, c.H, c.B);
     const bool kda = c.gate == LA_GATE_KEY;
     if (bwd) {
-        if (kda) hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(kChThreads), 0, s, p, in, rec);
-        else hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(kChThreads), 0, s, p, in, rec);
+        if (kda) hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(kPrepT), 0, s, p, in, rec);
+        else hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(kPrepT), 0, s, p, in, rec);
     } else {
-        if (kda) hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(kChThreads), 0, s, p, in, rec);
-        else hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(kChThreads), 0, s, p, in, rec);
+        if (kda) hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(kPrepT), 0, s, p, in, rec);
+        else hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(kPrepT), 0, s, p, in, rec);
     }
     return hipGetLastError();
 }

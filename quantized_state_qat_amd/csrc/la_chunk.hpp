@@ -93,32 +93,37 @@ __device__ __forceinline__ void lds_dma(float* dst, const float* __restrict__ sr
 }
 
 // Rows 0 .. 63 of a [token][128] bf16 or fp32 input (token r at element (tok0 + r H) 128) in
-// 16-byte pieces: thread t holds pieces t + 256 u of the chunk (u < 4 for bf16, u < 8 for fp32;
-// piece pc is row pc / P, bytes 16 (pc % P) of it, P = 16 or 32 pieces per row).  rows_load
+// 16-byte pieces: thread t of NT holds pieces t + NT u of the chunk (1024 pieces for bf16, 2048
+// for fp32; piece pc is row pc / P, bytes 16 (pc % P) of it, P = 16 or 32 pieces per row).  rows_load
 // only issues loads (a row past the end reads row 0), so the pieces of several arrays can all
 // be in flight together; rows_store widens them into LDS dst[r * 132 + k], rows L .. 63 zero.
+template <int NT = kChThreads>
 struct Rows {
-    uint4 x[8];
+    uint4 x[2048 / NT];
 };
-__device__ __forceinline__ void rows_load(Rows& R, const void* src, size_t tok0, int H, int L, int dtype) {
+template <int NT>
+__device__ __forceinline__ void rows_load(Rows<NT>& R, const void* src, size_t tok0, int H, int L, int dtype) {
+    constexpr int NU = 2048 / NT;  // pieces per thread for fp32 (half of them for bf16)
     const bool f32 = dtype == LA_F32;
-    const int sh = f32 ? 5 : 4, nu = f32 ? 8 : 4;
+    const int sh = f32 ? 5 : 4, nu = f32 ? NU : NU / 2;
     const size_t esz = f32 ? 4 : 2;
     const char* base = static_cast<const char*>(src) + tok0 * kChDk * esz;
     const size_t rstride = static_cast<size_t>(H) * kChDk * esz;
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
+    for (int u = 0; u < NU; u++) {
         if (u < nu) {
-            const int pc = threadIdx.x + kChThreads * u, r = pc >> sh, o = pc & ((1 << sh) - 1);
+            const int pc = threadIdx.x + NT * u, r = pc >> sh, o = pc & ((1 << sh) - 1);
             R.x[u] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(r < L ? r : 0) * rstride + 16 * o);
         }
     }
 }
-__device__ __forceinline__ void rows_store(float* dst, const Rows& R, int L, int dtype) {
+template <int NT>
+__device__ __forceinline__ void rows_store(float* dst, const Rows<NT>& R, int L, int dtype) {
+    constexpr int NU = 2048 / NT;
     if (dtype == LA_F32) {
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int pc = threadIdx.x + kChThreads * u, r = pc >> 5, o = pc & 31;
+        for (int u = 0; u < NU; u++) {
+            const int pc = threadIdx.x + NT * u, r = pc >> 5, o = pc & 31;
             const uint32_t m = r < L ? 0xFFFFFFFFu : 0u;
             const uint4 x = R.x[u];
             *reinterpret_cast<float4*>(dst + r * 132 + 4 * o) = make_float4(
@@ -126,8 +131,8 @@ __device__ __forceinline__ void rows_store(float* dst, const Rows& R, int L, int
         }
     } else {
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int pc = threadIdx.x + kChThreads * u, r = pc >> 4, o = pc & 15;
+        for (int u = 0; u < NU / 2; u++) {
+            const int pc = threadIdx.x + NT * u, r = pc >> 4, o = pc & 15;
             const uint32_t m = r < L ? 0xFFFFFFFFu : 0u;
             const uint32_t w[4] = {R.x[u].x & m, R.x[u].y & m, R.x[u].z & m, R.x[u].w & m};
             float4* d = reinterpret_cast<float4*>(dst + r * 132 + 8 * o);
@@ -193,6 +198,26 @@ __device__ __forceinline__ bool chunk_factorable(const float* G, int L, int* fla
     return *flag == 0;
 }
 
+// Rows kmap(i, g) of a chunk of a row-major array, addressed by buffer instructions with 32-bit
+// offsets: the lane part (g stride + col) esz bytes in a VGPR, the register part
+// (16 (i / 4) + 4 (i % 4)) stride esz bytes in an SGPR, over a resource of `bytes` bytes from
+// `base` (reads past it return zero, stores there are dropped).  The 64-bit products of general
+// pointer arithmetic (several quarter-rate instructions per element) are left out.
+struct ChunkRows {
+    __amdgpu_buffer_rsrc_t rs;
+    int voff, step;
+    __device__ __forceinline__ int soff(int i) const { return (16 * (i >> 2) + 4 * (i & 3)) * step; }
+    __device__ __forceinline__ uint32_t ld32(int i) const { return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff(i), 0); }
+    __device__ __forceinline__ uint32_t ld16(int i) const { return __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff(i), 0); }
+    __device__ __forceinline__ void st32(int i, uint32_t x) const { __builtin_amdgcn_raw_buffer_store_b32(x, rs, voff, soff(i), 0); }
+    __device__ __forceinline__ void st16(int i, uint16_t x) const { __builtin_amdgcn_raw_buffer_store_b16(x, rs, voff, soff(i), 0); }
+    __device__ __forceinline__ float ldf(int i) const { return __uint_as_float(ld32(i)); }
+    __device__ __forceinline__ void stf(int i, float x) const { st32(i, __float_as_uint(x)); }
+};
+__device__ __forceinline__ ChunkRows chunk_rows(const void* base, size_t bytes, int stride, int g, int col, int esz) {
+    return ChunkRows{make_rsrc(base, bytes), (g * stride + col) * esz, stride * esz};
+}
+
 // x, or zero when !ok, component by component (a select between whole vectors can leave
 // them in private memory).
 __device__ __forceinline__ float4 keep_if(bool ok, float4 x) {
@@ -228,6 +253,24 @@ __device__ __forceinline__ int kmap(int m, int g) { return 16 * (m >> 2) + 4 * (
 // LDS operands of an unrolled product loop the scheduler hoists (and keeps live) at once.
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
+// e^x to about two ulp for the chunk form's decays, in under ten instructions: x log2(e) as the
+// rounded product t plus its rounding error (exact by an FMA, the TwoProduct of Ogita, Rump and
+// Oishi) and that of the constant itself, then 2^t by the hardware (v_exp_f32) corrected to
+// first order, 2^t (1 + e ln 2).  Below the normal range 2^t is taken as 2^(t + 64) 2^-64, so
+// that subnormal results are rounded once (the hardware exponential flushes them); the
+// arguments here stay below +88, where 2^t does not overflow.
+__device__ __forceinline__ float exp_acc(float x) {
+    constexpr float kL2E = 1.44269502162933349609375f;  // log2(e) rounded to float
+    constexpr float kL2Elo = 1.925963033500011e-08f;    // log2(e) - kL2E
+    constexpr float kLn2 = 0.693147180559945309f;
+    const float t = x * kL2E;
+    const float e = __builtin_fmaf(x, kL2Elo, __builtin_fmaf(x, kL2E, -t));
+    const bool sub = t < -126.0f;
+    const float r = __builtin_amdgcn_exp2f(sub ? t + 64.0f : t);
+    const float y = __builtin_fmaf(r, e * kLn2, r);
+    return sub ? y * 5.42101086242752217e-20f : y;  // 2^-64
+}
+
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
@@ -235,30 +278,35 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 acc) {
 constexpr int kPW = 68;  // pitch of the 64 x 64 work matrices in LDS
 
 // C = op(A) op(B) (+ Cadd) for 64 x 64 fp32 matrices in LDS (pitch kPW) on the matrix cores,
-// op = transpose when TA / TB; wave w forms rows 16 w .. 16 w + 15.  The barrier between the
-// products and the stores lets C alias A, B or Cadd.  Every thread of the workgroup must call it.
-template <bool TA, bool TB>
+// op = transpose when TA / TB, by a workgroup of NW = 4 or 8 waves: wave w forms rows
+// 16 (w % 4) .. + 15 and, of those, column tiles (w / 4) (4 / (NW / 4)) onwards.  The barrier
+// between the products and the stores lets C alias A, B or Cadd.  Every thread of the workgroup
+// must call it.
+template <bool TA, bool TB, int NW = 4>
 __device__ void mm64(const float* A, const float* B, float* C, const float* Cadd) {
+    constexpr int NCT = 16 / NW;  // column tiles per wave
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-    f4 acc[4];
+    const int rw = w & 3, ct0 = (w >> 2) * NCT;
+    f4 acc[NCT];
 #pragma unroll
-    for (int ct = 0; ct < 4; ct++)
+    for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) acc[ct][r] = Cadd ? Cadd[(16 * w + 4 * g + r) * kPW + 16 * ct + c] : 0.0f;
+        for (int r = 0; r < 4; r++) acc[ct][r] = Cadd ? Cadd[(16 * rw + 4 * g + r) * kPW + 16 * (ct0 + ct) + c] : 0.0f;
 #pragma unroll 4
     for (int s = 0; s < 16; s++) {
-        const float a = TA ? A[(4 * s + g) * kPW + 16 * w + c] : A[(16 * w + c) * kPW + 4 * s + g];
+        const float a = TA ? A[(4 * s + g) * kPW + 16 * rw + c] : A[(16 * rw + c) * kPW + 4 * s + g];
 #pragma unroll
-        for (int ct = 0; ct < 4; ct++) {
-            const float b = TB ? B[(16 * ct + c) * kPW + 4 * s + g] : B[(4 * s + g) * kPW + 16 * ct + c];
+        for (int ct = 0; ct < NCT; ct++) {
+            const int col = 16 * (ct0 + ct);
+            const float b = TB ? B[(col + c) * kPW + 4 * s + g] : B[(4 * s + g) * kPW + col + c];
             acc[ct] = mfma4(a, b, acc[ct]);
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int ct = 0; ct < 4; ct++)
+    for (int ct = 0; ct < NCT; ct++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) C[(16 * w + 4 * g + r) * kPW + 16 * ct + c] = acc[ct][r];
+        for (int r = 0; r < 4; r++) C[(16 * rw + 4 * g + r) * kPW + 16 * (ct0 + ct) + c] = acc[ct][r];
     __syncthreads();
 }
 
