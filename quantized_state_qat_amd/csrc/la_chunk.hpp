@@ -253,6 +253,15 @@ __device__ __forceinline__ int kmap(int m, int g) { return 16 * (m >> 2) + 4 * (
 // LDS operands of an unrolled product loop the scheduler hoists (and keeps live) at once.
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
+// The same value, opaque to the compiler: lane indices passed through it at the top of a loop
+// body keep the addresses derived from them inside the body.  Otherwise every LDS address of
+// the unrolled products, being loop-invariant, is hoisted out of the chunk loop and held in
+// registers for its whole length.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // e^x to about two ulp for the chunk form's decays, in under ten instructions: x log2(e) as the
 // rounded product t plus its rounding error (exact by an FMA, the TwoProduct of Ogita, Rump and
 // Oishi) and that of the constant itself, then 2^t by the hardware (v_exp_f32) corrected to

@@ -11,15 +11,6 @@ namespace la {
 
 constexpr int kWave = 64;
 
-// The same value, opaque to the compiler (no instruction): lane indices passed through it at
-// the top of a loop body keep the addresses derived from them inside the body.  Otherwise every
-// address of an unrolled body, being loop-invariant, is hoisted out of the loop and held in
-// registers for its whole length, which can push other values out to scratch.
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 // ------------------------------------------------------------------ input widening
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
