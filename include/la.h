@@ -288,6 +288,9 @@ la_status la_decode_step(const la_config* cfg, const void* q, const void* k, con
  *           padding of a packed batch) leaves the pool untouched, writes zeros to o[b] and
  *           writes no codes or scales; so does an index outside [0, n_slots).  Two entries of
  *           one call must not name the same slot other than 0 (their updates would race).
+ * With B <= 1024 and n_slots <= 16384 the workgroups serve the entries in increasing slot
+ * order, so that the pool is streamed in address order whatever the order of the entries;
+ * every result is the same as in entry order.
  * cfg->T must be 1; n_slots >= 1.
  */
 la_status la_decode_step_slots(const la_config* cfg, const void* q, const void* k, const void* v,

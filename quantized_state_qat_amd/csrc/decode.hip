@@ -18,6 +18,7 @@ struct DecParams {
     int H, dv;
     int qkv_dt, gate_dt, out_dt;
     int rot;  // Hadamard mode with the state held rotated (Y = Hu S)
+    int sort_slots;  // slot pool: visit the entries in slot order (slot_rank_pick)
 };
 
 template <int DK, int NW>
@@ -86,15 +87,117 @@ __device__ __forceinline__ void dec_tile_wht(float* tile) {
     __syncthreads();
 }
 
+// Slot-ordered visiting of a slot pool.  A serving batch names its pool slots in any order;
+// visited in entry order, the step streams 1 MB states scattered over the pool (256 shuffled
+// slots of a 769-slot pool: 102.5 us per step, against 91.6 us for the same slots in
+// increasing order).  Each workgroup therefore ranks the batch's entries (padding entries
+// first, in entry order, then the valid entries by increasing slot) and serves the entry whose
+// rank is its blockIdx.z, so that consecutive workgroups walk the pool in address order.  The
+// ranking is a bitmap of the named slots in LDS with per-word prefix counts; every workgroup
+// computes the same ranking, so workgroups and entries stay in one-to-one correspondence.  If
+// two entries name the same valid slot (a caller error: their updates race) the number of
+// distinct slots falls short of the number of valid entries, and every workgroup keeps the
+// identity map instead.  Used for B <= kSortPerThread * NT and n_slots <= 32 kSortWords.
+constexpr int kSortWords = 512;
+constexpr int kSortPerThread = 4;
+
+template <int NW>
+struct SlotRankSmem {
+    unsigned bm[kSortWords];  // bit s: slot s is named by a valid entry
+    int pre[kSortWords];      // set bits in the words before this one
+    int npad[kSortPerThread][NW];
+    int wsum[NW];
+    int pick;
+};
+
+template <int NT>
+__device__ __forceinline__ int slot_rank_pick(const int32_t* slots, int B, int n_slots, SlotRankSmem<NT / 64>& ss) {
+    constexpr int NW = NT / 64, WPT = kSortWords / NT;
+    static_assert(kSortWords % NT == 0, "bitmap words per thread");
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int z = blockIdx.z;
+#pragma unroll
+    for (int j = 0; j < WPT; j++) ss.bm[WPT * tid + j] = 0u;
+    if (tid == 0) ss.pick = z;
+    __syncthreads();
+    int sl[kSortPerThread];
+    unsigned long long padmask[kSortPerThread];
+#pragma unroll
+    for (int i = 0; i < kSortPerThread; i++) {
+        const int e = i * NT + tid;
+        sl[i] = e < B ? slots[e] : 0;
+        const bool valid = sl[i] > 0 && sl[i] < n_slots;
+        if (valid) atomicOr(&ss.bm[sl[i] >> 5], 1u << (sl[i] & 31));
+        padmask[i] = __ballot(e < B && !valid);
+        if (lane == 0) ss.npad[i][w] = __popcll(padmask[i]);
+    }
+    __syncthreads();
+    // exclusive prefix of the words' bit counts: WPT words per thread, a scan across the
+    // wave's lanes, then the totals of the waves before
+    int cnt[WPT], local = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; j++) {
+        cnt[j] = __popc(ss.bm[WPT * tid + j]);
+        local += cnt[j];
+    }
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) ss.wsum[w] = incl;
+    __syncthreads();
+    int run = incl - local, distinct = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ww++) {
+        run += ww < w ? ss.wsum[ww] : 0;
+        distinct += ss.wsum[ww];
+    }
+#pragma unroll
+    for (int j = 0; j < WPT; j++) {
+        ss.pre[WPT * tid + j] = run;
+        run += cnt[j];
+    }
+    int npad = 0;
+#pragma unroll
+    for (int i = 0; i < kSortPerThread; i++)
+#pragma unroll
+        for (int ww = 0; ww < NW; ww++) npad += ss.npad[i][ww];
+    __syncthreads();
+    if (distinct != B - npad) return z;  // a valid slot named twice: identity map
+    int before = 0;  // padding entries before this thread's entry of pass i
+#pragma unroll
+    for (int i = 0; i < kSortPerThread; i++) {
+        const int e = i * NT + tid;
+        int pb = before;
+#pragma unroll
+        for (int ww = 0; ww < NW; ww++) pb += ww < w ? ss.npad[i][ww] : 0;
+        pb += __popcll(padmask[i] & ((1ull << lane) - 1ull));
+        if (e < B) {
+            const bool valid = sl[i] > 0 && sl[i] < n_slots;
+            const int rank = valid ? npad + ss.pre[sl[i] >> 5] + __popc(ss.bm[sl[i] >> 5] & ((1u << (sl[i] & 31)) - 1u))
+                                   : pb;
+            if (rank == z) ss.pick = e;
+        }
+#pragma unroll
+        for (int ww = 0; ww < NW; ww++) before += ss.npad[i][ww];
+    }
+    __syncthreads();
+    return ss.pick;
+}
+
 template <int DK, int R, int QMODE, int G, bool HAD, bool KDA, bool CODES>
 __global__ __launch_bounds__(16 * (DK / R)) void decode_kernel(DecParams p, DecodeArgs a) {
     constexpr int NT = 16 * (DK / R);  // threads
     constexpr int NW = NT / 64;        // waves
     __shared__ DecSmem<DK, NW> sm;
     __shared__ float tile[HAD ? DK * 64 : 1];
+    __shared__ SlotRankSmem<NW> ss;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int cq = tid & 15, rg = tid >> 4;
-    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int blk = blockIdx.x, h = blockIdx.y;
+    const int b = a.slots && p.sort_slots ? slot_rank_pick<NT>(a.slots, gridDim.z, a.n_slots, ss) : blockIdx.z;
     const int H = p.H, DV = p.dv;
     const size_t tok = static_cast<size_t>(b) * H + h;  // T == 1
     const int col0 = blk * 64 + cq * 4;
@@ -390,7 +493,8 @@ static hipError_t launch_dec_t(const la_config& c, const DecodeArgs& a, hipStrea
     p.rot = c.hadamard && c.state_rotated;
     constexpr int R = dec_rows<DK>();
     constexpr int NT = 16 * (DK / R);
-    constexpr size_t lds_static = sizeof(DecSmem<DK, NT / 64>) + sizeof(float) * (HAD ? DK * 64 : 1);
+    p.sort_slots = a.slots && c.B <= kSortPerThread * NT && a.n_slots <= 32 * kSortWords;
+    constexpr size_t lds_static = sizeof(DecSmem<DK, NT / 64>) + sizeof(SlotRankSmem<NT / 64>) + sizeof(float) * (HAD ? DK * 64 : 1);
     constexpr size_t lds_dyn = DK == 128 && lds_static < kDecLdsPerWg ? kDecLdsPerWg - lds_static : 0;
     dim3 grid(c.d_v / 64, c.H, c.B);
     if (a.codes || a.scales)

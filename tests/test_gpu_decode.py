@@ -234,3 +234,53 @@ def test_decode_slots(name, B, H, dk, dv, gate, mode, group, had):
     for b in np.nonzero(is_live)[0]:
         # one code step of difference at a near-tie moves an element by at most one grid step
         assert gu.err(P_phys[slots[b]], pool_r[slots[b]]) <= (2.0 / 127 if mode == la.LA_QDQ_INT8_GROUP else 1.0 / 8)
+
+
+SLOT_ORDER_CASES = [
+    # name, B, n_slots: the slot-ordered map (B <= 1024, n_slots <= 16384) over several waves,
+    # passes and bitmap words, and the identity map past either limit
+    ("ordered_b700_pool2000", 700, 2000),
+    ("ordered_b1024_pool16384", 1024, 16384),
+    ("identity_b1100", 1100, 1500),
+    ("identity_pool20000", 300, 20000),
+]
+
+
+@pytest.mark.parametrize("name,B,n_slots", SLOT_ORDER_CASES, ids=[c[0] for c in SLOT_ORDER_CASES])
+def test_decode_slots_visit_order(name, B, n_slots):
+    """Slot-pool decode of large shuffled batches with padding scattered among them (slot 0,
+    negative indices, indices past the pool): whichever workgroup serves an entry, every live
+    entry advances its own slot exactly as la_decode_step advances the gathered state (bit for
+    bit), o is written in entry order and matches the oracle, padding entries write zeros, and
+    slots no entry names keep their bits."""
+    torch = gu.torch_mod()
+    H, dk, dv = 1, 16, 64
+    w = synth.Workload(name, B=B, T=1, H=H, d_k=dk, d_v=dv, gate="scalar", s0_sigma=0.05, config_id=17)
+    d = synth.generate(w)
+    c = gu.cfg_for(w, d, qdq=la.LA_QDQ_INT8_GROUP, group=16)
+    rng = np.random.default_rng(11)
+    pool = (rng.standard_normal((n_slots, H, dk, dv)) * 0.05).astype(np.float32)
+    slots = rng.permutation(np.arange(1, n_slots))[:B].astype(np.int32)
+    pad = rng.choice(B, size=B // 10, replace=False)
+    slots[pad[0::3]] = 0
+    slots[pad[1::3]] = -5
+    slots[pad[2::3]] = n_slots + 7
+    di = {k_: gu.dev(d[k_]) for k_ in ("q", "k", "v", "g", "beta")}
+    P = torch.from_numpy(pool.copy()).cuda()
+    o = gu.nan_like(torch, (B, 1, H, dv))
+    la.la_decode_step_slots(c, di["q"], di["k"], di["v"], di["g"], di["beta"], P, torch.from_numpy(slots).cuda(),
+                            n_slots, o)
+    torch.cuda.synchronize()
+    P, o = P.cpu().numpy(), o.cpu().numpy()
+    is_live = (slots >= 1) & (slots < n_slots)
+    assert np.all(o[~is_live] == 0)
+    untouched = np.ones(n_slots, dtype=bool)
+    untouched[slots[is_live]] = False
+    np.testing.assert_array_equal(P[untouched], pool[untouched])
+    S_g, o_g, _, _ = _run_decode(c, d, pool[np.where(is_live, slots, 0)], want_codes=False)
+    live = np.nonzero(is_live)[0]
+    np.testing.assert_array_equal(P[slots[live]], S_g[live])
+    np.testing.assert_array_equal(o[live], o_g[live])
+    o_r, _ = oracle.decode_slots(d["q"].f64, d["k"].f64, d["v"].f64, d["g"].f64, d["beta"].f64,
+                                 pool, slots, gate=c.gate, qdq_mode=la.LA_QDQ_INT8_GROUP, group=16)
+    assert gu.err(o, o_r) <= 1e-5
