@@ -45,9 +45,6 @@ struct ChunkBwdPtrs {
     float* dD;            // dDelta, same layout
     float* dSe;           // [B H nch][128][d_v]: dL/d(state after the chunk)
     float* dbp;           // [ntile][B H nch][64]: beta-gradient partial per value tile
-    float* gsc;           // [B H nch][3][64][128]: dQp, dKp, dKd of the products over columns,
-                          // then the Kd terms of the gate gradient (dQp slot) and the rest of
-                          // the cumulative-decay gradient (dKd slot)
 };
 
 // U and Delta of one (sequence, head, chunk, 64 columns) from the chunk's checkpoint.
@@ -386,18 +383,8 @@ __global__ __launch_bounds__(kGT, 1) void chunk_grad_kernel(ChunkParams p, Chunk
         }
     }
     if (t < kChDk) elS[t] = el;
-    float* gsc = a.gsc + ch * 3 * kCh * kChDk;  // [3][64][128]
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int rt = j, kt = w;
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int o = (16 * rt + 4 * g + r) * kChDk + 16 * kt + c;
-            gsc[o] = accQ[j][r];
-            gsc[kCh * kChDk + o] = -accK[j][r];
-            gsc[2 * kCh * kChDk + o] = accD[j][r];
-        }
-    }
+    // accQ, accK and accD stay in registers: the pair sums below take the same tiles (rows of
+    // block j, keys 16 w + c) in the same lanes
     __syncthreads();
 
     // ---- backward of the solve: dA (strictly lower) from dP
@@ -498,15 +485,14 @@ __global__ __launch_bounds__(kGT, 1) void chunk_grad_kernel(ChunkParams p, Chunk
     // ---- the pair sums through A and M (D: the decays)
     //   T1 = sum_{i<r} dA_ri k_i D_ri,  T2 = sum_{i<=r} dM_ri k_i D_ri,
     //   T3 = sum_{s>r} beta_s dA_sr k_s D_sr + sum_{s>=r} dM_sr q_s D_sr,
-    // with the elementwise terms of Kp = k E, Qp = q E, Kd = k F: the outputs dq, dk and the
-    // cumulative-decay gradient dG (into the gsc dKd slot), and beta's pair term k_r T1
-    float* gKd = gsc + 2 * kCh * kChDk;
+    // with the elementwise terms of Kp = k E, Qp = q E, Kd = k F: the outputs dq, dk, the
+    // cumulative-decay gradient dG and the Kd terms of the gate gradient (both held in registers
+    // until the key and query arrays are no longer read), and beta's pair term k_r T1
     const size_t ntok = static_cast<size_t>(p.B) * p.T * p.H;
     const auto rdq = make_rsrc(a.dq + tok0 * kChDk, (ntok - tok0) * kChDk * 4);
     const auto rdk = make_rsrc(a.dk + tok0 * kChDk, (ntok - tok0) * kChDk * 4);
-    auto finish = [&](int row, int key, float t1, float t2, float t3, float dQp, float dKp, float dKd)
-                      __attribute__((always_inline)) {
-        const int o = row * kChDk + key;
+    auto finish = [&](int row, int key, float t1, float t2, float t3, float dQp, float dKp, float dKd, float& dG,
+                      float& kdt) __attribute__((always_inline)) {
         const float G = Gof(row, key), GL = Gof(L - 1, key);
         const float E = exp_acc(G), F = exp_acc(GL - G);
         const float kv = kS[row * 132 + key], qv = qS[row * 132 + key], bt = bS[row];
@@ -518,29 +504,20 @@ __global__ __launch_bounds__(kGT, 1) void chunk_grad_kernel(ChunkParams p, Chunk
             __builtin_amdgcn_raw_buffer_store_b32(
                 __float_as_uint(__builtin_fmaf(E, dKp, __builtin_fmaf(F, dKd, __builtin_fmaf(bt, t1, t3)))), rdk, voff, soff, 0);
         }
-        gKd[o] = __builtin_fmaf(dKp, Kp, dQp * Qp) + __builtin_fmaf(bt * kv, t1, __builtin_fmaf(qv, t2, -kv * t3));
+        dG = __builtin_fmaf(dKp, Kp, dQp * Qp) + __builtin_fmaf(bt * kv, t1, __builtin_fmaf(qv, t2, -kv * t3));
         // Kd = k F, F = e^{G_{L-1} - G}: its term reaches the gates of the tokens after this row
         // only, summed below as a prefix (as the total at row L - 1 less a suffix it would
         // cancel badly under steep decay, where the later rows dominate the total)
-        gsc[o] = dKd * Kd;
+        kdt = dKd * Kd;
     };
     // KDA: every decay factored on 16-token blocks (chunk_factorable), else per-key sums
     __shared__ int flag;
     const bool fact = !KDA || chunk_factorable(Gs, L, &flag);
     // tiles (rt, w) of this wave: rows of block rt, keys 16 w + c
-    float bc[4][4];
+    float bc[4][4], dGr[4][4], kdr[4][4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int rt = j, key = 16 * w + c;
-        // the products over columns for this tile's elements, loaded while the pair sums run
-        float pq[4], pk[4], pd[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int o = (16 * rt + 4 * g + r) * kChDk + key;
-            pq[r] = gsc[o];
-            pk[r] = gsc[kCh * kChDk + o];
-            pd[r] = gKd[o];
-        }
         f4 T1 = {0.0f, 0.0f, 0.0f, 0.0f}, T2 = T1, T3 = T1;
         if (!KDA) {
             // one decay per pair, folded into dA and dM above
@@ -620,7 +597,7 @@ __global__ __launch_bounds__(kGT, 1) void chunk_grad_kernel(ChunkParams p, Chunk
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int row = 16 * rt + 4 * g + r;
-            finish(row, key, T1[r], T2[r], T3[r], pq[r], pk[r], pd[r]);
+            finish(row, key, T1[r], T2[r], T3[r], accQ[j][r], -accK[j][r], accD[j][r], dGr[rt][r], kdr[rt][r]);
             bc[rt][r] = kS[row * 132 + key] * T1[r];
         }
         sched_fence();
@@ -633,21 +610,22 @@ __global__ __launch_bounds__(kGT, 1) void chunk_grad_kernel(ChunkParams p, Chunk
             if (c == 0) bpart[w][16 * rt + 4 * g + r] = v;
         }
 
-    // ---- gate and beta gradients: dG and the Kd terms from gsc into LDS (the key and query
-    // arrays are no longer read)
+    // ---- gate and beta gradients: dG and the Kd terms into LDS over the key and query arrays
+    // (no longer read once every wave is past the barrier)
     float* dGs = big;
     float* cS = big + kTK;
     __syncthreads();
 #pragma unroll
-    for (int idx = t; idx < kCh * kChDk; idx += kGT) {
-        const int r = idx >> 7, kk = idx & 127;
-        float v = gKd[r * kChDk + kk];
-        const float cv = gsc[r * kChDk + kk];
-        // E_L = exp(G_{L-1}) feeds dG_{L-1} as well
-        if (r == L - 1) v += elS[kk] * exp_acc(Gof(L - 1, kk));
-        dGs[r * 132 + kk] = r < L ? v : 0.0f;
-        cS[r * 132 + kk] = r < L ? cv : 0.0f;
-    }
+    for (int rt = 0; rt < 4; rt++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int row = 16 * rt + 4 * g + r, kk = 16 * w + c;
+            float v = dGr[rt][r];
+            // E_L = exp(G_{L-1}) feeds dG_{L-1} as well
+            if (row == L - 1) v += elS[kk] * exp_acc(Gof(L - 1, kk));
+            dGs[row * 132 + kk] = row < L ? v : 0.0f;
+            cS[row * 132 + kk] = row < L ? kdr[rt][r] : 0.0f;
+        }
     __syncthreads();
     if (KDA) {
         // dg_r = sum_{r' >= r} dG_r' + sum_{r' < r} dKd_r' Kd_r' per key (G is the running sum of g)
@@ -705,8 +683,7 @@ ChunkBwdLayout chunk_bwd_layout(const la_config& c) {
     L.dD = L.D + up(units * kCh * c.d_v * sizeof(float));
     L.dSe = L.dD + up(units * kCh * c.d_v * sizeof(float));
     L.dbp = L.dSe + up(units * kChDk * c.d_v * sizeof(float));
-    L.gsc = L.dbp + up(static_cast<size_t>(c.d_v / 64) * units * kCh * sizeof(float));
-    L.total = L.gsc + up(units * 3 * kCh * kChDk * sizeof(float));
+    L.total = L.dbp + up(static_cast<size_t>(c.d_v / 64) * units * kCh * sizeof(float));
     return L;
 }
 
@@ -735,7 +712,7 @@ hipError_t launch_chunk_bwd(const la_config& c, const FwdArgs& fa, const BwdArgs
     ChunkBwdPtrs a{ck, ba.dout, ba.dST, ba.dq, ba.dk, ba.dv, ba.dg, ba.dbeta, ba.dS0, rec,
                    reinterpret_cast<float*>(ws + L.U), reinterpret_cast<float*>(ws + L.D),
                    reinterpret_cast<float*>(ws + L.dD), reinterpret_cast<float*>(ws + L.dSe),
-                   reinterpret_cast<float*>(ws + L.dbp), reinterpret_cast<float*>(ws + L.gsc)};
+                   reinterpret_cast<float*>(ws + L.dbp)};
     const unsigned units = static_cast<unsigned>(c.B) * c.H * p.nch;
     hipLaunchKernelGGL(chunk_recompute_kernel, dim3(units * p.ntile), dim3(kChThreads), 0, s, p, in, a);
     e = hipGetLastError();

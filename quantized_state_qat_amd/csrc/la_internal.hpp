@@ -128,7 +128,7 @@ hipError_t launch_chunk_fwd(const la_config& c, const FwdArgs& a, float* records
 // Backward of the chunk form (chunk_bwd.hip), from checkpoints every 64 tokens (ba.ckpts, or
 // recomputed into the workspace's room when null).  Workspace regions, byte offsets:
 struct ChunkBwdLayout {
-    size_t rec, ckpts, U, D, dD, dSe, dbp, gsc, total;
+    size_t rec, ckpts, U, D, dD, dSe, dbp, total;
 };
 ChunkBwdLayout chunk_bwd_layout(const la_config& c);
 struct BwdArgs;
