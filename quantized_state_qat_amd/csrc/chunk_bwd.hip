@@ -53,7 +53,11 @@ __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams
     __shared__ __align__(16) float P_s[kCh * RecB::PP];
     __shared__ __align__(16) float b_s[kCh];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-    const int tile = blockIdx.x % p.ntile, rest = blockIdx.x / p.ntile;
+    // the value tiles of a chunk 8 workgroups apart: one XCD, so the second reads the chunk's
+    // record from that XCD's L2
+    int tile, rest;
+    chunk_tile_of(blockIdx.x, p.ntile, tile, rest);
+    if (rest >= p.B * p.H * p.nch) return;
     const int cc = rest % p.nch, bh = rest / p.nch;
     const int b = bh / p.H, h = bh - b * p.H;
     const int dv = p.dv, col = tile * 64 + 16 * w + c;
@@ -628,37 +632,66 @@ __global__ __launch_bounds__(kGT, 1) void chunk_grad_kernel(ChunkParams p, Chunk
         }
     __syncthreads();
     if (KDA) {
-        // dg_r = sum_{r' >= r} dG_r' + sum_{r' < r} dKd_r' Kd_r' per key (G is the running sum of g)
-        if (t < kChDk) {
-            float pre = 0.0f;
-            for (int r = 0; r < L; r++) {
-                const float x = cS[r * 132 + t];
-                cS[r * 132 + t] = pre;
-                pre += x;
-            }
-            float acc = 0.0f;
-            for (int r = L - 1; r >= 0; r--) {
-                acc += dGs[r * 132 + t];
-                a.dg[(tok0 + static_cast<size_t>(r) * p.H) * kChDk + t] = acc + cS[r * 132 + t];
-            }
+        // dg_r = sum_{r' >= r} dG_r' + sum_{r' < r} dKd_r' Kd_r' per key (G is the running sum of
+        // g); thread (part, key) takes rows 16 part .. 16 part + 15 after the sums of the other
+        // quarters (rows past the end hold zeros)
+        const int key = t & (kChDk - 1), part = t >> 7;
+        float* qC = big + 2 * kTK;  // [4][128] quarter sums of the Kd terms, then of dG
+        float* qG = qC + 4 * kChDk;  // (over the cumulative gates, no longer read)
+        float sc = 0.0f, sg = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            sc += cS[(16 * part + i) * 132 + key];
+            sg += dGs[(16 * part + i) * 132 + key];
+        }
+        qC[part * kChDk + key] = sc;
+        qG[part * kChDk + key] = sg;
+        __syncthreads();
+        float pre = 0.0f, acc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            pre += q < part ? qC[q * kChDk + key] : 0.0f;
+            acc += q > part ? qG[q * kChDk + key] : 0.0f;
+        }
+        float cp[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            cp[i] = pre;
+            pre += cS[(16 * part + i) * 132 + key];
+        }
+#pragma unroll
+        for (int i = 15; i >= 0; i--) {
+            const int r = 16 * part + i;
+            acc += dGs[r * 132 + key];
+            if (r < L) a.dg[(tok0 + static_cast<size_t>(r) * p.H) * kChDk + key] = acc + cp[i];
         }
     } else {
-        if (t < kCh) {
+        // row sums over the keys by eight threads per row (16 keys each), then across the 64
+        // rows a suffix of dG and an exclusive prefix of the Kd terms in one wave
+        {
+            const int row = t >> 3, part = t & 7;
             float rs = 0.0f, cs = 0.0f;
-            for (int kk = 0; kk < kChDk; kk++) {
-                rs += dGs[t * 132 + kk];
-                cs += cS[t * 132 + kk];
+#pragma unroll
+            for (int j = 0; j < 16; j++) {
+                rs += dGs[row * 132 + 16 * part + j];
+                cs += cS[row * 132 + 16 * part + j];
             }
-            elS[t] = rs;
-            const float inc = wave_prefix_sum(cs);
-            const float exc = __shfl_up(inc, 1, 64);
-            gS[t] = t > 0 ? exc : 0.0f;  // the cumulative gates are no longer read
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) {
+                rs += __shfl_xor(rs, o, 64);
+                cs += __shfl_xor(cs, o, 64);
+            }
+            if (part == 0) {
+                elS[row] = rs;
+                gS[row] = cs;  // the cumulative gates are no longer read
+            }
         }
         __syncthreads();
-        if (t < L) {
-            float acc = 0.0f;
-            for (int r = L - 1; r >= t; r--) acc += elS[r];
-            a.dg[tok0 + static_cast<size_t>(t) * p.H] = acc + gS[t];
+        if (t < kCh) {
+            const float suf = wave_prefix_sum(elS[kCh - 1 - t]);  // lane i: rows 63 - i .. 63
+            const float exc = __shfl_up(wave_prefix_sum(gS[t]), 1, 64);
+            const float dgs = __shfl(suf, kCh - 1 - t, 64);
+            if (t < L) a.dg[tok0 + static_cast<size_t>(t) * p.H] = dgs + (t > 0 ? exc : 0.0f);
         }
     }
     if (t < L) {
@@ -714,7 +747,7 @@ hipError_t launch_chunk_bwd(const la_config& c, const FwdArgs& fa, const BwdArgs
                    reinterpret_cast<float*>(ws + L.dD), reinterpret_cast<float*>(ws + L.dSe),
                    reinterpret_cast<float*>(ws + L.dbp)};
     const unsigned units = static_cast<unsigned>(c.B) * c.H * p.nch;
-    hipLaunchKernelGGL(chunk_recompute_kernel, dim3(units * p.ntile), dim3(kChThreads), 0, s, p, in, a);
+    hipLaunchKernelGGL(chunk_recompute_kernel, dim3(chunk_tile_blocks(units, p.ntile)), dim3(kChThreads), 0, s, p, in, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(chunk_dstate_kernel, dim3(chunk_tile_blocks(c.B * c.H, p.ntile)), dim3(kChThreads), 0, s, p,
