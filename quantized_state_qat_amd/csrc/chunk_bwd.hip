@@ -187,9 +187,14 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
             for (int rt = 0; rt < 4; rt++) DD[rt] = mfma4(RA[RecB::KD + cmap(rt, c) * RecB::PKD + key], ds[m], DD[rt]);
             if ((m & 3) == 3) sched_fence();
         }
+        // (the loaded values pass an empty asm here so that their first use, and the wait for
+        // them, stay after the products above)
         float dO[16];
 #pragma unroll
-        for (int i = 0; i < 16; i++) dO[i] = kmap(i, g) < L ? dOr[i] : 0.0f;
+        for (int i = 0; i < 16; i++) {
+            const float x = opaque_f(dOr[i]);
+            dO[i] = kmap(i, g) < L ? x : 0.0f;
+        }
 #pragma unroll
         for (int m = 0; m < 16; m++) {
             const int tk = kmap(m, g);

@@ -261,6 +261,10 @@ __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
     return x;
 }
+__device__ __forceinline__ float opaque_f(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // e^x to about two ulp for the chunk form's decays, in under ten instructions: x log2(e) as the
 // rounded product t plus its rounding error (exact by an FMA, the TwoProduct of Ogita, Rump and
