@@ -163,7 +163,9 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
         // part 1 of this chunk's record is here, part 2 of the later chunk free: load part 2
         wait_all_mem();
         __syncthreads();
-        lds_dma(RB, recu + static_cast<size_t>(cc) * RecB::SIZE + RecB::PART2, RecB::LDS_SIZE - RecB::PART2);
+        const float* part2 = recu + static_cast<size_t>(cc) * RecB::SIZE + RecB::PART2;
+        constexpr int n2 = RecB::LDS_SIZE - RecB::PART2;
+        static_assert(lds_dma_pieces(n2) <= 32, "part 2 pieces exceed the k-steps");
         // upstream gradient (rows past the end are zeroed where used) and U
         const size_t ntok = static_cast<size_t>(p.B) * p.T * p.H;
         const ChunkRows rdo = chunk_rows(a.dout + tok0 * dv, (ntok - tok0) * dv * 4, p.H * dv, g, col, 4);
@@ -182,6 +184,7 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_dstate_kernel(ChunkParams
         for (int rt = 0; rt < 4; rt++) DD[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int m = 0; m < 32; m++) {
+            if (m < lds_dma_pieces(n2)) lds_dma_piece(RB, part2, n2, m);  // part 2, a piece per k-step
             const int key = kmap(m, g);
 #pragma unroll
             for (int rt = 0; rt < 4; rt++) DD[rt] = mfma4(RA[RecB::KD + cmap(rt, c) * RecB::PKD + key], ds[m], DD[rt]);

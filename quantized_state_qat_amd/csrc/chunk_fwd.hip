@@ -328,15 +328,16 @@ __global__ __launch_bounds__(kChThreads, 1) void chunk_fwd_kernel(ChunkParams p,
                 for (int i = 0; i < 16; i++) vr[i] = rv.ld16(i);
             }
         }
-        // part 2 while the first products run
-        lds_dma(RB, recu + static_cast<size_t>(cc) * RecF::SIZE + RecF::PART2, RecF::SIZE - RecF::PART2);
-
-        // X = Kp S, Y = Qp S
+        // X = Kp S, Y = Qp S, with part 2 of the record loaded a piece per k-step meanwhile
+        const float* part2 = recu + static_cast<size_t>(cc) * RecF::SIZE + RecF::PART2;
+        constexpr int n2 = RecF::SIZE - RecF::PART2;
+        static_assert(lds_dma_pieces(n2) <= 32, "part 2 pieces exceed the k-steps");
         f4 X[4], Y[4];
 #pragma unroll
         for (int rt = 0; rt < 4; rt++) X[rt] = Y[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int m = 0; m < 32; m++) {
+            if (m < lds_dma_pieces(n2)) lds_dma_piece(RB, part2, n2, m);
             const int key = kmap(m, g);
 #pragma unroll
             for (int rt = 0; rt < 4; rt++) {

@@ -92,6 +92,21 @@ __device__ __forceinline__ void lds_dma(float* dst, const float* __restrict__ sr
                                          16, 0, 0);
 }
 
+// lds_dma issued a piece at a time, so that the copy's instructions can sit between other work
+// (a wave that issues the whole copy at once waits for the vector memory queue to take each
+// instruction): piece j of wave w moves 256-float block w + 4 j, the partial block at the end
+// with the piece that reaches it.  Pieces 0 .. lds_dma_pieces(n) - 1 together move what
+// lds_dma(dst, src, n) moves.
+constexpr int lds_dma_pieces(int n) { return (n >> 10) + 1; }
+__device__ __forceinline__ void lds_dma_piece(float* dst, const float* __restrict__ src, int n, int j) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int full = n >> 8, i = w + 4 * j, rem = n & 255;
+    if (i < full)
+        __builtin_amdgcn_global_load_lds(src + (i << 8) + 4 * lane, (lds_void_t*)(dst + (i << 8)), 16, 0, 0);
+    else if (i == full && rem && 4 * lane < rem)
+        __builtin_amdgcn_global_load_lds(src + (full << 8) + 4 * lane, (lds_void_t*)(dst + (full << 8)), 16, 0, 0);
+}
+
 // Rows 0 .. 63 of a [token][128] bf16 or fp32 input (token r at element (tok0 + r H) 128) in
 // 16-byte pieces: thread t of NT holds pieces t + NT u of the chunk (1024 pieces for bf16, 2048
 // for fp32; piece pc is row pc / P, bytes 16 (pc % P) of it, P = 16 or 32 pieces per row).  rows_load
