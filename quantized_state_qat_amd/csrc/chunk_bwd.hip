@@ -86,8 +86,23 @@ __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams
 #pragma unroll
     for (int m = 0; m < 32; m++) s[m] = rs.ldf(m);
     lds_dma(Kp_s, R + RecB::KP, kCh * RecB::PK);
-    lds_dma(P_s, R + RecB::P, kCh * RecB::PP);
-    lds_dma(b_s, R + RecB::BT, kCh);
+    wait_all_mem();
+    __syncthreads();
+    // P and beta a piece per k-step of X = Kp S
+    constexpr int nP = kCh * RecB::PP, nPc = lds_dma_pieces(nP);
+    static_assert(nPc + lds_dma_pieces(kCh) <= 32, "P and beta pieces exceed the k-steps");
+    f4 X[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; rt++) X[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < 32; m++) {
+        if (m < nPc) lds_dma_piece(P_s, R + RecB::P, nP, m);
+        else if (m < nPc + lds_dma_pieces(kCh)) lds_dma_piece(b_s, R + RecB::BT, kCh, m - nPc);
+        const int key = kmap(m, g);
+#pragma unroll
+        for (int rt = 0; rt < 4; rt++) X[rt] = mfma4(Kp_s[cmap(rt, c) * RecB::PK + key], s[m], X[rt]);
+        if ((m & 3) == 3) sched_fence();
+    }
     wait_all_mem();
     __syncthreads();
     float vv[16], bb[16];
@@ -96,16 +111,6 @@ __global__ __launch_bounds__(kChThreads) void chunk_recompute_kernel(ChunkParams
         const int tk = kmap(i, g);
         vv[i] = tk < L ? raw_f32(vr[i], p.qkv_dt) : 0.0f;
         bb[i] = b_s[tk];
-    }
-    f4 X[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; rt++) X[rt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int m = 0; m < 32; m++) {
-        const int key = kmap(m, g);
-#pragma unroll
-        for (int rt = 0; rt < 4; rt++) X[rt] = mfma4(Kp_s[cmap(rt, c) * RecB::PK + key], s[m], X[rt]);
-        if ((m & 3) == 3) sched_fence();
     }
     float u[16], rv[16];
 #pragma unroll
