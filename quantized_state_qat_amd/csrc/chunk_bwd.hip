@@ -403,6 +403,13 @@ __global__ __launch_bounds__(kGT, 1) void chunk_grad_kernel(ChunkParams p, Chunk
     // accQ, accK and accD stay in registers: the pair sums below take the same tiles (rows of
     // block j, keys 16 w + c) in the same lanes
     __syncthreads();
+    // k, q and the gates of the chunk, loaded now and stored to LDS after the solve's backward
+    Rows<kGT> rk, rq, rg;
+    uint32_t gr[1];
+    rows_load(rk, in.k, tok0, p.H, L, p.qkv_dt);
+    rows_load(rq, in.q, tok0, p.H, L, p.qkv_dt);
+    if (KDA) rows_load(rg, in.g, tok0, p.H, L, p.gate_dt);
+    else load_raw<1>(gr, in.g, p.gate_dt, [&](int) { return tok0 + static_cast<size_t>(t < L ? t & 63 : 0) * p.H; });
 
     // ---- backward of the solve: dA (strictly lower) from dP
     {
@@ -464,19 +471,11 @@ __global__ __launch_bounds__(kGT, 1) void chunk_grad_kernel(ChunkParams p, Chunk
     float* kS = big;
     float* qS = big + kTK;
     float* Gs = big + 2 * kTK;
-    {
-        Rows<kGT> rk, rq, rg;
-        rows_load(rk, in.k, tok0, p.H, L, p.qkv_dt);
-        rows_load(rq, in.q, tok0, p.H, L, p.qkv_dt);
-        if (KDA) rows_load(rg, in.g, tok0, p.H, L, p.gate_dt);
-        uint32_t gr[1];
-        if (!KDA) load_raw<1>(gr, in.g, p.gate_dt, [&](int) { return tok0 + static_cast<size_t>(t < L ? t & 63 : 0) * p.H; });
-        __syncthreads();
-        rows_store(kS, rk, L, p.qkv_dt);
-        rows_store(qS, rq, L, p.qkv_dt);
-        if (KDA) rows_store(Gs, rg, L, p.gate_dt);
-        else if (t < kCh) gS[t] = t < L ? raw_f32(gr[0], p.gate_dt) : 0.0f;
-    }
+    __syncthreads();
+    rows_store(kS, rk, L, p.qkv_dt);
+    rows_store(qS, rq, L, p.qkv_dt);
+    if (KDA) rows_store(Gs, rg, L, p.gate_dt);
+    else if (t < kCh) gS[t] = t < L ? raw_f32(gr[0], p.gate_dt) : 0.0f;
     __syncthreads();
     if (KDA) {
         if (t < kChDk) cumsum_cols(Gs, t);
