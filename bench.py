@@ -550,7 +550,9 @@ def bench_varlen(steps=3, warmup=1):
                                              "the INT8 codec is not counted; the longest sequence sets the time"),
         "issue_floor": _issue_roofline(12.0, w.d_k * w.d_v * w.H * T, t, "token step (4) and INT8 codec (8) per "
                                                                        "element and token"),
-        "issue_floor_bwd": _issue_roofline(33.0, w.d_k * w.d_v * w.H * T, t_b, "recompute twice (24) and adjoint (9)"),
+        "issue_floor_bwd": _issue_roofline(23.0, w.d_k * w.d_v * w.H * T, t_b,
+                                           "recompute with the codec once (12), decode of the kept codes (2) and "
+                                           "adjoint (9)"),
     }
 
 
@@ -602,9 +604,10 @@ def bench_wht_fwdbwd(steps=2, warmup=1):
         "roofline_bwd": _fp32_roofline(22.0 * unit, t_b, "backward only (recompute + adjoint)"),
         "issue_floor_fwd": _issue_roofline(12.0, unit, t_f, "decay, projections, update (4) and the INT8 codec (8) "
                                                             "per element and token (the state is carried rotated)"),
-        "issue_floor_bwd": _issue_roofline(33.0, unit, t_b, "the forward token step with its codec twice (recompute "
-                                                            "of the chunk, then of each group of four: 24) and the "
-                                                            "adjoint (9) per element and token"),
+        "issue_floor_bwd": _issue_roofline(23.0, unit, t_b, "the forward token step with its codec once (recompute "
+                                                            "of the chunk keeping every token's codes: 12), the "
+                                                            "decode of the kept codes (2) and the adjoint (9) per "
+                                                            "element and token"),
     }
 
 

@@ -8,6 +8,11 @@
 //   phase B  for each group of four tokens, last to first: recompute it from the stored
 //            state, keeping the state entering every token in registers, then walk it
 //            backwards with the adjoint lambda = dL/dS in registers.
+// When every token is a rounding point of the INT8 codec (bwd_tok_coded), each carried state
+// is its codes times its group scales: phase A runs the whole chunk and keeps every token's
+// codes (fp16, exact) and scales in the workspace and its u and delta in LDS, and phase B
+// walks the chunk's tokens last to first decoding the state entering each (the codes of the
+// token before, loaded one token ahead) with no recompute.
 // A block's token records (la_tok.hpp) are published once per pass by its eight waves (wave w:
 // token w of the block), and the next block's inputs are fetched while a block is processed.
 // Per token (S~ = diag(a) S, u = S~^T k, S' = S~ + ku delta^T, o = S'^T qq; the quantizer
@@ -104,7 +109,7 @@ __device__ __forceinline__ void tok_adjoint(const float (&st)[S::R], float u, fl
     }
 }
 
-template <int DK, int QMODE, int G, bool HAD, bool KDA>
+template <int DK, int QMODE, int G, bool HAD, bool KDA, bool CODED>
 __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdArgs a) {
     using S = TokShape<DK, QMODE, G>;
     constexpr int R = S::R, TC = S::TC;
@@ -116,6 +121,10 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     __shared__ float2 red[2][kTokWaves][TC];
     __shared__ TokQdqShared<S> qsh;
     __shared__ float tile[HAD ? 2 * DK * TC : 1];  // tok_rotate's two tiles
+    // the coded walk (bwd_tok_coded: every token an INT8 rounding point): u and delta of the
+    // chunk's tokens
+    static_assert(!CODED || (QMODE == LA_QDQ_INT8_GROUP && !RQ && R % 2 == 0 && R <= 8), "coded walk");
+    __shared__ float2 ud[CODED ? kCodedMaxChunk : 1][TC];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -149,8 +158,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
         }
     }
     const int nck = (T + C - 1) / C;
-    const int nsub = (C + kSubTok - 1) / kSubTok;
-    float* wsS = a.ws_states + wg * static_cast<size_t>(nsub) * DK * TC;
+    float* wsS = a.ws_states + wg * bwd_tok_ws_floats(C, DK, TC, G, CODED);
     const TokInputs in{a.q, a.k, a.v, a.g, a.beta, a.dout};
 
     float lam[R];
@@ -184,90 +192,220 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     for (int c = nck - 1; c >= 0; c--) {
         const int t0 = c * C, t1 = min(T, t0 + C);
         const int nb = nblocks(c);
-        const int last_sub = ((t1 - t0 - 1) / kSubTok) * kSubTok;  // chunk offset of the last stored state
-
-        // ---------------- phase A: advance through the chunk, storing the state entering
-        // every fourth token (the chunk's first state is its checkpoint)
-        {
-            float s[R];
-            const float* ck = a.ckpts + (ck0 + c) * DK * DV;
+        if constexpr (CODED) {
+            constexpr int NH = R / 2;                   // fp16 code pairs per lane and token
+            constexpr int NSC = (64 / G) * R;           // scales per wave and token
+            const int tid = threadIdx.x, L = t1 - t0;
+            uint32_t* wcode = reinterpret_cast<uint32_t*>(wsS);  // [C][kTokThreads][NH]
+            float* wscl = wsS + static_cast<size_t>(C) * kTokThreads * NH;  // [C][kTokWaves][NSC]
+            // the codes and scales of the state after chunk token `off`
+            auto code_ptr = [&](int off) { return wcode + (static_cast<size_t>(off) * kTokThreads + tid) * NH; };
+            auto scale_ptr = [&](int off) {
+                return wscl + (static_cast<size_t>(off) * kTokWaves + w) * NSC + (lane / G) * R;
+            };
+            // the checkpoint: the state entering the chunk's first token
+            float ckr[R];
+            {
+                const float* ck = a.ckpts + (ck0 + c) * DK * DV;
 #pragma unroll
-            for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
-#pragma unroll 1
-            for (int j = 0; j < nb; j++) {
-                const int tb = t0 + kBlkTok * j;
-                const int nt = min(kBlkTok, t1 - tb);
-                if (j + 1 < nb) publish(nt, c, j + 1);
-                else publish(nt, c, j);  // phase B starts with the same block
-#pragma unroll 1
-                for (int i = 0; i < nt; i++) {
-                    const int off = kBlkTok * j + i;  // token offset in the chunk
-                    if ((off % kSubTok) == 0 && off > 0) {
-                        float* dst = wsS + static_cast<size_t>(off / kSubTok) * DK * TC;
+                for (int m = 0; m < R; m++) ckr[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
+            }
+            // ---------------- phase A: the whole chunk, keeping every token's u and delta
+            // and every rounded state but the last
+            {
+                float s[R];
 #pragma unroll
-                        for (int m = 0; m < R; m++) dst[(r0 + m) * TC + lane % TC] = s[m];
+                for (int m = 0; m < R; m++) s[m] = ckr[m];
+                const int wrow = (lane / G) * R + reduce_scatter_row<R, G>(lane);
+                const bool wsc = (lane & (G / R - 1)) == 0;  // one lane of each (row, group) stores its scale
+#pragma unroll 1
+                for (int j = 0; j < nb; j++) {
+                    const int tb = t0 + kBlkTok * j;
+                    const int nt = min(kBlkTok, t1 - tb);
+                    if (j + 1 < nb) publish(nt, c, j + 1);
+                    else publish(nt, c, j);  // phase B starts with the same block
+#pragma unroll 1
+                    for (int i = 0; i < nt; i++) {
+                        const int off = kBlkTok * j + i;
+                        TokOps<S, KDA> op;
+                        tok_read<S, KDA, true>(op, ring, i, w, lane);
+                        float u, dl, o;
+                        tok_step<S, KDA, RC>(s, op, red[rp], w, lane, u, dl, o);
+                        rp ^= 1;
+                        if (w == 0 && lane < TC) ud[off][lane] = make_float2(u, dl);
+                        if (off + 1 < L) {
+                            uint32_t hc[NH];
+                            float scl;
+                            tok_int8<R, G, true>(s, qsh.scr[w], lane, hc, &scl);
+                            uint32_t* dst = code_ptr(off);
+#pragma unroll
+                            for (int q = 0; q < NH; q++) dst[q] = hc[q];
+                            if (wsc) wscl[(static_cast<size_t>(off) * kTokWaves + w) * NSC + wrow] = scl;
+                        }
                     }
-                    // the last group of the chunk is recomputed in phase B from its stored state
-                    if (off >= last_sub) break;
-                    TokOps<S, KDA> op;
-                    tok_read<S, KDA, true>(op, ring, i, w, lane);
-                    float u, dl, o;
-                    const int t = tb + i;
-                    const bool qpt = QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1);
-                    tok_step<S, KDA, RC>(s, op, red[rp], w, lane, u, dl, o, p.replay && !qpt);
-                    rp ^= 1;
-                    if (qpt) tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
                 }
             }
-        }
-        // ---------------- phase B: per group of four tokens, last first: recompute it keeping
-        // every entering state, then the adjoint
-#pragma unroll 1
-        for (int j = nb - 1; j >= 0; j--) {
-            const int tb = t0 + kBlkTok * j;
-            const int nt = min(kBlkTok, t1 - tb);
-            if (j > 0) publish(nt, c, j - 1);
-            else publish(nt, c - 1, 0);
-#pragma unroll 1
-            for (int hh = (nt - 1) / kSubTok; hh >= 0; hh--) {
-                const int i0 = kSubTok * hh, n = min(kSubTok, nt - i0);
-                float s[R];
-                if (j == 0 && hh == 0) {
-                    const float* ck = a.ckpts + (ck0 + c) * DK * DV;
+            // every store of phase A has completed before any lane reads it back
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            // ---------------- phase B: tokens last to first, the entering state decoded from
+            // the codes of the token before (the checkpoint for the chunk's first token), loaded
+            // one token ahead into the other of two register sets: the sets alternate by token
+            // (the loop takes two tokens per pass), so that no loaded value is copied between
+            // iterations and the loads stay in flight over the adjoint.  Loads are unconditional (a clamped index reads codes that
+            // are not used), which keeps the token free of branches.
+            struct Entering {
+                uint32_t hc[NH];  // codes
+                float sc[R];      // their scales
+            };
+            auto load_entering = [&](int k, Entering& e) __attribute__((always_inline)) {  // after token k
+                const uint32_t* src = code_ptr(k);
 #pragma unroll
-                    for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
+                for (int q = 0; q < NH; q++) e.hc[q] = src[q];
+                if constexpr (R % 4 == 0) {
+                    const float4* sp = reinterpret_cast<const float4*>(scale_ptr(k));
+#pragma unroll
+                    for (int m = 0; m < R / 4; m++) {
+                        const float4 x = sp[m];
+                        e.sc[4 * m] = x.x;
+                        e.sc[4 * m + 1] = x.y;
+                        e.sc[4 * m + 2] = x.z;
+                        e.sc[4 * m + 3] = x.w;
+                    }
                 } else {
-                    const float* src = wsS + static_cast<size_t>(kBlkTok / kSubTok * j + hh) * DK * TC;
+                    const float2* sp = reinterpret_cast<const float2*>(scale_ptr(k));
 #pragma unroll
-                    for (int m = 0; m < R; m++) s[m] = src[(r0 + m) * TC + lane % TC];
-                }
-                float st[kSubTok][R];
-                float uu[kSubTok], dd[kSubTok];
-#pragma unroll
-                for (int i = 0; i < kSubTok; i++) {
-                    if (i < n) {
-#pragma unroll
-                        for (int m = 0; m < R; m++) st[i][m] = s[m];
-                        TokOps<S, KDA> op;
-                        tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
-                        float o;
-                        const int t = tb + i0 + i;
-                        const bool qpt = QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1);
-                        tok_step<S, KDA, RC>(s, op, red[rp], w, lane, uu[i], dd[i], o, p.replay && !qpt);
-                        rp ^= 1;
-                        if (qpt && i + 1 < n) tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
+                    for (int m = 0; m < R / 2; m++) {
+                        const float2 x = sp[m];
+                        e.sc[2 * m] = x.x;
+                        e.sc[2 * m + 1] = x.y;
                     }
                 }
+            };
+            auto token = [&](int j, int i, const Entering& cur, Entering& nxt) __attribute__((always_inline)) {
+                const int off = kBlkTok * j + i, tb = t0 + kBlkTok * j;
+                load_entering(max(off - 2, 0), nxt);
+                float st[R];
 #pragma unroll
-                for (int i = kSubTok - 1; i >= 0; i--) {
-                    if (i < n) {
+                for (int q = 0; q < NH; q++) {
+                    const auto h = __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), cur.hc[q]);
+                    st[2 * q] = off == 0 ? ckr[2 * q] : static_cast<float>(h[0]) * cur.sc[2 * q];
+                    st[2 * q + 1] = off == 0 ? ckr[2 * q + 1] : static_cast<float>(h[1]) * cur.sc[2 * q + 1];
+                }
+                TokOps<S, KDA> op;
+                tok_read<S, KDA, true>(op, ring, i, w, lane);
+                const float2 x = ud[off][lane % TC];
+                const size_t tok = tok0 + static_cast<size_t>(tb + i) * H;
+                float* part = a.ws_part + (static_cast<size_t>(blk) * ntok + tok) * PW;
+                tok_adjoint<S, KDA, RC>(st, x.x, x.y, op, ring.ga[i], lam, red[rp], w, lane, part,
+                                        a.dv + tok * DV + col, w == i);
+                rp ^= 1;
+            };
+            Entering e0, e1;
+            load_entering(max(L - 2, 0), e0);
+#pragma unroll 1
+            for (int j = nb - 1; j >= 0; j--) {
+                const int nt = min(kBlkTok, t1 - (t0 + kBlkTok * j));
+                if (j > 0) publish(nt, c, j - 1);
+                else publish(nt, c - 1, 0);
+                int i = nt - 1;
+                if (nt & 1) {  // (only the chunk's last block can hold an odd number of tokens)
+                    token(j, i, e0, e1);
+                    e0 = e1;
+                    i--;
+                }
+#pragma unroll 1
+                for (; i >= 1; i -= 2) {
+                    token(j, i, e0, e1);
+                    token(j, i - 1, e1, e0);
+                }
+            }
+        } else {
+            const int last_sub = ((t1 - t0 - 1) / kSubTok) * kSubTok;  // chunk offset of the last stored state
+
+            // ---------------- phase A: advance through the chunk, storing the state entering
+            // every fourth token (the chunk's first state is its checkpoint)
+            {
+                float s[R];
+                const float* ck = a.ckpts + (ck0 + c) * DK * DV;
+#pragma unroll
+                for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
+#pragma unroll 1
+                for (int j = 0; j < nb; j++) {
+                    const int tb = t0 + kBlkTok * j;
+                    const int nt = min(kBlkTok, t1 - tb);
+                    if (j + 1 < nb) publish(nt, c, j + 1);
+                    else publish(nt, c, j);  // phase B starts with the same block
+#pragma unroll 1
+                    for (int i = 0; i < nt; i++) {
+                        const int off = kBlkTok * j + i;  // token offset in the chunk
+                        if ((off % kSubTok) == 0 && off > 0) {
+                            float* dst = wsS + static_cast<size_t>(off / kSubTok) * DK * TC;
+#pragma unroll
+                            for (int m = 0; m < R; m++) dst[(r0 + m) * TC + lane % TC] = s[m];
+                        }
+                        // the last group of the chunk is recomputed in phase B from its stored state
+                        if (off >= last_sub) break;
                         TokOps<S, KDA> op;
-                        tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
-                        const size_t tok = tok0 + static_cast<size_t>(tb + i0 + i) * H;
-                        float* part = a.ws_part + (static_cast<size_t>(blk) * ntok + tok) * PW;
-                        tok_adjoint<S, KDA, RC>(st[i], uu[i], dd[i], op, ring.ga[i0 + i], lam, red[rp], w, lane,
-                                                  part, a.dv + tok * DV + col, w == i0 + i);
+                        tok_read<S, KDA, true>(op, ring, i, w, lane);
+                        float u, dl, o;
+                        const int t = tb + i;
+                        const bool qpt = QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1);
+                        tok_step<S, KDA, RC>(s, op, red[rp], w, lane, u, dl, o, p.replay && !qpt);
                         rp ^= 1;
+                        if (qpt) tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
+                    }
+                }
+            }
+            // ---------------- phase B: per group of four tokens, last first: recompute it keeping
+            // every entering state, then the adjoint
+#pragma unroll 1
+            for (int j = nb - 1; j >= 0; j--) {
+                const int tb = t0 + kBlkTok * j;
+                const int nt = min(kBlkTok, t1 - tb);
+                if (j > 0) publish(nt, c, j - 1);
+                else publish(nt, c - 1, 0);
+#pragma unroll 1
+                for (int hh = (nt - 1) / kSubTok; hh >= 0; hh--) {
+                    const int i0 = kSubTok * hh, n = min(kSubTok, nt - i0);
+                    float s[R];
+                    if (j == 0 && hh == 0) {
+                        const float* ck = a.ckpts + (ck0 + c) * DK * DV;
+#pragma unroll
+                        for (int m = 0; m < R; m++) s[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
+                    } else {
+                        const float* src = wsS + static_cast<size_t>(kBlkTok / kSubTok * j + hh) * DK * TC;
+#pragma unroll
+                        for (int m = 0; m < R; m++) s[m] = src[(r0 + m) * TC + lane % TC];
+                    }
+                    float st[kSubTok][R];
+                    float uu[kSubTok], dd[kSubTok];
+#pragma unroll
+                    for (int i = 0; i < kSubTok; i++) {
+                        if (i < n) {
+#pragma unroll
+                            for (int m = 0; m < R; m++) st[i][m] = s[m];
+                            TokOps<S, KDA> op;
+                            tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
+                            float o;
+                            const int t = tb + i0 + i;
+                            const bool qpt = QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1);
+                            tok_step<S, KDA, RC>(s, op, red[rp], w, lane, uu[i], dd[i], o, p.replay && !qpt);
+                            rp ^= 1;
+                            if (qpt && i + 1 < n) tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
+                        }
+                    }
+#pragma unroll
+                    for (int i = kSubTok - 1; i >= 0; i--) {
+                        if (i < n) {
+                            TokOps<S, KDA> op;
+                            tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
+                            const size_t tok = tok0 + static_cast<size_t>(tb + i0 + i) * H;
+                            float* part = a.ws_part + (static_cast<size_t>(blk) * ntok + tok) * PW;
+                            tok_adjoint<S, KDA, RC>(st[i], uu[i], dd[i], op, ring.ga[i0 + i], lam, red[rp], w, lane,
+                                                      part, a.dv + tok * DV + col, w == i0 + i);
+                            rp ^= 1;
+                        }
                     }
                 }
             }
@@ -407,7 +545,12 @@ hipError_t launch_bwd_t(const la_config& c, const BwdArgs& a, hipStream_t s) {
     }
     constexpr int TC = tok_tile_cols(DK, QMODE, G);
     dim3 grid(c.d_v / TC, c.H, c.B);
-    hipLaunchKernelGGL((bwd_tok_kernel<DK, QMODE, G, HAD, KDA>), grid, dim3(kTokThreads), 0, s, p, a);
+    constexpr bool CODED_OK = QMODE == LA_QDQ_INT8_GROUP && !(HAD && KDA) && tok_rows_per_lane(DK, TC) % 2 == 0 &&
+                              tok_rows_per_lane(DK, TC) <= 8;
+    if (CODED_OK && bwd_tok_coded(c))
+        hipLaunchKernelGGL((bwd_tok_kernel<DK, QMODE, G, HAD, KDA, CODED_OK>), grid, dim3(kTokThreads), 0, s, p, a);
+    else
+        hipLaunchKernelGGL((bwd_tok_kernel<DK, QMODE, G, HAD, KDA, false>), grid, dim3(kTokThreads), 0, s, p, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t ntok = static_cast<size_t>(p.ntok);

@@ -128,11 +128,10 @@ WsLayout ws_layout(const la_config& c) {
         return L;
     }
     // the backward runs in the token layout: tiles of tok_tile_cols value columns
-    const size_t tc = static_cast<size_t>(la::tok_tile_cols(c.d_k, c.qdq, c.group));
     const size_t tiles = static_cast<size_t>(la::tok_tiles(c));
     const size_t nwg = static_cast<size_t>(c.B) * c.H * tiles;
     L.states = 0;
-    L.part = round_up(nwg * static_cast<size_t>(la::n_sub_states(c)) * c.d_k * tc * sizeof(float));
+    L.part = round_up(nwg * la::bwd_tok_ws_floats(c) * sizeof(float));
     L.ckpts = L.part + round_up(tiles * c.B * c.T * c.H * la::part_width(c) * sizeof(float));
     L.total = L.ckpts + round_up(static_cast<size_t>(c.B) * c.H * la::n_ckpts(c) * c.d_k * c.d_v * sizeof(float));
     return L;
@@ -142,11 +141,10 @@ WsLayout ws_layout(const la_config& c) {
 // row sums per value tile and packed token-head, checkpoints in the packed slot layout.
 WsLayout ws_layout_varlen(const la_config& c) {
     WsLayout L;
-    const size_t tc = static_cast<size_t>(la::tok_tile_cols(c.d_k, c.qdq, c.group));
     const size_t tiles = static_cast<size_t>(la::tok_tiles(c));
     const size_t nwg = static_cast<size_t>(c.B) * c.H * tiles;
     L.states = 0;
-    L.part = round_up(nwg * static_cast<size_t>(la::n_sub_states(c)) * c.d_k * tc * sizeof(float));
+    L.part = round_up(nwg * la::bwd_tok_ws_floats(c) * sizeof(float));
     L.ckpts = L.part + round_up(tiles * static_cast<size_t>(c.T) * c.H * la::part_width(c) * sizeof(float));
     L.total = L.ckpts + round_up(static_cast<size_t>(c.H) * la::varlen_ckpt_slots(c) * c.d_k * c.d_v * sizeof(float));
     return L;

@@ -101,8 +101,29 @@ inline int n_ckpts(const la_config& c) {
 // Backward partial sums per (value tile, token): two d_k rows, the gate term (KDA: one per
 // key row; GDN: one per wave of the eight-wave token layout) and beta.
 inline int part_width(const la_config& c) { return 2 * c.d_k + (c.gate == LA_GATE_KEY ? c.d_k : 8) + 1; }
-// Backward states per workgroup: the state entering every fourth token of a chunk.
-inline int n_sub_states(const la_config& c) { return (c.ckpt_interval + 3) / 4; }
+// Token backward with every token a rounding point of the INT8 codec (no replay windows, no
+// rotation around the rounding points, checkpoints at most kCodedMaxChunk tokens apart, an
+// even number of key rows per lane, at most eight): each rounded state is its codes times its
+// group scales,
+// so the chunk's recompute keeps the codes (as fp16) and the scales of every token, and the
+// adjoint decodes the states instead of recomputing the chunk a second time.
+constexpr int kCodedMaxChunk = 64;
+constexpr int tok_rows_per_lane(int dk, int tc) { return (dk / 8) / (64 / tc); }
+inline bool bwd_tok_coded(const la_config& c) {
+    const int tc = tok_tile_cols(c.d_k, c.qdq, c.group);
+    return c.qdq == LA_QDQ_INT8_GROUP && c.qdq_interval == 1 && !c.replay && !(c.hadamard && c.gate == LA_GATE_KEY) &&
+           c.ckpt_interval >= 1 && c.ckpt_interval <= kCodedMaxChunk && tok_rows_per_lane(c.d_k, tc) % 2 == 0 &&
+           tok_rows_per_lane(c.d_k, tc) <= 8;
+}
+// Floats of one workgroup's backward states for chunks of C tokens: coded, per token the
+// d_k x tc codes as fp16 and the d_k tc / g scales; else the state entering every fourth token.
+constexpr size_t bwd_tok_ws_floats(int C, int dk, int tc, int g, bool coded) {
+    return coded ? static_cast<size_t>(C) * (static_cast<size_t>(dk) * tc / 2 + static_cast<size_t>(dk) * tc / g)
+                 : static_cast<size_t>((C + 3) / 4) * dk * tc;
+}
+inline size_t bwd_tok_ws_floats(const la_config& c) {
+    return bwd_tok_ws_floats(c.ckpt_interval, c.d_k, tok_tile_cols(c.d_k, c.qdq, c.group), c.group, bwd_tok_coded(c));
+}
 
 hipError_t launch_decode(const la_config& c, const DecodeArgs& a, hipStream_t s);
 // The forward kernel that serves c: c.kernel if it is not LA_KERNEL_AUTO and that kernel

@@ -440,8 +440,12 @@ __device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>&
 // x R float2 per wave); each element is then coded by int8_code_fast.  A group whose scale is
 // below 2^-100 takes the IEEE division and the clamp instead (the whole wave, when any lane
 // has one).
-template <int R, int G>
-__device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
+// With KEEP the codes are also returned (hc: pairs of rows as fp16, which holds every code and
+// the sign of a zero code exactly, so that float(code) * scale gives back the rounded state bit
+// for bit) with the scale of this lane's (row, group) (sc_out).
+template <int R, int G, bool KEEP = false>
+__device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane, uint32_t* hc = nullptr,
+                                         float* sc_out = nullptr) {
     uint32_t x[R];
 #pragma unroll
     for (int m = 0; m < R; m++) x[m] = __float_as_uint(s[m]) & 0x7FFFFFFFu;
@@ -449,6 +453,7 @@ __device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
     const int row = reduce_scatter_row<R, G>(lane), grp = lane / G;
     float sc, y;
     const bool tiny_l = !int8_scale_recip(mx, sc, y);
+    if constexpr (KEEP) *sc_out = sc;
     scr[grp * R + row] = make_float2(sc, y);
     const bool tiny = __any(tiny_l);
     __builtin_amdgcn_wave_barrier();
@@ -456,12 +461,20 @@ __device__ __forceinline__ void tok_int8(float (&s)[R], float2* scr, int lane) {
     float2 sy[R];
 #pragma unroll
     for (int m = 0; m < R; m++) sy[m] = scr[grp * R + m];
+    float cd[R];
     if (!tiny) {
 #pragma unroll
-        for (int m = 0; m < R; m++) s[m] = int8_code_fast(s[m], sy[m].x, sy[m].y) * sy[m].x;
+        for (int m = 0; m < R; m++) cd[m] = int8_code_fast(s[m], sy[m].x, sy[m].y);
     } else {
 #pragma unroll
-        for (int m = 0; m < R; m++) s[m] = int8_code(s[m], sy[m].x) * sy[m].x;
+        for (int m = 0; m < R; m++) cd[m] = int8_code(s[m], sy[m].x);
+    }
+#pragma unroll
+    for (int m = 0; m < R; m++) s[m] = cd[m] * sy[m].x;
+    if constexpr (KEEP) {
+        static_assert(R % 2 == 0, "codes kept in row pairs");
+#pragma unroll
+        for (int m = 0; m < R; m += 2) hc[m / 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(cd[m], cd[m + 1]));
     }
     __builtin_amdgcn_wave_barrier();  // scr is rewritten only after every lane has read it
 }

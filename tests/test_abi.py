@@ -128,15 +128,20 @@ def test_decode_slots_checks():
 def test_bwd_workspace_and_checks():
     c = cfg(T=256, ckpt_interval=64)
     n = la.la_bwd_workspace_bytes(c)
-    # INT8 groups of 32: the backward's tiles are 32 value columns wide (4 per head).  Per
-    # workgroup (B x H x tiles) the state entering every fourth token of a chunk; per tile and
-    # token the partial sums (two d_k rows, eight GDN gate terms, beta); room for recomputed
-    # checkpoints
+    # INT8 groups of 32 after every token: the backward's tiles are 32 value columns wide (4 per
+    # head).  Per workgroup (B x H x tiles) and chunk token the rounded state as fp16 codes and
+    # one scale per (row, group); per tile and token the partial sums (two d_k rows, eight GDN
+    # gate terms, beta); room for recomputed checkpoints
     nwg = 2 * 2 * 4
-    states = nwg * (64 // 4) * 128 * 32 * 4
+    states = nwg * 64 * (128 * 32 * 2 + 128 * 4)
     part = 4 * 2 * 256 * 2 * (2 * 128 + 8 + 1) * 4
     ck = 2 * 2 * 4 * 128 * 128 * 4
     assert n >= states + part + ck and n < states + part + ck + 3 * 256
+    # rounding every second token: the state entering every fourth token of a chunk
+    c2 = cfg(T=256, ckpt_interval=64, qdq_interval=2)
+    n2 = la.la_bwd_workspace_bytes(c2)
+    states2 = nwg * (64 // 4) * 128 * 32 * 4
+    assert n2 >= states2 + part + ck and n2 < states2 + part + ck + 3 * 256
     c64 = cfg(T=256, ckpt_interval=64, group=64)   # groups of 64: tiles of 64 columns
     n64 = la.la_bwd_workspace_bytes(c64)
     states64 = 2 * 2 * 2 * (64 // 4) * 128 * 64 * 4
