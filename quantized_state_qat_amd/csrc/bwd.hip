@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     __shared__ float tile[HAD ? 2 * DK * TC : 1];  // tok_rotate's two tiles
     // the coded walk (bwd_tok_coded: every token an INT8 rounding point): u and delta of the
     // chunk's tokens
-    static_assert(!CODED || (QMODE == LA_QDQ_INT8_GROUP && !RQ && R % 2 == 0 && R <= 8), "coded walk");
+    static_assert(!CODED || (QMODE == LA_QDQ_INT8_GROUP && !RQ && R % 2 == 0), "coded walk");
     __shared__ float2 ud[CODED ? kCodedMaxChunk : 1][TC];
 
     const int lane = threadIdx.x & 63;
@@ -545,8 +545,7 @@ hipError_t launch_bwd_t(const la_config& c, const BwdArgs& a, hipStream_t s) {
     }
     constexpr int TC = tok_tile_cols(DK, QMODE, G);
     dim3 grid(c.d_v / TC, c.H, c.B);
-    constexpr bool CODED_OK = QMODE == LA_QDQ_INT8_GROUP && !(HAD && KDA) && tok_rows_per_lane(DK, TC) % 2 == 0 &&
-                              tok_rows_per_lane(DK, TC) <= 8;
+    constexpr bool CODED_OK = QMODE == LA_QDQ_INT8_GROUP && !(HAD && KDA) && tok_rows_per_lane(DK, TC) % 2 == 0;
     if (CODED_OK && bwd_tok_coded(c))
         hipLaunchKernelGGL((bwd_tok_kernel<DK, QMODE, G, HAD, KDA, CODED_OK>), grid, dim3(kTokThreads), 0, s, p, a);
     else

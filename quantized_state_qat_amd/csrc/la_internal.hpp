@@ -103,8 +103,7 @@ inline int n_ckpts(const la_config& c) {
 inline int part_width(const la_config& c) { return 2 * c.d_k + (c.gate == LA_GATE_KEY ? c.d_k : 8) + 1; }
 // Token backward with every token a rounding point of the INT8 codec (no replay windows, no
 // rotation around the rounding points, checkpoints at most kCodedMaxChunk tokens apart, an
-// even number of key rows per lane, at most eight): each rounded state is its codes times its
-// group scales,
+// even number of key rows per lane): each rounded state is its codes times its group scales,
 // so the chunk's recompute keeps the codes (as fp16) and the scales of every token, and the
 // adjoint decodes the states instead of recomputing the chunk a second time.
 constexpr int kCodedMaxChunk = 64;
@@ -112,8 +111,7 @@ constexpr int tok_rows_per_lane(int dk, int tc) { return (dk / 8) / (64 / tc); }
 inline bool bwd_tok_coded(const la_config& c) {
     const int tc = tok_tile_cols(c.d_k, c.qdq, c.group);
     return c.qdq == LA_QDQ_INT8_GROUP && c.qdq_interval == 1 && !c.replay && !(c.hadamard && c.gate == LA_GATE_KEY) &&
-           c.ckpt_interval >= 1 && c.ckpt_interval <= kCodedMaxChunk && tok_rows_per_lane(c.d_k, tc) % 2 == 0 &&
-           tok_rows_per_lane(c.d_k, tc) <= 8;
+           c.ckpt_interval >= 1 && c.ckpt_interval <= kCodedMaxChunk && tok_rows_per_lane(c.d_k, tc) % 2 == 0;
 }
 // Floats of one workgroup's backward states for chunks of C tokens: coded, per token the
 // d_k x tc codes as fp16 and the d_k tc / g scales; else the state entering every fourth token.

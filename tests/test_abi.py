@@ -144,7 +144,7 @@ def test_bwd_workspace_and_checks():
     assert n2 >= states2 + part + ck and n2 < states2 + part + ck + 3 * 256
     c64 = cfg(T=256, ckpt_interval=64, group=64)   # groups of 64: tiles of 64 columns
     n64 = la.la_bwd_workspace_bytes(c64)
-    states64 = 2 * 2 * 2 * (64 // 4) * 128 * 64 * 4
+    states64 = 2 * 2 * 2 * 64 * (128 * 64 * 2 + 128 * 4)
     part64 = 2 * 2 * 256 * 2 * (2 * 128 + 8 + 1) * 4
     assert n64 >= states64 + part64 + ck and n64 < states64 + part64 + ck + 3 * 256
     assert la.la_bwd_workspace_bytes(cfg(ckpt_interval=0)) == 0
