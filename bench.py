@@ -378,6 +378,25 @@ def bench_kda_tok(steps=3, warmup=1):
     stream = torch.cuda.current_stream()
     t = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
                                                 ST, stream=stream), steps, warmup, stream)
+    # the training pair of the same workload: forward with 64-token checkpoints, then the
+    # straight-through backward from them (upstream gradient ~ N(0, 1))
+    c.ckpt_interval = 64
+    ck = torch.empty((w.B, w.H, (w.T + 63) // 64, w.d_k, w.d_v), device="cuda")
+    dout = torch.randn((w.B, w.T, w.H, w.d_v), device="cuda", generator=torch.Generator("cuda").manual_seed(3))
+    grads = [torch.empty((w.B, w.T, w.H, w.d_k), device="cuda") for _ in range(3)]
+    dv = torch.empty((w.B, w.T, w.H, w.d_v), device="cuda")
+    dbeta = torch.empty((w.B, w.T, w.H), device="cuda")
+    dS0 = torch.empty((w.B, w.H, w.d_k, w.d_v), device="cuda")
+    nbytes = la.la_bwd_workspace_bytes(c)
+    ws = torch.empty((nbytes + 255) // 4, dtype=torch.float32, device="cuda")
+    t_f = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
+                                                  ST, ck, stream=stream), steps, warmup, stream)
+    t_b = _time_calls(lambda: la.la_recurrent_bwd_ste(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, ck,
+                                                      dout, None, grads[0], grads[1], dv, grads[2], dbeta, dS0, ws,
+                                                      nbytes, stream=stream), steps, warmup, stream)
+    kernel_bwd = la.la_bwd_kernel_name(c)
+    del ws, grads, dv, dout, ck
+    c.ckpt_interval = 0
     c.hadamard = 1
     t_h = _time_calls(lambda: la.la_recurrent_fwd(c, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], None, o,
                                                   ST, stream=stream), steps, warmup, stream)
@@ -390,6 +409,13 @@ def bench_kda_tok(steps=3, warmup=1):
         "issue_floor": _issue_roofline(12.0, w.d_k * w.d_v * w.B * w.H * w.T, t,
                                        "decay, two projections and the update (4) plus the INT8 codec (8) per element "
                                        "and token"),
+        "training_pair": {
+            "ms_fwd": t_f * 1e3, "ms_bwd": t_b * 1e3, "kernel_bwd": kernel_bwd, "workspace_bytes_bwd": nbytes,
+            "issue_floor_bwd": _issue_roofline(23.0, w.d_k * w.d_v * w.B * w.H * w.T, t_b,
+                                               "recompute with the codec once (12), decode of the kept codes (2) and "
+                                               "adjoint (9) per element and token"),
+            "note": "forward with 64-token checkpoints, then the straight-through backward from them",
+        },
         "ms_per_call_hadamard": t_h * 1e3,
         "issue_floor_hadamard": _issue_roofline(26.0, w.d_k * w.d_v * w.B * w.H * w.T, t_h,
                                                 "as above plus two 7-stage butterfly rotations of the state (14) per "
