@@ -45,32 +45,45 @@ struct PartLayout {
     static constexpr int PW = 2 * DK + GW + 1;
 };
 
-// One token of the adjoint.  st: the state entering the token; u, dl: its u and delta;
-// lam: dL/dS_t on entry, dL/dS_{t-1} on return.  Row sums run over the tile's TC columns.
+// One token of the adjoint, in two halves around its barrier.  st: the state entering the
+// token; u, dl: its u and delta; lam: dL/dS_t on entry, dL/dS_{t-1} on return.  Row sums run
+// over the tile's TC columns.  adj_pre forms dS' = lambda + qq do^T and the partial sums of
+// ddelta = dS'^T ku into red; adj_post takes ddelta, forms S~ and S' again (the same
+// operations, so the same values, and no registers held over the barrier), the row sums, du,
+// dS~ and the gate term (ga: exp(g) of this lane's reduce-scatter row, per-key gates only), and
+// returns lambda = diag(a) dS~.
 template <class S, bool KDA, bool HAD>
-__device__ __forceinline__ void tok_adjoint(const float (&st)[S::R], float u, float dl, const TokOps<S, KDA>& op,
-                                            const float* ga_row, float (&lam)[S::R], float2 (*red)[S::TC], int w,
-                                            int lane, float* part, float* dv_out, bool writer) {
+__device__ __forceinline__ void adj_pre(const TokOps<S, KDA>& op, float (&lam)[S::R], float2 (*red)[S::TC], int w,
+                                        int lane) {
+    constexpr float c1 = HAD ? 1.0f / S::DK : 1.0f;
+    // c1 is a power of two: (q c1) do and q (c1 do) round to the same value
+    const float c1do = c1 * op.dj;
+    float pd = 0.0f;
+#pragma unroll
+    for (int m = 0; m < S::R; m++) {
+        lam[m] = __builtin_fmaf(op.qr[m], c1do, lam[m]);             // dS' = lambda + qq do^T
+        pd = __builtin_fmaf(lam[m], op.kr[m], pd);
+    }
+    pd = tok_rows_combine<S>(pd);
+    if (lane < S::TC) red[w][lane] = make_float2(pd, 0.0f);
+}
+
+template <class S, bool KDA, bool HAD>
+__device__ __forceinline__ void adj_post(const float (&st)[S::R], float u, float dl, const TokOps<S, KDA>& op, float ga,
+                                         float (&lam)[S::R], const float2 (*red)[S::TC], int w, int lane, float* part,
+                                         float* dv_out, bool writer) {
     constexpr int R = S::R, TC = S::TC, DK = S::DK;
     constexpr float c1 = HAD ? 1.0f / DK : 1.0f;
     constexpr int GW = PartLayout<DK, KDA>::GW;
     const int row = tok_row0<S>(w, lane) + reduce_scatter_row<R, TC>(lane);
-    // c1 is a power of two: (q c1) do and q (c1 do) round to the same value
-    const float c1do = c1 * op.dj;
+    const int c = lane % TC;
     float sa[R], x[R];
-    float pd = 0.0f;
 #pragma unroll
     for (int m = 0; m < R; m++) {
         sa[m] = (KDA ? op.ar[m] : op.a) * st[m];                     // S~
         const float spm = __builtin_fmaf(op.kr[m], dl, sa[m]);       // S' (before rounding)
-        lam[m] = __builtin_fmaf(op.qr[m], c1do, lam[m]);             // dS' = lambda + qq do^T
         x[m] = spm * op.dj;
-        pd = __builtin_fmaf(lam[m], op.kr[m], pd);
     }
-    pd = tok_rows_combine<S>(pd);
-    if (lane < TC) red[w][lane] = make_float2(pd, 0.0f);
-    __syncthreads();
-    const int c = lane % TC;
     float r[kTokWaves];
 #pragma unroll
     for (int i = 0; i < kTokWaves; i++) r[i] = red[i][c].x;
@@ -92,7 +105,7 @@ __device__ __forceinline__ void tok_adjoint(const float (&st)[S::R], float u, fl
 #pragma unroll
         for (int m = 0; m < R; m++) x[m] = st[m] * lam[m];
         const float x3 = reduce_scatter<OpAdd, R, TC>(x, lane);
-        part[2 * DK + row] = ga_row[row] * x3;
+        part[2 * DK + row] = ga * x3;
     } else {
         float gp = 0.0f;
 #pragma unroll
@@ -109,6 +122,16 @@ __device__ __forceinline__ void tok_adjoint(const float (&st)[S::R], float u, fl
     }
 }
 
+template <class S, bool KDA, bool HAD>
+__device__ __forceinline__ void tok_adjoint(const float (&st)[S::R], float u, float dl, const TokOps<S, KDA>& op,
+                                            const float* ga_row, float (&lam)[S::R], float2 (*red)[S::TC], int w,
+                                            int lane, float* part, float* dv_out, bool writer) {
+    adj_pre<S, KDA, HAD>(op, lam, red, w, lane);
+    __syncthreads();
+    const float ga = KDA ? ga_row[tok_row0<S>(w, lane) + reduce_scatter_row<S::R, S::TC>(lane)] : 0.0f;
+    adj_post<S, KDA, HAD>(st, u, dl, op, ga, lam, red, w, lane, part, dv_out, writer);
+}
+
 template <int DK, int QMODE, int G, bool HAD, bool KDA, bool CODED>
 __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdArgs a) {
     using S = TokShape<DK, QMODE, G>;
@@ -122,9 +145,14 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     __shared__ TokQdqShared<S> qsh;
     __shared__ float tile[HAD ? 2 * DK * TC : 1];  // tok_rotate's two tiles
     // the coded walk (bwd_tok_coded: every token an INT8 rounding point): u and delta of the
-    // chunk's tokens
+    // chunk's tokens.  With 32-column tiles and the scalar gate (PIPE) the adjoint of one chunk runs beside the
+    // recompute of the chunk before it: a second token ring and reduction buffers for the
+    // adjoint, and u and delta of two chunks.
     static_assert(!CODED || (QMODE == LA_QDQ_INT8_GROUP && !RQ && R % 2 == 0), "coded walk");
-    __shared__ float2 ud[CODED ? kCodedMaxChunk : 1][TC];
+    constexpr bool PIPE = CODED && TC == 32 && !KDA;
+    __shared__ float2 ud[PIPE ? 2 : 1][CODED ? kCodedMaxChunk : 1][TC];
+    __shared__ std::conditional_t<PIPE, TokRing<S, KDA, true>, char> ringB;
+    __shared__ float2 redB[PIPE ? 2 : 1][kTokWaves][TC];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -158,7 +186,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
         }
     }
     const int nck = (T + C - 1) / C;
-    float* wsS = a.ws_states + wg * bwd_tok_ws_floats(C, DK, TC, G, CODED);
+    float* wsS = a.ws_states + wg * bwd_tok_ws_floats(C, DK, TC, G, CODED, PIPE);
     const TokInputs in{a.q, a.k, a.v, a.g, a.beta, a.dout};
 
     float lam[R];
@@ -188,121 +216,153 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     fetch(nck - 1, 0);
     __builtin_amdgcn_s_waitcnt(0);
     int rp = 0;
-#pragma unroll 1
-    for (int c = nck - 1; c >= 0; c--) {
-        const int t0 = c * C, t1 = min(T, t0 + C);
-        const int nb = nblocks(c);
-        if constexpr (CODED) {
-            constexpr int NH = R / 2;                   // fp16 code pairs per lane and token
-            constexpr int NSC = (64 / G) * R;           // scales per wave and token
-            const int tid = threadIdx.x, L = t1 - t0;
-            uint32_t* wcode = reinterpret_cast<uint32_t*>(wsS);  // [C][kTokThreads][NH]
-            float* wscl = wsS + static_cast<size_t>(C) * kTokThreads * NH;  // [C][kTokWaves][NSC]
-            // the codes and scales of the state after chunk token `off`
-            auto code_ptr = [&](int off) { return wcode + (static_cast<size_t>(off) * kTokThreads + tid) * NH; };
-            auto scale_ptr = [&](int off) {
-                return wscl + (static_cast<size_t>(off) * kTokWaves + w) * NSC + (lane / G) * R;
-            };
-            // the checkpoint: the state entering the chunk's first token
-            float ckr[R];
-            {
-                const float* ck = a.ckpts + (ck0 + c) * DK * DV;
+    if constexpr (CODED) {
+        constexpr int NH = R / 2;            // fp16 code pairs per lane and token
+        constexpr int NSC = (64 / G) * R;    // scales per wave and token
+        const int tid = threadIdx.x;
+        // per chunk parity: codes [C][kTokThreads][NH], then scales [C][kTokWaves][NSC]
+        const size_t region = static_cast<size_t>(C) * (kTokThreads * NH + kTokWaves * NSC);
+        auto code_ptr = [&](int c, int off) {
+            return reinterpret_cast<uint32_t*>(wsS + (PIPE ? (c & 1) : 0) * region) +
+                   (static_cast<size_t>(off) * kTokThreads + tid) * NH;
+        };
+        auto scale_row = [&](int c, int off) {  // this wave's scales after chunk token off
+            return wsS + (PIPE ? (c & 1) : 0) * region + static_cast<size_t>(C) * kTokThreads * NH +
+                   (static_cast<size_t>(off) * kTokWaves + w) * NSC;
+        };
+        auto udp = [&](int c) { return ud[PIPE ? (c & 1) : 0]; };
+        const int wrow = (lane / G) * R + reduce_scatter_row<R, G>(lane);
+        const bool wsc = (lane & (G / R - 1)) == 0;  // one lane of each (row, group) stores its scale
+        auto load_ck = [&](int c, float (&x)[R]) __attribute__((always_inline)) {
+            const float* ck = a.ckpts + (ck0 + c) * DK * DV;
 #pragma unroll
-                for (int m = 0; m < R; m++) ckr[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
+            for (int m = 0; m < R; m++) x[m] = ck[static_cast<size_t>(r0 + m) * DV + col];
+        };
+        auto chunk_len = [&](int c) { return min(T, (c + 1) * C) - c * C; };
+        // after the recompute's token off of chunk c (of L tokens): keep u and delta and, but for
+        // the chunk's last token, round the state keeping its codes and scales
+        auto keep = [&](int c, int off, int L, float (&st)[R], float u, float dl) __attribute__((always_inline)) {
+            if (w == 0 && lane < TC) udp(c)[off][lane] = make_float2(u, dl);
+            if (off + 1 < L) {
+                uint32_t hc[NH];
+                float scl;
+                tok_int8<R, G, true>(st, qsh.scr[w], lane, hc, &scl);
+                uint32_t* dst = code_ptr(c, off);
+#pragma unroll
+                for (int q = 0; q < NH; q++) dst[q] = hc[q];
+                if (wsc) scale_row(c, off)[wrow] = scl;
             }
-            // ---------------- phase A: the whole chunk, keeping every token's u and delta
-            // and every rounded state but the last
-            {
-                float s[R];
+        };
+        // the state entering a token, loaded one token ahead into the other of two register sets
+        // (the sets alternate by token and every loop takes two tokens per pass, so that no
+        // loaded value is copied between iterations and the loads stay in flight over the
+        // adjoint)
+        struct Entering {
+            uint32_t hc[NH];  // codes
+            float sc[R];      // their scales
+        };
+        // the codes and scales of the state after token k of chunk c
+        auto load_codes = [&](int c, int k, Entering& e) __attribute__((always_inline)) {
+            const uint32_t* src = code_ptr(c, k);
 #pragma unroll
-                for (int m = 0; m < R; m++) s[m] = ckr[m];
-                const int wrow = (lane / G) * R + reduce_scatter_row<R, G>(lane);
-                const bool wsc = (lane & (G / R - 1)) == 0;  // one lane of each (row, group) stores its scale
-#pragma unroll 1
-                for (int j = 0; j < nb; j++) {
-                    const int tb = t0 + kBlkTok * j;
-                    const int nt = min(kBlkTok, t1 - tb);
-                    if (j + 1 < nb) publish(nt, c, j + 1);
-                    else publish(nt, c, j);  // phase B starts with the same block
-#pragma unroll 1
-                    for (int i = 0; i < nt; i++) {
-                        const int off = kBlkTok * j + i;
-                        TokOps<S, KDA> op;
-                        tok_read<S, KDA, true>(op, ring, i, w, lane);
-                        float u, dl, o;
-                        tok_step<S, KDA, RC>(s, op, red[rp], w, lane, u, dl, o);
-                        rp ^= 1;
-                        if (w == 0 && lane < TC) ud[off][lane] = make_float2(u, dl);
-                        if (off + 1 < L) {
-                            uint32_t hc[NH];
-                            float scl;
-                            tok_int8<R, G, true>(s, qsh.scr[w], lane, hc, &scl);
-                            uint32_t* dst = code_ptr(off);
+            for (int q = 0; q < NH; q++) e.hc[q] = src[q];
+            const float* sp = scale_row(c, k) + (lane / G) * R;
+            if constexpr (R % 4 == 0) {
 #pragma unroll
-                            for (int q = 0; q < NH; q++) dst[q] = hc[q];
-                            if (wsc) wscl[(static_cast<size_t>(off) * kTokWaves + w) * NSC + wrow] = scl;
-                        }
-                    }
+                for (int m = 0; m < R / 4; m++) {
+                    const float4 x = reinterpret_cast<const float4*>(sp)[m];
+                    e.sc[4 * m] = x.x;
+                    e.sc[4 * m + 1] = x.y;
+                    e.sc[4 * m + 2] = x.z;
+                    e.sc[4 * m + 3] = x.w;
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < R / 2; m++) {
+                    const float2 x = reinterpret_cast<const float2*>(sp)[m];
+                    e.sc[2 * m] = x.x;
+                    e.sc[2 * m + 1] = x.y;
                 }
             }
-            // every store of phase A has completed before any lane reads it back
-            __builtin_amdgcn_s_waitcnt(0);
+        };
+        // the state entering token k of chunk c: for k > 0 the codes and scales of token k - 1;
+        // for k = 0 the checkpoint's values as scales of unit codes (1 x value is exact)
+        auto load_entering = [&](int c, int k, Entering& e) __attribute__((always_inline)) {
+            if (k > 0) {
+                load_codes(c, k - 1, e);
+                return;
+            }
+            float x[R];
+            load_ck(c, x);
+#pragma unroll
+            for (int q = 0; q < NH; q++) e.hc[q] = 0x3C003C00u;  // fp16 (1, 1)
+#pragma unroll
+            for (int m = 0; m < R; m++) e.sc[m] = x[m];
+        };
+        auto decode = [&](const Entering& cur, float (&st)[R]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int q = 0; q < NH; q++) {
+                const auto hv = __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), cur.hc[q]);
+                st[2 * q] = static_cast<float>(hv[0]) * cur.sc[2 * q];
+                st[2 * q + 1] = static_cast<float>(hv[1]) * cur.sc[2 * q + 1];
+            }
+        };
+        // the recompute of chunk c alone (the block protocol of the recompute-per-group walk)
+        auto run_a = [&](int c) {
+            const int L = chunk_len(c), nb = nblocks(c), t0 = c * C, t1 = t0 + L;
+            float st[R];
+            load_ck(c, st);
+#pragma unroll 1
+            for (int j = 0; j < nb; j++) {
+                const int nt = min(kBlkTok, t1 - (t0 + kBlkTok * j));
+                if (j + 1 < nb) publish(nt, c, j + 1);
+                else publish(nt, c, j);  // the adjoint starts with the same block
+#pragma unroll 1
+                for (int i = 0; i < nt; i++) {
+                    TokOps<S, KDA> op;
+                    tok_read<S, KDA, true>(op, ring, i, w, lane);
+                    float u, dl, o;
+                    tok_step<S, KDA, RC>(st, op, red[rp], w, lane, u, dl, o);
+                    rp ^= 1;
+                    keep(c, kBlkTok * j + i, L, st, u, dl);
+                }
+            }
+        };
+        // the adjoint of chunk c alone, tokens last to first
+        auto run_b = [&](int c) {
+            __builtin_amdgcn_s_waitcnt(0);  // every kept code is stored before any lane reads it
             __syncthreads();
-            // ---------------- phase B: tokens last to first, the entering state decoded from
-            // the codes of the token before (the checkpoint for the chunk's first token), loaded
-            // one token ahead into the other of two register sets: the sets alternate by token
-            // (the loop takes two tokens per pass), so that no loaded value is copied between
-            // iterations and the loads stay in flight over the adjoint.  Loads are unconditional (a clamped index reads codes that
-            // are not used), which keeps the token free of branches.
-            struct Entering {
-                uint32_t hc[NH];  // codes
-                float sc[R];      // their scales
-            };
-            auto load_entering = [&](int k, Entering& e) __attribute__((always_inline)) {  // after token k
-                const uint32_t* src = code_ptr(k);
-#pragma unroll
-                for (int q = 0; q < NH; q++) e.hc[q] = src[q];
-                if constexpr (R % 4 == 0) {
-                    const float4* sp = reinterpret_cast<const float4*>(scale_ptr(k));
-#pragma unroll
-                    for (int m = 0; m < R / 4; m++) {
-                        const float4 x = sp[m];
-                        e.sc[4 * m] = x.x;
-                        e.sc[4 * m + 1] = x.y;
-                        e.sc[4 * m + 2] = x.z;
-                        e.sc[4 * m + 3] = x.w;
-                    }
-                } else {
-                    const float2* sp = reinterpret_cast<const float2*>(scale_ptr(k));
-#pragma unroll
-                    for (int m = 0; m < R / 2; m++) {
-                        const float2 x = sp[m];
-                        e.sc[2 * m] = x.x;
-                        e.sc[2 * m + 1] = x.y;
-                    }
-                }
-            };
+            const int L = chunk_len(c), nb = nblocks(c), t0 = c * C, t1 = t0 + L;
+            // The pipelined kernel keeps registers free: the checkpoint arrives as the entering
+            // set of the chunk's first token.  The others hold it in registers and load codes
+            // unconditionally (a clamped index reads codes that are not used), which keeps
+            // their token free of branches.
+            float ckr[PIPE ? 1 : R];
+            if constexpr (!PIPE) load_ck(c, ckr);
             auto token = [&](int j, int i, const Entering& cur, Entering& nxt) __attribute__((always_inline)) {
-                const int off = kBlkTok * j + i, tb = t0 + kBlkTok * j;
-                load_entering(max(off - 2, 0), nxt);
+                const int off = kBlkTok * j + i;
                 float st[R];
+                if constexpr (PIPE) {
+                    if (off > 0) load_entering(c, off - 1, nxt);
+                    decode(cur, st);
+                } else {
+                    load_codes(c, max(off - 2, 0), nxt);
+                    decode(cur, st);
 #pragma unroll
-                for (int q = 0; q < NH; q++) {
-                    const auto h = __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), cur.hc[q]);
-                    st[2 * q] = off == 0 ? ckr[2 * q] : static_cast<float>(h[0]) * cur.sc[2 * q];
-                    st[2 * q + 1] = off == 0 ? ckr[2 * q + 1] : static_cast<float>(h[1]) * cur.sc[2 * q + 1];
+                    for (int m = 0; m < R; m++) st[m] = off == 0 ? ckr[m] : st[m];
                 }
                 TokOps<S, KDA> op;
                 tok_read<S, KDA, true>(op, ring, i, w, lane);
-                const float2 x = ud[off][lane % TC];
-                const size_t tok = tok0 + static_cast<size_t>(tb + i) * H;
+                const float2 x = udp(c)[off][lane % TC];
+                const size_t tok = tok0 + static_cast<size_t>(t0 + off) * H;
                 float* part = a.ws_part + (static_cast<size_t>(blk) * ntok + tok) * PW;
                 tok_adjoint<S, KDA, RC>(st, x.x, x.y, op, ring.ga[i], lam, red[rp], w, lane, part,
                                         a.dv + tok * DV + col, w == i);
                 rp ^= 1;
             };
             Entering e0, e1;
-            load_entering(max(L - 2, 0), e0);
+            if constexpr (PIPE) load_entering(c, L - 1, e0);
+            else load_codes(c, max(L - 2, 0), e0);
 #pragma unroll 1
             for (int j = nb - 1; j >= 0; j--) {
                 const int nt = min(kBlkTok, t1 - (t0 + kBlkTok * j));
@@ -320,7 +380,107 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                     token(j, i - 1, e1, e0);
                 }
             }
+        };
+        if constexpr (!PIPE) {
+#pragma unroll 1
+            for (int c = nck - 1; c >= 0; c--) {
+                run_a(c);
+                run_b(c);
+            }
         } else {
+            // The adjoint of full chunk c beside the recompute of chunk c - 1: per step one token
+            // of each, their partial sums meeting behind one barrier (double-buffered by token
+            // parity), so that the two independent chains fill each other's latencies.
+            TokFetch<S, KDA, true> fa;  // the recompute's next block (f holds the adjoint's)
+            auto fetch_a = [&](int c, int j) __attribute__((always_inline)) {
+                if (c < 0) return;
+                const int t = c * C + kBlkTok * j + w;
+                if (t < min(T, (c + 1) * C)) fa.fetch(in, p, tok0 + static_cast<size_t>(t) * H, col, lane);
+            };
+            auto run_ab = [&](int c, bool first) {
+                __builtin_amdgcn_s_waitcnt(0);  // the kept codes of chunk c are stored
+                __syncthreads();
+                if (first) fetch_a(c - 1, 0);
+                const int nbk = C / kBlkTok, t0 = c * C;
+                float sa_[R];
+                load_ck(c - 1, sa_);
+                auto step = [&](int m, int i, const Entering& cur, Entering& nxt) __attribute__((always_inline)) {
+                    // recompute: token 8m + i of chunk c - 1; adjoint: token C - 1 - (8m + i) of
+                    // chunk c, which is slot 7 - i of the adjoint's ring
+                    const int offa = kBlkTok * m + i, offb = C - 1 - offa, ib = kBlkTok - 1 - i;
+                    TokOps<S, KDA> opa, opb;
+                    tok_read<S, KDA, true>(opa, ring, i, w, lane);
+                    tok_read<S, KDA, true>(opb, ringB, ib, w, lane);
+                    const float2 x = udp(c)[offb][lane % TC];
+                    const float ga = KDA ? ringB.ga[ib][r0 + reduce_scatter_row<R, TC>(lane)] : 0.0f;
+                    if (offb > 0) load_entering(c, offb - 1, nxt);
+                    float st[R];
+                    decode(cur, st);
+                    tok_step_pre<S, KDA>(sa_, opa, red[i & 1], w, lane);
+                    adj_pre<S, KDA, RC>(opb, lam, redB[i & 1], w, lane);
+                    __syncthreads();
+                    float u, dl, o;
+                    tok_step_post<S, KDA, RC>(sa_, opa, red[i & 1], lane, u, dl, o);
+                    keep(c - 1, offa, C, sa_, u, dl);
+                    const size_t tok = tok0 + static_cast<size_t>(t0 + offb) * H;
+                    float* part = a.ws_part + (static_cast<size_t>(blk) * ntok + tok) * PW;
+                    adj_post<S, KDA, RC>(st, x.x, x.y, opb, ga, lam, redB[i & 1], w, lane, part,
+                                         a.dv + tok * DV + col, w == ib);
+                };
+                Entering e0, e1;
+                load_entering(c, C - 1, e0);
+#pragma unroll 1
+                for (int m = 0; m < nbk; m++) {
+                    // publish block nbk-1-m of the adjoint and block m of the recompute; fetch the next two
+                    __syncthreads();
+                    f.template publish<RC>(ringB, w, p, lane);
+                    fa.template publish<RC>(ring, w, p, lane);
+                    if (m + 1 < nbk) {
+                        fetch(c, nbk - 2 - m);
+                        fetch_a(c - 1, m + 1);
+                    } else {
+                        fetch(c - 1, nbk - 1);
+                        fetch_a(c - 2, 0);
+                    }
+                    __syncthreads();
+#pragma unroll 1
+                    for (int i = 0; i < kBlkTok; i += 2) {
+                        step(m, i, e0, e1);
+                        step(m, i + 1, e1, e0);
+                    }
+                }
+            };
+            int c = nck - 1;
+            if (C % kBlkTok != 0) {
+#pragma unroll 1
+                for (; c >= 0; c--) {
+                    run_a(c);
+                    run_b(c);
+                }
+            } else {
+                if (chunk_len(c) != C) {  // a ragged last chunk runs alone
+                    run_a(c);
+                    run_b(c);
+                    c--;
+                }
+                if (c >= 0) {
+                    run_a(c);
+                    bool first = true;
+#pragma unroll 1
+                    for (; c >= 1; c--) {
+                        run_ab(c, first);
+                        first = false;
+                    }
+                    run_b(0);
+                }
+            }
+        }
+    } else {
+#pragma unroll 1
+    for (int c = nck - 1; c >= 0; c--) {
+        const int t0 = c * C, t1 = min(T, t0 + C);
+        const int nb = nblocks(c);
+        {
             const int last_sub = ((t1 - t0 - 1) / kSubTok) * kSubTok;  // chunk offset of the last stored state
 
             // ---------------- phase A: advance through the chunk, storing the state entering
@@ -410,6 +570,7 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                 }
             }
         }
+    }
     }
     if (RC && !p.rot) tok_rotate<S>(lam, tile, w, lane, 1.0f);  // dL/dS = Hu dL/dY
 #pragma unroll

@@ -113,14 +113,22 @@ inline bool bwd_tok_coded(const la_config& c) {
     return c.qdq == LA_QDQ_INT8_GROUP && c.qdq_interval == 1 && !c.replay && !(c.hadamard && c.gate == LA_GATE_KEY) &&
            c.ckpt_interval >= 1 && c.ckpt_interval <= kCodedMaxChunk && tok_rows_per_lane(c.d_k, tc) % 2 == 0;
 }
+// The coded walk with 32-column tiles and the scalar gate runs the adjoint of one chunk beside
+// the recompute of the chunk before it, so it keeps the codes of two chunks.
+inline bool bwd_tok_coded_pipe(const la_config& c) {
+    return bwd_tok_coded(c) && tok_tile_cols(c.d_k, c.qdq, c.group) == 32 && c.gate != LA_GATE_KEY;
+}
 // Floats of one workgroup's backward states for chunks of C tokens: coded, per token the
-// d_k x tc codes as fp16 and the d_k tc / g scales; else the state entering every fourth token.
-constexpr size_t bwd_tok_ws_floats(int C, int dk, int tc, int g, bool coded) {
-    return coded ? static_cast<size_t>(C) * (static_cast<size_t>(dk) * tc / 2 + static_cast<size_t>(dk) * tc / g)
+// d_k x tc codes as fp16 and the d_k tc / g scales, for one chunk or (pipe) two; else the state
+// entering every fourth token.
+constexpr size_t bwd_tok_ws_floats(int C, int dk, int tc, int g, bool coded, bool pipe) {
+    return coded ? (pipe ? 2 : 1) * static_cast<size_t>(C) *
+                       (static_cast<size_t>(dk) * tc / 2 + static_cast<size_t>(dk) * tc / g)
                  : static_cast<size_t>((C + 3) / 4) * dk * tc;
 }
 inline size_t bwd_tok_ws_floats(const la_config& c) {
-    return bwd_tok_ws_floats(c.ckpt_interval, c.d_k, tok_tile_cols(c.d_k, c.qdq, c.group), c.group, bwd_tok_coded(c));
+    return bwd_tok_ws_floats(c.ckpt_interval, c.d_k, tok_tile_cols(c.d_k, c.qdq, c.group), c.group, bwd_tok_coded(c),
+                             bwd_tok_coded_pipe(c));
 }
 
 hipError_t launch_decode(const la_config& c, const DecodeArgs& a, hipStream_t s);

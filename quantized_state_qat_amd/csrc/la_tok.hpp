@@ -392,14 +392,11 @@ __device__ __forceinline__ float tok_rows_combine(float x) {
 }
 
 // ------------------------------------------------------------------ one token
-// s: the state entering the token (this lane's rows of its column), advanced in place to
-// S' = a S + ku delta^T (before rounding), or, with enc (a replay-window token that is not a
-// rounding point), to a S + ku bf16(delta)^T.  red: this token's reduction buffer (kTokWaves
-// x TC float2).  Returns u = S~^T k, delta and o = S'^T q for the column (from the unencoded
-// delta).
-template <class S, bool KDA, bool HAD>
-__device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>& op, float2 (*red)[S::TC],
-                                         int w, int lane, float& u, float& delta, float& o, bool enc = false) {
+// The two halves of a token step around its barrier (tok_step runs both): the decay and the
+// partial projections into red, then the sums, delta and the update.
+template <class S, bool KDA>
+__device__ __forceinline__ void tok_step_pre(float (&s)[S::R], const TokOps<S, KDA>& op, float2 (*red)[S::TC], int w,
+                                             int lane) {
     float pk = 0.0f, pq = 0.0f;
 #pragma unroll
     for (int m = 0; m < S::R; m++) {
@@ -410,7 +407,11 @@ __device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>&
     pk = tok_rows_combine<S>(pk);
     pq = tok_rows_combine<S>(pq);
     if (lane < S::TC) red[w][lane] = make_float2(pk, pq);
-    __syncthreads();
+}
+
+template <class S, bool KDA, bool HAD>
+__device__ __forceinline__ void tok_step_post(float (&s)[S::R], const TokOps<S, KDA>& op, const float2 (*red)[S::TC],
+                                              int lane, float& u, float& delta, float& o, bool enc = false) {
     const int c = lane % S::TC;
     float2 x[kTokWaves];
 #pragma unroll
@@ -431,6 +432,19 @@ __device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>&
     const float du = enc ? bf16_rne(delta) : delta;
 #pragma unroll
     for (int m = 0; m < S::R; m++) s[m] = __builtin_fmaf(op.kr[m], du, s[m]);
+}
+
+// s: the state entering the token (this lane's rows of its column), advanced in place to
+// S' = a S + ku delta^T (before rounding), or, with enc (a replay-window token that is not a
+// rounding point), to a S + ku bf16(delta)^T.  red: this token's reduction buffer (kTokWaves
+// x TC float2).  Returns u = S~^T k, delta and o = S'^T q for the column (from the unencoded
+// delta).
+template <class S, bool KDA, bool HAD>
+__device__ __forceinline__ void tok_step(float (&s)[S::R], const TokOps<S, KDA>& op, float2 (*red)[S::TC],
+                                         int w, int lane, float& u, float& delta, float& o, bool enc = false) {
+    tok_step_pre<S, KDA>(s, op, red, w, lane);
+    __syncthreads();
+    tok_step_post<S, KDA, HAD>(s, op, red, lane, u, delta, o, enc);
 }
 
 // ------------------------------------------------------------------ codecs

@@ -130,10 +130,11 @@ def test_bwd_workspace_and_checks():
     n = la.la_bwd_workspace_bytes(c)
     # INT8 groups of 32 after every token: the backward's tiles are 32 value columns wide (4 per
     # head).  Per workgroup (B x H x tiles) and chunk token the rounded state as fp16 codes and
-    # one scale per (row, group); per tile and token the partial sums (two d_k rows, eight GDN
-    # gate terms, beta); room for recomputed checkpoints
+    # one scale per (row, group), for two chunks (the adjoint of one runs beside the recompute
+    # of the next); per tile and token the partial sums (two d_k rows, eight GDN gate terms,
+    # beta); room for recomputed checkpoints
     nwg = 2 * 2 * 4
-    states = nwg * 64 * (128 * 32 * 2 + 128 * 4)
+    states = nwg * 2 * 64 * (128 * 32 * 2 + 128 * 4)
     part = 4 * 2 * 256 * 2 * (2 * 128 + 8 + 1) * 4
     ck = 2 * 2 * 4 * 128 * 128 * 4
     assert n >= states + part + ck and n < states + part + ck + 3 * 256
