@@ -204,3 +204,46 @@ def test_bwd_steep_gates(name, w, mode, group, had, interval, ckpt):
     g = gu.run_bwd(c, d, d["do"].f32, S0=d["S0"].f32, dST=d["dST"].f32)
     errs = _check_against_oracle(c, d, d["S0"].f32, d["do"].f32, d["dST"].f32, g, gu.TOL_F32)
     print(name, {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+CODED_CASES = [
+    # id, workload, group, hadamard, ckpt
+    ("gdn_wht_int8g32_c64_ragged", synth.Workload("cw1", B=2, T=300, H=2, d_k=128, d_v=128, s0_sigma=0.2,
+                                                  config_id=61), 32, 1, 64),
+    ("gdn_int8g16_c16", synth.Workload("cw2", B=1, T=96, H=2, d_k=64, d_v=64, s0_sigma=0.2, config_id=62),
+     16, 0, 16),
+    ("gdn_int8g32_c5", synth.Workload("cw3", B=1, T=23, H=2, d_k=128, d_v=64, s0_sigma=0.2, config_id=63),
+     32, 0, 5),
+    ("gdn_wht_int8g16_dk32_c8", synth.Workload("cw4", B=1, T=40, H=2, d_k=32, d_v=64, s0_sigma=0.2,
+                                               config_id=64), 16, 1, 8),
+    ("kda_int8g64_c64", synth.Workload("cw5", B=2, T=150, H=2, d_k=128, d_v=128, gate="key", s0_sigma=0.2,
+                                       config_id=65), 64, 0, 64),
+    ("kda_int8g32_c32", synth.Workload("cw6", B=1, T=130, H=2, d_k=128, d_v=128, gate="key", s0_sigma=0.2,
+                                       config_id=66), 32, 0, 32),
+    ("gdn_int8g64_c1", synth.Workload("cw7", B=1, T=20, H=2, d_k=128, d_v=128, s0_sigma=0.2, config_id=67),
+     64, 0, 1),
+]
+
+
+@pytest.mark.parametrize("name,w,group,had,ckpt", CODED_CASES, ids=[x[0] for x in CODED_CASES])
+def test_bwd_coded_walk_matches_recompute_walk(name, w, group, had, ckpt):
+    """With INT8 rounding after every token the token backward keeps each token's codes during
+    its chunk recompute and decodes them for the adjoint (the coded walk).  Replay windows of one
+    token round after every token too, with the same arithmetic ("Torch GDN/KDA decode QAT +
+    INT8", What does this PR do?: a window of one writes a checkpoint each token), and take the
+    recompute-per-group walk; the two walks' gradients must agree bit for bit."""
+    d = synth.generate(w, with_do=True, with_dST=True)
+    c = gu.cfg_for(w, d, qdq=la.LA_QDQ_INT8_GROUP, group=group, hadamard=had, qdq_interval=1)
+    S0, dST = d["S0"].f32, d["dST"].f32
+    _, _, ck = gu.run_fwd(c, d, S0=S0, ckpt_interval=ckpt)
+    c.ckpt_interval = ckpt
+    cr = dataclasses.replace(c, replay=1)
+    _, _, ckr = gu.run_fwd(cr, d, S0=S0, ckpt_interval=ckpt)
+    np.testing.assert_array_equal(ck, ckr)  # the forwards agree too
+    cr.ckpt_interval = ckpt
+    assert la.la_bwd_workspace_bytes(c) != la.la_bwd_workspace_bytes(cr)  # the two walks' layouts
+    g_coded = gu.run_bwd(c, d, d["do"].f32, S0=S0, dST=dST, ckpts=ck)
+    g_group = gu.run_bwd(cr, d, d["do"].f32, S0=S0, dST=dST, ckpts=ck)
+    for name_ in GRADS:
+        assert np.all(np.isfinite(g_coded[name_])), name_
+        np.testing.assert_array_equal(g_coded[name_].view(np.uint32), g_group[name_].view(np.uint32), err_msg=name_)
