@@ -7,7 +7,9 @@
 //            storing the state entering every fourth token in the workspace;
 //   phase B  for each group of four tokens, last to first: recompute it from the stored
 //            state, keeping the state entering every token in registers, then walk it
-//            backwards with the adjoint lambda = dL/dS in registers.
+//            backwards with the adjoint lambda = dL/dS in registers.  For chunks of at most 64
+//            tokens phase A keeps every token's u and delta in LDS and the recompute is the
+//            decay and the update with the kept delta alone.
 // When every token is a rounding point of the INT8 codec (bwd_tok_coded), each carried state
 // is its codes times its group scales: phase A runs the whole chunk and keeps every token's
 // codes (fp16, exact) and scales in the workspace and its u and delta in LDS, and phase B
@@ -144,13 +146,13 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     __shared__ float2 red[2][kTokWaves][TC];
     __shared__ TokQdqShared<S> qsh;
     __shared__ float tile[HAD ? 2 * DK * TC : 1];  // tok_rotate's two tiles
-    // the coded walk (bwd_tok_coded: every token an INT8 rounding point): u and delta of the
-    // chunk's tokens.  With 32-column tiles and the scalar gate (PIPE) the adjoint of one chunk runs beside the
+    // u and delta of the chunk's tokens (both walks, for chunks of at most kCodedMaxChunk
+    // tokens).  With 32-column tiles and the scalar gate (PIPE) the adjoint of one chunk runs beside the
     // recompute of the chunk before it: a second token ring and reduction buffers for the
     // adjoint, and u and delta of two chunks.
     static_assert(!CODED || (QMODE == LA_QDQ_INT8_GROUP && !RQ && R % 2 == 0), "coded walk");
     constexpr bool PIPE = CODED && TC == 32 && !KDA;
-    __shared__ float2 ud[PIPE ? 2 : 1][CODED ? kCodedMaxChunk : 1][TC];
+    __shared__ float2 ud[PIPE ? 2 : 1][kCodedMaxChunk][TC];
     __shared__ std::conditional_t<PIPE, TokRing<S, KDA, true>, char> ringB;
     __shared__ float2 redB[PIPE ? 2 : 1][kTokWaves][TC];
 
@@ -482,6 +484,11 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
         const int nb = nblocks(c);
         {
             const int last_sub = ((t1 - t0 - 1) / kSubTok) * kSubTok;  // chunk offset of the last stored state
+            // chunks of at most kCodedMaxChunk tokens keep every token's u and delta in LDS, and
+            // phase B then re-forms each group's states from the kept values alone (the decay and
+            // the update with the same delta: the same operations as the token step, without its
+            // projections and barrier)
+            const bool kept = C <= kCodedMaxChunk;
 
             // ---------------- phase A: advance through the chunk, storing the state entering
             // every fourth token (the chunk's first state is its checkpoint)
@@ -504,8 +511,9 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
 #pragma unroll
                             for (int m = 0; m < R; m++) dst[(r0 + m) * TC + lane % TC] = s[m];
                         }
-                        // the last group of the chunk is recomputed in phase B from its stored state
-                        if (off >= last_sub) break;
+                        // without kept values the last group of the chunk is recomputed in phase B
+                        // from its stored state
+                        if (!kept && off >= last_sub) break;
                         TokOps<S, KDA> op;
                         tok_read<S, KDA, true>(op, ring, i, w, lane);
                         float u, dl, o;
@@ -513,7 +521,8 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                         const bool qpt = QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1);
                         tok_step<S, KDA, RC>(s, op, red[rp], w, lane, u, dl, o, p.replay && !qpt);
                         rp ^= 1;
-                        if (qpt) tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
+                        if (kept && w == 0 && lane < TC) ud[0][off][lane] = make_float2(u, dl);
+                        if (qpt && t + 1 < t1) tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
                     }
                 }
             }
@@ -547,11 +556,23 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
                             for (int m = 0; m < R; m++) st[i][m] = s[m];
                             TokOps<S, KDA> op;
                             tok_read<S, KDA, true>(op, ring, i0 + i, w, lane);
-                            float o;
                             const int t = tb + i0 + i;
                             const bool qpt = QMODE != LA_QDQ_NONE && (((t + 1) % p.qdq_interval) == 0 || t == T - 1);
-                            tok_step<S, KDA, RC>(s, op, red[rp], w, lane, uu[i], dd[i], o, p.replay && !qpt);
-                            rp ^= 1;
+                            if (kept) {
+                                const float2 x = ud[0][kBlkTok * j + i0 + i][lane % TC];
+                                uu[i] = x.x;
+                                dd[i] = x.y;
+                                const float du = p.replay && !qpt ? bf16_rne(x.y) : x.y;
+#pragma unroll
+                                for (int m = 0; m < R; m++) {
+                                    s[m] = (KDA ? op.ar[m] : op.a) * s[m];
+                                    s[m] = __builtin_fmaf(op.kr[m], du, s[m]);
+                                }
+                            } else {
+                                float o;
+                                tok_step<S, KDA, RC>(s, op, red[rp], w, lane, uu[i], dd[i], o, p.replay && !qpt);
+                                rp ^= 1;
+                            }
                             if (qpt && i + 1 < n) tok_qdq_at<S, RQ>(s, qsh, tile, w, lane);
                         }
                     }
