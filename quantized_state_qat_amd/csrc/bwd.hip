@@ -652,19 +652,35 @@ __global__ __launch_bounds__(64) void bwd_reduce_kernel(TokParams p, BwdArgs a, 
         }
         if (!in_part) return;
     }
-    float x1[NV], x2[NV];
+    // One loop over the tiles for every field, so that the loads of several tiles are in
+    // flight together; each sum keeps its tile order.
+    float x1[NV], x2[NV], x3[NV];
+    float gacc = 0.0f, bacc = 0.0f;
 #pragma unroll
     for (int j = 0; j < NV; j++) {
         x1[j] = 0.0f;
         x2[j] = 0.0f;
-        const int i = lane + 64 * j;
-        if (i < DK) {
-            for (int nb = 0; nb < NB; nb++) {
-                const float* part = a.ws_part + (static_cast<size_t>(nb) * ntok + tok) * PW;
+        x3[j] = 0.0f;
+    }
+#pragma unroll 4
+    for (int nb = 0; nb < NB; nb++) {
+        // loads with no branch around them where every lane owns rows (d_k a multiple of 64;
+        // every lane also forms the per-token sums), so that the compiler issues them together
+        const float* part = a.ws_part + (static_cast<size_t>(nb) * ntok + tok) * PW;
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+            const int i = lane + 64 * j;
+            if (DK % 64 == 0 || i < DK) {
                 x1[j] += part[i];
                 x2[j] += part[DK + i];
+                if (KDA) x3[j] += part[2 * DK + i];
             }
         }
+        if (!KDA) {
+#pragma unroll
+            for (int i = 0; i < GW; i++) gacc += part[2 * DK + i];
+        }
+        bacc += part[2 * DK + GW];
     }
     if (HAD) {
         if (NV == 2) {
@@ -697,23 +713,12 @@ __global__ __launch_bounds__(64) void bwd_reduce_kernel(TokParams p, BwdArgs a, 
 #pragma unroll
         for (int j = 0; j < NV; j++) {
             const int i = lane + 64 * j;
-            if (i < DK) {
-                float acc = 0.0f;
-                for (int nb = 0; nb < NB; nb++) acc += a.ws_part[(static_cast<size_t>(nb) * ntok + tok) * PW + 2 * DK + i];
-                a.dg[tok * DK + i] = acc;
-            }
+            if (i < DK) a.dg[tok * DK + i] = x3[j];
         }
     } else if (lane == 0) {
-        float acc = 0.0f;
-        for (int nb = 0; nb < NB; nb++)
-            for (int i = 0; i < GW; i++) acc += a.ws_part[(static_cast<size_t>(nb) * ntok + tok) * PW + 2 * DK + i];
-        a.dg[tok] = acc;
+        a.dg[tok] = gacc;
     }
-    if (lane == 0) {
-        float acc = 0.0f;
-        for (int nb = 0; nb < NB; nb++) acc += a.ws_part[(static_cast<size_t>(nb) * ntok + tok) * PW + 2 * DK + GW];
-        a.dbeta[tok] = acc;
-    }
+    if (lane == 0) a.dbeta[tok] = bacc;
 }
 
 namespace {
