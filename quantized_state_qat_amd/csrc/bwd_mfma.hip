@@ -563,49 +563,75 @@ __global__ __launch_bounds__(256) void bwd_mfma_reduce_kernel(BwParams p, BwdArg
     const bool ok = t0 + i < T;
     const size_t tseq = static_cast<size_t>(b) * p.stride_T + p.t_off;  // the segment's first token
     const size_t o = ((tseq + t0 + i) * H + h) * DK + 8 * rc;
-    {
-        u4 kw = {0u, 0u, 0u, 0u}, qw = {0u, 0u, 0u, 0u};
-        if (ok) {
-            kw = *reinterpret_cast<const u4*>(static_cast<const uint16_t*>(a.k) + o);
-            qw = *reinterpret_cast<const u4*>(static_cast<const uint16_t*>(a.q) + o);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            Kf[i][8 * rc + 2 * e] = __uint_as_float(kw[e] << 16);
-            Kf[i][8 * rc + 2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
-            Qf[i][8 * rc + 2 * e] = __uint_as_float(qw[e] << 16);
-            Qf[i][8 * rc + 2 * e + 1] = __uint_as_float(qw[e] & 0xFFFF0000u);
-        }
-    }
-    {
-        float sa = 0.0f, sc = 0.0f;
-        for (int wg = 0; wg < nwg; wg++) {
-            sa += rec0[wg * static_cast<size_t>(kRec) + kRecA + tid];
-            sc += rec0[wg * static_cast<size_t>(kRec) + kRecC + tid];
-        }
-        Ab[tid / kBlk][tid % kBlk] = sa;
-        Cb[tid / kBlk][tid % kBlk] = sc;
-    }
-    if (tid < kBlk) {
-        float sg = 0.0f, sb = 0.0f;
-        for (int wg = 0; wg < nwg; wg++) {
-            const float* r = rec0 + wg * static_cast<size_t>(kRec);
-            sg += r[kRecGr + tid] + r[kRecGc + tid];
-            sb += r[kRecB + tid];
-        }
-        dG[tid] = sg;
-        if (t0 + tid < T) a.dbeta[(tseq + t0 + tid) * H + h] = sb;
-    }
+    // k and q of this thread's token and rows (a valid address for every thread; rows past the
+    // sequence are zeroed), loaded before the records so that their latencies overlap
+    const size_t oc = ok ? o : ((tseq + t0) * H + h) * DK + 8 * rc;
+    u4 kw = *reinterpret_cast<const u4*>(static_cast<const uint16_t*>(a.k) + oc);
+    u4 qw = *reinterpret_cast<const u4*>(static_cast<const uint16_t*>(a.q) + oc);
+    const int tg = tid & (kBlk - 1);
+    float sa = 0.0f, sc = 0.0f, sg = 0.0f, sb = 0.0f;
     // the slices' key/query sums for this thread's eight rows
     f4 dks[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
     f4 dqs[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-    for (int wg = 0; wg < nwg; wg++) {
-        const float* r = rec0 + wg * static_cast<size_t>(kRec) + i * DK + 8 * rc;
+    // one slice's fields, loaded together, then added in slice order
+    struct Slice {
+        float a, c, gr, gc, b;
+        f4 dk[2], dq[2];
+    };
+    auto load_slice = [&](int wg, Slice& x) __attribute__((always_inline)) {
+        const float* r = rec0 + wg * static_cast<size_t>(kRec);
+        x.a = r[kRecA + tid];
+        x.c = r[kRecC + tid];
+        x.gr = r[kRecGr + tg];
+        x.gc = r[kRecGc + tg];
+        x.b = r[kRecB + tg];
+        const float* rr = r + i * DK + 8 * rc;
 #pragma unroll
         for (int hh = 0; hh < 2; hh++) {
-            dks[hh] += *reinterpret_cast<const f4*>(r + kRecDk + 4 * hh);
-            dqs[hh] += *reinterpret_cast<const f4*>(r + kRecDq + 4 * hh);
+            x.dk[hh] = *reinterpret_cast<const f4*>(rr + kRecDk + 4 * hh);
+            x.dq[hh] = *reinterpret_cast<const f4*>(rr + kRecDq + 4 * hh);
         }
+    };
+    auto add_slice = [&](const Slice& x) __attribute__((always_inline)) {
+        sa += x.a;
+        sc += x.c;
+        sg += x.gr + x.gc;
+        sb += x.b;
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            dks[hh] += x.dk[hh];
+            dqs[hh] += x.dq[hh];
+        }
+    };
+    if (nwg == 2) {  // (d_v = 128) both slices' loads in flight together
+        Slice x0, x1;
+        load_slice(0, x0);
+        load_slice(1, x1);
+        add_slice(x0);
+        add_slice(x1);
+    } else {
+        for (int wg = 0; wg < nwg; wg++) {
+            Slice x;
+            load_slice(wg, x);
+            add_slice(x);
+        }
+    }
+    if (!ok) {
+        kw = u4{0u, 0u, 0u, 0u};
+        qw = u4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        Kf[i][8 * rc + 2 * e] = __uint_as_float(kw[e] << 16);
+        Kf[i][8 * rc + 2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
+        Qf[i][8 * rc + 2 * e] = __uint_as_float(qw[e] << 16);
+        Qf[i][8 * rc + 2 * e + 1] = __uint_as_float(qw[e] & 0xFFFF0000u);
+    }
+    Ab[tid / kBlk][tid % kBlk] = sa;
+    Cb[tid / kBlk][tid % kBlk] = sc;
+    if (tid < kBlk) {
+        dG[tid] = sg;
+        if (t0 + tid < T) a.dbeta[(tseq + t0 + tid) * H + h] = sb;
     }
     __syncthreads();
     float qdot = 0.0f;
