@@ -203,9 +203,10 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
     auto nblocks = [&](int c) { return (min(T, (c + 1) * C) - c * C + kBlkTok - 1) / kBlkTok; };
     TokFetch<S, KDA, true> f;
     auto fetch = [&](int c, int j) __attribute__((always_inline)) {
-        if (c < 0) return;
-        const int t = c * C + kBlkTok * j + w;
-        if (t < min(T, (c + 1) * C)) f.fetch(in, p, tok0 + static_cast<size_t>(t) * H, col, lane);
+        // (tokens past the chunk or the sequence, or of no chunk, fetch a valid token that is
+        // never published: the loads stay unconditional)
+        const int t = min(max(c, 0) * C + kBlkTok * j + w, T - 1);
+        f.fetch(in, p, tok0 + static_cast<size_t>(t) * H, col, lane);
     };
     // publish block (c, j) from the fetched words, fetch (nc, nj), make the records visible
     auto publish = [&](int nt, int nc, int nj) __attribute__((always_inline)) {
@@ -395,9 +396,8 @@ __global__ __launch_bounds__(kTokThreads) void bwd_tok_kernel(TokParams p, BwdAr
             // parity), so that the two independent chains fill each other's latencies.
             TokFetch<S, KDA, true> fa;  // the recompute's next block (f holds the adjoint's)
             auto fetch_a = [&](int c, int j) __attribute__((always_inline)) {
-                if (c < 0) return;
-                const int t = c * C + kBlkTok * j + w;
-                if (t < min(T, (c + 1) * C)) fa.fetch(in, p, tok0 + static_cast<size_t>(t) * H, col, lane);
+                const int t = min(max(c, 0) * C + kBlkTok * j + w, T - 1);
+                fa.fetch(in, p, tok0 + static_cast<size_t>(t) * H, col, lane);
             };
             auto run_ab = [&](int c, bool first) {
                 __builtin_amdgcn_s_waitcnt(0);  // the kept codes of chunk c are stored

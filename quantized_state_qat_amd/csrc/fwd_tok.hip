@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kTokThreads) void fwd_tok_kernel(TokParams p, FwdAr
     }
 
     TokFetch<S, KDA, false> f;
-    auto fetch = [&](int u) __attribute__((always_inline)) {
-        if (u < T) f.fetch(in, p, tok0 + static_cast<size_t>(u) * H, col, lane);
+    auto fetch = [&](int u) __attribute__((always_inline)) {  // (a token past the end fetches the last; never published)
+        f.fetch(in, p, tok0 + static_cast<size_t>(min(u, T - 1)) * H, col, lane);
     };
     auto publish = [&](int u) __attribute__((always_inline)) {
         if (u < T) f.template publish<RC>(ring, u % kTokRing, p, lane);

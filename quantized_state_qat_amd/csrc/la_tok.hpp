@@ -261,43 +261,58 @@ __device__ __forceinline__ void lane_wht(float& x0, float& x1, int lane, bool bf
 template <class S, bool KDA, bool BWD>
 struct TokFetch {
     static constexpr int DK = S::DK;
-    uint32_t k0 = 0, k1 = 0, q0 = 0, q1 = 0, g0 = 0, g1 = 0, b = 0, v = 0;
+    uint32_t k0 = 0, k1 = 0, q0 = 0, q1 = 0, g0 = 0, g1 = 0, gh = 0, b = 0, bh = 0, v = 0;
     float d = 0.0f;
 
+    // Every load is issued by every lane with no branch around it, from an address inside the
+    // tensor (lanes past a field's width read a word of the same row; the dtype only changes the
+    // address), so that the compiler keeps the loads in flight until publish instead of waiting
+    // for them where branches join.  publish selects what each lane uses.
     __device__ __forceinline__ void fetch(const TokInputs& in, const TokParams& p, size_t tok, int col, int lane) {
         const bool bf = p.qkv_dt == LA_BF16, gf = p.gate_dt == LA_F32;
-        if (bf) {
-            if (lane < DK / 2) {
-                k0 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(in.k) + tok * DK)[lane];
-                q0 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(in.q) + tok * DK)[lane];
-            }
-            if (lane < S::TC) v = static_cast<const uint16_t*>(in.v)[tok * p.dv + col];
-        } else {
-            const uint32_t* kp = static_cast<const uint32_t*>(in.k) + tok * DK;
-            const uint32_t* qp = static_cast<const uint32_t*>(in.q) + tok * DK;
-            if (lane < DK) { k0 = kp[lane]; q0 = qp[lane]; }
-            if (lane + 64 < DK) { k1 = kp[lane + 64]; q1 = qp[lane + 64]; }
-            if (lane < S::TC) v = static_cast<const uint32_t*>(in.v)[tok * p.dv + col];
-        }
+        // k and q: a row holds DK / 2 words (bf16 pairs) or DK words (fp32: lane and lane + 64)
+        const int w0 = min(lane, bf ? DK / 2 - 1 : DK - 1);
+        const int w1 = bf ? w0 : min(lane + 64, DK - 1);
+        const size_t rb = tok * DK * (bf ? 2 : 4);
+        const uint32_t* kp = reinterpret_cast<const uint32_t*>(static_cast<const char*>(in.k) + rb);
+        const uint32_t* qp = reinterpret_cast<const uint32_t*>(static_cast<const char*>(in.q) + rb);
+        k0 = kp[w0];
+        k1 = kp[w1];
+        q0 = qp[w0];
+        q1 = qp[w1];
+        // v: the word holding this column's element (bf16: the pair of columns 2i, 2i + 1; d_v is
+        // even, so the pair lies in the row)
+        const size_t ve = tok * p.dv + col;
+        v = *(bf ? reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(in.v) + (ve & ~static_cast<size_t>(1)))
+                 : static_cast<const uint32_t*>(in.v) + ve);
         if (KDA) {
-            if (!gf) {
-                if (lane < DK / 2) g0 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(in.g) + tok * DK)[lane];
-            } else {
-                const uint32_t* gp = static_cast<const uint32_t*>(in.g) + tok * DK;
-                if (lane < DK) g0 = gp[lane];
-                if (lane + 64 < DK) g1 = gp[lane + 64];
-            }
+            const int u0 = min(lane, gf ? DK - 1 : DK / 2 - 1);
+            const int u1 = gf ? min(lane + 64, DK - 1) : u0;
+            const uint32_t* gp = reinterpret_cast<const uint32_t*>(static_cast<const char*>(in.g) + tok * DK * (gf ? 4 : 2));
+            g0 = gp[u0];
+            g1 = gp[u1];
         } else {
-            g0 = gf ? static_cast<const uint32_t*>(in.g)[tok] : static_cast<const uint16_t*>(in.g)[tok];
+            // one element: two 16-bit loads (the fp32 value's halves, or the bf16 value twice)
+            const uint16_t* gp = static_cast<const uint16_t*>(in.g) + (gf ? 2 * tok : tok);
+            g0 = gp[0];
+            gh = gp[gf ? 1 : 0];
         }
-        b = gf ? static_cast<const uint32_t*>(in.beta)[tok] : static_cast<const uint16_t*>(in.beta)[tok];
-        if (BWD && lane < S::TC) d = in.dout[tok * p.dv + col];
+        const uint16_t* bp = static_cast<const uint16_t*>(in.beta) + (gf ? 2 * tok : tok);
+        b = bp[0];
+        bh = bp[gf ? 1 : 0];
+        if (BWD) d = in.dout[ve];
     }
 
     template <bool HAD>
     __device__ __forceinline__ void publish(TokRing<S, KDA, BWD>& ring, int slot, const TokParams& p, int lane) const {
         const bool bf = p.qkv_dt == LA_BF16, gf = p.gate_dt == LA_F32;
         auto wid = [](uint32_t x, bool b16) { return b16 ? __uint_as_float(x << 16) : __uint_as_float(x); };
+        // the words past the row's width are zero (they enter k . q)
+        const bool ok0 = lane < (bf ? DK / 2 : DK), ok1 = !bf && lane + 64 < DK;
+        const uint32_t k0 = ok0 ? this->k0 : 0u, q0 = ok0 ? this->q0 : 0u;
+        const uint32_t k1 = ok1 ? this->k1 : 0u, q1 = ok1 ? this->q1 : 0u;
+        const uint32_t g0w = gf ? (gh << 16) | g0 : g0, bw = gf ? (bh << 16) | b : b;
+        const uint32_t vw = bf ? ((lane & 1) ? v >> 16 : v & 0xFFFFu) : v;  // the column's parity is the lane's
         float kx0, kx1, qx0, qx1;
         if (bf) {
             kx0 = __uint_as_float(k0 << 16);
@@ -339,13 +354,13 @@ struct TokFetch {
                 if (i < DK) ring.ga[slot][i] = expf(e ? gx1 : gx0);
             }
         } else {
-            a = expf(wid(g0, !gf));
+            a = expf(wid(g0w, !gf));
         }
         if (lane < S::TC) {
-            ring.v[slot][lane] = wid(v, bf);
+            ring.v[slot][lane] = wid(vw, bf);
             if (BWD) ring.dout[slot][lane] = d;
         }
-        if (lane == 0) ring.sc[slot] = make_float4(a, wid(b, !gf), kq, 0.0f);
+        if (lane == 0) ring.sc[slot] = make_float4(a, wid(bw, !gf), kq, 0.0f);
     }
 };
 
